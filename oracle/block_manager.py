@@ -1,0 +1,210 @@
+"""Pure-Python model of the host block manager.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  The C++ block manager
+in the product library is checked against this model, operation by operation,
+on seeded random operation sequences.
+
+Rules, as the pages state them:
+  * A sequence of S tokens holds ceil(S / B) blocks ([P1] section 8 item 3).
+  * Fork copies the parent's block table and raises the reference count of
+    every block in it; no data moves ([P1] section 16 step 2).
+  * Appending at position S ([P1] sections 15-16):
+      - S mod B == 0: the tail is full, take a fresh block and write offset 0;
+      - S mod B != 0 and the tail block is shared (ref > 1): copy-on-write --
+        take a fresh block, copy the tail's valid tokens into it, drop the old
+        block's count by one, point the table at the new block (ref 1), write
+        there;
+      - S mod B != 0 and the tail is private (ref == 1): write in place.
+  * On release every block's count drops by one; a block reaching 0 returns
+    to the free list ([P1] section 17).
+  * Running out of free blocks fails the operation and changes nothing
+    ([P1] section 20, test 4: exhaustion leaves the sequence untouched).
+
+Readings taken where the pages leave a detail open (also in the design doc):
+  * The free list is a LIFO stack: the most recently released block is handed
+    out first.  [P1]'s teaching model pops from the end of a list that starts
+    as the block ids in reverse order, so with no explicit order blocks
+    0, 1, 2, ... are handed out in that order.  ``pop_order`` lets a caller
+    fix the initial hand-out order (the first entry is handed out first).
+  * The copy-on-write copy is reported as a (src, dst) pair; the device copy
+    clones the whole block.
+  * A batch append is all-or-nothing: when one sequence of the batch cannot
+    get a block, the appends already done in that batch are undone in reverse
+    order, which restores the free list exactly.
+  * Operations on unknown or duplicate sequence ids fail with NOT_FOUND or
+    EXISTS and change nothing.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_NO_FREE_BLOCKS = 3
+ERR_EXISTS = 4
+ERR_NOT_FOUND = 5
+
+
+class BlockManagerModel:
+    def __init__(self, num_blocks: int, block_size: int,
+                 pop_order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        if pop_order is None:
+            pop_order = range(num_blocks)
+        pop_order = [int(b) for b in pop_order]
+        if sorted(pop_order) != list(range(num_blocks)):
+            raise ValueError("pop_order must be a permutation of the block ids")
+        # top of the stack is the end of the list
+        self.free: List[int] = list(reversed(pop_order))
+        self.ref: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+        self.cow_copies = 0
+
+    # -- allocation -------------------------------------------------------
+    def _pop(self) -> int:
+        b = self.free.pop()
+        self.ref[b] = 1
+        return b
+
+    def add_seq(self, seq: int, num_tokens: int) -> int:
+        if num_tokens <= 0:
+            return ERR_INVALID_ARG
+        if seq in self.tables:
+            return ERR_EXISTS
+        need = -(-num_tokens // self.block_size)
+        if len(self.free) < need:
+            return ERR_NO_FREE_BLOCKS
+        self.tables[seq] = [self._pop() for _ in range(need)]
+        self.lens[seq] = num_tokens
+        return OK
+
+    def fork(self, parent: int, child: int) -> int:
+        if parent not in self.tables:
+            return ERR_NOT_FOUND
+        if child in self.tables:
+            return ERR_EXISTS
+        for b in self.tables[parent]:
+            self.ref[b] += 1
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        return OK
+
+    def append_slot(self, seq: int) -> Tuple[int, int, int, int]:
+        """Reserve the slot of position len(seq).  Returns (status, slot, cow_src, cow_dst)."""
+        if seq not in self.tables:
+            return ERR_NOT_FOUND, -1, -1, -1
+        table = self.tables[seq]
+        length = self.lens[seq]
+        off = length % self.block_size
+        src = dst = -1
+        if off != 0:
+            tail = table[-1]
+            if self.ref[tail] > 1:
+                if not self.free:
+                    return ERR_NO_FREE_BLOCKS, -1, -1, -1
+                new = self._pop()
+                self.ref[tail] -= 1
+                table[-1] = new
+                src, dst = tail, new
+                self.cow_copies += 1
+                block = new
+            else:
+                block = tail
+        else:
+            if not self.free:
+                return ERR_NO_FREE_BLOCKS, -1, -1, -1
+            block = self._pop()
+            table.append(block)
+        self.lens[seq] = length + 1
+        return OK, block * self.block_size + off, src, dst
+
+    def _undo_append(self, seq: int, src: int, dst: int) -> None:
+        table = self.tables[seq]
+        length = self.lens[seq] - 1
+        self.lens[seq] = length
+        if src >= 0:  # copy-on-write: give the new block back, re-share the old tail
+            self.ref[dst] = 0
+            self.free.append(dst)
+            self.ref[src] += 1
+            table[-1] = src
+            self.cow_copies -= 1
+        elif length % self.block_size == 0:  # a fresh block was taken
+            b = table.pop()
+            self.ref[b] = 0
+            self.free.append(b)
+
+    def append_slots(self, seqs: Sequence[int]) -> Tuple[int, List[int], List[Tuple[int, int]], int]:
+        """Batch append, all-or-nothing.  Returns (status, slots, cow_pairs, failed_index)."""
+        done: List[Tuple[int, int, int]] = []
+        slots: List[int] = []
+        pairs: List[Tuple[int, int]] = []
+        for i, seq in enumerate(seqs):
+            st, slot, src, dst = self.append_slot(seq)
+            if st != OK:
+                for s, a, b in reversed(done):
+                    self._undo_append(s, a, b)
+                return st, [], [], i
+            done.append((seq, src, dst))
+            slots.append(slot)
+            if src >= 0:
+                pairs.append((src, dst))
+        return OK, slots, pairs, -1
+
+    def free_seq(self, seq: int) -> int:
+        if seq not in self.tables:
+            return ERR_NOT_FOUND
+        for b in self.tables[seq]:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.tables[seq]
+        del self.lens[seq]
+        return OK
+
+    # -- queries ----------------------------------------------------------
+    def build_batch(self, seqs: Sequence[int], max_blocks: int) -> Tuple[int, List[List[int]], List[int]]:
+        tables, lens = [], []
+        for seq in seqs:
+            if seq not in self.tables:
+                return ERR_NOT_FOUND, [], []
+            t = self.tables[seq]
+            if len(t) > max_blocks:
+                return ERR_INVALID_ARG, [], []
+            tables.append(t + [0] * (max_blocks - len(t)))
+            lens.append(self.lens[seq])
+        return OK, tables, lens
+
+    def pop_order(self) -> List[int]:
+        """The free list in hand-out order (next block first)."""
+        return list(reversed(self.free))
+
+    def stats(self) -> Dict[str, int]:
+        """Pool accounting in the terms of [P1] section 17.
+
+        A block's fill is the number of valid tokens it holds (the largest
+        count over the sequences that reference it); stored tokens sum the
+        fills, so shared blocks count once, and tail waste is the slots of
+        blocks in use minus the stored tokens.
+        """
+        fill: Dict[int, int] = {}
+        for seq, table in self.tables.items():
+            length = self.lens[seq]
+            for lb, b in enumerate(table):
+                valid = min(self.block_size, length - lb * self.block_size)
+                fill[b] = max(fill.get(b, 0), valid)
+        used = sum(1 for r in self.ref if r > 0)
+        stored = sum(fill.values())
+        return {
+            "num_blocks": self.num_blocks,
+            "num_free": len(self.free),
+            "num_used": used,
+            "num_seqs": len(self.tables),
+            "cow_copies": self.cow_copies,
+            "stored_tokens": stored,
+            "tail_waste_slots": used * self.block_size - stored,
+        }
