@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+A step is one pass of the whole decode-step path over a batch of sequences:
+  1. host block manager: one batch append (slot per sequence, copy-on-write
+     pairs), block tables and lengths for the batch;
+  2. one host-to-device copy of slots, lengths and tables (pinned staging);
+  3. pa_copy_blocks (when the batch produced copy-on-write pairs);
+  4. pa_append_kv of the new token of every sequence;
+  5. pa_decode over every sequence's context (partitions + merge).
+Contexts grow by one token per step.  Inputs are resident in HBM before the
+timed region starts.  `value` is the KV bytes the decode reads per step
+(sum of context lengths x 2 x Hkv x d_head x 2 bytes) divided by the
+wall-clock time of a step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa8b]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (KV read) + µs/step, 8B GQA shape"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa8b", choices=["gqa8b", "sweep_b8", "sweep_b16", "sweep_b32"])
+    ap.add_argument("--replicas", type=int, default=4,
+                    help="pool copies rotated step to step so reads come from HBM, not the 256 MB Infinity Cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def workload(name):
+    import synth
+    if name == "gqa8b":
+        return synth.gqa8b()
+    return synth.sweep(int(name.split("_b")[1]))
+
+
+class Runner:
+    """Holds the resident state of one benchmark workload."""
+
+    def __init__(self, w, steps_total, replicas, device="cuda"):
+        import torch
+        import synth
+        import paged_kv_cache_124_amd as pa
+        self.pa = pa
+        self.torch = torch
+        self.w = w
+        self.lens0 = synth.seq_lengths(w)
+        self.n = len(self.lens0)
+        bs = w.block_size
+        grown = [s + steps_total for s in self.lens0]
+        self.num_blocks = synth.pool_blocks(w, grown)
+        self.max_blocks = max(-(-s // bs) for s in grown)
+        self.max_ctx = max(grown)
+        self.bm = pa.BlockManager(self.num_blocks, bs, synth.pop_order(self.num_blocks, w.seed))
+        for i, s in enumerate(self.lens0):
+            assert self.bm.add_seq(i, s) == 0
+        self.seqs = np.arange(self.n, dtype=np.int64)
+        dt = synth.torch_dtype(w)
+        kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, torch.tensor([], dtype=dt).element_size())
+        self.k = [synth.fill_randn_(torch.empty(kshape, dtype=dt, device=device), w.value_scale, w.seed * 10 + 1 + 7 * r)
+                  for r in range(replicas)]
+        self.v = [synth.fill_randn_(torch.empty(vshape, dtype=dt, device=device), w.value_scale, w.seed * 10 + 2 + 7 * r)
+                  for r in range(replicas)]
+        self.q = synth.randn((self.n, w.hq, w.d), dt, w.value_scale, w.seed * 10 + 3, device)
+        self.k_new = synth.randn((self.n, w.hkv, w.d), dt, w.value_scale, w.seed * 10 + 4, device)
+        self.v_new = synth.randn((self.n, w.hkv, w.d), dt, w.value_scale, w.seed * 10 + 5, device)
+        self.out = torch.empty_like(self.q)
+        ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+        self.part = pa.pa_decode_partition_tokens(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
+        # staging: [slots N | lens N | pairs 2N | tables N*max_blocks]
+        self.words = 4 * self.n + self.n * self.max_blocks
+        self.host = [torch.empty(self.words, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.host_ev = [None, None]
+        self.dev = torch.empty(self.words, dtype=torch.int32, device=device)
+        self.step_i = 0
+        self.replicas = replicas
+        self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
+        self.decode_events = []
+
+    def step(self, time_decode=False):
+        torch, pa = self.torch, self.pa
+        n, mb = self.n, self.max_blocks
+        st, slots, pairs, _ = self.bm.append_slots(self.seqs)
+        if st != 0:
+            raise RuntimeError(f"block manager append failed: status {st}")
+        b = self.step_i & 1
+        if self.host_ev[b] is not None:
+            self.host_ev[b].synchronize()
+        h = self.host[b].numpy()
+        h[:n] = slots
+        npairs = len(pairs)
+        if npairs:
+            h[2 * n:2 * n + 2 * npairs] = pairs.reshape(-1)
+        st, tables, lens = self.bm.build_batch(self.seqs, mb)
+        assert st == 0
+        h[n:2 * n] = lens
+        h[4 * n:] = tables.reshape(-1)
+        self.dev.copy_(self.host[b], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.host_ev[b] = ev
+        d = self.dev
+        r = self.step_i % self.replicas
+        k, v = self.k[r], self.v[r]
+        if npairs:
+            pa.pa_copy_blocks(k, v, d[2 * n:2 * n + 2 * npairs].view(npairs, 2))
+        pa.pa_append_kv(k, v, self.k_new, self.v_new, d[:n])
+        if time_decode:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        pa.pa_decode(self.out, self.q, k, v, d[4 * n:].view(n, mb), d[n:2 * n], self.w.scale, self.max_ctx,
+                     workspace=self.ws)
+        if time_decode:
+            e1.record()
+            self.decode_events.append((e0, e1))
+        self.step_i += 1
+        return int(lens.sum()) * self.kv_bytes_per_token
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle on this host's cores over a bounded sample of the same workload (one BLAS thread).
+
+    Inputs (one decode step of every sequence, values as stored in bf16) are
+    built first and kept in host memory; then whole passes over all sequences
+    are timed until `seconds` of compute have accumulated.
+    """
+    import torch
+    import synth
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as OA
+    lens = synth.seq_lengths(w)
+    rng = np.random.default_rng(0)
+    bs, hkv, d = w.block_size, w.hkv, w.d
+    inputs = []
+    for n, s in enumerate(lens):
+        nb = -(-s // bs)
+        kp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 5000 + n).float().numpy()
+        vp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 6000 + n).float().numpy()
+        q = synth.randn((1, w.hq, d), torch.bfloat16, w.value_scale, 7000 + n).double().numpy()
+        table = rng.permutation(nb)[None]
+        kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+        kp2[table[0]] = kp
+        vp2[table[0]] = vp
+        inputs.append((q, kp2, vp2, table, s))
+    step_bytes = sum(lens) * 2 * hkv * d * 2
+    passes, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        while t_total < seconds:
+            t0 = time.perf_counter()
+            for q, kp, vp, table, s in inputs:
+                OA.paged_decode(q, kp, vp, table, [s], w.scale)
+            t_total += time.perf_counter() - t0
+            passes += 1
+    return {"value": round(passes * step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over one decode step of all {len(lens)} sequences of the same workload "
+                      f"(all {w.hq} query heads; fp64 NumPy oracle, one thread), {t_total:.1f} s of compute",
+            "us_per_step": round(t_total / passes * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode path needs no inter-GPU exchange: sequences or KV heads shard with no collective).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    w = workload(args.workload)
+    total = args.steps + args.warmup + 1
+    print(f"[bench] building workload {w.name}", file=sys.stderr, flush=True)
+    run = Runner(w, total, args.replicas)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    kv_bytes = 0
+    for _ in range(args.steps):
+        kv_bytes += run.step(time_decode=True)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_step = max(gpu_ms, wall * 1e3) / args.steps
+    value = kv_bytes / args.steps / (ms_step * 1e-3) / 1e9
+    dec_ms = [a.elapsed_time(b) for a, b in run.decode_events]
+    dec_avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
+    bytes_per_launch = kv_bytes / args.steps
+    achieved = bytes_per_launch / (dec_avg_us * 1e-6) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, block {w.block_size}, "
+                               f"bf16, contexts {min(run.lens0)}..{max(run.lens0)} growing 1/step",
+                   "num_seqs": run.n, "block_size": w.block_size, "pool_blocks": run.num_blocks,
+                   "pool_replicas": args.replicas, "partition_tokens": run.part,
+                   "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode (decode_mfma + merge_partitions)", "avg_us": round(dec_avg_us, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

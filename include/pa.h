@@ -1,0 +1,246 @@
+/*
+ * pa.h -- PagedAttention decode on AMD Instinct MI355X (gfx950): C ABI of libpa.so
+ *
+ * The KV cache of every sequence lives in fixed-size physical blocks of a
+ * shared pool and is reached through a per-sequence block table of int32
+ * physical block ids ("PagedAttention: Virtual Memory for the KV Cache",
+ * sections 5-7).  One query token per sequence attends over its cache
+ * (same page, section 1; "PagedAttention in vLLM: scattered memory, exact
+ * attention", section 10).
+ *
+ * Conventions for every entry point
+ *   - Array arguments of the device entry points (pa_decode, pa_append_kv,
+ *     pa_copy_blocks) are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps device memory.  Block-manager (pa_bm_*)
+ *     arguments are HOST pointers owned by the caller.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t passed
+ *     as void*; NULL = the default stream) and is ordered with other work on
+ *     that stream only.  Within one decode step call pa_copy_blocks, then
+ *     pa_append_kv, then pa_decode, on one stream.
+ *   - Every entry point returns an int status (PA_OK = 0).  Argument errors
+ *     are detected on the host before anything is enqueued and leave all
+ *     state unchanged.  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation.  No C++ exception crosses the ABI.
+ *   - All sizes are in elements unless a name ends in _bytes.
+ *
+ * Physical pool layout (one layer; a multi-layer pool stacks layers with a
+ * stride of layer_stride_elems elements).  E = element size, x = 16 / E
+ * (x = 8 for bf16, 4 for fp32), B = block_size, D = d_head:
+ *
+ *   K pool: [num_blocks][Hkv][D / x][B][x]
+ *       key element d of the token in slot `off` of block `pb`, KV head j:
+ *       k_pool[(((pb * Hkv + j) * (D / x) + d / x) * B + off) * x + d % x]
+ *   V pool: [num_blocks][Hkv][D][B]
+ *       value element d: v_pool[((pb * Hkv + j) * D + d) * B + off]
+ *
+ *   The pages call the in-block layout an implementation choice ("PagedAttention:
+ *   Virtual Memory for the KV Cache", section 12).  This one is chosen for
+ *   gfx950 matrix-core operands: one 16-byte load per lane of each key row
+ *   chunk, and runs of consecutive tokens per value element.  Each
+ *   (block, KV head) is one contiguous run of B * D * E bytes in each pool.
+ *
+ * Address translation ("PagedAttention: Virtual Memory for the KV Cache",
+ * section 7): token i of a sequence lives in logical block i / B at offset
+ * i % B, i.e. physical block block_table[i / B]; its slot is
+ * block_table[i / B] * B + i % B.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes and element types ------------------------------------ */
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,    /* bad pointer, size or combination of sizes           */
+  PA_ERR_UNSUPPORTED = 2,    /* valid request outside the compiled shapes/dtypes    */
+  PA_ERR_NO_FREE_BLOCKS = 3, /* pool exhausted; the operation changed nothing       */
+  PA_ERR_EXISTS = 4,         /* sequence id already present                        */
+  PA_ERR_NOT_FOUND = 5,      /* sequence id unknown                                 */
+  PA_ERR_WORKSPACE = 6,      /* workspace missing or smaller than required          */
+  PA_ERR_HIP = 7             /* the HIP runtime refused a launch                    */
+};
+
+enum { PA_F32 = 0, PA_BF16 = 1 };
+
+/* Text for a status code (static storage; never NULL). */
+const char* pa_status_string(int status);
+
+/* Library ABI version; bumped on any incompatible change. */
+int pa_version(void);
+
+/* ---- decode attention ------------------------------------------------------
+ *
+ * pa_decode: one decode step of paged attention for a batch of sequences.
+ * Defined by "PagedAttention: Virtual Memory for the KV Cache", sections 1
+ * and 13, and "PagedAttention in vLLM: scattered memory, exact attention",
+ * sections 10-11.  For sequence n, query head h, KV head j = h / (Hq / Hkv)
+ * and tokens t < S = context_lens[n]:
+ *
+ *     s_t = scale * dot(q[n][h], K_t),  K_t, V_t gathered through the table
+ *     out[n][h] = sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s)
+ *
+ * Long contexts are split into partitions processed in parallel; each writes
+ * a (max, shifted weight sum, shifted value sum) summary into `workspace` and
+ * a second kernel merges them with the common-maximum rule of the second page,
+ * section 11.  The partition size and the merge order are fixed for a given
+ * (num_seqs, Hkv, d_head, block_size, max_context_len), so repeated calls on
+ * the same inputs give bit-identical outputs.
+ *
+ *   out            [num_seqs][Hq][d_head], element type `dtype`
+ *   q              [num_seqs][Hq][d_head], element type `dtype`
+ *   k_pool, v_pool one layer's pools in the layout above, `num_blocks` blocks
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]; entries at logical
+ *                  blocks >= ceil(S / B) are never read
+ *   context_lens   int32 [num_seqs], 0 <= S <= max_context_len and
+ *                  ceil(S / B) <= max_blocks_per_seq.  S = 0 gives zeros.
+ *   scale          multiplies q.K (1 / sqrt(d_head) for the textbook rule)
+ *   max_context_len an upper bound of all S (sizes the launch without a
+ *                  device read)
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
+ *                  bytes; may be NULL when that size is 0.  Contents on entry
+ *                  are ignored.
+ * Supported: Hq % Hkv == 0, Hq / Hkv <= 64, d_head in {64, 128},
+ * block_size in {8, 16, 32}, dtype PA_F32 or PA_BF16 (fp32 accumulation;
+ * bf16 outputs are rounded to nearest even).  Block ids outside
+ * [0, num_blocks) are never dereferenced (they read as zero keys and values).
+ */
+int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* context_lens,
+              int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+              int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_decode needs for these sizes (0 when no split is used). */
+size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                                 int max_context_len, int dtype);
+
+/* Tokens per partition that pa_decode uses for these sizes (for reporting). */
+int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                               int max_context_len, int dtype);
+
+/* ---- KV append ---------------------------------------------------------------
+ *
+ * pa_append_kv: write each new token's key and value, for all KV heads, into
+ * its slot: block slot / B, offset slot % B ("PagedAttention: Virtual Memory
+ * for the KV Cache", section 16: the appended position is written into its
+ * block at its offset).  Bit-exact copy of the input elements.
+ *
+ *   k_new, v_new   [num_tokens][Hkv][d_head], element type `dtype`
+ *   slot_mapping   int32 [num_tokens]; slot < 0 skips the token; slots at or
+ *                  beyond num_blocks * block_size are skipped as well
+ * Slots must be distinct within one call.
+ */
+int pa_append_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, int num_tokens, int Hkv, int d_head,
+                 int block_size, int num_blocks, int dtype, void* stream);
+
+/* ---- copy-on-write block copy ------------------------------------------------
+ *
+ * pa_copy_blocks: for each pair (src, dst) and each of num_layers layers,
+ * copy block src of both pools over block dst, all KV heads and all slots
+ * ("PagedAttention: Virtual Memory for the KV Cache", sections 15-16: a shared
+ * tail block is cloned before a sequence writes into it).  Bit-exact.
+ *
+ *   src_dst_pairs  int32 [num_pairs][2] on the device; destinations are
+ *                  distinct and no destination is a source in the same call;
+ *                  pairs with an id outside [0, num_blocks) are skipped
+ *   layer_stride_elems  elements between consecutive layers of each pool
+ *                  (ignored when num_layers == 1)
+ */
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int num_pairs,
+                   int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
+                   int64_t layer_stride_elems, int dtype, void* stream);
+
+/* ---- host block manager ------------------------------------------------------
+ *
+ * Free list, per-block reference counts, block tables, fork and copy-on-write
+ * of a shared unaligned tail ("PagedAttention: Virtual Memory for the KV
+ * Cache", sections 14-17 and the teaching allocator of section 20).  Host
+ * only; no device calls.  A handle is not thread-safe: one thread at a time.
+ *
+ * Rules:
+ *   - a sequence of S tokens holds ceil(S / B) blocks;
+ *   - fork copies the parent's table and adds one reference to every block;
+ *   - appending at position S: if S % B == 0 a fresh block is taken; else if
+ *     the tail block is shared (ref > 1) a fresh block is taken, the pair
+ *     (old tail, fresh block) is reported for a device block copy, the old
+ *     tail loses one reference and the table points at the fresh block; else
+ *     the token is written in place.  The returned slot is always in a block
+ *     with exactly one reference;
+ *   - release drops one reference per block; blocks reaching zero return to
+ *     the free list, which is LIFO (the last block released is handed out
+ *     next).  The caller must not let later work reuse a freed block before
+ *     earlier device work that reads it is ordered before it (same stream);
+ *   - any failure (PA_ERR_*) leaves the manager exactly as it was.
+ */
+typedef struct pa_bm pa_bm;
+
+typedef struct pa_bm_stats_t {
+  int64_t num_blocks;       /* pool size                                          */
+  int64_t num_free;         /* blocks on the free list                            */
+  int64_t num_used;         /* blocks with at least one reference                 */
+  int64_t num_seqs;         /* live sequences                                     */
+  int64_t cow_copies;       /* copy-on-write pairs issued so far                  */
+  int64_t stored_tokens;    /* valid token slots in used blocks, shared ones once */
+  int64_t tail_waste_slots; /* num_used * block_size - stored_tokens              */
+} pa_bm_stats_t;
+
+/* Create a manager of num_blocks blocks of block_size tokens.  pop_order
+ * (nullable, host, num_blocks distinct ids) fixes the order in which free
+ * blocks are first handed out; NULL hands out 0, 1, 2, ...  Returns NULL on
+ * invalid sizes or a pop_order that is not a permutation. */
+pa_bm* pa_bm_create(int num_blocks, int block_size, const int32_t* pop_order);
+void pa_bm_destroy(pa_bm* bm);
+
+/* New sequence of num_tokens >= 1 tokens (its prompt): ceil(n / B) blocks. */
+int pa_bm_add_seq(pa_bm* bm, int64_t seq, int num_tokens);
+
+/* New sequence `child` sharing every block of `parent`. */
+int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+
+/* Reserve the slot of the next position of `seq`.  *slot receives
+ * block * B + offset; *cow_src / *cow_dst receive the copy-on-write pair or
+ * -1 / -1.  On failure all three receive -1. */
+int pa_bm_append_slot(pa_bm* bm, int64_t seq, int32_t* slot, int32_t* cow_src, int32_t* cow_dst);
+
+/* Batch append, all-or-nothing, in array order: slots[i] for seqs[i];
+ * cow_pairs (capacity n pairs, int32 [n][2]) receives the copy-on-write pairs
+ * in order and *num_pairs their count.  On failure nothing changes and
+ * *num_pairs receives -(index of the failing sequence) - 1. */
+int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int n, int32_t* slots,
+                       int32_t* cow_pairs, int* num_pairs);
+
+/* Release a sequence. */
+int pa_bm_free_seq(pa_bm* bm, int64_t seq);
+
+/* Fill block_tables_out int32 [n][max_blocks_per_seq] (unused entries 0) and
+ * context_lens_out int32 [n] for the listed sequences. */
+int pa_bm_build_batch(pa_bm* bm, const int64_t* seqs, int n, int max_blocks_per_seq,
+                      int32_t* block_tables_out, int32_t* context_lens_out);
+
+/* Reference count of a block (-1 for an id outside the pool). */
+int pa_bm_refcount(pa_bm* bm, int block);
+/* Number of free blocks. */
+int pa_bm_num_free(pa_bm* bm);
+/* Length of a sequence in tokens (-1 if unknown). */
+int64_t pa_bm_seq_len(pa_bm* bm, int64_t seq);
+/* Copy a sequence's table into out (capacity cap); *n_out = its length. */
+int pa_bm_block_table(pa_bm* bm, int64_t seq, int32_t* out, int cap, int* n_out);
+/* Copy the free list in hand-out order (next block first). */
+int pa_bm_free_list(pa_bm* bm, int32_t* out, int cap, int* n_out);
+/* True (1) when a new sequence of num_tokens tokens fits the free blocks. */
+int pa_bm_can_allocate(pa_bm* bm, int num_tokens);
+/* Pool accounting in the terms of the first page's section 17. */
+int pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

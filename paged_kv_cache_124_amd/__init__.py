@@ -1,0 +1,22 @@
+"""PagedAttention decode for AMD Instinct MI355X (gfx950).
+
+The work runs in libpa.so (hand-written HIP kernels and a C++ block manager,
+C ABI in ``include/pa.h``).  This package is its thin Python binding: the
+functions below have the names of the C entry points and only marshal
+arguments.
+"""
+
+from ._lib import (  # noqa: F401
+    PA_BF16,
+    PA_F32,
+    PA_OK,
+    BlockManager,
+    PAError,
+    lib,
+    pa_append_kv,
+    pa_copy_blocks,
+    pa_decode,
+    pa_decode_partition_tokens,
+    pa_decode_workspace_bytes,
+    pool_shapes,
+)

@@ -1,0 +1,311 @@
+"""ctypes binding of libpa.so: argument marshalling only.
+
+Every function here forwards to the C entry point of the same name declared in
+``include/pa.h``.  Device arrays are passed as torch tensors (their data
+pointers go across the ABI); host arrays of the block manager as NumPy arrays.
+No computation of the method happens in Python: there is no fallback, and a
+missing library raises at import of this module.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PA_LIBRARY", os.path.join(_HERE, "libpa.so"))
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = 1
+PA_ERR_UNSUPPORTED = 2
+PA_ERR_NO_FREE_BLOCKS = 3
+PA_ERR_EXISTS = 4
+PA_ERR_NOT_FOUND = 5
+PA_ERR_WORKSPACE = 6
+PA_ERR_HIP = 7
+PA_F32 = 0
+PA_BF16 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libpa.so not found at {LIB_PATH}; build it with "
+                      f"`python -m paged_kv_cache_124_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.pa_status_string(status).decode()} (status {status})")
+
+
+class BMStats(ctypes.Structure):
+    _fields_ = [(n, c_int64) for n in ("num_blocks", "num_free", "num_used", "num_seqs",
+                                       "cow_copies", "stored_tokens", "tail_waste_slots")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_P32 = POINTER(c_int32)
+_P64 = POINTER(c_int64)
+_SIGS = {
+    "pa_status_string": (ctypes.c_char_p, [c_int]),
+    "pa_version": (c_int, []),
+    "pa_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                          c_int, c_float, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "pa_decode_workspace_bytes": (c_size_t, [c_int] * 7),
+    "pa_decode_partition_tokens": (c_int, [c_int] * 7),
+    "pa_append_kv": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                             c_int, c_void_p]),
+    "pa_copy_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int64,
+                               c_int, c_void_p]),
+    "pa_bm_create": (c_void_p, [c_int, c_int, _P32]),
+    "pa_bm_destroy": (None, [c_void_p]),
+    "pa_bm_add_seq": (c_int, [c_void_p, c_int64, c_int]),
+    "pa_bm_fork": (c_int, [c_void_p, c_int64, c_int64]),
+    "pa_bm_append_slot": (c_int, [c_void_p, c_int64, _P32, _P32, _P32]),
+    "pa_bm_append_slots": (c_int, [c_void_p, _P64, c_int, _P32, _P32, POINTER(c_int)]),
+    "pa_bm_free_seq": (c_int, [c_void_p, c_int64]),
+    "pa_bm_build_batch": (c_int, [c_void_p, _P64, c_int, c_int, _P32, _P32]),
+    "pa_bm_refcount": (c_int, [c_void_p, c_int]),
+    "pa_bm_num_free": (c_int, [c_void_p]),
+    "pa_bm_seq_len": (c_int64, [c_void_p, c_int64]),
+    "pa_bm_block_table": (c_int, [c_void_p, c_int64, _P32, c_int, POINTER(c_int)]),
+    "pa_bm_free_list": (c_int, [c_void_p, _P32, c_int, POINTER(c_int)]),
+    "pa_bm_can_allocate": (c_int, [c_void_p, c_int]),
+    "pa_bm_stats": (c_int, [c_void_p, POINTER(BMStats)]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def _check(status: int, where: str) -> None:
+    if status != PA_OK:
+        raise PAError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors in, data pointers across the ABI)
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return c_void_p(t.data_ptr())
+
+
+def pool_shapes(num_blocks: int, hkv: int, d_head: int, block_size: int, elem_bytes: int):
+    """Shapes of one layer's K and V pools in the library's layout (see include/pa.h)."""
+    x = 16 // elem_bytes
+    return (num_blocks, hkv, d_head // x, block_size, x), (num_blocks, hkv, d_head, block_size)
+
+
+def _pool_dims(k_pool, v_pool):
+    if k_pool.dim() != 5 or v_pool.dim() != 4:
+        raise ValueError("k_pool must be [num_blocks][Hkv][D/x][B][x] and v_pool [num_blocks][Hkv][D][B]")
+    nb, hkv, dx, bs, x = k_pool.shape
+    if tuple(v_pool.shape) != (nb, hkv, dx * x, bs) or x * k_pool.element_size() != 16:
+        raise ValueError("k_pool / v_pool shapes do not match the pool layout")
+    return nb, hkv, dx * x, bs
+
+
+def pa_decode_workspace_bytes(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype) -> int:
+    return int(lib.pa_decode_workspace_bytes(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype))
+
+
+def pa_decode_partition_tokens(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype) -> int:
+    return int(lib.pa_decode_partition_tokens(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype))
+
+
+def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+              workspace=None, stream=None):
+    """pa_decode of include/pa.h on torch device tensors.
+
+    q, out [N][Hq][D]; k_pool/v_pool one layer in the library layout; block_tables
+    int32 [N][max_blocks]; context_lens int32 [N].  ``workspace`` is a uint8
+    device tensor of at least pa_decode_workspace_bytes(...) bytes; when None a
+    buffer is allocated through torch for this call.
+    """
+    import torch
+    n, hq, d = q.shape
+    nb, hkv, d2, bs = _pool_dims(k_pool, v_pool)
+    if d2 != d or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or k_pool.dtype != q.dtype:
+        raise ValueError("q, out and the pools disagree in shape or dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or tuple(context_lens.shape) != (n,):
+        raise ValueError("block_tables must be [N][max_blocks] and context_lens [N]")
+    dt = _dtype_code(q)
+    need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pa_decode(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                       _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+                       n, hq, hkv, d, bs, float(scale), block_tables.shape[1], int(max_context_len), nb, dt,
+                       ws_ptr, ws_bytes, _stream_ptr(stream))
+    _check(st, "pa_decode")
+    return out
+
+
+def pa_append_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
+    """pa_append_kv of include/pa.h: k_new/v_new [T][Hkv][D], slot_mapping int32 [T]."""
+    import torch
+    nb, hkv, d, bs = _pool_dims(k_pool, v_pool)
+    t = k_new.shape[0]
+    if tuple(k_new.shape) != (t, hkv, d) or tuple(v_new.shape) != (t, hkv, d):
+        raise ValueError("k_new / v_new must be [T][Hkv][D]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new / v_new must have the pool's element type")
+    if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (t,):
+        raise ValueError("slot_mapping must be int32 [T]")
+    st = lib.pa_append_kv(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                          _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"), t, hkv, d, bs, nb,
+                          _dtype_code(k_pool), _stream_ptr(stream))
+    _check(st, "pa_append_kv")
+
+
+def pa_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
+    """pa_copy_blocks of include/pa.h.
+
+    Pools are one layer ([num_blocks]...) or all layers ([L][num_blocks]...);
+    src_dst_pairs is an int32 device tensor [P][2].
+    """
+    import torch
+    layered = k_pool.dim() == 6
+    kl, vl = (k_pool[0], v_pool[0]) if layered else (k_pool, v_pool)
+    nb, hkv, d, bs = _pool_dims(kl, vl)
+    layers = k_pool.shape[0] if layered else 1
+    if src_dst_pairs.dtype != torch.int32 or src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int32 [P][2]")
+    stride = kl.numel() if layered else 0
+    st = lib.pa_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(src_dst_pairs, "src_dst_pairs"),
+                            src_dst_pairs.shape[0], hkv, d, bs, nb, layers, stride, _dtype_code(k_pool),
+                            _stream_ptr(stream))
+    _check(st, "pa_copy_blocks")
+
+
+# ---------------------------------------------------------------------------
+# host block manager
+# ---------------------------------------------------------------------------
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr32(a):
+    return a.ctypes.data_as(_P32)
+
+
+class BlockManager:
+    """Owning wrapper of a pa_bm handle; each method is one pa_bm_* call."""
+
+    def __init__(self, num_blocks: int, block_size: int, pop_order=None):
+        order = None if pop_order is None else _i32(pop_order)
+        if order is not None and order.shape != (num_blocks,):
+            raise ValueError("pop_order must hold num_blocks entries")
+        self._h = lib.pa_bm_create(num_blocks, block_size, None if order is None else _ptr32(order))
+        if not self._h:
+            raise PAError(PA_ERR_INVALID_ARG, "pa_bm_create")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_seq(self, seq: int, num_tokens: int) -> int:
+        return lib.pa_bm_add_seq(self._h, seq, num_tokens)
+
+    def fork(self, parent: int, child: int) -> int:
+        return lib.pa_bm_fork(self._h, parent, child)
+
+    def append_slot(self, seq: int):
+        slot, src, dst = c_int32(), c_int32(), c_int32()
+        st = lib.pa_bm_append_slot(self._h, seq, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst))
+        return st, slot.value, src.value, dst.value
+
+    def append_slots(self, seqs):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        npairs = c_int()
+        st = lib.pa_bm_append_slots(self._h, s.ctypes.data_as(_P64), n, _ptr32(slots), _ptr32(pairs),
+                                    ctypes.byref(npairs))
+        if st != PA_OK:
+            return st, slots[:0], pairs[:0], -npairs.value - 1
+        return st, slots[:n], pairs[:npairs.value], -1
+
+    def free_seq(self, seq: int) -> int:
+        return lib.pa_bm_free_seq(self._h, seq)
+
+    def build_batch(self, seqs, max_blocks: int):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        tables = np.zeros((n, max_blocks), dtype=np.int32)
+        lens = np.zeros(n, dtype=np.int32)
+        st = lib.pa_bm_build_batch(self._h, s.ctypes.data_as(_P64), n, max_blocks, _ptr32(tables), _ptr32(lens))
+        return st, tables, lens
+
+    def refcount(self, block: int) -> int:
+        return lib.pa_bm_refcount(self._h, block)
+
+    def num_free(self) -> int:
+        return lib.pa_bm_num_free(self._h)
+
+    def seq_len(self, seq: int) -> int:
+        return lib.pa_bm_seq_len(self._h, seq)
+
+    def block_table(self, seq: int):
+        n = c_int()
+        cap = max(self.num_blocks, 1)
+        out = np.empty(cap, dtype=np.int32)
+        st = lib.pa_bm_block_table(self._h, seq, _ptr32(out), cap, ctypes.byref(n))
+        return st, out[: n.value].tolist() if st == PA_OK else []
+
+    def free_list(self):
+        n = c_int()
+        out = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        st = lib.pa_bm_free_list(self._h, _ptr32(out), out.shape[0], ctypes.byref(n))
+        _check(st, "pa_bm_free_list")
+        return out[: n.value].tolist()
+
+    def can_allocate(self, num_tokens: int) -> bool:
+        return bool(lib.pa_bm_can_allocate(self._h, num_tokens))
+
+    def stats(self):
+        s = BMStats()
+        _check(lib.pa_bm_stats(self._h, ctypes.byref(s)), "pa_bm_stats")
+        return s.as_dict()

@@ -1,0 +1,291 @@
+// Host block manager: free list, per-block reference counts, block tables,
+// fork, copy-on-write of a shared unaligned tail, release.
+//
+// Rules from "PagedAttention: Virtual Memory for the KV Cache": a sequence of
+// S tokens holds ceil(S / B) blocks (section 8); fork duplicates the table and
+// adds a reference per block (section 16); an append into a shared tail block
+// clones it first (sections 15-16); release returns blocks whose count reaches
+// zero to the free list (section 17); running out of blocks fails without
+// changing anything (section 20, test 4).  The free list is a LIFO stack (the
+// teaching allocator of section 20 pops from and pushes to the same end).
+//
+// Data structures are sized for large pools: a flat int32 refcount array, an
+// int32 stack for the free list, and per-sequence vectors in a hash map.  All
+// operations are O(1) amortised except fork/release (O(table length)) and
+// stats (O(total table entries)).
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pa.h"
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> table;
+  int64_t len = 0;
+};
+
+struct Undo {  // what one append did, so a failed batch can be rolled back
+  int64_t seq;
+  int32_t cow_src;  // -1 when no copy-on-write happened
+  int32_t cow_dst;
+};
+
+}  // namespace
+
+struct pa_bm {
+  int32_t num_blocks;
+  int32_t block_size;
+  std::vector<int32_t> free_stack;  // top = back()
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t cow_copies = 0;
+
+  int32_t pop() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    ref[b] = 1;
+    return b;
+  }
+
+  int append(int64_t id, int32_t* slot, int32_t* src, int32_t* dst) {
+    *slot = -1;
+    *src = -1;
+    *dst = -1;
+    auto it = seqs.find(id);
+    if (it == seqs.end()) return PA_ERR_NOT_FOUND;
+    Seq& s = it->second;
+    const int32_t off = static_cast<int32_t>(s.len % block_size);
+    int32_t block;
+    if (off != 0) {
+      const int32_t tail = s.table.back();
+      if (ref[tail] > 1) {  // shared unaligned tail: clone before writing
+        if (free_stack.empty()) return PA_ERR_NO_FREE_BLOCKS;
+        block = pop();
+        ref[tail] -= 1;
+        s.table.back() = block;
+        *src = tail;
+        *dst = block;
+        ++cow_copies;
+      } else {
+        block = tail;
+      }
+    } else {  // tail full (or no tail yet): take a fresh block
+      if (free_stack.empty()) return PA_ERR_NO_FREE_BLOCKS;
+      block = pop();
+      s.table.push_back(block);
+    }
+    s.len += 1;
+    *slot = block * block_size + off;
+    return PA_OK;
+  }
+
+  void undo(const Undo& u) {
+    Seq& s = seqs[u.seq];
+    s.len -= 1;
+    if (u.cow_src >= 0) {
+      ref[u.cow_dst] = 0;
+      free_stack.push_back(u.cow_dst);
+      ref[u.cow_src] += 1;
+      s.table.back() = u.cow_src;
+      --cow_copies;
+    } else if (s.len % block_size == 0) {
+      const int32_t b = s.table.back();
+      s.table.pop_back();
+      ref[b] = 0;
+      free_stack.push_back(b);
+    }
+  }
+};
+
+extern "C" {
+
+pa_bm* pa_bm_create(int num_blocks, int block_size, const int32_t* pop_order) {
+  if (num_blocks <= 0 || block_size <= 0) return nullptr;
+  pa_bm* bm = new (std::nothrow) pa_bm();
+  if (!bm) return nullptr;
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->ref.assign(num_blocks, 0);
+  bm->free_stack.resize(num_blocks);
+  if (pop_order) {
+    std::vector<uint8_t> seen(num_blocks, 0);
+    for (int i = 0; i < num_blocks; ++i) {
+      const int32_t b = pop_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        return nullptr;
+      }
+      seen[b] = 1;
+      bm->free_stack[num_blocks - 1 - i] = b;  // first entry ends on top
+    }
+  } else {
+    for (int i = 0; i < num_blocks; ++i) bm->free_stack[i] = num_blocks - 1 - i;
+  }
+  return bm;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+int pa_bm_add_seq(pa_bm* bm, int64_t seq, int num_tokens) {
+  if (!bm || num_tokens <= 0) return PA_ERR_INVALID_ARG;
+  if (bm->seqs.count(seq)) return PA_ERR_EXISTS;
+  const int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
+  if (static_cast<int64_t>(bm->free_stack.size()) < need) return PA_ERR_NO_FREE_BLOCKS;
+  Seq s;
+  s.table.reserve(need + 1);
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->pop());
+  s.len = num_tokens;
+  bm->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return PA_ERR_INVALID_ARG;
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  if (bm->seqs.count(child)) return PA_ERR_EXISTS;
+  Seq s = it->second;  // copy of the table; no data moves
+  for (int32_t b : s.table) bm->ref[b] += 1;
+  bm->seqs.emplace(child, std::move(s));
+  return PA_OK;
+}
+
+int pa_bm_append_slot(pa_bm* bm, int64_t seq, int32_t* slot, int32_t* cow_src, int32_t* cow_dst) {
+  if (!bm || !slot || !cow_src || !cow_dst) return PA_ERR_INVALID_ARG;
+  return bm->append(seq, slot, cow_src, cow_dst);
+}
+
+int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int n, int32_t* slots, int32_t* cow_pairs,
+                       int* num_pairs) {
+  if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_pairs)
+    return PA_ERR_INVALID_ARG;
+  std::vector<Undo> done;
+  done.reserve(n);
+  int pairs = 0;
+  for (int i = 0; i < n; ++i) {
+    int32_t slot, src, dst;
+    const int st = bm->append(seqs[i], &slot, &src, &dst);
+    if (st != PA_OK) {
+      for (auto u = done.rbegin(); u != done.rend(); ++u) bm->undo(*u);
+      *num_pairs = -i - 1;
+      return st;
+    }
+    done.push_back({seqs[i], src, dst});
+    slots[i] = slot;
+    if (src >= 0) {
+      cow_pairs[2 * pairs] = src;
+      cow_pairs[2 * pairs + 1] = dst;
+      ++pairs;
+    }
+  }
+  *num_pairs = pairs;
+  return PA_OK;
+}
+
+int pa_bm_free_seq(pa_bm* bm, int64_t seq) {
+  if (!bm) return PA_ERR_INVALID_ARG;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  for (int32_t b : it->second.table) {
+    if (--bm->ref[b] == 0) bm->free_stack.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+int pa_bm_build_batch(pa_bm* bm, const int64_t* seqs, int n, int max_blocks_per_seq,
+                      int32_t* block_tables_out, int32_t* context_lens_out) {
+  if (!bm || n < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+  if (n > 0 && (!seqs || !context_lens_out || (max_blocks_per_seq > 0 && !block_tables_out)))
+    return PA_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {  // validate everything before writing anything
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+    if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq) return PA_ERR_INVALID_ARG;
+    if (it->second.len > INT32_MAX) return PA_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n; ++i) {
+    const Seq& s = bm->seqs.find(seqs[i])->second;
+    int32_t* row = block_tables_out + static_cast<int64_t>(i) * max_blocks_per_seq;
+    const size_t nb = s.table.size();
+    if (nb) std::memcpy(row, s.table.data(), nb * sizeof(int32_t));
+    for (int64_t j = nb; j < max_blocks_per_seq; ++j) row[j] = 0;
+    context_lens_out[i] = static_cast<int32_t>(s.len);
+  }
+  return PA_OK;
+}
+
+int pa_bm_refcount(pa_bm* bm, int block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->ref[block];
+}
+
+int pa_bm_num_free(pa_bm* bm) { return bm ? static_cast<int>(bm->free_stack.size()) : -1; }
+
+int64_t pa_bm_seq_len(pa_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : it->second.len;
+}
+
+int pa_bm_block_table(pa_bm* bm, int64_t seq, int32_t* out, int cap, int* n_out) {
+  if (!bm || !n_out || cap < 0) return PA_ERR_INVALID_ARG;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  const auto& t = it->second.table;
+  *n_out = static_cast<int>(t.size());
+  if (static_cast<int64_t>(t.size()) > cap || (!out && !t.empty())) return PA_ERR_INVALID_ARG;
+  if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
+  return PA_OK;
+}
+
+int pa_bm_free_list(pa_bm* bm, int32_t* out, int cap, int* n_out) {
+  if (!bm || !n_out || cap < 0) return PA_ERR_INVALID_ARG;
+  const int64_t n = static_cast<int64_t>(bm->free_stack.size());
+  *n_out = static_cast<int>(n);
+  if (n > cap || (!out && n > 0)) return PA_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = bm->free_stack[n - 1 - i];
+  return PA_OK;
+}
+
+int pa_bm_can_allocate(pa_bm* bm, int num_tokens) {
+  if (!bm || num_tokens <= 0) return 0;
+  const int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
+  return static_cast<int64_t>(bm->free_stack.size()) >= need ? 1 : 0;
+}
+
+int pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
+  if (!bm || !out) return PA_ERR_INVALID_ARG;
+  // fill of a block = valid tokens it holds; sharers of a block agree on it,
+  // take the largest over the sequences that reference it
+  std::vector<int32_t> fill(bm->num_blocks, 0);
+  for (const auto& kv : bm->seqs) {
+    const Seq& s = kv.second;
+    for (size_t lb = 0; lb < s.table.size(); ++lb) {
+      const int64_t valid = s.len - static_cast<int64_t>(lb) * bm->block_size;
+      const int32_t v = static_cast<int32_t>(valid < bm->block_size ? valid : bm->block_size);
+      int32_t& f = fill[s.table[lb]];
+      if (v > f) f = v;
+    }
+  }
+  int64_t used = 0, stored = 0;
+  for (int32_t b = 0; b < bm->num_blocks; ++b) {
+    if (bm->ref[b] > 0) ++used;
+    stored += fill[b];
+  }
+  out->num_blocks = bm->num_blocks;
+  out->num_free = static_cast<int64_t>(bm->free_stack.size());
+  out->num_used = used;
+  out->num_seqs = static_cast<int64_t>(bm->seqs.size());
+  out->cow_copies = bm->cow_copies;
+  out->stored_tokens = stored;
+  out->tail_waste_slots = used * bm->block_size - stored;
+  return PA_OK;
+}
+
+}  // extern "C"

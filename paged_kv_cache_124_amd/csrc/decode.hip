@@ -1,0 +1,534 @@
+// Paged decode attention for gfx950 (MI355X) and its C entry point.
+//
+// What is computed ("PagedAttention: Virtual Memory for the KV Cache",
+// sections 1 and 13; "PagedAttention in vLLM: scattered memory, exact
+// attention", sections 10-11): for each sequence n and query head h, with KV
+// head j = h / G (G = Hq / Hkv), out = softmax(scale * q K^T) V over the S
+// cached tokens, K and V gathered block by block through the block table.
+//
+// Structure
+//   * The context of a sequence is cut into partitions of `part` tokens.  One
+//     workgroup handles one (partition, KV head, sequence) and all G query
+//     heads of that KV head, so every key/value byte is read once.
+//   * Inside a partition the running maximum, shifted weight sum and shifted
+//     value sum are updated tile by tile (the online form of section 13 of the
+//     first page).  Scores are kept in base 2 (s * log2 e).
+//   * If a sequence has one partition its workgroup writes the output
+//     directly; otherwise each partition stores its (m, z, u) summary in the
+//     workspace and `merge_partitions` combines them with the common-maximum
+//     rule of section 11 of the second page, in partition order.
+//
+// Two kernels compute a partition:
+//   decode_mfma   bf16, D in {64, 128}, G <= 16.  q.K^T and P.V run on the
+//                 matrix cores (v_mfma_f32_16x16x32_bf16): the G query heads
+//                 of a KV head form the N = 16 side (padded), 16 tokens of a
+//                 block the M side, d_head the contraction; P.V contracts over
+//                 32 tokens.  4 waves per workgroup split the partition's
+//                 32-token tiles; their summaries are merged through LDS.
+//   decode_generic fp32 or bf16, any G: one wave per (partition, query head,
+//                 sequence); per-token dot products with wave reductions.
+//
+// Pool layout (per layer), x = 16 / sizeof(elem):
+//   K [num_blocks][Hkv][D/x][B][x],  V [num_blocks][Hkv][D][B].
+
+#include <cstdlib>
+
+#include "common.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;       // waves per workgroup in decode_mfma
+constexpr int kTile = 32;       // tokens per wave iteration in decode_mfma
+constexpr int kGenericPart = 256;
+
+struct Plan {
+  bool mfma;
+  int part;   // tokens per partition
+  int p_max;  // partitions of the longest sequence
+};
+
+inline int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+bool mfma_eligible(int g, int d, int block_size, int dtype) {
+  return dtype == PA_BF16 && (d == 64 || d == 128) && g >= 1 && g <= 16 &&
+         (block_size == 8 || block_size == 16 || block_size == 32);
+}
+
+// Partition size: the largest of 512, 256, 128 tokens that still yields at
+// least ~2048 workgroups (8 per CU over 256 CUs) for the longest sequence,
+// capped so that a partition spans at most 64 blocks (one table entry per
+// lane).  PA_PART_TOKENS (a multiple of 128) overrides it for tuning sweeps.
+Plan make_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, int dtype) {
+  Plan p{};
+  const int g = hkv > 0 ? hq / hkv : 0;
+  p.mfma = mfma_eligible(g, d, block_size, dtype);
+  if (p.mfma) {
+    int part = 128;
+    const int cap = 64 * block_size;
+    for (int cand : {512, 256, 128}) {
+      if (cand > cap) continue;
+      const int64_t wgs = static_cast<int64_t>(num_seqs) * hkv * ceil_div(max_ctx > 0 ? max_ctx : 1, cand);
+      part = cand;
+      if (wgs >= 2048) break;
+    }
+    if (const char* env = std::getenv("PA_PART_TOKENS")) {
+      const int v = std::atoi(env);
+      if (v >= 128 && v % 128 == 0 && v <= cap) part = v;
+    }
+    p.part = part;
+  } else {
+    p.part = kGenericPart;
+  }
+  p.p_max = max_ctx > 0 ? ceil_div(max_ctx, p.part) : 1;
+  return p;
+}
+
+size_t plan_workspace_bytes(const Plan& p, int num_seqs, int hq, int d) {
+  if (p.p_max <= 1) return 0;
+  return static_cast<size_t>(num_seqs) * hq * p.p_max * (d + 2) * sizeof(float);
+}
+
+// ---------------------------------------------------------------------------
+// decode_mfma
+// ---------------------------------------------------------------------------
+//
+// Lane roles (lane = 16 * gq + r, gq in 0..3, r in 0..15), per 32-token tile
+// made of two 16-token slabs a = 0, 1:
+//   q.K^T  S^T[token][head] = K[token][:] . Q[head][:]
+//          A operand (16 x 32): lane holds key row r of the slab, d-chunk
+//          c = 4 jj + gq (8 elements, one 16-byte load from the K layout);
+//          B operand (32 x 16): Q[head r][chunk c], zero for r >= G;
+//          result: lane holds S^T[tokens 4 gq .. 4 gq + 3][head r].
+//   P.V    O^T[d][head] += V^T[d][tokens] . P^T[tokens][head]
+//          A operand: V^T[d = 16 mm + r][8 tokens] = 4 tokens of slab 0 and 4
+//          of slab 1 at rows 4 gq .. 4 gq + 3 (two 8-byte loads);
+//          B operand: P^T for those 8 tokens and head r -- exactly the 8
+//          scores this lane already holds, so P needs no data movement;
+//          result: lane holds O^T[d = 16 mm + 4 gq + i][head r].
+// P is split into a bf16 high part and a bf16 residual so that P.V keeps
+// about 16 mantissa bits of each weight.
+template <int D, int B>
+__global__ __launch_bounds__(256) void decode_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
+    float* __restrict__ ws, int hq, int hkv, int g, int max_blocks, int num_blocks, int part, int p_max,
+    float scale_log2) {
+  constexpr int X = 8;            // bf16 elements per 16 bytes
+  constexpr int KCH = D / 32;     // MFMA steps over d in q.K^T
+  constexpr int VT = D / 16;      // output tiles over d in P.V
+  constexpr int64_t BLK = static_cast<int64_t>(D) * B;  // elements per (block, KV head)
+
+  extern __shared__ float lds[];  // [kWaves][g][D] values, then [kWaves][16] m, [kWaves][16] z
+
+  const int part_id = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int S = context_lens[seq];
+  const int tok0 = part_id * part;
+  // a length beyond the launch bound (caller error) is cut at p_max partitions
+  const int n_parts = S > 0 ? min((S + part - 1) / part, p_max) : 0;
+
+  if (tok0 >= S) {
+    if (S <= 0 && part_id == 0) {  // empty context: defined as zeros
+      for (int e = threadIdx.x; e < g * D; e += blockDim.x)
+        out[(static_cast<int64_t>(seq) * hq + kvh * g) * D + e] = 0;
+    }
+    return;
+  }
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+
+  // block ids of this partition: lane i holds entry (first block + i)
+  const int lb0 = tok0 / B;
+  const int nb_part = min(min(part / B, (S + B - 1) / B - lb0), max_blocks - lb0);
+  int tbl = 0;
+  if (lane < nb_part) tbl = block_tables[static_cast<int64_t>(seq) * max_blocks + lb0 + lane];
+
+  // Q operand: head r of this KV head's group, chunks c = 4 jj + gq
+  bf16x8 qop[KCH];
+  {
+    const uint16_t* qh = q + (static_cast<int64_t>(seq) * hq + kvh * g + r) * D;
+#pragma unroll
+    for (int jj = 0; jj < KCH; ++jj) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < g) v = *reinterpret_cast<const uint4*>(qh + (4 * jj + gq) * X);
+      qop[jj] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x4 acc[VT];
+#pragma unroll
+  for (int mm = 0; mm < VT; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float z_run = 0.f;
+
+  const int tiles = min(part, S - tok0 + kTile - 1) / kTile;  // tiles holding >= 1 valid token
+  const uint16_t* kh = k_pool + static_cast<int64_t>(kvh) * BLK;
+  const uint16_t* vh = v_pool + static_cast<int64_t>(kvh) * BLK;
+  const int64_t blk_stride = static_cast<int64_t>(hkv) * BLK;
+
+  for (int tile = wave; tile < tiles; tile += kWaves) {
+    const int t0 = tok0 + tile * kTile;
+
+    // ---- loads -------------------------------------------------------------
+    bf16x8 kop[2][KCH];
+    bf16x8 vop[VT];
+    uint2 vlo[VT], vhi[VT];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      // key row r of slab a
+      const int tk = t0 + 16 * a + r;
+      const int pbk = __shfl(tbl, (tk / B) - lb0);
+      const bool kval = tk < S && pbk >= 0 && pbk < num_blocks;
+      const uint16_t* kb = kh + static_cast<int64_t>(pbk) * blk_stride + (tk % B) * X;
+#pragma unroll
+      for (int jj = 0; jj < KCH; ++jj) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (kval) v = *reinterpret_cast<const uint4*>(kb + (4 * jj + gq) * (B * X));
+        kop[a][jj] = __builtin_bit_cast(bf16x8, v);
+      }
+      // value rows: tokens 4 gq .. 4 gq + 3 of slab a
+      const int tv = t0 + 16 * a + 4 * gq;
+      const int pbv = __shfl(tbl, (tv / B) - lb0);
+      const bool vval = tv < S && pbv >= 0 && pbv < num_blocks;
+      const uint16_t* vb = vh + static_cast<int64_t>(pbv) * blk_stride + (tv % B);
+#pragma unroll
+      for (int mm = 0; mm < VT; ++mm) {
+        uint2 v = make_uint2(0, 0);
+        if (vval) v = *reinterpret_cast<const uint2*>(vb + (16 * mm + r) * B);
+        if (a == 0) vlo[mm] = v; else vhi[mm] = v;
+      }
+    }
+    // zero the value elements of tokens past the end (a stale or NaN slot
+    // must not reach P.V: 0 * NaN is NaN)
+    {
+      const int tv0 = t0 + 4 * gq;
+      const int tv1 = t0 + 16 + 4 * gq;
+      const int n0 = min(max(S - tv0, 0), 4);
+      const int n1 = min(max(S - tv1, 0), 4);
+      const uint32_t m0a = n0 >= 2 ? 0xffffffffu : (n0 == 1 ? 0x0000ffffu : 0u);
+      const uint32_t m0b = n0 >= 4 ? 0xffffffffu : (n0 == 3 ? 0x0000ffffu : 0u);
+      const uint32_t m1a = n1 >= 2 ? 0xffffffffu : (n1 == 1 ? 0x0000ffffu : 0u);
+      const uint32_t m1b = n1 >= 4 ? 0xffffffffu : (n1 == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+      for (int mm = 0; mm < VT; ++mm) {
+        uint4 w = make_uint4(vlo[mm].x & m0a, vlo[mm].y & m0b, vhi[mm].x & m1a, vhi[mm].y & m1b);
+        vop[mm] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+
+    // ---- scores: S^T = K . Q^T --------------------------------------------
+    f32x4 s[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < KCH; ++jj)
+        s[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[a][jj], qop[jj], s[a], 0, 0, 0);
+    }
+
+    // ---- online softmax (base 2) -------------------------------------------
+    float x[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * a + 4 * gq + i;
+        x[a][i] = tok < S ? s[a][i] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[a][i]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[a][i] - m_new);
+        psum += p;
+        const __bf16 h = static_cast<__bf16>(p);
+        phi[4 * a + i] = h;
+        plo[4 * a + i] = static_cast<__bf16>(p - static_cast<float>(h));
+      }
+    z_run = z_run * alpha + psum;
+
+    // ---- O^T += V^T . P^T ------------------------------------------------------
+#pragma unroll
+    for (int mm = 0; mm < VT; ++mm) {
+      acc[mm] *= alpha;
+      acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[mm], phi, acc[mm], 0, 0, 0);
+      acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[mm], plo, acc[mm], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the 4 waves through LDS -----------------------------------------
+  z_run += __shfl_xor(z_run, 16);
+  z_run += __shfl_xor(z_run, 32);
+  float* lds_u = lds;                         // [kWaves][g][D]
+  float* lds_m = lds + kWaves * g * D;        // [kWaves][16]
+  float* lds_z = lds_m + kWaves * 16;         // [kWaves][16]
+  if (r < g) {
+#pragma unroll
+    for (int mm = 0; mm < VT; ++mm)
+      *reinterpret_cast<f32x4*>(lds_u + (wave * g + r) * D + 16 * mm + 4 * gq) = acc[mm];
+    if (gq == 0) {
+      lds_m[wave * 16 + r] = m_run;
+      lds_z[wave * 16 + r] = z_run;
+    }
+  }
+  __syncthreads();
+
+  const int64_t head0 = static_cast<int64_t>(seq) * hq + kvh * g;
+  for (int e = threadIdx.x; e < g * D; e += blockDim.x) {
+    const int h = e / D;
+    const int dd = e - h * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, lds_m[w * 16 + h]);
+    float zz = 0.f, uu = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(lds_m[w * 16 + h] - mx);  // exp2(-inf) = 0 for idle waves
+      zz += f * lds_z[w * 16 + h];
+      uu += f * lds_u[(w * g + h) * D + dd];
+    }
+    if (n_parts == 1) {
+      out[(head0 + h) * D + dd] = f32_to_bf16_bits(uu / zz);
+    } else {
+      const int64_t row = (head0 + h) * p_max + part_id;
+      const int64_t n_rows = static_cast<int64_t>(gridDim.z) * hq * p_max;
+      ws[2 * n_rows + row * D + dd] = uu;
+      if (dd == 0) {
+        ws[row] = mx;
+        ws[n_rows + row] = zz;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode_generic: one wave per (partition, query head, sequence)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_generic(
+    const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, T* __restrict__ out,
+    float* __restrict__ ws, int hq, int hkv, int block_size, int max_blocks, int num_blocks, int part, int p_max,
+    float scale_log2) {
+  constexpr int X = 16 / static_cast<int>(sizeof(T));
+  constexpr int E = D / 64;  // elements per lane
+  const int part_id = blockIdx.x;
+  const int h = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int g = hq / hkv;
+  const int kvh = h / g;
+  const int S = context_lens[seq];
+  const int tok0 = part_id * part;
+  const int lane = threadIdx.x;
+  const int64_t orow = (static_cast<int64_t>(seq) * hq + h) * D;
+  if (tok0 >= S) {
+    if (S <= 0 && part_id == 0)
+      for (int e = 0; e < E; ++e) Elem<T>::store(out + orow + lane + 64 * e, 0.f);
+    return;
+  }
+  const int tok1 = min(S, tok0 + part);
+  const int n_parts = min((S + part - 1) / part, p_max);
+
+  float qv[E], u[E];
+  for (int e = 0; e < E; ++e) {
+    qv[e] = Elem<T>::load(q + orow + lane + 64 * e);
+    u[e] = 0.f;
+  }
+  float m_run = -INFINITY, z_run = 0.f;
+  const int64_t blk_stride = static_cast<int64_t>(hkv) * D * block_size;
+  for (int t = tok0; t < tok1; ++t) {
+    const int lb = t / block_size;
+    const int pb = lb < max_blocks ? block_tables[static_cast<int64_t>(seq) * max_blocks + lb] : -1;
+    const int off = t % block_size;
+    const bool ok = pb >= 0 && pb < num_blocks;
+    const T* kb = k_pool + static_cast<int64_t>(pb) * blk_stride + static_cast<int64_t>(kvh) * D * block_size;
+    const T* vb = v_pool + static_cast<int64_t>(pb) * blk_stride + static_cast<int64_t>(kvh) * D * block_size;
+    float dot = 0.f;
+    float vv[E];
+    for (int e = 0; e < E; ++e) {
+      const int d = lane + 64 * e;
+      const float kx = ok ? Elem<T>::load(kb + ((d / X) * block_size + off) * X + d % X) : 0.f;
+      vv[e] = ok ? Elem<T>::load(vb + d * block_size + off) : 0.f;
+      dot += qv[e] * kx;
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
+    const float s2 = dot * scale_log2;
+    const float m_new = fmaxf(m_run, s2);
+    const float alpha = exp2f(m_run - m_new);
+    const float p = exp2f(s2 - m_new);
+    z_run = z_run * alpha + p;
+    for (int e = 0; e < E; ++e) u[e] = u[e] * alpha + p * vv[e];
+    m_run = m_new;
+  }
+  if (n_parts == 1) {
+    for (int e = 0; e < E; ++e) Elem<T>::store(out + orow + lane + 64 * e, u[e] / z_run);
+  } else {
+    const int64_t row = (static_cast<int64_t>(seq) * hq + h) * p_max + part_id;
+    const int64_t n_rows = static_cast<int64_t>(gridDim.z) * hq * p_max;
+    for (int e = 0; e < E; ++e) ws[2 * n_rows + row * D + lane + 64 * e] = u[e];
+    if (lane == 0) {
+      ws[row] = m_run;
+      ws[n_rows + row] = z_run;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge_partitions: common-maximum merge of the partition summaries,
+// partitions combined in index order.  One workgroup of D threads per
+// (query head, sequence); sequences with a single partition were finished by
+// the decode kernel.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(D) void merge_partitions(const float* __restrict__ ws,
+                                                      const int32_t* __restrict__ context_lens, T* __restrict__ out,
+                                                      int num_seqs, int hq, int part, int p_max) {
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int S = context_lens[seq];
+  const int n_parts = S > 0 ? min((S + part - 1) / part, p_max) : 0;
+  if (n_parts <= 1) return;
+  const int64_t n_rows = static_cast<int64_t>(num_seqs) * hq * p_max;
+  const int64_t row0 = (static_cast<int64_t>(seq) * hq + h) * p_max;
+  const int dd = threadIdx.x;
+  float mx = -INFINITY;
+  for (int p = 0; p < n_parts; ++p) mx = fmaxf(mx, ws[row0 + p]);
+  float zz = 0.f, uu = 0.f;
+  for (int p = 0; p < n_parts; ++p) {
+    const float f = __builtin_amdgcn_exp2f(ws[row0 + p] - mx);
+    zz += f * ws[n_rows + row0 + p];
+    uu += f * ws[2 * n_rows + (row0 + p) * D + dd];
+  }
+  Elem<T>::store(out + (static_cast<int64_t>(seq) * hq + h) * D + dd, uu / zz);
+}
+
+template <int D, int B>
+void launch_mfma(const Plan& pl, dim3 grid, size_t lds, hipStream_t s, const void* q, const void* k, const void* v,
+                 const int32_t* bt, const int32_t* cl, void* out, float* ws, int hq, int hkv, int g, int max_blocks,
+                 int num_blocks, float scale_log2) {
+  decode_mfma<D, B><<<grid, dim3(256), lds, s>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bt, cl,
+      static_cast<uint16_t*>(out), ws, hq, hkv, g, max_blocks, num_blocks, pl.part, pl.p_max, scale_log2);
+}
+
+template <int D>
+void launch_mfma_b(int block_size, const Plan& pl, dim3 grid, size_t lds, hipStream_t s, const void* q,
+                   const void* k, const void* v, const int32_t* bt, const int32_t* cl, void* out, float* ws, int hq,
+                   int hkv, int g, int max_blocks, int num_blocks, float scale_log2) {
+  switch (block_size) {
+    case 8: launch_mfma<D, 8>(pl, grid, lds, s, q, k, v, bt, cl, out, ws, hq, hkv, g, max_blocks, num_blocks, scale_log2); break;
+    case 16: launch_mfma<D, 16>(pl, grid, lds, s, q, k, v, bt, cl, out, ws, hq, hkv, g, max_blocks, num_blocks, scale_log2); break;
+    default: launch_mfma<D, 32>(pl, grid, lds, s, q, k, v, bt, cl, out, ws, hq, hkv, g, max_blocks, num_blocks, scale_log2); break;
+  }
+}
+
+template <typename T, int D>
+void launch_generic(const Plan& pl, dim3 grid, hipStream_t s, const void* q, const void* k, const void* v,
+                    const int32_t* bt, const int32_t* cl, void* out, float* ws, int hq, int hkv, int block_size,
+                    int max_blocks, int num_blocks, float scale_log2) {
+  decode_generic<T, D><<<grid, dim3(64), 0, s>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+                                                 static_cast<const T*>(v), bt, cl, static_cast<T*>(out), ws, hq, hkv,
+                                                 block_size, max_blocks, num_blocks, pl.part, pl.p_max, scale_log2);
+}
+
+template <typename T, int D>
+void launch_merge(const Plan& pl, hipStream_t s, const float* ws, const int32_t* cl, void* out, int num_seqs, int hq) {
+  merge_partitions<T, D><<<dim3(hq, num_seqs), dim3(D), 0, s>>>(ws, cl, static_cast<T*>(out), num_seqs, hq, pl.part,
+                                                                pl.p_max);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                                            int max_context_len, int dtype) {
+  if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_context_len < 0) return 0;
+  const pa::Plan p = pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
+  return pa::plan_workspace_bytes(p, num_seqs, Hq, d_head);
+}
+
+extern "C" int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                                          int max_context_len, int dtype) {
+  if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0) return 0;
+  return pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype).part;
+}
+
+extern "C" int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq, int Hkv,
+                         int d_head, int block_size, float scale, int max_blocks_per_seq, int max_context_len,
+                         int num_blocks, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace pa;
+  if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+      max_context_len < 0 || num_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size < max_context_len) return PA_ERR_INVALID_ARG;
+  if (!(d_head == 64 || d_head == 128) || !(block_size == 8 || block_size == 16 || block_size == 32) ||
+      Hq / Hkv > 64)
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || Hq > 65535) return PA_ERR_UNSUPPORTED;
+
+  const Plan pl = make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
+  const size_t need = plan_workspace_bytes(pl, num_seqs, Hq, d_head);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  float* ws = static_cast<float*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale_log2 = scale * kLog2e;
+  const int g = Hq / Hkv;
+
+  if (pl.mfma) {
+    const dim3 grid(pl.p_max, Hkv, num_seqs);
+    const size_t lds = (static_cast<size_t>(kWaves) * g * d_head + 2 * kWaves * 16) * sizeof(float);
+    if (d_head == 128)
+      launch_mfma_b<128>(block_size, pl, grid, lds, s, q, k_pool, v_pool, block_tables, context_lens, out, ws, Hq,
+                         Hkv, g, max_blocks_per_seq, num_blocks, scale_log2);
+    else
+      launch_mfma_b<64>(block_size, pl, grid, lds, s, q, k_pool, v_pool, block_tables, context_lens, out, ws, Hq,
+                        Hkv, g, max_blocks_per_seq, num_blocks, scale_log2);
+  } else {
+    const dim3 grid(pl.p_max, Hq, num_seqs);
+    if (dtype == PA_BF16) {
+      if (d_head == 128)
+        launch_generic<uint16_t, 128>(pl, grid, s, q, k_pool, v_pool, block_tables, context_lens, out, ws, Hq, Hkv,
+                                      block_size, max_blocks_per_seq, num_blocks, scale_log2);
+      else
+        launch_generic<uint16_t, 64>(pl, grid, s, q, k_pool, v_pool, block_tables, context_lens, out, ws, Hq, Hkv,
+                                     block_size, max_blocks_per_seq, num_blocks, scale_log2);
+    } else {
+      if (d_head == 128)
+        launch_generic<float, 128>(pl, grid, s, q, k_pool, v_pool, block_tables, context_lens, out, ws, Hq, Hkv,
+                                   block_size, max_blocks_per_seq, num_blocks, scale_log2);
+      else
+        launch_generic<float, 64>(pl, grid, s, q, k_pool, v_pool, block_tables, context_lens, out, ws, Hq, Hkv,
+                                  block_size, max_blocks_per_seq, num_blocks, scale_log2);
+    }
+  }
+  int st = launch_status();
+  if (st != PA_OK || pl.p_max <= 1) return st;
+  if (dtype == PA_BF16) {
+    if (d_head == 128) launch_merge<uint16_t, 128>(pl, s, ws, context_lens, out, num_seqs, Hq);
+    else launch_merge<uint16_t, 64>(pl, s, ws, context_lens, out, num_seqs, Hq);
+  } else {
+    if (d_head == 128) launch_merge<float, 128>(pl, s, ws, context_lens, out, num_seqs, Hq);
+    else launch_merge<float, 64>(pl, s, ws, context_lens, out, num_seqs, Hq);
+  }
+  return launch_status();
+}

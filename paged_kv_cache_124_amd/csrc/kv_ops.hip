@@ -1,0 +1,127 @@
+// KV append and copy-on-write block copy kernels (gfx950) and their C entry points.
+//
+// Append: "PagedAttention: Virtual Memory for the KV Cache", section 16 -- the
+// new position's key and value are written into its block at its offset.
+// Copy: same page, sections 15-16 -- a shared tail block is cloned before a
+// sequence writes into it.  Both are pure data movement and bit-exact.
+//
+// Pool layout (per layer), x = 16 / sizeof(elem):
+//   K [num_blocks][Hkv][D/x][B][x],  V [num_blocks][Hkv][D][B].
+
+#include "common.h"
+
+namespace pa {
+namespace {
+
+// One thread per (token, KV head, 16-byte key chunk).  The key chunk is one
+// 16-byte store; the matching x value elements go to x different rows of the
+// value block (stride B elements).
+template <typename T>
+__global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ k_pool, T* __restrict__ v_pool,
+                                                        const T* __restrict__ k_new,
+                                                        const T* __restrict__ v_new,
+                                                        const int32_t* __restrict__ slot_mapping,
+                                                        int num_tokens, int hkv, int d, int block_size,
+                                                        int64_t num_slots) {
+  constexpr int X = 16 / static_cast<int>(sizeof(T));
+  const int chunks = d / X;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;
+  const int j = static_cast<int>(th % hkv);
+  const int64_t t = th / hkv;
+  if (t >= num_tokens) return;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t pb = slot / block_size;
+  const int off = static_cast<int>(slot % block_size);
+
+  const int64_t src = (t * hkv + j) * d + static_cast<int64_t>(c) * X;
+  const int64_t head = pb * hkv + j;  // (block, KV head) index
+  // key: one 16-byte chunk
+  const uint4 kc = *reinterpret_cast<const uint4*>(k_new + src);
+  *reinterpret_cast<uint4*>(k_pool + ((head * chunks + c) * block_size + off) * X) = kc;
+  // value: X elements, one per row d of the transposed block
+  const uint4 vc = *reinterpret_cast<const uint4*>(v_new + src);
+  T vals[X];
+  __builtin_memcpy(vals, &vc, 16);
+  T* vdst = v_pool + (head * d + static_cast<int64_t>(c) * X) * block_size + off;
+#pragma unroll
+  for (int e = 0; e < X; ++e) vdst[static_cast<int64_t>(e) * block_size] = vals[e];
+}
+
+// grid = (ceil(2 * n16 / 256), num_pairs, num_layers); each thread moves 16 bytes.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                          const int32_t* __restrict__ pairs, int64_t block_bytes,
+                                                          int num_blocks, int64_t layer_stride_bytes) {
+  const int64_t n16 = block_bytes / 16;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= 2 * n16) return;
+  const int32_t src = pairs[2 * blockIdx.y];
+  const int32_t dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint8_t* base = (idx < n16 ? k_pool : v_pool) + static_cast<int64_t>(blockIdx.z) * layer_stride_bytes;
+  const int64_t i = idx < n16 ? idx : idx - n16;
+  const uint4* s = reinterpret_cast<const uint4*>(base + src * block_bytes) + i;
+  uint4* t = reinterpret_cast<uint4*>(base + dst * block_bytes) + i;
+  *t = *s;
+}
+
+bool shape_ok(int hkv, int d, int block_size, int dtype) {
+  return hkv > 0 && (d == 64 || d == 128) && (block_size == 8 || block_size == 16 || block_size == 32) &&
+         (dtype == PA_F32 || dtype == PA_BF16);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_append_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                            const int32_t* slot_mapping, int num_tokens, int Hkv, int d_head,
+                            int block_size, int num_blocks, int dtype, void* stream) {
+  using namespace pa;
+  if (num_tokens < 0 || num_blocks < 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (!shape_ok(Hkv, d_head, block_size, dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  const int x = 16 / elem_bytes(dtype);
+  const int64_t threads = static_cast<int64_t>(num_tokens) * Hkv * (d_head / x);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PA_BF16) {
+    append_kv_kernel<uint16_t><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s>>>(
+        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), static_cast<const uint16_t*>(k_new),
+        static_cast<const uint16_t*>(v_new), slot_mapping, num_tokens, Hkv, d_head, block_size, num_slots);
+  } else {
+    append_kv_kernel<float><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s>>>(
+        static_cast<float*>(k_pool), static_cast<float*>(v_pool), static_cast<const float*>(k_new),
+        static_cast<const float*>(v_new), slot_mapping, num_tokens, Hkv, d_head, block_size, num_slots);
+  }
+  return launch_status();
+}
+
+extern "C" int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int num_pairs,
+                              int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
+                              int64_t layer_stride_elems, int dtype, void* stream) {
+  using namespace pa;
+  if (num_pairs < 0 || num_blocks < 0 || num_layers <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (!shape_ok(Hkv, d_head, block_size, dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src_dst_pairs) return PA_ERR_INVALID_ARG;
+  if (num_pairs > 65535 || num_layers > 65535) return PA_ERR_UNSUPPORTED;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * d_head * block_size * eb;
+  if (num_layers > 1 && layer_stride_elems < static_cast<int64_t>(num_blocks) * Hkv * d_head * block_size)
+    return PA_ERR_INVALID_ARG;
+  const int64_t layer_stride_bytes = num_layers > 1 ? layer_stride_elems * eb : 0;
+  const int64_t gx = (2 * (block_bytes / 16) + 255) / 256;
+  copy_blocks_kernel<<<dim3(static_cast<uint32_t>(gx), num_pairs, num_layers), dim3(256), 0,
+                       static_cast<hipStream_t>(stream)>>>(static_cast<uint8_t*>(k_pool),
+                                                          static_cast<uint8_t*>(v_pool), src_dst_pairs,
+                                                          block_bytes, num_blocks, layer_stride_bytes);
+  return launch_status();
+}

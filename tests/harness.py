@@ -1,0 +1,165 @@
+"""Builds seeded decode workloads for the GPU parity tests and ``smoke()``.
+
+Both sides get the same inputs from ``synth``: the product side allocates with
+the C++ block manager of libpa.so and runs the HIP kernels through the C ABI;
+the oracle side allocates with ``oracle.block_manager`` and evaluates
+``oracle.attention`` in fp64 on the CPU.  Block tables from the two managers
+must agree exactly before any attention is compared.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import synth
+from oracle import attention as OA
+from oracle.block_manager import BlockManagerModel
+from pool_layout import k_to_logical, poison_unused_
+
+# Acceptance bar for attention against the fp64 oracle (bf16 inputs, fp32 accumulation).
+MAX_ABS = 1e-2
+REL_L2 = 5e-3
+
+
+@dataclass
+class DecodeCase:
+    w: synth.Workload
+    lens: List[int]
+    hq: int
+    hkv: int
+    d: int
+    block_size: int
+    dtype: torch.dtype
+    num_blocks: int
+    max_blocks: int
+    bm: object                  # product block manager
+    model: BlockManagerModel    # oracle block manager
+    tables: np.ndarray          # int32 [N][max_blocks] from the product manager
+    k: torch.Tensor             # device, [L][nb][Hkv][D/x][B][x] or [nb]...
+    v: torch.Tensor
+    q: torch.Tensor             # device [N][Hq][D]
+    tables_dev: torch.Tensor
+    lens_dev: torch.Tensor
+    scale: float
+
+    @property
+    def max_ctx(self):
+        return max(self.lens) if self.lens else 0
+
+
+def make_case(w: synth.Workload, lens: Optional[Sequence[int]] = None, *, hq=None, hkv=None, d=None,
+              block_size=None, dtype=None, num_blocks=None, max_blocks=None, layers=1, poison=True,
+              device="cuda", seed=None) -> DecodeCase:
+    import paged_kv_cache_124_amd as pa
+
+    hq = hq or w.hq
+    hkv = hkv or w.hkv
+    d = d or w.d
+    bs = block_size or w.block_size
+    dtype = dtype or synth.torch_dtype(w)
+    seed = w.seed if seed is None else seed
+    lens = list(synth.seq_lengths(w) if lens is None else lens)
+    if num_blocks is None:
+        num_blocks = synth.pool_blocks(dataclasses.replace(w, block_size=bs), lens)
+    order = synth.pop_order(num_blocks, seed)
+    bm = pa.BlockManager(num_blocks, bs, order)
+    model = BlockManagerModel(num_blocks, bs, order)
+    ids = [n for n, s in enumerate(lens) if s > 0]
+    for n in ids:
+        assert bm.add_seq(n, lens[n]) == 0
+        assert model.add_seq(n, lens[n]) == 0
+    need = max([-(-s // bs) for s in lens] + [1])
+    max_blocks = max_blocks or need
+    st, t_ids, _ = bm.build_batch(ids, max_blocks)
+    mst, m_ids, _ = model.build_batch(ids, max_blocks)
+    assert st == 0 and mst == 0
+    assert t_ids.tolist() == m_ids, "product and oracle block tables differ"
+    tables = np.zeros((len(lens), max_blocks), dtype=np.int32)
+    tables[ids] = t_ids
+
+    elem = torch.tensor([], dtype=dtype).element_size()
+    kshape, vshape = pa.pool_shapes(num_blocks, hkv, d, bs, elem)
+    if layers > 1:
+        kshape, vshape = (layers,) + kshape, (layers,) + vshape
+    k = torch.empty(kshape, dtype=dtype, device=device)
+    v = torch.empty(vshape, dtype=dtype, device=device)
+    synth.fill_randn_(k, w.value_scale, seed * 10 + 1)
+    synth.fill_randn_(v, w.value_scale, seed * 10 + 2)
+    if poison:
+        for layer in range(layers):
+            kl, vl = (k[layer], v[layer]) if layers > 1 else (k, v)
+            poison_unused_(kl, vl, tables, lens, bs)
+    q = synth.randn((len(lens), hq, d), dtype, w.value_scale, seed * 10 + 3, device)
+    return DecodeCase(w, lens, hq, hkv, d, bs, dtype, num_blocks, max_blocks, bm, model, tables, k, v, q,
+                      torch.from_numpy(tables).to(device), torch.tensor(lens, dtype=torch.int32, device=device),
+                      1.0 / math.sqrt(d))
+
+
+def run_decode(case: DecodeCase, layer: Optional[int] = None, q=None, out=None, lens_dev=None, tables_dev=None,
+               max_ctx=None):
+    import paged_kv_cache_124_amd as pa
+    k = case.k if layer is None else case.k[layer]
+    v = case.v if layer is None else case.v[layer]
+    q = case.q if q is None else q
+    out = torch.empty_like(q) if out is None else out
+    pa.pa_decode(out, q, k, v, case.tables_dev if tables_dev is None else tables_dev,
+                 case.lens_dev if lens_dev is None else lens_dev, case.scale,
+                 case.max_ctx if max_ctx is None else max_ctx)
+    return out
+
+
+def logical_blocks(pool: torch.Tensor, blocks: Sequence[int], is_key: bool) -> np.ndarray:
+    """Read some physical blocks back and return them in the oracle's logical layout, fp32 (exact for bf16)."""
+    idx = torch.as_tensor(list(blocks), dtype=torch.long, device=pool.device)
+    sel = pool.index_select(0, idx).cpu()
+    sel = k_to_logical(sel) if is_key else sel.permute(0, 1, 3, 2)
+    return sel.float().numpy()
+
+
+def oracle_outputs(case: DecodeCase, seqs: Sequence[int], layer: Optional[int] = None, q=None, lens=None,
+                   tables=None) -> np.ndarray:
+    """fp64 oracle outputs [len(seqs)][Hq][D] for the listed sequences.
+
+    Each sequence's blocks are read back and handed to the oracle with the
+    oracle manager's block table remapped onto the compact copy.
+    """
+    k = case.k if layer is None else case.k[layer]
+    v = case.v if layer is None else case.v[layer]
+    q = (case.q if q is None else q).float().cpu().numpy().astype(np.float64)
+    lens = case.lens if lens is None else lens
+    outs = []
+    for n in seqs:
+        s = int(lens[n])
+        nb = -(-s // case.block_size)
+        if tables is None:
+            row = list(case.model.tables.get(n, []))[:nb]
+        else:
+            row = list(tables[n][:nb])
+        kl = logical_blocks(k, row, True) if nb else np.zeros((0, case.hkv, case.block_size, case.d), np.float32)
+        vl = logical_blocks(v, row, False) if nb else np.zeros((0, case.hkv, case.block_size, case.d), np.float32)
+        tab = np.arange(max(nb, 1)).reshape(1, -1)
+        outs.append(OA.paged_decode(q[n:n + 1], kl, vl, tab, [s], case.scale)[0])
+    return np.stack(outs)
+
+
+def errors(got: torch.Tensor, ref: np.ndarray):
+    g = got.float().cpu().numpy().astype(np.float64)
+    diff = g - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    denom = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff) / denom) if denom > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, what: str, max_abs=MAX_ABS, rel_l2=REL_L2):
+    assert np.all(np.isfinite(got.float().cpu().numpy())), f"{what}: non-finite output"
+    ma, rl = errors(got, ref)
+    print(f"[parity] {what}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+    assert ma <= max_abs and rl <= rel_l2, f"{what}: max_abs {ma:.3e} rel_l2 {rl:.3e}"
+    return ma, rl

@@ -1,0 +1,125 @@
+"""GPU: pa_decode against the fp64 oracle on the five workloads and the edge cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import assert_close, make_case, oracle_outputs, run_decode
+from oracle import attention as OA
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_decode_append_decode():
+    """fp32, lengths {17, 33, 64, 100}: decode, append one token per sequence (64 -> 65 opens a block), decode.
+
+    The oracle side keeps its own pool: a snapshot taken before the device
+    append, updated with the oracle's append rule at the oracle manager's
+    slots, decoded through the oracle manager's tables.
+    """
+    import paged_kv_cache_124_amd as pa
+    from pool_layout import k_to_logical, v_to_logical
+    w = synth.tiny()
+    print("[case] tiny", flush=True)
+    c = make_case(w)
+    out = run_decode(c)
+    ref = oracle_outputs(c, range(4))
+    assert_close(out, ref, "tiny step 1", max_abs=1e-4, rel_l2=1e-5)
+
+    k_or = k_to_logical(c.k.cpu()).double().numpy().copy()
+    v_or = v_to_logical(c.v.cpu()).double().numpy().copy()
+    st, slots, pairs, _ = c.bm.append_slots(list(range(4)))
+    mst, mslots, mpairs, _ = c.model.append_slots(list(range(4)))
+    assert st == mst == 0 and list(slots) == mslots and len(pairs) == len(mpairs) == 0
+    kn = synth.randn((4, w.hkv, w.d), torch.float32, 1.0, 77, "cuda")
+    vn = synth.randn((4, w.hkv, w.d), torch.float32, 1.0, 78, "cuda")
+    pa.pa_append_kv(c.k, c.v, kn, vn, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    OA.append_kv(k_or, v_or, kn.cpu().double().numpy(), vn.cpu().double().numpy(), mslots)
+    # device pool after the append equals the oracle's pool, NaN slots included
+    assert np.array_equal(k_to_logical(c.k.cpu()).double().numpy(), k_or, equal_nan=True)
+    assert np.array_equal(v_to_logical(c.v.cpu()).double().numpy(), v_or, equal_nan=True)
+
+    lens2 = [s + 1 for s in c.lens]
+    st, tables2, l2 = c.bm.build_batch(list(range(4)), c.max_blocks + 1)
+    mst, mt2, ml2 = c.model.build_batch(list(range(4)), c.max_blocks + 1)
+    assert st == mst == 0 and tables2.tolist() == mt2 and l2.tolist() == ml2 == lens2
+    out2 = run_decode(c, lens_dev=torch.tensor(lens2, dtype=torch.int32, device="cuda"),
+                      tables_dev=torch.from_numpy(tables2).cuda(), max_ctx=max(lens2))
+    ref2 = OA.paged_decode(c.q.cpu().double().numpy(), k_or, v_or, np.array(mt2), ml2, c.scale)
+    assert_close(out2, ref2, "tiny step 2", max_abs=1e-4, rel_l2=1e-5)
+
+
+def test_gqa8b_all_sequences():
+    """8B-style GQA layer, 64 sequences of 512..4096 tokens, every output against the oracle."""
+    print("[case] gqa8b", flush=True)
+    c = make_case(synth.gqa8b())
+    out = run_decode(c)
+    ref = oracle_outputs(c, range(len(c.lens)))
+    assert_close(out, ref, "gqa8b")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_block_size_sweep_sampled(bs):
+    """256 sequences of 4096 - r tokens; 24 sampled sequences against the oracle; tail waste = sum r."""
+    w = synth.sweep(bs)
+    print(f"[case] sweep bs={bs}", flush=True)
+    c = make_case(w)
+    out = run_decode(c)
+    rng = np.random.default_rng(bs)
+    sample = sorted(rng.choice(len(c.lens), size=24, replace=False).tolist())
+    ref = oracle_outputs(c, sample)
+    assert_close(out[sample], ref, f"sweep bs={bs}")
+    waste = c.bm.stats()["tail_waste_slots"]
+    assert waste == sum(4096 - s for s in c.lens) == c.model.stats()["tail_waste_slots"]
+    del c
+    torch.cuda.empty_cache()
+
+
+def test_run_to_run_bit_identical():
+    c = make_case(synth.gqa8b())
+    a = run_decode(c)
+    b = run_decode(c)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+EDGE_LENS = [0, 1, 2, 7, 8, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 1500]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_edge_lengths(dtype, d, bs):
+    """Empty, single-token, block- and partition-aligned and ragged lengths, NaN in every unused slot."""
+    w = synth.gqa8b()
+    print(f"[case] edge dtype={dtype} d={d} bs={bs}", flush=True)
+    c = make_case(w, EDGE_LENS, d=d, block_size=bs, dtype=dtype, hq=8, hkv=2, seed=300 + d + bs)
+    out = run_decode(c)
+    ref = oracle_outputs(c, range(len(EDGE_LENS)))
+    assert torch.count_nonzero(out[0].float()) == 0  # S = 0 gives zeros
+    tol = (1e-4, 1e-5) if dtype == torch.float32 else (1e-2, 5e-3)
+    assert_close(out, ref, f"edge dtype={dtype} d={d} bs={bs}", *tol)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 1), (32, 2), (64, 4), (32, 1), (64, 1)])
+def test_group_sizes(hq, hkv):
+    """MHA (G = 1), MQA (Hkv = 1) and other group sizes, including G > 16 (generic kernel)."""
+    w = synth.gqa8b()
+    print(f"[case] group hq={hq} hkv={hkv}", flush=True)
+    lens = [1, 100, 600, 1300]
+    c = make_case(w, lens, hq=hq, hkv=hkv, seed=500 + hq + hkv)
+    out = run_decode(c)
+    ref = oracle_outputs(c, range(len(lens)))
+    assert_close(out, ref, f"group hq={hq} hkv={hkv}")
+
+
+def test_short_lengths_with_large_launch_bound():
+    """max_context_len far above the real lengths: extra partitions exit, results unchanged."""
+    c = make_case(synth.gqa8b(), [5, 40, 300], seed=700)
+    c.max_blocks = 4096 // 16
+    tables = np.zeros((3, c.max_blocks), dtype=np.int32)
+    tables[:, : c.tables.shape[1]] = c.tables
+    out = run_decode(c, tables_dev=torch.from_numpy(tables).cuda(), max_ctx=4096)
+    ref = oracle_outputs(c, range(3))
+    assert_close(out, ref, "short lengths, launch bound 4096")

@@ -1,0 +1,111 @@
+"""GPU: KV append and copy-on-write block copy, bit-exact against the oracle's storage rules."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as OA
+from pool_layout import k_to_logical, v_to_logical
+
+pytestmark = pytest.mark.gpu
+
+
+def _pools(num_blocks, hkv, d, bs, dtype, seed, layers=1):
+    import paged_kv_cache_124_amd as pa
+    kshape, vshape = pa.pool_shapes(num_blocks, hkv, d, bs, torch.tensor([], dtype=dtype).element_size())
+    if layers > 1:
+        kshape, vshape = (layers,) + kshape, (layers,) + vshape
+    k = synth.fill_randn_(torch.empty(kshape, dtype=dtype, device="cuda"), 1.0, seed)
+    v = synth.fill_randn_(torch.empty(vshape, dtype=dtype, device="cuda"), 1.0, seed + 1)
+    return k, v
+
+
+def _logical_np(k, v):
+    """Whole pool in the oracle's layout as raw bits (int16/int32 views) so comparisons are bit-exact."""
+    kl = k_to_logical(k.cpu()).contiguous()
+    vl = v_to_logical(v.cpu()).contiguous()
+    view = torch.int16 if k.dtype == torch.bfloat16 else torch.int32
+    return kl.view(view).numpy().copy(), vl.view(view).numpy().copy()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 8), (128, 32), (64, 16)])
+def test_append_kv_bit_exact(dtype, d, bs):
+    import paged_kv_cache_124_amd as pa
+    print(f"[case] append dtype={dtype} d={d} bs={bs}", flush=True)
+    nb, hkv, T = 37, 4, 50
+    k, v = _pools(nb, hkv, d, bs, dtype, 11)
+    k0, v0 = _logical_np(k, v)
+    rng = np.random.default_rng(3)
+    slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int32)
+    slots[5] = -1                      # skipped
+    slots[9] = nb * bs + 3             # beyond the pool: skipped
+    kn = synth.randn((T, hkv, d), dtype, 1.0, 21, "cuda")
+    vn = synth.randn((T, hkv, d), dtype, 1.0, 22, "cuda")
+    pa.pa_append_kv(k, v, kn, vn, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    view = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    kn_bits = kn.cpu().contiguous().view(view).numpy()
+    vn_bits = vn.cpu().contiguous().view(view).numpy()
+    expect_k, expect_v = k0.copy(), v0.copy()
+    ok_slots = np.where(slots < nb * bs, slots, -1)
+    OA.append_kv(expect_k, expect_v, kn_bits, vn_bits, ok_slots)
+    got_k, got_v = _logical_np(k, v)
+    assert np.array_equal(got_k, expect_k)
+    assert np.array_equal(got_v, expect_v)
+
+
+@pytest.mark.parametrize("layers", [1, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_copy_blocks_bit_exact(layers, dtype):
+    import paged_kv_cache_124_amd as pa
+    print(f"[case] copy layers={layers} dtype={dtype}", flush=True)
+    nb, hkv, d, bs = 40, 8, 128, 16
+    k, v = _pools(nb, hkv, d, bs, dtype, 31, layers)
+    rng = np.random.default_rng(5)
+    ids = rng.permutation(nb)
+    pairs = np.stack([ids[:12], ids[12:24]], axis=1).astype(np.int32)  # distinct dst, no dst is a src
+    view = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    before_k = k.cpu().view(view).numpy().copy()
+    before_v = v.cpu().view(view).numpy().copy()
+    pa.pa_copy_blocks(k, v, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    # the oracle's rule is layout-agnostic (whole blocks), so compare in the physical layout
+    exp_k, exp_v = before_k.copy(), before_v.copy()
+    if layers == 1:
+        exp_k, exp_v = exp_k[None], exp_v[None]
+    OA.copy_blocks(exp_k, exp_v, [tuple(p) for p in pairs])
+    got_k = k.cpu().view(view).numpy()
+    got_v = v.cpu().view(view).numpy()
+    if layers == 1:
+        got_k, got_v = got_k[None], got_v[None]
+    assert np.array_equal(got_k, exp_k) and np.array_equal(got_v, exp_v)
+
+
+def test_copy_then_append_matches_oracle_cow_step():
+    """One copy-on-write step: copy (src, dst) first, then append into dst -- the shared tail stays intact."""
+    import paged_kv_cache_124_amd as pa
+    from oracle.block_manager import BlockManagerModel
+    nb, hkv, d, bs = 16, 2, 64, 16
+    k, v = _pools(nb, hkv, d, bs, torch.bfloat16, 41)
+    bm = pa.BlockManager(nb, bs)
+    m = BlockManagerModel(nb, bs)
+    for x in (bm, m):
+        assert x.add_seq(1, 35) == 0 and x.fork(1, 2) == 0
+    st, slots, pairs, _ = bm.append_slots([1, 2])
+    mst, mslots, mpairs, _ = m.append_slots([1, 2])
+    assert st == mst == 0 and list(slots) == mslots and [tuple(p) for p in pairs] == mpairs == [(2, 3)]
+    k0, v0 = _logical_np(k, v)
+    kn = synth.randn((2, hkv, d), torch.bfloat16, 1.0, 51, "cuda")
+    vn = synth.randn((2, hkv, d), torch.bfloat16, 1.0, 52, "cuda")
+    pa.pa_copy_blocks(k, v, torch.from_numpy(np.asarray(pairs, dtype=np.int32)).cuda())
+    pa.pa_append_kv(k, v, kn, vn, torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda())
+    torch.cuda.synchronize()
+    ek, ev = k0.copy(), v0.copy()
+    OA.copy_blocks(ek, ev, mpairs)
+    OA.append_kv(ek, ev, kn.cpu().view(torch.int16).numpy(), vn.cpu().view(torch.int16).numpy(), mslots)
+    gk, gv = _logical_np(k, v)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+    # the shared prefix (blocks 0, 1) and B's tail (block 2) hold the prompt; A's tail (3) is a copy + new token
+    assert np.array_equal(gk[3, :, :3], k0[2, :, :3])
