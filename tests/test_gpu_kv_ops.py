@@ -66,20 +66,17 @@ def test_copy_blocks_bit_exact(layers, dtype):
     rng = np.random.default_rng(5)
     ids = rng.permutation(nb)
     pairs = np.stack([ids[:12], ids[12:24]], axis=1).astype(np.int32)  # distinct dst, no dst is a src
-    view = torch.int16 if dtype == torch.bfloat16 else torch.int32
-    before_k = k.cpu().view(view).numpy().copy()
-    before_v = v.cpu().view(view).numpy().copy()
+
+    def logical(kk, vv):  # [L][nb][Hkv][B][D] raw bits
+        kk, vv = (kk, vv) if layers > 1 else (kk[None], vv[None])
+        ks, vs = zip(*[_logical_np(kk[i], vv[i]) for i in range(kk.shape[0])])
+        return np.stack(ks), np.stack(vs)
+
+    exp_k, exp_v = logical(k, v)
     pa.pa_copy_blocks(k, v, torch.from_numpy(pairs).cuda())
     torch.cuda.synchronize()
-    # the oracle's rule is layout-agnostic (whole blocks), so compare in the physical layout
-    exp_k, exp_v = before_k.copy(), before_v.copy()
-    if layers == 1:
-        exp_k, exp_v = exp_k[None], exp_v[None]
-    OA.copy_blocks(exp_k, exp_v, [tuple(p) for p in pairs])
-    got_k = k.cpu().view(view).numpy()
-    got_v = v.cpu().view(view).numpy()
-    if layers == 1:
-        got_k, got_v = got_k[None], got_v[None]
+    OA.copy_blocks(exp_k, exp_v, [tuple(int(x) for x in p) for p in pairs])
+    got_k, got_v = logical(k, v)
     assert np.array_equal(got_k, exp_k) and np.array_equal(got_v, exp_v)
 
 
