@@ -44,6 +44,8 @@ def parse():
                     help="pool copies rotated step to step so reads come from HBM, not the 256 MB Infinity Cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (known bytes) to scale HBM counters")
     return ap.parse_args()
 
 
@@ -86,56 +88,81 @@ class Runner:
         self.v_new = synth.randn((self.n, w.hkv, w.d), dt, w.value_scale, w.seed * 10 + 5, device)
         self.out = torch.empty_like(self.q)
         ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
-        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+        self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)  # zero before first use
         self.part = pa.pa_decode_partition_tokens(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
-        # staging: [slots N | lens N | pairs 2N | tables N*max_blocks]
-        self.words = 4 * self.n + self.n * self.max_blocks
-        self.host = [torch.empty(self.words, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.host_ev = [None, None]
-        self.dev = torch.empty(self.words, dtype=torch.int32, device=device)
-        self.step_i = 0
-        self.replicas = replicas
-        self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
-        self.decode_events = []
-
-    def step(self, time_decode=False):
-        torch, pa = self.torch, self.pa
+        # Host staging [slots N | lens N | pairs 2N | tables N*max_blocks] in pinned memory,
+        # two of each (ping-pong, so the host fills one while the other uploads), and the
+        # matching device buffers.  The block manager writes straight into the staging buffer.
         n, mb = self.n, self.max_blocks
-        st, slots, pairs, _ = self.bm.append_slots(self.seqs)
+        self.words = 4 * n + n * mb
+        self.host = [torch.empty(self.words, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.dev = [torch.empty(self.words, dtype=torch.int32, device=device) for _ in range(2)]
+        self.host_ev = [torch.cuda.Event(), torch.cuda.Event()]
+        self.host_used = [False, False]
+        self.replicas = replicas
+        # pre-marshalled C calls per (replica, staging buffer)
+        import ctypes
+        self.ct = ctypes
+        L = pa.lib
+        self.lib = L
+        self.seqs_p = self.seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        p32 = ctypes.POINTER(ctypes.c_int32)
+        self.h_ptr = [ctypes.cast(hb.data_ptr(), p32) for hb in self.host]
+        self.npairs = ctypes.c_int()
+        self.append_slots_args = []
+        self.build_args = []
+        for b in range(2):
+            base = self.host[b].data_ptr()
+            self.append_slots_args.append((self.bm.handle, self.seqs_p, n, ctypes.cast(base, p32),
+                                           ctypes.cast(base + 8 * n, p32), ctypes.byref(self.npairs)))
+            self.build_args.append((self.bm.handle, self.seqs_p, n, mb, ctypes.cast(base + 16 * n, p32),
+                                    ctypes.cast(base + 4 * n, p32)))
+        self.dec_args, self.app_args, self.copy_args = {}, {}, {}
+        for r in range(replicas):
+            for b in range(2):
+                d = self.dev[b]
+                self.dec_args[r, b], _ = pa.pa_decode_args(self.out, self.q, self.k[r], self.v[r],
+                                                           d[4 * n:].view(n, mb), d[n:2 * n], w.scale,
+                                                           self.max_ctx, workspace=self.ws)
+                self.app_args[r, b] = pa.pa_append_kv_args(self.k[r], self.v[r], self.k_new, self.v_new, d[:n])
+                self.copy_args[r, b] = list(pa.pa_copy_blocks_args(self.k[r], self.v[r],
+                                                                   d[2 * n:4 * n].view(n, 2)))
+        self.step_i = 0
+        self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
+        self.lens_sum = sum(self.lens0)
+        self.timing_events = []
+        self.host_s = 0.0
+
+    def step(self, timing=None):
+        t_host = time.perf_counter()
+        L = self.lib
+        b = self.step_i & 1
+        if self.host_used[b]:
+            self.host_ev[b].synchronize()  # the upload from host[b] two steps ago has been read
+        st = L.pa_bm_append_slots(*self.append_slots_args[b])
         if st != 0:
             raise RuntimeError(f"block manager append failed: status {st}")
-        b = self.step_i & 1
-        if self.host_ev[b] is not None:
-            self.host_ev[b].synchronize()
-        h = self.host[b].numpy()
-        h[:n] = slots
-        npairs = len(pairs)
-        if npairs:
-            h[2 * n:2 * n + 2 * npairs] = pairs.reshape(-1)
-        st, tables, lens = self.bm.build_batch(self.seqs, mb)
+        npairs = self.npairs.value
+        st = L.pa_bm_build_batch(*self.build_args[b])
         assert st == 0
-        h[n:2 * n] = lens
-        h[4 * n:] = tables.reshape(-1)
-        self.dev.copy_(self.host[b], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self.host_ev[b] = ev
-        d = self.dev
+        self.dev[b].copy_(self.host[b], non_blocking=True)
+        self.host_ev[b].record()
+        self.host_used[b] = True
         r = self.step_i % self.replicas
-        k, v = self.k[r], self.v[r]
         if npairs:
-            pa.pa_copy_blocks(k, v, d[2 * n:2 * n + 2 * npairs].view(npairs, 2))
-        pa.pa_append_kv(k, v, self.k_new, self.v_new, d[:n])
-        if time_decode:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        pa.pa_decode(self.out, self.q, k, v, d[4 * n:].view(n, mb), d[n:2 * n], self.w.scale, self.max_ctx,
-                     workspace=self.ws)
-        if time_decode:
-            e1.record()
-            self.decode_events.append((e0, e1))
+            ca = self.copy_args[r, b]
+            ca[3] = npairs
+            assert L.pa_copy_blocks(*ca) == 0
+        assert L.pa_append_kv(*self.app_args[r, b]) == 0
+        if timing is not None:
+            timing[0].record()
+        assert L.pa_decode(*self.dec_args[r, b]) == 0
+        if timing is not None:
+            timing[1].record()
         self.step_i += 1
-        return int(lens.sum()) * self.kv_bytes_per_token
+        self.lens_sum += self.n
+        self.host_s += time.perf_counter() - t_host
+        return self.lens_sum * self.kv_bytes_per_token
 
 
 def cpu_baseline(w, seconds):
@@ -187,6 +214,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                          "launches": 5}))
+        return
     w = workload(args.workload)
     total = args.steps + args.warmup + 1
     print(f"[bench] building workload {w.name}", file=sys.stderr, flush=True)
@@ -197,19 +233,22 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timing = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
+    run.host_s = 0.0
     t0 = time.perf_counter()
     e0.record()
     kv_bytes = 0
-    for _ in range(args.steps):
-        kv_bytes += run.step(time_decode=True)
+    for i in range(args.steps):
+        kv_bytes += run.step(timing[i])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
     ms_step = max(gpu_ms, wall * 1e3) / args.steps
     value = kv_bytes / args.steps / (ms_step * 1e-3) / 1e9
-    dec_ms = [a.elapsed_time(b) for a, b in run.decode_events]
+    dec_ms = [a.elapsed_time(b) for a, b in timing]
     dec_avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
     bytes_per_launch = kv_bytes / args.steps
     achieved = bytes_per_launch / (dec_avg_us * 1e-6) / 1e9
@@ -230,10 +269,11 @@ def main():
                                f"bf16, contexts {min(run.lens0)}..{max(run.lens0)} growing 1/step",
                    "num_seqs": run.n, "block_size": w.block_size, "pool_blocks": run.num_blocks,
                    "pool_replicas": args.replicas, "partition_tokens": run.part,
-                   "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2)},
+                   "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2),
+                   "host_us_per_step": round(run.host_s / args.steps * 1e6, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pa_decode (decode_mfma + merge_partitions)", "avg_us": round(dec_avg_us, 2)},
+                     "kernel": "pa_decode (decode kernel + merge)", "avg_us": round(dec_avg_us, 2)},
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)

@@ -103,12 +103,16 @@ int pa_version(void);
  *   max_context_len an upper bound of all S (sizes the launch without a
  *                  device read)
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes; may be NULL when that size is 0.  Contents on entry
- *                  are ignored.
+ *                  bytes; may be NULL when that size is 0.  It must be
+ *                  zero-filled before its first use (it holds a work counter
+ *                  that every call returns to zero when it completes); calls
+ *                  that may overlap in time need separate workspaces.
  * Supported: Hq % Hkv == 0, Hq / Hkv <= 64, d_head in {64, 128},
  * block_size in {8, 16, 32}, dtype PA_F32 or PA_BF16 (fp32 accumulation;
  * bf16 outputs are rounded to nearest even).  Block ids outside
- * [0, num_blocks) are never dereferenced (they read as zero keys and values).
+ * [0, num_blocks) are never dereferenced: the tokens they hold are left out
+ * of the softmax.  num_blocks >= 1 and max_blocks_per_seq >= 1 when
+ * num_seqs > 0.
  */
 int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* context_lens,
@@ -116,11 +120,14 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes pa_decode needs for these sizes (0 when no split is used). */
+/* Workspace bytes pa_decode needs for these sizes on the current device
+ * (0 when no split is used). */
 size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                  int max_context_len, int dtype);
 
-/* Tokens per partition that pa_decode uses for these sizes (for reporting). */
+/* Tokens per partition that pa_decode uses for these sizes (for reporting);
+ * 0 when the balanced persistent kernel is used (bf16, Hq / Hkv <= 16,
+ * num_seqs <= 4096), whose split follows equal per-wave tile ranges. */
 int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                int max_context_len, int dtype);
 

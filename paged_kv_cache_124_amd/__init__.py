@@ -14,8 +14,11 @@ from ._lib import (  # noqa: F401
     PAError,
     lib,
     pa_append_kv,
+    pa_append_kv_args,
     pa_copy_blocks,
+    pa_copy_blocks_args,
     pa_decode,
+    pa_decode_args,
     pa_decode_partition_tokens,
     pa_decode_workspace_bytes,
     pool_shapes,

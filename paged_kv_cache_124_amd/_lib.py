@@ -140,14 +140,12 @@ def pa_decode_partition_tokens(num_seqs, Hq, Hkv, d_head, block_size, max_contex
     return int(lib.pa_decode_partition_tokens(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype))
 
 
-def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
-              workspace=None, stream=None):
-    """pa_decode of include/pa.h on torch device tensors.
+def pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                   workspace=None, stream=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode(*args)`` calls.
 
-    q, out [N][Hq][D]; k_pool/v_pool one layer in the library layout; block_tables
-    int32 [N][max_blocks]; context_lens int32 [N].  ``workspace`` is a uint8
-    device tensor of at least pa_decode_workspace_bytes(...) bytes; when None a
-    buffer is allocated through torch for this call.
+    The tuple holds raw pointers: the tensors (and the returned workspace)
+    must stay alive and in place while it is used.
     """
     import torch
     n, hq, d = q.shape
@@ -161,19 +159,34 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
     dt = _dtype_code(q)
     need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, dt)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.pa_decode(_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-                       _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
-                       n, hq, hkv, d, bs, float(scale), block_tables.shape[1], int(max_context_len), nb, dt,
-                       ws_ptr, ws_bytes, _stream_ptr(stream))
-    _check(st, "pa_decode")
+    args = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+            n, hq, hkv, d, bs, float(scale), block_tables.shape[1], int(max_context_len), nb, dt,
+            ws_ptr, ws_bytes, _stream_ptr(stream))
+    return args, workspace
+
+
+def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+              workspace=None, stream=None):
+    """pa_decode of include/pa.h on torch device tensors.
+
+    q, out [N][Hq][D]; k_pool/v_pool one layer in the library layout; block_tables
+    int32 [N][max_blocks]; context_lens int32 [N].  ``workspace`` is a uint8
+    device tensor of at least pa_decode_workspace_bytes(...) bytes, zero-filled
+    before its first use; when None a zeroed buffer is allocated through torch
+    for this call.
+    """
+    args, _ws = pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                               workspace, stream)
+    _check(lib.pa_decode(*args), "pa_decode")
     return out
 
 
-def pa_append_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
-    """pa_append_kv of include/pa.h: k_new/v_new [T][Hkv][D], slot_mapping int32 [T]."""
+def pa_append_kv_args(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
+    """Validate once and return the argument tuple for repeated ``lib.pa_append_kv(*args)`` calls."""
     import torch
     nb, hkv, d, bs = _pool_dims(k_pool, v_pool)
     t = k_new.shape[0]
@@ -183,17 +196,22 @@ def pa_append_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
         raise ValueError("k_new / v_new must have the pool's element type")
     if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (t,):
         raise ValueError("slot_mapping must be int32 [T]")
-    st = lib.pa_append_kv(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
-                          _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"), t, hkv, d, bs, nb,
-                          _dtype_code(k_pool), _stream_ptr(stream))
-    _check(st, "pa_append_kv")
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+            _dev(slot_mapping, "slot_mapping"), t, hkv, d, bs, nb, _dtype_code(k_pool), _stream_ptr(stream))
 
 
-def pa_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
-    """pa_copy_blocks of include/pa.h.
+def pa_append_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
+    """pa_append_kv of include/pa.h: k_new/v_new [T][Hkv][D], slot_mapping int32 [T]."""
+    _check(lib.pa_append_kv(*pa_append_kv_args(k_pool, v_pool, k_new, v_new, slot_mapping, stream)),
+           "pa_append_kv")
+
+
+def pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream=None):
+    """Validate once and return the argument tuple for ``lib.pa_copy_blocks(*args)``.
 
     Pools are one layer ([num_blocks]...) or all layers ([L][num_blocks]...);
-    src_dst_pairs is an int32 device tensor [P][2].
+    src_dst_pairs is an int32 device tensor [P][2] (P may be lowered in the
+    returned tuple's 4th entry to use a prefix of the pairs).
     """
     import torch
     layered = k_pool.dim() == 6
@@ -203,10 +221,13 @@ def pa_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
     if src_dst_pairs.dtype != torch.int32 or src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
         raise ValueError("src_dst_pairs must be int32 [P][2]")
     stride = kl.numel() if layered else 0
-    st = lib.pa_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(src_dst_pairs, "src_dst_pairs"),
-                            src_dst_pairs.shape[0], hkv, d, bs, nb, layers, stride, _dtype_code(k_pool),
-                            _stream_ptr(stream))
-    _check(st, "pa_copy_blocks")
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(src_dst_pairs, "src_dst_pairs"),
+            src_dst_pairs.shape[0], hkv, d, bs, nb, layers, stride, _dtype_code(k_pool), _stream_ptr(stream))
+
+
+def pa_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
+    """pa_copy_blocks of include/pa.h."""
+    _check(lib.pa_copy_blocks(*pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream)), "pa_copy_blocks")
 
 
 # ---------------------------------------------------------------------------
@@ -267,6 +288,11 @@ class BlockManager:
         if st != PA_OK:
             return st, slots[:0], pairs[:0], -npairs.value - 1
         return st, slots[:n], pairs[:npairs.value], -1
+
+    @property
+    def handle(self):
+        """The pa_bm* handle, for direct ``lib.pa_bm_*`` calls with caller-owned host buffers."""
+        return self._h
 
     def free_seq(self, seq: int) -> int:
         return lib.pa_bm_free_seq(self._h, seq)

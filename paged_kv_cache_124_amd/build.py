@@ -18,13 +18,17 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 
-HIP_SOURCES = ["decode.hip", "kv_ops.hip"]
+HIP_SOURCES = ["decode.hip", "decode_stream.hip", "kv_ops.hip"]
 HOST_SOURCES = ["block_manager.cpp", "status.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops on its own.
+# atomic optimizer off: it turns the decode kernel's lane-0 work claim into a
+# wave-aggregated atomic whose result is waited for at once, which would stall
+# the tile pipeline; the claim's result is only needed one worker later.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -34,6 +34,7 @@
 #include <cstdlib>
 
 #include "common.h"
+#include "decode_stream.h"
 
 namespace pa {
 namespace {
@@ -455,9 +456,24 @@ void launch_merge(const Plan& pl, hipStream_t s, const float* ws, const int32_t*
 }  // namespace
 }  // namespace pa
 
+namespace pa {
+namespace {
+// The persistent stream kernel serves bf16 with G <= 16; PA_DECODE_PATH=partition
+// selects the partitioned kernel instead (kept for A/B measurements).
+bool use_stream(int num_seqs, int hq, int hkv, int d, int block_size, int dtype) {
+  if (hkv <= 0 || hq % hkv != 0) return false;
+  if (!stream_eligible(num_seqs, hq / hkv, d, block_size, dtype)) return false;
+  const char* env = std::getenv("PA_DECODE_PATH");
+  return !(env && env[0] == 'p');
+}
+}  // namespace
+}  // namespace pa
+
 extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                             int max_context_len, int dtype) {
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_context_len < 0) return 0;
+  if (pa::use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype))
+    return pa::stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len).workspace_bytes;
   const pa::Plan p = pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
   return pa::plan_workspace_bytes(p, num_seqs, Hq, d_head);
 }
@@ -465,6 +481,7 @@ extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d
 extern "C" int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                           int max_context_len, int dtype) {
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0) return 0;
+  if (pa::use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) return 0;
   return pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype).part;
 }
 
@@ -484,8 +501,17 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_pool, const voi
     return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;  // kernels may read block 0 / entry 0
   if (num_seqs > 65535 || Hq > 65535) return PA_ERR_UNSUPPORTED;
 
+  const float scale_log2_s = scale * kLog2e;
+  if (use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) {
+    const StreamPlan sp = stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len);
+    if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
+    return launch_stream(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, out,
+                         workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq, num_blocks,
+                         scale_log2_s);
+  }
   const Plan pl = make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
   const size_t need = plan_workspace_bytes(pl, num_seqs, Hq, d_head);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;

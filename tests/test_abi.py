@@ -71,15 +71,21 @@ def test_decode_host_validation():
 
 def test_workspace_and_partition_plan():
     import paged_kv_cache_124_amd as pa
-    # one partition covers the whole context: no workspace
-    part = pa.pa_decode_partition_tokens(1, 32, 8, 128, 16, 100, pa.PA_BF16)
-    assert part % 128 == 0 and pa.pa_decode_workspace_bytes(1, 32, 8, 128, 16, 100, pa.PA_BF16) == 0
-    # long contexts: N * Hq * P * (D + 2) floats
+    # bf16, G <= 16: balanced persistent kernel, no fixed partition; workspace holds the
+    # tile prefix sums and summary records, independent of the context length bound
     for n, ctx, bs in ((64, 4096, 16), (16, 32768, 16), (256, 4096, 8), (256, 4096, 32)):
-        part = pa.pa_decode_partition_tokens(n, 32, 8, 128, bs, ctx, pa.PA_BF16)
-        assert part % 128 == 0 and part // bs <= 64
+        assert pa.pa_decode_partition_tokens(n, 32, 8, 128, bs, ctx, pa.PA_BF16) == 0
+        ws = pa.pa_decode_workspace_bytes(n, 32, 8, 128, bs, ctx, pa.PA_BF16)
+        assert ws >= (n + 1) * 4 and ws % 4 == 0
+        assert ws == pa.pa_decode_workspace_bytes(n, 32, 8, 128, bs, 2 * ctx, pa.PA_BF16)
+    # fp32: partitioned kernel; one partition covers a short context: no workspace
+    part = pa.pa_decode_partition_tokens(1, 8, 2, 64, 16, 100, pa.PA_F32)
+    assert part > 0 and pa.pa_decode_workspace_bytes(1, 8, 2, 64, 16, 100, pa.PA_F32) == 0
+    # long contexts: N * Hq * P * (D + 2) floats
+    for n, ctx in ((4, 1000), (3, 4096)):
+        part = pa.pa_decode_partition_tokens(n, 8, 2, 64, 16, ctx, pa.PA_F32)
         p = -(-ctx // part)
-        assert pa.pa_decode_workspace_bytes(n, 32, 8, 128, bs, ctx, pa.PA_BF16) == n * 32 * p * 130 * 4
+        assert pa.pa_decode_workspace_bytes(n, 8, 2, 64, 16, ctx, pa.PA_F32) == n * 8 * p * 66 * 4
 
 
 def test_append_and_copy_host_validation():
