@@ -3,11 +3,14 @@
 
 A step is one pass of the whole decode-step path over a batch of sequences:
   1. host block manager: one batch append (slot per sequence, copy-on-write
-     pairs), block tables and lengths for the batch;
-  2. one host-to-device copy of slots, lengths and tables (pinned staging);
+     pairs);
+  2. one host-to-device copy of the slots and pairs (pinned staging);
   3. pa_copy_blocks (when the batch produced copy-on-write pairs);
-  4. pa_append_kv of the new token of every sequence;
-  5. pa_decode over every sequence's context (partitions + merge).
+  4. pa_append_step: the new token of every sequence, and the device-resident
+     block tables and lengths moved forward as the block manager's were;
+  5. pa_decode over every sequence's context (pieces + merge).
+The block tables and lengths are uploaded once, before the timed region, and
+from then on follow the block manager through step 4.
 Contexts grow by one token per step.  Inputs are resident in HBM before the
 timed region starts.  `value` is the KV bytes the decode reads per step
 (sum of context lengths x 2 x Hkv x d_head x 2 bytes) divided by the
@@ -90,11 +93,16 @@ class Runner:
         ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
         self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)  # zero before first use
         self.part = pa.pa_decode_partition_tokens(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
-        # Host staging [slots N | lens N | pairs 2N | tables N*max_blocks] in pinned memory,
-        # two of each (ping-pong, so the host fills one while the other uploads), and the
-        # matching device buffers.  The block manager writes straight into the staging buffer.
+        # Block tables and lengths live on the device; pa_append_step moves them forward.
         n, mb = self.n, self.max_blocks
-        self.words = 4 * n + n * mb
+        st, tables, lens = self.bm.build_batch(self.seqs, mb)
+        assert st == 0
+        self.d_tables = torch.from_numpy(tables).to(device)
+        self.d_lens = torch.from_numpy(lens).to(device)
+        # Host staging [slots N | pairs 2N] in pinned memory, two of each (ping-pong, so the
+        # host fills one while the other uploads), and the matching device buffers.  The
+        # block manager writes straight into the staging buffer.
+        self.words = 3 * n
         self.host = [torch.empty(self.words, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self.dev = [torch.empty(self.words, dtype=torch.int32, device=device) for _ in range(2)]
         self.host_ev = [torch.cuda.Event(), torch.cuda.Event()]
@@ -107,26 +115,22 @@ class Runner:
         self.lib = L
         self.seqs_p = self.seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
         p32 = ctypes.POINTER(ctypes.c_int32)
-        self.h_ptr = [ctypes.cast(hb.data_ptr(), p32) for hb in self.host]
         self.npairs = ctypes.c_int()
         self.append_slots_args = []
-        self.build_args = []
         for b in range(2):
             base = self.host[b].data_ptr()
             self.append_slots_args.append((self.bm.handle, self.seqs_p, n, ctypes.cast(base, p32),
-                                           ctypes.cast(base + 8 * n, p32), ctypes.byref(self.npairs)))
-            self.build_args.append((self.bm.handle, self.seqs_p, n, mb, ctypes.cast(base + 16 * n, p32),
-                                    ctypes.cast(base + 4 * n, p32)))
+                                           ctypes.cast(base + 4 * n, p32), ctypes.byref(self.npairs)))
         self.dec_args, self.app_args, self.copy_args = {}, {}, {}
         for r in range(replicas):
+            self.dec_args[r], _ = pa.pa_decode_args(self.out, self.q, self.k[r], self.v[r], self.d_tables,
+                                                    self.d_lens, w.scale, self.max_ctx, workspace=self.ws)
             for b in range(2):
                 d = self.dev[b]
-                self.dec_args[r, b], _ = pa.pa_decode_args(self.out, self.q, self.k[r], self.v[r],
-                                                           d[4 * n:].view(n, mb), d[n:2 * n], w.scale,
-                                                           self.max_ctx, workspace=self.ws)
-                self.app_args[r, b] = pa.pa_append_kv_args(self.k[r], self.v[r], self.k_new, self.v_new, d[:n])
+                self.app_args[r, b] = pa.pa_append_step_args(self.k[r], self.v[r], self.k_new, self.v_new, d[:n],
+                                                             self.d_tables, self.d_lens)
                 self.copy_args[r, b] = list(pa.pa_copy_blocks_args(self.k[r], self.v[r],
-                                                                   d[2 * n:4 * n].view(n, 2)))
+                                                                   d[n:3 * n].view(n, 2)))
         self.step_i = 0
         self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
         self.lens_sum = sum(self.lens0)
@@ -143,9 +147,8 @@ class Runner:
         if st != 0:
             raise RuntimeError(f"block manager append failed: status {st}")
         npairs = self.npairs.value
-        st = L.pa_bm_build_batch(*self.build_args[b])
-        assert st == 0
-        self.dev[b].copy_(self.host[b], non_blocking=True)
+        words = self.n + 2 * npairs
+        self.dev[b][:words].copy_(self.host[b][:words], non_blocking=True)
         self.host_ev[b].record()
         self.host_used[b] = True
         r = self.step_i % self.replicas
@@ -153,16 +156,24 @@ class Runner:
             ca = self.copy_args[r, b]
             ca[3] = npairs
             assert L.pa_copy_blocks(*ca) == 0
-        assert L.pa_append_kv(*self.app_args[r, b]) == 0
+        assert L.pa_append_step(*self.app_args[r, b]) == 0
         if timing is not None:
             timing[0].record()
-        assert L.pa_decode(*self.dec_args[r, b]) == 0
+        assert L.pa_decode(*self.dec_args[r]) == 0
         if timing is not None:
             timing[1].record()
         self.step_i += 1
         self.lens_sum += self.n
         self.host_s += time.perf_counter() - t_host
         return self.lens_sum * self.kv_bytes_per_token
+
+
+    def check_device_batch(self):
+        """The device tables and lengths still equal the block manager's (after the timed steps)."""
+        st, tables, lens = self.bm.build_batch(self.seqs, self.max_blocks)
+        assert st == 0
+        if not (np.array_equal(self.d_tables.cpu().numpy(), tables) and np.array_equal(self.d_lens.cpu().numpy(), lens)):
+            raise RuntimeError("device block tables / lengths diverged from the block manager")
 
 
 def cpu_baseline(w, seconds):
@@ -245,6 +256,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    run.check_device_batch()
     gpu_ms = e0.elapsed_time(e1)
     ms_step = max(gpu_ms, wall * 1e3) / args.steps
     value = kv_bytes / args.steps / (ms_step * 1e-3) / 1e9

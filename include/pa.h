@@ -85,12 +85,13 @@ int pa_version(void);
  *     s_t = scale * dot(q[n][h], K_t),  K_t, V_t gathered through the table
  *     out[n][h] = sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s)
  *
- * Long contexts are split into partitions processed in parallel; each writes
- * a (max, shifted weight sum, shifted value sum) summary into `workspace` and
- * a second kernel merges them with the common-maximum rule of the second page,
- * section 11.  The partition size and the merge order are fixed for a given
- * (num_seqs, Hkv, d_head, block_size, max_context_len), so repeated calls on
- * the same inputs give bit-identical outputs.
+ * The work is split across the GPU in pieces of a sequence's context; each
+ * piece that does not cover its whole sequence leaves a (max, shifted weight
+ * sum, shifted value sum) summary in `workspace`, and a second kernel merges
+ * the pieces of a sequence with the common-maximum rule of the second page,
+ * section 11.  The split and the merge order are fixed for given sizes,
+ * context_lens and device, so repeated calls on the same inputs give
+ * bit-identical outputs.
  *
  *   out            [num_seqs][Hq][d_head], element type `dtype`
  *   q              [num_seqs][Hq][d_head], element type `dtype`
@@ -103,10 +104,10 @@ int pa_version(void);
  *   max_context_len an upper bound of all S (sizes the launch without a
  *                  device read)
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes; may be NULL when that size is 0.  It must be
- *                  zero-filled before its first use (it holds a work counter
- *                  that every call returns to zero when it completes); calls
- *                  that may overlap in time need separate workspaces.
+ *                  bytes; may be NULL when that size is 0.  Zero-fill it
+ *                  before its first use (counters kept in it are returned to
+ *                  zero by every call); calls that may overlap in time need
+ *                  separate workspaces.
  * Supported: Hq % Hkv == 0, Hq / Hkv <= 64, d_head in {64, 128},
  * block_size in {8, 16, 32}, dtype PA_F32 or PA_BF16 (fp32 accumulation;
  * bf16 outputs are rounded to nearest even).  Block ids outside
@@ -127,7 +128,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int 
 
 /* Tokens per partition that pa_decode uses for these sizes (for reporting);
  * 0 when the balanced persistent kernel is used (bf16, Hq / Hkv <= 16,
- * num_seqs <= 4096), whose split follows equal per-wave tile ranges. */
+ * num_seqs <= 3072), whose split follows equal per-wave tile ranges. */
 int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                int max_context_len, int dtype);
 
@@ -146,6 +147,33 @@ int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int bl
 int pa_append_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                  const int32_t* slot_mapping, int num_tokens, int Hkv, int d_head,
                  int block_size, int num_blocks, int dtype, void* stream);
+
+/* pa_append_step: pa_append_kv for one decode step of a batch whose block
+ * tables and lengths stay on the device, which also moves each row forward
+ * as the host block manager's append does ("PagedAttention: Virtual Memory
+ * for the KV Cache", sections 3 and 16: position S of a sequence lives in
+ * logical block S / B at offset S % B).  For row n with slot = slot_mapping[n]
+ * and S = context_lens[n] before the call:
+ *
+ *     K, V of token n written at `slot` (as pa_append_kv)
+ *     block_tables[n][S / B] = slot / B;  context_lens[n] = S + 1
+ *
+ * so the device batch equals what pa_bm_build_batch returns after the same
+ * pa_bm_append_slots, without uploading the tables again.
+ *
+ *   k_new, v_new   [num_seqs][Hkv][d_head], element type `dtype`
+ *   slot_mapping   int32 [num_seqs], device; slot < 0 or at or beyond
+ *                  num_blocks * block_size skips the row entirely
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq], device, updated
+ *   context_lens   int32 [num_seqs], device, updated
+ * A row whose slot does not sit at its next position (slot % B != S % B,
+ * S < 0 or S / B >= max_blocks_per_seq) keeps its table and length; its
+ * key and value are still written.  Slots must be distinct within one call.
+ */
+int pa_append_step(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                   const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                   int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size,
+                   int num_blocks, int dtype, void* stream);
 
 /* ---- copy-on-write block copy ------------------------------------------------
  *

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     lib,
     pa_append_kv,
     pa_append_kv_args,
+    pa_append_step,
+    pa_append_step_args,
     pa_copy_blocks,
     pa_copy_blocks_args,
     pa_decode,

@@ -31,7 +31,7 @@ PA_BF16 = 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libpa.so not found at {LIB_PATH}; build it with "
-                      f"`python -m paged_kv_cache_124_amd.build`")
+                      f"`python paged_kv_cache_124_amd/build.py`")
 lib = ctypes.CDLL(LIB_PATH)
 
 
@@ -60,6 +60,8 @@ _SIGS = {
     "pa_decode_partition_tokens": (c_int, [c_int] * 7),
     "pa_append_kv": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                              c_int, c_void_p]),
+    "pa_append_step": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                               c_int, c_int, c_int, c_int, c_int, c_void_p]),
     "pa_copy_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int64,
                                c_int, c_void_p]),
     "pa_bm_create": (c_void_p, [c_int, c_int, _P32]),
@@ -204,6 +206,35 @@ def pa_append_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
     """pa_append_kv of include/pa.h: k_new/v_new [T][Hkv][D], slot_mapping int32 [T]."""
     _check(lib.pa_append_kv(*pa_append_kv_args(k_pool, v_pool, k_new, v_new, slot_mapping, stream)),
            "pa_append_kv")
+
+
+def pa_append_step_args(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables, context_lens, stream=None):
+    """Validate once and return the argument tuple for repeated ``lib.pa_append_step(*args)`` calls."""
+    import torch
+    nb, hkv, d, bs = _pool_dims(k_pool, v_pool)
+    n = k_new.shape[0]
+    if tuple(k_new.shape) != (n, hkv, d) or tuple(v_new.shape) != (n, hkv, d):
+        raise ValueError("k_new / v_new must be [N][Hkv][D]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new / v_new must have the pool's element type")
+    for t, name in ((slot_mapping, "slot_mapping"), (block_tables, "block_tables"), (context_lens, "context_lens")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if tuple(slot_mapping.shape) != (n,) or tuple(context_lens.shape) != (n,):
+        raise ValueError("slot_mapping and context_lens must be [N]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n:
+        raise ValueError("block_tables must be [N][max_blocks]")
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+            _dev(slot_mapping, "slot_mapping"), _dev(block_tables, "block_tables"),
+            _dev(context_lens, "context_lens"), n, block_tables.shape[1], hkv, d, bs, nb, _dtype_code(k_pool),
+            _stream_ptr(stream))
+
+
+def pa_append_step(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables, context_lens, stream=None):
+    """pa_append_step of include/pa.h: append row n's token at slot_mapping[n] and advance
+    block_tables[n] / context_lens[n] (device tensors, updated in place)."""
+    _check(lib.pa_append_step(*pa_append_step_args(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
+                                                   context_lens, stream)), "pa_append_step")
 
 
 def pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream=None):

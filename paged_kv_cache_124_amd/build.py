@@ -1,6 +1,8 @@
 """Build libpa.so (HIP kernels for gfx950 + C ABI + host block manager) in-tree.
 
-    python -m paged_kv_cache_124_amd.build
+    python paged_kv_cache_124_amd/build.py
+
+(run as a file: importing the package loads the library this builds)
 
 Produces ``paged_kv_cache_124_amd/libpa.so``.  hipcc cross-compiles gfx950
 code objects without a GPU, so this runs on any machine with ROCm.

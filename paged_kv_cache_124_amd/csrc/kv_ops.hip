@@ -50,6 +50,55 @@ __global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ k_pool, 
   for (int e = 0; e < X; ++e) vdst[static_cast<int64_t>(e) * block_size] = vals[e];
 }
 
+// One decode step's append for a batch whose block tables and lengths stay
+// resident on the device: token n belongs to sequence row n.  Threads as in
+// append_kv_kernel; the thread of (n, head 0, chunk 0) also moves the row
+// forward -- block_tables[n][S / B] = slot / B and context_lens[n] = S + 1,
+// S being the row's length before the step -- which is what the host block
+// manager's table and length become after the same append (the slot's block
+// is the table entry of position S, whether the block was in place, fresh
+// or a copy-on-write destination).  Only that thread touches the row, so the
+// key / value writers never read a length being changed.
+template <typename T>
+__global__ __launch_bounds__(256) void append_step_kernel(T* __restrict__ k_pool, T* __restrict__ v_pool,
+                                                          const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                                          const int32_t* __restrict__ slot_mapping,
+                                                          int32_t* __restrict__ block_tables,
+                                                          int32_t* __restrict__ context_lens, int num_seqs,
+                                                          int max_blocks, int hkv, int d, int block_size,
+                                                          int64_t num_slots) {
+  constexpr int X = 16 / static_cast<int>(sizeof(T));
+  const int chunks = d / X;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;
+  const int j = static_cast<int>(th % hkv);
+  const int64_t n = th / hkv;
+  if (n >= num_seqs) return;
+  const int64_t slot = slot_mapping[n];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t pb = slot / block_size;
+  const int off = static_cast<int>(slot % block_size);
+  if (j == 0 && c == 0) {
+    const int pos = context_lens[n];
+    // a slot that does not sit at the row's next position leaves the row as it is
+    if (pos >= 0 && pos / block_size < max_blocks && pos % block_size == off) {
+      block_tables[n * max_blocks + pos / block_size] = static_cast<int32_t>(pb);
+      context_lens[n] = pos + 1;
+    }
+  }
+  const int64_t src = (n * hkv + j) * d + static_cast<int64_t>(c) * X;
+  const int64_t head = pb * hkv + j;
+  const uint4 kc = *reinterpret_cast<const uint4*>(k_new + src);
+  *reinterpret_cast<uint4*>(k_pool + ((head * chunks + c) * block_size + off) * X) = kc;
+  const uint4 vc = *reinterpret_cast<const uint4*>(v_new + src);
+  T vals[X];
+  __builtin_memcpy(vals, &vc, 16);
+  T* vdst = v_pool + (head * d + static_cast<int64_t>(c) * X) * block_size + off;
+#pragma unroll
+  for (int e = 0; e < X; ++e) vdst[static_cast<int64_t>(e) * block_size] = vals[e];
+}
+
 // grid = (ceil(2 * n16 / 256), num_pairs, num_layers); each thread moves 16 bytes.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                           const int32_t* __restrict__ pairs, int64_t block_bytes,
@@ -98,6 +147,38 @@ extern "C" int pa_append_kv(void* k_pool, void* v_pool, const void* k_new, const
     append_kv_kernel<float><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s>>>(
         static_cast<float*>(k_pool), static_cast<float*>(v_pool), static_cast<const float*>(k_new),
         static_cast<const float*>(v_new), slot_mapping, num_tokens, Hkv, d_head, block_size, num_slots);
+  }
+  return launch_status();
+}
+
+extern "C" int pa_append_step(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                              const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                              int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size,
+                              int num_blocks, int dtype, void* stream) {
+  using namespace pa;
+  if (num_seqs < 0 || num_blocks < 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (!shape_ok(Hkv, d_head, block_size, dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  const int x = 16 / elem_bytes(dtype);
+  const int64_t threads = static_cast<int64_t>(num_seqs) * Hkv * (d_head / x);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PA_BF16) {
+    append_step_kernel<uint16_t><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s>>>(
+        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), static_cast<const uint16_t*>(k_new),
+        static_cast<const uint16_t*>(v_new), slot_mapping, block_tables, context_lens, num_seqs,
+        max_blocks_per_seq, Hkv, d_head, block_size, num_slots);
+  } else {
+    append_step_kernel<float><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s>>>(
+        static_cast<float*>(k_pool), static_cast<float*>(v_pool), static_cast<const float*>(k_new),
+        static_cast<const float*>(v_new), slot_mapping, block_tables, context_lens, num_seqs,
+        max_blocks_per_seq, Hkv, d_head, block_size, num_slots);
   }
   return launch_status();
 }

@@ -106,3 +106,86 @@ def test_copy_then_append_matches_oracle_cow_step():
     assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
     # the shared prefix (blocks 0, 1) and B's tail (block 2) hold the prompt; A's tail (3) is a copy + new token
     assert np.array_equal(gk[3, :, :3], k0[2, :, :3])
+
+
+@pytest.mark.parametrize("dtype,d,bs", [(torch.bfloat16, 128, 16), (torch.bfloat16, 64, 8), (torch.float32, 64, 32)])
+def test_append_step_tracks_block_manager(dtype, d, bs):
+    """Decode steps with device-resident tables: copy-on-write pairs, then pa_append_step.
+
+    After every step the device tables and lengths equal the block manager's
+    build_batch bit for bit, and the pools equal the oracle's copy + append
+    applied to the previous pools.  Prompts of 2B + 7 tokens are forked into 3
+    samples each (shared unaligned tails -> copy-on-write on the first step);
+    the steps cross block boundaries; one step leaves a row out (slot -1).
+    """
+    import paged_kv_cache_124_amd as pa
+    from oracle.block_manager import BlockManagerModel
+    print(f"[case] append_step dtype={dtype} d={d} bs={bs}", flush=True)
+    hkv, prompts, samples, steps = 2, 4, 3, 2 * bs + 3
+    n = prompts * samples
+    nb = n * (-(-(2 * bs + 7 + steps) // bs)) + 8
+    mb = -(-(2 * bs + 7 + steps) // bs)
+    k, v = _pools(nb, hkv, d, bs, dtype, 61)
+    order = synth.pop_order(nb, 7)
+    bm = pa.BlockManager(nb, bs, order)
+    model = BlockManagerModel(nb, bs, [int(x) for x in order])
+    for x in (bm, model):
+        for p in range(prompts):
+            assert x.add_seq(p * samples, 2 * bs + 7) == 0
+            for s_ in range(1, samples):
+                assert x.fork(p * samples, p * samples + s_) == 0
+    seqs = list(range(n))
+    st, tables, lens = bm.build_batch(seqs, mb)
+    assert st == 0
+    d_tables = torch.from_numpy(tables).cuda()
+    d_lens = torch.from_numpy(lens).cuda()
+    view = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    ek, ev = _logical_np(k, v)
+    skip_step, skip_row = 5, 4
+    for step in range(steps):
+        active = [s_ for s_ in seqs if not (step == skip_step and s_ == skip_row)]
+        st, slots, pairs, _ = bm.append_slots(active)
+        mst, mslots, mpairs, _ = model.append_slots(active)
+        assert st == mst == 0 and list(slots) == mslots and [tuple(p) for p in pairs] == mpairs
+        row_slots = np.full(n, -1, dtype=np.int32)
+        row_slots[active] = slots
+        if len(pairs):
+            pa.pa_copy_blocks(k, v, torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda())
+        kn = synth.randn((n, hkv, d), dtype, 1.0, 1000 + step, "cuda")
+        vn = synth.randn((n, hkv, d), dtype, 1.0, 2000 + step, "cuda")
+        pa.pa_append_step(k, v, kn, vn, torch.from_numpy(row_slots).cuda(), d_tables, d_lens)
+        torch.cuda.synchronize()
+        st, tables, lens = bm.build_batch(seqs, mb)
+        assert st == 0
+        assert np.array_equal(d_tables.cpu().numpy(), tables), f"tables differ after step {step}"
+        assert np.array_equal(d_lens.cpu().numpy(), lens), f"lengths differ after step {step}"
+        assert model.build_batch(seqs, mb)[1] == tables.tolist()
+        OA.copy_blocks(ek, ev, mpairs)
+        OA.append_kv(ek, ev, kn.cpu().contiguous().view(view).numpy(), vn.cpu().contiguous().view(view).numpy(),
+                     list(row_slots))
+        gk, gv = _logical_np(k, v)
+        assert np.array_equal(gk, ek) and np.array_equal(gv, ev), f"pools differ after step {step}"
+    assert model.stats()["cow_copies"] == prompts * (samples - 1)
+
+
+def test_append_step_leaves_inconsistent_rows():
+    """A slot that is not at the row's next position writes K/V but keeps the row's table and length."""
+    import paged_kv_cache_124_amd as pa
+    print("[case] append_step inconsistent rows", flush=True)
+    nb, hkv, d, bs = 12, 1, 64, 16
+    k, v = _pools(nb, hkv, d, bs, torch.bfloat16, 71)
+    tables = torch.tensor([[3, 0], [5, 0], [7, 8]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([16, 10, 32], dtype=torch.int32, device="cuda")
+    # row 0: next position 16 -> block 1 of the row, offset 0: slot 9 * 16 is consistent
+    # row 1: offset should be 10, slot has offset 3; row 2: position 32 is beyond max_blocks = 2
+    slots = torch.tensor([9 * bs, 5 * bs + 3, 10 * bs], dtype=torch.int32, device="cuda")
+    kn = synth.randn((3, hkv, d), torch.bfloat16, 1.0, 72, "cuda")
+    vn = synth.randn((3, hkv, d), torch.bfloat16, 1.0, 73, "cuda")
+    k0, v0 = _logical_np(k, v)
+    pa.pa_append_step(k, v, kn, vn, slots, tables, lens)
+    torch.cuda.synchronize()
+    assert tables.cpu().tolist() == [[3, 9], [5, 0], [7, 8]]
+    assert lens.cpu().tolist() == [17, 10, 32]
+    OA.append_kv(k0, v0, kn.cpu().view(torch.int16).numpy(), vn.cpu().view(torch.int16).numpy(), slots.cpu().tolist())
+    gk, gv = _logical_np(k, v)
+    assert np.array_equal(gk, k0) and np.array_equal(gv, v0)
