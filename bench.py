@@ -35,6 +35,34 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved HBM GB/s (KV read) + µs/step, 8B GQA shape"
 HBM_PEAK_GBS = 8000.0
+EVENT_EVERY = 4
+
+
+# HBM traffic of the decode kernels, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a
+# plain copy of known size; valid only while the kernel sources are those it was taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_gqa8b_traffic.txt")
+KERNEL_SOURCES = ["decode_stream.hip", "decode_stream.h", "decode.hip", "common.h"]
+
+
+def measured_traffic(workload_name):
+    """(fetched + written bytes per pa_decode launch, algorithmic bytes of those launches), or None."""
+    import hashlib
+    if workload_name != "gqa8b" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_124_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if kv.get("sources_sha256") != h.hexdigest():
+        return None
+    total = sum(float(kv[k]) for k in ("fetch_bytes_per_launch", "write_bytes_per_launch",
+                                       "merge_fetch_bytes_per_launch", "merge_write_bytes_per_launch"))
+    return total, float(kv["algorithmic_bytes_per_launch"])
 
 
 def parse():
@@ -134,7 +162,6 @@ class Runner:
         self.step_i = 0
         self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
         self.lens_sum = sum(self.lens0)
-        self.timing_events = []
         self.host_s = 0.0
 
     def step(self, timing=None):
@@ -244,15 +271,21 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    timing = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # pa_decode is bracketed by events on every EVENT_EVERY-th step (on the stream it is
+    # launched on); a pair of event records costs the step a few microseconds
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    timing = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     torch.cuda.synchronize()
     run.host_s = 0.0
     t0 = time.perf_counter()
     e0.record()
-    kv_bytes = 0
+    kv_bytes, sampled_bytes = 0, 0
     for i in range(args.steps):
-        kv_bytes += run.step(timing[i])
+        ev = timing.get(i)
+        step_bytes = run.step(ev)
+        kv_bytes += step_bytes
+        if ev is not None:
+            sampled_bytes += step_bytes
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -260,10 +293,11 @@ def main():
     gpu_ms = e0.elapsed_time(e1)
     ms_step = max(gpu_ms, wall * 1e3) / args.steps
     value = kv_bytes / args.steps / (ms_step * 1e-3) / 1e9
-    dec_ms = [a.elapsed_time(b) for a, b in timing]
-    dec_avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
+    dec_us = [1e3 * a.elapsed_time(b) for a, b in timing.values()]
+    dec_avg_us = sum(dec_us) / len(dec_us)
     bytes_per_launch = kv_bytes / args.steps
-    achieved = bytes_per_launch / (dec_avg_us * 1e-6) / 1e9
+    achieved = sampled_bytes / (sum(dec_us) * 1e-6) / 1e9
+    traffic = measured_traffic(w.name)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -284,8 +318,10 @@ def main():
                    "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2),
                    "host_us_per_step": round(run.host_s / args.steps * 1e6, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pa_decode (decode kernel + merge)", "avg_us": round(dec_avg_us, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
+                     "traffic_algorithmic": None if traffic is None else int(traffic[1]),
+                     "kernel": "pa_decode (decode kernel + merge)", "avg_us": round(dec_avg_us, 2),
+                     "launches_timed": len(dec_us)},
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
