@@ -123,3 +123,34 @@ def test_short_lengths_with_large_launch_bound():
     out = run_decode(c, tables_dev=torch.from_numpy(tables).cuda(), max_ctx=4096)
     ref = oracle_outputs(c, range(3))
     assert_close(out, ref, "short lengths, launch bound 4096")
+
+
+def test_partitioned_path_gqa8b_and_edges(monkeypatch):
+    """The partitioned bf16 kernel + merge (the path for very large batches), forced on the 8B GQA layer and edge lengths."""
+    import paged_kv_cache_124_amd as pa
+    monkeypatch.setenv("PA_DECODE_PATH", "partition")
+    print("[case] partitioned gqa8b", flush=True)
+    c = make_case(synth.gqa8b())
+    assert pa.pa_decode_partition_tokens(len(c.lens), c.hq, c.hkv, c.d, c.block_size, c.max_ctx, pa.PA_BF16) > 0
+    out = run_decode(c)
+    assert_close(out, oracle_outputs(c, range(len(c.lens))), "partitioned gqa8b")
+    for bs in (8, 16, 32):
+        e = make_case(synth.gqa8b(), EDGE_LENS, block_size=bs, seed=800 + bs)
+        out = run_decode(e)
+        assert torch.count_nonzero(out[0].float()) == 0
+        assert_close(out, oracle_outputs(e, range(len(EDGE_LENS))), f"partitioned edges bs={bs}")
+
+
+def test_many_sequences_take_partitioned_path():
+    """More sequences than the persistent kernel's per-launch limit (3072): the partitioned kernel serves them."""
+    import paged_kv_cache_124_amd as pa
+    rng = np.random.default_rng(12)
+    lens = [int(x) for x in rng.integers(0, 400, size=3100)]
+    print("[case] 3100 sequences", flush=True)
+    c = make_case(synth.gqa8b(), lens, seed=900)
+    assert pa.pa_decode_partition_tokens(len(lens), c.hq, c.hkv, c.d, c.block_size, c.max_ctx, pa.PA_BF16) > 0
+    out = run_decode(c)
+    sample = sorted(set(rng.choice(len(lens), size=48, replace=False).tolist()) | {0, len(lens) - 1})
+    assert_close(out[sample], oracle_outputs(c, sample), "3100 sequences")
+    zero = [i for i, s in enumerate(lens) if s == 0]
+    assert zero and torch.count_nonzero(out[zero].float()) == 0
