@@ -4,7 +4,8 @@
 A step is one pass of the whole decode-step path over a batch of sequences:
   1. host block manager: one batch append (slot per sequence, copy-on-write
      pairs);
-  2. one host-to-device copy of the slots and pairs (pinned staging);
+  2. the slots and pairs reach the GPU through pinned host memory that the
+     kernels read directly (a ring of buffers);
   3. pa_copy_blocks (when the batch produced copy-on-write pairs);
   4. pa_append_step: the new token of every sequence, and the device-resident
      block tables and lengths moved forward as the block manager's were;
@@ -35,7 +36,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved HBM GB/s (KV read) + µs/step, 8B GQA shape"
 HBM_PEAK_GBS = 8000.0
-EVENT_EVERY = 4
+EVENT_EVERY = 10
+RING = 32
 
 
 # HBM traffic of the decode kernels, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a
@@ -127,38 +129,52 @@ class Runner:
         assert st == 0
         self.d_tables = torch.from_numpy(tables).to(device)
         self.d_lens = torch.from_numpy(lens).to(device)
-        # Host staging [slots N | pairs 2N] in pinned memory, two of each (ping-pong, so the
-        # host fills one while the other uploads), and the matching device buffers.  The
-        # block manager writes straight into the staging buffer.
-        self.words = 3 * n
-        self.host = [torch.empty(self.words, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.dev = [torch.empty(self.words, dtype=torch.int32, device=device) for _ in range(2)]
-        self.host_ev = [torch.cuda.Event(), torch.cuda.Event()]
-        self.host_used = [False, False]
-        self.replicas = replicas
-        # pre-marshalled C calls per (replica, staging buffer)
+        # Host staging: a ring of RING pinned buffers [slots N | pairs 2N].  The block
+        # manager writes a step's slots and copy-on-write pairs straight into one of them
+        # and the kernels read them there through the buffer's device mapping, so a step
+        # has no copy and no event of its own.  One event per half ring tells the host
+        # when the GPU is done with a half before it is written again.  Where pinned
+        # memory has no device mapping, the buffer is uploaded in-stream instead.
         import ctypes
         self.ct = ctypes
+        self.words = 3 * n
+        self.ring = RING
+        self.host = [torch.empty(self.words, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+        hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded
+        self.mapped = []
+        for hb in self.host:
+            dp = ctypes.c_void_p()
+            ok = hip.hipHostGetDevicePointer(ctypes.byref(dp), ctypes.c_void_p(hb.data_ptr()), 0) == 0
+            self.mapped.append(dp.value if ok and dp.value else None)
+        self.zero_copy = all(m is not None for m in self.mapped)
+        self.dev = None if self.zero_copy else [torch.empty(self.words, dtype=torch.int32, device=device)
+                                                for _ in range(RING)]
+        self.half_ev = [torch.cuda.Event(), torch.cuda.Event()]
+        self.half_used = [False, False]
+        self.replicas = replicas
+        # pre-marshalled C calls per (replica, ring buffer)
         L = pa.lib
         self.lib = L
         self.seqs_p = self.seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
         p32 = ctypes.POINTER(ctypes.c_int32)
         self.npairs = ctypes.c_int()
         self.append_slots_args = []
-        for b in range(2):
+        for b in range(RING):
             base = self.host[b].data_ptr()
             self.append_slots_args.append((self.bm.handle, self.seqs_p, n, ctypes.cast(base, p32),
                                            ctypes.cast(base + 4 * n, p32), ctypes.byref(self.npairs)))
+        check = torch.empty(self.words, dtype=torch.int32, device=device)  # shapes for validation only
         self.dec_args, self.app_args, self.copy_args = {}, {}, {}
         for r in range(replicas):
             self.dec_args[r], _ = pa.pa_decode_args(self.out, self.q, self.k[r], self.v[r], self.d_tables,
                                                     self.d_lens, w.scale, self.max_ctx, workspace=self.ws)
-            for b in range(2):
-                d = self.dev[b]
-                self.app_args[r, b] = pa.pa_append_step_args(self.k[r], self.v[r], self.k_new, self.v_new, d[:n],
-                                                             self.d_tables, self.d_lens)
-                self.copy_args[r, b] = list(pa.pa_copy_blocks_args(self.k[r], self.v[r],
-                                                                   d[n:3 * n].view(n, 2)))
+            app = pa.pa_append_step_args(self.k[r], self.v[r], self.k_new, self.v_new, check[:n],
+                                         self.d_tables, self.d_lens)
+            cpy = pa.pa_copy_blocks_args(self.k[r], self.v[r], check[n:3 * n].view(n, 2))
+            for b in range(RING):
+                base = self.mapped[b] if self.zero_copy else self.dev[b].data_ptr()
+                self.app_args[r, b] = app[:4] + (ctypes.c_void_p(base),) + app[5:]
+                self.copy_args[r, b] = list(cpy[:2]) + [ctypes.c_void_p(base + 4 * n)] + list(cpy[3:])
         self.step_i = 0
         self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
         self.lens_sum = sum(self.lens0)
@@ -167,23 +183,26 @@ class Runner:
     def step(self, timing=None):
         t_host = time.perf_counter()
         L = self.lib
-        b = self.step_i & 1
-        if self.host_used[b]:
-            self.host_ev[b].synchronize()  # the upload from host[b] two steps ago has been read
-        st = L.pa_bm_append_slots(*self.append_slots_args[b])
+        k = self.step_i % self.ring
+        half = RING // 2
+        if k % half == 0 and self.half_used[k // half]:
+            self.half_ev[k // half].synchronize()  # the GPU is done with this half of the ring
+        st = L.pa_bm_append_slots(*self.append_slots_args[k])
         if st != 0:
             raise RuntimeError(f"block manager append failed: status {st}")
         npairs = self.npairs.value
-        words = self.n + 2 * npairs
-        self.dev[b][:words].copy_(self.host[b][:words], non_blocking=True)
-        self.host_ev[b].record()
-        self.host_used[b] = True
+        if not self.zero_copy:
+            words = self.n + 2 * npairs
+            self.dev[k][:words].copy_(self.host[k][:words], non_blocking=True)
         r = self.step_i % self.replicas
         if npairs:
-            ca = self.copy_args[r, b]
+            ca = self.copy_args[r, k]
             ca[3] = npairs
             assert L.pa_copy_blocks(*ca) == 0
-        assert L.pa_append_step(*self.app_args[r, b]) == 0
+        assert L.pa_append_step(*self.app_args[r, k]) == 0
+        if k % half == half - 1:
+            self.half_ev[k // half].record()
+            self.half_used[k // half] = True
         if timing is not None:
             timing[0].record()
         assert L.pa_decode(*self.dec_args[r]) == 0
@@ -193,7 +212,6 @@ class Runner:
         self.lens_sum += self.n
         self.host_s += time.perf_counter() - t_host
         return self.lens_sum * self.kv_bytes_per_token
-
 
     def check_device_batch(self):
         """The device tables and lengths still equal the block manager's (after the timed steps)."""
@@ -272,7 +290,8 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # pa_decode is bracketed by events on every EVENT_EVERY-th step (on the stream it is
-    # launched on); a pair of event records costs the step a few microseconds
+    # launched on); an event record costs the stream a few microseconds, so not every
+    # step carries them
     sampled = list(range(0, args.steps, EVENT_EVERY))
     timing = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     torch.cuda.synchronize()
@@ -316,7 +335,8 @@ def main():
                    "num_seqs": run.n, "block_size": w.block_size, "pool_blocks": run.num_blocks,
                    "pool_replicas": args.replicas, "partition_tokens": run.part,
                    "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2),
-                   "host_us_per_step": round(run.host_s / args.steps * 1e6, 2)},
+                   "host_us_per_step": round(run.host_s / args.steps * 1e6, 2),
+                   "staging": "pinned host ring read by the kernels" if run.zero_copy else "pinned ring, in-stream copy"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),

@@ -29,6 +29,10 @@ PA_ERR_HIP = 7
 PA_F32 = 0
 PA_BF16 = 1
 
+# torch first: libpa.so then binds to the HIP runtime torch has loaded, so
+# torch's streams and device memory are valid in the library's calls.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libpa.so not found at {LIB_PATH}; build it with "
                       f"`python paged_kv_cache_124_amd/build.py`")

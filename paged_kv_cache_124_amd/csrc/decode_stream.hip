@@ -192,7 +192,10 @@ __device__ __forceinline__ void read_tile(Buf<D>& b, const unsigned char* stage,
       else
         b.v1[mm] = v;
     }
-    const int pv = tb.blk[tv / B];
+    int pv = tb.blk[0];  // tb.blk[tv / B] by selects: a lane-dependent index would put tb in scratch
+#pragma unroll
+    for (int i = 1; i < 32 / B; ++i)
+      if (tv / B == i) pv = tb.blk[i];
     const bool ok = pv >= 0 && pv < num_blocks;
     if (a == 0)
       b.blk0 = ok;
@@ -415,6 +418,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const TilePos nxt2 = x + 2 < x1 ? advance(nxt, s_pre, hkv) : nxt;
     Buf<D> b;
     read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
+    // keep the stage's LDS reads ahead of the copies below: an LDS read issued
+    // after them would wait for all of them
+    __builtin_amdgcn_sched_barrier(0);
     tb2 = load_tb<B>(nxt2, block_tables, max_blocks, s_len);
     load_q<D>(qn, nxt, q, hq, g, r, gq);
     dma_tile<D, B>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
@@ -492,14 +498,25 @@ __global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ re
       const float* rr = record(base + lane, h);
       const float f = rr ? __builtin_amdgcn_exp2f(rr[0] - mx) : 0.f;
       if (rr) zz += f * rr[1];
+      // value rows in batches of 8 records, their loads issued together
       const int cnt = static_cast<int>(min<int64_t>(64, v_hi - base + 1));
-      for (int kk = 0; kk < cnt; ++kk) {
-        const float fk = __shfl(f, kk);
-        const float* rk = record(base + kk, h);
-        if (rk) {
+      for (int k0 = 0; k0 < cnt; k0 += 8) {
+        float val[8][E];
+        float fk[8];
 #pragma unroll
-          for (int e = 0; e < E; ++e) uu[e] += fk * rk[4 + lane + 64 * e];
+        for (int i = 0; i < 8; ++i) {
+          const int k = k0 + i;
+          const float* rk = k < cnt ? record(base + k, h) : nullptr;
+          fk[i] = __shfl(f, k & 63);
+          if (!rk) fk[i] = 0.f;
+          rk = rk ? rk : rec;  // any valid address; weighted by zero
+#pragma unroll
+          for (int e = 0; e < E; ++e) val[i][e] = rk[4 + lane + 64 * e];
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < E; ++e) uu[e] += fk[i] * val[i][e];
       }
     }
 #pragma unroll
