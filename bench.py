@@ -7,9 +7,10 @@ A step is one pass of the whole decode-step path over a batch of sequences:
   2. the slots and pairs reach the GPU through pinned host memory that the
      kernels read directly (a ring of buffers);
   3. pa_copy_blocks (when the batch produced copy-on-write pairs);
-  4. pa_append_step: the new token of every sequence, and the device-resident
-     block tables and lengths moved forward as the block manager's were;
-  5. pa_decode over every sequence's context (pieces + merge).
+  4. pa_decode_step: attention of every sequence over its context and its new
+     token (taken from k_new / v_new), then the new token stored at its slot
+     and the device-resident block tables and lengths moved forward as the
+     block manager's were (decode kernel, then merge + append kernel).
 The block tables and lengths are uploaded once, before the timed region, and
 from then on follow the block manager through step 4.
 Contexts grow by one token per step.  Inputs are resident in HBM before the
@@ -164,16 +165,14 @@ class Runner:
             self.append_slots_args.append((self.bm.handle, self.seqs_p, n, ctypes.cast(base, p32),
                                            ctypes.cast(base + 4 * n, p32), ctypes.byref(self.npairs)))
         check = torch.empty(self.words, dtype=torch.int32, device=device)  # shapes for validation only
-        self.dec_args, self.app_args, self.copy_args = {}, {}, {}
+        self.step_args, self.copy_args = {}, {}
         for r in range(replicas):
-            self.dec_args[r], _ = pa.pa_decode_args(self.out, self.q, self.k[r], self.v[r], self.d_tables,
-                                                    self.d_lens, w.scale, self.max_ctx, workspace=self.ws)
-            app = pa.pa_append_step_args(self.k[r], self.v[r], self.k_new, self.v_new, check[:n],
-                                         self.d_tables, self.d_lens)
             cpy = pa.pa_copy_blocks_args(self.k[r], self.v[r], check[n:3 * n].view(n, 2))
             for b in range(RING):
                 base = self.mapped[b] if self.zero_copy else self.dev[b].data_ptr()
-                self.app_args[r, b] = app[:4] + (ctypes.c_void_p(base),) + app[5:]
+                self.step_args[r, b], _ = pa.pa_decode_step_args(
+                    self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], check[:n], self.d_tables,
+                    self.d_lens, w.scale, self.max_ctx, workspace=self.ws, slot_pointer=base)
                 self.copy_args[r, b] = list(cpy[:2]) + [ctypes.c_void_p(base + 4 * n)] + list(cpy[3:])
         self.step_i = 0
         self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
@@ -199,15 +198,14 @@ class Runner:
             ca = self.copy_args[r, k]
             ca[3] = npairs
             assert L.pa_copy_blocks(*ca) == 0
-        assert L.pa_append_step(*self.app_args[r, k]) == 0
+        if timing is not None:
+            timing[0].record()
+        assert L.pa_decode_step(*self.step_args[r, k]) == 0
+        if timing is not None:
+            timing[1].record()
         if k % half == half - 1:
             self.half_ev[k // half].record()
             self.half_used[k // half] = True
-        if timing is not None:
-            timing[0].record()
-        assert L.pa_decode(*self.dec_args[r]) == 0
-        if timing is not None:
-            timing[1].record()
         self.step_i += 1
         self.lens_sum += self.n
         self.host_s += time.perf_counter() - t_host
@@ -340,7 +338,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),
-                     "kernel": "pa_decode (decode kernel + merge)", "avg_us": round(dec_avg_us, 2),
+                     "kernel": "pa_decode_step (decode kernel + merge/append kernel)", "avg_us": round(dec_avg_us, 2),
                      "launches_timed": len(dec_us)},
     }
     if not args.no_cpu_baseline:

@@ -121,6 +121,40 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode_step: one whole decode step of the batch.  Each row attends to
+ * its S cached tokens and to its new token (key and value from k_new / v_new,
+ * at position S); then the new token is stored and the row moved forward
+ * exactly as pa_append_step does ("PagedAttention: Virtual Memory for the KV
+ * Cache", sections 13 and 16; "PagedAttention in vLLM: scattered memory,
+ * exact attention", sections 10-11).  The attention takes the new token from
+ * k_new / v_new, so its store does not have to finish first.  For row n with
+ * S = context_lens[n] on entry and slot = slot_mapping[n]:
+ *
+ *     out[n] = attention of q[n] over the S cached tokens and the new token;
+ *     when slot is the row's next position -- inside the pool, slot % B ==
+ *     S % B and S / B < max_blocks_per_seq -- the new token's K/V are
+ *     stored at slot, block_tables[n][S / B] = slot / B and
+ *     context_lens[n] = S + 1; otherwise nothing is stored or changed.
+ *
+ * Where every row's slot is its next position this is, bit for bit,
+ * pa_append_step followed by pa_decode.
+ *
+ *   k_new, v_new   [num_seqs][Hkv][d_head], element type `dtype`, device
+ *   slot_mapping   int32 [num_seqs]; device-readable (device memory, or
+ *                  pinned host memory mapped for the device)
+ *   block_tables, context_lens   as for pa_decode, updated in place
+ *   max_context_len an upper bound of S + 1
+ * Other arguments, the workspace (pa_decode_workspace_bytes) and the errors
+ * as for pa_decode.  Served for bf16, Hq / Hkv <= 16, num_seqs <= 3072 (the
+ * persistent kernel); other shapes return PA_ERR_UNSUPPORTED and take
+ * pa_append_step + pa_decode.
+ */
+int pa_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                   const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens, int num_seqs,
+                   int Hq, int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq,
+                   int max_context_len, int num_blocks, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Workspace bytes pa_decode needs for these sizes on the current device
  * (0 when no split is used). */
 size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,

@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     pa_decode,
     pa_decode_args,
     pa_decode_partition_tokens,
+    pa_decode_step,
+    pa_decode_step_args,
     pa_decode_workspace_bytes,
     pool_shapes,
 )

@@ -60,6 +60,7 @@ _SIGS = {
     "pa_version": (c_int, []),
     "pa_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                           c_int, c_float, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "pa_decode_step": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_workspace_bytes": (c_size_t, [c_int] * 7),
     "pa_decode_partition_tokens": (c_int, [c_int] * 7),
     "pa_append_kv": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
@@ -188,6 +189,52 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
     args, _ws = pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
                                workspace, stream)
     _check(lib.pa_decode(*args), "pa_decode")
+    return out
+
+
+def pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens, scale,
+                        max_context_len, workspace=None, stream=None, slot_pointer=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode_step(*args)`` calls.
+
+    ``slot_pointer`` (an int) replaces slot_mapping's data pointer, e.g. with the
+    device mapping of a pinned host buffer of the same shape.
+    """
+    import torch
+    n, hq, d = q.shape
+    nb, hkv, d2, bs = _pool_dims(k_pool, v_pool)
+    if d2 != d or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or k_pool.dtype != q.dtype:
+        raise ValueError("q, out and the pools disagree in shape or dtype")
+    if tuple(k_new.shape) != (n, hkv, d) or tuple(v_new.shape) != (n, hkv, d):
+        raise ValueError("k_new / v_new must be [N][Hkv][D]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError("k_new / v_new must have q's element type")
+    for t, name in ((slot_mapping, "slot_mapping"), (block_tables, "block_tables"), (context_lens, "context_lens")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if tuple(slot_mapping.shape) != (n,) or tuple(context_lens.shape) != (n,):
+        raise ValueError("slot_mapping and context_lens must be [N]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n:
+        raise ValueError("block_tables must be [N][max_blocks]")
+    dt = _dtype_code(q)
+    need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, dt)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
+    ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    slots = c_void_p(slot_pointer) if slot_pointer is not None else _dev(slot_mapping, "slot_mapping")
+    args = (_dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_pool, "k_pool"),
+            _dev(v_pool, "v_pool"), slots, _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+            n, hq, hkv, d, bs, float(scale), block_tables.shape[1], int(max_context_len), nb, dt, ws_ptr, ws_bytes,
+            _stream_ptr(stream))
+    return args, workspace
+
+
+def pa_decode_step(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens, scale,
+                   max_context_len, workspace=None, stream=None):
+    """pa_decode_step of include/pa.h: store each row's new token, advance the rows, and decode with it."""
+    args, _ws = pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens,
+                                    scale, max_context_len, workspace, stream)
+    _check(lib.pa_decode_step(*args), "pa_decode_step")
     return out
 
 

@@ -485,10 +485,11 @@ extern "C" int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_h
   return pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype).part;
 }
 
-extern "C" int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq, int Hkv,
-                         int d_head, int block_size, float scale, int max_blocks_per_seq, int max_context_len,
-                         int num_blocks, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                const int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream, const pa::StepInputs* step) {
   using namespace pa;
   if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0 || num_blocks < 0)
@@ -510,7 +511,7 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_pool, const voi
     if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
     return launch_stream(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, out,
                          workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq, num_blocks,
-                         scale_log2_s);
+                         scale_log2_s, step);
   }
   const Plan pl = make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
   const size_t need = plan_workspace_bytes(pl, num_seqs, Hq, d_head);
@@ -557,4 +558,30 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_pool, const voi
     else launch_merge<float, 64>(pl, s, ws, context_lens, out, num_seqs, Hq);
   }
   return launch_status();
+}
+}  // namespace
+
+extern "C" int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq, int Hkv,
+                         int d_head, int block_size, float scale, int max_blocks_per_seq, int max_context_len,
+                         int num_blocks, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
+                     scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+extern "C" int pa_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                              void* v_pool, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                              int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                              int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace pa;
+  if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  // served by the persistent bf16 kernel only; other shapes use pa_append_step + pa_decode
+  if (!use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) return PA_ERR_UNSUPPORTED;
+  const StepInputs step{k_new, v_new, slot_mapping};
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
+                     scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes,
+                     stream, &step);
 }

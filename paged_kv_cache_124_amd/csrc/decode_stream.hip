@@ -87,6 +87,63 @@ __device__ __forceinline__ TilePos advance(TilePos t, const int32_t* s_pre, int 
   return t;
 }
 
+// Per sequence the kernel keeps (tokens << 2) | (fits << 1) | new: `tokens`
+// counts the attended tokens, `new` marks that the last of them is the step's
+// new token (taken from k_new / v_new, not from the pool), `fits` that the
+// row's next position is inside its table (so the token may be stored).
+__device__ __forceinline__ int attended_tokens(int packed) { return packed >> 2; }
+__device__ __forceinline__ bool has_new_token(int packed) { return packed & 1; }
+__device__ __forceinline__ bool next_fits(int packed) { return (packed >> 1) & 1; }
+__device__ __forceinline__ int pool_tokens(int packed) { return (packed >> 2) - (packed & 1); }
+
+// The step's new token of one (sequence, KV head) in the lanes' MFMA operand
+// roles: key chunk 4 jj + gq (8 values) and value rows d = 16 mm + r.
+template <int D>
+struct NewTok {
+  bf16x8 k[D / 32];
+  uint32_t v[D / 32];  // value rows 16 mm + r, two per word (even mm low)
+  int slot;            // the row's slot
+};
+
+template <int D>
+__device__ __forceinline__ void load_new(NewTok<D>& nt, TilePos t, const uint16_t* __restrict__ k_new,
+                                         const uint16_t* __restrict__ v_new, const int32_t* __restrict__ slots,
+                                         int hkv, int r, int gq) {
+  const int64_t row = (static_cast<int64_t>(t.n) * hkv + t.j) * D;
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj)
+    nt.k[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k_new + row + (4 * jj + gq) * 8));
+#pragma unroll
+  for (int m2 = 0; m2 < D / 32; ++m2)
+    nt.v[m2] = uint32_t(v_new[row + 32 * m2 + r]) | (uint32_t(v_new[row + 32 * m2 + 16 + r]) << 16);
+  nt.slot = slots[t.n];
+}
+
+// Store the new token at its slot (block slot / B, offset slot % B) in the
+// pool layout: key chunks of 8 values from the lanes of row 0, value rows
+// d = 16 mm + r from the lanes of group 0.  Only when the slot is the row's
+// next position (S % B): its block is then the row's own tail or a block no
+// table reaches yet, read by no other wave, and this wave has read it already.
+template <int D, int B>
+__device__ __forceinline__ void store_new(const NewTok<D>& nt, int j, int S, bool fits,
+                                          uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int hkv,
+                                          int64_t num_slots, int r, int gq) {
+  const int64_t slot = nt.slot;
+  if (!fits || slot < 0 || slot >= num_slots || static_cast<int>(slot % B) != S % B) return;
+  const int64_t head = (slot / B) * hkv + j;
+  const int off = static_cast<int>(slot % B);
+  if (r == 0) {
+#pragma unroll
+    for (int jj = 0; jj < D / 32; ++jj)
+      *reinterpret_cast<bf16x8*>(k_pool + ((head * (D / 8) + 4 * jj + gq) * B + off) * 8) = nt.k[jj];
+  }
+  if (gq == 0) {
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm)
+      v_pool[(head * D + 16 * mm + r) * B + off] = static_cast<uint16_t>(nt.v[mm >> 1] >> (16 * (mm & 1)));
+  }
+}
+
 // Table entries of a tile's blocks.  Always loaded (index clamped into the
 // row) and replaced by -1 past the end of the sequence, so no load sits behind
 // a branch and the compiler can keep the pipeline's loads in flight.
@@ -94,7 +151,7 @@ template <int B>
 __device__ __forceinline__ Tb<B> load_tb(TilePos t, const int32_t* __restrict__ block_tables, int max_blocks,
                                          const int32_t* s_len) {
   const int32_t* row = block_tables + static_cast<int64_t>(t.n) * max_blocks;
-  const int S = s_len[t.n];
+  const int S = pool_tokens(s_len[t.n]);
   const int t0 = t.ti * 32;
   Tb<B> tb;
 #pragma unroll
@@ -202,6 +259,38 @@ __device__ __forceinline__ void read_tile(Buf<D>& b, const unsigned char* stage,
     else
       b.blk1 = ok;
   }
+}
+
+// Put the new token (tile-relative position p) into a staged tile's operands
+// and count its value group as present: its block may not be in the table yet.
+template <int D>
+__device__ __forceinline__ void patch_new(Buf<D>& b, const NewTok<D>& nt, int p, int r, int gq) {
+  // every operand is rewritten with selects: indexing the register arrays by a
+  // run-time slab would move them to scratch
+  const int a = p >> 4;        // slab
+  const int rr = p & 15;       // key row in the slab
+  const int idx = rr & 3;      // token within the lane's value group
+  const bool krow0 = a == 0 && r == rr, krow1 = a == 1 && r == rr;
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj) {
+    b.k[0][jj] = krow0 ? nt.k[jj] : b.k[0][jj];
+    b.k[1][jj] = krow1 ? nt.k[jj] : b.k[1][jj];
+  }
+  const bool grp = gq == (rr >> 2);
+  const bool lo = idx < 2;
+  const int sh = (idx & 1) * 16;
+  const uint32_t keep = ~(0xffffu << sh);
+  const bool g0 = grp && a == 0, g1 = grp && a == 1;
+#pragma unroll
+  for (int mm = 0; mm < D / 16; ++mm) {
+    const uint32_t val = ((nt.v[mm >> 1] >> (16 * (mm & 1))) & 0xffffu) << sh;
+    b.v0[mm].x = g0 && lo ? ((b.v0[mm].x & keep) | val) : b.v0[mm].x;
+    b.v0[mm].y = g0 && !lo ? ((b.v0[mm].y & keep) | val) : b.v0[mm].y;
+    b.v1[mm].x = g1 && lo ? ((b.v1[mm].x & keep) | val) : b.v1[mm].x;
+    b.v1[mm].y = g1 && !lo ? ((b.v1[mm].y & keep) | val) : b.v1[mm].y;
+  }
+  b.blk0 = b.blk0 || g0;
+  b.blk1 = b.blk1 || g1;
 }
 
 // Scores of one 32-token tile on the matrix cores: S^T = K . Q^T.
@@ -322,9 +411,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     float* __restrict__ rec, int32_t* __restrict__ prefix_out, int n_seqs, int hq, int hkv, int g, int max_blocks,
-    int num_blocks, float scale_log2) {
+    int num_blocks, float scale_log2, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out, uint16_t* __restrict__ k_store,
+    uint16_t* __restrict__ v_store) {
   extern __shared__ int32_t sm[];
-  int32_t* s_len = sm;            // [n_seqs] lengths (clamped to the table)
+  int32_t* s_len = sm;            // [n_seqs] packed attended-token counts (pool part clamped to the table)
   int32_t* s_pre = sm + n_seqs;   // [n_seqs + 1] tile prefix sums
   __shared__ int32_t s_wsum[kSW];
 
@@ -339,16 +430,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   int carry = 0;
   for (int base = 0; base < n_seqs; base += 256) {
     const int i = base + tid;
-    int S = i < n_seqs ? context_lens[i] : 0;
-    S = min(max(S, 0), s_cap);
-    int v = (S + 31) >> 5;
+    const int S_raw = i < n_seqs ? context_lens[i] : 0;
+    const int S = min(max(S_raw, 0), s_cap);
+    const int hn = k_new != nullptr ? 1 : 0;  // pa_decode_step: every row attends to its new token
+    const int fits = S_raw >= 0 && S_raw < s_cap ? 1 : 0;
+    const int S_att = S + hn;
+    int v = (S_att + 31) >> 5;
 #pragma unroll
     for (int dlt = 1; dlt < 64; dlt <<= 1) {
       const int u = __shfl_up(v, dlt);
       if (lane >= dlt) v += u;
     }
     if (lane == 63) s_wsum[wave] = v;
-    if (i < n_seqs) s_len[i] = S;
+    if (i < n_seqs) s_len[i] = (S_att << 2) | (fits << 1) | hn;
     __syncthreads();
     int off = carry;
     for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
@@ -405,6 +499,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // while `nxt` streams into the other stage / qn (its blocks tbn are known)
   // and the table entries of the tile after it load into tb2.  Returns false
   // after the last tile.
+  // the step's new token, for tiles that end a segment holding one
+  auto wants_new = [&](TilePos t) -> bool {
+    return k_new != nullptr && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
+  };
+  // one buffer: a step patches its tile before it loads the next tile's token
+  NewTok<D> ntok;
+  if (wants_new(cur)) load_new<D>(ntok, cur, k_new, v_new, slots, hkv, r, gq);
   auto step = [&](auto sc_tag, QOp<D>& qc, const Tb<B>& tbc, QOp<D>& qn, const Tb<B>& tbn, Tb<B>& tb2) -> bool {
     constexpr int SC = decltype(sc_tag)::value;
     unsigned char(&stc)[4][kStageBytes] = SC == 0 ? g_stage0 : g_stage1;
@@ -413,7 +514,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     // current stage is read into registers first; the next tile's copies are
     // issued after it and stay in flight through this tile's compute.
     const bool has_next = x + 1 < x1;
-    const int S = s_len[cur.n];
+    const int packed = s_len[cur.n];
+    const int S = attended_tokens(packed);
     const int nt_cur = tiles_of(s_pre, cur.n);
     const TilePos nxt2 = x + 2 < x1 ? advance(nxt, s_pre, hkv) : nxt;
     Buf<D> b;
@@ -421,10 +523,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     // keep the stage's LDS reads ahead of the copies below: an LDS read issued
     // after them would wait for all of them
     __builtin_amdgcn_sched_barrier(0);
+    const int t0 = cur.ti * 32;
+    if (k_new != nullptr && has_new_token(packed) && cur.ti == nt_cur - 1) {
+      patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
+      store_new<D, B>(ntok, cur.j, pool_tokens(packed), next_fits(packed), k_store, v_store, hkv,
+                      static_cast<int64_t>(num_blocks) * B, r, gq);
+      // the slot, read from wherever the caller keeps it, goes on to the row update
+      if (cur.j == 0 && lane == 0) slots_out[cur.n] = ntok.slot;
+    }
     tb2 = load_tb<B>(nxt2, block_tables, max_blocks, s_len);
     load_q<D>(qn, nxt, q, hq, g, r, gq);
+    if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
     dma_tile<D, B>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
-    const int t0 = cur.ti * 32;
     const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
     f32x4 sco[2];
     qk_tile<D>(sco, b, qc);
@@ -447,18 +557,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   }
 }
 
-// Combine the summary records of segments cut by wave-range boundaries, and
-// write zeros for empty sequences.  One workgroup per (KV head, sequence);
-// wave h' takes heads h', h' + 4, ...; lanes read records in parallel (wave
-// v_lo + lane), so the merge costs a few memory latencies rather than one per
-// record.  Records combine in wave order, which is tile order.
+// The step's row update, done by the merge kernel once every decode wave has
+// read the tables and lengths: row n moves forward -- table entry S / B =
+// slot / B, length S + 1 -- when its slot (copied to the workspace by the
+// decode kernel, which also stored the new token) is at its next position
+// ("PagedAttention: Virtual Memory for the KV Cache", sections 7 and 16).
+// Same rules as pa_append_step.
+struct AppendArgs {
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const uint16_t* k_new;  // nullptr: plain decode, no append
+  const uint16_t* v_new;
+  const int32_t* slots;   // the workspace copy
+  int32_t* block_tables;
+  int32_t* context_lens;
+  int max_blocks, block_size;
+  int64_t num_slots;
+};
+
+__device__ __forceinline__ void advance_row(const AppendArgs& ap, int64_t slot, int n) {
+  if (slot < 0 || slot >= ap.num_slots) return;
+  const int B = ap.block_size;
+  const int pos = ap.context_lens[n];
+  if (pos >= 0 && pos / B < ap.max_blocks && pos % B == static_cast<int>(slot % B)) {
+    ap.block_tables[static_cast<int64_t>(n) * ap.max_blocks + pos / B] = static_cast<int32_t>(slot / B);
+    ap.context_lens[n] = pos + 1;
+  }
+}
+
+// Combine the summary records of one segment cut by wave-range boundaries,
+// or write zeros for an empty sequence.  Wave h' of the workgroup takes heads
+// h', h' + 4, ...; lanes read records in parallel (wave v_lo + lane), so the
+// merge costs a few memory latencies rather than one per record.  Records
+// combine in wave order, which is tile order.
 template <int D>
-__global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ rec,
-                                                    const int32_t* __restrict__ prefix, uint16_t* __restrict__ out,
-                                                    int n_seqs, int hq, int hkv, int g, int64_t total_waves) {
+__device__ __forceinline__ void merge_segment(const float* __restrict__ rec, const int32_t* __restrict__ prefix,
+                                              uint16_t* __restrict__ out, int n_seqs, int hq, int hkv, int g,
+                                              int64_t total_waves, int j, int n) {
   constexpr int E = D / 64;  // output elements per lane
-  const int j = blockIdx.x;
-  const int n = blockIdx.y;
   const int64_t p_n = prefix[n];
   const int nt = prefix[n + 1] - prefix[n];
   uint16_t* o = out + (static_cast<int64_t>(n) * hq + j * g) * D;
@@ -525,6 +661,19 @@ __global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ re
 #pragma unroll
     for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
   }
+}
+
+// Second kernel of a decode: one workgroup per (KV head, sequence) merges the
+// segment's pieces; for pa_decode_step it also moves the row forward.
+template <int D>
+__global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ rec,
+                                                    const int32_t* __restrict__ prefix, uint16_t* __restrict__ out,
+                                                    int n_seqs, int hq, int hkv, int g, int64_t total_waves,
+                                                    AppendArgs ap) {
+  const int j = blockIdx.x;
+  const int n = blockIdx.y;
+  if (ap.k_new != nullptr && j == 0 && threadIdx.x == 0) advance_row(ap, ap.slots[n], n);
+  merge_segment<D>(rec, prefix, out, n_seqs, hq, hkv, g, total_waves, j, n);
 }
 
 template <int D, int B>
@@ -608,7 +757,8 @@ StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int
   const int64_t waves = wgs * kSW;
   p.prefix_offset = 0;
   const size_t prefix_bytes = ((static_cast<size_t>(num_seqs) + 1) * sizeof(int32_t) + 255) / 256 * 256;
-  p.records_offset = p.prefix_offset + prefix_bytes;
+  p.slots_offset = p.prefix_offset + prefix_bytes;
+  p.records_offset = p.slots_offset + prefix_bytes;
   p.workspace_bytes = p.records_offset + static_cast<size_t>(waves) * 2 * g * (d + 4) * sizeof(float);
   p.lds_bytes = stream_lds(num_seqs);
   return p;
@@ -617,25 +767,43 @@ StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int
 template <int D, int B>
 static void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
                              const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv,
-                             int max_blocks, int num_blocks, float scale_log2) {
+                             int max_blocks, int num_blocks, float scale_log2, const StepInputs* step) {
   char* base = static_cast<char*>(ws);
   int32_t* prefix = reinterpret_cast<int32_t*>(base + p.prefix_offset);
+  int32_t* slots_ws = reinterpret_cast<int32_t*>(base + p.slots_offset);
   float* rec = reinterpret_cast<float*>(base + p.records_offset);
   const int g = hq / hkv;
+  AppendArgs ap{};
+  const int32_t* slots_in = nullptr;
+  if (step) {
+    ap.k_pool = static_cast<uint16_t*>(const_cast<void*>(k));
+    ap.v_pool = static_cast<uint16_t*>(const_cast<void*>(v));
+    ap.k_new = static_cast<const uint16_t*>(step->k_new);
+    ap.v_new = static_cast<const uint16_t*>(step->v_new);
+    slots_in = step->slots;
+    ap.slots = slots_ws;  // the decode kernel copies each row's slot there
+    ap.block_tables = const_cast<int32_t*>(bt);
+    ap.context_lens = const_cast<int32_t*>(cl);
+    ap.max_blocks = max_blocks;
+    ap.block_size = B;
+    ap.num_slots = static_cast<int64_t>(num_blocks) * B;
+  }
   decode_stream<D, B><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bt, cl,
-      static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g, max_blocks, num_blocks, scale_log2);
+      static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g, max_blocks, num_blocks, scale_log2, ap.k_new,
+      ap.v_new, slots_in, slots_ws, ap.k_pool, ap.v_pool);
   merge_stream<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, prefix, static_cast<uint16_t*>(out), n, hq, hkv, g,
-                                                     static_cast<int64_t>(p.workgroups) * kSW);
+                                                     static_cast<int64_t>(p.workgroups) * kSW, ap);
 }
 
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
-                  int max_blocks, int num_blocks, float scale_log2) {
-#define PA_STREAM_CASE(DD, BB)                                                                              \
-  if (d == DD && block_size == BB) {                                                                        \
-    launch_stream_db<DD, BB>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks, scale_log2); \
-    return launch_status();                                                                                 \
+                  int max_blocks, int num_blocks, float scale_log2, const StepInputs* step) {
+#define PA_STREAM_CASE(DD, BB)                                                                            \
+  if (d == DD && block_size == BB) {                                                                      \
+    launch_stream_db<DD, BB>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks, scale_log2, \
+                             step);                                                                       \
+    return launch_status();                                                                               \
   }
   PA_STREAM_CASE(128, 16)
   PA_STREAM_CASE(128, 8)
