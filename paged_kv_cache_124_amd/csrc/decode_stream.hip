@@ -102,7 +102,7 @@ template <int D>
 struct NewTok {
   bf16x8 k[D / 32];
   uint32_t v[D / 32];  // value rows 16 mm + r, two per word (even mm low)
-  int slot;            // the row's slot
+  int slot;            // the row's slot (read with KV head 0's token)
 };
 
 template <int D>
@@ -116,32 +116,7 @@ __device__ __forceinline__ void load_new(NewTok<D>& nt, TilePos t, const uint16_
 #pragma unroll
   for (int m2 = 0; m2 < D / 32; ++m2)
     nt.v[m2] = uint32_t(v_new[row + 32 * m2 + r]) | (uint32_t(v_new[row + 32 * m2 + 16 + r]) << 16);
-  nt.slot = slots[t.n];
-}
-
-// Store the new token at its slot (block slot / B, offset slot % B) in the
-// pool layout: key chunks of 8 values from the lanes of row 0, value rows
-// d = 16 mm + r from the lanes of group 0.  Only when the slot is the row's
-// next position (S % B): its block is then the row's own tail or a block no
-// table reaches yet, read by no other wave, and this wave has read it already.
-template <int D, int B>
-__device__ __forceinline__ void store_new(const NewTok<D>& nt, int j, int S, bool fits,
-                                          uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int hkv,
-                                          int64_t num_slots, int r, int gq) {
-  const int64_t slot = nt.slot;
-  if (!fits || slot < 0 || slot >= num_slots || static_cast<int>(slot % B) != S % B) return;
-  const int64_t head = (slot / B) * hkv + j;
-  const int off = static_cast<int>(slot % B);
-  if (r == 0) {
-#pragma unroll
-    for (int jj = 0; jj < D / 32; ++jj)
-      *reinterpret_cast<bf16x8*>(k_pool + ((head * (D / 8) + 4 * jj + gq) * B + off) * 8) = nt.k[jj];
-  }
-  if (gq == 0) {
-#pragma unroll
-    for (int mm = 0; mm < D / 16; ++mm)
-      v_pool[(head * D + 16 * mm + r) * B + off] = static_cast<uint16_t>(nt.v[mm >> 1] >> (16 * (mm & 1)));
-  }
+  if (t.j == 0) nt.slot = slots[t.n];
 }
 
 // Table entries of a tile's blocks.  Always loaded (index clamped into the
@@ -412,8 +387,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     float* __restrict__ rec, int32_t* __restrict__ prefix_out, int n_seqs, int hq, int hkv, int g, int max_blocks,
     int num_blocks, float scale_log2, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out, uint16_t* __restrict__ k_store,
-    uint16_t* __restrict__ v_store) {
+    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out) {
   extern __shared__ int32_t sm[];
   int32_t* s_len = sm;            // [n_seqs] packed attended-token counts (pool part clamped to the table)
   int32_t* s_pre = sm + n_seqs;   // [n_seqs + 1] tile prefix sums
@@ -526,10 +500,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int t0 = cur.ti * 32;
     if (k_new != nullptr && has_new_token(packed) && cur.ti == nt_cur - 1) {
       patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
-      store_new<D, B>(ntok, cur.j, pool_tokens(packed), next_fits(packed), k_store, v_store, hkv,
-                      static_cast<int64_t>(num_blocks) * B, r, gq);
-      // the slot, read from wherever the caller keeps it, goes on to the row update
-      if (cur.j == 0 && lane == 0) slots_out[cur.n] = ntok.slot;
+      // the row's slot, read from wherever the caller keeps it, goes on to the
+      // merge kernel (which stores the token): the slot when it is the row's
+      // next position, else -1
+      if (cur.j == 0 && lane == 0) {
+        const int S0 = pool_tokens(packed);
+        const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
+                             static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
+                             ntok.slot % B == S0 % B;
+        slots_out[cur.n] = at_next ? ntok.slot : -1;
+      }
     }
     tb2 = load_tb<B>(nxt2, block_tables, max_blocks, s_len);
     load_q<D>(qn, nxt, q, hq, g, r, gq);
@@ -557,30 +537,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   }
 }
 
-// The step's row update, done by the merge kernel once every decode wave has
-// read the tables and lengths: row n moves forward -- table entry S / B =
-// slot / B, length S + 1 -- when its slot (copied to the workspace by the
-// decode kernel, which also stored the new token) is at its next position
-// ("PagedAttention: Virtual Memory for the KV Cache", sections 7 and 16).
-// Same rules as pa_append_step.
+// The step's append, done by the merge kernel once every decode wave has
+// read the pool, the tables and the lengths: when row n's slot is its next
+// position (the decode kernel checked it and left the slot, or -1, in the
+// workspace), the new token of KV head j goes to block slot / B, offset
+// slot % B, and the row moves forward -- table entry S / B = slot / B,
+// length S + 1 ("PagedAttention: Virtual Memory for the KV Cache", sections 7
+// and 16).
 struct AppendArgs {
   uint16_t* k_pool;
   uint16_t* v_pool;
   const uint16_t* k_new;  // nullptr: plain decode, no append
   const uint16_t* v_new;
-  const int32_t* slots;   // the workspace copy
+  const int32_t* slots;   // workspace: the slot when it is the row's next position, else -1
   int32_t* block_tables;
   int32_t* context_lens;
   int max_blocks, block_size;
-  int64_t num_slots;
 };
 
-__device__ __forceinline__ void advance_row(const AppendArgs& ap, int64_t slot, int n) {
-  if (slot < 0 || slot >= ap.num_slots) return;
+// The new token of (row n, KV head j) as thread t of the workgroup holds it:
+// key chunk t (t < D / 8) and value row d = t (t < D).  Loaded when the merge
+// kernel starts, stored when it ends.
+template <int D>
+struct RowToken {
+  int64_t slot;
+  uint4 k;
+  uint16_t v;
+};
+
+template <int D>
+__device__ __forceinline__ RowToken<D> load_row_token(const AppendArgs& ap, int n, int j, int hkv) {
+  RowToken<D> rt;
+  const int64_t src = (static_cast<int64_t>(n) * hkv + j) * D;
+  const int t = threadIdx.x;
+  rt.slot = ap.slots[n];
+  rt.k = t < D / 8 ? *reinterpret_cast<const uint4*>(ap.k_new + src + t * 8) : make_uint4(0, 0, 0, 0);
+  rt.v = t < D ? ap.v_new[src + t] : 0;
+  return rt;
+}
+
+template <int D>
+__device__ __forceinline__ void append_row(const AppendArgs& ap, const RowToken<D>& rt, int n, int j, int hkv) {
+  if (rt.slot < 0) return;
   const int B = ap.block_size;
-  const int pos = ap.context_lens[n];
-  if (pos >= 0 && pos / B < ap.max_blocks && pos % B == static_cast<int>(slot % B)) {
-    ap.block_tables[static_cast<int64_t>(n) * ap.max_blocks + pos / B] = static_cast<int32_t>(slot / B);
+  const int64_t pb = rt.slot / B;
+  const int off = static_cast<int>(rt.slot % B);
+  const int64_t head = pb * hkv + j;
+  const int t = threadIdx.x;
+  if (t < D / 8) *reinterpret_cast<uint4*>(ap.k_pool + ((head * (D / 8) + t) * B + off) * 8) = rt.k;
+  if (t < D) ap.v_pool[(head * D + t) * B + off] = rt.v;
+  if (j == 0 && t == 0) {  // the only thread that reads or writes the row
+    const int pos = ap.context_lens[n];
+    ap.block_tables[static_cast<int64_t>(n) * ap.max_blocks + pos / B] = static_cast<int32_t>(pb);
     ap.context_lens[n] = pos + 1;
   }
 }
@@ -618,6 +626,44 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
     const int slot = (v == v_lo && lo_second) ? 1 : 0;
     return rec + ((v * 2 + slot) * g + h) * (D + 4);
   };
+  if (v_hi - v_lo < 8) {
+    // up to 8 pieces (the usual case): the maxima, sums and value rows of all
+    // pieces load together, in one memory round trip
+    const int cnt = static_cast<int>(v_hi - v_lo + 1);
+    for (int h = wave; h < g; h += 4) {
+      const float* mine = lane < cnt ? record(v_lo + lane, h) : nullptr;
+      const float* ml = mine ? mine : rec;  // any valid address; unused
+      const float m_l = ml[0], z_l = ml[1];
+      float val[8][E];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* rk = k < cnt ? record(v_lo + k, h) : nullptr;
+        rk = rk ? rk : rec;  // weighted by zero below
+#pragma unroll
+        for (int e = 0; e < E; ++e) val[k][e] = rk[4 + lane + 64 * e];
+      }
+      float mx = mine ? m_l : -INFINITY;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+      const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
+      float zz = mine ? f * z_l : 0.f;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+      float uu[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) uu[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float fk = __shfl(f, k);  // zero for k >= cnt and empty ranges
+#pragma unroll
+        for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
+      }
+      const float inv = 1.f / zz;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+    }
+    return;
+  }
   for (int h = wave; h < g; h += 4) {
     float mx = -INFINITY;
     for (int64_t base = v_lo; base <= v_hi; base += 64) {
@@ -664,7 +710,8 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
 }
 
 // Second kernel of a decode: one workgroup per (KV head, sequence) merges the
-// segment's pieces; for pa_decode_step it also moves the row forward.
+// segment's pieces; for pa_decode_step it also stores the new token and moves
+// the row forward.
 template <int D>
 __global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ rec,
                                                     const int32_t* __restrict__ prefix, uint16_t* __restrict__ out,
@@ -672,8 +719,13 @@ __global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ re
                                                     AppendArgs ap) {
   const int j = blockIdx.x;
   const int n = blockIdx.y;
-  if (ap.k_new != nullptr && j == 0 && threadIdx.x == 0) advance_row(ap, ap.slots[n], n);
+  if (ap.k_new == nullptr) {
+    merge_segment<D>(rec, prefix, out, n_seqs, hq, hkv, g, total_waves, j, n);
+    return;
+  }
+  const RowToken<D> rt = load_row_token<D>(ap, n, j, hkv);  // in flight during the merge
   merge_segment<D>(rec, prefix, out, n_seqs, hq, hkv, g, total_waves, j, n);
+  append_row<D>(ap, rt, n, j, hkv);
 }
 
 template <int D, int B>
@@ -786,12 +838,11 @@ static void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, 
     ap.context_lens = const_cast<int32_t*>(cl);
     ap.max_blocks = max_blocks;
     ap.block_size = B;
-    ap.num_slots = static_cast<int64_t>(num_blocks) * B;
   }
   decode_stream<D, B><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bt, cl,
       static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g, max_blocks, num_blocks, scale_log2, ap.k_new,
-      ap.v_new, slots_in, slots_ws, ap.k_pool, ap.v_pool);
+      ap.v_new, slots_in, slots_ws);
   merge_stream<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, prefix, static_cast<uint16_t*>(out), n, hq, hkv, g,
                                                      static_cast<int64_t>(p.workgroups) * kSW, ap);
 }
