@@ -334,7 +334,8 @@ def main():
                    "pool_replicas": args.replicas, "partition_tokens": run.part,
                    "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2),
                    "host_us_per_step": round(run.host_s / args.steps * 1e6, 2),
-                   "staging": "pinned host ring read by the kernels" if run.zero_copy else "pinned ring, in-stream copy"},
+                   "staging": "pinned host ring read by the kernels" if run.zero_copy else "pinned ring, in-stream copy",
+                   "tail_waste_slots": run.bm.stats()["tail_waste_slots"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),

@@ -31,7 +31,8 @@ def _bits(k, v):
     return kl, vl
 
 
-def test_fork_cow_sixteen_steps():
+@pytest.mark.parametrize("fused", [False, True])
+def test_fork_cow_sixteen_steps(fused):
     import paged_kv_cache_124_amd as pa
     w = synth.fork()
     P, S, steps = synth.FORK_PROMPTS, synth.FORK_SAMPLES, synth.FORK_STEPS
@@ -44,7 +45,7 @@ def test_fork_cow_sixteen_steps():
     new_blocks = P * (S - 1) + n * (-(-final // bs) - (-(-prompt // bs)))
     nb = synth.pool_blocks(w, list(w.fixed_lens), extra=new_blocks)
     mb = -(-final // bs)
-    print(f"[case] fork: {n} seqs, pool {nb} blocks, {steps} steps", flush=True)
+    print(f"[case] fork: {n} seqs, pool {nb} blocks, {steps} steps, fused={fused}", flush=True)
     order = synth.pop_order(nb, w.seed)
     bm = pa.BlockManager(nb, bs, order)
     model = BlockManagerModel(nb, bs, [int(x) for x in order])
@@ -79,9 +80,13 @@ def test_fork_cow_sixteen_steps():
             pa.pa_copy_blocks(k, v, torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda())
         kn = synth.randn((n, hkv, d), torch.bfloat16, w.value_scale, 5000 + step, "cuda")
         vn = synth.randn((n, hkv, d), torch.bfloat16, w.value_scale, 6000 + step, "cuda")
-        pa.pa_append_step(k, v, kn, vn, torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda(), d_tables, d_lens)
         q = synth.randn((n, hq, d), torch.bfloat16, w.value_scale, 7000 + step, "cuda")
-        pa.pa_decode(out, q, k, v, d_tables, d_lens, case.scale, final)
+        d_slots = torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda()
+        if fused:  # attention with the new token from k_new / v_new, then the store and the row advance
+            pa.pa_decode_step(out, q, kn, vn, k, v, d_slots, d_tables, d_lens, case.scale, final)
+        else:
+            pa.pa_append_step(k, v, kn, vn, d_slots, d_tables, d_lens)
+            pa.pa_decode(out, q, k, v, d_tables, d_lens, case.scale, final)
         torch.cuda.synchronize()
         OA.copy_blocks(ek, ev, mpairs)
         OA.append_kv(ek, ev, kn.cpu().view(torch.int16).numpy(), vn.cpu().view(torch.int16).numpy(), mslots)
