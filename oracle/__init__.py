@@ -17,6 +17,10 @@ attention      fp64 paged decode attention (gather through the block table,
 block_manager  pure-Python block manager: LIFO free list, per-block reference
                counts, block tables, fork, copy-on-write of a shared tail
                block, release, batch building.
+fp8            KV cache held as FP8 E4M3 codes with per-(block, KV head)
+               scales: code values, the saturating round-to-nearest-even
+               quantizer, the quantizing append, block copy with scales, and
+               decode over the dequantized cache.
 sizing         KV sizing, block-table footprint, tail waste and capacity
                arithmetic.
 
