@@ -66,7 +66,9 @@ enum {
   PA_ERR_HIP = 7             /* the HIP runtime refused a launch                    */
 };
 
-enum { PA_F32 = 0, PA_BF16 = 1 };
+/* PA_FP8_E4M3 names a cache of FP8 codes (see pa_decode_fp8); queries,
+ * outputs and new tokens stay bf16 there. */
+enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 };
 
 /* Text for a status code (static storage; never NULL). */
 const char* pa_status_string(int status);
@@ -156,7 +158,7 @@ int pa_decode_step(void* out, const void* q, const void* k_new, const void* v_ne
                    void* stream);
 
 /* Workspace bytes pa_decode needs for these sizes on the current device
- * (0 when no split is used). */
+ * (0 when no split is used); dtype PA_FP8_E4M3 gives pa_decode_fp8's. */
 size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                  int max_context_len, int dtype);
 
@@ -225,6 +227,61 @@ int pa_append_step(void* k_pool, void* v_pool, const void* k_new, const void* v_
 int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int num_pairs,
                    int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
                    int64_t layer_stride_elems, int dtype, void* stream);
+
+/* ---- FP8 (E4M3) KV cache ------------------------------------------------------
+ *
+ * A cache of 8-bit codes halves the bytes per token of a bf16 cache
+ * ("PagedAttention and KV Memory", "Alternatives and ecosystem": quantized
+ * KV cuts per-token size and combines with paging).  Attention over it is the
+ * exact attention over the values the codes stand for ("PagedAttention in
+ * vLLM: scattered memory, exact attention", sections 8 and 11: quantization
+ * changes precision, not the attention rule).
+ *
+ * Codes: FP8 E4M3 of the OCP 8-bit floating point format (exponent bias 7,
+ * subnormals, no infinities, NaN = 0x7F / 0xFF, largest finite 448).
+ * Scales: fp32, one per (physical block, KV head) for keys (k_scale) and one
+ * for values (v_scale), each [num_blocks][Hkv] on the device, owned by the
+ * caller, positive and finite.  Code c of block pb, KV head j stands for
+ * value(c) * scale[pb][j].  Static per-head scaling is the case where all
+ * blocks of a head carry the same scale.
+ * Pool layout: as above with E = 1, x = 16:
+ *   K codes [num_blocks][Hkv][D / 16][B][16], V codes [num_blocks][Hkv][D][B].
+ */
+
+/* pa_decode over an FP8 cache.  q and out are bf16 [num_seqs][Hq][d_head];
+ * the other arguments, the workspace (pa_decode_workspace_bytes with dtype
+ * PA_FP8_E4M3), the split and the errors are as for pa_decode.  Scores are
+ * scale * k_scale * dot(q, value(codes)) and P.V weighs value(codes) *
+ * v_scale, accumulated in fp32.  Served for Hq / Hkv <= 16, num_seqs <= 3072,
+ * d_head in {64, 128}, block_size in {8, 16, 32}; other shapes return
+ * PA_ERR_UNSUPPORTED.  Scales of blocks the tables reach must be positive and
+ * finite; a block id outside [0, num_blocks) is never dereferenced. */
+int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
+                  const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                  int Hq, int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq,
+                  int max_context_len, int num_blocks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_append_kv into an FP8 cache: each element x of token t's bf16 key and
+ * value (k_new, v_new [num_tokens][Hkv][d_head]) is stored at slot
+ * slot_mapping[t] ("PagedAttention: Virtual Memory for the KV Cache",
+ * section 16) as the sign of x and the finite E4M3 magnitude nearest to the
+ * real quotient |x| / scale of the destination (block, KV head), ties to an
+ * even mantissa; magnitudes beyond 448 saturate to 448.  NaN input, or a scale
+ * that is not positive and finite, stores 0x7F.  Slots as for pa_append_kv.
+ * Deterministic: the codes depend only on x and the scale. */
+int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                     const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+                     int Hkv, int d_head, int block_size, int num_blocks, void* stream);
+
+/* pa_copy_blocks for an FP8 cache: codes of block src over block dst, and its
+ * scales with them, k_scale[dst][*] = k_scale[src][*] and likewise v_scale
+ * ("PagedAttention: Virtual Memory for the KV Cache", sections 15-16).
+ * Bit-exact.  layer_stride_elems counts codes (bytes) between layers of each
+ * pool, scale_layer_stride floats between layers of each scale array (both
+ * ignored when num_layers == 1).  Pairs as for pa_copy_blocks. */
+int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, const int32_t* src_dst_pairs,
+                       int num_pairs, int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
+                       int64_t layer_stride_elems, int64_t scale_layer_stride, void* stream);
 
 /* ---- host block manager ------------------------------------------------------
  *

@@ -9,18 +9,25 @@ arguments.
 from ._lib import (  # noqa: F401
     PA_BF16,
     PA_F32,
+    PA_FP8_E4M3,
     PA_OK,
     BlockManager,
     PAError,
     lib,
     pa_append_kv,
     pa_append_kv_args,
+    pa_append_kv_fp8,
+    pa_append_kv_fp8_args,
     pa_append_step,
     pa_append_step_args,
     pa_copy_blocks,
     pa_copy_blocks_args,
+    pa_copy_blocks_fp8,
+    pa_copy_blocks_fp8_args,
     pa_decode,
     pa_decode_args,
+    pa_decode_fp8,
+    pa_decode_fp8_args,
     pa_decode_partition_tokens,
     pa_decode_step,
     pa_decode_step_args,

@@ -28,6 +28,7 @@ PA_ERR_WORKSPACE = 6
 PA_ERR_HIP = 7
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 
 # torch first: libpa.so then binds to the HIP runtime torch has loaded, so
 # torch's streams and device memory are valid in the library's calls.
@@ -69,6 +70,9 @@ _SIGS = {
                                c_int, c_int, c_int, c_int, c_int, c_void_p]),
     "pa_copy_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int64,
                                c_int, c_void_p]),
+    "pa_decode_fp8": (c_int, [c_void_p] * 8 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
+    "pa_append_kv_fp8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
+    "pa_copy_blocks_fp8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
     "pa_bm_create": (c_void_p, [c_int, c_int, _P32]),
     "pa_bm_destroy": (None, [c_void_p]),
     "pa_bm_add_seq": (c_int, [c_void_p, c_int64, c_int]),
@@ -310,6 +314,109 @@ def pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream=None):
 def pa_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
     """pa_copy_blocks of include/pa.h."""
     _check(lib.pa_copy_blocks(*pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream)), "pa_copy_blocks")
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) cache: uint8 code pools in the layout above (x = 16) and float32
+# scales [num_blocks][Hkv] (or [L][num_blocks][Hkv] for a layered copy)
+# ---------------------------------------------------------------------------
+
+def _fp8_pools(k_pool, v_pool):
+    import torch
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise ValueError("FP8 pools hold uint8 codes")
+    return _pool_dims(k_pool, v_pool)
+
+
+def _scales(k_scale, v_scale, nb, hkv, lead=()):
+    import torch
+    want = tuple(lead) + (nb, hkv)
+    for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.dtype != torch.float32 or tuple(t.shape) != want:
+            raise ValueError(f"{name} must be float32 {list(want)}")
+
+
+def pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+                       max_context_len, workspace=None, stream=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode_fp8(*args)`` calls."""
+    import torch
+    n, hq, d = q.shape
+    nb, hkv, d2, bs = _fp8_pools(k_pool, v_pool)
+    _scales(k_scale, v_scale, nb, hkv)
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or d2 != d:
+        raise ValueError("q and out must be bf16 [N][Hq][D] matching the pools")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or tuple(context_lens.shape) != (n,):
+        raise ValueError("block_tables must be [N][max_blocks] and context_lens [N]")
+    need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, PA_FP8_E4M3)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(block_tables, "block_tables"),
+            _dev(context_lens, "context_lens"), n, hq, hkv, d, bs, float(scale), block_tables.shape[1],
+            int(max_context_len), nb, ws_ptr, ws_bytes, _stream_ptr(stream))
+    return args, workspace
+
+
+def pa_decode_fp8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale, max_context_len,
+                  workspace=None, stream=None):
+    """pa_decode_fp8 of include/pa.h: bf16 q/out over uint8 E4M3 code pools with float32 scales."""
+    args, _ws = pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+                                   max_context_len, workspace, stream)
+    _check(lib.pa_decode_fp8(*args), "pa_decode_fp8")
+    return out
+
+
+def pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, stream=None):
+    """Validate once and return the argument tuple for ``lib.pa_append_kv_fp8(*args)``."""
+    import torch
+    nb, hkv, d, bs = _fp8_pools(k_pool, v_pool)
+    _scales(k_scale, v_scale, nb, hkv)
+    t = k_new.shape[0]
+    if tuple(k_new.shape) != (t, hkv, d) or tuple(v_new.shape) != (t, hkv, d):
+        raise ValueError("k_new / v_new must be [T][Hkv][D]")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new / v_new must be bf16")
+    if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (t,):
+        raise ValueError("slot_mapping must be int32 [T]")
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+            _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"), t, hkv, d, bs, nb,
+            _stream_ptr(stream))
+
+
+def pa_append_kv_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, stream=None):
+    """pa_append_kv_fp8 of include/pa.h: quantize bf16 k_new/v_new [T][Hkv][D] into their slots."""
+    _check(lib.pa_append_kv_fp8(*pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+                                                       slot_mapping, stream)), "pa_append_kv_fp8")
+
+
+def pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
+    """Validate once and return the argument tuple for ``lib.pa_copy_blocks_fp8(*args)``.
+
+    Pools and scales are one layer or all layers (leading [L] on both).
+    """
+    import torch
+    layered = k_pool.dim() == 6
+    kl, vl = (k_pool[0], v_pool[0]) if layered else (k_pool, v_pool)
+    nb, hkv, d, bs = _fp8_pools(kl, vl)
+    layers = k_pool.shape[0] if layered else 1
+    _scales(k_scale, v_scale, nb, hkv, (layers,) if layered else ())
+    if src_dst_pairs.dtype != torch.int32 or src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int32 [P][2]")
+    stride = kl.numel() if layered else 0
+    sstride = nb * hkv if layered else 0
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+            _dev(src_dst_pairs, "src_dst_pairs"), src_dst_pairs.shape[0], hkv, d, bs, nb, layers, stride, sstride,
+            _stream_ptr(stream))
+
+
+def pa_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
+    """pa_copy_blocks_fp8 of include/pa.h: codes and scales of each src block over its dst."""
+    _check(lib.pa_copy_blocks_fp8(*pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream)),
+           "pa_copy_blocks_fp8")
 
 
 # ---------------------------------------------------------------------------

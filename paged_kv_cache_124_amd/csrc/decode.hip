@@ -472,6 +472,10 @@ bool use_stream(int num_seqs, int hq, int hkv, int d, int block_size, int dtype)
 extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                             int max_context_len, int dtype) {
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_context_len < 0) return 0;
+  if (dtype == PA_FP8_E4M3) {
+    if (Hq % Hkv != 0 || !pa::stream_eligible_fp8(num_seqs, Hq / Hkv, d_head, block_size)) return 0;
+    return pa::stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, true).workspace_bytes;
+  }
   if (pa::use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype))
     return pa::stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len).workspace_bytes;
   const pa::Plan p = pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
@@ -481,6 +485,7 @@ extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d
 extern "C" int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                           int max_context_len, int dtype) {
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0) return 0;
+  if (dtype == PA_FP8_E4M3) return 0;
   if (pa::use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) return 0;
   return pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype).part;
 }
@@ -584,4 +589,27 @@ extern "C" int pa_decode_step(void* out, const void* q, const void* k_new, const
   return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
                      scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes,
                      stream, &step);
+}
+
+extern "C" int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
+                             const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                             int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  using namespace pa;
+  if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+      max_context_len < 0 || num_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size < max_context_len) return PA_ERR_INVALID_ARG;
+  if (!stream_eligible_fp8(num_seqs, Hq / Hkv, d_head, block_size) || Hq > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;  // the kernel may read block 0 / entry 0
+  const StreamPlan sp = stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, true);
+  if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
+  return launch_stream(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, out,
+                       workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq, num_blocks,
+                       scale * kLog2e, nullptr, k_scale, v_scale);
 }

@@ -1,4 +1,4 @@
-// Internal interface of the persistent bf16 decode kernel (decode_stream.hip).
+// Internal interface of the persistent decode kernel (decode_stream.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,9 +26,15 @@ struct StepInputs {
 };
 
 bool stream_eligible(int num_seqs, int g, int d, int block_size, int dtype);
-StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx);
+// Shapes the FP8-cache kernel serves (bf16 queries and outputs).
+bool stream_eligible_fp8(int num_seqs, int g, int d, int block_size);
+// fp8: 64-token tiles over an FP8 cache instead of 32-token bf16 tiles.
+StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, bool fp8 = false);
+// k_scale / v_scale non-null: the pools hold FP8 codes with per-(block, KV
+// head) scales (no fused step for them).
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
-                  int max_blocks, int num_blocks, float scale_log2, const StepInputs* step);
+                  int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
+                  const float* k_scale = nullptr, const float* v_scale = nullptr);
 
 }  // namespace pa

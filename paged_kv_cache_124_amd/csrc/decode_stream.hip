@@ -62,10 +62,17 @@ struct QOp {
   bf16x8 q[D / 32];
 };
 
-template <int B>
-struct Tb {  // physical blocks of a tile's 32 tokens, -1 where the sequence has ended (wave-uniform)
-  int blk[32 / B];
+template <int NB>
+struct Tb {  // physical blocks of a tile's tokens, -1 where the sequence has ended (wave-uniform)
+  int blk[NB];
 };
+
+// Tokens per tile: 32 for a bf16 cache, 64 for an FP8 cache (the same 16 KiB
+// of keys and values per tile either way).
+template <bool F8>
+constexpr int kTok = F8 ? 64 : 32;
+template <bool F8>
+constexpr int kTokShift = F8 ? 6 : 5;
 
 __device__ __forceinline__ int tiles_of(const int32_t* s_pre, int n) { return s_pre[n + 1] - s_pre[n]; }
 
@@ -122,29 +129,35 @@ __device__ __forceinline__ void load_new(NewTok<D>& nt, TilePos t, const uint16_
 // Table entries of a tile's blocks.  Always loaded (index clamped into the
 // row) and replaced by -1 past the end of the sequence, so no load sits behind
 // a branch and the compiler can keep the pipeline's loads in flight.
-template <int B>
-__device__ __forceinline__ Tb<B> load_tb(TilePos t, const int32_t* __restrict__ block_tables, int max_blocks,
-                                         const int32_t* s_len) {
+template <int B, int TOK>
+__device__ __forceinline__ Tb<TOK / B> load_tb(TilePos t, const int32_t* __restrict__ block_tables, int max_blocks,
+                                               const int32_t* s_len) {
   const int32_t* row = block_tables + static_cast<int64_t>(t.n) * max_blocks;
   const int S = pool_tokens(s_len[t.n]);
-  const int t0 = t.ti * 32;
-  Tb<B> tb;
+  const int t0 = t.ti * TOK;
+  Tb<TOK / B> tb;
 #pragma unroll
-  for (int i = 0; i < 32 / B; ++i) {
+  for (int i = 0; i < TOK / B; ++i) {
     const int e = row[min(t0 / B + i, max_blocks - 1)];
     tb.blk[i] = t0 + i * B < S ? e : -1;
   }
   return tb;
 }
 
-template <int D>
+// Q^T operand of MFMA jj: 8 elements of head r.  With a bf16 cache lane gq
+// takes d-chunk 4 jj + gq (as the key layout interleaves chunks); with an FP8
+// cache it takes elements gq D / 4 + 8 jj .. + 7, the lane's contiguous
+// quarter of d, which its 16-byte key reads cover.
+template <int D, bool F8>
 __device__ __forceinline__ void load_q(QOp<D>& qo, TilePos t, const uint16_t* __restrict__ q, int hq, int g, int r,
                                        int gq) {
   // padding columns r >= G read head 0 of the group; their results are never used
   const uint16_t* qh = q + (static_cast<int64_t>(t.n) * hq + t.j * g + (r < g ? r : 0)) * D;
 #pragma unroll
-  for (int jj = 0; jj < D / 32; ++jj)
-    qo.q[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qh + (4 * jj + gq) * 8));
+  for (int jj = 0; jj < D / 32; ++jj) {
+    const int e0 = F8 ? gq * (D / 4) + 8 * jj : (4 * jj + gq) * 8;
+    qo.q[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qh + e0));
+  }
 }
 
 template <int D>
@@ -171,41 +184,57 @@ __shared__ __attribute__((aligned(16))) unsigned char g_stage0[4][kStageBytes];
 __shared__ __attribute__((aligned(16))) unsigned char g_stage1[4][kStageBytes];
 
 // Bytes of one tile's keys (and, again, of its values) in LDS: the images of
-// the 32 / B blocks (B * D * 2 bytes each) that hold its 32 tokens.
+// the blocks that hold its tokens -- 32 / B bf16 images of B * D * 2 bytes, or
+// 64 / B FP8 images of B * D bytes.
 template <int D>
-constexpr int kStageHalf = 32 * D * 2;
+constexpr int kStageHalf = 64 * D;
 
 // Copy one tile's key and value block images into an LDS stage with
 // global_load_lds (16 bytes per lane, 1 KiB per instruction, straight to LDS:
 // no registers held while in flight).  A missing block (past the end, or an
 // id outside the pool) is read from block 0 -- a valid address -- and its
 // tokens are masked out in pv_tile.
-template <int D, int B>
-__device__ __forceinline__ void dma_tile(unsigned char* stage_ptr, int j, const Tb<B>& tb, const uint16_t* __restrict__ k_pool,
-                                         const uint16_t* __restrict__ v_pool, int hkv, int num_blocks, int lane) {
-  constexpr int IMG = D * B * 2;        // bytes of one (block, KV head) image
-  constexpr int PIECES = IMG / 1024;    // 1 KiB pieces per image
+// The tile's images lie back to back in the stage; 1 KiB piece p of them is
+// one instruction, lane l bringing bytes p * 1024 + 16 l .. + 15.  An image
+// smaller than 1 KiB (FP8, D = 64, B = 8: 512 bytes) shares a piece with the
+// next block's image, so the lanes of one instruction read two blocks.
+template <int D, int B, bool F8>
+__device__ __forceinline__ void dma_tile(unsigned char* stage_ptr, int j, const Tb<kTok<F8> / B>& tb,
+                                         const void* __restrict__ k_pool, const void* __restrict__ v_pool, int hkv,
+                                         int num_blocks, int lane) {
+  constexpr int NB = kTok<F8> / B;
+  constexpr int IMG = D * B * (F8 ? 1 : 2);  // bytes of one (block, KV head) image
+  constexpr int PIECES = NB * IMG / 1024;
   lds_byte* stage = (lds_byte*)stage_ptr;  // LDS address for the copy engine
   const int64_t blk_stride = static_cast<int64_t>(hkv) * IMG;
-  const char* kb = reinterpret_cast<const char*>(k_pool) + static_cast<int64_t>(j) * IMG + lane * 16;
-  const char* vb = reinterpret_cast<const char*>(v_pool) + static_cast<int64_t>(j) * IMG + lane * 16;
+  const char* kb = reinterpret_cast<const char*>(k_pool) + static_cast<int64_t>(j) * IMG;
+  const char* vb = reinterpret_cast<const char*>(v_pool) + static_cast<int64_t>(j) * IMG;
 #pragma unroll
-  for (int bi = 0; bi < 32 / B; ++bi) {
-    const int pb = (tb.blk[bi] >= 0 && tb.blk[bi] < num_blocks) ? tb.blk[bi] : 0;
+  for (int p = 0; p < PIECES; ++p) {
+    int e, off;
+    if constexpr (IMG >= 1024) {
+      e = tb.blk[p * 1024 / IMG];
+      off = p * 1024 % IMG + lane * 16;
+    } else {
+      constexpr int PER = 1024 / IMG;  // images per piece
+      const int bi = p * PER + lane * 16 / IMG;
+      e = tb.blk[p * PER];  // tb.blk[bi] by selects: a lane-dependent index would put tb in scratch
 #pragma unroll
-    for (int p = 0; p < PIECES; ++p) {
-      const int off = (bi * PIECES + p) * 1024;
-      __builtin_amdgcn_global_load_lds(kb + pb * blk_stride + p * 1024, stage + off, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + pb * blk_stride + p * 1024, stage + kStageHalf<D> + off, 16, 0, 0);
+      for (int i = 1; i < PER; ++i)
+        if (bi == p * PER + i) e = tb.blk[p * PER + i];
+      off = lane * 16 % IMG;
     }
+    const int64_t pb = (e >= 0 && e < num_blocks) ? e : 0;
+    __builtin_amdgcn_global_load_lds(kb + pb * blk_stride + off, stage + p * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + pb * blk_stride + off, stage + kStageHalf<D> + p * 1024, 16, 0, 0);
   }
 }
 
 // Read a staged tile's MFMA operands from LDS into registers (the same lane
 // roles as direct loads would give) and mark which value groups exist.
 template <int D, int B>
-__device__ __forceinline__ void read_tile(Buf<D>& b, const unsigned char* stage, const Tb<B>& tb, int num_blocks, int r,
-                                          int gq) {
+__device__ __forceinline__ void read_tile(Buf<D>& b, const unsigned char* stage, const Tb<32 / B>& tb, int num_blocks,
+                                          int r, int gq) {
   constexpr int IMG = D * B * 2;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -340,6 +369,163 @@ __device__ __forceinline__ void pv_tile(Acc<D>& st, const f32x4 (&s)[2], const B
   }
 }
 
+// ---- FP8 (E4M3) cache ----------------------------------------------------------
+//
+// Codes are OCP E4M3; a stored code c stands for value(c) * scale, one fp32
+// scale per (block, KV head) for keys and one for values.  gfx950 converts
+// two codes to two bf16 in one instruction, exactly (every E4M3 value is a
+// bf16 value), so both products stay bf16 x bf16 MFMAs on the codes' values
+// and the scales are applied outside them: the key scale multiplies a
+// token's score, the value scale its probability in P.V (the weight sum uses
+// the unscaled probability).  A 64-token tile is two 32-token sub-tiles,
+// each computed as a bf16 tile is.
+
+// Register image of a staged FP8 tile for lane (r, gq).
+template <int D>
+struct Buf8 {
+  uint4 k[2][2][D / 64];     // [sub-tile][slab] key row 16 slab + r: the 16-byte chunks of d quarter gq
+  uint32_t v[2][2][D / 16];  // [sub-tile][slab][mm] value row 16 mm + r, tokens 4 gq .. 4 gq + 3 of the slab
+  bool ok[2][2];             // the block of that value group is in the pool
+};
+
+// Scales of the blocks of the lane's token groups (0 where the block is missing).
+struct Sc8 {
+  float k[2][2], v[2][2];  // [sub-tile][slab]
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight codes (two words, lowest byte first) as eight bf16 values.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Block of the lane's 4-token group that starts at tile token first + 4 gq
+// (first a multiple of 16, known at compile time after unrolling).  With
+// B >= 16 the 16 tokens from `first` lie in one block; with B = 8 in two,
+// chosen by one select (an index computed at run time would move tb to scratch).
+template <int B>
+__device__ __forceinline__ int group_block(const Tb<64 / B>& tb, int first, int gq) {
+  if constexpr (B >= 16)
+    return tb.blk[first / B];
+  else
+    return gq >= 2 ? tb.blk[first / B + 1] : tb.blk[first / B];
+}
+
+template <int B>
+__device__ __forceinline__ Sc8 load_scales(const Tb<64 / B>& tb, const float* __restrict__ k_scale,
+                                           const float* __restrict__ v_scale, int j, int hkv, int num_blocks, int gq) {
+  Sc8 sc;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int e = group_block<B>(tb, 32 * u + 16 * a, gq);
+      const bool ok = e >= 0 && e < num_blocks;
+      const int64_t idx = static_cast<int64_t>(ok ? e : 0) * hkv + j;
+      const float kv = k_scale[idx], vv = v_scale[idx];
+      sc.k[u][a] = ok ? kv : 0.f;
+      sc.v[u][a] = ok ? vv : 0.f;
+    }
+  return sc;
+}
+
+template <int D, int B>
+__device__ __forceinline__ void read_tile8(Buf8<D>& b, const unsigned char* stage, const Tb<64 / B>& tb, int num_blocks,
+                                           int r, int gq) {
+  constexpr int IMG = D * B;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int tk = 32 * u + 16 * a + r;  // key row
+      const unsigned char* kimg = stage + (tk / B) * IMG + (tk % B) * 16;
+#pragma unroll
+      for (int w = 0; w < D / 64; ++w)
+        b.k[u][a][w] = *reinterpret_cast<const uint4*>(kimg + (gq * (D / 64) + w) * B * 16);
+      const int tv = 32 * u + 16 * a + 4 * gq;  // first token of the value group
+      const unsigned char* vimg = stage + kStageHalf<D> + (tv / B) * IMG + tv % B;
+#pragma unroll
+      for (int mm = 0; mm < D / 16; ++mm) b.v[u][a][mm] = *reinterpret_cast<const uint32_t*>(vimg + (16 * mm + r) * B);
+      const int e = group_block<B>(tb, 32 * u + 16 * a, gq);
+      b.ok[u][a] = e >= 0 && e < num_blocks;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void qk_tile8(f32x4 (&s)[2], const uint4 (&k)[2][D / 64], const QOp<D>& qo) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < D / 32; ++jj) {
+      const uint4 c = k[a][jj >> 1];
+      const bf16x8 kop = (jj & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+      s[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qo.q[jj], s[a], 0, 0, 0);
+    }
+  }
+}
+
+// pv_tile for one FP8 sub-tile: sk[a] = scale_log2 * key scale and sv[a] =
+// value scale of the lane's token group in slab a.
+template <int D>
+__device__ __forceinline__ void pv_tile8(Acc<D>& st, const f32x4 (&s)[2], const uint32_t (&v)[2][D / 16],
+                                         const bool (&ok)[2], int t0, int S, bool full, const float (&sk)[2],
+                                         const float (&sv)[2], int gq) {
+  int n0 = 4, n1 = 4;
+  if (!full) {
+    n0 = ok[0] ? min(max(S - (t0 + 4 * gq), 0), 4) : 0;
+    n1 = ok[1] ? min(max(S - (t0 + 16 + 4 * gq), 0), 4) : 0;
+  }
+  float x[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[a][i] = i < (a ? n1 : n0) ? s[a][i] * sk[a] : -INFINITY;
+      tmax = fmaxf(tmax, x[a][i]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(st.m, tmax);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  st.m = m_new;
+  float psum = 0.f;
+  bf16x8 phi, plo;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(x[a][i] - m_new);
+      psum += p;
+      const float pv = p * sv[a];
+      const __bf16 h = static_cast<__bf16>(pv);
+      phi[4 * a + i] = h;
+      plo[4 * a + i] = static_cast<__bf16>(pv - static_cast<float>(h));
+    }
+  st.z = st.z * alpha + psum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm) st.o[mm] *= alpha;
+  }
+  uint32_t m0 = 0xffffffffu, m1 = 0xffffffffu;
+  if (!full) {  // zero the codes of missing tokens: stale or NaN codes must not reach P.V
+    m0 = n0 >= 4 ? 0xffffffffu : (1u << (8 * n0)) - 1u;
+    m1 = n1 >= 4 ? 0xffffffffu : (1u << (8 * n1)) - 1u;
+  }
+#pragma unroll
+  for (int mm = 0; mm < D / 16; ++mm) {
+    const bf16x8 vop = fp8x8_to_bf16(v[0][mm] & m0, v[1][mm] & m1);
+    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, st.o[mm], 0, 0, 0);
+    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, st.o[mm], 0, 0, 0);
+  }
+}
+
 // End of a piece of segment t: write the normalised output (whole segment) or a summary record.
 template <int D>
 __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slot, int64_t wave_id, uint16_t* out,
@@ -381,13 +567,16 @@ struct Split {
   __device__ int64_t wave_of(int64_t x) const { return ((x + 1) * W - 1) / T; }
 };
 
-template <int D, int B>
+template <int D, int B, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void decode_stream(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+    const uint16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     float* __restrict__ rec, int32_t* __restrict__ prefix_out, int n_seqs, int hq, int hkv, int g, int max_blocks,
     int num_blocks, float scale_log2, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out) {
+    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
+  constexpr int TOK = kTok<F8>;
+  constexpr int NB = TOK / B;
   extern __shared__ int32_t sm[];
   int32_t* s_len = sm;            // [n_seqs] packed attended-token counts (pool part clamped to the table)
   int32_t* s_pre = sm + n_seqs;   // [n_seqs + 1] tile prefix sums
@@ -409,7 +598,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int hn = k_new != nullptr ? 1 : 0;  // pa_decode_step: every row attends to its new token
     const int fits = S_raw >= 0 && S_raw < s_cap ? 1 : 0;
     const int S_att = S + hn;
-    int v = (S_att + 31) >> 5;
+    int v = (S_att + TOK - 1) >> kTokShift<F8>;
 #pragma unroll
     for (int dlt = 1; dlt < 64; dlt <<= 1) {
       const int u = __shfl_up(v, dlt);
@@ -463,10 +652,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // tile's addresses).
   QOp<D> qA, qB;
   TilePos nxt = x1 - x0 > 1 ? advance(cur, s_pre, hkv) : cur;
-  Tb<B> tbA = load_tb<B>(cur, block_tables, max_blocks, s_len);
-  Tb<B> tbB = load_tb<B>(nxt, block_tables, max_blocks, s_len);
-  load_q<D>(qA, cur, q, hq, g, r, gq);
-  dma_tile<D, B>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
+  Tb<NB> tbA = load_tb<B, TOK>(cur, block_tables, max_blocks, s_len);
+  Tb<NB> tbB = load_tb<B, TOK>(nxt, block_tables, max_blocks, s_len);
+  load_q<D, F8>(qA, cur, q, hq, g, r, gq);
+  dma_tile<D, B, F8>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
+  // FP8: the scales of a tile's blocks travel with it, one tile ahead like its Q
+  Sc8 scA{}, scB{};
+  if constexpr (F8) scA = load_scales<B>(tbA, k_scale, v_scale, cur.j, hkv, num_blocks, gq);
 
   int64_t x = x0;
   // One step: tile `cur` (staged in stage SC, Q in qc, blocks tbc) is computed
@@ -475,12 +667,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // after the last tile.
   // the step's new token, for tiles that end a segment holding one
   auto wants_new = [&](TilePos t) -> bool {
-    return k_new != nullptr && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
+    return !F8 && k_new != nullptr && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
   };
   // one buffer: a step patches its tile before it loads the next tile's token
   NewTok<D> ntok;
   if (wants_new(cur)) load_new<D>(ntok, cur, k_new, v_new, slots, hkv, r, gq);
-  auto step = [&](auto sc_tag, QOp<D>& qc, const Tb<B>& tbc, QOp<D>& qn, const Tb<B>& tbn, Tb<B>& tb2) -> bool {
+  auto step = [&](auto sc_tag, QOp<D>& qc, const Tb<NB>& tbc, const Sc8& scc, QOp<D>& qn, const Tb<NB>& tbn,
+                  Sc8& scn, Tb<NB>& tb2) -> bool {
     constexpr int SC = decltype(sc_tag)::value;
     unsigned char(&stc)[4][kStageBytes] = SC == 0 ? g_stage0 : g_stage1;
     unsigned char(&stn)[4][kStageBytes] = SC == 0 ? g_stage1 : g_stage0;
@@ -492,33 +685,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int S = attended_tokens(packed);
     const int nt_cur = tiles_of(s_pre, cur.n);
     const TilePos nxt2 = x + 2 < x1 ? advance(nxt, s_pre, hkv) : nxt;
-    Buf<D> b;
-    read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
-    // keep the stage's LDS reads ahead of the copies below: an LDS read issued
-    // after them would wait for all of them
-    __builtin_amdgcn_sched_barrier(0);
-    const int t0 = cur.ti * 32;
-    if (k_new != nullptr && has_new_token(packed) && cur.ti == nt_cur - 1) {
-      patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
-      // the row's slot, read from wherever the caller keeps it, goes on to the
-      // merge kernel (which stores the token): the slot when it is the row's
-      // next position, else -1
-      if (cur.j == 0 && lane == 0) {
-        const int S0 = pool_tokens(packed);
-        const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
-                             static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
-                             ntok.slot % B == S0 % B;
-        slots_out[cur.n] = at_next ? ntok.slot : -1;
+    const int t0 = cur.ti * TOK;
+    if constexpr (F8) {
+      Buf8<D> b;
+      read_tile8<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
+      __builtin_amdgcn_sched_barrier(0);
+      tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
+      load_q<D, F8>(qn, nxt, q, hq, g, r, gq);
+      scn = load_scales<B>(tbn, k_scale, v_scale, nxt.j, hkv, num_blocks, gq);
+      dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
+      const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4 sco[2];
+        qk_tile8<D>(sco, b.k[u], qc);
+        const float sk[2] = {scale_log2 * scc.k[u][0], scale_log2 * scc.k[u][1]};
+        const float sv[2] = {scc.v[u][0], scc.v[u][1]};
+        pv_tile8<D>(st, sco, b.v[u], b.ok[u], t0 + 32 * u, S, full, sk, sv, gq);
       }
+    } else {
+      Buf<D> b;
+      read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
+      // keep the stage's LDS reads ahead of the copies below: an LDS read issued
+      // after them would wait for all of them
+      __builtin_amdgcn_sched_barrier(0);
+      if (k_new != nullptr && has_new_token(packed) && cur.ti == nt_cur - 1) {
+        patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
+        // the row's slot, read from wherever the caller keeps it, goes on to the
+        // merge kernel (which stores the token): the slot when it is the row's
+        // next position, else -1
+        if (cur.j == 0 && lane == 0) {
+          const int S0 = pool_tokens(packed);
+          const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
+                               static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
+                               ntok.slot % B == S0 % B;
+          slots_out[cur.n] = at_next ? ntok.slot : -1;
+        }
+      }
+      tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
+      load_q<D, F8>(qn, nxt, q, hq, g, r, gq);
+      if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
+      dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
+      const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
+      f32x4 sco[2];
+      qk_tile<D>(sco, b, qc);
+      pv_tile<D>(st, sco, b, t0, S, full, scale_log2, gq);
     }
-    tb2 = load_tb<B>(nxt2, block_tables, max_blocks, s_len);
-    load_q<D>(qn, nxt, q, hq, g, r, gq);
-    if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
-    dma_tile<D, B>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
-    const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
-    f32x4 sco[2];
-    qk_tile<D>(sco, b, qc);
-    pv_tile<D>(st, sco, b, t0, S, full, scale_log2, gq);
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
       flush<D>(st, cur, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, hq, g, r, gq);
@@ -532,8 +744,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     return true;
   };
   while (true) {
-    if (!step(std::integral_constant<int, 0>{}, qA, tbA, qB, tbB, tbA)) break;
-    if (!step(std::integral_constant<int, 1>{}, qB, tbB, qA, tbA, tbB)) break;
+    if (!step(std::integral_constant<int, 0>{}, qA, tbA, scA, qB, tbB, scB, tbA)) break;
+    if (!step(std::integral_constant<int, 1>{}, qB, tbB, scB, qA, tbA, scA, tbB)) break;
   }
 }
 
@@ -730,7 +942,7 @@ __global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ re
 
 template <int D, int B>
 const void* stream_kernel() {
-  return reinterpret_cast<const void*>(&decode_stream<D, B>);
+  return reinterpret_cast<const void*>(&decode_stream<D, B, false>);
 }
 
 const void* stream_kernel_for(int d, int b) {
@@ -786,7 +998,11 @@ bool stream_eligible(int num_seqs, int g, int d, int block_size, int dtype) {
          (block_size == 8 || block_size == 16 || block_size == 32) && num_seqs <= kMaxSeqs;
 }
 
-StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx) {
+bool stream_eligible_fp8(int num_seqs, int g, int d, int block_size) {
+  return stream_eligible(num_seqs, g, d, block_size, PA_BF16);
+}
+
+StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, bool fp8) {
   const DeviceShape& ds = device_shape();
   const int ai = d == 128 ? 1 : 0;
   const int bi = block_size == 8 ? 0 : (block_size == 16 ? 1 : 2);
@@ -800,7 +1016,8 @@ StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int
   }
   int64_t wgs = static_cast<int64_t>(ds.cus) * per_cu;
   // no more waves than tiles / 2 (upper bound of the work from max_context_len)
-  const int64_t t_bound = static_cast<int64_t>(num_seqs) * hkv * ((max_ctx + 31) / 32);
+  const int tok = fp8 ? kTok<true> : kTok<false>;
+  const int64_t t_bound = static_cast<int64_t>(num_seqs) * hkv * ((max_ctx + tok - 1) / tok);
   const int64_t by_work = (t_bound + 2 * kSW - 1) / (2 * kSW);
   if (by_work < wgs) wgs = by_work;
   if (wgs < 1) wgs = 1;
@@ -816,10 +1033,11 @@ StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int
   return p;
 }
 
-template <int D, int B>
+template <int D, int B, bool F8>
 static void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
                              const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv,
-                             int max_blocks, int num_blocks, float scale_log2, const StepInputs* step) {
+                             int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
+                             const float* k_scale, const float* v_scale) {
   char* base = static_cast<char*>(ws);
   int32_t* prefix = reinterpret_cast<int32_t*>(base + p.prefix_offset);
   int32_t* slots_ws = reinterpret_cast<int32_t*>(base + p.slots_offset);
@@ -839,22 +1057,28 @@ static void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, 
     ap.max_blocks = max_blocks;
     ap.block_size = B;
   }
-  decode_stream<D, B><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bt, cl,
-      static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g, max_blocks, num_blocks, scale_log2, ap.k_new,
-      ap.v_new, slots_in, slots_ws);
+  decode_stream<D, B, F8><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
+      static_cast<const uint16_t*>(q), k, v, bt, cl, static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g,
+      max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws, k_scale, v_scale);
   merge_stream<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, prefix, static_cast<uint16_t*>(out), n, hq, hkv, g,
                                                      static_cast<int64_t>(p.workgroups) * kSW, ap);
 }
 
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
-                  int max_blocks, int num_blocks, float scale_log2, const StepInputs* step) {
-#define PA_STREAM_CASE(DD, BB)                                                                            \
-  if (d == DD && block_size == BB) {                                                                      \
-    launch_stream_db<DD, BB>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks, scale_log2, \
-                             step);                                                                       \
-    return launch_status();                                                                               \
+                  int max_blocks, int num_blocks, float scale_log2, const StepInputs* step, const float* k_scale,
+                  const float* v_scale) {
+  const bool f8 = k_scale != nullptr;
+  if (f8 && step) return PA_ERR_UNSUPPORTED;
+#define PA_STREAM_CASE(DD, BB)                                                                               \
+  if (d == DD && block_size == BB) {                                                                         \
+    if (f8)                                                                                                  \
+      launch_stream_db<DD, BB, true>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,     \
+                                     scale_log2, nullptr, k_scale, v_scale);                                 \
+    else                                                                                                     \
+      launch_stream_db<DD, BB, false>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,    \
+                                      scale_log2, step, nullptr, nullptr);                                   \
+    return launch_status();                                                                                  \
   }
   PA_STREAM_CASE(128, 16)
   PA_STREAM_CASE(128, 8)

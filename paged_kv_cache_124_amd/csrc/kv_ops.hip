@@ -1,4 +1,6 @@
-// KV append and copy-on-write block copy kernels (gfx950) and their C entry points.
+// KV append and copy-on-write block copy kernels (gfx950) and their C entry
+// points, for bf16 / fp32 caches and for a cache of FP8 (E4M3) codes with
+// per-(block, KV head) scales.
 //
 // Append: "PagedAttention: Virtual Memory for the KV Cache", section 16 -- the
 // new position's key and value are written into its block at its offset.
@@ -99,16 +101,96 @@ __global__ __launch_bounds__(256) void append_step_kernel(T* __restrict__ k_pool
   for (int e = 0; e < X; ++e) vdst[static_cast<int64_t>(e) * block_size] = vals[e];
 }
 
-// grid = (ceil(2 * n16 / 256), num_pairs, num_layers); each thread moves 16 bytes.
+// ---- FP8 (E4M3) cache ----------------------------------------------------------
+//
+// A value x goes into the cache under scale s as the sign of x and the finite
+// E4M3 magnitude nearest to the real quotient |x| / s, ties to an even
+// mantissa, saturating at 448 (E4M3 of the OCP 8-bit floating point format:
+// exponent bias 7, subnormals, NaN at 0x7F / 0xFF).  The quotient is formed in
+// fp64: for 24-bit x and s it is never rounded across a midpoint the exact
+// quotient does not reach, so the code is the one the exact quotient gives.
+// NaN input, or a scale that is not positive and finite, stores 0x7F.
+__device__ __forceinline__ uint32_t e4m3_code(float x, float s) {
+  if (!(s > 0.f) || !(s < INFINITY) || x != x) return 0x7Fu;
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const double y = fabs(static_cast<double>(x)) / static_cast<double>(s);
+  uint32_t mag;
+  if (y >= 448.0) {
+    mag = 0x7Eu;
+  } else if (y < 0x1p-6) {
+    // subnormal grid 2^-9 (code = multiple of 2^-9); 8 * 2^-9 is the smallest normal, code 0x08
+    mag = static_cast<uint32_t>(rint(y * 512.0));
+  } else {
+    int e2 = 0;
+    (void)frexp(y, &e2);                                  // y = f * 2^e2, f in [0.5, 1)
+    const int e = e2 - 1;                                 // floor(log2 y), -6 .. 8
+    const double m = rint(ldexp(y, 3 - e));               // 8 .. 16 steps of 2^(e-3), ties to even
+    mag = static_cast<uint32_t>((e + 7) * 8) + static_cast<uint32_t>(m) - 8u;  // m = 16 carries into e + 1
+  }
+  return sign | mag;
+}
+
+// One thread per (token, KV head, 16-element key chunk): 16 bf16 in, one
+// 16-byte key store, 16 one-byte value stores (stride B).  The scales of the
+// destination (block, KV head) are read once per thread.
+__global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                         const float* __restrict__ k_scale,
+                                                         const float* __restrict__ v_scale,
+                                                         const uint16_t* __restrict__ k_new,
+                                                         const uint16_t* __restrict__ v_new,
+                                                         const int32_t* __restrict__ slot_mapping, int num_tokens,
+                                                         int hkv, int d, int block_size, int64_t num_slots) {
+  const int chunks = d / 16;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;
+  const int j = static_cast<int>(th % hkv);
+  const int64_t t = th / hkv;
+  if (t >= num_tokens) return;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t pb = slot / block_size;
+  const int off = static_cast<int>(slot % block_size);
+  const int64_t head = pb * hkv + j;
+  const float ks = k_scale[head], vs = v_scale[head];
+  const int64_t src = (t * hkv + j) * d + static_cast<int64_t>(c) * 16;
+  uint16_t kin[16], vin[16];
+  *reinterpret_cast<uint4*>(kin) = *reinterpret_cast<const uint4*>(k_new + src);
+  *reinterpret_cast<uint4*>(kin + 8) = *reinterpret_cast<const uint4*>(k_new + src + 8);
+  *reinterpret_cast<uint4*>(vin) = *reinterpret_cast<const uint4*>(v_new + src);
+  *reinterpret_cast<uint4*>(vin + 8) = *reinterpret_cast<const uint4*>(v_new + src + 8);
+  uint32_t kw[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) kw[e >> 2] |= e4m3_code(bf16_bits_to_f32(kin[e]), ks) << (8 * (e & 3));
+  *reinterpret_cast<uint4*>(k_pool + ((head * chunks + c) * block_size + off) * 16) =
+      make_uint4(kw[0], kw[1], kw[2], kw[3]);
+  uint8_t* vdst = v_pool + (head * d + static_cast<int64_t>(c) * 16) * block_size + off;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    vdst[static_cast<int64_t>(e) * block_size] = static_cast<uint8_t>(e4m3_code(bf16_bits_to_f32(vin[e]), vs));
+}
+
+// grid = (ceil((2 * n16 + 2 * scales_per_block) / 256), num_pairs, num_layers);
+// each thread moves 16 bytes of a block image, or one of the block's (KV
+// head) scales when the pools hold FP8 codes (scales_per_block = Hkv, else 0).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                           const int32_t* __restrict__ pairs, int64_t block_bytes,
-                                                          int num_blocks, int64_t layer_stride_bytes) {
+                                                          int num_blocks, int64_t layer_stride_bytes,
+                                                          float* __restrict__ k_scale, float* __restrict__ v_scale,
+                                                          int scales_per_block, int64_t scale_layer_stride) {
   const int64_t n16 = block_bytes / 16;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= 2 * n16) return;
+  if (idx >= 2 * n16 + 2 * scales_per_block) return;
   const int32_t src = pairs[2 * blockIdx.y];
   const int32_t dst = pairs[2 * blockIdx.y + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (idx >= 2 * n16) {
+    const int64_t i = idx - 2 * n16;
+    float* sc = (i < scales_per_block ? k_scale : v_scale) + static_cast<int64_t>(blockIdx.z) * scale_layer_stride;
+    const int64_t h = i < scales_per_block ? i : i - scales_per_block;
+    sc[static_cast<int64_t>(dst) * scales_per_block + h] = sc[static_cast<int64_t>(src) * scales_per_block + h];
+    return;
+  }
   uint8_t* base = (idx < n16 ? k_pool : v_pool) + static_cast<int64_t>(blockIdx.z) * layer_stride_bytes;
   const int64_t i = idx < n16 ? idx : idx - n16;
   const uint4* s = reinterpret_cast<const uint4*>(base + src * block_bytes) + i;
@@ -203,6 +285,48 @@ extern "C" int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst
   copy_blocks_kernel<<<dim3(static_cast<uint32_t>(gx), num_pairs, num_layers), dim3(256), 0,
                        static_cast<hipStream_t>(stream)>>>(static_cast<uint8_t*>(k_pool),
                                                           static_cast<uint8_t*>(v_pool), src_dst_pairs,
-                                                          block_bytes, num_blocks, layer_stride_bytes);
+                                                          block_bytes, num_blocks, layer_stride_bytes, nullptr,
+                                                          nullptr, 0, 0);
+  return launch_status();
+}
+
+extern "C" int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                                const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+                                int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
+  using namespace pa;
+  if (num_tokens < 0 || num_blocks < 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
+  if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  const int64_t threads = static_cast<int64_t>(num_tokens) * Hkv * (d_head / 16);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
+  append_fp8_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scale, v_scale,
+      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, num_tokens, Hkv, d_head,
+      block_size, static_cast<int64_t>(num_blocks) * block_size);
+  return launch_status();
+}
+
+extern "C" int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                  const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size,
+                                  int num_blocks, int num_layers, int64_t layer_stride_elems,
+                                  int64_t scale_layer_stride, void* stream) {
+  using namespace pa;
+  if (num_pairs < 0 || num_blocks < 0 || num_layers <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !src_dst_pairs) return PA_ERR_INVALID_ARG;
+  if (num_pairs > 65535 || num_layers > 65535) return PA_ERR_UNSUPPORTED;
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * d_head * block_size;
+  if (num_layers > 1 && (layer_stride_elems < static_cast<int64_t>(num_blocks) * block_bytes ||
+                         scale_layer_stride < static_cast<int64_t>(num_blocks) * Hkv))
+    return PA_ERR_INVALID_ARG;
+  const int64_t gx = (2 * (block_bytes / 16) + 2 * Hkv + 255) / 256;
+  copy_blocks_kernel<<<dim3(static_cast<uint32_t>(gx), num_pairs, num_layers), dim3(256), 0,
+                       static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), src_dst_pairs, block_bytes, num_blocks,
+      num_layers > 1 ? layer_stride_elems : 0, k_scale, v_scale, Hkv, num_layers > 1 ? scale_layer_stride : 0);
   return launch_status();
 }

@@ -20,6 +20,13 @@ Workloads (shapes and distributions of the pages' 8B-style GQA example:
            (64 GiB of K and V), bf16, N(0, 1) / sqrt(d)
 Values are drawn in fp32 and rounded once to the storage type; both sides
 read those stored values.
+
+FP8 caches (E4M3 codes with per-(block, KV head) scales) are drawn as codes
+directly: random sign, exponent field round(N(12, 1)) clamped to [0, 15],
+uniform mantissa, the NaN magnitude 0x7F replaced by 0x7E -- the shape of
+amax-scaled normal data -- and fp32 scales value_scale / 78 * U(0.5, 2) per
+(block, KV head), 78 being the RMS of those code values, so that the values
+the cache stands for have an RMS of about value_scale.
 """
 
 from __future__ import annotations
@@ -142,3 +149,30 @@ def fill_randn_(t, scale: float, seed: int, chunk_rows: int = 0):
         t[start:stop].copy_(x)
         del x
     return t
+
+
+FP8_CODE_RMS = 78.0
+
+
+def fill_fp8_codes_(t, seed: int):
+    """Fill a uint8 tensor in place with random E4M3 codes (no NaN codes); see the module docstring."""
+    import torch
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = tuple(t.shape)
+    sign = torch.randint(0, 2, shape, generator=g, dtype=torch.int32)
+    expo = torch.round(torch.randn(shape, generator=g) + 12.0).clamp_(0, 15).to(torch.int32)
+    mant = torch.randint(0, 8, shape, generator=g, dtype=torch.int32)
+    mag = expo * 8 + mant
+    mag = torch.where(mag == 0x7F, torch.full_like(mag, 0x7E), mag)
+    t.copy_((sign * 0x80 + mag).to(torch.uint8))
+    return t
+
+
+def fp8_scales(num_blocks: int, hkv: int, value_scale: float, seed: int, device="cpu"):
+    """float32 [num_blocks][hkv] scales value_scale / FP8_CODE_RMS * U(0.5, 2)."""
+    import torch
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    u = torch.rand((num_blocks, hkv), generator=g) * 1.5 + 0.5
+    return (u * (value_scale / FP8_CODE_RMS)).to(torch.float32).to(device)

@@ -123,3 +123,43 @@ def test_pool_layout_adapter_matches_header_formulas():
             assert vp[((pb * hkv + j) * d + dd) * bs + off] == log[pb, j, off, dd]
         assert torch.equal(k_to_logical(k_to_physical(log)), log)
         assert torch.equal(v_to_logical(v_to_physical(log)), log)
+
+
+def test_fp8_host_validation():
+    import paged_kv_cache_124_amd as pa
+    L = pa.lib
+    # pa_decode_fp8(out, q, k, v, k_scale, v_scale, tables, lens, n, Hq, Hkv, d, B, scale, maxb, maxctx, nb, ws, wsb, stream)
+    need = pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, pa.PA_FP8_E4M3)
+    assert need > 0 and need == pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 8192, pa.PA_FP8_E4M3)
+    assert pa.pa_decode_partition_tokens(64, 32, 8, 128, 16, 4096, pa.PA_FP8_E4M3) == 0
+
+    def dec(n=4, hq=32, hkv=8, d=128, bs=16, ks=FAKE, ws=FAKE, wsb=None):
+        wsb = need if wsb is None else wsb
+        return L.pa_decode_fp8(FAKE, FAKE, FAKE, FAKE, ks, FAKE, FAKE, FAKE, n, hq, hkv, d, bs, 0.088, 256, 4096,
+                               1000, ws, wsb, NUL)
+    assert dec(n=0) == 0
+    assert dec(hq=30) == 1
+    assert dec(hq=64, hkv=2) == 2        # 32 query heads per KV head: not served
+    assert dec(d=96) == 2 and dec(bs=64) == 2
+    assert dec(ks=NUL) == 1
+    assert dec(ws=NUL) == 6 and dec(wsb=16) == 6
+    # pa_append_kv_fp8(k, v, k_scale, v_scale, k_new, v_new, slots, T, Hkv, d, B, nb, stream)
+    assert L.pa_append_kv_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, NUL) == 0
+    assert L.pa_append_kv_fp8(FAKE, FAKE, NUL, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 100, NUL) == 1
+    assert L.pa_append_kv_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 16, 100, NUL) == 2
+    # pa_copy_blocks_fp8(k, v, k_scale, v_scale, pairs, P, Hkv, d, B, nb, layers, stride, scale_stride, stream)
+    assert L.pa_copy_blocks_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, 1, 0, 0, NUL) == 0
+    assert L.pa_copy_blocks_fp8(FAKE, FAKE, NUL, FAKE, FAKE, 2, 8, 128, 16, 100, 1, 0, 0, NUL) == 1
+    full = 100 * 8 * 128 * 16
+    assert L.pa_copy_blocks_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 100, 2, full, 10, NUL) == 1
+
+
+def test_fp8_pool_layout_adapter_matches_header_formulas():
+    from pool_layout import k_to_logical, k_to_physical
+    nb, hkv, bs, d, x = 3, 2, 8, 32, 16
+    log = (torch.arange(nb * hkv * bs * d) % 251).to(torch.uint8).reshape(nb, hkv, bs, d)
+    kp = k_to_physical(log).flatten()
+    for pb, j, off, dd in ((0, 0, 0, 0), (2, 1, 7, 31), (1, 0, 3, 17), (2, 0, 5, 4)):
+        assert kp[(((pb * hkv + j) * (d // x) + dd // x) * bs + off) * x + dd % x] == log[pb, j, off, dd]
+    assert torch.equal(k_to_logical(k_to_physical(log)), log)
+
