@@ -18,7 +18,13 @@ timed region starts.  `value` is the KV bytes the decode reads per step
 (sum of context lengths x 2 x Hkv x d_head x 2 bytes) divided by the
 wall-clock time of a step.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa8b]
+With --kv fp8 the cache holds FP8 (E4M3) codes with per-(block, KV head)
+scales and steps 3-4 are pa_copy_blocks_fp8 (when there are pairs),
+pa_append_step_fp8 (quantizing append, rows moved forward) and
+pa_decode_fp8; the KV bytes per step are then the codes (1 byte per element)
+plus the 8 bytes of scales per (block, KV head) the contexts span.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa8b] [--kv bf16|fp8]
 """
 
 from __future__ import annotations
@@ -43,17 +49,19 @@ RING = 32
 
 # HBM traffic of the decode kernels, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a
 # plain copy of known size; valid only while the kernel sources are those it was taken on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_gqa8b_traffic.txt")
+TRAFFIC_FILES = {"bf16": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_traffic.txt"),
+                 "fp8": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_fp8_traffic.txt")}
 KERNEL_SOURCES = ["decode_stream.hip", "decode_stream.h", "decode.hip", "common.h"]
 
 
-def measured_traffic(workload_name):
-    """(fetched + written bytes per pa_decode launch, algorithmic bytes of those launches), or None."""
+def measured_traffic(workload_name, kv_kind="bf16"):
+    """(fetched + written bytes per decode launch, algorithmic bytes of those launches), or None."""
     import hashlib
-    if workload_name != "gqa8b" or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES[kv_kind]
+    if workload_name != "gqa8b" or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
@@ -76,6 +84,8 @@ def parse():
     ap.add_argument("--workload", default="gqa8b", choices=["gqa8b", "sweep_b8", "sweep_b16", "sweep_b32"])
     ap.add_argument("--replicas", type=int, default=4,
                     help="pool copies rotated step to step so reads come from HBM, not the 256 MB Infinity Cache")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="cache element type: bf16, or FP8 E4M3 codes with per-(block, KV head) scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -93,13 +103,14 @@ def workload(name):
 class Runner:
     """Holds the resident state of one benchmark workload."""
 
-    def __init__(self, w, steps_total, replicas, device="cuda"):
+    def __init__(self, w, steps_total, replicas, device="cuda", kv_kind="bf16"):
         import torch
         import synth
         import paged_kv_cache_124_amd as pa
         self.pa = pa
         self.torch = torch
         self.w = w
+        self.fp8 = kv_kind == "fp8"
         self.lens0 = synth.seq_lengths(w)
         self.n = len(self.lens0)
         bs = w.block_size
@@ -112,16 +123,28 @@ class Runner:
             assert self.bm.add_seq(i, s) == 0
         self.seqs = np.arange(self.n, dtype=np.int64)
         dt = synth.torch_dtype(w)
-        kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, torch.tensor([], dtype=dt).element_size())
-        self.k = [synth.fill_randn_(torch.empty(kshape, dtype=dt, device=device), w.value_scale, w.seed * 10 + 1 + 7 * r)
-                  for r in range(replicas)]
-        self.v = [synth.fill_randn_(torch.empty(vshape, dtype=dt, device=device), w.value_scale, w.seed * 10 + 2 + 7 * r)
-                  for r in range(replicas)]
+        if self.fp8:
+            kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, 1)
+            self.k = [synth.fill_fp8_codes_(torch.empty(kshape, dtype=torch.uint8, device=device), w.seed * 10 + 1 + 7 * r)
+                      for r in range(replicas)]
+            self.v = [synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8, device=device), w.seed * 10 + 2 + 7 * r)
+                      for r in range(replicas)]
+            self.ks = [synth.fp8_scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 8 + 7 * r, device)
+                       for r in range(replicas)]
+            self.vs = [synth.fp8_scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 9 + 7 * r, device)
+                       for r in range(replicas)]
+        else:
+            kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, torch.tensor([], dtype=dt).element_size())
+            self.k = [synth.fill_randn_(torch.empty(kshape, dtype=dt, device=device), w.value_scale,
+                                        w.seed * 10 + 1 + 7 * r) for r in range(replicas)]
+            self.v = [synth.fill_randn_(torch.empty(vshape, dtype=dt, device=device), w.value_scale,
+                                        w.seed * 10 + 2 + 7 * r) for r in range(replicas)]
         self.q = synth.randn((self.n, w.hq, w.d), dt, w.value_scale, w.seed * 10 + 3, device)
         self.k_new = synth.randn((self.n, w.hkv, w.d), dt, w.value_scale, w.seed * 10 + 4, device)
         self.v_new = synth.randn((self.n, w.hkv, w.d), dt, w.value_scale, w.seed * 10 + 5, device)
         self.out = torch.empty_like(self.q)
-        ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
+        ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx,
+                                          pa.PA_FP8_E4M3 if self.fp8 else pa.PA_BF16)
         self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)  # zero before first use
         self.part = pa.pa_decode_partition_tokens(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
         # Block tables and lengths live on the device; pa_append_step moves them forward.
@@ -165,18 +188,33 @@ class Runner:
             self.append_slots_args.append((self.bm.handle, self.seqs_p, n, ctypes.cast(base, p32),
                                            ctypes.cast(base + 4 * n, p32), ctypes.byref(self.npairs)))
         check = torch.empty(self.words, dtype=torch.int32, device=device)  # shapes for validation only
-        self.step_args, self.copy_args = {}, {}
+        self.step_args, self.copy_args, self.append_args = {}, {}, {}
         for r in range(replicas):
-            cpy = pa.pa_copy_blocks_args(self.k[r], self.v[r], check[n:3 * n].view(n, 2))
+            if self.fp8:
+                cpy = pa.pa_copy_blocks_fp8_args(self.k[r], self.v[r], self.ks[r], self.vs[r], check[n:3 * n].view(n, 2))
+                app = pa.pa_append_step_fp8_args(self.k[r], self.v[r], self.ks[r], self.vs[r], self.k_new, self.v_new,
+                                                 check[:n], self.d_tables, self.d_lens)
+                dec, _ = pa.pa_decode_fp8_args(self.out, self.q, self.k[r], self.v[r], self.ks[r], self.vs[r],
+                                               self.d_tables, self.d_lens, w.scale, self.max_ctx, workspace=self.ws)
+            else:
+                cpy = pa.pa_copy_blocks_args(self.k[r], self.v[r], check[n:3 * n].view(n, 2))
             for b in range(RING):
                 base = self.mapped[b] if self.zero_copy else self.dev[b].data_ptr()
-                self.step_args[r, b], _ = pa.pa_decode_step_args(
-                    self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], check[:n], self.d_tables,
-                    self.d_lens, w.scale, self.max_ctx, workspace=self.ws, slot_pointer=base)
-                self.copy_args[r, b] = list(cpy[:2]) + [ctypes.c_void_p(base + 4 * n)] + list(cpy[3:])
+                pairs_at = 4 if self.fp8 else 2  # position of src_dst_pairs in the copy call
+                self.copy_args[r, b] = (list(cpy[:pairs_at]) + [ctypes.c_void_p(base + 4 * n)] +
+                                        list(cpy[pairs_at + 1:]))
+                if self.fp8:
+                    self.append_args[r, b] = app[:6] + (ctypes.c_void_p(base),) + app[7:]
+                    self.step_args[r, b] = dec
+                else:
+                    self.step_args[r, b], _ = pa.pa_decode_step_args(
+                        self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], check[:n], self.d_tables,
+                        self.d_lens, w.scale, self.max_ctx, workspace=self.ws, slot_pointer=base)
         self.step_i = 0
-        self.kv_bytes_per_token = 2 * w.hkv * w.d * 2
-        self.lens_sum = sum(self.lens0)
+        # KV bytes the decode reads per token of context, and per (block, KV head) of it (FP8 scales)
+        self.kv_bytes_per_token = 2 * w.hkv * w.d * (1 if self.fp8 else 2)
+        self.scale_bytes_per_block = 2 * w.hkv * 4 if self.fp8 else 0
+        self.lens = np.array(self.lens0, dtype=np.int64)
         self.host_s = 0.0
 
     def step(self, timing=None):
@@ -194,22 +232,35 @@ class Runner:
             words = self.n + 2 * npairs
             self.dev[k][:words].copy_(self.host[k][:words], non_blocking=True)
         r = self.step_i % self.replicas
-        if npairs:
-            ca = self.copy_args[r, k]
-            ca[3] = npairs
-            assert L.pa_copy_blocks(*ca) == 0
-        if timing is not None:
-            timing[0].record()
-        assert L.pa_decode_step(*self.step_args[r, k]) == 0
-        if timing is not None:
-            timing[1].record()
+        if self.fp8:
+            if npairs:
+                ca = self.copy_args[r, k]
+                ca[5] = npairs
+                assert L.pa_copy_blocks_fp8(*ca) == 0
+            assert L.pa_append_step_fp8(*self.append_args[r, k]) == 0
+            if timing is not None:
+                timing[0].record()
+            assert L.pa_decode_fp8(*self.step_args[r, k]) == 0
+            if timing is not None:
+                timing[1].record()
+        else:
+            if npairs:
+                ca = self.copy_args[r, k]
+                ca[3] = npairs
+                assert L.pa_copy_blocks(*ca) == 0
+            if timing is not None:
+                timing[0].record()
+            assert L.pa_decode_step(*self.step_args[r, k]) == 0
+            if timing is not None:
+                timing[1].record()
         if k % half == half - 1:
             self.half_ev[k // half].record()
             self.half_used[k // half] = True
         self.step_i += 1
-        self.lens_sum += self.n
+        self.lens += 1
         self.host_s += time.perf_counter() - t_host
-        return self.lens_sum * self.kv_bytes_per_token
+        bs = self.w.block_size
+        return int(self.lens.sum()) * self.kv_bytes_per_token + int((-(-self.lens // bs)).sum()) * self.scale_bytes_per_block
 
     def check_device_batch(self):
         """The device tables and lengths still equal the block manager's (after the timed steps)."""
@@ -219,44 +270,63 @@ class Runner:
             raise RuntimeError("device block tables / lengths diverged from the block manager")
 
 
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, kv_kind="bf16"):
     """The fp64 oracle on this host's cores over a bounded sample of the same workload (one BLAS thread).
 
-    Inputs (one decode step of every sequence, values as stored in bf16) are
-    built first and kept in host memory; then whole passes over all sequences
-    are timed until `seconds` of compute have accumulated.
+    Inputs (one decode step of every sequence, values as stored in bf16, or
+    FP8 codes and scales) are built first and kept in host memory; then whole
+    passes over all sequences are timed until `seconds` of compute have
+    accumulated.
     """
     import torch
     import synth
     from threadpoolctl import threadpool_limits
     from oracle import attention as OA
+    from oracle import fp8 as OF
+    fp8 = kv_kind == "fp8"
     lens = synth.seq_lengths(w)
     rng = np.random.default_rng(0)
     bs, hkv, d = w.block_size, w.hkv, w.d
     inputs = []
     for n, s in enumerate(lens):
         nb = -(-s // bs)
-        kp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 5000 + n).float().numpy()
-        vp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 6000 + n).float().numpy()
+        if fp8:
+            kp = synth.fill_fp8_codes_(torch.empty((nb, hkv, bs, d), dtype=torch.uint8), 5000 + n).numpy()
+            vp = synth.fill_fp8_codes_(torch.empty((nb, hkv, bs, d), dtype=torch.uint8), 6000 + n).numpy()
+            ks = synth.fp8_scales(nb, hkv, w.value_scale, 8000 + n).double().numpy()
+            vs = synth.fp8_scales(nb, hkv, w.value_scale, 9000 + n).double().numpy()
+        else:
+            kp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 5000 + n).float().numpy()
+            vp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 6000 + n).float().numpy()
+            ks = vs = None
         q = synth.randn((1, w.hq, d), torch.bfloat16, w.value_scale, 7000 + n).double().numpy()
         table = rng.permutation(nb)[None]
         kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
         kp2[table[0]] = kp
         vp2[table[0]] = vp
-        inputs.append((q, kp2, vp2, table, s))
-    step_bytes = sum(lens) * 2 * hkv * d * 2
+        if fp8:
+            ks2, vs2 = np.empty_like(ks), np.empty_like(vs)
+            ks2[table[0]] = ks
+            vs2[table[0]] = vs
+            ks, vs = ks2, vs2
+        inputs.append((q, kp2, vp2, ks, vs, table, s))
+    step_bytes = sum(lens) * 2 * hkv * d * (1 if fp8 else 2) + (sum(-(-s // bs) for s in lens) * 2 * hkv * 4 if fp8 else 0)
     passes, t_total = 0, 0.0
     with threadpool_limits(limits=1):
         torch.set_num_threads(1)
         while t_total < seconds:
             t0 = time.perf_counter()
-            for q, kp, vp, table, s in inputs:
-                OA.paged_decode(q, kp, vp, table, [s], w.scale)
+            for q, kp, vp, ks, vs, table, s in inputs:
+                if fp8:
+                    OF.paged_decode(q, kp, vp, ks, vs, table, [s], w.scale)
+                else:
+                    OA.paged_decode(q, kp, vp, table, [s], w.scale)
             t_total += time.perf_counter() - t0
             passes += 1
     return {"value": round(passes * step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} passes over one decode step of all {len(lens)} sequences of the same workload "
-                      f"(all {w.hq} query heads; fp64 NumPy oracle, one thread), {t_total:.1f} s of compute",
+                      f"({'FP8 cache, ' if fp8 else ''}all {w.hq} query heads; fp64 NumPy oracle, one thread), "
+                      f"{t_total:.1f} s of compute",
             "us_per_step": round(t_total / passes * 1e6, 1)}
 
 
@@ -280,7 +350,7 @@ def main():
     w = workload(args.workload)
     total = args.steps + args.warmup + 1
     print(f"[bench] building workload {w.name}", file=sys.stderr, flush=True)
-    run = Runner(w, total, args.replicas)
+    run = Runner(w, total, args.replicas, kv_kind=args.kv)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run.step()
@@ -314,7 +384,8 @@ def main():
     dec_avg_us = sum(dec_us) / len(dec_us)
     bytes_per_launch = kv_bytes / args.steps
     achieved = sampled_bytes / (sum(dec_us) * 1e-6) / 1e9
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name, args.kv)
+    fp8 = args.kv == "fp8"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -326,10 +397,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 cache, bf16 q/out" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, block {w.block_size}, "
-                               f"bf16, contexts {min(run.lens0)}..{max(run.lens0)} growing 1/step",
+        "config": {"workload": f"{w.name}{'-fp8' if fp8 else ''}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, "
+                               f"block {w.block_size}, {'FP8 E4M3 cache with per-(block, KV head) scales' if fp8 else 'bf16'}, "
+                               f"contexts {min(run.lens0)}..{max(run.lens0)} growing 1/step",
                    "num_seqs": run.n, "block_size": w.block_size, "pool_blocks": run.num_blocks,
                    "pool_replicas": args.replicas, "partition_tokens": run.part,
                    "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2),
@@ -339,12 +411,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),
-                     "kernel": "pa_decode_step (decode kernel + merge/append kernel)", "avg_us": round(dec_avg_us, 2),
+                     "kernel": "pa_decode_fp8 (decode kernel + merge kernel)" if fp8 else
+                               "pa_decode_step (decode kernel + merge/append kernel)", "avg_us": round(dec_avg_us, 2),
                      "launches_timed": len(dec_us)},
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.kv)
     print(json.dumps(res), flush=True)
 
 

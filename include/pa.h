@@ -273,6 +273,16 @@ int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const flo
                      const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
                      int Hkv, int d_head, int block_size, int num_blocks, void* stream);
 
+/* pa_append_step into an FP8 cache: the codes as pa_append_kv_fp8 stores
+ * them (row n's token at slot_mapping[n]) and each row moved forward as
+ * pa_append_step does (block_tables[n][S / B] = slot / B, context_lens[n] =
+ * S + 1 when the slot is the row's next position).  k_new, v_new bf16
+ * [num_seqs][Hkv][d_head]; other arguments as for pa_append_step. */
+int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+                       const void* v_new, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                       int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
+                       void* stream);
+
 /* pa_copy_blocks for an FP8 cache: codes of block src over block dst, and its
  * scales with them, k_scale[dst][*] = k_scale[src][*] and likewise v_scale
  * ("PagedAttention: Virtual Memory for the KV Cache", sections 15-16).

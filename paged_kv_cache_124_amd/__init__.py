@@ -20,6 +20,8 @@ from ._lib import (  # noqa: F401
     pa_append_kv_fp8_args,
     pa_append_step,
     pa_append_step_args,
+    pa_append_step_fp8,
+    pa_append_step_fp8_args,
     pa_copy_blocks,
     pa_copy_blocks_args,
     pa_copy_blocks_fp8,

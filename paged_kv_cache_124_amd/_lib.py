@@ -73,6 +73,7 @@ _SIGS = {
     "pa_decode_fp8": (c_int, [c_void_p] * 8 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
     "pa_append_kv_fp8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
     "pa_copy_blocks_fp8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
+    "pa_append_step_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
     "pa_bm_create": (c_void_p, [c_int, c_int, _P32]),
     "pa_bm_destroy": (None, [c_void_p]),
     "pa_bm_add_seq": (c_int, [c_void_p, c_int64, c_int]),
@@ -391,6 +392,38 @@ def pa_append_kv_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mappin
     """pa_append_kv_fp8 of include/pa.h: quantize bf16 k_new/v_new [T][Hkv][D] into their slots."""
     _check(lib.pa_append_kv_fp8(*pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
                                                        slot_mapping, stream)), "pa_append_kv_fp8")
+
+
+def pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables,
+                            context_lens, stream=None):
+    """Validate once and return the argument tuple for ``lib.pa_append_step_fp8(*args)``."""
+    import torch
+    nb, hkv, d, bs = _fp8_pools(k_pool, v_pool)
+    _scales(k_scale, v_scale, nb, hkv)
+    n = k_new.shape[0]
+    if tuple(k_new.shape) != (n, hkv, d) or tuple(v_new.shape) != (n, hkv, d):
+        raise ValueError("k_new / v_new must be [N][Hkv][D]")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new / v_new must be bf16")
+    for t, name in ((slot_mapping, "slot_mapping"), (block_tables, "block_tables"), (context_lens, "context_lens")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if tuple(slot_mapping.shape) != (n,) or tuple(context_lens.shape) != (n,):
+        raise ValueError("slot_mapping and context_lens must be [N]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != n:
+        raise ValueError("block_tables must be [N][max_blocks]")
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+            _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), n, block_tables.shape[1], hkv, d,
+            bs, nb, _stream_ptr(stream))
+
+
+def pa_append_step_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables, context_lens,
+                       stream=None):
+    """pa_append_step_fp8 of include/pa.h: quantizing append of row n's token and the row moved forward."""
+    _check(lib.pa_append_step_fp8(*pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+                                                           slot_mapping, block_tables, context_lens, stream)),
+           "pa_append_step_fp8")
 
 
 def pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):

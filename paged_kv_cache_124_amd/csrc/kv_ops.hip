@@ -130,20 +130,25 @@ __device__ __forceinline__ uint32_t e4m3_code(float x, float s) {
   return sign | mag;
 }
 
-// One thread per (token, KV head, 16-element key chunk): 16 bf16 in, one
-// 16-byte key store, 16 one-byte value stores (stride B).  The scales of the
-// destination (block, KV head) are read once per thread.
+// One thread per (token, KV head, 4 consecutive elements): a 4-byte store of
+// four key codes (inside one 16-code chunk) and four one-byte value stores
+// (stride B).  Four elements per thread keep enough waves in flight to hide
+// the fp64 division of each element.  With block_tables non-null (a decode
+// step, token n = row n) the thread of (n, head 0, elements 0..3) also moves
+// the row forward, as append_step_kernel does.
 __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          const float* __restrict__ k_scale,
                                                          const float* __restrict__ v_scale,
                                                          const uint16_t* __restrict__ k_new,
                                                          const uint16_t* __restrict__ v_new,
                                                          const int32_t* __restrict__ slot_mapping, int num_tokens,
-                                                         int hkv, int d, int block_size, int64_t num_slots) {
-  const int chunks = d / 16;
+                                                         int hkv, int d, int block_size, int64_t num_slots,
+                                                         int32_t* __restrict__ block_tables,
+                                                         int32_t* __restrict__ context_lens, int max_blocks) {
+  const int quads = d / 4;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int c = static_cast<int>(gid % chunks);
-  const int64_t th = gid / chunks;
+  const int c4 = static_cast<int>(gid % quads);
+  const int64_t th = gid / quads;
   const int j = static_cast<int>(th % hkv);
   const int64_t t = th / hkv;
   if (t >= num_tokens) return;
@@ -151,23 +156,29 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k
   if (slot < 0 || slot >= num_slots) return;
   const int64_t pb = slot / block_size;
   const int off = static_cast<int>(slot % block_size);
+  if (block_tables != nullptr && j == 0 && c4 == 0) {
+    const int pos = context_lens[t];
+    if (pos >= 0 && pos / block_size < max_blocks && pos % block_size == off) {
+      block_tables[t * max_blocks + pos / block_size] = static_cast<int32_t>(pb);
+      context_lens[t] = pos + 1;
+    }
+  }
   const int64_t head = pb * hkv + j;
   const float ks = k_scale[head], vs = v_scale[head];
-  const int64_t src = (t * hkv + j) * d + static_cast<int64_t>(c) * 16;
-  uint16_t kin[16], vin[16];
-  *reinterpret_cast<uint4*>(kin) = *reinterpret_cast<const uint4*>(k_new + src);
-  *reinterpret_cast<uint4*>(kin + 8) = *reinterpret_cast<const uint4*>(k_new + src + 8);
-  *reinterpret_cast<uint4*>(vin) = *reinterpret_cast<const uint4*>(v_new + src);
-  *reinterpret_cast<uint4*>(vin + 8) = *reinterpret_cast<const uint4*>(v_new + src + 8);
-  uint32_t kw[4] = {0, 0, 0, 0};
+  const int e0 = c4 * 4;  // first element
+  const int64_t src = (t * hkv + j) * d + e0;
+  const uint2 kin = *reinterpret_cast<const uint2*>(k_new + src);
+  const uint2 vin = *reinterpret_cast<const uint2*>(v_new + src);
+  const uint32_t kb[4] = {kin.x & 0xffffu, kin.x >> 16, kin.y & 0xffffu, kin.y >> 16};
+  const uint32_t vb[4] = {vin.x & 0xffffu, vin.x >> 16, vin.y & 0xffffu, vin.y >> 16};
+  uint32_t kw = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) kw[e >> 2] |= e4m3_code(bf16_bits_to_f32(kin[e]), ks) << (8 * (e & 3));
-  *reinterpret_cast<uint4*>(k_pool + ((head * chunks + c) * block_size + off) * 16) =
-      make_uint4(kw[0], kw[1], kw[2], kw[3]);
-  uint8_t* vdst = v_pool + (head * d + static_cast<int64_t>(c) * 16) * block_size + off;
+  for (int e = 0; e < 4; ++e) kw |= e4m3_code(bf16_bits_to_f32(kb[e]), ks) << (8 * e);
+  *reinterpret_cast<uint32_t*>(k_pool + ((head * (d / 16) + e0 / 16) * block_size + off) * 16 + e0 % 16) = kw;
+  uint8_t* vdst = v_pool + (head * d + e0) * block_size + off;
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    vdst[static_cast<int64_t>(e) * block_size] = static_cast<uint8_t>(e4m3_code(bf16_bits_to_f32(vin[e]), vs));
+  for (int e = 0; e < 4; ++e)
+    vdst[static_cast<int64_t>(e) * block_size] = static_cast<uint8_t>(e4m3_code(bf16_bits_to_f32(vb[e]), vs));
 }
 
 // grid = (ceil((2 * n16 + 2 * scales_per_block) / 256), num_pairs, num_layers);
@@ -298,13 +309,35 @@ extern "C" int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale
   if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
-  const int64_t threads = static_cast<int64_t>(num_tokens) * Hkv * (d_head / 16);
+  const int64_t threads = static_cast<int64_t>(num_tokens) * Hkv * (d_head / 4);
   const int64_t grid = (threads + 255) / 256;
   if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
   append_fp8_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scale, v_scale,
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, num_tokens, Hkv, d_head,
-      block_size, static_cast<int64_t>(num_blocks) * block_size);
+      block_size, static_cast<int64_t>(num_blocks) * block_size, nullptr, nullptr, 0);
+  return launch_status();
+}
+
+extern "C" int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                                  const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                  int32_t* block_tables, int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
+                                  int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
+  using namespace pa;
+  if (num_seqs < 0 || num_blocks < 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
+  if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !slot_mapping || !block_tables ||
+      !context_lens)
+    return PA_ERR_INVALID_ARG;
+  const int64_t threads = static_cast<int64_t>(num_seqs) * Hkv * (d_head / 4);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
+  append_fp8_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scale, v_scale,
+      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, num_seqs, Hkv, d_head,
+      block_size, static_cast<int64_t>(num_blocks) * block_size, block_tables, context_lens, max_blocks_per_seq);
   return launch_status();
 }
 

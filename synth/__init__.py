@@ -154,18 +154,26 @@ def fill_randn_(t, scale: float, seed: int, chunk_rows: int = 0):
 FP8_CODE_RMS = 78.0
 
 
-def fill_fp8_codes_(t, seed: int):
-    """Fill a uint8 tensor in place with random E4M3 codes (no NaN codes); see the module docstring."""
+def fill_fp8_codes_(t, seed: int, chunk_rows: int = 0):
+    """Fill a uint8 tensor in place with random E4M3 codes (no NaN codes); see the module docstring.
+
+    Drawn on the tensor's device, chunk by chunk along dim 0 (seed per chunk).
+    """
     import torch
-    g = torch.Generator(device="cpu")
-    g.manual_seed(seed)
-    shape = tuple(t.shape)
-    sign = torch.randint(0, 2, shape, generator=g, dtype=torch.int32)
-    expo = torch.round(torch.randn(shape, generator=g) + 12.0).clamp_(0, 15).to(torch.int32)
-    mant = torch.randint(0, 8, shape, generator=g, dtype=torch.int32)
-    mag = expo * 8 + mant
-    mag = torch.where(mag == 0x7F, torch.full_like(mag, 0x7E), mag)
-    t.copy_((sign * 0x80 + mag).to(torch.uint8))
+    rows = t.shape[0]
+    if chunk_rows <= 0:
+        chunk_rows = max(1, (1 << 26) // max(1, t[0].numel()))
+    g = torch.Generator(device=t.device)
+    for i, start in enumerate(range(0, rows, chunk_rows)):
+        stop = min(rows, start + chunk_rows)
+        g.manual_seed(seed * 1000003 + i)
+        shape = tuple(t[start:stop].shape)
+        sign = torch.randint(0, 2, shape, generator=g, dtype=torch.int32, device=t.device)
+        expo = torch.round(torch.randn(shape, generator=g, device=t.device) + 12.0).clamp_(0, 15).to(torch.int32)
+        mant = torch.randint(0, 8, shape, generator=g, dtype=torch.int32, device=t.device)
+        mag = expo * 8 + mant
+        mag = torch.where(mag == 0x7F, torch.full_like(mag, 0x7E), mag)
+        t[start:stop].copy_((sign * 0x80 + mag).to(torch.uint8))
     return t
 
 

@@ -94,8 +94,8 @@ def make_case(w: synth.Workload, lens: Optional[Sequence[int]] = None, *, hq=Non
     if fp8:
         assert layers == 1
         kshape, vshape = pa.pool_shapes(num_blocks, hkv, d, bs, 1)
-        k = synth.fill_fp8_codes_(torch.empty(kshape, dtype=torch.uint8), seed * 10 + 1).to(device)
-        v = synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8), seed * 10 + 2).to(device)
+        k = synth.fill_fp8_codes_(torch.empty(kshape, dtype=torch.uint8, device=device), seed * 10 + 1)
+        v = synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8, device=device), seed * 10 + 2)
         ks = synth.fp8_scales(num_blocks, hkv, w.value_scale, seed * 10 + 4, device)
         vs = synth.fp8_scales(num_blocks, hkv, w.value_scale, seed * 10 + 5, device)
         if poison:  # NaN codes in unused blocks and tail slots, NaN scales on unused blocks

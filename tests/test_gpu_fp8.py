@@ -214,3 +214,63 @@ def test_fp8_unsupported_shapes_are_refused():
     with pytest.raises(pa.PAError) as e:
         run_decode(c)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 8)])
+def test_append_step_fp8_tracks_block_manager(d, bs):
+    """Decode steps over an FP8 cache with device-resident tables: copy-on-write (codes and scales), then
+    pa_append_step_fp8.  After every step the device tables and lengths equal the block manager's and the
+    codes and scales equal the oracle's copy + quantizing append.  Prompts of 2B + 7 tokens forked into 3
+    samples; one step leaves a row out (slot -1)."""
+    import paged_kv_cache_124_amd as pa
+    from oracle.block_manager import BlockManagerModel
+    print(f"[case] append_step fp8 d={d} bs={bs}", flush=True)
+    hkv, prompts, samples, steps = 2, 4, 3, bs + 3
+    n = prompts * samples
+    nb = n * (-(-(2 * bs + 7 + steps) // bs)) + 8
+    mb = -(-(2 * bs + 7 + steps) // bs)
+    kshape, vshape = pa.pool_shapes(nb, hkv, d, bs, 1)
+    k = synth.fill_fp8_codes_(torch.empty(kshape, dtype=torch.uint8), 61).cuda()
+    v = synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8), 62).cuda()
+    ks = synth.fp8_scales(nb, hkv, 0.09, 63, "cuda")
+    vs = synth.fp8_scales(nb, hkv, 0.09, 64, "cuda")
+    order = synth.pop_order(nb, 7)
+    bm = pa.BlockManager(nb, bs, order)
+    model = BlockManagerModel(nb, bs, [int(x) for x in order])
+    for x in (bm, model):
+        for p in range(prompts):
+            assert x.add_seq(p * samples, 2 * bs + 7) == 0
+            for s_ in range(1, samples):
+                assert x.fork(p * samples, p * samples + s_) == 0
+    seqs = list(range(n))
+    st, tables, lens = bm.build_batch(seqs, mb)
+    assert st == 0
+    d_tables = torch.from_numpy(tables).cuda()
+    d_lens = torch.from_numpy(lens).cuda()
+    ek, ev = _logical_pools(k, v)
+    eks, evs = ks.cpu().double().numpy(), vs.cpu().double().numpy()
+    skip_step, skip_row = 2, 4
+    for step in range(steps):
+        active = [s_ for s_ in seqs if not (step == skip_step and s_ == skip_row)]
+        st, slots, pairs, _ = bm.append_slots(active)
+        mst, mslots, mpairs, _ = model.append_slots(active)
+        assert st == mst == 0 and list(slots) == mslots and [tuple(p) for p in pairs] == mpairs
+        row_slots = np.full(n, -1, dtype=np.int32)
+        row_slots[active] = slots
+        if len(pairs):
+            pa.pa_copy_blocks_fp8(k, v, ks, vs, torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda())
+        kn = synth.randn((n, hkv, d), torch.bfloat16, 0.09, 1000 + step, "cuda")
+        vn = synth.randn((n, hkv, d), torch.bfloat16, 0.09, 2000 + step, "cuda")
+        pa.pa_append_step_fp8(k, v, ks, vs, kn, vn, torch.from_numpy(row_slots).cuda(), d_tables, d_lens)
+        torch.cuda.synchronize()
+        st, tables, lens = bm.build_batch(seqs, mb)
+        assert st == 0
+        assert np.array_equal(d_tables.cpu().numpy(), tables), f"tables differ after step {step}"
+        assert np.array_equal(d_lens.cpu().numpy(), lens), f"lengths differ after step {step}"
+        OF.copy_blocks(ek, ev, eks, evs, mpairs)
+        OF.append_kv(ek, ev, eks, evs, kn.float().cpu().numpy().astype(np.float64),
+                     vn.float().cpu().numpy().astype(np.float64), list(row_slots))
+        gk, gv = _logical_pools(k, v)
+        assert np.array_equal(gk, ek) and np.array_equal(gv, ev), f"codes differ after step {step}"
+        assert np.array_equal(ks.cpu().double().numpy(), eks) and np.array_equal(vs.cpu().double().numpy(), evs)
+    assert model.stats()["cow_copies"] == prompts * (samples - 1)
