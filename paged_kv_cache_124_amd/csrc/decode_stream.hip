@@ -621,7 +621,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
 
   Split sp;
   sp.init(static_cast<int64_t>(hkv) * s_pre[n_seqs], static_cast<int64_t>(gridDim.x) * kSW);
-  const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * kSW + wave;
+  // XCD-major order: workgroups are dealt to the 8 XCDs in turn (workgroup b
+  // runs on XCD b % 8), so this numbering gives each XCD one contiguous share
+  // of the tile list: the waves of one sequence's KV heads share that XCD's
+  // L2 for Q, table rows and scales.  The merge kernel sees the same numbering.
+  const int64_t wg = gridDim.x % 8 == 0 ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int64_t wave_id = wg * kSW + wave;
   const int64_t x0 = sp.start(wave_id);
   const int64_t x1 = sp.start(wave_id + 1);
   if (x0 >= x1) return;
