@@ -208,3 +208,50 @@ class BlockManagerModel:
             "stored_tokens": stored,
             "tail_waste_slots": used * self.block_size - stored,
         }
+
+
+def shared_prefix_groups(tables: Sequence[Sequence[int]], lens: Sequence[int], block_size: int,
+                         max_members: int) -> List[Tuple[int, int, int]]:
+    """Groups of consecutive batch rows that read the same full leading blocks.
+
+    [P1] section 15 item 1: a full block referenced by several sequences is
+    immutable, and its payload may be read by all of them at once.  A decode
+    can then read such a block once for every sequence whose table holds it
+    and combine that part of the attention with each sequence's own blocks
+    ([P2] section 11: summaries of disjoint token sets merge exactly).  This
+    function is the host rule that picks the groups; it fixes no arithmetic.
+
+    Row n holds floor(lens[n] / B) full blocks.  Rows are walked in batch
+    order.  A run starts at a row with L = its full-block count.  The next row
+    joins the run when the run has fewer than ``max_members`` rows and the
+    row's table starts with c >= 1 of the run's first L entries (c counted
+    among the row's own full blocks) and joining does not lower the bytes the
+    run saves: with k rows so far, k * c >= (k - 1) * L.  Then L becomes c.
+    Otherwise the run closes and the row starts a new one.  Each closed run of
+    at least 2 rows with L >= 1 is returned as (first row, rows, L * B shared
+    tokens).
+    """
+    groups: List[Tuple[int, int, int]] = []
+    n = len(lens)
+    full = [max(int(s), 0) // block_size for s in lens]
+
+    def close(first: int, count: int, shared_blocks: int) -> None:
+        if count >= 2 and shared_blocks >= 1:
+            groups.append((first, count, shared_blocks * block_size))
+
+    if n == 0:
+        return groups
+    first, count, L = 0, 1, full[0]
+    for row in range(1, n):
+        c = 0
+        limit = min(L, full[row])
+        while c < limit and tables[row][c] == tables[first][c]:
+            c += 1
+        if count < max_members and c >= 1 and count * c >= (count - 1) * L:
+            count += 1
+            L = c
+        else:
+            close(first, count, L)
+            first, count, L = row, 1, full[row]
+    close(first, count, L)
+    return groups
