@@ -360,6 +360,25 @@ int pa_bm_free_seq(pa_bm* bm, int64_t seq);
 int pa_bm_build_batch(pa_bm* bm, const int64_t* seqs, int n, int max_blocks_per_seq,
                       int32_t* block_tables_out, int32_t* context_lens_out);
 
+/* Groups of consecutive batch rows that read the same full leading blocks,
+ * for pa_decode_shared.  A full block referenced by several sequences is
+ * immutable and may be read by all of them at once ("PagedAttention: Virtual
+ * Memory for the KV Cache", section 15), so a decode can read it once for the
+ * whole group.  Row i is seqs[i]; row i holds floor(len / B) full blocks.
+ * Rows are walked in order: a run starts at a row with L = its full-block
+ * count; the next row joins while the run has fewer than max_members rows,
+ * the row's table starts with c >= 1 of the run's first L entries (among the
+ * row's own full blocks) and k * c >= (k - 1) * L for the k rows so far (the
+ * bytes the run saves do not drop); L becomes c.  Every run of >= 2 rows
+ * with L >= 1 is written to groups_out as int32 [3] = (first row, rows,
+ * L * B shared tokens), in row order; *num_groups receives their count.
+ *   groups_out   host int32 [cap][3], caller-owned (nullable when cap == 0)
+ * Errors: PA_ERR_NOT_FOUND for an unknown sequence; PA_ERR_INVALID_ARG for
+ * bad arguments or when more than cap groups are found (*num_groups then
+ * holds the number needed).  Nothing in the manager changes. */
+int pa_bm_shared_groups(pa_bm* bm, const int64_t* seqs, int n, int max_members, int32_t* groups_out, int cap,
+                        int* num_groups);
+
 /* Reference count of a block (-1 for an id outside the pool). */
 int pa_bm_refcount(pa_bm* bm, int block);
 /* Number of free blocks. */

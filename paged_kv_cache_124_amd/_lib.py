@@ -82,6 +82,7 @@ _SIGS = {
     "pa_bm_append_slots": (c_int, [c_void_p, _P64, c_int, _P32, _P32, POINTER(c_int)]),
     "pa_bm_free_seq": (c_int, [c_void_p, c_int64]),
     "pa_bm_build_batch": (c_int, [c_void_p, _P64, c_int, c_int, _P32, _P32]),
+    "pa_bm_shared_groups": (c_int, [c_void_p, _P64, c_int, c_int, _P32, c_int, POINTER(c_int)]),
     "pa_bm_refcount": (c_int, [c_void_p, c_int]),
     "pa_bm_num_free": (c_int, [c_void_p]),
     "pa_bm_seq_len": (c_int64, [c_void_p, c_int64]),
@@ -526,6 +527,17 @@ class BlockManager:
         lens = np.zeros(n, dtype=np.int32)
         st = lib.pa_bm_build_batch(self._h, s.ctypes.data_as(_P64), n, max_blocks, _ptr32(tables), _ptr32(lens))
         return st, tables, lens
+
+    def shared_groups(self, seqs, max_members: int):
+        """(status, int32 [G][3] groups (first row, rows, shared tokens)) of pa_bm_shared_groups."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        cap = max(n // 2, 1)
+        out = np.zeros((cap, 3), dtype=np.int32)
+        g = c_int()
+        st = lib.pa_bm_shared_groups(self._h, s.ctypes.data_as(_P64), n, max_members, _ptr32(out), cap,
+                                     ctypes.byref(g))
+        return st, out[: g.value].copy() if st == PA_OK else np.zeros((0, 3), dtype=np.int32)
 
     def refcount(self, block: int) -> int:
         return lib.pa_bm_refcount(self._h, block)

@@ -14,6 +14,7 @@
 // operations are O(1) amortised except fork/release (O(table length)) and
 // stats (O(total table entries)).
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -217,6 +218,57 @@ int pa_bm_build_batch(pa_bm* bm, const int64_t* seqs, int n, int max_blocks_per_
     for (int64_t j = nb; j < max_blocks_per_seq; ++j) row[j] = 0;
     context_lens_out[i] = static_cast<int32_t>(s.len);
   }
+  return PA_OK;
+}
+
+int pa_bm_shared_groups(pa_bm* bm, const int64_t* seqs, int n, int max_members, int32_t* groups_out, int cap,
+                        int* num_groups) {
+  if (!bm || n < 0 || max_members < 1 || cap < 0 || !num_groups) return PA_ERR_INVALID_ARG;
+  if (n > 0 && !seqs) return PA_ERR_INVALID_ARG;
+  std::vector<const Seq*> rows(n);
+  for (int i = 0; i < n; ++i) {  // validate everything before writing anything
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+    rows[i] = &it->second;
+  }
+  const int64_t B = bm->block_size;
+  auto full = [&](int i) { return rows[i]->len / B; };  // full blocks of row i
+  // Greedy runs in batch order: a row joins the run while the run has room,
+  // the row starts with c >= 1 of the run's L shared full blocks, and joining
+  // keeps the bytes saved (k * c >= (k - 1) * L for k rows so far).
+  std::vector<int32_t> found;
+  auto close = [&](int first, int count, int64_t shared_blocks) {
+    if (count >= 2 && shared_blocks >= 1) {
+      found.push_back(first);
+      found.push_back(count);
+      found.push_back(static_cast<int32_t>(shared_blocks * B));
+    }
+  };
+  if (n > 0) {
+    int first = 0, count = 1;
+    int64_t L = full(0);
+    for (int i = 1; i < n; ++i) {
+      const int64_t limit = std::min(L, full(i));
+      const std::vector<int32_t>& a = rows[first]->table;
+      const std::vector<int32_t>& b = rows[i]->table;
+      int64_t c = 0;
+      while (c < limit && a[c] == b[c]) ++c;
+      if (count < max_members && c >= 1 && static_cast<int64_t>(count) * c >= static_cast<int64_t>(count - 1) * L) {
+        ++count;
+        L = c;
+      } else {
+        close(first, count, L);
+        first = i;
+        count = 1;
+        L = full(i);
+      }
+    }
+    close(first, count, L);
+  }
+  const int g = static_cast<int>(found.size() / 3);
+  *num_groups = g;
+  if (g > cap || (g > 0 && !groups_out)) return PA_ERR_INVALID_ARG;
+  if (g > 0) std::memcpy(groups_out, found.data(), found.size() * sizeof(int32_t));
   return PA_OK;
 }
 

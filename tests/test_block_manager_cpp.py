@@ -124,3 +124,61 @@ def test_differential_against_model(pa, seed):
             assert tables.tolist() == mtables and lens.tolist() == mlens
         live = sorted(m.tables)
         assert _snapshot_cpp(bm, live) == _snapshot_model(m), f"diverged at step {step}"
+
+
+def test_shared_groups_on_the_pages_traces(pa):
+    """pa_bm_shared_groups on the fork trace (32 shared tokens) and exercise 2 (16), [P1] sections 14-17 and 24."""
+    g = golden("block_manager_traces.json")["fork_35"]
+    order = g["pop_order_prefix"] + [b for b in range(g["num_blocks"]) if b not in g["pop_order_prefix"]]
+    bm = pa.BlockManager(g["num_blocks"], g["block_size"], order)
+    assert bm.add_seq(1, g["prompt"]) == 0 and bm.fork(1, 2) == 0
+    assert bm.append_slot(1)[0] == 0 and bm.append_slot(2)[0] == 0
+    st, groups = bm.shared_groups([1, 2], 8)
+    assert st == 0 and groups.tolist() == [[0, 2, g["after_step"]["shared_full_prefix_tokens"]]]
+    st, groups = bm.shared_groups([1, 2], 1)
+    assert st == 0 and groups.shape == (0, 3)
+    e = golden("block_manager_traces.json")["exercise_2"]
+    bm = pa.BlockManager(e["num_blocks"], e["block_size"])
+    assert bm.add_seq(1, e["prompt"]) == 0 and bm.fork(1, 2) == 0
+    for _ in range(e["appends_A"]):
+        assert bm.append_slot(1)[0] == 0
+    st, groups = bm.shared_groups([1, 2], 8)
+    assert st == 0 and groups.tolist() == [[0, 2, e["final"]["shared_prefix_tokens"]]]
+    assert bm.shared_groups([1, 3], 8)[0] == 5  # unknown sequence: PA_ERR_NOT_FOUND
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_shared_groups_match_the_oracle_rule(pa, seed):
+    """Random fork forests in random batch orders: the C++ groups equal the oracle's, entry for entry."""
+    from oracle.block_manager import shared_prefix_groups
+    rng = random.Random(500 + seed)
+    B = rng.choice([8, 16, 32])
+    nb = 4096
+    order = rng.sample(range(nb), nb)
+    bm = pa.BlockManager(nb, B, order)
+    model = BlockManagerModel(nb, B, order)
+    live, nid = [], 0
+    for _ in range(rng.randint(2, 6)):
+        L = rng.randint(1, 10 * B)
+        assert bm.add_seq(nid, L) == 0 and model.add_seq(nid, L) == 0
+        live.append(nid)
+        nid += 1
+    for _ in range(rng.randint(10, 60)):
+        if rng.random() < 0.35:
+            p = rng.choice(live)
+            assert bm.fork(p, nid) == 0 and model.fork(p, nid) == 0
+            live.append(nid)
+            nid += 1
+        else:
+            s = rng.choice(live)
+            for _ in range(rng.randint(1, B)):
+                assert bm.append_slot(s)[0] == 0 and model.append_slot(s)[0] == 0
+    batch = list(live)
+    if seed % 3 == 0:
+        rng.shuffle(batch)
+    cap = rng.choice([2, 4, 8, 16])
+    st, groups = bm.shared_groups(batch, cap)
+    assert st == 0
+    tables = [model.tables[s] for s in batch]
+    lens = [model.lens[s] for s in batch]
+    assert [tuple(r) for r in groups.tolist()] == shared_prefix_groups(tables, lens, B, cap)
