@@ -81,7 +81,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa8b", choices=["gqa8b", "sweep_b8", "sweep_b16", "sweep_b32"])
+    ap.add_argument("--workload", default="gqa8b", choices=["gqa8b", "sweep_b8", "sweep_b16", "sweep_b32", "fork"])
+    ap.add_argument("--shared", action="store_true",
+                    help="fork workload: decode with pa_decode_step_shared, each prompt's shared full blocks read "
+                         "once per step for its samples (default: pa_decode_step)")
     ap.add_argument("--replicas", type=int, default=4,
                     help="pool copies rotated step to step so reads come from HBM, not the 256 MB Infinity Cache")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
@@ -97,13 +100,15 @@ def workload(name):
     import synth
     if name == "gqa8b":
         return synth.gqa8b()
+    if name == "fork":
+        return synth.fork()
     return synth.sweep(int(name.split("_b")[1]))
 
 
 class Runner:
     """Holds the resident state of one benchmark workload."""
 
-    def __init__(self, w, steps_total, replicas, device="cuda", kv_kind="bf16"):
+    def __init__(self, w, steps_total, replicas, device="cuda", kv_kind="bf16", shared=False):
         import torch
         import synth
         import paged_kv_cache_124_amd as pa
@@ -111,17 +116,42 @@ class Runner:
         self.torch = torch
         self.w = w
         self.fp8 = kv_kind == "fp8"
-        self.lens0 = synth.seq_lengths(w)
-        self.n = len(self.lens0)
+        self.fork = w.name == "fork"
+        self.shared = shared
         bs = w.block_size
-        grown = [s + steps_total for s in self.lens0]
-        self.num_blocks = synth.pool_blocks(w, grown)
+        if self.fork:
+            # parallel sampling: each prompt forked into FORK_SAMPLES samples that share its blocks;
+            # the first step copies the shared 7-token tails on write
+            P, S = synth.FORK_PROMPTS, synth.FORK_SAMPLES
+            prompt = w.fixed_lens[0]
+            self.lens0 = [prompt] * (P * S)
+            grown = [s + steps_total for s in self.lens0]
+            extra = P * (S - 1) + P * S * (-(-grown[0] // bs) - (-(-prompt // bs)))
+            self.num_blocks = synth.pool_blocks(w, list(w.fixed_lens), extra=extra)
+        else:
+            self.lens0 = synth.seq_lengths(w)
+            grown = [s + steps_total for s in self.lens0]
+            self.num_blocks = synth.pool_blocks(w, grown)
+        self.n = len(self.lens0)
         self.max_blocks = max(-(-s // bs) for s in grown)
         self.max_ctx = max(grown)
         self.bm = pa.BlockManager(self.num_blocks, bs, synth.pop_order(self.num_blocks, w.seed))
-        for i, s in enumerate(self.lens0):
-            assert self.bm.add_seq(i, s) == 0
+        if self.fork:
+            for p in range(P):
+                assert self.bm.add_seq(p * S, prompt) == 0
+                for j in range(1, S):
+                    assert self.bm.fork(p * S, p * S + j) == 0
+        else:
+            for i, s in enumerate(self.lens0):
+                assert self.bm.add_seq(i, s) == 0
         self.seqs = np.arange(self.n, dtype=np.int64)
+        self.groups = None
+        if self.shared:
+            st, groups = self.bm.shared_groups(self.seqs, 32 // (w.hq // w.hkv))
+            assert st == 0 and len(groups) > 0
+            self.groups = torch.from_numpy(groups).to(device)
+            # KV bytes a step needs once: each group's shared tokens once, every row's own tokens
+            self.shared_tokens_saved = int(sum((c - 1) * p for _, c, p in groups.tolist()))
         dt = synth.torch_dtype(w)
         if self.fp8:
             kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, 1)
@@ -143,8 +173,12 @@ class Runner:
         self.k_new = synth.randn((self.n, w.hkv, w.d), dt, w.value_scale, w.seed * 10 + 4, device)
         self.v_new = synth.randn((self.n, w.hkv, w.d), dt, w.value_scale, w.seed * 10 + 5, device)
         self.out = torch.empty_like(self.q)
-        ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx,
-                                          pa.PA_FP8_E4M3 if self.fp8 else pa.PA_BF16)
+        if self.shared:
+            ws = pa.pa_decode_shared_workspace_bytes(self.n, len(self.groups), w.hq, w.hkv, w.d, bs, self.max_ctx,
+                                                     pa.PA_BF16)
+        else:
+            ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx,
+                                              pa.PA_FP8_E4M3 if self.fp8 else pa.PA_BF16)
         self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)  # zero before first use
         self.part = pa.pa_decode_partition_tokens(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
         # Block tables and lengths live on the device; pa_append_step moves them forward.
@@ -206,6 +240,10 @@ class Runner:
                 if self.fp8:
                     self.append_args[r, b] = app[:6] + (ctypes.c_void_p(base),) + app[7:]
                     self.step_args[r, b] = dec
+                elif self.shared:
+                    self.step_args[r, b], _ = pa.pa_decode_step_shared_args(
+                        self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], check[:n], self.d_tables,
+                        self.d_lens, self.groups, w.scale, self.max_ctx, workspace=self.ws, slot_pointer=base)
                 else:
                     self.step_args[r, b], _ = pa.pa_decode_step_args(
                         self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], check[:n], self.d_tables,
@@ -250,7 +288,10 @@ class Runner:
                 assert L.pa_copy_blocks(*ca) == 0
             if timing is not None:
                 timing[0].record()
-            assert L.pa_decode_step(*self.step_args[r, k]) == 0
+            if self.shared:
+                assert L.pa_decode_step_shared(*self.step_args[r, k]) == 0
+            else:
+                assert L.pa_decode_step(*self.step_args[r, k]) == 0
             if timing is not None:
                 timing[1].record()
         if k % half == half - 1:
@@ -330,6 +371,11 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
             "us_per_step": round(t_total / passes * 1e6, 1)}
 
 
+def synth_fork_prompts():
+    import synth
+    return synth.FORK_PROMPTS
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -350,7 +396,10 @@ def main():
     w = workload(args.workload)
     total = args.steps + args.warmup + 1
     print(f"[bench] building workload {w.name}", file=sys.stderr, flush=True)
-    run = Runner(w, total, args.replicas, kv_kind=args.kv)
+    if args.shared and (w.name != "fork" or args.kv != "bf16"):
+        print("--shared applies to the bf16 fork workload", file=sys.stderr)
+        sys.exit(2)
+    run = Runner(w, total, args.replicas, kv_kind=args.kv, shared=args.shared)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run.step()
@@ -384,8 +433,23 @@ def main():
     dec_avg_us = sum(dec_us) / len(dec_us)
     bytes_per_launch = kv_bytes / args.steps
     achieved = sampled_bytes / (sum(dec_us) * 1e-6) / 1e9
-    traffic = measured_traffic(w.name, args.kv)
+    traffic = measured_traffic(w.name, args.kv) if not args.shared else None
     fp8 = args.kv == "fp8"
+    if run.fork:
+        # bytes a step needs from memory when each prompt's shared full blocks are read once
+        st, groups = run.bm.shared_groups(run.seqs, 32 // (w.hq // w.hkv))
+        assert st == 0
+        saved = sum((c - 1) * p for _, c, p in groups.tolist()) * run.kv_bytes_per_token
+        unique_per_step = bytes_per_launch - saved
+        workload_desc = (f"fork: {synth_fork_prompts()} prompts of {run.lens0[0]} tokens, each forked into "
+                         f"{run.n // synth_fork_prompts()} samples ({run.n} seqs sharing 128 full prefix blocks per "
+                         f"prompt), Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, block {w.block_size}, bf16, copy-on-write "
+                         f"of the tails on the first step, contexts growing 1/step; decode "
+                         f"{'pa_decode_step_shared (shared blocks read once per group)' if args.shared else 'pa_decode_step (every row reads its own table)'}")
+    else:
+        workload_desc = (f"{w.name}{'-fp8' if fp8 else ''}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, "
+                         f"block {w.block_size}, {'FP8 E4M3 cache with per-(block, KV head) scales' if fp8 else 'bf16'}, "
+                         f"contexts {min(run.lens0)}..{max(run.lens0)} growing 1/step")
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -399,9 +463,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8-e4m3 cache, bf16 q/out" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}{'-fp8' if fp8 else ''}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, "
-                               f"block {w.block_size}, {'FP8 E4M3 cache with per-(block, KV head) scales' if fp8 else 'bf16'}, "
-                               f"contexts {min(run.lens0)}..{max(run.lens0)} growing 1/step",
+        "config": {"workload": workload_desc,
                    "num_seqs": run.n, "block_size": w.block_size, "pool_blocks": run.num_blocks,
                    "pool_replicas": args.replicas, "partition_tokens": run.part,
                    "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2),
@@ -412,9 +474,16 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),
                      "kernel": "pa_decode_fp8 (decode kernel + merge kernel)" if fp8 else
-                               "pa_decode_step (decode kernel + merge/append kernel)", "avg_us": round(dec_avg_us, 2),
-                     "launches_timed": len(dec_us)},
+                               ("pa_decode_step_shared (shared-prefix decode kernel + merge/append kernel)"
+                                if args.shared else "pa_decode_step (decode kernel + merge/append kernel)"),
+                     "avg_us": round(dec_avg_us, 2), "launches_timed": len(dec_us)},
     }
+    if run.fork:
+        # value and roofline count the KV the attention consumes (every row's own context); with
+        # sharing most of it is read once per group, so the bytes a step needs are given beside it
+        res["config"]["unique_kv_bytes_per_step"] = int(unique_per_step)
+        res["config"]["unique_gb_s"] = round(unique_per_step / (ms_step * 1e-3) / 1e9, 2)
+        res["roofline"]["achieved_unique"] = round(achieved * unique_per_step / bytes_per_launch, 1)
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.kv)

@@ -157,6 +157,58 @@ int pa_decode_step(void* out, const void* q, const void* k_new, const void* v_ne
                    int max_context_len, int num_blocks, int dtype, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* pa_decode_shared: pa_decode, with the full blocks that a group of
+ * consecutive rows shares read once for the whole group.  A full block
+ * referenced by several sequences is immutable, so every sharer sees the same
+ * keys and values in it ("PagedAttention: Virtual Memory for the KV Cache",
+ * section 15), and a row's attention is the common-maximum merge of the
+ * summaries of its shared tokens and of the rest ("PagedAttention in vLLM:
+ * scattered memory, exact attention", section 11).  The output is that of
+ * pa_decode on the same arguments (same tolerance; not bitwise, as the split
+ * differs).
+ *
+ *   groups      int32 [num_groups][3] = (first row, rows, P tokens),
+ *               device-readable (device memory, or pinned host memory
+ *               mapped for the device), e.g. from pa_bm_shared_groups.
+ *               Rows first .. first + rows - 1 read tokens 0 .. P - 1
+ *               through row `first`'s table.
+ *   num_groups  >= 0; 0 is plain pa_decode
+ *
+ * Precondition (caller): for every group, the members' block_tables rows
+ * agree on their first P / block_size entries.  Everything else is checked
+ * on the device and a group that fails is ignored for this call, which
+ * leaves the result exact: rows outside the batch, rows claimed by another
+ * group (one of the two is used), P < block_size.  P is cut to the shortest
+ * member's context length and rounded down to whole blocks; a group keeps at
+ * most 32 / (Hq / Hkv) rows (later rows attend alone).  The groups must stay
+ * unchanged until the call has run.  Served by the shared-prefix kernel for
+ * bf16, Hq / Hkv <= 16, num_seqs <= 1024, num_groups <= 512; other shapes run
+ * pa_decode (the groups unused).  Workspace: pa_decode_shared_workspace_bytes.
+ * Other arguments and errors as for pa_decode.
+ */
+int pa_decode_shared(void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* groups,
+                     int num_groups, int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                     int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* pa_decode_step_shared: pa_decode_step with groups as for pa_decode_shared.
+ * Each row's new token belongs to its own part, so the rows move forward
+ * exactly as with pa_decode_step; the groups stay valid for the next step as
+ * long as P stays within every member's table (shared blocks are never
+ * written).  Shapes outside the shared-prefix kernel run pa_decode_step;
+ * shapes outside pa_decode_step return PA_ERR_UNSUPPORTED. */
+int pa_decode_step_shared(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                          void* v_pool, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                          const int32_t* groups, int num_groups, int num_seqs, int Hq, int Hkv, int d_head,
+                          int block_size, float scale, int max_blocks_per_seq, int max_context_len, int num_blocks,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_decode_shared / pa_decode_step_shared need for these
+ * sizes on the current device (pa_decode's when the groups go unused). */
+size_t pa_decode_shared_workspace_bytes(int num_seqs, int num_groups, int Hq, int Hkv, int d_head, int block_size,
+                                        int max_context_len, int dtype);
+
 /* Workspace bytes pa_decode needs for these sizes on the current device
  * (0 when no split is used); dtype PA_FP8_E4M3 gives pa_decode_fp8's. */
 size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,

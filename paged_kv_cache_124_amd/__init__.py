@@ -31,8 +31,13 @@ from ._lib import (  # noqa: F401
     pa_decode_fp8,
     pa_decode_fp8_args,
     pa_decode_partition_tokens,
+    pa_decode_shared,
+    pa_decode_shared_args,
+    pa_decode_shared_workspace_bytes,
     pa_decode_step,
     pa_decode_step_args,
+    pa_decode_step_shared,
+    pa_decode_step_shared_args,
     pa_decode_workspace_bytes,
     pool_shapes,
 )

@@ -63,6 +63,10 @@ _SIGS = {
                           c_int, c_float, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "pa_decode_step": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_workspace_bytes": (c_size_t, [c_int] * 7),
+    "pa_decode_shared": (c_int, [c_void_p] * 7 + [c_int] * 6 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
+    "pa_decode_step_shared": (c_int, [c_void_p] * 10 + [c_int] * 6 + [c_float] + [c_int] * 4
+                              + [c_void_p, c_size_t, c_void_p]),
+    "pa_decode_shared_workspace_bytes": (c_size_t, [c_int] * 8),
     "pa_decode_partition_tokens": (c_int, [c_int] * 7),
     "pa_append_kv": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                              c_int, c_void_p]),
@@ -241,6 +245,85 @@ def pa_decode_step(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tab
     args, _ws = pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens,
                                     scale, max_context_len, workspace, stream)
     _check(lib.pa_decode_step(*args), "pa_decode_step")
+    return out
+
+
+def pa_decode_shared_workspace_bytes(num_seqs, num_groups, Hq, Hkv, d_head, block_size, max_context_len,
+                                     dtype) -> int:
+    return int(lib.pa_decode_shared_workspace_bytes(num_seqs, num_groups, Hq, Hkv, d_head, block_size,
+                                                    max_context_len, dtype))
+
+
+def _groups_arg(groups, groups_pointer):
+    """(pointer, count) of an int32 [G][3] device tensor of groups, or of a mapped host buffer."""
+    import torch
+    if groups is None:
+        return c_void_p(0), 0
+    if groups.dtype != torch.int32 or groups.dim() != 2 or groups.shape[1] != 3:
+        raise ValueError("groups must be int32 [G][3] (first row, rows, shared tokens)")
+    g = groups.shape[0]
+    if groups_pointer is not None:
+        return c_void_p(groups_pointer), g
+    return (_dev(groups, "groups") if g else c_void_p(0)), g
+
+
+def pa_decode_shared_args(out, q, k_pool, v_pool, block_tables, context_lens, groups, scale, max_context_len,
+                          workspace=None, stream=None, groups_pointer=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode_shared(*args)`` calls.
+
+    ``groups`` is int32 [G][3] (device, or ``groups_pointer`` = the device
+    mapping of a pinned host buffer of that shape).
+    """
+    import torch
+    base, _ = pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                             torch.empty(0, dtype=torch.uint8, device=q.device), stream)
+    gp, ng = _groups_arg(groups, groups_pointer)
+    n, hq, d = q.shape
+    nb, hkv, _, bs = _pool_dims(k_pool, v_pool)
+    need = pa_decode_shared_workspace_bytes(n, ng, hq, hkv, d, bs, max_context_len, _dtype_code(q))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
+    ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = base[:6] + (gp, ng) + base[6:16] + (ws_ptr, ws_bytes, base[18])
+    return args, workspace
+
+
+def pa_decode_shared(out, q, k_pool, v_pool, block_tables, context_lens, groups, scale, max_context_len,
+                     workspace=None, stream=None):
+    """pa_decode_shared of include/pa.h: pa_decode with each group's shared full blocks read once."""
+    args, _ws = pa_decode_shared_args(out, q, k_pool, v_pool, block_tables, context_lens, groups, scale,
+                                      max_context_len, workspace, stream)
+    _check(lib.pa_decode_shared(*args), "pa_decode_shared")
+    return out
+
+
+def pa_decode_step_shared_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens,
+                               groups, scale, max_context_len, workspace=None, stream=None, slot_pointer=None,
+                               groups_pointer=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode_step_shared(*args)`` calls."""
+    import torch
+    base, _ = pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens,
+                                  scale, max_context_len, torch.empty(0, dtype=torch.uint8, device=q.device),
+                                  stream, slot_pointer)
+    gp, ng = _groups_arg(groups, groups_pointer)
+    n, hq, d = q.shape
+    nb, hkv, _, bs = _pool_dims(k_pool, v_pool)
+    need = pa_decode_shared_workspace_bytes(n, ng, hq, hkv, d, bs, max_context_len, _dtype_code(q))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
+    ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = base[:9] + (gp, ng) + base[9:19] + (ws_ptr, ws_bytes, base[21])
+    return args, workspace
+
+
+def pa_decode_step_shared(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens, groups,
+                          scale, max_context_len, workspace=None, stream=None):
+    """pa_decode_step_shared of include/pa.h: pa_decode_step with each group's shared full blocks read once."""
+    args, _ws = pa_decode_step_shared_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
+                                           context_lens, groups, scale, max_context_len, workspace, stream)
+    _check(lib.pa_decode_step_shared(*args), "pa_decode_step_shared")
     return out
 
 

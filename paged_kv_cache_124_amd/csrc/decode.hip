@@ -466,6 +466,13 @@ bool use_stream(int num_seqs, int hq, int hkv, int d, int block_size, int dtype)
   const char* env = std::getenv("PA_DECODE_PATH");
   return !(env && env[0] == 'p');
 }
+// Groups are served by the shared-prefix kernel where the persistent kernel
+// runs and the sizes fit it; elsewhere they are ignored, which gives the same
+// attention.
+bool use_shared(int num_seqs, int num_groups, int hq, int hkv, int d, int block_size, int dtype) {
+  return num_groups > 0 && use_stream(num_seqs, hq, hkv, d, block_size, dtype) &&
+         shared_eligible(num_seqs, num_groups, hq / hkv, d, block_size, dtype);
+}
 }  // namespace
 }  // namespace pa
 
@@ -482,6 +489,16 @@ extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d
   return pa::plan_workspace_bytes(p, num_seqs, Hq, d_head);
 }
 
+extern "C" size_t pa_decode_shared_workspace_bytes(int num_seqs, int num_groups, int Hq, int Hkv, int d_head,
+                                                   int block_size, int max_context_len, int dtype) {
+  if (num_seqs <= 0 || num_groups < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 ||
+      max_context_len < 0 || Hq % Hkv != 0 || dtype == PA_FP8_E4M3)
+    return 0;
+  if (pa::use_shared(num_seqs, num_groups, Hq, Hkv, d_head, block_size, dtype))
+    return pa::shared_plan(num_seqs, num_groups, Hq, Hkv, d_head, block_size, max_context_len).workspace_bytes;
+  return pa_decode_workspace_bytes(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
+}
+
 extern "C" int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                           int max_context_len, int dtype) {
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0) return 0;
@@ -494,7 +511,8 @@ namespace {
 int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                 const int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
                 int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype, void* workspace,
-                size_t workspace_bytes, void* stream, const pa::StepInputs* step) {
+                size_t workspace_bytes, void* stream, const pa::StepInputs* step, const int32_t* groups = nullptr,
+                int num_groups = 0) {
   using namespace pa;
   if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0 || num_blocks < 0)
@@ -511,6 +529,14 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
   if (num_seqs > 65535 || Hq > 65535) return PA_ERR_UNSUPPORTED;
 
   const float scale_log2_s = scale * kLog2e;
+  if (num_groups < 0 || (num_groups > 0 && !groups)) return PA_ERR_INVALID_ARG;
+  if (use_shared(num_seqs, num_groups, Hq, Hkv, d_head, block_size, dtype)) {
+    const StreamPlan sp = shared_plan(num_seqs, num_groups, Hq, Hkv, d_head, block_size, max_context_len);
+    if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
+    return launch_shared(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, groups,
+                         num_groups, out, workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq,
+                         num_blocks, scale_log2_s, step);
+  }
   if (use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) {
     const StreamPlan sp = stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len);
     if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
@@ -589,6 +615,32 @@ extern "C" int pa_decode_step(void* out, const void* q, const void* k_new, const
   return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
                      scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes,
                      stream, &step);
+}
+
+extern "C" int pa_decode_shared(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens, const int32_t* groups,
+                                int num_groups, int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                                float scale, int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
+                     scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes, stream,
+                     nullptr, groups, num_groups);
+}
+
+extern "C" int pa_decode_step_shared(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                     void* v_pool, const int32_t* slot_mapping, int32_t* block_tables,
+                                     int32_t* context_lens, const int32_t* groups, int num_groups, int num_seqs,
+                                     int Hq, int Hkv, int d_head, int block_size, float scale,
+                                     int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace pa;
+  if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  if (!use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) return PA_ERR_UNSUPPORTED;
+  const StepInputs step{k_new, v_new, slot_mapping};
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
+                     scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes,
+                     stream, &step, groups, num_groups);
 }
 
 extern "C" int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,

@@ -1,0 +1,705 @@
+// Paged decode attention, bf16, with full blocks shared by a group of
+// sequences read once for the whole group.
+//
+// Why it is exact ("PagedAttention: Virtual Memory for the KV Cache", section
+// 15; "PagedAttention in vLLM: scattered memory, exact attention", section
+// 11): a full block referenced by several sequences is immutable, so every
+// sharer sees the same keys and values in it.  Sequence n's attention over
+// its S_n tokens is the common-maximum merge of the (m, z, u) summary over
+// its first P tokens and the summary over tokens P .. S_n - 1.  When rows
+// first .. first + count - 1 of the batch hold the same physical blocks for
+// their first P / B table entries, the first summary of every member comes
+// from one pass over those blocks with all members' queries at once.
+//
+// Work decomposition (the persistent equal split of decode_stream.hip over
+// "units" instead of sequences):
+//   unit n < N       sequence n's own tokens [base_n, S_n + new), where
+//                    base_n = P of its group (0 when it has none);
+//   unit N + i       group i's shared tokens [0, P_i), read through the table
+//                    row of its first member, with count_i * G query columns
+//                    (member m, head h -> column m G + h; at most 32).
+// Tiles of all (unit, KV head) segments form one list; wave w takes tiles
+// [w T / W, (w + 1) T / W).  A group tile is one 16 KiB read of keys and
+// values used by two 16-column blocks of matrix-core products instead of one.
+//
+// Output: a sequence without a group whose segment a wave finishes whole is
+// written directly.  Every other finished piece leaves an (m, z, u) record:
+// a whole segment in its own slot (rows [KV head][2 N G]), a piece cut by
+// range boundaries in the wave's two slots (32 rows each).  `merge_shared`
+// combines, per (sequence, KV head), the pieces of its group unit (its
+// columns) and of its own unit, in that order.
+//
+// Groups that are not usable are ignored, which keeps the result exact: a
+// group is used only when all its rows lie in the batch, no other group
+// claims one of them and it shares at least one whole block; its P is cut to
+// the shortest member's cached length, rounded down to whole blocks, and its
+// rows to 32 / G (members past that compute alone).  The caller guarantees
+// what the kernel cannot see: the members' table rows agree on the first
+// P / B entries.
+
+#include <cstdlib>
+
+#include "common.h"
+#include "decode_stream.h"
+#include "decode_tile.h"
+
+namespace pa {
+namespace {
+
+constexpr int kShMaxSeqs = 1024;
+constexpr int kShMaxGroups = 512;
+constexpr int kShCols = 32;  // query columns of one tile: two 16-column blocks
+
+// LDS of the kernel besides the stages: lengths and prefix sums of the units,
+// per-sequence base (shared tokens skipped) and group, per-group first row,
+// rows and shared tokens.
+size_t shared_lds(int n, int g) { return (4 * static_cast<size_t>(n) + 5 * static_cast<size_t>(g) + 1) * 4; }
+
+// Where a unit's tiles read and whom they serve; wave-uniform, from LDS.
+struct UnitView {
+  const int32_t* s_len;
+  const int32_t* s_base;
+  const int32_t* s_gfirst;
+  const int32_t* s_gcount;
+  int n_seqs, g;
+  __device__ bool is_group(int u) const { return u >= n_seqs; }
+  __device__ int table_row(int u) const { return u < n_seqs ? u : s_gfirst[u - n_seqs]; }
+  __device__ int base(int u) const { return u < n_seqs ? s_base[u] : 0; }
+  __device__ int cols(int u) const { return u < n_seqs ? g : s_gcount[u - n_seqs] * g; }
+  // record rows of the unit in the whole-segment area: sequence n -> n G,
+  // group i -> (N + first_i) G (groups are disjoint row ranges)
+  __device__ int64_t row_base(int u) const {
+    return static_cast<int64_t>(u < n_seqs ? u : n_seqs + s_gfirst[u - n_seqs]) * g;
+  }
+};
+
+// Table entries of a unit's tile: tokens base + 32 ti .. + 31 of the unit's
+// table row, -1 past the unit's tokens (base is a multiple of B).
+template <int B>
+__device__ __forceinline__ Tb<32 / B> load_tb_unit(TilePos t, const UnitView& uv,
+                                                   const int32_t* __restrict__ block_tables, int max_blocks) {
+  const int32_t* row = block_tables + static_cast<int64_t>(uv.table_row(t.n)) * max_blocks;
+  const int S = pool_tokens(uv.s_len[t.n]);
+  const int t0 = t.ti * 32;
+  const int b0 = (uv.base(t.n) + t0) / B;
+  Tb<32 / B> tb;
+#pragma unroll
+  for (int i = 0; i < 32 / B; ++i) {
+    const int e = row[min(b0 + i, max_blocks - 1)];
+    tb.blk[i] = t0 + i * B < S ? e : -1;
+  }
+  return tb;
+}
+
+// Q^T operands of both column blocks for a unit's tile.  Column c = 16 cb + r
+// is head c of the sequence (c < G), or member c / G, head c % G of the group;
+// padding columns read a valid row whose results are never used.
+template <int D>
+__device__ __forceinline__ void load_q_unit(QOp<D> (&qo)[2], TilePos t, const UnitView& uv,
+                                            const uint16_t* __restrict__ q, int hq, const int (&col_m)[2],
+                                            const int (&col_h)[2], int r, int gq) {
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    int seq, h;
+    if (!uv.is_group(t.n)) {
+      const int c = 16 * cb + r;
+      seq = t.n;
+      h = c < uv.g ? c : 0;
+    } else {
+      const int i = t.n - uv.n_seqs;
+      const bool ok = col_m[cb] < uv.s_gcount[i];
+      seq = uv.s_gfirst[i] + (ok ? col_m[cb] : 0);
+      h = ok ? col_h[cb] : 0;
+    }
+    const uint16_t* qh = q + (static_cast<int64_t>(seq) * hq + t.j * uv.g + h) * D;
+#pragma unroll
+    for (int jj = 0; jj < D / 32; ++jj)
+      qo[cb].q[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qh + (4 * jj + gq) * 8));
+  }
+}
+
+// End of a piece of unit segment t: direct output, a whole-segment record or a
+// wave-slot record (see the top of the file).
+template <int D>
+__device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], TilePos t, const UnitView& uv, bool whole, int slot,
+                                           int64_t wave_id, uint16_t* out, float* rec, float* rec_whole, int hq,
+                                           int hkv, int r, int gq) {
+  const int cols = uv.cols(t.n);
+  const bool direct = whole && !uv.is_group(t.n) && uv.s_base[t.n] == 0;
+  const int64_t total_rows = 2 * static_cast<int64_t>(uv.n_seqs) * uv.g;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    if (cb == 1 && cols <= 16) break;
+    float zt = st[cb].z + __shfl_xor(st[cb].z, 16);
+    zt += __shfl_xor(zt, 32);
+    const int c = 16 * cb + r;
+    if (c < cols) {
+      if (direct) {
+        const float inv = 1.f / zt;
+        uint16_t* o = out + (static_cast<int64_t>(t.n) * hq + t.j * uv.g + c) * D + 4 * gq;
+#pragma unroll
+        for (int mm = 0; mm < D / 16; ++mm) {
+          const uint32_t lo =
+              f32_to_bf16_bits(st[cb].o[mm][0] * inv) | (uint32_t(f32_to_bf16_bits(st[cb].o[mm][1] * inv)) << 16);
+          const uint32_t hi =
+              f32_to_bf16_bits(st[cb].o[mm][2] * inv) | (uint32_t(f32_to_bf16_bits(st[cb].o[mm][3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(o + 16 * mm) = make_uint2(lo, hi);
+        }
+      } else {
+        float* rr = whole ? rec_whole + (static_cast<int64_t>(t.j) * total_rows + uv.row_base(t.n) + c) * (D + 4)
+                          : rec + (static_cast<int64_t>(wave_id * 2 + slot) * kShCols + c) * (D + 4);
+#pragma unroll
+        for (int mm = 0; mm < D / 16; ++mm) *reinterpret_cast<f32x4*>(rr + 4 + 16 * mm + 4 * gq) = st[cb].o[mm];
+        if (gq == 0) {
+          rr[0] = st[cb].m;
+          rr[1] = zt;
+        }
+      }
+    }
+  }
+  reset(st[0]);
+  reset(st[1]);
+}
+
+// A group tile with more than 16 query columns: both column blocks in one
+// pass.  The two score products, the two online-softmax updates and the two
+// P.V products are independent, so their latencies overlap (one wave per SIMD
+// has no other wave to hide them behind).  Same arithmetic as qk_tile +
+// pv_tile per column block.
+template <int D>
+__device__ __forceinline__ void tile2(Acc<D> (&st)[2], const Buf<D>& b, const QOp<D> (&qo)[2], int t0, int S,
+                                      bool full, float scale_log2, int gq) {
+  f32x4 s[2][2];  // [column block][slab]
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) s[cb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        s[cb][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.k[a][jj], qo[cb].q[jj], s[cb][a], 0, 0, 0);
+  int n0 = 4, n1 = 4;
+  if (!full) {
+    n0 = b.blk0 ? min(max(S - (t0 + 4 * gq), 0), 4) : 0;
+    n1 = b.blk1 ? min(max(S - (t0 + 16 + 4 * gq), 0), 4) : 0;
+  }
+  float x[2][2][4];
+  float tmax[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[cb][a][i] = i < (a ? n1 : n0) ? s[cb][a][i] * scale_log2 : -INFINITY;
+        tmax[cb] = fmaxf(tmax[cb], x[cb][a][i]);
+      }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 16));
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 32));
+  float alpha[2];
+  bf16x8 phi[2], plo[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float m_new = fmaxf(st[cb].m, tmax[cb]);
+    alpha[cb] = __builtin_amdgcn_exp2f(st[cb].m - m_new);
+    st[cb].m = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[cb][a][i] - m_new);
+        psum += p;
+        const __bf16 h = static_cast<__bf16>(p);
+        phi[cb][4 * a + i] = h;
+        plo[cb][4 * a + i] = static_cast<__bf16>(p - static_cast<float>(h));
+      }
+    st[cb].z = st[cb].z * alpha[cb] + psum;
+  }
+  if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int mm = 0; mm < D / 16; ++mm) st[cb].o[mm] *= alpha[cb];
+  }
+  uint32_t m0a = 0xffffffffu, m0b = 0xffffffffu, m1a = 0xffffffffu, m1b = 0xffffffffu;
+  if (!full) {  // zero values of missing tokens (0 * NaN is NaN)
+    m0a = n0 >= 2 ? 0xffffffffu : (n0 == 1 ? 0x0000ffffu : 0u);
+    m0b = n0 >= 4 ? 0xffffffffu : (n0 == 3 ? 0x0000ffffu : 0u);
+    m1a = n1 >= 2 ? 0xffffffffu : (n1 == 1 ? 0x0000ffffu : 0u);
+    m1b = n1 >= 4 ? 0xffffffffu : (n1 == 3 ? 0x0000ffffu : 0u);
+  }
+#pragma unroll
+  for (int mm = 0; mm < D / 16; ++mm) {
+    const uint4 w = make_uint4(b.v0[mm].x & m0a, b.v0[mm].y & m0b, b.v1[mm].x & m1a, b.v1[mm].y & m1b);
+    const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) st[cb].o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[cb], st[cb].o[mm], 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) st[cb].o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[cb], st[cb].o[mm], 0, 0, 0);
+  }
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void decode_shared(
+    const uint16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ groups, int n_groups, uint16_t* __restrict__ out, float* __restrict__ rec,
+    float* __restrict__ rec_whole, int32_t* __restrict__ seq_info_out,
+    int n_seqs, int hq, int hkv, int g, int max_blocks, int num_blocks, float scale_log2,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, const int32_t* __restrict__ slots,
+    int32_t* __restrict__ slots_out) {
+  const int n_units = n_seqs + n_groups;
+  extern __shared__ int32_t sm[];
+  int32_t* s_len = sm;                   // [units] packed attended tokens of the unit
+  int32_t* s_pre = s_len + n_units;      // [units + 1] tile prefix sums
+  int32_t* s_base = s_pre + n_units + 1; // [N] claiming group, then shared tokens skipped
+  int32_t* s_gid = s_base + n_seqs;      // [N] group of the row, -1 for none
+  int32_t* s_gfirst = s_gid + n_seqs;    // [groups]
+  int32_t* s_gcount = s_gfirst + n_groups;
+  int32_t* s_gtok = s_gcount + n_groups;
+  __shared__ int32_t s_wsum[kSW];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+  const int s_cap = max_blocks * B;
+  const int max_members = kShCols / g;
+
+  // ---- groups: sanitize, claim rows, validate --------------------------------
+  for (int i = tid; i < n_seqs; i += 256) s_base[i] = -1;
+  for (int i = tid; i < n_groups; i += 256) {
+    const int first = groups[3 * i], cnt = groups[3 * i + 1], tok = groups[3 * i + 2];
+    const bool ok = first >= 0 && first < n_seqs && cnt >= 1 && tok >= B;
+    s_gfirst[i] = ok ? first : 0;
+    s_gcount[i] = ok ? min(min(cnt, n_seqs - first), max_members) : 0;
+    s_gtok[i] = ok ? min(tok, s_cap) : 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n_groups; i += 256)
+    for (int m = 0; m < s_gcount[i]; ++m) atomicCAS(&s_base[s_gfirst[i] + m], -1, i);
+  __syncthreads();
+  for (int i = tid; i < n_groups; i += 256) {
+    const int cnt = s_gcount[i];
+    bool ok = cnt >= 1;
+    int P = s_gtok[i];
+    for (int m = 0; m < cnt; ++m) {
+      const int n = s_gfirst[i] + m;
+      ok = ok && s_base[n] == i;
+      P = min(P, min(max(context_lens[n], 0), s_cap));  // no member attends past its own tokens
+    }
+    P -= P % B;
+    if (!ok || P < B) P = 0;
+    s_gtok[i] = P;
+  }
+  __syncthreads();
+  for (int i = tid; i < n_groups; i += 256)
+    if (s_gtok[i] == 0) s_gcount[i] = 0;
+  for (int n = tid; n < n_seqs; n += 256) {  // each thread reads and rewrites its own rows only
+    const int i = s_base[n];
+    const bool in = i >= 0 && s_gtok[i] > 0;
+    s_base[n] = in ? s_gtok[i] : 0;
+    s_gid[n] = in ? i : -1;
+  }
+  __syncthreads();
+
+  // ---- tiles per unit and their prefix sums (block-wide scan) ----------------
+  int carry = 0;
+  for (int base = 0; base < n_units; base += 256) {
+    const int u = base + tid;
+    int v = 0, packed = 0;
+    if (u < n_seqs) {
+      const int S_raw = context_lens[u];
+      const int S = min(max(S_raw, 0), s_cap);
+      const int hn = k_new != nullptr ? 1 : 0;  // the step: every row attends to its new token
+      const int fits = S_raw >= 0 && S_raw < s_cap ? 1 : 0;
+      const int rel = S + hn - s_base[u];
+      v = (rel + 31) >> 5;
+      packed = (rel << 2) | (fits << 1) | hn;
+    } else if (u < n_units) {
+      const int P = s_gcount[u - n_seqs] > 0 ? s_gtok[u - n_seqs] : 0;
+      v = (P + 31) >> 5;
+      packed = P << 2;
+    }
+#pragma unroll
+    for (int dlt = 1; dlt < 64; dlt <<= 1) {
+      const int w2 = __shfl_up(v, dlt);
+      if (lane >= dlt) v += w2;
+    }
+    if (lane == 63) s_wsum[wave] = v;
+    if (u < n_units) s_len[u] = packed;
+    __syncthreads();
+    int off = carry;
+    for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
+    if (u < n_units) s_pre[u + 1] = off + v;
+    carry += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
+  }
+  if (tid == 0) s_pre[0] = 0;
+  __syncthreads();
+  // what the merge kernel needs of row n, 8 words: its group and member (or
+  // -1), the group unit's first tile and tile count, all units' tiles, the
+  // row's own first tile and tile count
+  if (blockIdx.x == 0)
+    for (int n = tid; n < n_seqs; n += 256) {
+      const int i = s_gid[n];
+      const int gu = n_seqs + (i >= 0 ? i : 0);
+      const int4 a = make_int4(i >= 0 ? i * kShCols + (n - s_gfirst[i]) : -1, s_pre[gu], s_pre[gu + 1] - s_pre[gu],
+                               s_pre[n_units]);
+      const int4 b = make_int4(s_pre[n], s_pre[n + 1] - s_pre[n], 0, 0);
+      *reinterpret_cast<int4*>(seq_info_out + 8 * static_cast<int64_t>(n)) = a;
+      *reinterpret_cast<int4*>(seq_info_out + 8 * static_cast<int64_t>(n) + 4) = b;
+    }
+  // no barrier below this point: waves run independently
+
+  const UnitView uv{s_len, s_base, s_gfirst, s_gcount, n_seqs, g};
+  Split sp;
+  sp.init(static_cast<int64_t>(hkv) * s_pre[n_units], static_cast<int64_t>(gridDim.x) * kSW);
+  // XCD-major numbering, as in decode_stream
+  const int64_t wg = gridDim.x % 8 == 0 ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int64_t wave_id = wg * kSW + wave;
+  const int64_t x0 = sp.start(wave_id);
+  const int64_t x1 = sp.start(wave_id + 1);
+  if (x0 >= x1) return;
+
+  int lo = 0, hi = n_units - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (static_cast<int64_t>(hkv) * s_pre[mid] <= x0) lo = mid; else hi = mid - 1;
+  }
+  TilePos cur;
+  cur.n = lo;
+  {
+    const int64_t rem = x0 - static_cast<int64_t>(hkv) * s_pre[lo];
+    const int nt = tiles_of(s_pre, lo);
+    cur.j = static_cast<int>(rem / nt);
+    cur.ti = static_cast<int>(rem - static_cast<int64_t>(cur.j) * nt);
+  }
+  int piece_start = cur.ti;
+  bool first_piece = true;
+
+  int col_m[2], col_h[2];  // member and head of the lane's column in a group tile
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    col_m[cb] = (16 * cb + r) / g;
+    col_h[cb] = (16 * cb + r) - col_m[cb] * g;
+  }
+
+  Acc<D> st[2];
+  reset(st[0]);
+  reset(st[1]);
+  QOp<D> qA[2], qB[2];
+  TilePos nxt = x1 - x0 > 1 ? advance(cur, s_pre, hkv) : cur;
+  Tb<32 / B> tbA = load_tb_unit<B>(cur, uv, block_tables, max_blocks);
+  Tb<32 / B> tbB = load_tb_unit<B>(nxt, uv, block_tables, max_blocks);
+  load_q_unit<D>(qA, cur, uv, q, hq, col_m, col_h, r, gq);
+  dma_tile<D, B, false>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
+
+  int64_t x = x0;
+  auto wants_new = [&](TilePos t) -> bool {
+    return k_new != nullptr && !uv.is_group(t.n) && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
+  };
+  NewTok<D> ntok;
+  if (wants_new(cur)) load_new<D>(ntok, cur, k_new, v_new, slots, hkv, r, gq);
+  auto step = [&](auto sc_tag, QOp<D>(&qc)[2], const Tb<32 / B>& tbc, QOp<D>(&qn)[2], const Tb<32 / B>& tbn,
+                  Tb<32 / B>& tb2) -> bool {
+    constexpr int SC = decltype(sc_tag)::value;
+    unsigned char(&stc)[4][kStageBytes] = SC == 0 ? g_stage0 : g_stage1;
+    unsigned char(&stn)[4][kStageBytes] = SC == 0 ? g_stage1 : g_stage0;
+    const bool has_next = x + 1 < x1;
+    const int packed = s_len[cur.n];
+    const int S = attended_tokens(packed);
+    const int nt_cur = tiles_of(s_pre, cur.n);
+    const TilePos nxt2 = x + 2 < x1 ? advance(nxt, s_pre, hkv) : nxt;
+    const int t0 = cur.ti * 32;
+    Buf<D> b;
+    read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
+    // keep the stage's LDS reads ahead of the copies below
+    __builtin_amdgcn_sched_barrier(0);
+    if (wants_new(cur)) {
+      patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
+      if (cur.j == 0 && lane == 0) {  // the row's slot goes on to the merge kernel, which stores the token
+        const int S0 = uv.base(cur.n) + pool_tokens(packed);
+        const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
+                             static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
+                             ntok.slot % B == S0 % B;
+        slots_out[cur.n] = at_next ? ntok.slot : -1;
+      }
+    }
+    tb2 = load_tb_unit<B>(nxt2, uv, block_tables, max_blocks);
+    load_q_unit<D>(qn, nxt, uv, q, hq, col_m, col_h, r, gq);
+    if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
+    dma_tile<D, B, false>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
+    const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
+    if (uv.cols(cur.n) > 16) {  // a group of more than 16 query columns
+      tile2<D>(st, b, qc, t0, S, full, scale_log2, gq);
+    } else {
+      f32x4 sco[2];
+      qk_tile<D>(sco, b, qc[0]);
+      pv_tile<D>(st[0], sco, b, t0, S, full, scale_log2, gq);
+    }
+    const bool seg_end = cur.ti == nt_cur - 1;
+    if (seg_end || !has_next) {
+      flush_unit<D>(st, cur, uv, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, rec_whole, hq,
+                    hkv, r, gq);
+      first_piece = false;
+      piece_start = 0;
+    }
+    if (!has_next) return false;
+    ++x;
+    cur = nxt;
+    nxt = nxt2;
+    return true;
+  };
+  while (true) {
+    if (!step(std::integral_constant<int, 0>{}, qA, tbA, qB, tbB, tbA)) break;
+    if (!step(std::integral_constant<int, 1>{}, qB, tbB, qA, tbA, tbB)) break;
+  }
+}
+
+// Pieces of one (unit, KV head) segment: none (no tiles), one whole-segment
+// record, or the records of waves v_lo .. v_hi (a wave with an empty range
+// has none).  The unit's tiles start at `start` of the unit list and number nt.
+struct SegPieces {
+  int64_t v_lo;
+  int cnt;
+  bool whole, lo_second;
+};
+
+__device__ __forceinline__ SegPieces seg_pieces(const Split& sp, int start, int nt, int hkv, int j) {
+  SegPieces sg{};
+  if (nt <= 0) return sg;
+  const int64_t a = static_cast<int64_t>(hkv) * start + static_cast<int64_t>(j) * nt;
+  sg.v_lo = sp.wave_of(a);
+  const int64_t v_hi = sp.wave_of(a + nt - 1);
+  sg.whole = sg.v_lo == v_hi;
+  sg.lo_second = a > sp.start(sg.v_lo);
+  sg.cnt = sg.whole ? 1 : static_cast<int>(v_hi - sg.v_lo + 1);
+  return sg;
+}
+
+// Row 0 of piece k's record (rows are D + 4 floats apart), or nullptr.
+template <int D>
+__device__ __forceinline__ const float* piece_record(const SegPieces& sg, int k, const Split& sp, const float* rec,
+                                                     const float* rec_whole_row0) {
+  if (k < 0 || k >= sg.cnt) return nullptr;
+  if (sg.whole) return rec_whole_row0;
+  const int64_t v = sg.v_lo + k;
+  if (sp.start(v) == sp.start(v + 1)) return nullptr;
+  const int slot = (v == sg.v_lo && sg.lo_second) ? 1 : 0;
+  return rec + (v * 2 + slot) * kShCols * (D + 4);
+}
+
+// Second kernel: one workgroup per (KV head, sequence).  It merges the pieces
+// of the row's group unit (its columns) and then of its own unit, in that
+// order, with the common-maximum rule; a row without a group whose segment a
+// decode wave finished whole was written there.  The step's new token is
+// stored and the row moved forward as in merge_stream.
+template <int D>
+__global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ rec, const float* __restrict__ rec_whole,
+                                                    const int32_t* __restrict__ seq_info, uint16_t* __restrict__ out,
+                                                    int n_seqs, int hq, int hkv, int g, int64_t total_waves,
+                                                    AppendArgs ap) {
+  constexpr int E = D / 64;
+  const int j = blockIdx.x;
+  const int n = blockIdx.y;
+  RowToken<D> rt{};
+  if (ap.k_new != nullptr) rt = load_row_token<D>(ap, n, j, hkv);  // in flight during the merge
+  const int4 ia = *reinterpret_cast<const int4*>(seq_info + 8 * static_cast<int64_t>(n));
+  const int4 ib = *reinterpret_cast<const int4*>(seq_info + 8 * static_cast<int64_t>(n) + 4);
+  const int info = ia.x;
+  const int mi = info >= 0 ? info % kShCols : 0;
+  Split sp;
+  sp.init(static_cast<int64_t>(hkv) * ia.w, total_waves);
+  const SegPieces sa = info >= 0 ? seg_pieces(sp, ia.y, ia.z, hkv, j) : SegPieces{};
+  const SegPieces sb = seg_pieces(sp, ib.x, ib.y, hkv, j);
+  uint16_t* o = out + (static_cast<int64_t>(n) * hq + j * g) * D;
+  const int cnt = sa.cnt + sb.cnt;
+  const bool done_by_decode = info < 0 && sb.whole;
+  const int64_t total_rows = 2 * static_cast<int64_t>(n_seqs) * g;
+  const float* wa = rec_whole + (static_cast<int64_t>(j) * total_rows + static_cast<int64_t>(n_seqs + n - mi) * g) * (D + 4);
+  const float* wb = rec_whole + (static_cast<int64_t>(j) * total_rows + static_cast<int64_t>(n) * g) * (D + 4);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if (cnt == 0) {  // nothing to attend
+    for (int e = threadIdx.x; e < g * D; e += blockDim.x) o[e] = 0;
+  } else if (!done_by_decode && cnt <= 8) {
+    // the usual case: the maxima, sums and value rows of all pieces load together
+    const float* pb[8];
+    int ro[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pb[k] = k < sa.cnt ? piece_record<D>(sa, k, sp, rec, wa) : piece_record<D>(sb, k - sa.cnt, sp, rec, wb);
+      ro[k] = k < sa.cnt ? mi * g : 0;
+    }
+    for (int h = wave; h < g; h += 4) {
+      const float* mine = nullptr;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (lane == k && pb[k]) mine = pb[k] + (ro[k] + h) * (D + 4);
+      const float* ml = mine ? mine : rec;  // any valid address; unused
+      const float m_l = ml[0], z_l = ml[1];
+      float val[8][E];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* rk = pb[k] ? pb[k] + (ro[k] + h) * (D + 4) : rec;  // weighted by zero when missing
+#pragma unroll
+        for (int e = 0; e < E; ++e) val[k][e] = rk[4 + lane + 64 * e];
+      }
+      float mx = mine ? m_l : -INFINITY;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+      const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
+      float zz = mine ? f * z_l : 0.f;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+      float uu[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) uu[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float fk = __shfl(f, k);
+#pragma unroll
+        for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
+      }
+      const float inv = 1.f / zz;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+    }
+  } else if (!done_by_decode) {
+    auto record = [&](int k, int h) -> const float* {
+      const float* p0 =
+          k < sa.cnt ? piece_record<D>(sa, k, sp, rec, wa) : piece_record<D>(sb, k - sa.cnt, sp, rec, wb);
+      return p0 ? p0 + ((k < sa.cnt ? mi * g : 0) + h) * (D + 4) : nullptr;
+    };
+    for (int h = wave; h < g; h += 4) {
+      float mx = -INFINITY;
+      for (int base = 0; base < cnt; base += 64) {
+        const float* rr = base + lane < cnt ? record(base + lane, h) : nullptr;
+        if (rr) mx = fmaxf(mx, rr[0]);
+      }
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+      float zz = 0.f;
+      float uu[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) uu[e] = 0.f;
+      for (int base = 0; base < cnt; base += 64) {
+        const float* rr = base + lane < cnt ? record(base + lane, h) : nullptr;
+        const float f = rr ? __builtin_amdgcn_exp2f(rr[0] - mx) : 0.f;
+        if (rr) zz += f * rr[1];
+        const int c64 = min(64, cnt - base);
+        for (int k0 = 0; k0 < c64; k0 += 8) {
+          float val[8][E];
+          float fk[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int k = k0 + i;
+            const float* rk = k < c64 ? record(base + k, h) : nullptr;
+            fk[i] = __shfl(f, k & 63);
+            if (!rk) fk[i] = 0.f;
+            rk = rk ? rk : rec;  // any valid address; weighted by zero
+#pragma unroll
+            for (int e = 0; e < E; ++e) val[i][e] = rk[4 + lane + 64 * e];
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) uu[e] += fk[i] * val[i][e];
+        }
+      }
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+      const float inv = 1.f / zz;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+    }
+  }
+  if (ap.k_new != nullptr) append_row<D>(ap, rt, n, j, hkv);
+}
+
+}  // namespace
+
+bool shared_eligible(int num_seqs, int num_groups, int g, int d, int block_size, int dtype) {
+  return stream_eligible(num_seqs, g, d, block_size, dtype) && num_seqs <= kShMaxSeqs && num_groups >= 1 &&
+         num_groups <= kShMaxGroups && g <= 16;
+}
+
+StreamPlan shared_plan(int num_seqs, int num_groups, int hq, int hkv, int d, int block_size, int max_ctx) {
+  // a group unit has at most as many tiles as a sequence: size the grid as for
+  // num_seqs + num_groups sequences
+  StreamPlan p = stream_plan(num_seqs + num_groups, hq, hkv, d, block_size, max_ctx);
+  const int g = hq / hkv;
+  const int64_t waves = static_cast<int64_t>(p.workgroups) * kSW;
+  const auto round256 = [](size_t b) { return (b + 255) / 256 * 256; };
+  // workspace: [step slots | 8 words per row for the merge | wave records | whole-segment records]
+  p.prefix_offset = 0;  // unused: the merge reads each row's tile ranges from its 8 words
+  p.slots_offset = 0;
+  p.seq_group_offset = p.slots_offset + round256(static_cast<size_t>(num_seqs) * sizeof(int32_t));
+  p.records_offset = p.seq_group_offset + round256(static_cast<size_t>(num_seqs) * 8 * sizeof(int32_t));
+  p.whole_offset = p.records_offset + round256(static_cast<size_t>(waves) * 2 * kShCols * (d + 4) * sizeof(float));
+  p.workspace_bytes = p.whole_offset + static_cast<size_t>(hkv) * 2 * num_seqs * g * (d + 4) * sizeof(float);
+  p.lds_bytes = shared_lds(num_seqs, num_groups);
+  return p;
+}
+
+template <int D, int B>
+static void launch_shared_db(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
+                             const int32_t* bt, const int32_t* cl, const int32_t* groups, int n_groups, void* out,
+                             void* ws, int n, int hq, int hkv, int max_blocks, int num_blocks, float scale_log2,
+                             const StepInputs* step) {
+  char* base = static_cast<char*>(ws);
+  int32_t* slots_ws = reinterpret_cast<int32_t*>(base + p.slots_offset);
+  int32_t* seq_info = reinterpret_cast<int32_t*>(base + p.seq_group_offset);
+  float* rec = reinterpret_cast<float*>(base + p.records_offset);
+  float* rec_whole = reinterpret_cast<float*>(base + p.whole_offset);
+  const int g = hq / hkv;
+  AppendArgs ap{};
+  const int32_t* slots_in = nullptr;
+  if (step) {
+    ap.k_pool = static_cast<uint16_t*>(const_cast<void*>(k));
+    ap.v_pool = static_cast<uint16_t*>(const_cast<void*>(v));
+    ap.k_new = static_cast<const uint16_t*>(step->k_new);
+    ap.v_new = static_cast<const uint16_t*>(step->v_new);
+    slots_in = step->slots;
+    ap.slots = slots_ws;
+    ap.block_tables = const_cast<int32_t*>(bt);
+    ap.context_lens = const_cast<int32_t*>(cl);
+    ap.max_blocks = max_blocks;
+    ap.block_size = B;
+  }
+  decode_shared<D, B><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
+      static_cast<const uint16_t*>(q), k, v, bt, cl, groups, n_groups, static_cast<uint16_t*>(out), rec, rec_whole,
+      seq_info, n, hq, hkv, g, max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws);
+  merge_shared<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, rec_whole, seq_info, static_cast<uint16_t*>(out), n, hq, hkv,
+                                                     g, static_cast<int64_t>(p.workgroups) * kSW, ap);
+}
+
+int launch_shared(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
+                  const int32_t* cl, const int32_t* groups, int n_groups, void* out, void* ws, int n, int hq,
+                  int hkv, int d, int block_size, int max_blocks, int num_blocks, float scale_log2,
+                  const StepInputs* step) {
+#define PA_SHARED_CASE(DD, BB)                                                                                     \
+  if (d == DD && block_size == BB) {                                                                               \
+    launch_shared_db<DD, BB>(p, s, q, k, v, bt, cl, groups, n_groups, out, ws, n, hq, hkv, max_blocks, num_blocks, \
+                             scale_log2, step);                                                                    \
+    return launch_status();                                                                                        \
+  }
+  PA_SHARED_CASE(128, 16)
+  PA_SHARED_CASE(128, 8)
+  PA_SHARED_CASE(128, 32)
+  PA_SHARED_CASE(64, 16)
+  PA_SHARED_CASE(64, 8)
+  PA_SHARED_CASE(64, 32)
+#undef PA_SHARED_CASE
+  return PA_ERR_UNSUPPORTED;
+}
+
+}  // namespace pa

@@ -13,6 +13,8 @@ struct StreamPlan {
   size_t prefix_offset = 0;    // workspace: [tile prefix sums | step slots | summary records]
   size_t slots_offset = 0;
   size_t records_offset = 0;
+  size_t seq_group_offset = 0;  // decode_shared: group, member and tile ranges of each sequence
+  size_t whole_offset = 0;      // decode_shared: records of whole segments
   size_t workspace_bytes = 0;
   size_t lds_bytes = 0;
 };
@@ -36,5 +38,15 @@ int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void*
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
                   int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
                   const float* k_scale = nullptr, const float* v_scale = nullptr);
+
+// Shared-prefix kernel (decode_shared.hip): groups of consecutive rows whose
+// first P tokens lie in the same full blocks, int32 [num_groups][3] =
+// (first row, rows, P), read on the device.
+bool shared_eligible(int num_seqs, int num_groups, int g, int d, int block_size, int dtype);
+StreamPlan shared_plan(int num_seqs, int num_groups, int hq, int hkv, int d, int block_size, int max_ctx);
+int launch_shared(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
+                  const int32_t* cl, const int32_t* groups, int n_groups, void* out, void* ws, int n, int hq,
+                  int hkv, int d, int block_size, int max_blocks, int num_blocks, float scale_log2,
+                  const StepInputs* step);
 
 }  // namespace pa

@@ -1,0 +1,543 @@
+// Device building blocks of the persistent bf16 decode kernels
+// (decode_stream.hip, decode_shared.hip): the 32-token tile pipeline (block
+// table entries, LDS-staged key/value block images, Q operands, the step's new
+// token), the matrix-core tile math with its online softmax, the equal
+// per-wave work split, the merge of a segment's pieces and the step's append.
+//
+// What is computed ("PagedAttention: Virtual Memory for the KV Cache",
+// sections 1, 13 and 16; "PagedAttention in vLLM: scattered memory, exact
+// attention", sections 10-11): softmax(scale * q K^T) V over a sequence's
+// cached tokens, gathered block by block through its block table, as
+// (m, z, u) summaries of token ranges that merge with the common-maximum rule.
+//
+// Per tile (lane = 16 gq + r):
+//   q.K^T  A = 16 key rows x 32 d (lane: row r, chunk 4 jj + gq, one 16-byte
+//          load), B = Q^T (column r) -> S^T[4 gq + i][r]
+//   P.V    A = V^T rows d = 16 mm + r, 8 tokens (4 of each 16-token slab,
+//          two 8-byte loads), B = P^T: the lane's own 8 probabilities, split
+//          into bf16 high and residual parts -> O^T[16 mm + 4 gq + i][r].
+//
+// Pool layout (per layer): K [num_blocks][Hkv][D/8][B][8], V [num_blocks][Hkv][D][B].
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace pa {
+namespace {
+
+constexpr int kSW = 4;        // waves per workgroup
+
+struct TilePos {
+  int n, j, ti;
+};
+
+template <int D>
+struct Buf {
+  bf16x8 k[2][D / 32];  // key rows of slabs 0 and 1 (q.K^T A operands)
+  uint2 v0[D / 16];     // value groups of slab 0 (half of each P.V A operand)
+  uint2 v1[D / 16];     // value groups of slab 1
+  bool blk0, blk1;      // the lane's value-group block of slab 0 / 1 exists in the pool
+};
+
+template <int D>
+struct QOp {
+  bf16x8 q[D / 32];
+};
+
+template <int NB>
+struct Tb {  // physical blocks of a tile's tokens, -1 where the sequence has ended (wave-uniform)
+  int blk[NB];
+};
+
+// Tokens per tile: 32 for a bf16 cache, 64 for an FP8 cache (the same 16 KiB
+// of keys and values per tile either way).
+template <bool F8>
+constexpr int kTok = F8 ? 64 : 32;
+template <bool F8>
+constexpr int kTokShift = F8 ? 6 : 5;
+
+__device__ __forceinline__ int tiles_of(const int32_t* s_pre, int n) { return s_pre[n + 1] - s_pre[n]; }
+
+// Next tile in (n, j, ti) order; only called when one exists.
+__device__ __forceinline__ TilePos advance(TilePos t, const int32_t* s_pre, int hkv) {
+  if (t.ti + 1 < tiles_of(s_pre, t.n)) {
+    ++t.ti;
+    return t;
+  }
+  t.ti = 0;
+  if (t.j + 1 < hkv) {
+    ++t.j;
+    return t;
+  }
+  t.j = 0;
+  do {
+    ++t.n;
+  } while (tiles_of(s_pre, t.n) == 0);
+  return t;
+}
+
+// Per sequence the kernel keeps (tokens << 2) | (fits << 1) | new: `tokens`
+// counts the attended tokens, `new` marks that the last of them is the step's
+// new token (taken from k_new / v_new, not from the pool), `fits` that the
+// row's next position is inside its table (so the token may be stored).
+__device__ __forceinline__ int attended_tokens(int packed) { return packed >> 2; }
+__device__ __forceinline__ bool has_new_token(int packed) { return packed & 1; }
+__device__ __forceinline__ bool next_fits(int packed) { return (packed >> 1) & 1; }
+__device__ __forceinline__ int pool_tokens(int packed) { return (packed >> 2) - (packed & 1); }
+
+// The step's new token of one (sequence, KV head) in the lanes' MFMA operand
+// roles: key chunk 4 jj + gq (8 values) and value rows d = 16 mm + r.
+template <int D>
+struct NewTok {
+  bf16x8 k[D / 32];
+  uint32_t v[D / 32];  // value rows 16 mm + r, two per word (even mm low)
+  int slot;            // the row's slot (read with KV head 0's token)
+};
+
+template <int D>
+__device__ __forceinline__ void load_new(NewTok<D>& nt, TilePos t, const uint16_t* __restrict__ k_new,
+                                         const uint16_t* __restrict__ v_new, const int32_t* __restrict__ slots,
+                                         int hkv, int r, int gq) {
+  const int64_t row = (static_cast<int64_t>(t.n) * hkv + t.j) * D;
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj)
+    nt.k[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k_new + row + (4 * jj + gq) * 8));
+#pragma unroll
+  for (int m2 = 0; m2 < D / 32; ++m2)
+    nt.v[m2] = uint32_t(v_new[row + 32 * m2 + r]) | (uint32_t(v_new[row + 32 * m2 + 16 + r]) << 16);
+  if (t.j == 0) nt.slot = slots[t.n];
+}
+
+// Table entries of a tile's blocks.  Always loaded (index clamped into the
+// row) and replaced by -1 past the end of the sequence, so no load sits behind
+// a branch and the compiler can keep the pipeline's loads in flight.
+template <int B, int TOK>
+__device__ __forceinline__ Tb<TOK / B> load_tb(TilePos t, const int32_t* __restrict__ block_tables, int max_blocks,
+                                               const int32_t* s_len) {
+  const int32_t* row = block_tables + static_cast<int64_t>(t.n) * max_blocks;
+  const int S = pool_tokens(s_len[t.n]);
+  const int t0 = t.ti * TOK;
+  Tb<TOK / B> tb;
+#pragma unroll
+  for (int i = 0; i < TOK / B; ++i) {
+    const int e = row[min(t0 / B + i, max_blocks - 1)];
+    tb.blk[i] = t0 + i * B < S ? e : -1;
+  }
+  return tb;
+}
+
+// Q^T operand of MFMA jj: 8 elements of head r.  With a bf16 cache lane gq
+// takes d-chunk 4 jj + gq (as the key layout interleaves chunks); with an FP8
+// cache it takes elements gq D / 4 + 8 jj .. + 7, the lane's contiguous
+// quarter of d, which its 16-byte key reads cover.
+template <int D, bool F8>
+__device__ __forceinline__ void load_q(QOp<D>& qo, TilePos t, const uint16_t* __restrict__ q, int hq, int g, int r,
+                                       int gq) {
+  // padding columns r >= G read head 0 of the group; their results are never used
+  const uint16_t* qh = q + (static_cast<int64_t>(t.n) * hq + t.j * g + (r < g ? r : 0)) * D;
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj) {
+    const int e0 = F8 ? gq * (D / 4) + 8 * jj : (4 * jj + gq) * 8;
+    qo.q[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qh + e0));
+  }
+}
+
+template <int D>
+struct Acc {
+  f32x4 o[D / 16];
+  float m, z;
+};
+
+template <int D>
+__device__ __forceinline__ void reset(Acc<D>& st) {
+#pragma unroll
+  for (int mm = 0; mm < D / 16; ++mm) st.o[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.z = 0.f;
+}
+
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+
+// Per wave, two LDS stages for one tile's key and value block images (16 KiB
+// each at D = 128).  Two distinct objects, so the compiler can tell the wait
+// for one stage's copy from the other's.
+constexpr int kStageBytes = 2 * 32 * 128 * 2;
+__shared__ __attribute__((aligned(16))) unsigned char g_stage0[4][kStageBytes];
+__shared__ __attribute__((aligned(16))) unsigned char g_stage1[4][kStageBytes];
+
+// Bytes of one tile's keys (and, again, of its values) in LDS: the images of
+// the blocks that hold its tokens -- 32 / B bf16 images of B * D * 2 bytes, or
+// 64 / B FP8 images of B * D bytes.
+template <int D>
+constexpr int kStageHalf = 64 * D;
+
+// Copy one tile's key and value block images into an LDS stage with
+// global_load_lds (16 bytes per lane, 1 KiB per instruction, straight to LDS:
+// no registers held while in flight).  A missing block (past the end, or an
+// id outside the pool) is read from block 0 -- a valid address -- and its
+// tokens are masked out in pv_tile.
+// The tile's images lie back to back in the stage; 1 KiB piece p of them is
+// one instruction, lane l bringing bytes p * 1024 + 16 l .. + 15.  An image
+// smaller than 1 KiB (FP8, D = 64, B = 8: 512 bytes) shares a piece with the
+// next block's image, so the lanes of one instruction read two blocks.
+template <int D, int B, bool F8>
+__device__ __forceinline__ void dma_tile(unsigned char* stage_ptr, int j, const Tb<kTok<F8> / B>& tb,
+                                         const void* __restrict__ k_pool, const void* __restrict__ v_pool, int hkv,
+                                         int num_blocks, int lane) {
+  constexpr int NB = kTok<F8> / B;
+  constexpr int IMG = D * B * (F8 ? 1 : 2);  // bytes of one (block, KV head) image
+  constexpr int PIECES = NB * IMG / 1024;
+  lds_byte* stage = (lds_byte*)stage_ptr;  // LDS address for the copy engine
+  const int64_t blk_stride = static_cast<int64_t>(hkv) * IMG;
+  const char* kb = reinterpret_cast<const char*>(k_pool) + static_cast<int64_t>(j) * IMG;
+  const char* vb = reinterpret_cast<const char*>(v_pool) + static_cast<int64_t>(j) * IMG;
+#pragma unroll
+  for (int p = 0; p < PIECES; ++p) {
+    int e, off;
+    if constexpr (IMG >= 1024) {
+      e = tb.blk[p * 1024 / IMG];
+      off = p * 1024 % IMG + lane * 16;
+    } else {
+      constexpr int PER = 1024 / IMG;  // images per piece
+      const int bi = p * PER + lane * 16 / IMG;
+      e = tb.blk[p * PER];  // tb.blk[bi] by selects: a lane-dependent index would put tb in scratch
+#pragma unroll
+      for (int i = 1; i < PER; ++i)
+        if (bi == p * PER + i) e = tb.blk[p * PER + i];
+      off = lane * 16 % IMG;
+    }
+    const int64_t pb = (e >= 0 && e < num_blocks) ? e : 0;
+    __builtin_amdgcn_global_load_lds(kb + pb * blk_stride + off, stage + p * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + pb * blk_stride + off, stage + kStageHalf<D> + p * 1024, 16, 0, 0);
+  }
+}
+
+// Read a staged tile's MFMA operands from LDS into registers (the same lane
+// roles as direct loads would give) and mark which value groups exist.
+template <int D, int B>
+__device__ __forceinline__ void read_tile(Buf<D>& b, const unsigned char* stage, const Tb<32 / B>& tb, int num_blocks,
+                                          int r, int gq) {
+  constexpr int IMG = D * B * 2;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int tk = 16 * a + r;  // key row of slab a
+    const unsigned char* kimg = stage + (tk / B) * IMG + (tk % B) * 16;
+#pragma unroll
+    for (int jj = 0; jj < D / 32; ++jj)
+      b.k[a][jj] = *reinterpret_cast<const bf16x8*>(kimg + (4 * jj + gq) * B * 16);
+    const int tv = 16 * a + 4 * gq;  // first token of the value group
+    const unsigned char* vimg = stage + kStageHalf<D> + (tv / B) * IMG + (tv % B) * 2;
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm) {
+      const uint2 v = *reinterpret_cast<const uint2*>(vimg + (16 * mm + r) * B * 2);
+      if (a == 0)
+        b.v0[mm] = v;
+      else
+        b.v1[mm] = v;
+    }
+    int pv = tb.blk[0];  // tb.blk[tv / B] by selects: a lane-dependent index would put tb in scratch
+#pragma unroll
+    for (int i = 1; i < 32 / B; ++i)
+      if (tv / B == i) pv = tb.blk[i];
+    const bool ok = pv >= 0 && pv < num_blocks;
+    if (a == 0)
+      b.blk0 = ok;
+    else
+      b.blk1 = ok;
+  }
+}
+
+// Put the new token (tile-relative position p) into a staged tile's operands
+// and count its value group as present: its block may not be in the table yet.
+template <int D>
+__device__ __forceinline__ void patch_new(Buf<D>& b, const NewTok<D>& nt, int p, int r, int gq) {
+  // every operand is rewritten with selects: indexing the register arrays by a
+  // run-time slab would move them to scratch
+  const int a = p >> 4;        // slab
+  const int rr = p & 15;       // key row in the slab
+  const int idx = rr & 3;      // token within the lane's value group
+  const bool krow0 = a == 0 && r == rr, krow1 = a == 1 && r == rr;
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj) {
+    b.k[0][jj] = krow0 ? nt.k[jj] : b.k[0][jj];
+    b.k[1][jj] = krow1 ? nt.k[jj] : b.k[1][jj];
+  }
+  const bool grp = gq == (rr >> 2);
+  const bool lo = idx < 2;
+  const int sh = (idx & 1) * 16;
+  const uint32_t keep = ~(0xffffu << sh);
+  const bool g0 = grp && a == 0, g1 = grp && a == 1;
+#pragma unroll
+  for (int mm = 0; mm < D / 16; ++mm) {
+    const uint32_t val = ((nt.v[mm >> 1] >> (16 * (mm & 1))) & 0xffffu) << sh;
+    b.v0[mm].x = g0 && lo ? ((b.v0[mm].x & keep) | val) : b.v0[mm].x;
+    b.v0[mm].y = g0 && !lo ? ((b.v0[mm].y & keep) | val) : b.v0[mm].y;
+    b.v1[mm].x = g1 && lo ? ((b.v1[mm].x & keep) | val) : b.v1[mm].x;
+    b.v1[mm].y = g1 && !lo ? ((b.v1[mm].y & keep) | val) : b.v1[mm].y;
+  }
+  b.blk0 = b.blk0 || g0;
+  b.blk1 = b.blk1 || g1;
+}
+
+// Scores of one 32-token tile on the matrix cores: S^T = K . Q^T.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x4 (&s)[2], const Buf<D>& b, const QOp<D>& qo) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < D / 32; ++jj)
+      s[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.k[a][jj], qo.q[jj], s[a], 0, 0, 0);
+  }
+}
+
+// Online softmax (base 2) and weighted values on the matrix cores for one
+// tile.  `full` (wave-uniform): all 32 tokens exist and their blocks are in
+// the pool, so no masking is needed.
+template <int D>
+__device__ __forceinline__ void pv_tile(Acc<D>& st, const f32x4 (&s)[2], const Buf<D>& b, int t0, int S, bool full,
+                                        float scale_log2, int gq) {
+  // valid tokens of the lane's two value groups (its score rows are the same tokens)
+  int n0 = 4, n1 = 4;
+  if (!full) {
+    n0 = b.blk0 ? min(max(S - (t0 + 4 * gq), 0), 4) : 0;
+    n1 = b.blk1 ? min(max(S - (t0 + 16 + 4 * gq), 0), 4) : 0;
+  }
+  float x[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[a][i] = i < (a ? n1 : n0) ? s[a][i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, x[a][i]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(st.m, tmax);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  st.m = m_new;
+  float psum = 0.f;
+  bf16x8 phi, plo;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(x[a][i] - m_new);
+      psum += p;
+      const __bf16 h = static_cast<__bf16>(p);
+      phi[4 * a + i] = h;
+      plo[4 * a + i] = static_cast<__bf16>(p - static_cast<float>(h));
+    }
+  st.z = st.z * alpha + psum;
+  // rescale only when some running maximum moved (rare once it has settled)
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm) st.o[mm] *= alpha;
+  }
+  uint32_t m0a = 0xffffffffu, m0b = 0xffffffffu, m1a = 0xffffffffu, m1b = 0xffffffffu;
+  if (!full) {  // zero values of missing tokens: stale or NaN slots must not reach P.V (0 * NaN is NaN)
+    m0a = n0 >= 2 ? 0xffffffffu : (n0 == 1 ? 0x0000ffffu : 0u);
+    m0b = n0 >= 4 ? 0xffffffffu : (n0 == 3 ? 0x0000ffffu : 0u);
+    m1a = n1 >= 2 ? 0xffffffffu : (n1 == 1 ? 0x0000ffffu : 0u);
+    m1b = n1 >= 4 ? 0xffffffffu : (n1 == 3 ? 0x0000ffffu : 0u);
+  }
+#pragma unroll
+  for (int mm = 0; mm < D / 16; ++mm) {
+    const uint4 w = make_uint4(b.v0[mm].x & m0a, b.v0[mm].y & m0b, b.v1[mm].x & m1a, b.v1[mm].y & m1b);
+    const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, st.o[mm], 0, 0, 0);
+    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, st.o[mm], 0, 0, 0);
+  }
+}
+
+// Work split shared by decode_stream and merge_stream: tiles [w T / W,
+// (w + 1) T / W) belong to wave w.
+struct Split {
+  int64_t T, W;
+  __device__ void init(int64_t total_tiles, int64_t waves) {
+    T = total_tiles;
+    W = waves;
+  }
+  __device__ int64_t start(int64_t w) const { return w * T / W; }
+  __device__ int64_t wave_of(int64_t x) const { return ((x + 1) * W - 1) / T; }
+};
+
+// The step's append, done by the merge kernel once every decode wave has
+// read the pool, the tables and the lengths: when row n's slot is its next
+// position (the decode kernel checked it and left the slot, or -1, in the
+// workspace), the new token of KV head j goes to block slot / B, offset
+// slot % B, and the row moves forward -- table entry S / B = slot / B,
+// length S + 1 ("PagedAttention: Virtual Memory for the KV Cache", sections 7
+// and 16).
+struct AppendArgs {
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const uint16_t* k_new;  // nullptr: plain decode, no append
+  const uint16_t* v_new;
+  const int32_t* slots;   // workspace: the slot when it is the row's next position, else -1
+  int32_t* block_tables;
+  int32_t* context_lens;
+  int max_blocks, block_size;
+};
+
+// The new token of (row n, KV head j) as thread t of the workgroup holds it:
+// key chunk t (t < D / 8) and value row d = t (t < D).  Loaded when the merge
+// kernel starts, stored when it ends.
+template <int D>
+struct RowToken {
+  int64_t slot;
+  uint4 k;
+  uint16_t v;
+};
+
+template <int D>
+__device__ __forceinline__ RowToken<D> load_row_token(const AppendArgs& ap, int n, int j, int hkv) {
+  RowToken<D> rt;
+  const int64_t src = (static_cast<int64_t>(n) * hkv + j) * D;
+  const int t = threadIdx.x;
+  rt.slot = ap.slots[n];
+  rt.k = t < D / 8 ? *reinterpret_cast<const uint4*>(ap.k_new + src + t * 8) : make_uint4(0, 0, 0, 0);
+  rt.v = t < D ? ap.v_new[src + t] : 0;
+  return rt;
+}
+
+template <int D>
+__device__ __forceinline__ void append_row(const AppendArgs& ap, const RowToken<D>& rt, int n, int j, int hkv) {
+  if (rt.slot < 0) return;
+  const int B = ap.block_size;
+  const int64_t pb = rt.slot / B;
+  const int off = static_cast<int>(rt.slot % B);
+  const int64_t head = pb * hkv + j;
+  const int t = threadIdx.x;
+  if (t < D / 8) *reinterpret_cast<uint4*>(ap.k_pool + ((head * (D / 8) + t) * B + off) * 8) = rt.k;
+  if (t < D) ap.v_pool[(head * D + t) * B + off] = rt.v;
+  if (j == 0 && t == 0) {  // the only thread that reads or writes the row
+    const int pos = ap.context_lens[n];
+    ap.block_tables[static_cast<int64_t>(n) * ap.max_blocks + pos / B] = static_cast<int32_t>(pb);
+    ap.context_lens[n] = pos + 1;
+  }
+}
+
+// Combine the summary records of one segment cut by wave-range boundaries,
+// or write zeros for an empty sequence.  Unit n's tiles are prefix[n] ..
+// prefix[n + 1] - 1 of the n_units units; a wave's two record slots hold
+// `rows` rows each.  Wave h' of the workgroup takes heads
+// h', h' + 4, ...; lanes read records in parallel (wave v_lo + lane), so the
+// merge costs a few memory latencies rather than one per record.  Records
+// combine in wave order, which is tile order.
+template <int D>
+__device__ __forceinline__ void merge_segment(const float* __restrict__ rec, const int32_t* __restrict__ prefix,
+                                              uint16_t* __restrict__ out, int n_units, int hq, int hkv, int g,
+                                              int rows, int64_t total_waves, int j, int n) {
+  constexpr int E = D / 64;  // output elements per lane
+  const int64_t p_n = prefix[n];
+  const int nt = prefix[n + 1] - prefix[n];
+  uint16_t* o = out + (static_cast<int64_t>(n) * hq + j * g) * D;
+  if (nt == 0) {
+    for (int e = threadIdx.x; e < g * D; e += blockDim.x) o[e] = 0;
+    return;
+  }
+  Split sp;
+  sp.init(static_cast<int64_t>(hkv) * prefix[n_units], total_waves);
+  const int64_t a = hkv * p_n + static_cast<int64_t>(j) * nt;  // first tile of the segment
+  const int64_t b = a + nt;                                    // one past its last tile
+  const int64_t v_lo = sp.wave_of(a);
+  const int64_t v_hi = sp.wave_of(b - 1);
+  if (v_lo == v_hi) return;  // finished inside one wave
+  const bool lo_second = a > sp.start(v_lo);  // the segment is not the first piece of wave v_lo
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // the record of wave v for head h, or nullptr for a wave with an empty range
+  auto record = [&](int64_t v, int h) -> const float* {
+    if (v > v_hi || sp.start(v) == sp.start(v + 1)) return nullptr;
+    const int slot = (v == v_lo && lo_second) ? 1 : 0;
+    return rec + ((v * 2 + slot) * rows + h) * (D + 4);
+  };
+  if (v_hi - v_lo < 8) {
+    // up to 8 pieces (the usual case): the maxima, sums and value rows of all
+    // pieces load together, in one memory round trip
+    const int cnt = static_cast<int>(v_hi - v_lo + 1);
+    for (int h = wave; h < g; h += 4) {
+      const float* mine = lane < cnt ? record(v_lo + lane, h) : nullptr;
+      const float* ml = mine ? mine : rec;  // any valid address; unused
+      const float m_l = ml[0], z_l = ml[1];
+      float val[8][E];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* rk = k < cnt ? record(v_lo + k, h) : nullptr;
+        rk = rk ? rk : rec;  // weighted by zero below
+#pragma unroll
+        for (int e = 0; e < E; ++e) val[k][e] = rk[4 + lane + 64 * e];
+      }
+      float mx = mine ? m_l : -INFINITY;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+      const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
+      float zz = mine ? f * z_l : 0.f;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+      float uu[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) uu[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float fk = __shfl(f, k);  // zero for k >= cnt and empty ranges
+#pragma unroll
+        for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
+      }
+      const float inv = 1.f / zz;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+    }
+    return;
+  }
+  for (int h = wave; h < g; h += 4) {
+    float mx = -INFINITY;
+    for (int64_t base = v_lo; base <= v_hi; base += 64) {
+      const float* rr = record(base + lane, h);
+      if (rr) mx = fmaxf(mx, rr[0]);
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+    float zz = 0.f;
+    float uu[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) uu[e] = 0.f;
+    for (int64_t base = v_lo; base <= v_hi; base += 64) {
+      const float* rr = record(base + lane, h);
+      const float f = rr ? __builtin_amdgcn_exp2f(rr[0] - mx) : 0.f;
+      if (rr) zz += f * rr[1];
+      // value rows in batches of 8 records, their loads issued together
+      const int cnt = static_cast<int>(min<int64_t>(64, v_hi - base + 1));
+      for (int k0 = 0; k0 < cnt; k0 += 8) {
+        float val[8][E];
+        float fk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int k = k0 + i;
+          const float* rk = k < cnt ? record(base + k, h) : nullptr;
+          fk[i] = __shfl(f, k & 63);
+          if (!rk) fk[i] = 0.f;
+          rk = rk ? rk : rec;  // any valid address; weighted by zero
+#pragma unroll
+          for (int e = 0; e < E; ++e) val[i][e] = rk[4 + lane + 64 * e];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < E; ++e) uu[e] += fk[i] * val[i][e];
+      }
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+    const float inv = 1.f / zz;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+  }
+}
+
+}  // namespace
+}  // namespace pa

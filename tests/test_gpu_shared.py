@@ -1,0 +1,264 @@
+"""GPU: pa_decode_shared / pa_decode_step_shared against the fp64 oracle.
+
+The shared-prefix kernel reads each group's shared full blocks once for all
+its members; its output must still be the plain attention of every row
+([P1] section 15: shared full blocks are immutable; [P2] section 11: the
+summaries of the shared part and of the rest merge exactly).  The oracle is
+the plain paged decode; groups come from the product block manager
+(pa_bm_shared_groups), which the CPU tests check against the oracle rule.
+"""
+
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import DecodeCase, assert_close, oracle_outputs
+from oracle import attention as OA
+from oracle.block_manager import BlockManagerModel, shared_prefix_groups
+from pool_layout import k_to_logical, poison_unused_, v_to_logical
+
+pytestmark = pytest.mark.gpu
+
+
+def _case_from(bm, model, seqs, hq, hkv, d, bs, seed, dtype=torch.bfloat16):
+    """Batch `seqs` of both managers (tables must agree), seeded pools (unused slots NaN) and queries on the device."""
+    import paged_kv_cache_124_amd as pa
+    nb = model.num_blocks
+    mb = max(len(model.tables[s]) for s in seqs) + 2
+    st, tables, lens = bm.build_batch(seqs, mb)
+    mst, mtables, mlens = model.build_batch(seqs, mb)
+    assert st == mst == 0 and tables.tolist() == mtables and lens.tolist() == mlens
+    elem = torch.tensor([], dtype=dtype).element_size()
+    kshape, vshape = pa.pool_shapes(nb, hkv, d, bs, elem)
+    w = synth.gqa8b()
+    k = synth.fill_randn_(torch.empty(kshape, dtype=dtype, device="cuda"), w.value_scale, seed * 10 + 1)
+    v = synth.fill_randn_(torch.empty(vshape, dtype=dtype, device="cuda"), w.value_scale, seed * 10 + 2)
+    poison_unused_(k, v, tables, lens, bs)
+    q = synth.randn((len(seqs), hq, d), dtype, w.value_scale, seed * 10 + 3, "cuda")
+    return DecodeCase(w, list(lens), hq, hkv, d, bs, dtype, nb, mb, bm, model, tables, k, v, q,
+                      torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), 1.0 / math.sqrt(d))
+
+
+def _forest(seed, hq, hkv, d, bs, roots=4, max_len=40, forks=12, appends=30, extra=64):
+    """A seeded fork forest on both block managers and its batch (rows in sequence-id order)."""
+    import paged_kv_cache_124_amd as pa
+    rng = random.Random(seed)
+    lens0 = [rng.randint(bs, max_len * bs // 4) for _ in range(roots)]
+    nb = sum(-(-s // bs) for s in lens0) * 2 + forks * (appends // bs + 2) + extra
+    order = synth.pop_order(nb, seed)
+    bm = pa.BlockManager(nb, bs, order)
+    model = BlockManagerModel(nb, bs, [int(x) for x in order])
+    live, nid = [], 0
+    for s in lens0:
+        for x in (bm, model):
+            assert x.add_seq(nid, s) == 0
+        live.append(nid)
+        nid += 1
+    for _ in range(forks):
+        p = rng.choice(live)
+        for x in (bm, model):
+            assert x.fork(p, nid) == 0
+        live.append(nid)
+        nid += 1
+        for _ in range(rng.randint(0, appends)):
+            s = rng.choice(live)
+            for x in (bm, model):
+                assert x.append_slot(s)[0] == 0
+    seqs = sorted(live)
+    return _case_from(bm, model, seqs, hq, hkv, d, bs, seed), seqs
+
+
+def _groups(case, seqs, members=None):
+    g = case.hq // case.hkv
+    members = members or max(32 // g, 1)
+    st, groups = case.bm.shared_groups(seqs, members)
+    assert st == 0
+    mtables = [case.model.tables[s] for s in seqs]
+    assert [tuple(r) for r in groups.tolist()] == shared_prefix_groups(mtables, list(case.lens), case.block_size,
+                                                                       members)
+    return groups
+
+
+@pytest.mark.parametrize("d,bs,hq,hkv", [(128, 16, 32, 8), (128, 8, 32, 8), (128, 32, 32, 8), (64, 16, 8, 2),
+                                         (128, 16, 8, 8), (64, 32, 16, 1), (128, 16, 32, 4), (64, 8, 32, 2)])
+def test_forest_decode_matches_the_oracle(d, bs, hq, hkv):
+    """Random fork forests: every output of pa_decode_shared against the oracle, for G = 1 .. 16."""
+    import paged_kv_cache_124_amd as pa
+    seed = 31 * d + 7 * bs + hq + hkv
+    print(f"[case] forest d={d} B={bs} Hq={hq} Hkv={hkv} seed={seed}", flush=True)
+    case, seqs = _forest(seed, hq, hkv, d, bs)
+    groups = _groups(case, seqs)
+    assert len(groups) > 0
+    out = torch.empty_like(case.q)
+    pa.pa_decode_shared(out, case.q, case.k, case.v, case.tables_dev, case.lens_dev,
+                        torch.from_numpy(groups).cuda(), case.scale, case.max_ctx)
+    ref = oracle_outputs(case, range(len(seqs)))
+    assert_close(out, ref, f"forest shared d={d} B={bs} G={hq // hkv}")
+    plain = torch.empty_like(case.q)
+    pa.pa_decode(plain, case.q, case.k, case.v, case.tables_dev, case.lens_dev, case.scale, case.max_ctx)
+    assert_close(plain, ref, "forest plain")
+    # run to run: the split and the merge order are fixed, so the bits repeat
+    out2 = torch.empty_like(case.q)
+    pa.pa_decode_shared(out2, case.q, case.k, case.v, case.tables_dev, case.lens_dev,
+                        torch.from_numpy(groups).cuda(), case.scale, case.max_ctx)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_group_edge_cases():
+    """Groups the kernel must ignore or trim; every output stays the plain attention.
+
+    Batch: two unrelated rows, then one 87-token prompt (5 full blocks and a
+    7-token tail) forked into 10 samples that append 0 .. 30 tokens each, so
+    the samples agree on their first 5 blocks and no further.
+    """
+    import paged_kv_cache_124_amd as pa
+    hq, hkv, d, bs = 32, 8, 128, 16
+    nb = 128
+    order = synth.pop_order(nb, 91)
+    bm = pa.BlockManager(nb, bs, order)
+    model = BlockManagerModel(nb, bs, [int(x) for x in order])
+    appends = [0, 1, 9, 20, 30, 2, 3, 4, 5, 6]
+    for x in (bm, model):
+        assert x.add_seq(100, 33) == 0 and x.add_seq(101, 150) == 0 and x.add_seq(0, 87) == 0
+        for i in range(1, len(appends)):
+            assert x.fork(0, i) == 0
+        for i, a in enumerate(appends):
+            for _ in range(a):
+                assert x.append_slot(i)[0] == 0
+    seqs = [100, 101] + list(range(len(appends)))
+    case = _case_from(bm, model, seqs, hq, hkv, d, bs, 91)
+    n = len(seqs)
+    found = _groups(case, seqs)
+    assert found.tolist() == [[2, 8, 80], [10, 2, 80]]  # at most 32 / G = 8 rows per group
+    ref = oracle_outputs(case, range(n), tables=case.tables)  # rows are not sequence ids here
+    variants = {
+        "as found": found.tolist(),
+        "one group of all 10 samples (trimmed to 8 rows)": [[2, 10, 80]],
+        "P past the shortest member (cut to 87, then to 80)": [[2, 8, 1080], [10, 2, 80]],
+        "P not a multiple of B (75 -> 64)": [[2, 8, 75], [10, 2, 75]],
+        "P below one block (ignored)": [[2, 8, 15], [10, 2, 80]],
+        "rows past the batch (trimmed)": [[2, 8, 80], [10, 50, 80]],
+        "first row outside the batch (ignored)": [[n, 2, 16], [-3, 2, 16], [2, 8, 80]],
+        "no rows (ignored)": [[2, 0, 80], [10, 2, 80]],
+        "overlapping groups (one used)": [[2, 8, 80], [5, 3, 80], [10, 2, 80]],
+        "groups of one": [[2, 1, 80], [3, 1, 80]],
+    }
+    for what, gl in variants.items():
+        print(f"[case] edge: {what}", flush=True)
+        g_arr = torch.tensor(np.asarray(gl, dtype=np.int32).reshape(-1, 3), device="cuda")
+        out = torch.empty_like(case.q)
+        pa.pa_decode_shared(out, case.q, case.k, case.v, case.tables_dev, case.lens_dev, g_arr, case.scale,
+                            case.max_ctx)
+        assert_close(out, ref, f"edge: {what}")
+
+
+def test_member_with_no_tokens_of_its_own():
+    """Two rows of exactly 3 full blocks, forked: the second has nothing past the shared part."""
+    import paged_kv_cache_124_amd as pa
+    hq, hkv, d, bs = 32, 8, 128, 16
+    nb = 16
+    bm = pa.BlockManager(nb, bs, list(range(nb)))
+    model = BlockManagerModel(nb, bs, list(range(nb)))
+    for x in (bm, model):
+        assert x.add_seq(0, 3 * bs) == 0 and x.fork(0, 1) == 0 and x.add_seq(2, 40) == 0
+    seqs = [0, 1, 2]
+    st, tables, lens = bm.build_batch(seqs, 4)
+    assert st == 0
+    w = synth.gqa8b()
+    kshape, vshape = pa.pool_shapes(nb, hkv, d, bs, 2)
+    k = synth.fill_randn_(torch.empty(kshape, dtype=torch.bfloat16, device="cuda"), w.value_scale, 11)
+    v = synth.fill_randn_(torch.empty(vshape, dtype=torch.bfloat16, device="cuda"), w.value_scale, 12)
+    poison_unused_(k, v, tables, lens, bs)
+    q = synth.randn((3, hq, d), torch.bfloat16, w.value_scale, 13, "cuda")
+    case = DecodeCase(w, list(lens), hq, hkv, d, bs, torch.bfloat16, nb, 4, bm, model, tables, k, v, q,
+                      torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), 1.0 / math.sqrt(d))
+    st, groups = bm.shared_groups(seqs, 8)
+    assert st == 0 and groups.tolist() == [[0, 2, 3 * bs]]
+    out = torch.empty_like(q)
+    pa.pa_decode_shared(out, q, k, v, case.tables_dev, case.lens_dev, torch.from_numpy(groups).cuda(), case.scale,
+                        int(max(lens)))
+    assert_close(out, oracle_outputs(case, range(3)), "member with no own tokens")
+    # both members attend to the same tokens with different queries
+    assert not torch.equal(out[0], out[1])
+
+
+def _bits(k, v):
+    kl = k_to_logical(k.cpu()).contiguous().view(torch.int16).numpy().copy()
+    vl = v_to_logical(v.cpu()).contiguous().view(torch.int16).numpy().copy()
+    return kl, vl
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_fork_workload_shared_sixteen_steps(fused):
+    """32 prompts of 2,055 tokens forked into 8 samples; 16 steps of copy-on-write, append and decode with the
+    128 shared prefix blocks of each prompt read once per step for its 8 samples."""
+    import paged_kv_cache_124_amd as pa
+    w = synth.fork()
+    P, S, steps = synth.FORK_PROMPTS, synth.FORK_SAMPLES, synth.FORK_STEPS
+    n = P * S
+    bs, hkv, hq, d = w.block_size, w.hkv, w.hq, w.d
+    prompt = w.fixed_lens[0]
+    final = prompt + steps
+    new_blocks = P * (S - 1) + n * (-(-final // bs) - (-(-prompt // bs)))
+    nb = synth.pool_blocks(w, list(w.fixed_lens), extra=new_blocks)
+    mb = -(-final // bs)
+    print(f"[case] fork shared: {n} seqs, pool {nb} blocks, {steps} steps, fused={fused}", flush=True)
+    order = synth.pop_order(nb, w.seed)
+    bm = pa.BlockManager(nb, bs, order)
+    model = BlockManagerModel(nb, bs, [int(x) for x in order])
+    for x in (bm, model):
+        for p in range(P):
+            assert x.add_seq(p * S, prompt) == 0
+            for s_ in range(1, S):
+                assert x.fork(p * S, p * S + s_) == 0
+    seqs = list(range(n))
+    st, tables, lens = bm.build_batch(seqs, mb)
+    assert st == 0
+    st, groups = bm.shared_groups(seqs, S)
+    assert st == 0 and groups.tolist() == [[p * S, S, (prompt // bs) * bs] for p in range(P)]
+    d_groups = torch.from_numpy(groups).cuda()
+    kshape, vshape = pa.pool_shapes(nb, hkv, d, bs, 2)
+    k = synth.fill_randn_(torch.empty(kshape, dtype=torch.bfloat16, device="cuda"), w.value_scale, w.seed * 10 + 1)
+    v = synth.fill_randn_(torch.empty(vshape, dtype=torch.bfloat16, device="cuda"), w.value_scale, w.seed * 10 + 2)
+    poison_unused_(k, v, tables, lens, bs)
+    ek, ev = _bits(k, v)
+    d_tables = torch.from_numpy(tables).cuda()
+    d_lens = torch.from_numpy(lens).cuda()
+    out = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+    case = DecodeCase(w, list(lens), hq, hkv, d, bs, torch.bfloat16, nb, mb, bm, model, tables, k, v, None,
+                      d_tables, d_lens, 1.0 / math.sqrt(d))
+    rng = np.random.default_rng(4)
+    sample = sorted(set(range(S)) | set(int(x) for x in rng.choice(n, 24, replace=False)))
+    for step in range(steps):
+        st, slots, pairs, _ = bm.append_slots(seqs)
+        mst, mslots, mpairs, _ = model.append_slots(seqs)
+        assert st == mst == 0 and list(slots) == mslots and [tuple(p) for p in pairs] == mpairs
+        if len(pairs):
+            pa.pa_copy_blocks(k, v, torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda())
+        kn = synth.randn((n, hkv, d), torch.bfloat16, w.value_scale, 5000 + step, "cuda")
+        vn = synth.randn((n, hkv, d), torch.bfloat16, w.value_scale, 6000 + step, "cuda")
+        q = synth.randn((n, hq, d), torch.bfloat16, w.value_scale, 7000 + step, "cuda")
+        d_slots = torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda()
+        if fused:
+            pa.pa_decode_step_shared(out, q, kn, vn, k, v, d_slots, d_tables, d_lens, d_groups, case.scale, final)
+        else:
+            pa.pa_append_step(k, v, kn, vn, d_slots, d_tables, d_lens)
+            pa.pa_decode_shared(out, q, k, v, d_tables, d_lens, d_groups, case.scale, final)
+        torch.cuda.synchronize()
+        OA.copy_blocks(ek, ev, mpairs)
+        OA.append_kv(ek, ev, kn.cpu().view(torch.int16).numpy(), vn.cpu().view(torch.int16).numpy(), mslots)
+        st, tables, lens = bm.build_batch(seqs, mb)
+        mst, mtables, mlens = model.build_batch(seqs, mb)
+        assert st == mst == 0 and tables.tolist() == mtables and lens.tolist() == mlens
+        assert np.array_equal(d_tables.cpu().numpy(), tables) and np.array_equal(d_lens.cpu().numpy(), lens)
+        # the groups found before the steps still hold: the prefix blocks are never written
+        assert bm.shared_groups(seqs, S)[1].tolist() == groups.tolist()
+        if step in (0, 9, steps - 1):
+            ref = oracle_outputs(case, sample, q=q, lens=lens, tables=mtables)
+            assert_close(out[sample], ref, f"fork shared step {step}")
+    gk, gv = _bits(k, v)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev), "pool differs from the oracle's copy + append"
