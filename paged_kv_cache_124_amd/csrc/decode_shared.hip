@@ -4,30 +4,31 @@
 // Why it is exact ("PagedAttention: Virtual Memory for the KV Cache", section
 // 15; "PagedAttention in vLLM: scattered memory, exact attention", section
 // 11): a full block referenced by several sequences is immutable, so every
-// sharer sees the same keys and values in it.  Sequence n's attention over
-// its S_n tokens is the common-maximum merge of the (m, z, u) summary over
-// its first P tokens and the summary over tokens P .. S_n - 1.  When rows
-// first .. first + count - 1 of the batch hold the same physical blocks for
-// their first P / B table entries, the first summary of every member comes
-// from one pass over those blocks with all members' queries at once.
+// sharer sees the same keys and values in it.  The online softmax of a row
+// may take its tokens in any grouping, so when rows first .. first + count - 1
+// of the batch hold the same physical blocks for their first P / B table
+// entries, one pass over those blocks can serve all of them at once, with
+// every member's queries as columns of the same matrix-core products, and
+// each member's remaining tokens can follow in the same pass with only that
+// member's columns taking part.
 //
 // Work decomposition (the persistent equal split of decode_stream.hip over
 // "units" instead of sequences):
-//   unit n < N       sequence n's own tokens [base_n, S_n + new), where
-//                    base_n = P of its group (0 when it has none);
-//   unit N + i       group i's shared tokens [0, P_i), read through the table
-//                    row of its first member, with count_i * G query columns
-//                    (member m, head h -> column m G + h; at most 32).
+//   unit n < N       sequence n without a group: its tokens, 32 per tile;
+//                    a sequence in a group has no tiles of its own;
+//   unit N + i       group i: ceil(P_i / 32) prefix tiles read through the
+//                    table row of its first member with count_i * G query
+//                    columns (member m, head h -> column m G + h; at most 32),
+//                    then each member's own tokens P_i .. S + new, 32 per tile
+//                    through the member's row, the other members' columns
+//                    masked out (their scores -inf: no weight, no change).
 // Tiles of all (unit, KV head) segments form one list; wave w takes tiles
 // [w T / W, (w + 1) T / W).  A group tile is one 16 KiB read of keys and
 // values used by two 16-column blocks of matrix-core products instead of one.
-//
-// Output: a sequence without a group whose segment a wave finishes whole is
-// written directly.  Every other finished piece leaves an (m, z, u) record:
-// a whole segment in its own slot (rows [KV head][2 N G]), a piece cut by
-// range boundaries in the wave's two slots (32 rows each).  `merge_shared`
-// combines, per (sequence, KV head), the pieces of its group unit (its
-// columns) and of its own unit, in that order.
+// A segment a wave finishes whole is written directly (a group's for all its
+// rows); a segment cut by range boundaries leaves an (m, z, u) record per
+// piece and column (32 rows per wave slot), which `merge_shared` combines
+// per (sequence, KV head) in wave order.
 //
 // Groups that are not usable are ignored, which keeps the result exact: a
 // group is used only when all its rows lie in the batch, no other group
@@ -51,37 +52,117 @@ constexpr int kShMaxGroups = 512;
 constexpr int kShCols = 32;  // query columns of one tile: two 16-column blocks
 
 // LDS of the kernel besides the stages: lengths and prefix sums of the units,
-// per-sequence base (shared tokens skipped) and group, per-group first row,
-// rows and shared tokens.
-size_t shared_lds(int n, int g) { return (4 * static_cast<size_t>(n) + 5 * static_cast<size_t>(g) + 1) * 4; }
+// the group of each sequence, and per group its first row, rows, shared
+// tokens and tiles.
+size_t shared_lds(int n, int g) { return (3 * static_cast<size_t>(n) + 6 * static_cast<size_t>(g) + 1) * 4; }
 
-// Where a unit's tiles read and whom they serve; wave-uniform, from LDS.
-struct UnitView {
-  const int32_t* s_len;
-  const int32_t* s_base;
-  const int32_t* s_gfirst;
+// Position in the tile list: unit n, KV head j, tile ti of the segment; for a
+// group unit's member tiles also the member m and its tile k (m = -1 for
+// every other tile).
+struct UTile {
+  int n, j, ti, m, k;
+};
+
+// Wave-uniform views of the unit tables in LDS.
+struct Units {
+  const int32_t* s_len;    // [units] packed tokens: group units P << 2; sequences as in decode_stream,
+                           // counted from P for a sequence in a group
+  const int32_t* s_pre;    // [units + 1]
+  const int32_t* s_gid;    // [N]
+  const int32_t* s_gfirst; // [groups]
   const int32_t* s_gcount;
-  int n_seqs, g;
+  const int32_t* s_gtok;
+  int n_seqs, g, hkv;
   __device__ bool is_group(int u) const { return u >= n_seqs; }
-  __device__ int table_row(int u) const { return u < n_seqs ? u : s_gfirst[u - n_seqs]; }
-  __device__ int base(int u) const { return u < n_seqs ? s_base[u] : 0; }
-  __device__ int cols(int u) const { return u < n_seqs ? g : s_gcount[u - n_seqs] * g; }
-  // record rows of the unit in the whole-segment area: sequence n -> n G,
-  // group i -> (N + first_i) G (groups are disjoint row ranges)
-  __device__ int64_t row_base(int u) const {
-    return static_cast<int64_t>(u < n_seqs ? u : n_seqs + s_gfirst[u - n_seqs]) * g;
+  __device__ int tiles(int u) const { return s_pre[u + 1] - s_pre[u]; }
+  __device__ int prefix_tiles(int u) const { return (s_gtok[u - n_seqs] + 31) >> 5; }
+  // tiles of member m's own tokens in group unit u
+  __device__ int member_tiles(int u, int m) const {
+    return (attended_tokens(s_len[s_gfirst[u - n_seqs] + m]) + 31) >> 5;
+  }
+  // the first member at or after m with tiles of its own (the last member at most)
+  __device__ int next_member(int u, int m) const {
+    const int last = s_gcount[u - n_seqs] - 1;
+    while (m < last && member_tiles(u, m) == 0) ++m;
+    return m;
+  }
+  // the sequence whose table row, tokens and new token a tile uses
+  __device__ int seq_of(const UTile& t) const {
+    if (!is_group(t.n)) return t.n;
+    return s_gfirst[t.n - n_seqs] + (t.m >= 0 ? t.m : 0);
+  }
+  // tokens before the tile's token 0 (a multiple of B) and its packed tokens
+  __device__ int base(const UTile& t) const { return t.m >= 0 ? s_gtok[t.n - n_seqs] : 0; }
+  __device__ int packed(const UTile& t) const { return t.m >= 0 ? s_len[seq_of(t)] : s_len[t.n]; }
+  __device__ int t0(const UTile& t) const { return 32 * (t.m >= 0 ? t.k : t.ti); }
+  __device__ int cols(int u) const { return is_group(u) ? s_gcount[u - n_seqs] * g : g; }
+  // the tile that ends the attended tokens of its sequence (where the new token is)
+  __device__ bool ends_seq(const UTile& t) const {
+    return t.m >= 0 ? t.k == member_tiles(t.n, t.m) - 1 : (!is_group(t.n) && t.ti == tiles(t.n) - 1);
+  }
+  __device__ UTile locate(int u, int64_t rem) const {
+    UTile t;
+    t.n = u;
+    const int nt = tiles(u);
+    t.j = static_cast<int>(rem / nt);
+    t.ti = static_cast<int>(rem - static_cast<int64_t>(t.j) * nt);
+    t.m = -1;
+    t.k = 0;
+    if (is_group(u) && t.ti >= prefix_tiles(u)) {
+      int r = t.ti - prefix_tiles(u);
+      int m = next_member(u, 0);
+      while (r >= member_tiles(u, m) && m < s_gcount[u - n_seqs] - 1) {
+        r -= member_tiles(u, m);
+        m = next_member(u, m + 1);
+      }
+      t.m = m;
+      t.k = r;
+    }
+    return t;
+  }
+  // next tile in (unit, KV head, tile) order; only called when one exists
+  __device__ UTile advance(UTile t) const {
+    if (t.ti + 1 < tiles(t.n)) {
+      ++t.ti;
+      if (is_group(t.n)) {
+        if (t.m < 0) {
+          if (t.ti == prefix_tiles(t.n)) {
+            t.m = next_member(t.n, 0);
+            t.k = 0;
+          }
+        } else if (t.k + 1 < member_tiles(t.n, t.m)) {
+          ++t.k;
+        } else {
+          t.m = next_member(t.n, t.m + 1);
+          t.k = 0;
+        }
+      }
+      return t;
+    }
+    t.ti = 0;
+    t.m = -1;
+    t.k = 0;
+    if (t.j + 1 < hkv) {
+      ++t.j;
+      return t;
+    }
+    t.j = 0;
+    do {
+      ++t.n;
+    } while (tiles(t.n) == 0);
+    return t;
   }
 };
 
-// Table entries of a unit's tile: tokens base + 32 ti .. + 31 of the unit's
-// table row, -1 past the unit's tokens (base is a multiple of B).
+// Table entries of a tile: tokens base + t0 .. + 31 of its sequence's row (a
+// group's prefix: its first member's), -1 past the tokens in the pool.
 template <int B>
-__device__ __forceinline__ Tb<32 / B> load_tb_unit(TilePos t, const UnitView& uv,
+__device__ __forceinline__ Tb<32 / B> load_tb_unit(const UTile& t, const Units& us,
                                                    const int32_t* __restrict__ block_tables, int max_blocks) {
-  const int32_t* row = block_tables + static_cast<int64_t>(uv.table_row(t.n)) * max_blocks;
-  const int S = pool_tokens(uv.s_len[t.n]);
-  const int t0 = t.ti * 32;
-  const int b0 = (uv.base(t.n) + t0) / B;
+  const int32_t* row = block_tables + static_cast<int64_t>(us.seq_of(t)) * max_blocks;
+  const int S = pool_tokens(us.packed(t));
+  const int t0 = us.t0(t);
+  const int b0 = (us.base(t) + t0) / B;
   Tb<32 / B> tb;
 #pragma unroll
   for (int i = 0; i < 32 / B; ++i) {
@@ -91,87 +172,71 @@ __device__ __forceinline__ Tb<32 / B> load_tb_unit(TilePos t, const UnitView& uv
   return tb;
 }
 
-// Q^T operands of both column blocks for a unit's tile.  Column c = 16 cb + r
-// is head c of the sequence (c < G), or member c / G, head c % G of the group;
-// padding columns read a valid row whose results are never used.
+// Rows of q the lane's two columns read for a segment: column c = 16 cb + r
+// is head c of a sequence unit (c < G), or member c / G, head c % G of a
+// group; padding columns read a valid row whose results are never used.
+// Reads LDS only (see the step: no LDS read may follow the next tile's copies).
+struct QRows {
+  const uint16_t* p[2];
+};
+
 template <int D>
-__device__ __forceinline__ void load_q_unit(QOp<D> (&qo)[2], TilePos t, const UnitView& uv,
-                                            const uint16_t* __restrict__ q, int hq, const int (&col_m)[2],
-                                            const int (&col_h)[2], int r, int gq) {
+__device__ __forceinline__ QRows q_rows(const UTile& t, const Units& us, const uint16_t* __restrict__ q, int hq,
+                                        const int (&col_m)[2], const int (&col_h)[2], int r, int gq) {
+  QRows qr;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     int seq, h;
-    if (!uv.is_group(t.n)) {
+    if (!us.is_group(t.n)) {
       const int c = 16 * cb + r;
       seq = t.n;
-      h = c < uv.g ? c : 0;
+      h = c < us.g ? c : 0;
     } else {
-      const int i = t.n - uv.n_seqs;
-      const bool ok = col_m[cb] < uv.s_gcount[i];
-      seq = uv.s_gfirst[i] + (ok ? col_m[cb] : 0);
+      const int i = t.n - us.n_seqs;
+      const bool ok = col_m[cb] < us.s_gcount[i];
+      seq = us.s_gfirst[i] + (ok ? col_m[cb] : 0);
       h = ok ? col_h[cb] : 0;
     }
-    const uint16_t* qh = q + (static_cast<int64_t>(seq) * hq + t.j * uv.g + h) * D;
-#pragma unroll
-    for (int jj = 0; jj < D / 32; ++jj)
-      qo[cb].q[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qh + (4 * jj + gq) * 8));
+    qr.p[cb] = q + (static_cast<int64_t>(seq) * hq + t.j * us.g + h) * D + gq * 8;
   }
+  return qr;
 }
 
-// End of a piece of unit segment t: direct output, a whole-segment record or a
-// wave-slot record (see the top of the file).
+// Q^T operands of both column blocks (global loads only).
 template <int D>
-__device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], TilePos t, const UnitView& uv, bool whole, int slot,
-                                           int64_t wave_id, uint16_t* out, float* rec, float* rec_whole, int hq,
-                                           int hkv, int r, int gq) {
-  const int cols = uv.cols(t.n);
-  const bool direct = whole && !uv.is_group(t.n) && uv.s_base[t.n] == 0;
-  const int64_t total_rows = 2 * static_cast<int64_t>(uv.n_seqs) * uv.g;
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    if (cb == 1 && cols <= 16) break;
-    float zt = st[cb].z + __shfl_xor(st[cb].z, 16);
-    zt += __shfl_xor(zt, 32);
-    const int c = 16 * cb + r;
-    if (c < cols) {
-      if (direct) {
-        const float inv = 1.f / zt;
-        uint16_t* o = out + (static_cast<int64_t>(t.n) * hq + t.j * uv.g + c) * D + 4 * gq;
-#pragma unroll
-        for (int mm = 0; mm < D / 16; ++mm) {
-          const uint32_t lo =
-              f32_to_bf16_bits(st[cb].o[mm][0] * inv) | (uint32_t(f32_to_bf16_bits(st[cb].o[mm][1] * inv)) << 16);
-          const uint32_t hi =
-              f32_to_bf16_bits(st[cb].o[mm][2] * inv) | (uint32_t(f32_to_bf16_bits(st[cb].o[mm][3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(o + 16 * mm) = make_uint2(lo, hi);
-        }
-      } else {
-        float* rr = whole ? rec_whole + (static_cast<int64_t>(t.j) * total_rows + uv.row_base(t.n) + c) * (D + 4)
-                          : rec + (static_cast<int64_t>(wave_id * 2 + slot) * kShCols + c) * (D + 4);
-#pragma unroll
-        for (int mm = 0; mm < D / 16; ++mm) *reinterpret_cast<f32x4*>(rr + 4 + 16 * mm + 4 * gq) = st[cb].o[mm];
-        if (gq == 0) {
-          rr[0] = st[cb].m;
-          rr[1] = zt;
-        }
-      }
-    }
-  }
-  reset(st[0]);
-  reset(st[1]);
-}
-
-// A group tile with more than 16 query columns: both column blocks in one
-// pass.  The two score products, the two online-softmax updates and the two
-// P.V products are independent, so their latencies overlap (one wave per SIMD
-// has no other wave to hide them behind).  Same arithmetic as qk_tile +
-// pv_tile per column block.
-template <int D>
-__device__ __forceinline__ void tile2(Acc<D> (&st)[2], const Buf<D>& b, const QOp<D> (&qo)[2], int t0, int S,
-                                      bool full, float scale_log2, int gq) {
-  f32x4 s[2][2];  // [column block][slab]
+__device__ __forceinline__ void load_q_rows(QOp<D> (&qo)[2], const QRows& qr) {
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int jj = 0; jj < D / 32; ++jj)
+      qo[cb].q[jj] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qr.p[cb] + 32 * jj));
+}
+
+// One element of a per-column-block array, as an array of one (for
+// tile_group<D, 1>); indices stay compile-time, so nothing moves to scratch.
+template <typename T>
+__device__ __forceinline__ T (&one(T& x))[1] {
+  return *reinterpret_cast<T(*)[1]>(&x);
+}
+template <typename T>
+__device__ __forceinline__ const T (&one(const T& x))[1] {
+  return *reinterpret_cast<const T(*)[1]>(&x);
+}
+
+// A group tile on NC column blocks, all in one pass: the score products, the
+// online-softmax updates and the P.V products of the blocks are independent,
+// so their latencies overlap (one wave per SIMD has no other wave to hide
+// them behind).  Column c takes part when live[cb] (its lane's column); a
+// column that does not gets score -inf for every token: no weight, and its
+// running state is unchanged.  Same arithmetic as qk_tile + pv_tile per column
+// block otherwise; a column whose running maximum is still -inf is kept at
+// zero instead of 0 * inf.
+template <int D, int NC>
+__device__ __forceinline__ void tile_group(Acc<D> (&st)[NC], const Buf<D>& b, const QOp<D> (&qo)[NC], int t0, int S,
+                                           bool full, const bool (&live)[NC], float scale_log2, int gq) {
+  f32x4 s[NC][2];  // [column block][slab]
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
     for (int a = 0; a < 2; ++a) s[cb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -179,51 +244,56 @@ __device__ __forceinline__ void tile2(Acc<D> (&st)[2], const Buf<D>& b, const QO
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NC; ++cb)
         s[cb][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.k[a][jj], qo[cb].q[jj], s[cb][a], 0, 0, 0);
   int n0 = 4, n1 = 4;
   if (!full) {
     n0 = b.blk0 ? min(max(S - (t0 + 4 * gq), 0), 4) : 0;
     n1 = b.blk1 ? min(max(S - (t0 + 16 + 4 * gq), 0), 4) : 0;
   }
-  float x[2][2][4];
-  float tmax[2] = {-INFINITY, -INFINITY};
+  float x[NC][2][4];
+  float tmax[NC];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < NC; ++cb) {
+    tmax[cb] = -INFINITY;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[cb][a][i] = i < (a ? n1 : n0) ? s[cb][a][i] * scale_log2 : -INFINITY;
+        x[cb][a][i] = live[cb] && i < (a ? n1 : n0) ? s[cb][a][i] * scale_log2 : -INFINITY;
         tmax[cb] = fmaxf(tmax[cb], x[cb][a][i]);
       }
+  }
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 16));
+  for (int cb = 0; cb < NC; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 16));
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 32));
-  float alpha[2];
-  bf16x8 phi[2], plo[2];
+  for (int cb = 0; cb < NC; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 32));
+  float alpha[NC];
+  bf16x8 phi[NC], plo[NC];
+  bool moved = false;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NC; ++cb) {
     const float m_new = fmaxf(st[cb].m, tmax[cb]);
-    alpha[cb] = __builtin_amdgcn_exp2f(st[cb].m - m_new);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // no token yet: exponents of -inf give 0
+    alpha[cb] = __builtin_amdgcn_exp2f(st[cb].m - m_ref);
     st[cb].m = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(x[cb][a][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(x[cb][a][i] - m_ref);
         psum += p;
         const __bf16 h = static_cast<__bf16>(p);
         phi[cb][4 * a + i] = h;
         plo[cb][4 * a + i] = static_cast<__bf16>(p - static_cast<float>(h));
       }
     st[cb].z = st[cb].z * alpha[cb] + psum;
+    moved = moved || alpha[cb] != 1.f;
   }
-  if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+  if (__any(moved)) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
       for (int mm = 0; mm < D / 16; ++mm) st[cb].o[mm] *= alpha[cb];
   }
@@ -239,10 +309,56 @@ __device__ __forceinline__ void tile2(Acc<D> (&st)[2], const Buf<D>& b, const QO
     const uint4 w = make_uint4(b.v0[mm].x & m0a, b.v0[mm].y & m0b, b.v1[mm].x & m1a, b.v1[mm].y & m1b);
     const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) st[cb].o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[cb], st[cb].o[mm], 0, 0, 0);
+    for (int cb = 0; cb < NC; ++cb)
+      st[cb].o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[cb], st[cb].o[mm], 0, 0, 0);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) st[cb].o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[cb], st[cb].o[mm], 0, 0, 0);
+    for (int cb = 0; cb < NC; ++cb)
+      st[cb].o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[cb], st[cb].o[mm], 0, 0, 0);
   }
+}
+
+// End of a piece of segment t: the normalised outputs (whole segment) or a
+// wave-slot record per column.
+// `cols` and `first` (the group's first row, or the sequence) are the
+// segment's, read from LDS before the next tile's copies were issued.
+template <int D>
+__device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], const UTile& t, const Units& us, int cols, int first,
+                                           bool whole, int slot, int64_t wave_id, uint16_t* out, float* rec, int hq,
+                                           int r, int gq, const int (&col_m)[2], const int (&col_h)[2]) {
+  const bool grp = us.is_group(t.n);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    if (cb == 1 && cols <= 16) break;
+    float zt = st[cb].z + __shfl_xor(st[cb].z, 16);
+    zt += __shfl_xor(zt, 32);
+    const int c = 16 * cb + r;
+    if (c < cols) {
+      if (whole) {
+        const float inv = 1.f / zt;
+        const int seq = grp ? first + col_m[cb] : t.n;
+        const int h = grp ? col_h[cb] : c;
+        uint16_t* o = out + (static_cast<int64_t>(seq) * hq + t.j * us.g + h) * D + 4 * gq;
+#pragma unroll
+        for (int mm = 0; mm < D / 16; ++mm) {
+          const uint32_t lo =
+              f32_to_bf16_bits(st[cb].o[mm][0] * inv) | (uint32_t(f32_to_bf16_bits(st[cb].o[mm][1] * inv)) << 16);
+          const uint32_t hi =
+              f32_to_bf16_bits(st[cb].o[mm][2] * inv) | (uint32_t(f32_to_bf16_bits(st[cb].o[mm][3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(o + 16 * mm) = make_uint2(lo, hi);
+        }
+      } else {
+        float* rr = rec + (static_cast<int64_t>(wave_id * 2 + slot) * kShCols + c) * (D + 4);
+#pragma unroll
+        for (int mm = 0; mm < D / 16; ++mm) *reinterpret_cast<f32x4*>(rr + 4 + 16 * mm + 4 * gq) = st[cb].o[mm];
+        if (gq == 0) {
+          rr[0] = st[cb].m;
+          rr[1] = zt;
+        }
+      }
+    }
+  }
+  reset(st[0]);
+  reset(st[1]);
 }
 
 template <int D, int B>
@@ -250,19 +366,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const uint16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ groups, int n_groups, uint16_t* __restrict__ out, float* __restrict__ rec,
-    float* __restrict__ rec_whole, int32_t* __restrict__ seq_info_out,
-    int n_seqs, int hq, int hkv, int g, int max_blocks, int num_blocks, float scale_log2,
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, const int32_t* __restrict__ slots,
-    int32_t* __restrict__ slots_out) {
+    int32_t* __restrict__ seq_info_out, int n_seqs, int hq, int hkv, int g, int max_blocks, int num_blocks,
+    float scale_log2, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out) {
   const int n_units = n_seqs + n_groups;
   extern __shared__ int32_t sm[];
-  int32_t* s_len = sm;                   // [units] packed attended tokens of the unit
+  int32_t* s_len = sm;                   // [units]
   int32_t* s_pre = s_len + n_units;      // [units + 1] tile prefix sums
-  int32_t* s_base = s_pre + n_units + 1; // [N] claiming group, then shared tokens skipped
-  int32_t* s_gid = s_base + n_seqs;      // [N] group of the row, -1 for none
+  int32_t* s_gid = s_pre + n_units + 1;  // [N] claiming group, then the row's group or -1
   int32_t* s_gfirst = s_gid + n_seqs;    // [groups]
   int32_t* s_gcount = s_gfirst + n_groups;
   int32_t* s_gtok = s_gcount + n_groups;
+  int32_t* s_gtiles = s_gtok + n_groups;
   __shared__ int32_t s_wsum[kSW];
 
   const int tid = threadIdx.x;
@@ -272,9 +387,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   const int gq = lane >> 4;
   const int s_cap = max_blocks * B;
   const int max_members = kShCols / g;
+  const int hn = k_new != nullptr ? 1 : 0;  // the step: every row attends to its new token
 
   // ---- groups: sanitize, claim rows, validate --------------------------------
-  for (int i = tid; i < n_seqs; i += 256) s_base[i] = -1;
+  for (int i = tid; i < n_seqs; i += 256) s_gid[i] = -1;
   for (int i = tid; i < n_groups; i += 256) {
     const int first = groups[3 * i], cnt = groups[3 * i + 1], tok = groups[3 * i + 2];
     const bool ok = first >= 0 && first < n_seqs && cnt >= 1 && tok >= B;
@@ -284,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   }
   __syncthreads();
   for (int i = tid; i < n_groups; i += 256)
-    for (int m = 0; m < s_gcount[i]; ++m) atomicCAS(&s_base[s_gfirst[i] + m], -1, i);
+    for (int m = 0; m < s_gcount[i]; ++m) atomicCAS(&s_gid[s_gfirst[i] + m], -1, i);
   __syncthreads();
   for (int i = tid; i < n_groups; i += 256) {
     const int cnt = s_gcount[i];
@@ -292,21 +408,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     int P = s_gtok[i];
     for (int m = 0; m < cnt; ++m) {
       const int n = s_gfirst[i] + m;
-      ok = ok && s_base[n] == i;
+      ok = ok && s_gid[n] == i;
       P = min(P, min(max(context_lens[n], 0), s_cap));  // no member attends past its own tokens
     }
     P -= P % B;
     if (!ok || P < B) P = 0;
+    int tiles = (P + 31) >> 5;
+    for (int m = 0; m < (P > 0 ? cnt : 0); ++m) {  // each member's own tokens P .. S + new
+      const int S = min(max(context_lens[s_gfirst[i] + m], 0), s_cap);
+      tiles += (S + hn - P + 31) >> 5;
+    }
     s_gtok[i] = P;
+    s_gtiles[i] = P > 0 ? tiles : 0;
   }
   __syncthreads();
   for (int i = tid; i < n_groups; i += 256)
     if (s_gtok[i] == 0) s_gcount[i] = 0;
-  for (int n = tid; n < n_seqs; n += 256) {  // each thread reads and rewrites its own rows only
-    const int i = s_base[n];
-    const bool in = i >= 0 && s_gtok[i] > 0;
-    s_base[n] = in ? s_gtok[i] : 0;
-    s_gid[n] = in ? i : -1;
+  for (int n = tid; n < n_seqs; n += 256) {  // each thread rewrites its own rows only
+    const int i = s_gid[n];
+    s_gid[n] = i >= 0 && s_gtok[i] > 0 ? i : -1;
   }
   __syncthreads();
 
@@ -318,15 +438,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     if (u < n_seqs) {
       const int S_raw = context_lens[u];
       const int S = min(max(S_raw, 0), s_cap);
-      const int hn = k_new != nullptr ? 1 : 0;  // the step: every row attends to its new token
       const int fits = S_raw >= 0 && S_raw < s_cap ? 1 : 0;
-      const int rel = S + hn - s_base[u];
-      v = (rel + 31) >> 5;
+      const int i = s_gid[u];
+      const int rel = S + hn - (i >= 0 ? s_gtok[i] : 0);
+      v = i >= 0 ? 0 : (rel + 31) >> 5;  // a group member's tiles belong to its group
       packed = (rel << 2) | (fits << 1) | hn;
     } else if (u < n_units) {
-      const int P = s_gcount[u - n_seqs] > 0 ? s_gtok[u - n_seqs] : 0;
-      v = (P + 31) >> 5;
-      packed = P << 2;
+      v = s_gtiles[u - n_seqs];
+      packed = s_gtok[u - n_seqs] << 2;
     }
 #pragma unroll
     for (int dlt = 1; dlt < 64; dlt <<= 1) {
@@ -344,22 +463,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   }
   if (tid == 0) s_pre[0] = 0;
   __syncthreads();
-  // what the merge kernel needs of row n, 8 words: its group and member (or
-  // -1), the group unit's first tile and tile count, all units' tiles, the
-  // row's own first tile and tile count
+  // for the merge kernel, 4 words per row: the first tile and tile count of the
+  // unit holding its tokens, the row's first record row there, all units' tiles
   if (blockIdx.x == 0)
     for (int n = tid; n < n_seqs; n += 256) {
       const int i = s_gid[n];
-      const int gu = n_seqs + (i >= 0 ? i : 0);
-      const int4 a = make_int4(i >= 0 ? i * kShCols + (n - s_gfirst[i]) : -1, s_pre[gu], s_pre[gu + 1] - s_pre[gu],
-                               s_pre[n_units]);
-      const int4 b = make_int4(s_pre[n], s_pre[n + 1] - s_pre[n], 0, 0);
-      *reinterpret_cast<int4*>(seq_info_out + 8 * static_cast<int64_t>(n)) = a;
-      *reinterpret_cast<int4*>(seq_info_out + 8 * static_cast<int64_t>(n) + 4) = b;
+      const int u = i >= 0 ? n_seqs + i : n;
+      *reinterpret_cast<int4*>(seq_info_out + 4 * static_cast<int64_t>(n)) =
+          make_int4(s_pre[u], s_pre[u + 1] - s_pre[u], i >= 0 ? (n - s_gfirst[i]) * g : 0, s_pre[n_units]);
     }
   // no barrier below this point: waves run independently
 
-  const UnitView uv{s_len, s_base, s_gfirst, s_gcount, n_seqs, g};
+  const Units us{s_len, s_pre, s_gid, s_gfirst, s_gcount, s_gtok, n_seqs, g, hkv};
   Split sp;
   sp.init(static_cast<int64_t>(hkv) * s_pre[n_units], static_cast<int64_t>(gridDim.x) * kSW);
   // XCD-major numbering, as in decode_stream
@@ -374,14 +489,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int mid = (lo + hi + 1) >> 1;
     if (static_cast<int64_t>(hkv) * s_pre[mid] <= x0) lo = mid; else hi = mid - 1;
   }
-  TilePos cur;
-  cur.n = lo;
-  {
-    const int64_t rem = x0 - static_cast<int64_t>(hkv) * s_pre[lo];
-    const int nt = tiles_of(s_pre, lo);
-    cur.j = static_cast<int>(rem / nt);
-    cur.ti = static_cast<int>(rem - static_cast<int64_t>(cur.j) * nt);
-  }
+  UTile cur = us.locate(lo, x0 - static_cast<int64_t>(hkv) * s_pre[lo]);
   int piece_start = cur.ti;
   bool first_piece = true;
 
@@ -395,30 +503,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   Acc<D> st[2];
   reset(st[0]);
   reset(st[1]);
-  QOp<D> qA[2], qB[2];
-  TilePos nxt = x1 - x0 > 1 ? advance(cur, s_pre, hkv) : cur;
-  Tb<32 / B> tbA = load_tb_unit<B>(cur, uv, block_tables, max_blocks);
-  Tb<32 / B> tbB = load_tb_unit<B>(nxt, uv, block_tables, max_blocks);
-  load_q_unit<D>(qA, cur, uv, q, hq, col_m, col_h, r, gq);
+  // The queries of a segment are the same for all its tiles: one set of Q
+  // operands, loaded when a segment starts (registers are short here: two
+  // column blocks of accumulators, scores and operands).
+  QOp<D> qc[2];
+  UTile nxt = x1 - x0 > 1 ? us.advance(cur) : cur;
+  Tb<32 / B> tbA = load_tb_unit<B>(cur, us, block_tables, max_blocks);
+  Tb<32 / B> tbB = load_tb_unit<B>(nxt, us, block_tables, max_blocks);
+  load_q_rows<D>(qc, q_rows<D>(cur, us, q, hq, col_m, col_h, r, gq));
   dma_tile<D, B, false>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
 
   int64_t x = x0;
-  auto wants_new = [&](TilePos t) -> bool {
-    return k_new != nullptr && !uv.is_group(t.n) && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
+  auto wants_new = [&](const UTile& t) -> bool {
+    return k_new != nullptr && has_new_token(us.packed(t)) && us.ends_seq(t);
+  };
+  auto new_of = [&](NewTok<D>& nt, const UTile& t) {
+    TilePos p;
+    p.n = us.seq_of(t);
+    p.j = t.j;
+    p.ti = 0;
+    load_new<D>(nt, p, k_new, v_new, slots, hkv, r, gq);
   };
   NewTok<D> ntok;
-  if (wants_new(cur)) load_new<D>(ntok, cur, k_new, v_new, slots, hkv, r, gq);
-  auto step = [&](auto sc_tag, QOp<D>(&qc)[2], const Tb<32 / B>& tbc, QOp<D>(&qn)[2], const Tb<32 / B>& tbn,
-                  Tb<32 / B>& tb2) -> bool {
+  if (wants_new(cur)) new_of(ntok, cur);
+  auto step = [&](auto sc_tag, const Tb<32 / B>& tbc, const Tb<32 / B>& tbn, Tb<32 / B>& tb2) -> bool {
     constexpr int SC = decltype(sc_tag)::value;
     unsigned char(&stc)[4][kStageBytes] = SC == 0 ? g_stage0 : g_stage1;
     unsigned char(&stn)[4][kStageBytes] = SC == 0 ? g_stage1 : g_stage0;
+    // Every LDS read of the step comes before the next tile's copies below:
+    // an LDS read issued after them would wait for all of them.
     const bool has_next = x + 1 < x1;
-    const int packed = s_len[cur.n];
+    const int packed = us.packed(cur);
     const int S = attended_tokens(packed);
-    const int nt_cur = tiles_of(s_pre, cur.n);
-    const TilePos nxt2 = x + 2 < x1 ? advance(nxt, s_pre, hkv) : nxt;
-    const int t0 = cur.ti * 32;
+    const int nt_cur = us.tiles(cur.n);
+    const UTile nxt2 = x + 2 < x1 ? us.advance(nxt) : nxt;
+    const int t0 = us.t0(cur);
+    const int cols = us.cols(cur.n);
+    const int first = us.is_group(cur.n) ? us.s_gfirst[cur.n - n_seqs] : cur.n;
+    const QRows q_next = q_rows<D>(nxt, us, q, hq, col_m, col_h, r, gq);
     Buf<D> b;
     read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
     // keep the stage's LDS reads ahead of the copies below
@@ -426,20 +548,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     if (wants_new(cur)) {
       patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
       if (cur.j == 0 && lane == 0) {  // the row's slot goes on to the merge kernel, which stores the token
-        const int S0 = uv.base(cur.n) + pool_tokens(packed);
+        const int S0 = us.base(cur) + pool_tokens(packed);
         const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
                              static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
                              ntok.slot % B == S0 % B;
-        slots_out[cur.n] = at_next ? ntok.slot : -1;
+        slots_out[us.seq_of(cur)] = at_next ? ntok.slot : -1;
       }
     }
-    tb2 = load_tb_unit<B>(nxt2, uv, block_tables, max_blocks);
-    load_q_unit<D>(qn, nxt, uv, q, hq, col_m, col_h, r, gq);
-    if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
+    tb2 = load_tb_unit<B>(nxt2, us, block_tables, max_blocks);
+    if (has_next && wants_new(nxt)) new_of(ntok, nxt);
     dma_tile<D, B, false>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
     const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
-    if (uv.cols(cur.n) > 16) {  // a group of more than 16 query columns
-      tile2<D>(st, b, qc, t0, S, full, scale_log2, gq);
+    if (us.is_group(cur.n)) {
+      bool live[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) live[cb] = cur.m < 0 || col_m[cb] == cur.m;  // a member's tile: its columns
+      // the column blocks the tile needs: all the group's, or those holding the member's columns
+      const int cb_lo = cur.m < 0 ? 0 : (cur.m * g) >> 4;
+      const int cb_hi = cur.m < 0 ? (cols > 16 ? 1 : 0) : (cur.m * g + g - 1) >> 4;
+      if (cb_lo != cb_hi)
+        tile_group<D, 2>(st, b, qc, t0, S, full, live, scale_log2, gq);
+      else if (cb_lo == 0)
+        tile_group<D, 1>(one(st[0]), b, one(qc[0]), t0, S, full, one(live[0]), scale_log2, gq);
+      else
+        tile_group<D, 1>(one(st[1]), b, one(qc[1]), t0, S, full, one(live[1]), scale_log2, gq);
     } else {
       f32x4 sco[2];
       qk_tile<D>(sco, b, qc[0]);
@@ -447,26 +579,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     }
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
-      flush_unit<D>(st, cur, uv, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, rec_whole, hq,
-                    hkv, r, gq);
+      flush_unit<D>(st, cur, us, cols, first, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec,
+                    hq, r, gq, col_m, col_h);
       first_piece = false;
       piece_start = 0;
     }
     if (!has_next) return false;
+    if (seg_end) load_q_rows<D>(qc, q_next);  // the next segment's queries
     ++x;
     cur = nxt;
     nxt = nxt2;
     return true;
   };
   while (true) {
-    if (!step(std::integral_constant<int, 0>{}, qA, tbA, qB, tbB, tbA)) break;
-    if (!step(std::integral_constant<int, 1>{}, qB, tbB, qA, tbA, tbB)) break;
+    if (!step(std::integral_constant<int, 0>{}, tbA, tbB, tbA)) break;
+    if (!step(std::integral_constant<int, 1>{}, tbB, tbA, tbB)) break;
   }
 }
 
-// Pieces of one (unit, KV head) segment: none (no tiles), one whole-segment
-// record, or the records of waves v_lo .. v_hi (a wave with an empty range
-// has none).  The unit's tiles start at `start` of the unit list and number nt.
+// Pieces of one (unit, KV head) segment: the records of waves v_lo .. v_hi
+// (a wave with an empty range has none), or one whole piece the decode wrote.
+// The unit's tiles start at `start` of the unit list and number nt.
 struct SegPieces {
   int64_t v_lo;
   int cnt;
@@ -481,75 +614,60 @@ __device__ __forceinline__ SegPieces seg_pieces(const Split& sp, int start, int 
   const int64_t v_hi = sp.wave_of(a + nt - 1);
   sg.whole = sg.v_lo == v_hi;
   sg.lo_second = a > sp.start(sg.v_lo);
-  sg.cnt = sg.whole ? 1 : static_cast<int>(v_hi - sg.v_lo + 1);
+  sg.cnt = static_cast<int>(v_hi - sg.v_lo + 1);
   return sg;
 }
 
-// Row 0 of piece k's record (rows are D + 4 floats apart), or nullptr.
+// Row 0 of the record of piece k (rows are D + 4 floats apart), or nullptr.
 template <int D>
-__device__ __forceinline__ const float* piece_record(const SegPieces& sg, int k, const Split& sp, const float* rec,
-                                                     const float* rec_whole_row0) {
+__device__ __forceinline__ const float* piece_record(const SegPieces& sg, int k, const Split& sp, const float* rec) {
   if (k < 0 || k >= sg.cnt) return nullptr;
-  if (sg.whole) return rec_whole_row0;
   const int64_t v = sg.v_lo + k;
   if (sp.start(v) == sp.start(v + 1)) return nullptr;
   const int slot = (v == sg.v_lo && sg.lo_second) ? 1 : 0;
   return rec + (v * 2 + slot) * kShCols * (D + 4);
 }
 
-// Second kernel: one workgroup per (KV head, sequence).  It merges the pieces
-// of the row's group unit (its columns) and then of its own unit, in that
-// order, with the common-maximum rule; a row without a group whose segment a
-// decode wave finished whole was written there.  The step's new token is
-// stored and the row moved forward as in merge_stream.
+// Second kernel: one workgroup per (KV head, sequence) combines the pieces of
+// the segment that holds the row's tokens (its group's, at the row's columns,
+// or its own) with the common-maximum rule, in wave order; a segment a decode
+// wave finished whole was written there.  The step's new token is stored and
+// the row moved forward as in merge_stream.
 template <int D>
-__global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ rec, const float* __restrict__ rec_whole,
-                                                    const int32_t* __restrict__ seq_info, uint16_t* __restrict__ out,
-                                                    int n_seqs, int hq, int hkv, int g, int64_t total_waves,
-                                                    AppendArgs ap) {
+__global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ rec, const int32_t* __restrict__ seq_info,
+                                                    uint16_t* __restrict__ out, int hq, int hkv, int g,
+                                                    int64_t total_waves, AppendArgs ap) {
   constexpr int E = D / 64;
   const int j = blockIdx.x;
   const int n = blockIdx.y;
   RowToken<D> rt{};
   if (ap.k_new != nullptr) rt = load_row_token<D>(ap, n, j, hkv);  // in flight during the merge
-  const int4 ia = *reinterpret_cast<const int4*>(seq_info + 8 * static_cast<int64_t>(n));
-  const int4 ib = *reinterpret_cast<const int4*>(seq_info + 8 * static_cast<int64_t>(n) + 4);
-  const int info = ia.x;
-  const int mi = info >= 0 ? info % kShCols : 0;
+  const int4 si = *reinterpret_cast<const int4*>(seq_info + 4 * static_cast<int64_t>(n));
   Split sp;
-  sp.init(static_cast<int64_t>(hkv) * ia.w, total_waves);
-  const SegPieces sa = info >= 0 ? seg_pieces(sp, ia.y, ia.z, hkv, j) : SegPieces{};
-  const SegPieces sb = seg_pieces(sp, ib.x, ib.y, hkv, j);
+  sp.init(static_cast<int64_t>(hkv) * si.w, total_waves);
+  const SegPieces sg = seg_pieces(sp, si.x, si.y, hkv, j);
+  const int row0 = si.z;
   uint16_t* o = out + (static_cast<int64_t>(n) * hq + j * g) * D;
-  const int cnt = sa.cnt + sb.cnt;
-  const bool done_by_decode = info < 0 && sb.whole;
-  const int64_t total_rows = 2 * static_cast<int64_t>(n_seqs) * g;
-  const float* wa = rec_whole + (static_cast<int64_t>(j) * total_rows + static_cast<int64_t>(n_seqs + n - mi) * g) * (D + 4);
-  const float* wb = rec_whole + (static_cast<int64_t>(j) * total_rows + static_cast<int64_t>(n) * g) * (D + 4);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  if (cnt == 0) {  // nothing to attend
+  if (sg.cnt == 0) {  // nothing to attend
     for (int e = threadIdx.x; e < g * D; e += blockDim.x) o[e] = 0;
-  } else if (!done_by_decode && cnt <= 8) {
+  } else if (!sg.whole && sg.cnt <= 8) {
     // the usual case: the maxima, sums and value rows of all pieces load together
     const float* pb[8];
-    int ro[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pb[k] = k < sa.cnt ? piece_record<D>(sa, k, sp, rec, wa) : piece_record<D>(sb, k - sa.cnt, sp, rec, wb);
-      ro[k] = k < sa.cnt ? mi * g : 0;
-    }
+    for (int k = 0; k < 8; ++k) pb[k] = piece_record<D>(sg, k, sp, rec);
     for (int h = wave; h < g; h += 4) {
       const float* mine = nullptr;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (lane == k && pb[k]) mine = pb[k] + (ro[k] + h) * (D + 4);
+        if (lane == k && pb[k]) mine = pb[k] + (row0 + h) * (D + 4);
       const float* ml = mine ? mine : rec;  // any valid address; unused
       const float m_l = ml[0], z_l = ml[1];
       float val[8][E];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float* rk = pb[k] ? pb[k] + (ro[k] + h) * (D + 4) : rec;  // weighted by zero when missing
+        const float* rk = pb[k] ? pb[k] + (row0 + h) * (D + 4) : rec;  // weighted by zero when missing
 #pragma unroll
         for (int e = 0; e < E; ++e) val[k][e] = rk[4 + lane + 64 * e];
       }
@@ -573,16 +691,15 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
 #pragma unroll
       for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
     }
-  } else if (!done_by_decode) {
+  } else if (!sg.whole) {
     auto record = [&](int k, int h) -> const float* {
-      const float* p0 =
-          k < sa.cnt ? piece_record<D>(sa, k, sp, rec, wa) : piece_record<D>(sb, k - sa.cnt, sp, rec, wb);
-      return p0 ? p0 + ((k < sa.cnt ? mi * g : 0) + h) * (D + 4) : nullptr;
+      const float* p0 = piece_record<D>(sg, k, sp, rec);
+      return p0 ? p0 + (row0 + h) * (D + 4) : nullptr;
     };
     for (int h = wave; h < g; h += 4) {
       float mx = -INFINITY;
-      for (int base = 0; base < cnt; base += 64) {
-        const float* rr = base + lane < cnt ? record(base + lane, h) : nullptr;
+      for (int base = 0; base < sg.cnt; base += 64) {
+        const float* rr = base + lane < sg.cnt ? record(base + lane, h) : nullptr;
         if (rr) mx = fmaxf(mx, rr[0]);
       }
 #pragma unroll
@@ -591,11 +708,11 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
       float uu[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) uu[e] = 0.f;
-      for (int base = 0; base < cnt; base += 64) {
-        const float* rr = base + lane < cnt ? record(base + lane, h) : nullptr;
+      for (int base = 0; base < sg.cnt; base += 64) {
+        const float* rr = base + lane < sg.cnt ? record(base + lane, h) : nullptr;
         const float f = rr ? __builtin_amdgcn_exp2f(rr[0] - mx) : 0.f;
         if (rr) zz += f * rr[1];
-        const int c64 = min(64, cnt - base);
+        const int c64 = min(64, sg.cnt - base);
         for (int k0 = 0; k0 < c64; k0 += 8) {
           float val[8][E];
           float fk[8];
@@ -639,13 +756,12 @@ StreamPlan shared_plan(int num_seqs, int num_groups, int hq, int hkv, int d, int
   const int g = hq / hkv;
   const int64_t waves = static_cast<int64_t>(p.workgroups) * kSW;
   const auto round256 = [](size_t b) { return (b + 255) / 256 * 256; };
-  // workspace: [step slots | 8 words per row for the merge | wave records | whole-segment records]
-  p.prefix_offset = 0;  // unused: the merge reads each row's tile ranges from its 8 words
+  // workspace: [step slots | 4 words per row for the merge | wave records]
+  p.prefix_offset = 0;  // unused: the merge reads each row's tile range from its 4 words
   p.slots_offset = 0;
   p.seq_group_offset = p.slots_offset + round256(static_cast<size_t>(num_seqs) * sizeof(int32_t));
-  p.records_offset = p.seq_group_offset + round256(static_cast<size_t>(num_seqs) * 8 * sizeof(int32_t));
-  p.whole_offset = p.records_offset + round256(static_cast<size_t>(waves) * 2 * kShCols * (d + 4) * sizeof(float));
-  p.workspace_bytes = p.whole_offset + static_cast<size_t>(hkv) * 2 * num_seqs * g * (d + 4) * sizeof(float);
+  p.records_offset = p.seq_group_offset + round256(static_cast<size_t>(num_seqs) * 4 * sizeof(int32_t));
+  p.workspace_bytes = p.records_offset + static_cast<size_t>(waves) * 2 * kShCols * (d + 4) * sizeof(float);
   p.lds_bytes = shared_lds(num_seqs, num_groups);
   return p;
 }
@@ -659,7 +775,6 @@ static void launch_shared_db(const StreamPlan& p, hipStream_t s, const void* q, 
   int32_t* slots_ws = reinterpret_cast<int32_t*>(base + p.slots_offset);
   int32_t* seq_info = reinterpret_cast<int32_t*>(base + p.seq_group_offset);
   float* rec = reinterpret_cast<float*>(base + p.records_offset);
-  float* rec_whole = reinterpret_cast<float*>(base + p.whole_offset);
   const int g = hq / hkv;
   AppendArgs ap{};
   const int32_t* slots_in = nullptr;
@@ -676,10 +791,10 @@ static void launch_shared_db(const StreamPlan& p, hipStream_t s, const void* q, 
     ap.block_size = B;
   }
   decode_shared<D, B><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
-      static_cast<const uint16_t*>(q), k, v, bt, cl, groups, n_groups, static_cast<uint16_t*>(out), rec, rec_whole,
-      seq_info, n, hq, hkv, g, max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws);
-  merge_shared<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, rec_whole, seq_info, static_cast<uint16_t*>(out), n, hq, hkv,
-                                                     g, static_cast<int64_t>(p.workgroups) * kSW, ap);
+      static_cast<const uint16_t*>(q), k, v, bt, cl, groups, n_groups, static_cast<uint16_t*>(out), rec, seq_info,
+      n, hq, hkv, g, max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws);
+  merge_shared<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, seq_info, static_cast<uint16_t*>(out), hq, hkv, g,
+                                                     static_cast<int64_t>(p.workgroups) * kSW, ap);
 }
 
 int launch_shared(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,

@@ -13,8 +13,7 @@ struct StreamPlan {
   size_t prefix_offset = 0;    // workspace: [tile prefix sums | step slots | summary records]
   size_t slots_offset = 0;
   size_t records_offset = 0;
-  size_t seq_group_offset = 0;  // decode_shared: group, member and tile ranges of each sequence
-  size_t whole_offset = 0;      // decode_shared: records of whole segments
+  size_t seq_group_offset = 0;  // decode_shared: tile range and record row of each sequence
   size_t workspace_bytes = 0;
   size_t lds_bytes = 0;
 };

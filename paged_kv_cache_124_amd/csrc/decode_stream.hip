@@ -314,24 +314,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   reset(st);
   // Two LDS stages per wave: while tile x is computed (from registers read
   // out of one stage), tile x + 1's keys and values stream into the other
-  // stage, its Q into registers and the table entries of tile x + 2 as well.
-  // All loads are unconditional (a missing successor repeats the current
-  // tile's addresses).
-  QOp<D> qA, qB;
+  // stage and the table entries of tile x + 2 load as well.  These loads are
+  // unconditional (a missing successor repeats the current tile's addresses).
+  // The queries are those of the segment: loaded when a segment starts, not
+  // again for each of its tiles.
+  QOp<D> qc;
   TilePos nxt = x1 - x0 > 1 ? advance(cur, s_pre, hkv) : cur;
   Tb<NB> tbA = load_tb<B, TOK>(cur, block_tables, max_blocks, s_len);
   Tb<NB> tbB = load_tb<B, TOK>(nxt, block_tables, max_blocks, s_len);
-  load_q<D, F8>(qA, cur, q, hq, g, r, gq);
+  load_q<D, F8>(qc, cur, q, hq, g, r, gq);
   dma_tile<D, B, F8>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
   // FP8: the scales of a tile's blocks travel with it, one tile ahead like its Q
   Sc8 scA{}, scB{};
   if constexpr (F8) scA = load_scales<B>(tbA, k_scale, v_scale, cur.j, hkv, num_blocks, gq);
 
   int64_t x = x0;
-  // One step: tile `cur` (staged in stage SC, Q in qc, blocks tbc) is computed
-  // while `nxt` streams into the other stage / qn (its blocks tbn are known)
-  // and the table entries of the tile after it load into tb2.  Returns false
-  // after the last tile.
+  // One step: tile `cur` (staged in stage SC, blocks tbc) is computed while
+  // `nxt` streams into the other stage (its blocks tbn are known) and the
+  // table entries of the tile after it load into tb2.  Returns false after
+  // the last tile.
   // the step's new token, for tiles that end a segment holding one
   auto wants_new = [&](TilePos t) -> bool {
     return !F8 && k_new != nullptr && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
@@ -339,8 +340,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // one buffer: a step patches its tile before it loads the next tile's token
   NewTok<D> ntok;
   if (wants_new(cur)) load_new<D>(ntok, cur, k_new, v_new, slots, hkv, r, gq);
-  auto step = [&](auto sc_tag, QOp<D>& qc, const Tb<NB>& tbc, const Sc8& scc, QOp<D>& qn, const Tb<NB>& tbn,
-                  Sc8& scn, Tb<NB>& tb2) -> bool {
+  auto step = [&](auto sc_tag, const Tb<NB>& tbc, const Sc8& scc, const Tb<NB>& tbn, Sc8& scn,
+                  Tb<NB>& tb2) -> bool {
     constexpr int SC = decltype(sc_tag)::value;
     unsigned char(&stc)[4][kStageBytes] = SC == 0 ? g_stage0 : g_stage1;
     unsigned char(&stn)[4][kStageBytes] = SC == 0 ? g_stage1 : g_stage0;
@@ -358,7 +359,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       read_tile8<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
       __builtin_amdgcn_sched_barrier(0);
       tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
-      load_q<D, F8>(qn, nxt, q, hq, g, r, gq);
       scn = load_scales<B>(tbn, k_scale, v_scale, nxt.j, hkv, num_blocks, gq);
       dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
@@ -390,7 +390,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
         }
       }
       tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
-      load_q<D, F8>(qn, nxt, q, hq, g, r, gq);
       if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
       dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
@@ -405,14 +404,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       piece_start = 0;
     }
     if (!has_next) return false;
+    if (seg_end) load_q<D, F8>(qc, nxt, q, hq, g, r, gq);  // the next segment's queries
     ++x;
     cur = nxt;
     nxt = nxt2;
     return true;
   };
   while (true) {
-    if (!step(std::integral_constant<int, 0>{}, qA, tbA, scA, qB, tbB, scB, tbA)) break;
-    if (!step(std::integral_constant<int, 1>{}, qB, tbB, scB, qA, tbA, scA, tbB)) break;
+    if (!step(std::integral_constant<int, 0>{}, tbA, scA, tbB, scB, tbA)) break;
+    if (!step(std::integral_constant<int, 1>{}, tbB, scB, tbA, scA, tbB)) break;
   }
 }
 
