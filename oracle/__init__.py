@@ -16,8 +16,10 @@ attention      fp64 paged decode attention (gather through the block table,
                address translation, and the append / block-copy storage rules.
 block_manager  pure-Python block manager: LIFO free list, per-block reference
                counts, block tables, fork, copy-on-write of a shared tail
-               block, release, batch building, and the rule that groups
-               consecutive batch rows sharing full leading blocks.
+               block, release, batch building, the rule that groups
+               consecutive batch rows sharing full leading blocks, and a
+               prefix-caching variant (full blocks cached by their exact
+               token chain, idle LRU, revival, eviction under pressure).
 fp8            KV cache held as FP8 E4M3 codes with per-(block, KV head)
                scales: code values, the saturating round-to-nearest-even
                quantizer, the quantizing append, block copy with scales, and

@@ -66,6 +66,10 @@ class BlockManagerModel:
         self.cow_copies = 0
 
     # -- allocation -------------------------------------------------------
+    def _available(self) -> int:
+        """Blocks an allocation may take."""
+        return len(self.free)
+
     def _pop(self) -> int:
         b = self.free.pop()
         self.ref[b] = 1
@@ -77,7 +81,7 @@ class BlockManagerModel:
         if seq in self.tables:
             return ERR_EXISTS
         need = -(-num_tokens // self.block_size)
-        if len(self.free) < need:
+        if self._available() < need:
             return ERR_NO_FREE_BLOCKS
         self.tables[seq] = [self._pop() for _ in range(need)]
         self.lens[seq] = num_tokens
@@ -105,7 +109,7 @@ class BlockManagerModel:
         if off != 0:
             tail = table[-1]
             if self.ref[tail] > 1:
-                if not self.free:
+                if self._available() == 0:
                     return ERR_NO_FREE_BLOCKS, -1, -1, -1
                 new = self._pop()
                 self.ref[tail] -= 1
@@ -116,7 +120,7 @@ class BlockManagerModel:
             else:
                 block = tail
         else:
-            if not self.free:
+            if self._available() == 0:
                 return ERR_NO_FREE_BLOCKS, -1, -1, -1
             block = self._pop()
             table.append(block)
@@ -255,3 +259,197 @@ def shared_prefix_groups(tables: Sequence[Sequence[int]], lens: Sequence[int], b
             first, count, L = row, 1, full[row]
     close(first, count, L)
     return groups
+
+
+class PrefixCachingModel(BlockManagerModel):
+    """The block manager with automatic prefix caching.
+
+    What the pages fix ([P1] section 18; [P2] section 6; [P3] "Prefix
+    caching"): a full block is identified by its tokens together with its
+    whole preceding context, so equal text after a different prefix does not
+    match; a block whose reference count drops to 0 stays cached and
+    reusable, in an LRU structure; a request whose prefix matches takes the
+    cached blocks (0 -> 1 when idle) instead of recomputing them; allocation
+    under pressure reclaims idle cached blocks before it fails ([P1] section
+    19).
+
+    Readings where the pages leave details open (also in the design doc):
+      * A cached block is keyed by the exact token ids from the start of the
+        sequence to its own end (its chain).  Only full blocks are cached; a
+        lookup takes the longest run of leading full blocks whose chains are
+        cached and stops at the first miss.  A block whose parent was evicted
+        stays reachable: a request that recomputes the parent finds it again.
+      * A block that fills up through appends of known tokens is cached then;
+        if its chain is already cached in another block, it stays uncached.
+        An append without a token id ends the sequence's chain: its later
+        blocks are not cached.
+      * Release walks the table from its last block to its first; a cached
+        block reaching 0 joins the idle list at its most recent end, any
+        other block the LIFO free list.  So a finished sequence's deepest
+        blocks are evicted before its shallower ones.
+      * Allocation takes the free list first, then evicts the least recently
+        released idle block (its entry is dropped).
+      * Batch appends check capacity first (a dry run of the copy-on-write
+        decisions) and then cannot fail; nothing is undone.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, pop_order: Optional[Sequence[int]] = None):
+        super().__init__(num_blocks, block_size, pop_order)
+        self.index: Dict[Tuple[int, ...], int] = {}  # chain -> block
+        self.entry: Dict[int, Tuple[int, ...]] = {}  # block -> chain
+        self.idle: List[int] = []  # cached blocks with no reference, least recently released first
+        self.tokens: Dict[int, Optional[List[int]]] = {}  # seq -> its token ids (None: some unknown)
+        self.hit_blocks = 0
+        self.evictions = 0
+
+    # -- allocation with eviction -------------------------------------------
+    def _available(self) -> int:
+        return len(self.free) + len(self.idle)
+
+    def _pop(self) -> int:
+        if self.free:
+            b = self.free.pop()
+        else:
+            b = self.idle.pop(0)  # least recently released
+            del self.index[self.entry.pop(b)]
+            self.evictions += 1
+        self.ref[b] = 1
+        return b
+
+    def _take(self, b: int) -> None:
+        """One more reference to a cached block (0 -> 1 leaves the idle list)."""
+        if self.ref[b] == 0:
+            self.idle.remove(b)
+        self.ref[b] += 1
+
+    # -- requests -------------------------------------------------------------
+    def lookup(self, tokens: Sequence[int]) -> List[int]:
+        """Blocks of the longest cached run of leading full blocks of `tokens` (no state change)."""
+        B = self.block_size
+        blocks = []
+        for i in range(len(tokens) // B):
+            b = self.index.get(tuple(int(t) for t in tokens[:(i + 1) * B]))
+            if b is None:
+                break
+            blocks.append(b)
+        return blocks
+
+    def add_seq_tokens(self, seq: int, tokens: Sequence[int]) -> Tuple[int, int]:
+        """A new sequence with these prompt token ids.  Returns (status, cached tokens reused)."""
+        B = self.block_size
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        if n <= 0:
+            return ERR_INVALID_ARG, 0
+        if seq in self.tables:
+            return ERR_EXISTS, 0
+        hits = self.lookup(tokens)
+        nblocks = -(-n // B)
+        idle_hits = sum(1 for b in hits if self.ref[b] == 0)
+        if self._available() - idle_hits < nblocks - len(hits):
+            return ERR_NO_FREE_BLOCKS, 0
+        table: List[int] = []
+        for b in hits:
+            self._take(b)
+            table.append(b)
+        self.hit_blocks += len(hits)
+        for i in range(len(hits), nblocks):
+            b = self._pop()
+            table.append(b)
+            if (i + 1) * B <= n:  # a full block of the prompt: cache it
+                key = tuple(tokens[:(i + 1) * B])
+                self.index[key] = b
+                self.entry[b] = key
+        self.tables[seq] = table
+        self.lens[seq] = n
+        self.tokens[seq] = tokens
+        return OK, len(hits) * B
+
+    def add_seq(self, seq: int, num_tokens: int) -> int:
+        st = super().add_seq(seq, num_tokens)
+        if st == OK:  # no token ids: nothing of it can be cached
+            self.tokens[seq] = None
+        return st
+
+    def fork(self, parent: int, child: int) -> int:
+        st = super().fork(parent, child)
+        if st == OK:
+            t = self.tokens[parent]
+            self.tokens[child] = None if t is None else list(t)
+        return st
+
+    def append_token(self, seq: int, token: Optional[int]) -> Tuple[int, int, int, int]:
+        """append_slot, knowing the new token's id (None: unknown, which ends the chain)."""
+        if seq not in self.tables:
+            return ERR_NOT_FOUND, -1, -1, -1
+        st, slot, src, dst = BlockManagerModel.append_slot(self, seq)
+        if st != OK:
+            return st, slot, src, dst
+        t = self.tokens[seq]
+        if token is None or t is None:
+            self.tokens[seq] = None
+        else:
+            t.append(int(token))
+            if len(t) % self.block_size == 0:  # the tail block is now full: cache it unless its chain is
+                key = tuple(t)
+                if key not in self.index:
+                    b = self.tables[seq][-1]
+                    self.index[key] = b
+                    self.entry[b] = key
+        return OK, slot, src, dst
+
+    def append_slot(self, seq: int) -> Tuple[int, int, int, int]:
+        return self.append_token(seq, None)
+
+    def append_tokens(self, seqs: Sequence[int], tokens: Optional[Sequence[int]]):
+        """Batch append, all-or-nothing by a capacity check first.  Returns (status, slots, cow_pairs, failed_index)."""
+        for i, seq in enumerate(seqs):
+            if seq not in self.tables:
+                return ERR_NOT_FOUND, [], [], i
+        need, refs = 0, {}
+        for seq in seqs:
+            if self.lens[seq] % self.block_size == 0:
+                need += 1
+            else:
+                tail = self.tables[seq][-1]
+                r = refs.get(tail, self.ref[tail])
+                if r > 1:
+                    need += 1
+                    refs[tail] = r - 1
+        if need > self._available():
+            return ERR_NO_FREE_BLOCKS, [], [], -1
+        slots, pairs = [], []
+        for i, seq in enumerate(seqs):
+            st, slot, src, dst = self.append_token(seq, None if tokens is None else tokens[i])
+            assert st == OK
+            slots.append(slot)
+            if src >= 0:
+                pairs.append((src, dst))
+        return OK, slots, pairs, -1
+
+    def append_slots(self, seqs: Sequence[int]):
+        return self.append_tokens(seqs, None)
+
+    def free_seq(self, seq: int) -> int:
+        if seq not in self.tables:
+            return ERR_NOT_FOUND
+        for b in reversed(self.tables[seq]):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                (self.idle if b in self.entry else self.free).append(b)
+        del self.tables[seq]
+        del self.lens[seq]
+        del self.tokens[seq]
+        return OK
+
+    def cached_prefix(self, b: int) -> List[int]:
+        """The token ids a cached block stands for: the whole chain up to its end."""
+        return list(self.entry[b])
+
+    def stats(self) -> Dict[str, int]:
+        s = super().stats()
+        s["num_cached"] = len(self.entry)
+        s["num_idle"] = len(self.idle)
+        s["hit_blocks"] = self.hit_blocks
+        s["evictions"] = self.evictions
+        return s
