@@ -279,8 +279,10 @@ class PrefixCachingModel(BlockManagerModel):
         lookup takes the longest run of leading full blocks whose chains are
         cached and stops at the first miss.  A block whose parent was evicted
         stays reachable: a request that recomputes the parent finds it again.
-      * A block that fills up through appends of known tokens is cached then;
-        if its chain is already cached in another block, it stays uncached.
+      * A block that fills up (a prompt's full blocks past the cached run, or
+        a block filled through appends of known tokens) is cached then; if
+        its chain is already cached in another block (a request that missed
+        an evicted parent can meet its surviving child), it stays uncached.
         An append without a token id ends the sequence's chain: its later
         blocks are not cached.
       * Release walks the table from its last block to its first; a cached
@@ -356,8 +358,8 @@ class PrefixCachingModel(BlockManagerModel):
         for i in range(len(hits), nblocks):
             b = self._pop()
             table.append(b)
-            if (i + 1) * B <= n:  # a full block of the prompt: cache it
-                key = tuple(tokens[:(i + 1) * B])
+            key = tuple(tokens[:(i + 1) * B])
+            if (i + 1) * B <= n and key not in self.index:  # a full block of the prompt: cache it
                 self.index[key] = b
                 self.entry[b] = key
         self.tables[seq] = table
@@ -407,7 +409,7 @@ class PrefixCachingModel(BlockManagerModel):
             if seq not in self.tables:
                 return ERR_NOT_FOUND, [], [], i
         need, refs = 0, {}
-        for seq in seqs:
+        for i, seq in enumerate(seqs):
             if self.lens[seq] % self.block_size == 0:
                 need += 1
             else:
@@ -416,8 +418,8 @@ class PrefixCachingModel(BlockManagerModel):
                 if r > 1:
                     need += 1
                     refs[tail] = r - 1
-        if need > self._available():
-            return ERR_NO_FREE_BLOCKS, [], [], -1
+            if need > self._available():  # the append of seqs[i] would find no block
+                return ERR_NO_FREE_BLOCKS, [], [], i
         slots, pairs = [], []
         for i, seq in enumerate(seqs):
             st, slot, src, dst = self.append_token(seq, None if tokens is None else tokens[i])

@@ -173,6 +173,34 @@ def test_blocks_filled_by_generated_tokens_become_reusable():
     _check(m3)
 
 
+def test_a_miss_can_meet_a_cached_child_of_an_evicted_parent():
+    """Chains are content.  Two forks that generate the same tokens cache [1..4] in one's block and [1..6] in the
+    other's; after [1..4] is evicted, a request for 1..7 misses there (stop at the first miss), recomputes 3..6,
+    caches its new [1..4] and leaves [1..6] to the block that already holds it."""
+    m = BM.PrefixCachingModel(8, 2)
+    assert m.add_seq_tokens("P", [1, 2, 3]) == (BM.OK, 0)
+    assert m.fork("P", "Q") == BM.OK
+    m.append_token("Q", 4)  # Q copies the shared tail on write and caches [1..4]
+    m.append_token("P", 4)
+    for t in (5, 6):        # P first: P caches [1..6]
+        m.append_token("P", t)
+        m.append_token("Q", t)
+    x, p1, p2 = m.tables["P"]
+    _, q1, q2 = m.tables["Q"]
+    assert m.index[(1, 2, 3, 4)] == q1 and m.index[(1, 2, 3, 4, 5, 6)] == p2
+    m.free_seq("Q")   # q2 uncached -> free; q1 -> idle
+    m.free_seq("P")   # p2 -> idle, p1 -> free, x -> idle
+    assert m.idle == [q1, p2, x] and len(m.free) == 5
+    assert m.add_seq("F", 12) == BM.OK and m.evictions == 1  # 6 blocks: 5 free + q1 evicted
+    assert (1, 2, 3, 4) not in m.index and m.index[(1, 2, 3, 4, 5, 6)] == p2
+    m.free_seq("F")   # F's blocks were never cached: back to the free list
+    st, hit = m.add_seq_tokens("R", [1, 2, 3, 4, 5, 6, 7])
+    assert st == BM.OK and hit == 2 and m.tables["R"][0] == x
+    assert m.index[(1, 2, 3, 4)] == m.tables["R"][1]
+    assert m.index[(1, 2, 3, 4, 5, 6)] == p2 and m.tables["R"][2] not in m.entry
+    _check(m)
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_random_traces_hit_exactly_the_cached_prefixes(seed):
     """Random requests over a small vocabulary (so prefixes repeat), forks, appends with and without token ids,
