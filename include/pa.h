@@ -431,9 +431,73 @@ int pa_bm_build_batch(pa_bm* bm, const int64_t* seqs, int n, int max_blocks_per_
 int pa_bm_shared_groups(pa_bm* bm, const int64_t* seqs, int n, int max_members, int32_t* groups_out, int cap,
                         int* num_groups);
 
+/* ---- prefix cache ------------------------------------------------------------
+ *
+ * Automatic prefix caching ("PagedAttention: Virtual Memory for the KV
+ * Cache", sections 18-19; "PagedAttention in vLLM: scattered memory, exact
+ * attention", section 6; "PagedAttention and KV Memory", "Prefix caching"):
+ * a full block is identified by its token ids together with every token
+ * before it in its sequence, so equal text after a different prefix never
+ * matches.  A cached block whose reference count drops to 0 is kept (idle)
+ * and reused by a later request whose prefix matches (0 -> 1); under
+ * pressure an allocation reclaims the least recently released idle block
+ * before it fails.  Host only.
+ *
+ *   - only full blocks are cached: a prompt's full blocks, and a block that
+ *     fills up through pa_bm_append_tokens with known token ids; a block
+ *     whose chain is cached already stays uncached;
+ *   - a lookup takes the longest run of leading full blocks whose chains are
+ *     cached and stops at the first miss;
+ *   - appends without token ids (pa_bm_append_slot(s)), and sequences added
+ *     with pa_bm_add_seq, end a sequence's chain: its later blocks are not
+ *     cached;
+ *   - release walks a sequence's table from its last block to its first; a
+ *     cached block reaching 0 becomes the most recently released idle block,
+ *     any other block goes to the free list; allocation takes the free list
+ *     first, then evicts the least recently released idle block;
+ *   - a match compares the block's token ids and a 64-bit hash of the tokens
+ *     before it: a false match needs a 64-bit collision of two different
+ *     prefixes that end in the same block of tokens;
+ *   - batch appends check capacity first (a dry run of the copy-on-write
+ *     decisions) and then cannot fail.
+ *
+ * A reused block's KV is whatever its first owner's prefill wrote: that
+ * prefill must be ordered before the decode that reads it (one stream). */
+typedef struct pa_bm_cache_stats_t {
+  int64_t enabled;     /* 1 once pa_bm_enable_prefix_cache succeeded          */
+  int64_t num_cached;  /* blocks holding a cached chain (in use or idle)     */
+  int64_t num_idle;    /* cached blocks without references (evictable)       */
+  int64_t hit_blocks;  /* blocks reused by pa_bm_add_seq_tokens so far       */
+  int64_t evictions;   /* idle blocks reclaimed by allocations so far        */
+} pa_bm_cache_stats_t;
+
+/* Turn the prefix cache on.  Only while the manager holds no sequence
+ * (PA_ERR_INVALID_ARG otherwise); it stays on. */
+int pa_bm_enable_prefix_cache(pa_bm* bm);
+
+/* New sequence with prompt token ids tokens[0 .. num_tokens - 1] (host,
+ * caller-owned).  Reuses the longest cached run of its leading full blocks
+ * and takes fresh blocks for the rest; *cached_tokens (nullable) receives the
+ * number of leading tokens whose KV is already there (a multiple of B), which
+ * the caller's prefill may skip.  All-or-nothing (PA_ERR_NO_FREE_BLOCKS leaves
+ * the manager unchanged).  Without the prefix cache: pa_bm_add_seq. */
+int pa_bm_add_seq_tokens(pa_bm* bm, int64_t seq, const int32_t* tokens, int num_tokens, int* cached_tokens);
+
+/* pa_bm_append_slots, with the appended tokens' ids (tokens[i] for seqs[i];
+ * NULL: unknown), so blocks that fill up can be cached. */
+int pa_bm_append_tokens(pa_bm* bm, const int64_t* seqs, const int32_t* tokens, int n, int32_t* slots,
+                        int32_t* cow_pairs, int* num_pairs);
+
+/* Prefix-cache counters. */
+int pa_bm_cache_stats(pa_bm* bm, pa_bm_cache_stats_t* out);
+
+/* Copy the idle cached blocks, least recently released first (the eviction
+ * order); *n_out = their number. */
+int pa_bm_idle_list(pa_bm* bm, int32_t* out, int cap, int* n_out);
+
 /* Reference count of a block (-1 for an id outside the pool). */
 int pa_bm_refcount(pa_bm* bm, int block);
-/* Number of free blocks. */
+/* Number of blocks on the free list (idle cached blocks not included). */
 int pa_bm_num_free(pa_bm* bm);
 /* Length of a sequence in tokens (-1 if unknown). */
 int64_t pa_bm_seq_len(pa_bm* bm, int64_t seq);
@@ -441,7 +505,8 @@ int64_t pa_bm_seq_len(pa_bm* bm, int64_t seq);
 int pa_bm_block_table(pa_bm* bm, int64_t seq, int32_t* out, int cap, int* n_out);
 /* Copy the free list in hand-out order (next block first). */
 int pa_bm_free_list(pa_bm* bm, int32_t* out, int cap, int* n_out);
-/* True (1) when a new sequence of num_tokens tokens fits the free blocks. */
+/* True (1) when a new sequence of num_tokens tokens fits the free blocks
+ * (and the idle cached blocks, which an allocation may reclaim). */
 int pa_bm_can_allocate(pa_bm* bm, int num_tokens);
 /* Pool accounting in the terms of the first page's section 17. */
 int pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out);

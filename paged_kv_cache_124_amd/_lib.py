@@ -46,6 +46,13 @@ class PAError(RuntimeError):
         super().__init__(f"{where}: {lib.pa_status_string(status).decode()} (status {status})")
 
 
+class BMCacheStats(ctypes.Structure):
+    _fields_ = [(n, c_int64) for n in ("enabled", "num_cached", "num_idle", "hit_blocks", "evictions")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
 class BMStats(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in ("num_blocks", "num_free", "num_used", "num_seqs",
                                        "cow_copies", "stored_tokens", "tail_waste_slots")]
@@ -87,6 +94,11 @@ _SIGS = {
     "pa_bm_free_seq": (c_int, [c_void_p, c_int64]),
     "pa_bm_build_batch": (c_int, [c_void_p, _P64, c_int, c_int, _P32, _P32]),
     "pa_bm_shared_groups": (c_int, [c_void_p, _P64, c_int, c_int, _P32, c_int, POINTER(c_int)]),
+    "pa_bm_enable_prefix_cache": (c_int, [c_void_p]),
+    "pa_bm_add_seq_tokens": (c_int, [c_void_p, c_int64, _P32, c_int, POINTER(c_int)]),
+    "pa_bm_append_tokens": (c_int, [c_void_p, _P64, _P32, c_int, _P32, _P32, POINTER(c_int)]),
+    "pa_bm_cache_stats": (c_int, [c_void_p, POINTER(BMCacheStats)]),
+    "pa_bm_idle_list": (c_int, [c_void_p, _P32, c_int, POINTER(c_int)]),
     "pa_bm_refcount": (c_int, [c_void_p, c_int]),
     "pa_bm_num_free": (c_int, [c_void_p]),
     "pa_bm_seq_len": (c_int64, [c_void_p, c_int64]),
@@ -594,6 +606,42 @@ class BlockManager:
         if st != PA_OK:
             return st, slots[:0], pairs[:0], -npairs.value - 1
         return st, slots[:n], pairs[:npairs.value], -1
+
+    def enable_prefix_cache(self) -> int:
+        return lib.pa_bm_enable_prefix_cache(self._h)
+
+    def add_seq_tokens(self, seq: int, tokens):
+        """(status, cached tokens reused) of pa_bm_add_seq_tokens."""
+        t = _i32(tokens)
+        hit = c_int()
+        st = lib.pa_bm_add_seq_tokens(self._h, seq, _ptr32(t), t.shape[0], ctypes.byref(hit))
+        return st, hit.value
+
+    def append_tokens(self, seqs, tokens=None):
+        """pa_bm_append_tokens: (status, slots, cow pairs, failing index or -1); tokens None = unknown ids."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        t = None if tokens is None else _i32(tokens)
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        npairs = c_int()
+        st = lib.pa_bm_append_tokens(self._h, s.ctypes.data_as(_P64), None if t is None else _ptr32(t), n,
+                                     _ptr32(slots), _ptr32(pairs), ctypes.byref(npairs))
+        if st != PA_OK:
+            return st, slots[:0], pairs[:0], -npairs.value - 1
+        return st, slots[:n], pairs[:npairs.value], -1
+
+    def cache_stats(self):
+        out = BMCacheStats()
+        _check(lib.pa_bm_cache_stats(self._h, ctypes.byref(out)), "pa_bm_cache_stats")
+        return out.as_dict()
+
+    def idle_list(self):
+        n = c_int()
+        cap = max(self.num_blocks, 1)
+        out = np.empty(cap, dtype=np.int32)
+        st = lib.pa_bm_idle_list(self._h, _ptr32(out), cap, ctypes.byref(n))
+        return out[: n.value].tolist() if st == PA_OK else []
 
     @property
     def handle(self):

@@ -28,7 +28,31 @@ namespace {
 struct Seq {
   std::vector<int32_t> table;
   int64_t len = 0;
+  // prefix cache: token ids of the partial tail block, chain hash of the
+  // tokens before it, and whether all token ids of the sequence are known
+  std::vector<int32_t> pending;
+  uint64_t chain = 0;
+  bool known = false;
 };
+
+// Chain hash of a full block: its B token ids after the chain hash of the
+// tokens before it (0 for the first block).  splitmix64's finaliser mixes
+// each word in; a match is also checked on the parent hash and the block's
+// token ids, so a false match needs a 64-bit collision of two different
+// prefixes ending in the same block of tokens.
+uint64_t mix64(uint64_t x) {
+  x ^= x >> 30;
+  x *= 0xbf58476d1ce4e5b9ull;
+  x ^= x >> 27;
+  x *= 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+
+uint64_t chain_hash(uint64_t parent, const int32_t* tokens, int n) {
+  uint64_t h = mix64(parent + 0x9e3779b97f4a7c15ull);
+  for (int i = 0; i < n; ++i) h = mix64(h ^ static_cast<uint32_t>(tokens[i]) ^ (static_cast<uint64_t>(i + 1) << 32));
+  return h | 1;  // never 0, the first block's parent
+}
 
 struct Undo {  // what one append did, so a failed batch can be rolled back
   int64_t seq;
@@ -46,11 +70,99 @@ struct pa_bm {
   std::unordered_map<int64_t, Seq> seqs;
   int64_t cow_copies = 0;
 
+  // ---- prefix cache (off unless enabled while no sequence exists) ----------
+  bool caching = false;
+  std::vector<uint8_t> cached;       // block holds a cached full block
+  std::vector<uint64_t> blk_hash;    // its chain hash
+  std::vector<uint64_t> blk_parent;  // chain hash of the tokens before it
+  std::vector<int32_t> blk_tokens;   // [num_blocks][B] its token ids
+  std::unordered_multimap<uint64_t, int32_t> index;  // chain hash -> cached block
+  // idle list: cached blocks without references, least recently released at the head
+  std::vector<int32_t> idle_prev, idle_next;
+  int32_t idle_head = -1, idle_tail = -1;
+  int64_t idle_count = 0, hit_blocks = 0, evictions = 0;
+
+  int64_t available() const { return static_cast<int64_t>(free_stack.size()) + (caching ? idle_count : 0); }
+
+  void idle_push(int32_t b) {  // most recently released end
+    idle_prev[b] = idle_tail;
+    idle_next[b] = -1;
+    if (idle_tail >= 0) idle_next[idle_tail] = b; else idle_head = b;
+    idle_tail = b;
+    ++idle_count;
+  }
+  void idle_remove(int32_t b) {
+    const int32_t p = idle_prev[b], n = idle_next[b];
+    if (p >= 0) idle_next[p] = n; else idle_head = n;
+    if (n >= 0) idle_prev[n] = p; else idle_tail = p;
+    --idle_count;
+  }
+
+  // the cached block holding (parent, tokens), or -1
+  int32_t find(uint64_t parent, const int32_t* tokens) const {
+    const uint64_t h = chain_hash(parent, tokens, block_size);
+    auto range = index.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it) {
+      const int32_t b = it->second;
+      if (blk_parent[b] == parent &&
+          std::memcmp(&blk_tokens[static_cast<size_t>(b) * block_size], tokens, sizeof(int32_t) * block_size) == 0)
+        return b;
+    }
+    return -1;
+  }
+  // cache block b as (parent, tokens) unless that chain is cached already; returns the chain hash
+  uint64_t remember(int32_t b, uint64_t parent, const int32_t* tokens) {
+    const uint64_t h = chain_hash(parent, tokens, block_size);
+    if (find(parent, tokens) >= 0) return h;
+    cached[b] = 1;
+    blk_hash[b] = h;
+    blk_parent[b] = parent;
+    std::memcpy(&blk_tokens[static_cast<size_t>(b) * block_size], tokens, sizeof(int32_t) * block_size);
+    index.emplace(h, b);
+    return h;
+  }
+  void forget(int32_t b) {
+    auto range = index.equal_range(blk_hash[b]);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        index.erase(it);
+        break;
+      }
+    cached[b] = 0;
+  }
+
   int32_t pop() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {  // evict the least recently released idle cached block
+      b = idle_head;
+      idle_remove(b);
+      forget(b);
+      ++evictions;
+    }
     ref[b] = 1;
     return b;
+  }
+
+  void release(int32_t b) {  // a reference dropped to 0
+    if (caching && cached[b]) idle_push(b); else free_stack.push_back(b);
+  }
+
+  // after an append of `token` (nullptr: unknown) to sequence s
+  void note_token(Seq& s, const int32_t* token) {
+    if (!caching) return;
+    if (!token || !s.known) {
+      s.known = false;
+      s.pending.clear();
+      return;
+    }
+    s.pending.push_back(*token);
+    if (s.len % block_size == 0) {  // the tail block is full: cache it
+      s.chain = remember(s.table.back(), s.chain, s.pending.data());
+      s.pending.clear();
+    }
   }
 
   int append(int64_t id, int32_t* slot, int32_t* src, int32_t* dst) {
@@ -65,7 +177,7 @@ struct pa_bm {
     if (off != 0) {
       const int32_t tail = s.table.back();
       if (ref[tail] > 1) {  // shared unaligned tail: clone before writing
-        if (free_stack.empty()) return PA_ERR_NO_FREE_BLOCKS;
+        if (available() == 0) return PA_ERR_NO_FREE_BLOCKS;
         block = pop();
         ref[tail] -= 1;
         s.table.back() = block;
@@ -76,7 +188,7 @@ struct pa_bm {
         block = tail;
       }
     } else {  // tail full (or no tail yet): take a fresh block
-      if (free_stack.empty()) return PA_ERR_NO_FREE_BLOCKS;
+      if (available() == 0) return PA_ERR_NO_FREE_BLOCKS;
       block = pop();
       s.table.push_back(block);
     }
@@ -136,12 +248,69 @@ int pa_bm_add_seq(pa_bm* bm, int64_t seq, int num_tokens) {
   if (!bm || num_tokens <= 0) return PA_ERR_INVALID_ARG;
   if (bm->seqs.count(seq)) return PA_ERR_EXISTS;
   const int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
-  if (static_cast<int64_t>(bm->free_stack.size()) < need) return PA_ERR_NO_FREE_BLOCKS;
+  if (bm->available() < need) return PA_ERR_NO_FREE_BLOCKS;
   Seq s;
   s.table.reserve(need + 1);
   for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->pop());
   s.len = num_tokens;
+  s.known = false;  // no token ids: nothing of it is cached
   bm->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+int pa_bm_enable_prefix_cache(pa_bm* bm) {
+  if (!bm || !bm->seqs.empty()) return PA_ERR_INVALID_ARG;
+  if (bm->caching) return PA_OK;
+  const size_t nb = static_cast<size_t>(bm->num_blocks);
+  bm->cached.assign(nb, 0);
+  bm->blk_hash.assign(nb, 0);
+  bm->blk_parent.assign(nb, 0);
+  bm->blk_tokens.assign(nb * static_cast<size_t>(bm->block_size), 0);
+  bm->idle_prev.assign(nb, -1);
+  bm->idle_next.assign(nb, -1);
+  bm->caching = true;
+  return PA_OK;
+}
+
+int pa_bm_add_seq_tokens(pa_bm* bm, int64_t seq, const int32_t* tokens, int num_tokens, int* cached_tokens) {
+  if (!bm || num_tokens <= 0 || !tokens) return PA_ERR_INVALID_ARG;
+  if (cached_tokens) *cached_tokens = 0;
+  if (bm->seqs.count(seq)) return PA_ERR_EXISTS;
+  if (!bm->caching) return pa_bm_add_seq(bm, seq, num_tokens);
+  const int B = bm->block_size;
+  const int64_t nblocks = (static_cast<int64_t>(num_tokens) + B - 1) / B;
+  const int64_t full = num_tokens / B;
+  // the longest run of leading full blocks whose chains are cached (no change yet)
+  std::vector<int32_t> hits;
+  uint64_t parent = 0;
+  int64_t idle_hits = 0;
+  for (int64_t i = 0; i < full; ++i) {
+    const int32_t b = bm->find(parent, tokens + i * B);
+    if (b < 0) break;
+    hits.push_back(b);
+    if (bm->ref[b] == 0) ++idle_hits;
+    parent = bm->blk_hash[b];
+  }
+  if (bm->available() - idle_hits < nblocks - static_cast<int64_t>(hits.size())) return PA_ERR_NO_FREE_BLOCKS;
+  Seq s;
+  s.table.reserve(nblocks + 1);
+  for (int32_t b : hits) {  // reuse: 0 -> 1 leaves the idle list
+    if (bm->ref[b] == 0) bm->idle_remove(b);
+    bm->ref[b] += 1;
+    s.table.push_back(b);
+  }
+  bm->hit_blocks += static_cast<int64_t>(hits.size());
+  for (int64_t i = static_cast<int64_t>(hits.size()); i < nblocks; ++i) {
+    const int32_t b = bm->pop();
+    s.table.push_back(b);
+    if (i < full) parent = bm->remember(b, parent, tokens + i * B);  // a full block of the prompt
+  }
+  s.len = num_tokens;
+  s.chain = parent;
+  s.known = true;
+  s.pending.assign(tokens + full * B, tokens + num_tokens);
+  bm->seqs.emplace(seq, std::move(s));
+  if (cached_tokens) *cached_tokens = static_cast<int>(hits.size()) * B;
   return PA_OK;
 }
 
@@ -158,13 +327,74 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
 
 int pa_bm_append_slot(pa_bm* bm, int64_t seq, int32_t* slot, int32_t* cow_src, int32_t* cow_dst) {
   if (!bm || !slot || !cow_src || !cow_dst) return PA_ERR_INVALID_ARG;
-  return bm->append(seq, slot, cow_src, cow_dst);
+  const int st = bm->append(seq, slot, cow_src, cow_dst);
+  if (st == PA_OK) bm->note_token(bm->seqs[seq], nullptr);
+  return st;
+}
+
+// Batch append with a prefix cache: existence, then a dry run of the blocks
+// the appends take (fresh blocks and copy-on-write, with the reference
+// counts the earlier appends of the batch leave), then the appends, which
+// cannot fail.  tokens (nullable) are the appended token ids.
+static int append_batch_cached(pa_bm* bm, const int64_t* seqs, const int32_t* tokens, int n, int32_t* slots,
+                               int32_t* cow_pairs, int* num_pairs) {
+  std::vector<Seq*> rows(n);
+  for (int i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) {
+      *num_pairs = -i - 1;
+      return PA_ERR_NOT_FOUND;
+    }
+    rows[i] = &it->second;
+  }
+  std::unordered_map<int32_t, int32_t> refs;  // tail block -> references left by earlier appends
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    const Seq& s = *rows[i];
+    if (s.len % bm->block_size == 0) {
+      ++need;
+    } else {
+      const int32_t tail = s.table.back();
+      auto r = refs.find(tail);
+      const int32_t cur = r == refs.end() ? bm->ref[tail] : r->second;
+      if (cur > 1) {
+        ++need;
+        refs[tail] = cur - 1;
+      }
+    }
+    if (need > bm->available()) {
+      *num_pairs = -i - 1;
+      return PA_ERR_NO_FREE_BLOCKS;
+    }
+  }
+  int pairs = 0;
+  for (int i = 0; i < n; ++i) {
+    int32_t slot, src, dst;
+    bm->append(seqs[i], &slot, &src, &dst);  // checked above: cannot fail
+    bm->note_token(*rows[i], tokens ? tokens + i : nullptr);
+    slots[i] = slot;
+    if (src >= 0) {
+      cow_pairs[2 * pairs] = src;
+      cow_pairs[2 * pairs + 1] = dst;
+      ++pairs;
+    }
+  }
+  *num_pairs = pairs;
+  return PA_OK;
+}
+
+int pa_bm_append_tokens(pa_bm* bm, const int64_t* seqs, const int32_t* tokens, int n, int32_t* slots,
+                        int32_t* cow_pairs, int* num_pairs) {
+  if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_pairs) return PA_ERR_INVALID_ARG;
+  if (!bm->caching) return pa_bm_append_slots(bm, seqs, n, slots, cow_pairs, num_pairs);
+  return append_batch_cached(bm, seqs, tokens, n, slots, cow_pairs, num_pairs);
 }
 
 int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int n, int32_t* slots, int32_t* cow_pairs,
                        int* num_pairs) {
   if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_pairs)
     return PA_ERR_INVALID_ARG;
+  if (bm->caching) return append_batch_cached(bm, seqs, nullptr, n, slots, cow_pairs, num_pairs);
   std::vector<Undo> done;
   done.reserve(n);
   int pairs = 0;
@@ -192,8 +422,13 @@ int pa_bm_free_seq(pa_bm* bm, int64_t seq) {
   if (!bm) return PA_ERR_INVALID_ARG;
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
-  for (int32_t b : it->second.table) {
-    if (--bm->ref[b] == 0) bm->free_stack.push_back(b);
+  const std::vector<int32_t>& t = it->second.table;
+  if (bm->caching) {  // last block first: a sequence's deepest blocks become the oldest idle entries
+    for (auto b = t.rbegin(); b != t.rend(); ++b)
+      if (--bm->ref[*b] == 0) bm->release(*b);
+  } else {
+    for (int32_t b : t)
+      if (--bm->ref[b] == 0) bm->free_stack.push_back(b);
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -308,7 +543,7 @@ int pa_bm_free_list(pa_bm* bm, int32_t* out, int cap, int* n_out) {
 int pa_bm_can_allocate(pa_bm* bm, int num_tokens) {
   if (!bm || num_tokens <= 0) return 0;
   const int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
-  return static_cast<int64_t>(bm->free_stack.size()) >= need ? 1 : 0;
+  return bm->available() >= need ? 1 : 0;
 }
 
 int pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
@@ -337,6 +572,25 @@ int pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
   out->cow_copies = bm->cow_copies;
   out->stored_tokens = stored;
   out->tail_waste_slots = used * bm->block_size - stored;
+  return PA_OK;
+}
+
+int pa_bm_cache_stats(pa_bm* bm, pa_bm_cache_stats_t* out) {
+  if (!bm || !out) return PA_ERR_INVALID_ARG;
+  out->enabled = bm->caching ? 1 : 0;
+  out->num_cached = static_cast<int64_t>(bm->index.size());
+  out->num_idle = bm->idle_count;
+  out->hit_blocks = bm->hit_blocks;
+  out->evictions = bm->evictions;
+  return PA_OK;
+}
+
+int pa_bm_idle_list(pa_bm* bm, int32_t* out, int cap, int* n_out) {
+  if (!bm || !n_out || cap < 0) return PA_ERR_INVALID_ARG;
+  *n_out = static_cast<int>(bm->idle_count);
+  if (bm->idle_count > cap || (!out && bm->idle_count > 0)) return PA_ERR_INVALID_ARG;
+  int i = 0;
+  for (int32_t b = bm->idle_head; b >= 0; b = bm->idle_next[b]) out[i++] = b;
   return PA_OK;
 }
 

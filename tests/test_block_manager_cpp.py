@@ -182,3 +182,135 @@ def test_shared_groups_match_the_oracle_rule(pa, seed):
     tables = [model.tables[s] for s in batch]
     lens = [model.lens[s] for s in batch]
     assert [tuple(r) for r in groups.tolist()] == shared_prefix_groups(tables, lens, B, cap)
+
+
+# ---- prefix cache ---------------------------------------------------------------
+
+def _cached_pair(pa, nb, B, order=None):
+    from oracle.block_manager import PrefixCachingModel
+    bm = pa.BlockManager(nb, B, order)
+    assert bm.enable_prefix_cache() == 0
+    return bm, PrefixCachingModel(nb, B, order)
+
+
+def _same(bm, m, seqs):
+    for s in seqs:
+        assert bm.block_table(s)[1] == m.tables[s]
+        assert bm.seq_len(s) == m.lens[s]
+    assert bm.free_list() == m.pop_order()
+    assert bm.idle_list() == m.idle
+    assert [bm.refcount(b) for b in range(m.num_blocks)] == m.ref
+    cs = bm.cache_stats()
+    ms = m.stats()
+    assert (cs["num_cached"], cs["num_idle"], cs["hit_blocks"], cs["evictions"]) == \
+        (ms["num_cached"], ms["num_idle"], ms["hit_blocks"], ms["evictions"])
+    s = bm.stats()
+    assert (s["num_used"], s["num_free"], s["stored_tokens"]) == (ms["num_used"], ms["num_free"], ms["stored_tokens"])
+
+
+def test_prefix_cache_on_the_pages_cases(pa):
+    """[P2] section 6 and [P1] section 18 through the C ABI: shared first blocks, context-sensitive matching,
+    revival 0 -> 1, and the finished sharer whose suffix block is reclaimed first."""
+    g = golden("prefix_cache.json")
+    B = g["two_requests_same_prefix"]["block_size"]
+    bm, m = _cached_pair(pa, 32, B)
+    common = list(range(1, 9))
+    for x in (bm, m):
+        assert x.add_seq_tokens(1, common + [100, 101, 102]) == (0, 0)
+        assert x.add_seq_tokens(2, common + [200, 201]) == (0, 8)
+        assert x.add_seq_tokens(3, [9, 9, 9, 9, 5, 6, 7, 8]) == (0, 0)  # block 1's text after another prefix
+    _same(bm, m, [1, 2, 3])
+    t1 = bm.block_table(1)[1]
+    for x in (bm, m):
+        assert x.free_seq(1) == 0
+    assert bm.refcount(t1[0]) == g["finish_one_of_two"]["refs_after_A_finishes"]
+    for x in (bm, m):
+        assert x.add_seq_tokens(4, [50, 51]) == (0, 0)
+    assert bm.block_table(4)[1] == [t1[2]]  # the finished request's suffix block is reused first
+    _same(bm, m, [2, 3, 4])
+    for x in (bm, m):
+        for s in (2, 3, 4):
+            assert x.free_seq(s) == 0
+        assert x.add_seq_tokens(5, common + [7]) == (0, 8)  # revived from the idle cache
+    assert [bm.refcount(b) for b in bm.block_table(5)[1][:2]] == [g["revival"]["ref_after_reuse"]] * 2
+    _same(bm, m, [5])
+    # without the cache, pa_bm_add_seq_tokens is pa_bm_add_seq
+    plain = pa.BlockManager(8, 4)
+    assert plain.add_seq_tokens(1, [1, 2, 3, 4, 5]) == (0, 0) and plain.block_table(1)[1] == [0, 1]
+    assert plain.cache_stats()["enabled"] == 0
+    # the cache can only be turned on while no sequence exists
+    assert plain.enable_prefix_cache() == 1
+
+
+def test_prefix_cache_eviction_and_evicted_parent(pa):
+    bm, m = _cached_pair(pa, 8, 2)
+    for x in (bm, m):
+        assert x.add_seq_tokens(1, [1, 2, 3]) == (0, 0)
+        assert x.fork(1, 2) == 0
+    for x in (bm, m):  # Q (2) caches [1..4], P (1) caches [1..6]
+        for s, t in ((2, 4), (1, 4), (1, 5), (2, 5), (1, 6), (2, 6)):
+            assert x.append_tokens([s], [t])[0] == 0
+    _same(bm, m, [1, 2])
+    for x in (bm, m):
+        assert x.free_seq(2) == 0 and x.free_seq(1) == 0
+        assert x.add_seq(3, 12) == 0  # evicts the oldest idle block
+        assert x.free_seq(3) == 0
+        assert x.add_seq_tokens(4, [1, 2, 3, 4, 5, 6, 7]) == (0, 2)
+    _same(bm, m, [4])
+    # exhaustion: all-or-nothing, index of the first append that finds no block
+    bm2, m2 = _cached_pair(pa, 4, 2)
+    for x in (bm2, m2):
+        assert x.add_seq_tokens(1, [1, 2]) == (0, 0)
+        assert x.add_seq_tokens(2, [3, 4]) == (0, 0)
+        assert x.add_seq_tokens(3, [5, 6]) == (0, 0)
+    st, slots, pairs, failed = bm2.append_tokens([1, 2, 3], [7, 8, 9])
+    mst, mslots, mpairs, mfailed = m2.append_tokens([1, 2, 3], [7, 8, 9])
+    assert st == mst == 3 and failed == mfailed == 1
+    _same(bm2, m2, [1, 2, 3])
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_prefix_cache_matches_the_oracle_model(pa, seed):
+    """Random requests over a small vocabulary (prefixes repeat), forks, appends with and without token ids,
+    tokenless sequences and releases under pressure: the C++ manager and the oracle model agree after every
+    operation on tables, slots, copy-on-write pairs, hits, free and idle lists, and counters."""
+    rng = random.Random(900 + seed)
+    B = rng.choice([2, 4, 8, 16])
+    nb = rng.randint(16, 64)
+    order = rng.sample(range(nb), nb)
+    bm, m = _cached_pair(pa, nb, B, order)
+    prompts = [[rng.randrange(3) for _ in range(rng.randint(1, 5 * B))] for _ in range(5)]
+    live, nid = [], 0
+    for _ in range(150):
+        op = rng.random()
+        if op < 0.3:
+            base = rng.choice(prompts)
+            toks = base[:rng.randint(1, len(base))] + [rng.randrange(3) for _ in range(rng.randint(0, B))]
+            r1, r2 = bm.add_seq_tokens(nid, toks), m.add_seq_tokens(nid, toks)
+            assert r1 == r2
+            if r1[0] == 0:
+                live.append(nid)
+            nid += 1
+        elif op < 0.35:
+            n_tok = rng.randint(1, 3 * B)
+            assert bm.add_seq(nid, n_tok) == m.add_seq(nid, n_tok)
+            if m.tables.get(nid) is not None:
+                live.append(nid)
+            nid += 1
+        elif op < 0.5 and live:
+            p = rng.choice(live)
+            assert bm.fork(p, nid) == m.fork(p, nid) == 0
+            live.append(nid)
+            nid += 1
+        elif op < 0.8 and live:
+            seqs = rng.sample(live, rng.randint(1, len(live)))
+            toks = None if rng.random() < 0.2 else [rng.randrange(3) for _ in seqs]
+            st, slots, pairs, failed = bm.append_tokens(seqs, toks)
+            mst, mslots, mpairs, mfailed = m.append_tokens(seqs, toks)
+            assert st == mst and failed == mfailed
+            assert list(slots) == mslots and [tuple(x) for x in pairs] == mpairs
+        elif live:
+            s = rng.choice(live)
+            live.remove(s)
+            assert bm.free_seq(s) == m.free_seq(s) == 0
+        _same(bm, m, live)
