@@ -19,7 +19,8 @@ block_manager  pure-Python block manager: LIFO free list, per-block reference
                block, release, batch building, the rule that groups
                consecutive batch rows sharing full leading blocks, and a
                prefix-caching variant (full blocks cached by their exact
-               token chain, idle LRU, revival, eviction under pressure).
+               token chain, idle LRU, revival, eviction under pressure), and
+               swapping of sequences to a host block pool and back.
 fp8            KV cache held as FP8 E4M3 codes with per-(block, KV head)
                scales: code values, the saturating round-to-nearest-even
                quantizer, the quantizing append, block copy with scales, and

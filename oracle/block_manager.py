@@ -64,6 +64,10 @@ class BlockManagerModel:
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
         self.cow_copies = 0
+        # swapping ([P1] section 19): a host pool of blocks, and the sequences whose tables hold host ids
+        self.host_free: List[int] = []
+        self.host_ref: List[int] = []
+        self.swapped: set = set()
 
     # -- allocation -------------------------------------------------------
     def _available(self) -> int:
@@ -92,6 +96,8 @@ class BlockManagerModel:
             return ERR_NOT_FOUND
         if child in self.tables:
             return ERR_EXISTS
+        if parent in self.swapped:
+            return ERR_INVALID_ARG
         for b in self.tables[parent]:
             self.ref[b] += 1
         self.tables[child] = list(self.tables[parent])
@@ -102,6 +108,8 @@ class BlockManagerModel:
         """Reserve the slot of position len(seq).  Returns (status, slot, cow_src, cow_dst)."""
         if seq not in self.tables:
             return ERR_NOT_FOUND, -1, -1, -1
+        if seq in self.swapped:
+            return ERR_INVALID_ARG, -1, -1, -1
         table = self.tables[seq]
         length = self.lens[seq]
         off = length % self.block_size
@@ -162,6 +170,9 @@ class BlockManagerModel:
     def free_seq(self, seq: int) -> int:
         if seq not in self.tables:
             return ERR_NOT_FOUND
+        if seq in self.swapped:
+            self._free_host(seq)
+            return OK
         for b in self.tables[seq]:
             self.ref[b] -= 1
             if self.ref[b] == 0:
@@ -170,12 +181,112 @@ class BlockManagerModel:
         del self.lens[seq]
         return OK
 
+    def _free_host(self, seq: int) -> None:
+        for hb in self.tables[seq]:
+            self.host_ref[hb] -= 1
+            if self.host_ref[hb] == 0:
+                self.host_free.append(hb)
+        self.swapped.discard(seq)
+        del self.tables[seq]
+        del self.lens[seq]
+
+    # -- swapping ([P1] section 19, "Preemption via Swapping") ---------------
+    def enable_host_pool(self, num_host_blocks: int, pop_order: Optional[Sequence[int]] = None) -> int:
+        """A pool of host blocks for swapped-out sequences (host ids 0 .. num_host_blocks - 1)."""
+        if num_host_blocks <= 0 or self.host_ref:
+            return ERR_INVALID_ARG
+        order = list(range(num_host_blocks)) if pop_order is None else [int(b) for b in pop_order]
+        if sorted(order) != list(range(num_host_blocks)):
+            return ERR_INVALID_ARG
+        self.host_free = list(reversed(order))
+        self.host_ref = [0] * num_host_blocks
+        return OK
+
+    def _release(self, b: int) -> None:
+        """A device block whose last reference went away."""
+        self.free.append(b)
+
+    def _distinct_blocks(self, seqs: Sequence[int]) -> List[Tuple[int, int]]:
+        """(block, references from `seqs`) in order of first appearance (sequence order, then table order)."""
+        count: Dict[int, int] = {}
+        order: List[int] = []
+        for seq in seqs:
+            for b in self.tables[seq]:
+                if b not in count:
+                    count[b] = 0
+                    order.append(b)
+                count[b] += 1
+        return [(b, count[b]) for b in order]
+
+    def _swap_check(self, seqs: Sequence[int], want_swapped: bool) -> int:
+        if len(set(seqs)) != len(seqs):
+            return ERR_INVALID_ARG
+        for seq in seqs:
+            if seq not in self.tables:
+                return ERR_NOT_FOUND
+            if (seq in self.swapped) != want_swapped:
+                return ERR_INVALID_ARG
+        return OK
+
+    def swap_out(self, seqs: Sequence[int]) -> Tuple[int, List[Tuple[int, int]]]:
+        """Move these resident sequences to host blocks, all-or-nothing.  Returns (status, [(device block, host
+        block)]) -- the copies to make before the released device blocks are reused.
+
+        Each distinct device block the sequences reference gets one host block, which takes over their
+        references; a block also used by a sequence outside the list keeps its other references (its host
+        copy belongs to the listed sequences only), any other block is released.
+        """
+        st = self._swap_check(seqs, False)
+        if st != OK:
+            return st, []
+        blocks = self._distinct_blocks(seqs)
+        if len(self.host_free) < len(blocks):
+            return ERR_NO_FREE_BLOCKS, []
+        pairs, where = [], {}
+        for b, c in blocks:
+            hb = self.host_free.pop()
+            self.host_ref[hb] = c
+            self.ref[b] -= c
+            if self.ref[b] == 0:
+                self._release(b)
+            pairs.append((b, hb))
+            where[b] = hb
+        for seq in seqs:
+            self.tables[seq] = [where[b] for b in self.tables[seq]]
+            self.swapped.add(seq)
+        return OK, pairs
+
+    def swap_in(self, seqs: Sequence[int]) -> Tuple[int, List[Tuple[int, int]]]:
+        """Bring these swapped sequences back into fresh device blocks, all-or-nothing.  Returns (status,
+        [(host block, device block)]) -- the copies to make before the sequences are decoded."""
+        st = self._swap_check(seqs, True)
+        if st != OK:
+            return st, []
+        blocks = self._distinct_blocks(seqs)
+        if self._available() < len(blocks):
+            return ERR_NO_FREE_BLOCKS, []
+        pairs, where = [], {}
+        for hb, c in blocks:
+            b = self._pop()
+            self.ref[b] = c
+            self.host_ref[hb] -= c
+            if self.host_ref[hb] == 0:
+                self.host_free.append(hb)
+            pairs.append((hb, b))
+            where[hb] = b
+        for seq in seqs:
+            self.tables[seq] = [where[hb] for hb in self.tables[seq]]
+            self.swapped.discard(seq)
+        return OK, pairs
+
     # -- queries ----------------------------------------------------------
     def build_batch(self, seqs: Sequence[int], max_blocks: int) -> Tuple[int, List[List[int]], List[int]]:
         tables, lens = [], []
         for seq in seqs:
             if seq not in self.tables:
                 return ERR_NOT_FOUND, [], []
+            if seq in self.swapped:
+                return ERR_INVALID_ARG, [], []
             t = self.tables[seq]
             if len(t) > max_blocks:
                 return ERR_INVALID_ARG, [], []
@@ -197,6 +308,8 @@ class BlockManagerModel:
         """
         fill: Dict[int, int] = {}
         for seq, table in self.tables.items():
+            if seq in self.swapped:  # host blocks: not part of the device pool
+                continue
             length = self.lens[seq]
             for lb, b in enumerate(table):
                 valid = min(self.block_size, length - lb * self.block_size)
@@ -212,6 +325,10 @@ class BlockManagerModel:
             "stored_tokens": stored,
             "tail_waste_slots": used * self.block_size - stored,
         }
+
+    def swap_stats(self) -> Dict[str, int]:
+        return {"num_swapped": len(self.swapped), "host_free": len(self.host_free),
+                "host_blocks": len(self.host_ref)}
 
 
 def shared_prefix_groups(tables: Sequence[Sequence[int]], lens: Sequence[int], block_size: int,
@@ -408,6 +525,8 @@ class PrefixCachingModel(BlockManagerModel):
         for i, seq in enumerate(seqs):
             if seq not in self.tables:
                 return ERR_NOT_FOUND, [], [], i
+            if seq in self.swapped:
+                return ERR_INVALID_ARG, [], [], i
         need, refs = 0, {}
         for i, seq in enumerate(seqs):
             if self.lens[seq] % self.block_size == 0:
@@ -432,15 +551,21 @@ class PrefixCachingModel(BlockManagerModel):
     def append_slots(self, seqs: Sequence[int]):
         return self.append_tokens(seqs, None)
 
+    def _release(self, b: int) -> None:
+        (self.idle if b in self.entry else self.free).append(b)
+
     def free_seq(self, seq: int) -> int:
         if seq not in self.tables:
             return ERR_NOT_FOUND
-        for b in reversed(self.tables[seq]):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                (self.idle if b in self.entry else self.free).append(b)
-        del self.tables[seq]
-        del self.lens[seq]
+        if seq in self.swapped:
+            self._free_host(seq)
+        else:
+            for b in reversed(self.tables[seq]):
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self._release(b)
+            del self.tables[seq]
+            del self.lens[seq]
         del self.tokens[seq]
         return OK
 
