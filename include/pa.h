@@ -495,6 +495,44 @@ int pa_bm_cache_stats(pa_bm* bm, pa_bm_cache_stats_t* out);
  * order); *n_out = their number. */
 int pa_bm_idle_list(pa_bm* bm, int32_t* out, int cap, int* n_out);
 
+/* ---- swapping ------------------------------------------------------------------
+ *
+ * Preemption by swapping ("PagedAttention: Virtual Memory for the KV Cache",
+ * section 19): a running sequence's blocks move to host memory, its device
+ * blocks serve other requests, and it comes back once device blocks are
+ * released.  The manager tracks a pool of host blocks (ids 0 .. H - 1, in a
+ * host pool the caller allocates with the device pool's per-block layout);
+ * the data moves with pa_swap_blocks.  Host only.
+ *
+ *   - pa_bm_swap_out moves the listed resident sequences: each distinct
+ *     device block they reference (in order of first appearance: sequence
+ *     order, then table order) gets one host block that takes over their
+ *     references; a block also referenced by a sequence outside the list
+ *     keeps those references (the host copy belongs to the listed
+ *     sequences), any other block is released (to the free list, or the idle
+ *     cache if it is cached).  Their tables then hold host ids.
+ *     pairs_out receives (device block, host block) per distinct block: copy
+ *     them device -> host before any later work reuses the released blocks.
+ *   - pa_bm_swap_in brings the listed swapped sequences back into fresh
+ *     device blocks (may evict idle cached blocks); pairs_out receives
+ *     (host block, device block): copy them host -> device before the
+ *     sequences are decoded.  Sharing among the listed sequences is kept.
+ *   - both are all-or-nothing; a sequence listed twice, or in the wrong state,
+ *     is PA_ERR_INVALID_ARG; more pairs than cap is PA_ERR_INVALID_ARG with
+ *     *num_pairs = the number needed; nothing changes on any error.
+ *   - a swapped sequence cannot be appended to, forked, batched or grouped
+ *     (PA_ERR_INVALID_ARG); pa_bm_free_seq returns its host blocks;
+ *     pa_bm_block_table returns its host ids.
+ */
+
+/* A host pool of num_host_blocks blocks (once).  pop_order (nullable, host)
+ * fixes the hand-out order as in pa_bm_create. */
+int pa_bm_enable_host_pool(pa_bm* bm, int num_host_blocks, const int32_t* pop_order);
+int pa_bm_swap_out(pa_bm* bm, const int64_t* seqs, int n, int32_t* pairs_out, int cap, int* num_pairs);
+int pa_bm_swap_in(pa_bm* bm, const int64_t* seqs, int n, int32_t* pairs_out, int cap, int* num_pairs);
+/* Swapped sequences, free host blocks, host blocks in the pool. */
+int pa_bm_swap_stats(pa_bm* bm, int64_t* num_swapped, int64_t* host_free, int64_t* host_blocks);
+
 /* Reference count of a block (-1 for an id outside the pool). */
 int pa_bm_refcount(pa_bm* bm, int block);
 /* Number of blocks on the free list (idle cached blocks not included). */

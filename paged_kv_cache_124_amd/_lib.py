@@ -99,6 +99,10 @@ _SIGS = {
     "pa_bm_append_tokens": (c_int, [c_void_p, _P64, _P32, c_int, _P32, _P32, POINTER(c_int)]),
     "pa_bm_cache_stats": (c_int, [c_void_p, POINTER(BMCacheStats)]),
     "pa_bm_idle_list": (c_int, [c_void_p, _P32, c_int, POINTER(c_int)]),
+    "pa_bm_enable_host_pool": (c_int, [c_void_p, c_int, _P32]),
+    "pa_bm_swap_out": (c_int, [c_void_p, _P64, c_int, _P32, c_int, POINTER(c_int)]),
+    "pa_bm_swap_in": (c_int, [c_void_p, _P64, c_int, _P32, c_int, POINTER(c_int)]),
+    "pa_bm_swap_stats": (c_int, [c_void_p, _P64, _P64, _P64]),
     "pa_bm_refcount": (c_int, [c_void_p, c_int]),
     "pa_bm_num_free": (c_int, [c_void_p]),
     "pa_bm_seq_len": (c_int64, [c_void_p, c_int64]),
@@ -642,6 +646,32 @@ class BlockManager:
         out = np.empty(cap, dtype=np.int32)
         st = lib.pa_bm_idle_list(self._h, _ptr32(out), cap, ctypes.byref(n))
         return out[: n.value].tolist() if st == PA_OK else []
+
+    def enable_host_pool(self, num_host_blocks: int, pop_order=None) -> int:
+        order = None if pop_order is None else _i32(pop_order)
+        return lib.pa_bm_enable_host_pool(self._h, num_host_blocks, None if order is None else _ptr32(order))
+
+    def _swap(self, fn, seqs):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        cap = max(sum(self.block_table(int(x))[1].__len__() for x in s), 1)
+        pairs = np.empty((cap, 2), dtype=np.int32)
+        npairs = c_int()
+        st = fn(self._h, s.ctypes.data_as(_P64), n, _ptr32(pairs), cap, ctypes.byref(npairs))
+        return st, pairs[: npairs.value].copy() if st == PA_OK else np.zeros((0, 2), dtype=np.int32)
+
+    def swap_out(self, seqs):
+        """(status, int32 [P][2] (device block, host block)) of pa_bm_swap_out."""
+        return self._swap(lib.pa_bm_swap_out, seqs)
+
+    def swap_in(self, seqs):
+        """(status, int32 [P][2] (host block, device block)) of pa_bm_swap_in."""
+        return self._swap(lib.pa_bm_swap_in, seqs)
+
+    def swap_stats(self):
+        a, b, c = c_int64(), c_int64(), c_int64()
+        _check(lib.pa_bm_swap_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "pa_bm_swap_stats")
+        return {"num_swapped": a.value, "host_free": b.value, "host_blocks": c.value}
 
     @property
     def handle(self):

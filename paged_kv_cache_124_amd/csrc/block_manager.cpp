@@ -33,6 +33,7 @@ struct Seq {
   std::vector<int32_t> pending;
   uint64_t chain = 0;
   bool known = false;
+  bool swapped = false;  // the table holds host block ids
 };
 
 // Chain hash of a full block: its B token ids after the chain hash of the
@@ -81,6 +82,11 @@ struct pa_bm {
   std::vector<int32_t> idle_prev, idle_next;
   int32_t idle_head = -1, idle_tail = -1;
   int64_t idle_count = 0, hit_blocks = 0, evictions = 0;
+
+  // ---- host pool for swapped-out sequences ---------------------------------
+  std::vector<int32_t> host_free;  // top = back()
+  std::vector<int32_t> host_ref;
+  int64_t num_swapped = 0;
 
   int64_t available() const { return static_cast<int64_t>(free_stack.size()) + (caching ? idle_count : 0); }
 
@@ -172,6 +178,7 @@ struct pa_bm {
     auto it = seqs.find(id);
     if (it == seqs.end()) return PA_ERR_NOT_FOUND;
     Seq& s = it->second;
+    if (s.swapped) return PA_ERR_INVALID_ARG;
     const int32_t off = static_cast<int32_t>(s.len % block_size);
     int32_t block;
     if (off != 0) {
@@ -319,6 +326,7 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
   if (bm->seqs.count(child)) return PA_ERR_EXISTS;
+  if (it->second.swapped) return PA_ERR_INVALID_ARG;
   Seq s = it->second;  // copy of the table; no data moves
   for (int32_t b : s.table) bm->ref[b] += 1;
   bm->seqs.emplace(child, std::move(s));
@@ -341,9 +349,9 @@ static int append_batch_cached(pa_bm* bm, const int64_t* seqs, const int32_t* to
   std::vector<Seq*> rows(n);
   for (int i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seqs[i]);
-    if (it == bm->seqs.end()) {
+    if (it == bm->seqs.end() || it->second.swapped) {
       *num_pairs = -i - 1;
-      return PA_ERR_NOT_FOUND;
+      return it == bm->seqs.end() ? PA_ERR_NOT_FOUND : PA_ERR_INVALID_ARG;
     }
     rows[i] = &it->second;
   }
@@ -423,7 +431,11 @@ int pa_bm_free_seq(pa_bm* bm, int64_t seq) {
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
   const std::vector<int32_t>& t = it->second.table;
-  if (bm->caching) {  // last block first: a sequence's deepest blocks become the oldest idle entries
+  if (it->second.swapped) {  // host blocks
+    for (int32_t hb : t)
+      if (--bm->host_ref[hb] == 0) bm->host_free.push_back(hb);
+    --bm->num_swapped;
+  } else if (bm->caching) {  // last block first: a sequence's deepest blocks become the oldest idle entries
     for (auto b = t.rbegin(); b != t.rend(); ++b)
       if (--bm->ref[*b] == 0) bm->release(*b);
   } else {
@@ -442,6 +454,7 @@ int pa_bm_build_batch(pa_bm* bm, const int64_t* seqs, int n, int max_blocks_per_
   for (int i = 0; i < n; ++i) {  // validate everything before writing anything
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+    if (it->second.swapped) return PA_ERR_INVALID_ARG;
     if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq) return PA_ERR_INVALID_ARG;
     if (it->second.len > INT32_MAX) return PA_ERR_INVALID_ARG;
   }
@@ -464,6 +477,7 @@ int pa_bm_shared_groups(pa_bm* bm, const int64_t* seqs, int n, int max_members, 
   for (int i = 0; i < n; ++i) {  // validate everything before writing anything
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+    if (it->second.swapped) return PA_ERR_INVALID_ARG;
     rows[i] = &it->second;
   }
   const int64_t B = bm->block_size;
@@ -553,6 +567,7 @@ int pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
   std::vector<int32_t> fill(bm->num_blocks, 0);
   for (const auto& kv : bm->seqs) {
     const Seq& s = kv.second;
+    if (s.swapped) continue;  // host blocks are not part of the device pool
     for (size_t lb = 0; lb < s.table.size(); ++lb) {
       const int64_t valid = s.len - static_cast<int64_t>(lb) * bm->block_size;
       const int32_t v = static_cast<int32_t>(valid < bm->block_size ? valid : bm->block_size);
@@ -572,6 +587,119 @@ int pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
   out->cow_copies = bm->cow_copies;
   out->stored_tokens = stored;
   out->tail_waste_slots = used * bm->block_size - stored;
+  return PA_OK;
+}
+
+int pa_bm_enable_host_pool(pa_bm* bm, int num_host_blocks, const int32_t* pop_order) {
+  if (!bm || num_host_blocks <= 0 || !bm->host_ref.empty()) return PA_ERR_INVALID_ARG;
+  std::vector<int32_t> stack(num_host_blocks);
+  if (pop_order) {
+    std::vector<uint8_t> seen(num_host_blocks, 0);
+    for (int i = 0; i < num_host_blocks; ++i) {
+      const int32_t b = pop_order[i];
+      if (b < 0 || b >= num_host_blocks || seen[b]) return PA_ERR_INVALID_ARG;
+      seen[b] = 1;
+      stack[num_host_blocks - 1 - i] = b;  // first entry ends on top
+    }
+  } else {
+    for (int i = 0; i < num_host_blocks; ++i) stack[i] = num_host_blocks - 1 - i;
+  }
+  bm->host_free = std::move(stack);
+  bm->host_ref.assign(num_host_blocks, 0);
+  return PA_OK;
+}
+
+// The listed sequences' distinct blocks in order of first appearance
+// (sequence order, then table order), with the references they hold.
+static int swap_prepare(pa_bm* bm, const int64_t* seqs, int n, bool want_swapped, std::vector<Seq*>& rows,
+                        std::vector<int32_t>& blocks, std::vector<int32_t>& counts) {
+  if (bm->host_ref.empty()) return PA_ERR_INVALID_ARG;
+  std::unordered_map<int64_t, int> ids;
+  rows.resize(n);
+  for (int i = 0; i < n; ++i) {
+    if (!ids.emplace(seqs[i], i).second) return PA_ERR_INVALID_ARG;  // listed twice
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+    if (it->second.swapped != want_swapped) return PA_ERR_INVALID_ARG;
+    rows[i] = &it->second;
+  }
+  std::unordered_map<int32_t, int32_t> pos;
+  for (Seq* s : rows)
+    for (int32_t b : s->table) {
+      auto r = pos.emplace(b, static_cast<int32_t>(blocks.size()));
+      if (r.second) {
+        blocks.push_back(b);
+        counts.push_back(0);
+      }
+      ++counts[r.first->second];
+    }
+  return PA_OK;
+}
+
+int pa_bm_swap_out(pa_bm* bm, const int64_t* seqs, int n, int32_t* pairs_out, int cap, int* num_pairs) {
+  if (!bm || n < 0 || (n > 0 && !seqs) || cap < 0 || !num_pairs) return PA_ERR_INVALID_ARG;
+  std::vector<Seq*> rows;
+  std::vector<int32_t> blocks, counts;
+  int st = swap_prepare(bm, seqs, n, false, rows, blocks, counts);
+  if (st != PA_OK) return st;
+  const int need = static_cast<int>(blocks.size());
+  *num_pairs = need;
+  if (need > cap || (need > 0 && !pairs_out)) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(bm->host_free.size()) < need) return PA_ERR_NO_FREE_BLOCKS;
+  std::unordered_map<int32_t, int32_t> where;
+  for (int k = 0; k < need; ++k) {
+    const int32_t b = blocks[k];
+    const int32_t hb = bm->host_free.back();
+    bm->host_free.pop_back();
+    bm->host_ref[hb] = counts[k];
+    bm->ref[b] -= counts[k];
+    if (bm->ref[b] == 0) bm->release(b);  // other holders keep the device block
+    pairs_out[2 * k] = b;
+    pairs_out[2 * k + 1] = hb;
+    where[b] = hb;
+  }
+  for (Seq* s : rows) {
+    for (int32_t& b : s->table) b = where[b];
+    s->swapped = true;
+  }
+  bm->num_swapped += n;
+  return PA_OK;
+}
+
+int pa_bm_swap_in(pa_bm* bm, const int64_t* seqs, int n, int32_t* pairs_out, int cap, int* num_pairs) {
+  if (!bm || n < 0 || (n > 0 && !seqs) || cap < 0 || !num_pairs) return PA_ERR_INVALID_ARG;
+  std::vector<Seq*> rows;
+  std::vector<int32_t> blocks, counts;
+  int st = swap_prepare(bm, seqs, n, true, rows, blocks, counts);
+  if (st != PA_OK) return st;
+  const int need = static_cast<int>(blocks.size());
+  *num_pairs = need;
+  if (need > cap || (need > 0 && !pairs_out)) return PA_ERR_INVALID_ARG;
+  if (bm->available() < need) return PA_ERR_NO_FREE_BLOCKS;
+  std::unordered_map<int32_t, int32_t> where;
+  for (int k = 0; k < need; ++k) {
+    const int32_t hb = blocks[k];
+    const int32_t b = bm->pop();
+    bm->ref[b] = counts[k];
+    bm->host_ref[hb] -= counts[k];
+    if (bm->host_ref[hb] == 0) bm->host_free.push_back(hb);
+    pairs_out[2 * k] = hb;
+    pairs_out[2 * k + 1] = b;
+    where[hb] = b;
+  }
+  for (Seq* s : rows) {
+    for (int32_t& hb : s->table) hb = where[hb];
+    s->swapped = false;
+  }
+  bm->num_swapped -= n;
+  return PA_OK;
+}
+
+int pa_bm_swap_stats(pa_bm* bm, int64_t* num_swapped, int64_t* host_free, int64_t* host_blocks) {
+  if (!bm || !num_swapped || !host_free || !host_blocks) return PA_ERR_INVALID_ARG;
+  *num_swapped = bm->num_swapped;
+  *host_free = static_cast<int64_t>(bm->host_free.size());
+  *host_blocks = static_cast<int64_t>(bm->host_ref.size());
   return PA_OK;
 }
 

@@ -314,3 +314,80 @@ def test_prefix_cache_matches_the_oracle_model(pa, seed):
             live.remove(s)
             assert bm.free_seq(s) == m.free_seq(s) == 0
         _same(bm, m, live)
+
+
+# ---- swapping ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(20))
+def test_swapping_matches_the_oracle_model(pa, seed):
+    """Random traces of add, fork, append, swap-out / swap-in of groups and release, with and without the
+    prefix cache: after every operation the C++ manager and the oracle model agree on tables (host ids for
+    swapped sequences), swap pairs, reference counts, free and idle lists and counters."""
+    from oracle.block_manager import BlockManagerModel, PrefixCachingModel
+    rng = random.Random(1300 + seed)
+    B = rng.choice([4, 8, 16])
+    nb, nh = rng.randint(12, 48), rng.randint(8, 48)
+    order = rng.sample(range(nb), nb)
+    horder = rng.sample(range(nh), nh)
+    cached = seed % 2 == 1
+    bm = pa.BlockManager(nb, B, order)
+    m = (PrefixCachingModel if cached else BlockManagerModel)(nb, B, order)
+    if cached:
+        assert bm.enable_prefix_cache() == 0
+    assert bm.enable_host_pool(nh, horder) == 0 and m.enable_host_pool(nh, horder) == 0
+    live, nid = [], 0
+    for step in range(160):
+        op = rng.random()
+        resident = [s for s in live if s not in m.swapped]
+        swapped = [s for s in live if s in m.swapped]
+        if op < 0.2:
+            n = rng.randint(1, 4 * B)
+            if cached and rng.random() < 0.6:
+                toks = [rng.randrange(3) for _ in range(n)]
+                r = bm.add_seq_tokens(nid, toks)
+                assert r == m.add_seq_tokens(nid, toks)
+                st = r[0]
+            else:
+                st = bm.add_seq(nid, n)
+                assert st == m.add_seq(nid, n)
+            if st == 0:
+                live.append(nid)
+            nid += 1
+        elif op < 0.3 and live:
+            p = rng.choice(live)
+            st = bm.fork(p, nid)
+            assert st == m.fork(p, nid)
+            if st == 0:
+                live.append(nid)
+                nid += 1
+        elif op < 0.55 and live:
+            seqs = rng.sample(live, rng.randint(1, min(4, len(live))))
+            st, slots, pairs, failed = bm.append_slots(seqs)
+            mst, mslots, mpairs, mfailed = m.append_slots(seqs)
+            assert st == mst and failed == mfailed
+            assert list(slots) == mslots and [tuple(x) for x in pairs] == mpairs
+        elif op < 0.7 and live:
+            group = rng.sample(live, rng.randint(1, min(3, len(live))))
+            st, pairs = bm.swap_out(group)
+            mst, mpairs = m.swap_out(group)
+            assert st == mst and [tuple(x) for x in pairs] == mpairs
+        elif op < 0.85 and live:
+            group = rng.sample(live, rng.randint(1, min(3, len(live))))
+            st, pairs = bm.swap_in(group)
+            mst, mpairs = m.swap_in(group)
+            assert st == mst and [tuple(x) for x in pairs] == mpairs
+        elif live:
+            s = rng.choice(live)
+            live.remove(s)
+            assert bm.free_seq(s) == m.free_seq(s) == 0
+        for s in live:
+            assert bm.block_table(s)[1] == m.tables[s], f"step {step}"
+        assert [bm.refcount(b) for b in range(nb)] == m.ref
+        assert bm.free_list() == m.pop_order()
+        assert bm.swap_stats() == m.swap_stats()
+        if cached:
+            assert bm.idle_list() == m.idle
+        s = bm.stats()
+        ms = m.stats()
+        assert (s["num_used"], s["num_free"], s["stored_tokens"]) == (ms["num_used"], ms["num_free"],
+                                                                       ms["stored_tokens"])
