@@ -345,6 +345,39 @@ int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scal
                        int num_pairs, int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
                        int64_t layer_stride_elems, int64_t scale_layer_stride, void* stream);
 
+/* ---- swapping blocks between pools ----------------------------------------------
+ *
+ * pa_swap_blocks: preemption by swapping ("PagedAttention: Virtual Memory for
+ * the KV Cache", section 19) moves whole blocks between the device pool and a
+ * host pool.  For each pair (src, dst) of src_dst_pairs (int32 [num_pairs][2],
+ * device-readable), block src of the source pools is copied to block dst of
+ * the destination pools, K and V, in each of num_layers layers; bit-exact.
+ * Both pools have the device pool's per-block layout (see the top of this
+ * file); each is device memory or pinned host memory mapped for the device
+ * (pass the device pointer of the mapping), so one call moves a batch of
+ * scattered blocks over PCIe with no staging.  Use the pairs pa_bm_swap_out
+ * (device -> host) or pa_bm_swap_in (host -> device) returns, on the stream
+ * that runs the decode, before the released blocks are reused / before the
+ * swapped-in sequences are decoded.
+ *   src_num_blocks / dst_num_blocks  blocks in one layer of each pool (a pair
+ *                     outside them is skipped)
+ *   *_layer_stride_elems  elements between layers of each pool (ignored when
+ *                     num_layers == 1)
+ *   dtype             PA_F32 or PA_BF16; pa_swap_blocks_fp8 moves FP8 codes
+ *                     and their per-(block, KV head) key and value scales
+ *                     (scale strides in floats).
+ * Argument errors as for pa_copy_blocks. */
+int pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_pool, const void* src_v_pool,
+                   const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size, int dtype,
+                   int src_num_blocks, int dst_num_blocks, int num_layers, int64_t src_layer_stride_elems,
+                   int64_t dst_layer_stride_elems, void* stream);
+int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
+                       const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
+                       const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head,
+                       int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
+                       int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, int64_t src_scale_layer_stride,
+                       int64_t dst_scale_layer_stride, void* stream);
+
 /* ---- host block manager ------------------------------------------------------
  *
  * Free list, per-block reference counts, block tables, fork and copy-on-write

@@ -39,5 +39,8 @@ from ._lib import (  # noqa: F401
     pa_decode_step_shared,
     pa_decode_step_shared_args,
     pa_decode_workspace_bytes,
+    pa_swap_blocks,
+    pa_swap_blocks_fp8,
+    host_device_pointer,
     pool_shapes,
 )

@@ -85,6 +85,8 @@ _SIGS = {
     "pa_append_kv_fp8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
     "pa_copy_blocks_fp8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
     "pa_append_step_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
+    "pa_swap_blocks": (c_int, [c_void_p] * 5 + [c_int] * 8 + [c_int64, c_int64, c_void_p]),
+    "pa_swap_blocks_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
     "pa_bm_create": (c_void_p, [c_int, c_int, _P32]),
     "pa_bm_destroy": (None, [c_void_p]),
     "pa_bm_add_seq": (c_int, [c_void_p, c_int64, c_int]),
@@ -415,6 +417,76 @@ def pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream=None):
 def pa_copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
     """pa_copy_blocks of include/pa.h."""
     _check(lib.pa_copy_blocks(*pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream)), "pa_copy_blocks")
+
+
+# ---------------------------------------------------------------------------
+# swapping: blocks between the device pool and a pinned host pool
+# ---------------------------------------------------------------------------
+
+_HIP = None
+
+
+def host_device_pointer(t) -> int:
+    """Device address of a pinned host tensor's memory (hipHostGetDevicePointer), for kernels that read or write
+    it over PCIe."""
+    global _HIP
+    if not t.is_pinned():
+        raise ValueError("host pools must be pinned (torch.empty(..., pin_memory=True))")
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded
+    dp = c_void_p()
+    if _HIP.hipHostGetDevicePointer(ctypes.byref(dp), c_void_p(t.data_ptr()), 0) != 0 or not dp.value:
+        raise PAError(PA_ERR_HIP, "hipHostGetDevicePointer")
+    return dp.value
+
+
+def _pool_ptr(t, name):
+    """Device pointer of a pool: a device tensor's data, or the mapping of a pinned host tensor."""
+    if t.is_cuda:
+        return _dev(t, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return c_void_p(host_device_pointer(t))
+
+
+def _layers(k_pool):
+    """(layers, blocks per layer, elements per layer) of a one-layer [nb]... or layered [L][nb]... K pool."""
+    if k_pool.dim() == 6:
+        return k_pool.shape[0], k_pool.shape[1], k_pool[0].numel()
+    return 1, k_pool.shape[0], k_pool.numel()
+
+
+def pa_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None):
+    """pa_swap_blocks of include/pa.h.  Pools: device tensors or pinned host tensors of the library layout,
+    one layer [nb]... or layered [L][nb]...; pairs: int32 [P][2] device tensor (src block, dst block)."""
+    import torch
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [P][2]")
+    ls, nbs, es = _layers(src_k)
+    ld, nbd, ed = _layers(dst_k)
+    if ls != ld or src_k.dtype != dst_k.dtype:
+        raise ValueError("pools disagree in layers or element type")
+    kl = src_k[0] if src_k.dim() == 6 else src_k
+    vl = src_v[0] if src_v.dim() == 5 else src_v
+    _, hkv, d, bs = _pool_dims(kl, vl)
+    _check(lib.pa_swap_blocks(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), _pool_ptr(src_k, "src_k"),
+                              _pool_ptr(src_v, "src_v"), _dev(pairs, "pairs") if pairs.shape[0] else c_void_p(0),
+                              pairs.shape[0], hkv, d, bs, _dtype_code(src_k), nbs, nbd, ls, es, ed,
+                              _stream_ptr(stream)), "pa_swap_blocks")
+
+
+def pa_swap_blocks_fp8(dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream=None):
+    """pa_swap_blocks_fp8 of include/pa.h (one-layer FP8 pools with their [nb][Hkv] scales)."""
+    import torch
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [P][2]")
+    _, hkv, d, bs = _fp8_pools(src_k, src_v)
+    _check(lib.pa_swap_blocks_fp8(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), _pool_ptr(dst_ks, "dst_ks"),
+                                  _pool_ptr(dst_vs, "dst_vs"), _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"),
+                                  _pool_ptr(src_ks, "src_ks"), _pool_ptr(src_vs, "src_vs"),
+                                  _dev(pairs, "pairs") if pairs.shape[0] else c_void_p(0), pairs.shape[0], hkv, d, bs,
+                                  src_k.shape[0], dst_k.shape[0], 1, 0, 0, 0, 0, _stream_ptr(stream)),
+           "pa_swap_blocks_fp8")
 
 
 # ---------------------------------------------------------------------------

@@ -209,6 +209,41 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
   *t = *s;
 }
 
+// Block images between two pools (preemption by swapping, "PagedAttention:
+// Virtual Memory for the KV Cache", section 19): pair (src, dst) copies block
+// src of the source pool to block dst of the destination pool, in every
+// layer.  Either pool may be device memory or pinned host memory mapped for
+// the device (then each 16-byte access crosses PCIe).
+// grid = (ceil((2 * n16 + 2 * scales_per_block) / 256), num_pairs, num_layers).
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, const uint8_t* __restrict__ src_k,
+    const uint8_t* __restrict__ src_v, const int32_t* __restrict__ pairs, int64_t block_bytes, int src_blocks,
+    int dst_blocks, int64_t src_layer_bytes, int64_t dst_layer_bytes, float* __restrict__ dst_ks,
+    float* __restrict__ dst_vs, const float* __restrict__ src_ks, const float* __restrict__ src_vs,
+    int scales_per_block, int64_t src_scale_layer, int64_t dst_scale_layer) {
+  const int64_t n16 = block_bytes / 16;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= 2 * n16 + 2 * scales_per_block) return;
+  const int32_t src = pairs[2 * blockIdx.y];
+  const int32_t dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const int64_t layer = blockIdx.z;
+  if (idx >= 2 * n16) {
+    const int64_t i = idx - 2 * n16;
+    const bool key = i < scales_per_block;
+    const int64_t h = key ? i : i - scales_per_block;
+    const float* ss = (key ? src_ks : src_vs) + layer * src_scale_layer;
+    float* ds = (key ? dst_ks : dst_vs) + layer * dst_scale_layer;
+    ds[static_cast<int64_t>(dst) * scales_per_block + h] = ss[static_cast<int64_t>(src) * scales_per_block + h];
+    return;
+  }
+  const bool key = idx < n16;
+  const int64_t i = key ? idx : idx - n16;
+  const uint4* sp = reinterpret_cast<const uint4*>((key ? src_k : src_v) + layer * src_layer_bytes + src * block_bytes);
+  uint4* dp = reinterpret_cast<uint4*>((key ? dst_k : dst_v) + layer * dst_layer_bytes + dst * block_bytes);
+  dp[i] = sp[i];
+}
+
 bool shape_ok(int hkv, int d, int block_size, int dtype) {
   return hkv > 0 && (d == 64 || d == 128) && (block_size == 8 || block_size == 16 || block_size == 32) &&
          (dtype == PA_F32 || dtype == PA_BF16);
@@ -362,4 +397,64 @@ extern "C" int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, fl
       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), src_dst_pairs, block_bytes, num_blocks,
       num_layers > 1 ? layer_stride_elems : 0, k_scale, v_scale, Hkv, num_layers > 1 ? scale_layer_stride : 0);
   return launch_status();
+}
+
+namespace {
+int swap_impl(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs, int num_pairs,
+              int Hkv, int d_head, int block_size, int elem, int src_blocks, int dst_blocks, int num_layers,
+              int64_t src_layer_elems, int64_t dst_layer_elems, float* dst_ks, float* dst_vs, const float* src_ks,
+              const float* src_vs, int64_t src_scale_layer, int64_t dst_scale_layer, void* stream) {
+  using namespace pa;
+  if (num_pairs < 0 || src_blocks < 0 || dst_blocks < 0 || num_layers <= 0 || Hkv <= 0 || d_head <= 0 ||
+      block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!(d_head == 64 || d_head == 128) || !(block_size == 8 || block_size == 16 || block_size == 32))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return PA_ERR_INVALID_ARG;
+  if (num_pairs > 65535 || num_layers > 65535) return PA_ERR_UNSUPPORTED;
+  const int64_t block_elems = static_cast<int64_t>(Hkv) * d_head * block_size;
+  const int64_t block_bytes = block_elems * elem;
+  if (num_layers > 1 && (src_layer_elems < static_cast<int64_t>(src_blocks) * block_elems ||
+                         dst_layer_elems < static_cast<int64_t>(dst_blocks) * block_elems))
+    return PA_ERR_INVALID_ARG;
+  const bool scales = src_ks != nullptr;
+  if (scales && num_layers > 1 &&
+      (src_scale_layer < static_cast<int64_t>(src_blocks) * Hkv || dst_scale_layer < static_cast<int64_t>(dst_blocks) * Hkv))
+    return PA_ERR_INVALID_ARG;
+  const int spb = scales ? Hkv : 0;
+  const int64_t gx = (2 * (block_bytes / 16) + 2 * spb + 255) / 256;
+  swap_blocks_kernel<<<dim3(static_cast<uint32_t>(gx), num_pairs, num_layers), dim3(256), 0,
+                       static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint8_t*>(dst_k), static_cast<uint8_t*>(dst_v), static_cast<const uint8_t*>(src_k),
+      static_cast<const uint8_t*>(src_v), pairs, block_bytes, src_blocks, dst_blocks,
+      num_layers > 1 ? src_layer_elems * elem : 0, num_layers > 1 ? dst_layer_elems * elem : 0, dst_ks, dst_vs, src_ks,
+      src_vs, spb, num_layers > 1 ? src_scale_layer : 0, num_layers > 1 ? dst_scale_layer : 0);
+  return launch_status();
+}
+}  // namespace
+
+extern "C" int pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_pool, const void* src_v_pool,
+                              const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size,
+                              int dtype, int src_num_blocks, int dst_num_blocks, int num_layers,
+                              int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, void* stream) {
+  using namespace pa;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  return swap_impl(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, src_dst_pairs, num_pairs, Hkv, d_head, block_size,
+                   elem_bytes(dtype), src_num_blocks, dst_num_blocks, num_layers, src_layer_stride_elems,
+                   dst_layer_stride_elems, nullptr, nullptr, nullptr, nullptr, 0, 0, stream);
+}
+
+extern "C" int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
+                                  const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
+                                  const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv,
+                                  int d_head, int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
+                                  int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems,
+                                  int64_t src_scale_layer_stride, int64_t dst_scale_layer_stride, void* stream) {
+  using namespace pa;
+  if (num_pairs > 0 && (!dst_k_scale || !dst_v_scale || !src_k_scale || !src_v_scale)) return PA_ERR_INVALID_ARG;
+  return swap_impl(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, src_dst_pairs, num_pairs, Hkv, d_head, block_size,
+                   1, src_num_blocks, dst_num_blocks, num_layers, src_layer_stride_elems, dst_layer_stride_elems,
+                   dst_k_scale, dst_v_scale, src_k_scale, src_v_scale, src_scale_layer_stride, dst_scale_layer_stride,
+                   stream);
 }
