@@ -81,7 +81,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa8b", choices=["gqa8b", "sweep_b8", "sweep_b16", "sweep_b32", "fork"])
+    ap.add_argument("--workload", default="gqa8b",
+                    choices=["gqa8b", "sweep_b8", "sweep_b16", "sweep_b32", "fork", "long"])
     ap.add_argument("--shared", action="store_true",
                     help="fork workload: decode with pa_decode_step_shared, each prompt's shared full blocks read "
                          "once per step for its samples (default: pa_decode_step)")
@@ -102,6 +103,8 @@ def workload(name):
         return synth.gqa8b()
     if name == "fork":
         return synth.fork()
+    if name == "long":
+        return synth.long()
     return synth.sweep(int(name.split("_b")[1]))
 
 
@@ -311,6 +314,87 @@ class Runner:
             raise RuntimeError("device block tables / lengths diverged from the block manager")
 
 
+class LongRunner:
+    """The 32-layer long-context step: 16 sequences of 32,768 tokens, 64 GiB of KV in one allocation per tensor.
+
+    One step appends each sequence's new token in every layer (pa_append_step on layer 0 stores it and moves the
+    device-resident rows forward; pa_append_kv stores it in layers 1..31 at the same slots) and then decodes every
+    layer over S + 1 tokens.  The block manager's slots for all steps are computed before the timed region.
+    """
+
+    def __init__(self, w, steps_total, device="cuda"):
+        import torch
+        import synth
+        import paged_kv_cache_124_amd as pa
+        self.pa, self.w = pa, w
+        self.lens0 = synth.seq_lengths(w)
+        self.n = len(self.lens0)
+        bs, L = w.block_size, w.layers
+        extra = self.n * (steps_total // bs + 2)
+        self.num_blocks = synth.pool_blocks(w, self.lens0, extra=extra)
+        self.max_ctx = max(self.lens0) + steps_total
+        self.max_blocks = -(-self.max_ctx // bs)
+        bm = pa.BlockManager(self.num_blocks, bs, synth.pop_order(self.num_blocks, w.seed))
+        self.bm = bm
+        for i, s_ in enumerate(self.lens0):
+            assert bm.add_seq(i, s_) == 0
+        seqs = np.arange(self.n, dtype=np.int64)
+        st, tables, lens = bm.build_batch(seqs, self.max_blocks)
+        assert st == 0
+        slots = []
+        for _ in range(steps_total):
+            st, sl, pairs, _ = bm.append_slots(seqs)
+            assert st == 0 and len(pairs) == 0
+            slots.append(sl.copy())
+        self.slots = torch.from_numpy(np.stack(slots).astype(np.int32)).to(device)
+        kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, 2)
+        self.k = synth.fill_randn_(torch.empty((L,) + kshape, dtype=torch.bfloat16, device=device), w.value_scale,
+                                   w.seed * 10 + 1)
+        self.v = synth.fill_randn_(torch.empty((L,) + vshape, dtype=torch.bfloat16, device=device), w.value_scale,
+                                   w.seed * 10 + 2)
+        self.q = synth.randn((L, self.n, w.hq, w.d), torch.bfloat16, w.value_scale, w.seed * 10 + 3, device)
+        self.kn = synth.randn((L, self.n, w.hkv, w.d), torch.bfloat16, w.value_scale, w.seed * 10 + 4, device)
+        self.vn = synth.randn((L, self.n, w.hkv, w.d), torch.bfloat16, w.value_scale, w.seed * 10 + 5, device)
+        self.out = torch.empty_like(self.q)
+        self.d_tables = torch.from_numpy(tables).to(device)
+        self.d_lens = torch.from_numpy(lens).to(device)
+        ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
+        self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)
+        self.dec_args = [pa.pa_decode_args(self.out[l], self.q[l], self.k[l], self.v[l], self.d_tables, self.d_lens,
+                                           w.scale, self.max_ctx, workspace=self.ws)[0] for l in range(L)]
+        self.step_i = 0
+        self.lens = np.array(self.lens0, dtype=np.int64)
+        self.kv_bytes_per_token = 2 * w.hkv * w.d * 2 * L
+        self.host_s = 0.0
+        self.zero_copy = False
+        self.fork = False
+        self.part = pa.pa_decode_partition_tokens(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
+
+    def step(self, timing=None):
+        pa, w, L = self.pa, self.w, self.w.layers
+        sl = self.slots[self.step_i]
+        pa.pa_append_step(self.k[0], self.v[0], self.kn[0], self.vn[0], sl, self.d_tables, self.d_lens)
+        for l in range(1, L):
+            pa.pa_append_kv(self.k[l], self.v[l], self.kn[l], self.vn[l], sl)
+        if timing is not None:
+            timing[0].record()
+        for l in range(L):
+            assert pa.lib.pa_decode(*self.dec_args[l]) == 0
+        if timing is not None:
+            timing[1].record()
+        self.step_i += 1
+        self.lens += 1
+        return int(self.lens.sum()) * self.kv_bytes_per_token
+
+    def check_device_batch(self):
+        st, tables, lens = self.bm.build_batch(np.arange(self.n, dtype=np.int64), self.max_blocks)
+        assert st == 0
+        got_lens = self.d_lens.cpu().numpy()
+        want = np.array(self.lens0) + self.step_i
+        if not np.array_equal(got_lens, want):
+            raise RuntimeError("device lengths diverged from the block manager's")
+
+
 def cpu_baseline(w, seconds, kv_kind="bf16"):
     """The fp64 oracle on this host's cores over a bounded sample of the same workload (one BLAS thread).
 
@@ -326,6 +410,8 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
     from oracle import fp8 as OF
     fp8 = kv_kind == "fp8"
     lens = synth.seq_lengths(w)
+    if w.name == "long":
+        lens = lens[:2]  # one layer of two 32,768-token sequences (the oracle holds them in host memory)
     rng = np.random.default_rng(0)
     bs, hkv, d = w.block_size, w.hkv, w.d
     inputs = []
@@ -365,7 +451,8 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
             t_total += time.perf_counter() - t0
             passes += 1
     return {"value": round(passes * step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} passes over one decode step of all {len(lens)} sequences of the same workload "
+            "sample": f"{passes} passes over one decode step of {'one layer of ' if w.name == 'long' else ''}"
+                      f"{'the first' if w.name == 'long' else 'all'} {len(lens)} sequences of the same workload "
                       f"({'FP8 cache, ' if fp8 else ''}all {w.hq} query heads; fp64 NumPy oracle, one thread), "
                       f"{t_total:.1f} s of compute",
             "us_per_step": round(t_total / passes * 1e6, 1)}
@@ -399,7 +486,13 @@ def main():
     if args.shared and (w.name != "fork" or args.kv != "bf16"):
         print("--shared applies to the bf16 fork workload", file=sys.stderr)
         sys.exit(2)
-    run = Runner(w, total, args.replicas, kv_kind=args.kv, shared=args.shared)
+    if w.name == "long":
+        if args.kv != "bf16" or args.shared:
+            print("the long workload runs the bf16 decode", file=sys.stderr)
+            sys.exit(2)
+        run = LongRunner(w, total)
+    else:
+        run = Runner(w, total, args.replicas, kv_kind=args.kv, shared=args.shared)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run.step()
@@ -409,7 +502,8 @@ def main():
     # pa_decode is bracketed by events on every EVENT_EVERY-th step (on the stream it is
     # launched on); an event record costs the stream a few microseconds, so not every
     # step carries them
-    sampled = list(range(0, args.steps, EVENT_EVERY))
+    long_ctx = w.name == "long"
+    sampled = list(range(0, args.steps, 1 if long_ctx else EVENT_EVERY))  # a long step is ~12 ms: events every step
     timing = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     torch.cuda.synchronize()
     run.host_s = 0.0
@@ -446,6 +540,11 @@ def main():
                          f"prompt), Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, block {w.block_size}, bf16, copy-on-write "
                          f"of the tails on the first step, contexts growing 1/step; decode "
                          f"{'pa_decode_step_shared (shared blocks read once per group)' if args.shared else 'pa_decode_step (every row reads its own table)'}")
+    elif long_ctx:
+        workload_desc = (f"long: {w.layers} layers x {run.n} seqs of {run.lens0[0]} tokens (64 GiB of KV in one "
+                         f"allocation per tensor), Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, block {w.block_size}, bf16, "
+                         f"random placement; a step appends each sequence's new token in every layer and decodes every "
+                         f"layer over S + 1 tokens, contexts growing 1/step")
     else:
         workload_desc = (f"{w.name}{'-fp8' if fp8 else ''}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, "
                          f"block {w.block_size}, {'FP8 E4M3 cache with per-(block, KV head) scales' if fp8 else 'bf16'}, "
@@ -465,17 +564,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_desc,
                    "num_seqs": run.n, "block_size": w.block_size, "pool_blocks": run.num_blocks,
-                   "pool_replicas": args.replicas, "partition_tokens": run.part,
+                   "pool_replicas": 1 if long_ctx else args.replicas, "partition_tokens": run.part,
                    "kv_bytes_per_step": int(bytes_per_launch), "us_per_step": round(ms_step * 1e3, 2),
                    "host_us_per_step": round(run.host_s / args.steps * 1e6, 2),
-                   "staging": "pinned host ring read by the kernels" if run.zero_copy else "pinned ring, in-stream copy",
+                   "staging": ("slots of every step on the device before the timed region" if long_ctx else
+                               "pinned host ring read by the kernels" if run.zero_copy else "pinned ring, in-stream copy"),
                    "tail_waste_slots": run.bm.stats()["tail_waste_slots"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),
                      "kernel": "pa_decode_fp8 (decode kernel + merge kernel)" if fp8 else
                                ("pa_decode_step_shared (shared-prefix decode kernel + merge/append kernel)"
-                                if args.shared else "pa_decode_step (decode kernel + merge/append kernel)"),
+                                if args.shared else
+                                (f"pa_decode x {w.layers} layers (decode kernel + merge kernel each)" if long_ctx
+                                 else "pa_decode_step (decode kernel + merge/append kernel)")),
                      "avg_us": round(dec_avg_us, 2), "launches_timed": len(dec_us)},
     }
     if run.fork:
