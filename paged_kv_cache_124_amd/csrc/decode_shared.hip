@@ -667,9 +667,14 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
       float val[8][E];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float* rk = pb[k] ? pb[k] + (row0 + h) * (D + 4) : rec;  // weighted by zero when missing
+        // a missing piece loads from any valid address and contributes zero
+        // (selected, not multiplied by zero: that address may hold NaN)
+        const float* rk = pb[k] ? pb[k] + (row0 + h) * (D + 4) : rec;
 #pragma unroll
-        for (int e = 0; e < E; ++e) val[k][e] = rk[4 + lane + 64 * e];
+        for (int e = 0; e < E; ++e) {
+          const float x = rk[4 + lane + 64 * e];
+          val[k][e] = pb[k] ? x : 0.f;
+        }
       }
       float mx = mine ? m_l : -INFINITY;
 #pragma unroll
@@ -722,9 +727,12 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
             const float* rk = k < c64 ? record(base + k, h) : nullptr;
             fk[i] = __shfl(f, k & 63);
             if (!rk) fk[i] = 0.f;
-            rk = rk ? rk : rec;  // any valid address; weighted by zero
+            const float* ra = rk ? rk : rec;  // any valid address; the value is replaced by zero
 #pragma unroll
-            for (int e = 0; e < E; ++e) val[i][e] = rk[4 + lane + 64 * e];
+            for (int e = 0; e < E; ++e) {
+              const float x = ra[4 + lane + 64 * e];
+              val[i][e] = rk ? x : 0.f;
+            }
           }
 #pragma unroll
           for (int i = 0; i < 8; ++i)
@@ -753,7 +761,6 @@ StreamPlan shared_plan(int num_seqs, int num_groups, int hq, int hkv, int d, int
   // a group unit has at most as many tiles as a sequence: size the grid as for
   // num_seqs + num_groups sequences
   StreamPlan p = stream_plan(num_seqs + num_groups, hq, hkv, d, block_size, max_ctx);
-  const int g = hq / hkv;
   const int64_t waves = static_cast<int64_t>(p.workgroups) * kSW;
   const auto round256 = [](size_t b) { return (b + 255) / 256 * 256; };
   // workspace: [step slots | 4 words per row for the merge | wave records]

@@ -421,6 +421,51 @@ __device__ __forceinline__ void append_row(const AppendArgs& ap, const RowToken<
   }
 }
 
+// One head's merge when the segment has at most KP pieces (2 <= cnt <= KP):
+// the maxima, sums and value rows of all pieces load together, in one memory
+// round trip.  Piece 0's record is at `first`, piece k >= 1's at
+// later + (k - 1) * stride; bit k of `present` says piece k exists (a range
+// can be empty when there are fewer tiles than waves).
+template <int D, int KP>
+__device__ __forceinline__ void merge_head_few(const float* __restrict__ first, const float* __restrict__ later,
+                                               int stride, uint64_t present, int cnt, uint16_t* o, int lane) {
+  constexpr int E = D / 64;  // output elements per lane
+  const bool mine = (present >> lane) & 1;
+  const float* ma = mine ? (lane == 0 ? first : later + (lane - 1) * stride) : first;
+  const float m_l = ma[0], z_l = ma[1];
+  float val[KP][E];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    // a missing piece loads from a valid address and contributes zero
+    // (selected, not multiplied by zero: that address may hold NaN)
+    const bool pk = k < cnt && ((present >> k) & 1);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float x = k == 0 ? first[4 + lane + 64 * e] : later[(pk ? (k - 1) * stride : 0) + 4 + lane + 64 * e];
+      val[k][e] = pk ? x : 0.f;
+    }
+  }
+  float mx = mine ? m_l : -INFINITY;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+  const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
+  float zz = mine ? f * z_l : 0.f;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+  float uu[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) uu[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const float fk = __shfl(f, k);  // zero for missing pieces
+#pragma unroll
+    for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
+  }
+  const float inv = 1.f / zz;
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+}
+
 // Combine the summary records of one segment cut by wave-range boundaries,
 // or write zeros for an empty sequence.  Unit n's tiles are prefix[n] ..
 // prefix[n + 1] - 1 of the n_units units; a wave's two record slots hold
@@ -456,41 +501,23 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
     const int slot = (v == v_lo && lo_second) ? 1 : 0;
     return rec + ((v * 2 + slot) * rows + h) * (D + 4);
   };
-  if (v_hi - v_lo < 8) {
-    // up to 8 pieces (the usual case): the maxima, sums and value rows of all
-    // pieces load together, in one memory round trip
+  if (v_hi - v_lo < 16) {
+    // Up to 16 pieces: one round trip.  The first piece is slot 1 of wave
+    // v_lo when the segment is not that wave's first piece; every later piece
+    // is slot 0 of its wave, and the slot-0 records of consecutive waves lie
+    // 2 rows (D + 4) floats apart.  A range is empty only when there are
+    // fewer tiles than waves.
     const int cnt = static_cast<int>(v_hi - v_lo + 1);
+    const bool has = lane < cnt && (sp.T >= sp.W || sp.start(v_lo + lane) != sp.start(v_lo + lane + 1));
+    const uint64_t present = __ballot(has);
+    const int stride = 2 * rows * (D + 4);
     for (int h = wave; h < g; h += 4) {
-      const float* mine = lane < cnt ? record(v_lo + lane, h) : nullptr;
-      const float* ml = mine ? mine : rec;  // any valid address; unused
-      const float m_l = ml[0], z_l = ml[1];
-      float val[8][E];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float* rk = k < cnt ? record(v_lo + k, h) : nullptr;
-        rk = rk ? rk : rec;  // weighted by zero below
-#pragma unroll
-        for (int e = 0; e < E; ++e) val[k][e] = rk[4 + lane + 64 * e];
-      }
-      float mx = mine ? m_l : -INFINITY;
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
-      const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
-      float zz = mine ? f * z_l : 0.f;
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
-      float uu[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) uu[e] = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float fk = __shfl(f, k);  // zero for k >= cnt and empty ranges
-#pragma unroll
-        for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
-      }
-      const float inv = 1.f / zz;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+      const float* first = rec + ((v_lo * 2 + (lo_second ? 1 : 0)) * rows + h) * (D + 4);
+      const float* later = rec + ((v_lo + 1) * 2 * rows + h) * (D + 4);
+      if (cnt <= 8)
+        merge_head_few<D, 8>(first, later, stride, present, cnt, o + h * D, lane);
+      else
+        merge_head_few<D, 16>(first, later, stride, present, cnt, o + h * D, lane);
     }
     return;
   }
@@ -521,9 +548,12 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
           const float* rk = k < cnt ? record(base + k, h) : nullptr;
           fk[i] = __shfl(f, k & 63);
           if (!rk) fk[i] = 0.f;
-          rk = rk ? rk : rec;  // any valid address; weighted by zero
+          const float* ra = rk ? rk : rec;  // any valid address; the value is replaced by zero
 #pragma unroll
-          for (int e = 0; e < E; ++e) val[i][e] = rk[4 + lane + 64 * e];
+          for (int e = 0; e < E; ++e) {
+            const float x = ra[4 + lane + 64 * e];
+            val[i][e] = rk ? x : 0.f;
+          }
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)

@@ -101,10 +101,14 @@ def test_forest_decode_matches_the_oracle(d, bs, hq, hkv):
     plain = torch.empty_like(case.q)
     pa.pa_decode(plain, case.q, case.k, case.v, case.tables_dev, case.lens_dev, case.scale, case.max_ctx)
     assert_close(plain, ref, "forest plain")
-    # run to run: the split and the merge order are fixed, so the bits repeat
-    out2 = torch.empty_like(case.q)
-    pa.pa_decode_shared(out2, case.q, case.k, case.v, case.tables_dev, case.lens_dev,
-                        torch.from_numpy(groups).cuda(), case.scale, case.max_ctx)
+    # run to run: the split and the merge order are fixed, so the bits repeat, also over a workspace whose
+    # every byte is 0xFF (NaN as floats): each word the call reads it writes first
+    out2 = torch.full_like(case.q, float("nan"))
+    args, ws = pa.pa_decode_shared_args(out2, case.q, case.k, case.v, case.tables_dev, case.lens_dev,
+                                        torch.from_numpy(groups).cuda(), case.scale, case.max_ctx)
+    ws.fill_(0xFF)
+    assert pa.lib.pa_decode_shared(*args) == 0
+    torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
