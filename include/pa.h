@@ -106,9 +106,9 @@ int pa_version(void);
  *   max_context_len an upper bound of all S (sizes the launch without a
  *                  device read)
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes; may be NULL when that size is 0.  Zero-fill it
- *                  before its first use (counters kept in it are returned to
- *                  zero by every call); calls that may overlap in time need
+ *                  bytes; may be NULL when that size is 0.  Its contents
+ *                  need no initialisation: a call writes every word of it
+ *                  that the call reads.  Calls that may overlap in time need
  *                  separate workspaces.
  * Supported: Hq % Hkv == 0, Hq / Hkv <= 64, d_head in {64, 128},
  * block_size in {8, 16, 32}, dtype PA_F32 or PA_BF16 (fp32 accumulation;

@@ -194,7 +194,7 @@ def pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, ma
     dt = _dtype_code(q)
     need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, dt)
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
@@ -210,9 +210,8 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
 
     q, out [N][Hq][D]; k_pool/v_pool one layer in the library layout; block_tables
     int32 [N][max_blocks]; context_lens int32 [N].  ``workspace`` is a uint8
-    device tensor of at least pa_decode_workspace_bytes(...) bytes, zero-filled
-    before its first use; when None a zeroed buffer is allocated through torch
-    for this call.
+    device tensor of at least pa_decode_workspace_bytes(...) bytes (contents need
+    no initialisation); when None one is allocated through torch for this call.
     """
     args, _ws = pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
                                workspace, stream)
@@ -246,7 +245,7 @@ def pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, bloc
     dt = _dtype_code(q)
     need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, dt)
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     slots = c_void_p(slot_pointer) if slot_pointer is not None else _dev(slot_mapping, "slot_mapping")
@@ -300,7 +299,7 @@ def pa_decode_shared_args(out, q, k_pool, v_pool, block_tables, context_lens, gr
     nb, hkv, _, bs = _pool_dims(k_pool, v_pool)
     need = pa_decode_shared_workspace_bytes(n, ng, hq, hkv, d, bs, max_context_len, _dtype_code(q))
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = base[:6] + (gp, ng) + base[6:16] + (ws_ptr, ws_bytes, base[18])
@@ -329,7 +328,7 @@ def pa_decode_step_shared_args(out, q, k_new, v_new, k_pool, v_pool, slot_mappin
     nb, hkv, _, bs = _pool_dims(k_pool, v_pool)
     need = pa_decode_shared_workspace_bytes(n, ng, hq, hkv, d, bs, max_context_len, _dtype_code(q))
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero before first use
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = base[:9] + (gp, ng) + base[9:19] + (ws_ptr, ws_bytes, base[21])
@@ -524,7 +523,7 @@ def pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, c
         raise ValueError("block_tables must be [N][max_blocks] and context_lens [N]")
     need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, PA_FP8_E4M3)
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),

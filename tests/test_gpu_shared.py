@@ -248,7 +248,12 @@ def test_fork_workload_shared_sixteen_steps(fused):
         q = synth.randn((n, hq, d), torch.bfloat16, w.value_scale, 7000 + step, "cuda")
         d_slots = torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda()
         if fused:
-            pa.pa_decode_step_shared(out, q, kn, vn, k, v, d_slots, d_tables, d_lens, d_groups, case.scale, final)
+            if step == 0:  # one workspace for every step, 0xFF bytes (NaN as floats) to begin with
+                need = pa.pa_decode_shared_workspace_bytes(n, int(d_groups.shape[0]), hq, hkv, d, bs, final,
+                                                           pa.PA_BF16)
+                ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+            pa.pa_decode_step_shared(out, q, kn, vn, k, v, d_slots, d_tables, d_lens, d_groups, case.scale, final,
+                                     workspace=ws)
         else:
             pa.pa_append_step(k, v, kn, vn, d_slots, d_tables, d_lens)
             pa.pa_decode_shared(out, q, k, v, d_tables, d_lens, d_groups, case.scale, final)

@@ -65,7 +65,10 @@ def test_step_equals_append_then_decode(d, bs):
     pa.pa_append_step(k1, v1, kn, vn, slots, t1, l1)
     pa.pa_decode(out1, c.q, k1, v1, t1, l1, c.scale, max_ctx)
     out2 = torch.empty_like(c.q)
-    pa.pa_decode_step(out2, c.q, kn, vn, k2, v2, slots, t2, l2, c.scale, max_ctx)
+    # a workspace of 0xFF bytes (NaN as floats): the step writes every word it reads, the row slots included
+    need = pa.pa_decode_workspace_bytes(len(c.lens), c.hq, c.hkv, d, bs, max_ctx, pa.PA_BF16)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    pa.pa_decode_step(out2, c.q, kn, vn, k2, v2, slots, t2, l2, c.scale, max_ctx, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(_bits(out1), _bits(out2)), "fused output differs from append + decode"
     assert torch.equal(_bits(k1), _bits(k2)) and torch.equal(_bits(v1), _bits(v2)), "pools differ"
