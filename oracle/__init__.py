@@ -25,6 +25,10 @@ fp8            KV cache held as FP8 E4M3 codes with per-(block, KV head)
                scales: code values, the saturating round-to-nearest-even
                quantizer, the quantizing append, block copy with scales, and
                decode over the dequantized cache.
+int8           KV cache held as signed 8-bit integer codes with per-(block,
+               KV head) scales: code values, the clamped round-half-to-even
+               quantizer, the quantizing append, block copy with scales, and
+               decode over the dequantized cache.
 sizing         KV sizing, block-table footprint, tail waste and capacity
                arithmetic.
 
