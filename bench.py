@@ -24,7 +24,11 @@ pa_append_step_fp8 (quantizing append, rows moved forward) and
 pa_decode_fp8; the KV bytes per step are then the codes (1 byte per element)
 plus the 8 bytes of scales per (block, KV head) the contexts span.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa8b] [--kv bf16|fp8]
+With --kv int8 the cache holds INT8 codes with the same scales and layout and
+the INT8 entry points (pa_copy_blocks_int8, pa_append_step_int8,
+pa_decode_int8) take their places.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa8b] [--kv bf16|fp8|int8]
 """
 
 from __future__ import annotations
@@ -50,8 +54,10 @@ RING = 32
 # HBM traffic of the decode kernels, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a
 # plain copy of known size; valid only while the kernel sources are those it was taken on.
 TRAFFIC_FILES = {"bf16": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_traffic.txt"),
-                 "fp8": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_fp8_traffic.txt")}
-KERNEL_SOURCES = ["decode_stream.hip", "decode_stream.h", "decode_tile.h", "decode.hip", "common.h"]
+                 "fp8": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_fp8_traffic.txt"),
+                 "int8": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_int8_traffic.txt")}
+KERNEL_SOURCES = ["decode_stream.hip", "decode_stream_kernel.h", "decode_stream_i8.hip", "decode_stream.h", "decode_tile.h",
+                  "decode.hip", "common.h"]
 
 
 def measured_traffic(workload_name, kv_kind="bf16"):
@@ -88,8 +94,8 @@ def parse():
                          "once per step for its samples (default: pa_decode_step)")
     ap.add_argument("--replicas", type=int, default=4,
                     help="pool copies rotated step to step so reads come from HBM, not the 256 MB Infinity Cache")
-    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
-                    help="cache element type: bf16, or FP8 E4M3 codes with per-(block, KV head) scales")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8", "int8"],
+                    help="cache element type: bf16, or FP8 E4M3 / INT8 codes with per-(block, KV head) scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -118,7 +124,8 @@ class Runner:
         self.pa = pa
         self.torch = torch
         self.w = w
-        self.fp8 = kv_kind == "fp8"
+        self.fp8 = kv_kind in ("fp8", "int8")  # one-byte codes with scales
+        self.int8 = kv_kind == "int8"
         self.fork = w.name == "fork"
         self.shared = shared
         bs = w.block_size
@@ -158,13 +165,15 @@ class Runner:
         dt = synth.torch_dtype(w)
         if self.fp8:
             kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, 1)
-            self.k = [synth.fill_fp8_codes_(torch.empty(kshape, dtype=torch.uint8, device=device), w.seed * 10 + 1 + 7 * r)
+            fill = synth.fill_int8_codes_ if self.int8 else synth.fill_fp8_codes_
+            scales = synth.int8_scales if self.int8 else synth.fp8_scales
+            self.k = [fill(torch.empty(kshape, dtype=torch.uint8, device=device), w.seed * 10 + 1 + 7 * r)
                       for r in range(replicas)]
-            self.v = [synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8, device=device), w.seed * 10 + 2 + 7 * r)
+            self.v = [fill(torch.empty(vshape, dtype=torch.uint8, device=device), w.seed * 10 + 2 + 7 * r)
                       for r in range(replicas)]
-            self.ks = [synth.fp8_scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 8 + 7 * r, device)
+            self.ks = [scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 8 + 7 * r, device)
                        for r in range(replicas)]
-            self.vs = [synth.fp8_scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 9 + 7 * r, device)
+            self.vs = [scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 9 + 7 * r, device)
                        for r in range(replicas)]
         else:
             kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, torch.tensor([], dtype=dt).element_size())
@@ -181,7 +190,7 @@ class Runner:
                                                      pa.PA_BF16)
         else:
             ws = pa.pa_decode_workspace_bytes(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx,
-                                              pa.PA_FP8_E4M3 if self.fp8 else pa.PA_BF16)
+                                              pa.PA_INT8 if self.int8 else pa.PA_FP8_E4M3 if self.fp8 else pa.PA_BF16)
         self.ws = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)  # zero before first use
         self.part = pa.pa_decode_partition_tokens(self.n, w.hq, w.hkv, w.d, bs, self.max_ctx, pa.PA_BF16)
         # Block tables and lengths live on the device; pa_append_step moves them forward.
@@ -231,8 +240,9 @@ class Runner:
                 cpy = pa.pa_copy_blocks_fp8_args(self.k[r], self.v[r], self.ks[r], self.vs[r], check[n:3 * n].view(n, 2))
                 app = pa.pa_append_step_fp8_args(self.k[r], self.v[r], self.ks[r], self.vs[r], self.k_new, self.v_new,
                                                  check[:n], self.d_tables, self.d_lens)
-                dec, _ = pa.pa_decode_fp8_args(self.out, self.q, self.k[r], self.v[r], self.ks[r], self.vs[r],
-                                               self.d_tables, self.d_lens, w.scale, self.max_ctx, workspace=self.ws)
+                dec_args = pa.pa_decode_int8_args if self.int8 else pa.pa_decode_fp8_args
+                dec, _ = dec_args(self.out, self.q, self.k[r], self.v[r], self.ks[r], self.vs[r],
+                                  self.d_tables, self.d_lens, w.scale, self.max_ctx, workspace=self.ws)
             else:
                 cpy = pa.pa_copy_blocks_args(self.k[r], self.v[r], check[n:3 * n].view(n, 2))
             for b in range(RING):
@@ -277,11 +287,11 @@ class Runner:
             if npairs:
                 ca = self.copy_args[r, k]
                 ca[5] = npairs
-                assert L.pa_copy_blocks_fp8(*ca) == 0
-            assert L.pa_append_step_fp8(*self.append_args[r, k]) == 0
+                assert (L.pa_copy_blocks_int8 if self.int8 else L.pa_copy_blocks_fp8)(*ca) == 0
+            assert (L.pa_append_step_int8 if self.int8 else L.pa_append_step_fp8)(*self.append_args[r, k]) == 0
             if timing is not None:
                 timing[0].record()
-            assert L.pa_decode_fp8(*self.step_args[r, k]) == 0
+            assert (L.pa_decode_int8 if self.int8 else L.pa_decode_fp8)(*self.step_args[r, k]) == 0
             if timing is not None:
                 timing[1].record()
         else:
@@ -399,7 +409,7 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
     """The fp64 oracle on this host's cores over a bounded sample of the same workload (one BLAS thread).
 
     Inputs (one decode step of every sequence, values as stored in bf16, or
-    FP8 codes and scales) are built first and kept in host memory; then whole
+    FP8 / INT8 codes and scales) are built first and kept in host memory; then whole
     passes over all sequences are timed until `seconds` of compute have
     accumulated.
     """
@@ -408,7 +418,11 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
     from threadpoolctl import threadpool_limits
     from oracle import attention as OA
     from oracle import fp8 as OF
-    fp8 = kv_kind == "fp8"
+    from oracle import int8 as OI
+    fp8 = kv_kind in ("fp8", "int8")  # one-byte codes with scales
+    OC = OI if kv_kind == "int8" else OF
+    fill = synth.fill_int8_codes_ if kv_kind == "int8" else synth.fill_fp8_codes_
+    scales = synth.int8_scales if kv_kind == "int8" else synth.fp8_scales
     lens = synth.seq_lengths(w)
     if w.name == "long":
         lens = lens[:2]  # one layer of two 32,768-token sequences (the oracle holds them in host memory)
@@ -418,10 +432,10 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
     for n, s in enumerate(lens):
         nb = -(-s // bs)
         if fp8:
-            kp = synth.fill_fp8_codes_(torch.empty((nb, hkv, bs, d), dtype=torch.uint8), 5000 + n).numpy()
-            vp = synth.fill_fp8_codes_(torch.empty((nb, hkv, bs, d), dtype=torch.uint8), 6000 + n).numpy()
-            ks = synth.fp8_scales(nb, hkv, w.value_scale, 8000 + n).double().numpy()
-            vs = synth.fp8_scales(nb, hkv, w.value_scale, 9000 + n).double().numpy()
+            kp = fill(torch.empty((nb, hkv, bs, d), dtype=torch.uint8), 5000 + n).numpy()
+            vp = fill(torch.empty((nb, hkv, bs, d), dtype=torch.uint8), 6000 + n).numpy()
+            ks = scales(nb, hkv, w.value_scale, 8000 + n).double().numpy()
+            vs = scales(nb, hkv, w.value_scale, 9000 + n).double().numpy()
         else:
             kp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 5000 + n).float().numpy()
             vp = synth.randn((nb, hkv, bs, d), torch.bfloat16, w.value_scale, 6000 + n).float().numpy()
@@ -445,7 +459,7 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
             t0 = time.perf_counter()
             for q, kp, vp, ks, vs, table, s in inputs:
                 if fp8:
-                    OF.paged_decode(q, kp, vp, ks, vs, table, [s], w.scale)
+                    OC.paged_decode(q, kp, vp, ks, vs, table, [s], w.scale)
                 else:
                     OA.paged_decode(q, kp, vp, table, [s], w.scale)
             t_total += time.perf_counter() - t0
@@ -453,7 +467,8 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
     return {"value": round(passes * step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} passes over one decode step of {'one layer of ' if w.name == 'long' else ''}"
                       f"{'the first' if w.name == 'long' else 'all'} {len(lens)} sequences of the same workload "
-                      f"({'FP8 cache, ' if fp8 else ''}all {w.hq} query heads; fp64 NumPy oracle, one thread), "
+                      f"({kv_kind.upper() + ' cache, ' if fp8 else ''}all {w.hq} query heads; fp64 NumPy oracle, "
+                      f"one thread), "
                       f"{t_total:.1f} s of compute",
             "us_per_step": round(t_total / passes * 1e6, 1)}
 
@@ -528,7 +543,8 @@ def main():
     bytes_per_launch = kv_bytes / args.steps
     achieved = sampled_bytes / (sum(dec_us) * 1e-6) / 1e9
     traffic = measured_traffic(w.name, args.kv) if not args.shared else None
-    fp8 = args.kv == "fp8"
+    fp8 = args.kv in ("fp8", "int8")  # one-byte codes with scales
+    codes_name = {"fp8": "FP8 E4M3", "int8": "INT8"}.get(args.kv, "")
     if run.fork:
         # bytes a step needs from memory when each prompt's shared full blocks are read once
         st, groups = run.bm.shared_groups(run.seqs, 32 // (w.hq // w.hkv))
@@ -546,8 +562,8 @@ def main():
                          f"random placement; a step appends each sequence's new token in every layer and decodes every "
                          f"layer over S + 1 tokens, contexts growing 1/step")
     else:
-        workload_desc = (f"{w.name}{'-fp8' if fp8 else ''}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, "
-                         f"block {w.block_size}, {'FP8 E4M3 cache with per-(block, KV head) scales' if fp8 else 'bf16'}, "
+        workload_desc = (f"{w.name}{'-' + args.kv if fp8 else ''}: {run.n} seqs, Hq {w.hq}, Hkv {w.hkv}, d_head {w.d}, "
+                         f"block {w.block_size}, {codes_name + ' cache with per-(block, KV head) scales' if fp8 else 'bf16'}, "
                          f"contexts {min(run.lens0)}..{max(run.lens0)} growing 1/step")
     res = {
         "metric": METRIC,
@@ -560,7 +576,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 cache, bf16 q/out" if fp8 else "bf16",
+        "dtype": {"fp8": "fp8-e4m3 cache, bf16 q/out", "int8": "int8 cache, bf16 q/out"}.get(args.kv, "bf16"),
         "data": "synthetic",
         "config": {"workload": workload_desc,
                    "num_seqs": run.n, "block_size": w.block_size, "pool_blocks": run.num_blocks,
@@ -573,7 +589,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),
-                     "kernel": "pa_decode_fp8 (decode kernel + merge kernel)" if fp8 else
+                     "kernel": f"pa_decode_{args.kv} (decode kernel + merge kernel)" if fp8 else
                                ("pa_decode_step_shared (shared-prefix decode kernel + merge/append kernel)"
                                 if args.shared else
                                 (f"pa_decode x {w.layers} layers (decode kernel + merge kernel each)" if long_ctx

@@ -66,9 +66,9 @@ enum {
   PA_ERR_HIP = 7             /* the HIP runtime refused a launch                    */
 };
 
-/* PA_FP8_E4M3 names a cache of FP8 codes (see pa_decode_fp8); queries,
- * outputs and new tokens stay bf16 there. */
-enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 };
+/* PA_FP8_E4M3 and PA_INT8 name caches of one-byte codes (see pa_decode_fp8,
+ * pa_decode_int8); queries, outputs and new tokens stay bf16 there. */
+enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2, PA_INT8 = 3 };
 
 /* Text for a status code (static storage; never NULL). */
 const char* pa_status_string(int status);
@@ -210,7 +210,8 @@ size_t pa_decode_shared_workspace_bytes(int num_seqs, int num_groups, int Hq, in
                                         int max_context_len, int dtype);
 
 /* Workspace bytes pa_decode needs for these sizes on the current device
- * (0 when no split is used); dtype PA_FP8_E4M3 gives pa_decode_fp8's. */
+ * (0 when no split is used); dtype PA_FP8_E4M3 or PA_INT8 gives
+ * pa_decode_fp8's or pa_decode_int8's (the same size). */
 size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                  int max_context_len, int dtype);
 
@@ -345,6 +346,54 @@ int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scal
                        int num_pairs, int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
                        int64_t layer_stride_elems, int64_t scale_layer_stride, void* stream);
 
+/* ---- INT8 KV cache -----------------------------------------------------------------
+ *
+ * The other quantized format that "PagedAttention and KV Memory"
+ * ("Alternatives and ecosystem") names beside FP8: the same bytes per token,
+ * the same scales and layout as the FP8 cache above, integer codes.  Attention
+ * over it is the exact attention over the values the codes stand for
+ * ("PagedAttention in vLLM: scattered memory, exact attention", sections 8
+ * and 11).
+ *
+ * Codes: signed 8-bit two's complement integers; code c of block pb, KV head j
+ * stands for c * scale[pb][j].  The appenders write only -127..127; a stored
+ * -128 stands for -128 * scale.  Scales, pool layout and ownership as for the
+ * FP8 cache.
+ */
+
+/* pa_decode over an INT8 cache: as pa_decode_fp8 with the values c * scale
+ * (workspace: pa_decode_workspace_bytes with dtype PA_INT8; shapes, split and
+ * errors as for pa_decode_fp8). */
+int pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
+                   const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                   int Hq, int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq,
+                   int max_context_len, int num_blocks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_append_kv into an INT8 cache: each element x of token t's bf16 key and
+ * value is stored at slot slot_mapping[t] ("PagedAttention: Virtual Memory for
+ * the KV Cache", section 16) as the integer nearest to the real quotient
+ * x / scale of the destination (block, KV head), ties to even, clamped to
+ * -127..127.  NaN input, or a scale that is not positive and finite, stores 0
+ * (an 8-bit integer has no NaN).  Other arguments as for pa_append_kv_fp8. */
+int pa_append_kv_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                      const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+                      int Hkv, int d_head, int block_size, int num_blocks, void* stream);
+
+/* pa_append_step into an INT8 cache: the codes as pa_append_kv_int8 stores
+ * them and each row moved forward as pa_append_step does; arguments as for
+ * pa_append_step_fp8. */
+int pa_append_step_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+                        const void* v_new, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                        int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
+                        void* stream);
+
+/* pa_copy_blocks for an INT8 cache: codes and scales of block src over block
+ * dst, exactly as pa_copy_blocks_fp8 (the copy moves bytes and scales,
+ * whatever the codes mean). */
+int pa_copy_blocks_int8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, const int32_t* src_dst_pairs,
+                        int num_pairs, int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
+                        int64_t layer_stride_elems, int64_t scale_layer_stride, void* stream);
+
 /* ---- swapping blocks between pools ----------------------------------------------
  *
  * pa_swap_blocks: preemption by swapping ("PagedAttention: Virtual Memory for
@@ -365,7 +414,8 @@ int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scal
  *                     num_layers == 1)
  *   dtype             PA_F32 or PA_BF16; pa_swap_blocks_fp8 moves FP8 codes
  *                     and their per-(block, KV head) key and value scales
- *                     (scale strides in floats).
+ *                     (scale strides in floats), pa_swap_blocks_int8 INT8
+ *                     codes and scales the same way.
  * Argument errors as for pa_copy_blocks. */
 int pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_pool, const void* src_v_pool,
                    const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size, int dtype,
@@ -377,6 +427,12 @@ int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, f
                        int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
                        int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, int64_t src_scale_layer_stride,
                        int64_t dst_scale_layer_stride, void* stream);
+int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
+                        const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
+                        const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head,
+                        int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
+                        int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, int64_t src_scale_layer_stride,
+                        int64_t dst_scale_layer_stride, void* stream);
 
 /* ---- host block manager ------------------------------------------------------
  *

@@ -29,6 +29,7 @@ PA_ERR_HIP = 7
 PA_F32 = 0
 PA_BF16 = 1
 PA_FP8_E4M3 = 2
+PA_INT8 = 3
 
 # torch first: libpa.so then binds to the HIP runtime torch has loaded, so
 # torch's streams and device memory are valid in the library's calls.
@@ -87,6 +88,11 @@ _SIGS = {
     "pa_append_step_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
     "pa_swap_blocks": (c_int, [c_void_p] * 5 + [c_int] * 8 + [c_int64, c_int64, c_void_p]),
     "pa_swap_blocks_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
+    "pa_decode_int8": (c_int, [c_void_p] * 8 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
+    "pa_append_kv_int8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
+    "pa_copy_blocks_int8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
+    "pa_append_step_int8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
+    "pa_swap_blocks_int8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
     "pa_bm_create": (c_void_p, [c_int, c_int, _P32]),
     "pa_bm_destroy": (None, [c_void_p]),
     "pa_bm_add_seq": (c_int, [c_void_p, c_int64, c_int]),
@@ -474,29 +480,40 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None):
                               _stream_ptr(stream)), "pa_swap_blocks")
 
 
-def pa_swap_blocks_fp8(dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream=None):
-    """pa_swap_blocks_fp8 of include/pa.h (one-layer FP8 pools with their [nb][Hkv] scales)."""
+def _swap_codes(fn, name, dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream):
     import torch
     if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be int32 [P][2]")
     _, hkv, d, bs = _fp8_pools(src_k, src_v)
-    _check(lib.pa_swap_blocks_fp8(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), _pool_ptr(dst_ks, "dst_ks"),
-                                  _pool_ptr(dst_vs, "dst_vs"), _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"),
-                                  _pool_ptr(src_ks, "src_ks"), _pool_ptr(src_vs, "src_vs"),
-                                  _dev(pairs, "pairs") if pairs.shape[0] else c_void_p(0), pairs.shape[0], hkv, d, bs,
-                                  src_k.shape[0], dst_k.shape[0], 1, 0, 0, 0, 0, _stream_ptr(stream)),
-           "pa_swap_blocks_fp8")
+    _check(fn(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), _pool_ptr(dst_ks, "dst_ks"),
+              _pool_ptr(dst_vs, "dst_vs"), _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"),
+              _pool_ptr(src_ks, "src_ks"), _pool_ptr(src_vs, "src_vs"),
+              _dev(pairs, "pairs") if pairs.shape[0] else c_void_p(0), pairs.shape[0], hkv, d, bs,
+              src_k.shape[0], dst_k.shape[0], 1, 0, 0, 0, 0, _stream_ptr(stream)), name)
+
+
+def pa_swap_blocks_fp8(dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream=None):
+    """pa_swap_blocks_fp8 of include/pa.h (one-layer FP8 pools with their [nb][Hkv] scales)."""
+    _swap_codes(lib.pa_swap_blocks_fp8, "pa_swap_blocks_fp8", dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks,
+                src_vs, pairs, stream)
+
+
+def pa_swap_blocks_int8(dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream=None):
+    """pa_swap_blocks_int8 of include/pa.h (one-layer INT8 pools with their [nb][Hkv] scales)."""
+    _swap_codes(lib.pa_swap_blocks_int8, "pa_swap_blocks_int8", dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks,
+                src_vs, pairs, stream)
 
 
 # ---------------------------------------------------------------------------
-# FP8 (E4M3) cache: uint8 code pools in the layout above (x = 16) and float32
-# scales [num_blocks][Hkv] (or [L][num_blocks][Hkv] for a layered copy)
+# FP8 (E4M3) and INT8 caches: uint8 code pools in the layout above (x = 16)
+# and float32 scales [num_blocks][Hkv] (or [L][num_blocks][Hkv] for a layered
+# copy); the INT8 functions take the same arguments as the FP8 ones
 # ---------------------------------------------------------------------------
 
 def _fp8_pools(k_pool, v_pool):
     import torch
     if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
-        raise ValueError("FP8 pools hold uint8 codes")
+        raise ValueError("code pools hold uint8 bytes")
     return _pool_dims(k_pool, v_pool)
 
 
@@ -511,6 +528,19 @@ def _scales(k_scale, v_scale, nb, hkv, lead=()):
 def pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
                        max_context_len, workspace=None, stream=None):
     """Validate once and return (args, workspace) for repeated ``lib.pa_decode_fp8(*args)`` calls."""
+    return _decode_codes_args(PA_FP8_E4M3, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                              scale, max_context_len, workspace, stream)
+
+
+def pa_decode_int8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+                        max_context_len, workspace=None, stream=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode_int8(*args)`` calls."""
+    return _decode_codes_args(PA_INT8, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                              scale, max_context_len, workspace, stream)
+
+
+def _decode_codes_args(dtype_code, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+                       max_context_len, workspace, stream):
     import torch
     n, hq, d = q.shape
     nb, hkv, d2, bs = _fp8_pools(k_pool, v_pool)
@@ -521,7 +551,7 @@ def pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, c
         raise ValueError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != n or tuple(context_lens.shape) != (n,):
         raise ValueError("block_tables must be [N][max_blocks] and context_lens [N]")
-    need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, PA_FP8_E4M3)
+    need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, dtype_code)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
@@ -539,6 +569,15 @@ def pa_decode_fp8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, contex
     args, _ws = pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
                                    max_context_len, workspace, stream)
     _check(lib.pa_decode_fp8(*args), "pa_decode_fp8")
+    return out
+
+
+def pa_decode_int8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale, max_context_len,
+                   workspace=None, stream=None):
+    """pa_decode_int8 of include/pa.h: bf16 q/out over INT8 code pools (uint8 bytes) with float32 scales."""
+    args, _ws = pa_decode_int8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+                                    max_context_len, workspace, stream)
+    _check(lib.pa_decode_int8(*args), "pa_decode_int8")
     return out
 
 
@@ -563,6 +602,12 @@ def pa_append_kv_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mappin
     """pa_append_kv_fp8 of include/pa.h: quantize bf16 k_new/v_new [T][Hkv][D] into their slots."""
     _check(lib.pa_append_kv_fp8(*pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
                                                        slot_mapping, stream)), "pa_append_kv_fp8")
+
+
+def pa_append_kv_int8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, stream=None):
+    """pa_append_kv_int8 of include/pa.h: quantize bf16 k_new/v_new [T][Hkv][D] into their slots as INT8 codes."""
+    _check(lib.pa_append_kv_int8(*pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+                                                        slot_mapping, stream)), "pa_append_kv_int8")
 
 
 def pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables,
@@ -597,6 +642,14 @@ def pa_append_step_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapp
            "pa_append_step_fp8")
 
 
+def pa_append_step_int8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables, context_lens,
+                        stream=None):
+    """pa_append_step_int8 of include/pa.h: INT8 quantizing append of row n's token and the row moved forward."""
+    _check(lib.pa_append_step_int8(*pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+                                                            slot_mapping, block_tables, context_lens, stream)),
+           "pa_append_step_int8")
+
+
 def pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
     """Validate once and return the argument tuple for ``lib.pa_copy_blocks_fp8(*args)``.
 
@@ -621,6 +674,12 @@ def pa_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=N
     """pa_copy_blocks_fp8 of include/pa.h: codes and scales of each src block over its dst."""
     _check(lib.pa_copy_blocks_fp8(*pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream)),
            "pa_copy_blocks_fp8")
+
+
+def pa_copy_blocks_int8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
+    """pa_copy_blocks_int8 of include/pa.h: INT8 codes and scales of each src block over its dst."""
+    _check(lib.pa_copy_blocks_int8(*pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs,
+                                                            stream)), "pa_copy_blocks_int8")
 
 
 # ---------------------------------------------------------------------------

@@ -479,7 +479,7 @@ bool use_shared(int num_seqs, int num_groups, int hq, int hkv, int d, int block_
 extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                             int max_context_len, int dtype) {
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_context_len < 0) return 0;
-  if (dtype == PA_FP8_E4M3) {
+  if (dtype == PA_FP8_E4M3 || dtype == PA_INT8) {  // one-byte codes: 64-token tiles
     if (Hq % Hkv != 0 || !pa::stream_eligible_fp8(num_seqs, Hq / Hkv, d_head, block_size)) return 0;
     return pa::stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, true).workspace_bytes;
   }
@@ -643,11 +643,13 @@ extern "C" int pa_decode_step_shared(void* out, const void* q, const void* k_new
                      stream, &step, groups, num_groups);
 }
 
-extern "C" int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
-                             const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
-                             int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
-                             int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+namespace {
+
+// pa_decode over a cache of one-byte codes (FP8 E4M3 or INT8) with scales.
+int decode_codes(int codes, void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
+                 const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq,
+                 int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq, int max_context_len,
+                 int num_blocks, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pa;
   if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0 || num_blocks < 0)
@@ -663,5 +665,28 @@ extern "C" int pa_decode_fp8(void* out, const void* q, const void* k_pool, const
   if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
   return launch_stream(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, out,
                        workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq, num_blocks,
-                       scale * kLog2e, nullptr, k_scale, v_scale);
+                       scale * kLog2e, nullptr, k_scale, v_scale, codes);
 }
+
+}  // namespace
+
+extern "C" int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
+                             const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                             int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return decode_codes(pa::kKvE4m3, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                      Hq, Hkv, d_head, block_size, scale, max_blocks_per_seq, max_context_len, num_blocks, workspace,
+                      workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
+                              const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                              int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                              int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return decode_codes(pa::kKvInt8, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, num_seqs,
+                      Hq, Hkv, d_head, block_size, scale, max_blocks_per_seq, max_context_len, num_blocks, workspace,
+                      workspace_bytes, stream);
+}
+

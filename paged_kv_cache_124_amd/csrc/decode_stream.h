@@ -18,6 +18,10 @@ struct StreamPlan {
   size_t lds_bytes = 0;
 };
 
+// Element format of the cache the decode reads: bf16 values, or one-byte
+// codes with per-(block, KV head) scales (FP8 E4M3 or INT8).
+enum KvCodes { kKvBf16 = 0, kKvE4m3 = 1, kKvInt8 = 2 };
+
 // The step's new tokens for pa_decode_step: k_new / v_new [N][Hkv][D] and
 // their slots (device-readable).
 struct StepInputs {
@@ -31,12 +35,19 @@ bool stream_eligible(int num_seqs, int g, int d, int block_size, int dtype);
 bool stream_eligible_fp8(int num_seqs, int g, int d, int block_size);
 // fp8: 64-token tiles over an FP8 cache instead of 32-token bf16 tiles.
 StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, bool fp8 = false);
-// k_scale / v_scale non-null: the pools hold FP8 codes with per-(block, KV
-// head) scales (no fused step for them).
+// codes != kKvBf16: the pools hold one-byte codes with per-(block, KV head)
+// scales k_scale / v_scale (no fused step for them).
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
                   int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
-                  const float* k_scale = nullptr, const float* v_scale = nullptr);
+                  const float* k_scale = nullptr, const float* v_scale = nullptr, int codes = kKvBf16);
+
+// The INT8-cache instances of the kernel (decode_stream_i8.hip); launch_stream
+// calls it for codes == kKvInt8.
+int launch_stream_int8(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
+                       const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d,
+                       int block_size, int max_blocks, int num_blocks, float scale_log2, const float* k_scale,
+                       const float* v_scale);
 
 // Shared-prefix kernel (decode_shared.hip): groups of consecutive rows whose
 // first P tokens lie in the same full blocks, int32 [num_groups][3] =

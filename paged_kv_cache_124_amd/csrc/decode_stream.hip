@@ -1,443 +1,19 @@
-// Paged decode attention, bf16, matrix cores: one persistent, balanced pass.
-//
-// What is computed ("PagedAttention: Virtual Memory for the KV Cache",
-// sections 1 and 13; "PagedAttention in vLLM: scattered memory, exact
-// attention", sections 10-11): out[n][h] = softmax(scale * q[n][h] K^T) V over
-// the S_n cached tokens of sequence n, K and V of KV head h / G gathered
-// through the block table.
-//
-// Work decomposition
-//   The work is the list of 32-token tiles of every (sequence n, KV head j)
-//   "segment", segments in (n, j) order: T = Hkv * sum_n ceil(S_n / 32) tiles.
-//   The launch holds exactly as many waves W as the chip keeps resident, and
-//   wave w walks the tiles [w T / W, (w + 1) T / W): every wave reads the same
-//   number of bytes, so all finish together and no workgroup round is left
-//   half empty.  A segment that starts and ends inside one wave's range is
-//   finished by that wave (output written directly).  A segment cut by range
-//   boundaries leaves one (m, z, u) summary per piece; `merge_stream` combines
-//   them with the common-maximum rule of the second page, section 11, in wave
-//   order.
-//
-// Per wave, two tiles are in flight: while one tile is computed, the next
-// tile's Q, keys and values and the block-table entries of the tile after it
-// are loading.  One wave per SIMD (one workgroup per CU): with more, the
-// oldest waves win the memory pipe and the equal split finishes unevenly.
-//
-// Per tile the matrix-core roles of decode_tile.h, with the G query heads of
-// the KV head as the 16 columns (head r, padding for r >= G).
-//
-// Pool layout (per layer): K [num_blocks][Hkv][D/8][B][8], V [num_blocks][Hkv][D][B].
+// Paged decode attention: the host side of the persistent decode kernel of
+// decode_stream_kernel.h -- the launch plan (workgroups, workspace layout),
+// the resident-workgroup query and the dispatch over head size, block size and
+// cache format (bf16 and FP8 E4M3 here; INT8 in decode_stream_i8.hip).
 
 #include <cstdlib>
 #include <mutex>
-#include <type_traits>
 
-#include "common.h"
-#include "decode_stream.h"
-#include "decode_tile.h"
+#include "decode_stream_kernel.h"
 
 namespace pa {
 namespace {
 
-constexpr int kMaxSeqs = 3072;  // lengths and tile prefix sums live in LDS beside the stages
-
-
-// ---- FP8 (E4M3) cache ----------------------------------------------------------
-//
-// Codes are OCP E4M3; a stored code c stands for value(c) * scale, one fp32
-// scale per (block, KV head) for keys and one for values.  gfx950 converts
-// two codes to two bf16 in one instruction, exactly (every E4M3 value is a
-// bf16 value), so both products stay bf16 x bf16 MFMAs on the codes' values
-// and the scales are applied outside them: the key scale multiplies a
-// token's score, the value scale its probability in P.V (the weight sum uses
-// the unscaled probability).  A 64-token tile is two 32-token sub-tiles,
-// each computed as a bf16 tile is.
-
-// Register image of a staged FP8 tile for lane (r, gq).
-template <int D>
-struct Buf8 {
-  uint4 k[2][2][D / 64];     // [sub-tile][slab] key row 16 slab + r: the 16-byte chunks of d quarter gq
-  uint32_t v[2][2][D / 16];  // [sub-tile][slab][mm] value row 16 mm + r, tokens 4 gq .. 4 gq + 3 of the slab
-  bool ok[2][2];             // the block of that value group is in the pool
-};
-
-// Scales of the blocks of the lane's token groups (0 where the block is missing).
-struct Sc8 {
-  float k[2][2], v[2][2];  // [sub-tile][slab]
-};
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Eight codes (two words, lowest byte first) as eight bf16 values.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// Block of the lane's 4-token group that starts at tile token first + 4 gq
-// (first a multiple of 16, known at compile time after unrolling).  With
-// B >= 16 the 16 tokens from `first` lie in one block; with B = 8 in two,
-// chosen by one select (an index computed at run time would move tb to scratch).
-template <int B>
-__device__ __forceinline__ int group_block(const Tb<64 / B>& tb, int first, int gq) {
-  if constexpr (B >= 16)
-    return tb.blk[first / B];
-  else
-    return gq >= 2 ? tb.blk[first / B + 1] : tb.blk[first / B];
-}
-
-template <int B>
-__device__ __forceinline__ Sc8 load_scales(const Tb<64 / B>& tb, const float* __restrict__ k_scale,
-                                           const float* __restrict__ v_scale, int j, int hkv, int num_blocks, int gq) {
-  Sc8 sc;
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int e = group_block<B>(tb, 32 * u + 16 * a, gq);
-      const bool ok = e >= 0 && e < num_blocks;
-      const int64_t idx = static_cast<int64_t>(ok ? e : 0) * hkv + j;
-      const float kv = k_scale[idx], vv = v_scale[idx];
-      sc.k[u][a] = ok ? kv : 0.f;
-      sc.v[u][a] = ok ? vv : 0.f;
-    }
-  return sc;
-}
-
-template <int D, int B>
-__device__ __forceinline__ void read_tile8(Buf8<D>& b, const unsigned char* stage, const Tb<64 / B>& tb, int num_blocks,
-                                           int r, int gq) {
-  constexpr int IMG = D * B;
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int tk = 32 * u + 16 * a + r;  // key row
-      const unsigned char* kimg = stage + (tk / B) * IMG + (tk % B) * 16;
-#pragma unroll
-      for (int w = 0; w < D / 64; ++w)
-        b.k[u][a][w] = *reinterpret_cast<const uint4*>(kimg + (gq * (D / 64) + w) * B * 16);
-      const int tv = 32 * u + 16 * a + 4 * gq;  // first token of the value group
-      const unsigned char* vimg = stage + kStageHalf<D> + (tv / B) * IMG + tv % B;
-#pragma unroll
-      for (int mm = 0; mm < D / 16; ++mm) b.v[u][a][mm] = *reinterpret_cast<const uint32_t*>(vimg + (16 * mm + r) * B);
-      const int e = group_block<B>(tb, 32 * u + 16 * a, gq);
-      b.ok[u][a] = e >= 0 && e < num_blocks;
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void qk_tile8(f32x4 (&s)[2], const uint4 (&k)[2][D / 64], const QOp<D>& qo) {
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jj = 0; jj < D / 32; ++jj) {
-      const uint4 c = k[a][jj >> 1];
-      const bf16x8 kop = (jj & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
-      s[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qo.q[jj], s[a], 0, 0, 0);
-    }
-  }
-}
-
-// pv_tile for one FP8 sub-tile: sk[a] = scale_log2 * key scale and sv[a] =
-// value scale of the lane's token group in slab a.
-template <int D>
-__device__ __forceinline__ void pv_tile8(Acc<D>& st, const f32x4 (&s)[2], const uint32_t (&v)[2][D / 16],
-                                         const bool (&ok)[2], int t0, int S, bool full, const float (&sk)[2],
-                                         const float (&sv)[2], int gq) {
-  int n0 = 4, n1 = 4;
-  if (!full) {
-    n0 = ok[0] ? min(max(S - (t0 + 4 * gq), 0), 4) : 0;
-    n1 = ok[1] ? min(max(S - (t0 + 16 + 4 * gq), 0), 4) : 0;
-  }
-  float x[2][4];
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[a][i] = i < (a ? n1 : n0) ? s[a][i] * sk[a] : -INFINITY;
-      tmax = fmaxf(tmax, x[a][i]);
-    }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float m_new = fmaxf(st.m, tmax);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  st.m = m_new;
-  float psum = 0.f;
-  bf16x8 phi, plo;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(x[a][i] - m_new);
-      psum += p;
-      const float pv = p * sv[a];
-      const __bf16 h = static_cast<__bf16>(pv);
-      phi[4 * a + i] = h;
-      plo[4 * a + i] = static_cast<__bf16>(pv - static_cast<float>(h));
-    }
-  st.z = st.z * alpha + psum;
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int mm = 0; mm < D / 16; ++mm) st.o[mm] *= alpha;
-  }
-  uint32_t m0 = 0xffffffffu, m1 = 0xffffffffu;
-  if (!full) {  // zero the codes of missing tokens: stale or NaN codes must not reach P.V
-    m0 = n0 >= 4 ? 0xffffffffu : (1u << (8 * n0)) - 1u;
-    m1 = n1 >= 4 ? 0xffffffffu : (1u << (8 * n1)) - 1u;
-  }
-#pragma unroll
-  for (int mm = 0; mm < D / 16; ++mm) {
-    const bf16x8 vop = fp8x8_to_bf16(v[0][mm] & m0, v[1][mm] & m1);
-    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, st.o[mm], 0, 0, 0);
-    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, st.o[mm], 0, 0, 0);
-  }
-}
-
-// End of a piece of segment t: write the normalised output (whole segment) or a summary record.
-template <int D>
-__device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slot, int64_t wave_id, uint16_t* out,
-                                      float* rec, int hq, int g, int r, int gq) {
-  float zt = st.z + __shfl_xor(st.z, 16);
-  zt += __shfl_xor(zt, 32);
-  if (r < g) {
-    if (whole) {
-      const float inv = 1.f / zt;
-      uint16_t* o = out + (static_cast<int64_t>(t.n) * hq + t.j * g + r) * D + 4 * gq;
-#pragma unroll
-      for (int mm = 0; mm < D / 16; ++mm) {
-        const uint32_t lo = f32_to_bf16_bits(st.o[mm][0] * inv) | (uint32_t(f32_to_bf16_bits(st.o[mm][1] * inv)) << 16);
-        const uint32_t hi = f32_to_bf16_bits(st.o[mm][2] * inv) | (uint32_t(f32_to_bf16_bits(st.o[mm][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(o + 16 * mm) = make_uint2(lo, hi);
-      }
-    } else {
-      float* rr = rec + (static_cast<int64_t>(wave_id * 2 + slot) * g + r) * (D + 4);
-#pragma unroll
-      for (int mm = 0; mm < D / 16; ++mm) *reinterpret_cast<f32x4*>(rr + 4 + 16 * mm + 4 * gq) = st.o[mm];
-      if (gq == 0) {
-        rr[0] = st.m;
-        rr[1] = zt;
-      }
-    }
-  }
-  reset(st);
-}
-
-
-template <int D, int B, bool F8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void decode_stream(
-    const uint16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
-    float* __restrict__ rec, int32_t* __restrict__ prefix_out, int n_seqs, int hq, int hkv, int g, int max_blocks,
-    int num_blocks, float scale_log2, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale) {
-  constexpr int TOK = kTok<F8>;
-  constexpr int NB = TOK / B;
-  extern __shared__ int32_t sm[];
-  int32_t* s_len = sm;            // [n_seqs] packed attended-token counts (pool part clamped to the table)
-  int32_t* s_pre = sm + n_seqs;   // [n_seqs + 1] tile prefix sums
-  __shared__ int32_t s_wsum[kSW];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int r = lane & 15;
-  const int gq = lane >> 4;
-
-  // ---- tiles per sequence and their prefix sums (block-wide scan) ----------
-  const int s_cap = max_blocks * B;
-  int carry = 0;
-  for (int base = 0; base < n_seqs; base += 256) {
-    const int i = base + tid;
-    const int S_raw = i < n_seqs ? context_lens[i] : 0;
-    const int S = min(max(S_raw, 0), s_cap);
-    const int hn = k_new != nullptr ? 1 : 0;  // pa_decode_step: every row attends to its new token
-    const int fits = S_raw >= 0 && S_raw < s_cap ? 1 : 0;
-    const int S_att = S + hn;
-    int v = (S_att + TOK - 1) >> kTokShift<F8>;
-#pragma unroll
-    for (int dlt = 1; dlt < 64; dlt <<= 1) {
-      const int u = __shfl_up(v, dlt);
-      if (lane >= dlt) v += u;
-    }
-    if (lane == 63) s_wsum[wave] = v;
-    if (i < n_seqs) s_len[i] = (S_att << 2) | (fits << 1) | hn;
-    __syncthreads();
-    int off = carry;
-    for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
-    if (i < n_seqs) s_pre[i + 1] = off + v;
-    carry += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    __syncthreads();
-  }
-  if (tid == 0) s_pre[0] = 0;
-  __syncthreads();
-  if (blockIdx.x == 0)
-    for (int i = tid; i <= n_seqs; i += 256) prefix_out[i] = s_pre[i];
-  // no barrier below this point: waves run independently
-
-  Split sp;
-  sp.init(static_cast<int64_t>(hkv) * s_pre[n_seqs], static_cast<int64_t>(gridDim.x) * kSW);
-  // XCD-major order: workgroups are dealt to the 8 XCDs in turn (workgroup b
-  // runs on XCD b % 8), so this numbering gives each XCD one contiguous share
-  // of the tile list: the waves of one sequence's KV heads share that XCD's
-  // L2 for Q, table rows and scales.  The merge kernel sees the same numbering.
-  const int64_t wg = gridDim.x % 8 == 0 ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int64_t wave_id = wg * kSW + wave;
-  const int64_t x0 = sp.start(wave_id);
-  const int64_t x1 = sp.start(wave_id + 1);
-  if (x0 >= x1) return;
-
-  // locate x0: last n with hkv * s_pre[n] <= x0
-  int lo = 0, hi = n_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (static_cast<int64_t>(hkv) * s_pre[mid] <= x0) lo = mid; else hi = mid - 1;
-  }
-  TilePos cur;
-  cur.n = lo;
-  {
-    const int64_t rem = x0 - static_cast<int64_t>(hkv) * s_pre[lo];
-    const int nt = tiles_of(s_pre, lo);
-    cur.j = static_cast<int>(rem / nt);
-    cur.ti = static_cast<int>(rem - static_cast<int64_t>(cur.j) * nt);
-  }
-  int piece_start = cur.ti;  // first tile of the current piece
-  bool first_piece = true;
-
-  Acc<D> st;
-  reset(st);
-  // Two LDS stages per wave: while tile x is computed (from registers read
-  // out of one stage), tile x + 1's keys and values stream into the other
-  // stage and the table entries of tile x + 2 load as well.  These loads are
-  // unconditional (a missing successor repeats the current tile's addresses).
-  // The queries are those of the segment: loaded when a segment starts, not
-  // again for each of its tiles.
-  QOp<D> qc;
-  TilePos nxt = x1 - x0 > 1 ? advance(cur, s_pre, hkv) : cur;
-  Tb<NB> tbA = load_tb<B, TOK>(cur, block_tables, max_blocks, s_len);
-  Tb<NB> tbB = load_tb<B, TOK>(nxt, block_tables, max_blocks, s_len);
-  load_q<D, F8>(qc, cur, q, hq, g, r, gq);
-  dma_tile<D, B, F8>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
-  // FP8: the scales of a tile's blocks travel with it, one tile ahead like its Q
-  Sc8 scA{}, scB{};
-  if constexpr (F8) scA = load_scales<B>(tbA, k_scale, v_scale, cur.j, hkv, num_blocks, gq);
-
-  int64_t x = x0;
-  // One step: tile `cur` (staged in stage SC, blocks tbc) is computed while
-  // `nxt` streams into the other stage (its blocks tbn are known) and the
-  // table entries of the tile after it load into tb2.  Returns false after
-  // the last tile.
-  // the step's new token, for tiles that end a segment holding one
-  auto wants_new = [&](TilePos t) -> bool {
-    return !F8 && k_new != nullptr && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
-  };
-  // one buffer: a step patches its tile before it loads the next tile's token
-  NewTok<D> ntok;
-  if (wants_new(cur)) load_new<D>(ntok, cur, k_new, v_new, slots, hkv, r, gq);
-  auto step = [&](auto sc_tag, const Tb<NB>& tbc, const Sc8& scc, const Tb<NB>& tbn, Sc8& scn,
-                  Tb<NB>& tb2) -> bool {
-    constexpr int SC = decltype(sc_tag)::value;
-    unsigned char(&stc)[4][kStageBytes] = SC == 0 ? g_stage0 : g_stage1;
-    unsigned char(&stn)[4][kStageBytes] = SC == 0 ? g_stage1 : g_stage0;
-    // The compiler orders any LDS read after every outstanding LDS copy, so the
-    // current stage is read into registers first; the next tile's copies are
-    // issued after it and stay in flight through this tile's compute.
-    const bool has_next = x + 1 < x1;
-    const int packed = s_len[cur.n];
-    const int S = attended_tokens(packed);
-    const int nt_cur = tiles_of(s_pre, cur.n);
-    const TilePos nxt2 = x + 2 < x1 ? advance(nxt, s_pre, hkv) : nxt;
-    const int t0 = cur.ti * TOK;
-    if constexpr (F8) {
-      Buf8<D> b;
-      read_tile8<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
-      __builtin_amdgcn_sched_barrier(0);
-      tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
-      scn = load_scales<B>(tbn, k_scale, v_scale, nxt.j, hkv, num_blocks, gq);
-      dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
-      const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        f32x4 sco[2];
-        qk_tile8<D>(sco, b.k[u], qc);
-        const float sk[2] = {scale_log2 * scc.k[u][0], scale_log2 * scc.k[u][1]};
-        const float sv[2] = {scc.v[u][0], scc.v[u][1]};
-        pv_tile8<D>(st, sco, b.v[u], b.ok[u], t0 + 32 * u, S, full, sk, sv, gq);
-      }
-    } else {
-      Buf<D> b;
-      read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
-      // keep the stage's LDS reads ahead of the copies below: an LDS read issued
-      // after them would wait for all of them
-      __builtin_amdgcn_sched_barrier(0);
-      if (k_new != nullptr && has_new_token(packed) && cur.ti == nt_cur - 1) {
-        patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
-        // the row's slot, read from wherever the caller keeps it, goes on to the
-        // merge kernel (which stores the token): the slot when it is the row's
-        // next position, else -1
-        if (cur.j == 0 && lane == 0) {
-          const int S0 = pool_tokens(packed);
-          const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
-                               static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
-                               ntok.slot % B == S0 % B;
-          slots_out[cur.n] = at_next ? ntok.slot : -1;
-        }
-      }
-      tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
-      if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
-      dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
-      const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
-      f32x4 sco[2];
-      qk_tile<D>(sco, b, qc);
-      pv_tile<D>(st, sco, b, t0, S, full, scale_log2, gq);
-    }
-    const bool seg_end = cur.ti == nt_cur - 1;
-    if (seg_end || !has_next) {
-      flush<D>(st, cur, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, hq, g, r, gq);
-      first_piece = false;
-      piece_start = 0;
-    }
-    if (!has_next) return false;
-    if (seg_end) load_q<D, F8>(qc, nxt, q, hq, g, r, gq);  // the next segment's queries
-    ++x;
-    cur = nxt;
-    nxt = nxt2;
-    return true;
-  };
-  while (true) {
-    if (!step(std::integral_constant<int, 0>{}, tbA, scA, tbB, scB, tbA)) break;
-    if (!step(std::integral_constant<int, 1>{}, tbB, scB, tbA, scA, tbB)) break;
-  }
-}
-
-// Second kernel of a decode: one workgroup per (KV head, sequence) merges the
-// segment's pieces; for pa_decode_step it also stores the new token and moves
-// the row forward.
-template <int D>
-__global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ rec,
-                                                    const int32_t* __restrict__ prefix, uint16_t* __restrict__ out,
-                                                    int n_seqs, int hq, int hkv, int g, int64_t total_waves,
-                                                    AppendArgs ap) {
-  const int j = blockIdx.x;
-  const int n = blockIdx.y;
-  if (ap.k_new == nullptr) {
-    merge_segment<D>(rec, prefix, out, n_seqs, hq, hkv, g, g, total_waves, j, n);
-    return;
-  }
-  const RowToken<D> rt = load_row_token<D>(ap, n, j, hkv);  // in flight during the merge
-  merge_segment<D>(rec, prefix, out, n_seqs, hq, hkv, g, g, total_waves, j, n);
-  append_row<D>(ap, rt, n, j, hkv);
-}
-
 template <int D, int B>
 const void* stream_kernel() {
-  return reinterpret_cast<const void*>(&decode_stream<D, B, false>);
+  return reinterpret_cast<const void*>(&decode_stream<D, B, kKvBf16>);
 }
 
 const void* stream_kernel_for(int d, int b) {
@@ -528,51 +104,22 @@ StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int
   return p;
 }
 
-template <int D, int B, bool F8>
-static void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
-                             const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv,
-                             int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
-                             const float* k_scale, const float* v_scale) {
-  char* base = static_cast<char*>(ws);
-  int32_t* prefix = reinterpret_cast<int32_t*>(base + p.prefix_offset);
-  int32_t* slots_ws = reinterpret_cast<int32_t*>(base + p.slots_offset);
-  float* rec = reinterpret_cast<float*>(base + p.records_offset);
-  const int g = hq / hkv;
-  AppendArgs ap{};
-  const int32_t* slots_in = nullptr;
-  if (step) {
-    ap.k_pool = static_cast<uint16_t*>(const_cast<void*>(k));
-    ap.v_pool = static_cast<uint16_t*>(const_cast<void*>(v));
-    ap.k_new = static_cast<const uint16_t*>(step->k_new);
-    ap.v_new = static_cast<const uint16_t*>(step->v_new);
-    slots_in = step->slots;
-    ap.slots = slots_ws;  // the decode kernel copies each row's slot there
-    ap.block_tables = const_cast<int32_t*>(bt);
-    ap.context_lens = const_cast<int32_t*>(cl);
-    ap.max_blocks = max_blocks;
-    ap.block_size = B;
-  }
-  decode_stream<D, B, F8><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
-      static_cast<const uint16_t*>(q), k, v, bt, cl, static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g,
-      max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws, k_scale, v_scale);
-  merge_stream<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, prefix, static_cast<uint16_t*>(out), n, hq, hkv, g,
-                                                     static_cast<int64_t>(p.workgroups) * kSW, ap);
-}
-
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
                   int max_blocks, int num_blocks, float scale_log2, const StepInputs* step, const float* k_scale,
-                  const float* v_scale) {
-  const bool f8 = k_scale != nullptr;
-  if (f8 && step) return PA_ERR_UNSUPPORTED;
+                  const float* v_scale, int codes) {
+  if (codes != kKvBf16 && (step || !k_scale || !v_scale)) return PA_ERR_UNSUPPORTED;
+  if (codes == kKvInt8)
+    return launch_stream_int8(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, d, block_size, max_blocks, num_blocks,
+                              scale_log2, k_scale, v_scale);
 #define PA_STREAM_CASE(DD, BB)                                                                               \
   if (d == DD && block_size == BB) {                                                                         \
-    if (f8)                                                                                                  \
-      launch_stream_db<DD, BB, true>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,     \
-                                     scale_log2, nullptr, k_scale, v_scale);                                 \
+    if (codes == kKvE4m3)                                                                                    \
+      launch_stream_db<DD, BB, kKvE4m3>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,  \
+                                        scale_log2, nullptr, k_scale, v_scale);                              \
     else                                                                                                     \
-      launch_stream_db<DD, BB, false>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,    \
-                                      scale_log2, step, nullptr, nullptr);                                   \
+      launch_stream_db<DD, BB, kKvBf16>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,  \
+                                        scale_log2, step, nullptr, nullptr);                                 \
     return launch_status();                                                                                  \
   }
   PA_STREAM_CASE(128, 16)

@@ -130,13 +130,36 @@ __device__ __forceinline__ uint32_t e4m3_code(float x, float s) {
   return sign | mag;
 }
 
+// INT8 cache: x goes in under scale s as the integer nearest to the real
+// quotient x / s, ties to even, clamped to -127..127 (symmetric: negating x
+// negates the code), two's complement.  The quotient is formed in fp64, exact
+// for the decision by the argument above (a half-integer quotient of 24-bit x
+// and s is exact; any other lies far from every half-integer).  An 8-bit
+// integer has no NaN: NaN input, or a scale that is not positive and finite,
+// stores 0.
+__device__ __forceinline__ uint32_t i8_code(float x, float s) {
+  if (!(s > 0.f) || !(s < INFINITY) || x != x) return 0u;
+  const double y = static_cast<double>(x) / static_cast<double>(s);
+  const double c = y >= 127.0 ? 127.0 : (y <= -127.0 ? -127.0 : rint(y));  // rint: nearest, ties to even
+  return static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xFFu;
+}
+
+template <bool I8>
+__device__ __forceinline__ uint32_t code8(float x, float s) {
+  if constexpr (I8)
+    return i8_code(x, s);
+  else
+    return e4m3_code(x, s);
+}
+
 // One thread per (token, KV head, 4 consecutive elements): a 4-byte store of
 // four key codes (inside one 16-code chunk) and four one-byte value stores
 // (stride B).  Four elements per thread keep enough waves in flight to hide
 // the fp64 division of each element.  With block_tables non-null (a decode
 // step, token n = row n) the thread of (n, head 0, elements 0..3) also moves
 // the row forward, as append_step_kernel does.
-__global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+template <bool I8>
+__global__ __launch_bounds__(256) void append_codes_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          const float* __restrict__ k_scale,
                                                          const float* __restrict__ v_scale,
                                                          const uint16_t* __restrict__ k_new,
@@ -173,12 +196,12 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k
   const uint32_t vb[4] = {vin.x & 0xffffu, vin.x >> 16, vin.y & 0xffffu, vin.y >> 16};
   uint32_t kw = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) kw |= e4m3_code(bf16_bits_to_f32(kb[e]), ks) << (8 * e);
+  for (int e = 0; e < 4; ++e) kw |= code8<I8>(bf16_bits_to_f32(kb[e]), ks) << (8 * e);
   *reinterpret_cast<uint32_t*>(k_pool + ((head * (d / 16) + e0 / 16) * block_size + off) * 16 + e0 % 16) = kw;
   uint8_t* vdst = v_pool + (head * d + e0) * block_size + off;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    vdst[static_cast<int64_t>(e) * block_size] = static_cast<uint8_t>(e4m3_code(bf16_bits_to_f32(vb[e]), vs));
+    vdst[static_cast<int64_t>(e) * block_size] = static_cast<uint8_t>(code8<I8>(bf16_bits_to_f32(vb[e]), vs));
 }
 
 // grid = (ceil((2 * n16 + 2 * scales_per_block) / 256), num_pairs, num_layers);
@@ -336,10 +359,13 @@ extern "C" int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst
   return launch_status();
 }
 
-extern "C" int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
-                                const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
-                                int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
-  using namespace pa;
+namespace pa {
+namespace {
+
+template <bool I8>
+int append_codes(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+                 const void* v_new, const int32_t* slot_mapping, int num_tokens, int Hkv, int d_head, int block_size,
+                 int num_blocks, void* stream) {
   if (num_tokens < 0 || num_blocks < 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
   if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
@@ -347,18 +373,18 @@ extern "C" int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale
   const int64_t threads = static_cast<int64_t>(num_tokens) * Hkv * (d_head / 4);
   const int64_t grid = (threads + 255) / 256;
   if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
-  append_fp8_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+  append_codes_kernel<I8><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scale, v_scale,
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, num_tokens, Hkv, d_head,
       block_size, static_cast<int64_t>(num_blocks) * block_size, nullptr, nullptr, 0);
   return launch_status();
 }
 
-extern "C" int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
-                                  const void* k_new, const void* v_new, const int32_t* slot_mapping,
-                                  int32_t* block_tables, int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
-                                  int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
-  using namespace pa;
+template <bool I8>
+int append_step_codes(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+                      const void* v_new, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                      int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
+                      void* stream) {
   if (num_seqs < 0 || num_blocks < 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
   if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
@@ -369,11 +395,46 @@ extern "C" int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_sca
   const int64_t threads = static_cast<int64_t>(num_seqs) * Hkv * (d_head / 4);
   const int64_t grid = (threads + 255) / 256;
   if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
-  append_fp8_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+  append_codes_kernel<I8><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scale, v_scale,
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, num_seqs, Hkv, d_head,
       block_size, static_cast<int64_t>(num_blocks) * block_size, block_tables, context_lens, max_blocks_per_seq);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                                const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+                                int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
+  return pa::append_codes<false>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, num_tokens, Hkv,
+                                 d_head, block_size, num_blocks, stream);
+}
+
+extern "C" int pa_append_kv_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                                 const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+                                 int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
+  return pa::append_codes<true>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, num_tokens, Hkv,
+                                d_head, block_size, num_blocks, stream);
+}
+
+extern "C" int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                                  const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                  int32_t* block_tables, int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
+                                  int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
+  return pa::append_step_codes<false>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables,
+                                      context_lens, num_seqs, max_blocks_per_seq, Hkv, d_head, block_size, num_blocks,
+                                      stream);
+}
+
+extern "C" int pa_append_step_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                                   const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                   int32_t* block_tables, int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
+                                   int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
+  return pa::append_step_codes<true>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables,
+                                     context_lens, num_seqs, max_blocks_per_seq, Hkv, d_head, block_size, num_blocks,
+                                     stream);
 }
 
 extern "C" int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
@@ -457,4 +518,25 @@ extern "C" int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst
                    1, src_num_blocks, dst_num_blocks, num_layers, src_layer_stride_elems, dst_layer_stride_elems,
                    dst_k_scale, dst_v_scale, src_k_scale, src_v_scale, src_scale_layer_stride, dst_scale_layer_stride,
                    stream);
+}
+
+// An INT8 cache moves as an FP8 cache does: one-byte codes and their scales.
+extern "C" int pa_copy_blocks_int8(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                   const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size,
+                                   int num_blocks, int num_layers, int64_t layer_stride_elems,
+                                   int64_t scale_layer_stride, void* stream) {
+  return pa_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, num_pairs, Hkv, d_head, block_size,
+                            num_blocks, num_layers, layer_stride_elems, scale_layer_stride, stream);
+}
+
+extern "C" int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
+                                   const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
+                                   const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv,
+                                   int d_head, int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
+                                   int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems,
+                                   int64_t src_scale_layer_stride, int64_t dst_scale_layer_stride, void* stream) {
+  return pa_swap_blocks_fp8(dst_k_pool, dst_v_pool, dst_k_scale, dst_v_scale, src_k_pool, src_v_pool, src_k_scale,
+                            src_v_scale, src_dst_pairs, num_pairs, Hkv, d_head, block_size, src_num_blocks,
+                            dst_num_blocks, num_layers, src_layer_stride_elems, dst_layer_stride_elems,
+                            src_scale_layer_stride, dst_scale_layer_stride, stream);
 }

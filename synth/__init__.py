@@ -27,6 +27,11 @@ uniform mantissa, the NaN magnitude 0x7F replaced by 0x7E -- the shape of
 amax-scaled normal data -- and fp32 scales value_scale / 78 * U(0.5, 2) per
 (block, KV head), 78 being the RMS of those code values, so that the values
 the cache stands for have an RMS of about value_scale.
+
+INT8 caches (signed codes with per-(block, KV head) scales) are drawn as codes
+round(N(0, 36^2)) clamped to -127..127 -- amax-scaled normal data, the largest
+of a block's 2048 values (about 3.5 standard deviations) near 127 -- and fp32
+scales value_scale / 36 * U(0.5, 2), for values of RMS about value_scale.
 """
 
 from __future__ import annotations
@@ -175,6 +180,37 @@ def fill_fp8_codes_(t, seed: int, chunk_rows: int = 0):
         mag = torch.where(mag == 0x7F, torch.full_like(mag, 0x7E), mag)
         t[start:stop].copy_((sign * 0x80 + mag).to(torch.uint8))
     return t
+
+
+INT8_CODE_RMS = 36.0
+
+
+def fill_int8_codes_(t, seed: int, chunk_rows: int = 0):
+    """Fill a uint8 tensor in place with random INT8 codes (two's complement bytes); see the module docstring.
+
+    Drawn on the tensor's device, chunk by chunk along dim 0 (seed per chunk).
+    """
+    import torch
+    rows = t.shape[0]
+    if chunk_rows <= 0:
+        chunk_rows = max(1, (1 << 26) // max(1, t[0].numel()))
+    g = torch.Generator(device=t.device)
+    for i, start in enumerate(range(0, rows, chunk_rows)):
+        stop = min(rows, start + chunk_rows)
+        g.manual_seed(seed * 1000003 + i)
+        shape = tuple(t[start:stop].shape)
+        c = torch.round(torch.randn(shape, generator=g, device=t.device) * INT8_CODE_RMS).clamp_(-127, 127)
+        t[start:stop].copy_(c.to(torch.int32).bitwise_and(0xFF).to(torch.uint8))
+    return t
+
+
+def int8_scales(num_blocks: int, hkv: int, value_scale: float, seed: int, device="cpu"):
+    """float32 [num_blocks][hkv] scales value_scale / INT8_CODE_RMS * U(0.5, 2)."""
+    import torch
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    u = torch.rand((num_blocks, hkv), generator=g) * 1.5 + 0.5
+    return (u * (value_scale / INT8_CODE_RMS)).to(torch.float32).to(device)
 
 
 def fp8_scales(num_blocks: int, hkv: int, value_scale: float, seed: int, device="cpu"):

@@ -20,6 +20,7 @@ import torch
 import synth
 from oracle import attention as OA
 from oracle import fp8 as OF
+from oracle import int8 as OI
 from oracle.block_manager import BlockManagerModel
 from pool_layout import k_to_logical, poison_unused_
 
@@ -48,11 +49,13 @@ class DecodeCase:
     tables_dev: torch.Tensor
     lens_dev: torch.Tensor
     scale: float
-    k_scale: Optional[torch.Tensor] = None   # FP8 cache: float32 [nb][Hkv] device scales
+    k_scale: Optional[torch.Tensor] = None   # FP8 or INT8 cache: float32 [nb][Hkv] device scales
     v_scale: Optional[torch.Tensor] = None
+    codes: str = ""                          # "e4m3" or "int8" for a cache of one-byte codes
 
     @property
     def fp8(self):
+        """The cache holds one-byte codes with scales (E4M3 or INT8)."""
         return self.k_scale is not None
 
     @property
@@ -62,8 +65,9 @@ class DecodeCase:
 
 def make_case(w: synth.Workload, lens: Optional[Sequence[int]] = None, *, hq=None, hkv=None, d=None,
               block_size=None, dtype=None, num_blocks=None, max_blocks=None, layers=1, poison=True,
-              device="cuda", seed=None, fp8=False) -> DecodeCase:
-    """A seeded decode batch on both block managers; ``fp8`` gives a cache of E4M3 codes with scales and bf16 q."""
+              device="cuda", seed=None, fp8=False, int8=False) -> DecodeCase:
+    """A seeded decode batch on both block managers; ``fp8`` / ``int8`` give a cache of E4M3 / INT8 codes with
+    scales and bf16 q."""
     import paged_kv_cache_124_amd as pa
 
     hq = hq or w.hq
@@ -91,15 +95,17 @@ def make_case(w: synth.Workload, lens: Optional[Sequence[int]] = None, *, hq=Non
     tables = np.zeros((len(lens), max_blocks), dtype=np.int32)
     tables[ids] = t_ids
 
-    if fp8:
-        assert layers == 1
+    if fp8 or int8:
+        assert layers == 1 and not (fp8 and int8)
+        fill = synth.fill_int8_codes_ if int8 else synth.fill_fp8_codes_
+        scales = synth.int8_scales if int8 else synth.fp8_scales
         kshape, vshape = pa.pool_shapes(num_blocks, hkv, d, bs, 1)
-        k = synth.fill_fp8_codes_(torch.empty(kshape, dtype=torch.uint8, device=device), seed * 10 + 1)
-        v = synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8, device=device), seed * 10 + 2)
-        ks = synth.fp8_scales(num_blocks, hkv, w.value_scale, seed * 10 + 4, device)
-        vs = synth.fp8_scales(num_blocks, hkv, w.value_scale, seed * 10 + 5, device)
-        if poison:  # NaN codes in unused blocks and tail slots, NaN scales on unused blocks
-            poison_unused_(k, v, tables, lens, bs, value=0x7F)
+        k = fill(torch.empty(kshape, dtype=torch.uint8, device=device), seed * 10 + 1)
+        v = fill(torch.empty(vshape, dtype=torch.uint8, device=device), seed * 10 + 2)
+        ks = scales(num_blocks, hkv, w.value_scale, seed * 10 + 4, device)
+        vs = scales(num_blocks, hkv, w.value_scale, seed * 10 + 5, device)
+        if poison:  # NaN (E4M3) or -128 (INT8) codes in unused blocks and tail slots, NaN scales on unused blocks
+            poison_unused_(k, v, tables, lens, bs, value=0x80 if int8 else 0x7F)
             used = torch.zeros(num_blocks, dtype=torch.bool)
             for row, s in zip(tables, lens):
                 used[torch.as_tensor(row[: -(-int(s) // bs)], dtype=torch.long)] = True
@@ -108,7 +114,7 @@ def make_case(w: synth.Workload, lens: Optional[Sequence[int]] = None, *, hq=Non
         q = synth.randn((len(lens), hq, d), torch.bfloat16, w.value_scale, seed * 10 + 3, device)
         return DecodeCase(w, lens, hq, hkv, d, bs, torch.uint8, num_blocks, max_blocks, bm, model, tables, k, v, q,
                           torch.from_numpy(tables).to(device), torch.tensor(lens, dtype=torch.int32, device=device),
-                          1.0 / math.sqrt(d), ks, vs)
+                          1.0 / math.sqrt(d), ks, vs, "int8" if int8 else "e4m3")
     elem = torch.tensor([], dtype=dtype).element_size()
     kshape, vshape = pa.pool_shapes(num_blocks, hkv, d, bs, elem)
     if layers > 1:
@@ -138,7 +144,8 @@ def run_decode(case: DecodeCase, layer: Optional[int] = None, q=None, out=None, 
     lens_dev = case.lens_dev if lens_dev is None else lens_dev
     max_ctx = case.max_ctx if max_ctx is None else max_ctx
     if case.fp8:
-        pa.pa_decode_fp8(out, q, k, v, case.k_scale, case.v_scale, tables_dev, lens_dev, case.scale, max_ctx)
+        dec = pa.pa_decode_int8 if case.codes == "int8" else pa.pa_decode_fp8
+        dec(out, q, k, v, case.k_scale, case.v_scale, tables_dev, lens_dev, case.scale, max_ctx)
     else:
         pa.pa_decode(out, q, k, v, tables_dev, lens_dev, case.scale, max_ctx)
     return out
@@ -202,7 +209,8 @@ def _oracle_outputs_fp8(case: DecodeCase, seqs, q, lens, tables) -> np.ndarray:
             kc = vc = np.zeros((0, case.hkv, case.block_size, case.d), np.uint8)
             ks = vs = np.zeros((0, case.hkv))
         tab = np.arange(max(nb, 1)).reshape(1, -1)
-        outs.append(OF.paged_decode(q[n:n + 1], kc, vc, ks, vs, tab, [s], case.scale)[0])
+        oracle = OI if case.codes == "int8" else OF
+        outs.append(oracle.paged_decode(q[n:n + 1], kc, vc, ks, vs, tab, [s], case.scale)[0])
     return np.stack(outs)
 
 

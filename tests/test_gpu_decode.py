@@ -87,21 +87,21 @@ def test_run_to_run_bit_identical():
 EDGE_LENS = [0, 1, 2, 7, 8, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 1500]
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_workspace_contents_do_not_matter(fp8):
+@pytest.mark.parametrize("codes", ["bf16", "e4m3", "int8"])
+def test_workspace_contents_do_not_matter(codes):
     """Every word of the workspace that a call reads it has written first: a second call over a workspace whose
     every byte is 0xFF (NaN as floats) gives the same bits.  Lengths from 0 to 4000 tokens put segments in one
     wave's range and across up to 8, 9 to 16 and more ranges (each merge path), next to empty rows."""
     import paged_kv_cache_124_amd as pa
     rng = np.random.default_rng(44)
     lens = [0, 1, 31, 32, 33, 2048, 4000, 12000, 24000] + [int(x) for x in rng.integers(256, 2049, size=120)]
-    print(f"[case] workspace poison fp8={fp8}", flush=True)
-    c = make_case(synth.gqa8b(), lens, seed=1144, fp8=fp8)
+    print(f"[case] workspace poison {codes}", flush=True)
+    c = make_case(synth.gqa8b(), lens, seed=1144, fp8=codes == "e4m3", int8=codes == "int8")
     out = torch.empty_like(c.q)
-    if fp8:
-        args, ws = pa.pa_decode_fp8_args(out, c.q, c.k, c.v, c.k_scale, c.v_scale, c.tables_dev, c.lens_dev,
-                                         c.scale, c.max_ctx)
-        call = pa.lib.pa_decode_fp8
+    if codes != "bf16":
+        make = pa.pa_decode_int8_args if codes == "int8" else pa.pa_decode_fp8_args
+        args, ws = make(out, c.q, c.k, c.v, c.k_scale, c.v_scale, c.tables_dev, c.lens_dev, c.scale, c.max_ctx)
+        call = pa.lib.pa_decode_int8 if codes == "int8" else pa.lib.pa_decode_fp8
     else:
         args, ws = pa.pa_decode_args(out, c.q, c.k, c.v, c.tables_dev, c.lens_dev, c.scale, c.max_ctx)
         call = pa.lib.pa_decode
@@ -114,7 +114,7 @@ def test_workspace_contents_do_not_matter(fp8):
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), out.view(torch.int16))
     assert torch.count_nonzero(out[0].float()) == 0
-    assert_close(out, oracle_outputs(c, range(len(lens))), f"workspace poison fp8={fp8}")
+    assert_close(out, oracle_outputs(c, range(len(lens))), f"workspace poison {codes}")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
