@@ -48,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: achieved HBM GB/s (KV read) + µs/step, 8B GQA shape"
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 10
+EVENT_SPAN = 10  # steps per event pair on workloads whose steps launch nothing but the decode
 RING = 32
 
 
@@ -289,23 +290,23 @@ class Runner:
                 ca[5] = npairs
                 assert (L.pa_copy_blocks_int8 if self.int8 else L.pa_copy_blocks_fp8)(*ca) == 0
             assert (L.pa_append_step_int8 if self.int8 else L.pa_append_step_fp8)(*self.append_args[r, k]) == 0
-            if timing is not None:
+            if timing is not None and timing[0] is not None:
                 timing[0].record()
             assert (L.pa_decode_int8 if self.int8 else L.pa_decode_fp8)(*self.step_args[r, k]) == 0
-            if timing is not None:
+            if timing is not None and timing[1] is not None:
                 timing[1].record()
         else:
             if npairs:
                 ca = self.copy_args[r, k]
                 ca[3] = npairs
                 assert L.pa_copy_blocks(*ca) == 0
-            if timing is not None:
+            if timing is not None and timing[0] is not None:
                 timing[0].record()
             if self.shared:
                 assert L.pa_decode_step_shared(*self.step_args[r, k]) == 0
             else:
                 assert L.pa_decode_step(*self.step_args[r, k]) == 0
-            if timing is not None:
+            if timing is not None and timing[1] is not None:
                 timing[1].record()
         if k % half == half - 1:
             self.half_ev[k // half].record()
@@ -514,23 +515,44 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # pa_decode is bracketed by events on every EVENT_EVERY-th step (on the stream it is
-    # launched on); an event record costs the stream a few microseconds, so not every
-    # step carries them
+    # The decode is bracketed by events on the stream it is launched on.  An event
+    # record costs the stream a few microseconds, part of it inside the bracket, so
+    # where a step launches nothing but the decode (bf16 without copy-on-write) one
+    # pair brackets EVENT_SPAN consecutive steps, placed between the ring's own
+    # event records; elsewhere (an append or copy kernel between decodes) one pair
+    # brackets the decode of every EVENT_EVERY-th step.
     long_ctx = w.name == "long"
+    span = EVENT_SPAN if not (long_ctx or run.fp8 or run.fork) else 1
     sampled = list(range(0, args.steps, 1 if long_ctx else EVENT_EVERY))  # a long step is ~12 ms: events every step
     timing = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
+    spans, open_span = [], None  # [start event, end event, steps, bytes]
     torch.cuda.synchronize()
     run.host_s = 0.0
     t0 = time.perf_counter()
     e0.record()
     kv_bytes, sampled_bytes = 0, 0
     for i in range(args.steps):
-        ev = timing.get(i)
+        if span == 1:
+            ev = timing.get(i)
+        else:
+            pos = run.step_i % (RING // 2)  # the ring's event is recorded after the step at pos RING / 2 - 1
+            start = end = None
+            if open_span is None and pos == 0 and i + span <= args.steps:
+                open_span = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), 0, 0]
+                start = open_span[0]
+            if open_span is not None and pos == span - 1:
+                end = open_span[1]
+            ev = (start, end) if (start is not None or end is not None) else None
         step_bytes = run.step(ev)
         kv_bytes += step_bytes
-        if ev is not None:
+        if span == 1 and ev is not None:
             sampled_bytes += step_bytes
+        if open_span is not None:
+            open_span[2] += 1
+            open_span[3] += step_bytes
+            if ev is not None and ev[1] is not None:
+                spans.append(open_span)
+                open_span = None
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -538,7 +560,11 @@ def main():
     gpu_ms = e0.elapsed_time(e1)
     ms_step = max(gpu_ms, wall * 1e3) / args.steps
     value = kv_bytes / args.steps / (ms_step * 1e-3) / 1e9
-    dec_us = [1e3 * a.elapsed_time(b) for a, b in timing.values()]
+    if span == 1:
+        dec_us = [1e3 * a.elapsed_time(b) for a, b in timing.values()]
+    else:  # per-launch averages of the spans, each counted once per step it covers
+        dec_us = [1e3 * a.elapsed_time(b) / n for a, b, n, _ in spans for _ in range(n)]
+        sampled_bytes = sum(b for _, _, _, b in spans)
     dec_avg_us = sum(dec_us) / len(dec_us)
     bytes_per_launch = kv_bytes / args.steps
     achieved = sampled_bytes / (sum(dec_us) * 1e-6) / 1e9
