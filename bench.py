@@ -101,6 +101,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (known bytes) to scale HBM counters")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="run only pa_read_probe over 4 GiB: the achievable HBM read rate of this GPU")
     return ap.parse_args()
 
 
@@ -495,6 +497,24 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
                           "launches": 5}))
+        return
+    if args.read_ceiling:
+        import paged_kv_cache_124_amd as pa
+        buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")  # 4 GiB, 16x the Infinity Cache
+        sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+        rates = {}
+        for wgs in (256, 512, 1024, 2048):  # 4, 8, 16, 32 waves per CU on 256 CUs
+            for _ in range(3):
+                pa.pa_read_probe(buf, sink, wgs)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(20):
+                pa.pa_read_probe(buf, sink, wgs)
+            b.record()
+            torch.cuda.synchronize()
+            rates[wgs] = round(buf.numel() * 4 * 20 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+        print(json.dumps({"read_ceiling_gb_s": max(rates.values()), "by_workgroups": rates, "bytes": buf.numel() * 4,
+                          "launches": 20, "peak_gb_s": HBM_PEAK_GBS}))
         return
     w = workload(args.workload)
     total = args.steps + args.warmup + 1

@@ -434,6 +434,19 @@ int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, 
                         int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, int64_t src_scale_layer_stride,
                         int64_t dst_scale_layer_stride, void* stream);
 
+/* ---- measurement ---------------------------------------------------------------
+ *
+ * pa_read_probe: the achievable HBM read rate, against which the decode
+ * kernels' rates are read (the decode is a bandwidth-bound gather, "PagedAttention:
+ * Virtual Memory for the KV Cache", section 13).  Reads every byte of `buf`
+ * (device, `bytes` a multiple of 4096) once: wave w of the `workgroups`
+ * workgroups of 256 threads reads the 4 KiB pieces w, w + W, ... (W waves),
+ * four pieces of 16-byte loads in flight, and one word per workgroup goes to
+ * `sink` (device, uint32 [workgroups]).  Asynchronous on `stream`; time it
+ * with events.
+ */
+int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
+
 /* ---- host block manager ------------------------------------------------------
  *
  * Free list, per-block reference counts, block tables, fork and copy-on-write

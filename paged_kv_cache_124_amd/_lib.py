@@ -88,6 +88,7 @@ _SIGS = {
     "pa_append_step_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
     "pa_swap_blocks": (c_int, [c_void_p] * 5 + [c_int] * 8 + [c_int64, c_int64, c_void_p]),
     "pa_swap_blocks_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
+    "pa_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
     "pa_decode_int8": (c_int, [c_void_p] * 8 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
     "pa_append_kv_int8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
     "pa_copy_blocks_int8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
@@ -680,6 +681,18 @@ def pa_copy_blocks_int8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=
     """pa_copy_blocks_int8 of include/pa.h: INT8 codes and scales of each src block over its dst."""
     _check(lib.pa_copy_blocks_int8(*pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs,
                                                             stream)), "pa_copy_blocks_int8")
+
+
+def pa_read_probe(buf, sink, workgroups=2048, stream=None):
+    """pa_read_probe of include/pa.h: stream every byte of the device tensor ``buf`` once (the HBM read ceiling).
+
+    ``sink`` is an int32 device tensor (one word per workgroup) of at least ``workgroups`` entries."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < workgroups:
+        raise ValueError("buf must be a contiguous device tensor and sink an int32 tensor of >= workgroups entries")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.pa_read_probe(c_void_p(buf.data_ptr()), nbytes, _dev(sink, "sink"), workgroups, _stream_ptr(stream)),
+           "pa_read_probe")
 
 
 # ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 
-HIP_SOURCES = ["decode.hip", "decode_stream.hip", "decode_stream_i8.hip", "decode_shared.hip", "kv_ops.hip"]
+HIP_SOURCES = ["decode.hip", "decode_stream.hip", "decode_stream_i8.hip", "decode_shared.hip", "kv_ops.hip", "probe.hip"]
 HOST_SOURCES = ["block_manager.cpp", "status.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops on its own.
