@@ -9,7 +9,7 @@ logical pool layout
 so that ``k_pool[pb, j, off, :]`` is the key of the token stored in slot
 ``off`` of physical block ``pb`` for KV head ``j``.
 
-Readings of the pages taken here (each also listed in the design doc):
+Readings of the pages taken here:
   * GQA head mapping: query head ``h`` reads KV head ``h // (Hq // Hkv)``
     (consecutive query heads share a KV head).  [P2] section 7 only says that
     several query heads share one KV head.

@@ -20,7 +20,7 @@ Rules, as the pages state them:
   * Running out of free blocks fails the operation and changes nothing
     ([P1] section 20, test 4: exhaustion leaves the sequence untouched).
 
-Readings taken where the pages leave a detail open (also in the design doc):
+Readings taken where the pages leave a detail open:
   * The free list is a LIFO stack: the most recently released block is handed
     out first.  [P1]'s teaching model pops from the end of a list that starts
     as the block ids in reverse order, so with no explicit order blocks
@@ -390,7 +390,7 @@ class PrefixCachingModel(BlockManagerModel):
     under pressure reclaims idle cached blocks before it fails ([P1] section
     19).
 
-    Readings where the pages leave details open (also in the design doc):
+    Readings where the pages leave details open:
       * A cached block is keyed by the exact token ids from the start of the
         sequence to its own end (its chain).  Only full blocks are cached; a
         lookup takes the longest run of leading full blocks whose chains are

@@ -13,8 +13,8 @@ KV is a precision tradeoff of its own).  So the attention of a quantized cache i
 values the cache holds: the oracle dequantizes every stored code and then runs
 the ordinary fp64 paged decode of ``oracle.attention``.
 
-The pages do not name the 8-bit format or the scaling.  Readings taken here
-(each also listed in the design doc):
+The pages do not name the 8-bit format or the scaling.  Readings taken
+here:
   * Format: FP8 E4M3 as in the OCP 8-bit floating point specification -- one
     sign bit, four exponent bits with bias 7, three mantissa bits, subnormals
     at exponent field 0, no infinities, and the two codes 0x7F / 0xFF (all

@@ -12,8 +12,8 @@ precision.  As for the FP8 cache, the attention of an INT8 cache is the exact
 attention over the values the cache holds: the oracle dequantizes every
 stored code and runs the ordinary fp64 paged decode of ``oracle.attention``.
 
-The pages fix neither the integer range nor the scaling.  Readings taken here
-(each also listed in the design doc):
+The pages fix neither the integer range nor the scaling.  Readings taken
+here:
   * Codes: signed 8-bit two's complement integers; a stored code c stands for
     c * scale.  The appender writes only -127 .. 127 (symmetric, so negating
     a value negates its code); a stored -128 still stands for -128 * scale.
