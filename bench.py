@@ -19,14 +19,14 @@ timed region starts.  `value` is the KV bytes the decode reads per step
 wall-clock time of a step.
 
 With --kv fp8 the cache holds FP8 (E4M3) codes with per-(block, KV head)
-scales and steps 3-4 are pa_copy_blocks_fp8 (when there are pairs),
-pa_append_step_fp8 (quantizing append, rows moved forward) and
-pa_decode_fp8; the KV bytes per step are then the codes (1 byte per element)
+scales and steps 3-4 are pa_copy_blocks_fp8 (when there are pairs) and
+pa_decode_step_fp8 (attention to the new tokens as codes, then the codes
+stored and the rows moved forward); the KV bytes per step are then the codes (1 byte per element)
 plus the 8 bytes of scales per (block, KV head) the contexts span.
 
 With --kv int8 the cache holds INT8 codes with the same scales and layout and
-the INT8 entry points (pa_copy_blocks_int8, pa_append_step_int8,
-pa_decode_int8) take their places.
+the INT8 entry points (pa_copy_blocks_int8, pa_decode_step_int8) take their
+places.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa8b] [--kv bf16|fp8|int8]
 """
@@ -58,7 +58,7 @@ TRAFFIC_FILES = {"bf16": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_tra
                  "fp8": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_fp8_traffic.txt"),
                  "int8": os.path.join(ROOT, "profiles", "decode_stream_gqa8b_int8_traffic.txt")}
 KERNEL_SOURCES = ["decode_stream.hip", "decode_stream_kernel.h", "decode_stream_i8.hip", "decode_stream.h", "decode_tile.h",
-                  "decode.hip", "common.h"]
+                  "decode.hip", "common.h", "codes.h"]
 
 
 def measured_traffic(workload_name, kv_kind="bf16"):
@@ -241,11 +241,7 @@ class Runner:
         for r in range(replicas):
             if self.fp8:
                 cpy = pa.pa_copy_blocks_fp8_args(self.k[r], self.v[r], self.ks[r], self.vs[r], check[n:3 * n].view(n, 2))
-                app = pa.pa_append_step_fp8_args(self.k[r], self.v[r], self.ks[r], self.vs[r], self.k_new, self.v_new,
-                                                 check[:n], self.d_tables, self.d_lens)
-                dec_args = pa.pa_decode_int8_args if self.int8 else pa.pa_decode_fp8_args
-                dec, _ = dec_args(self.out, self.q, self.k[r], self.v[r], self.ks[r], self.vs[r],
-                                  self.d_tables, self.d_lens, w.scale, self.max_ctx, workspace=self.ws)
+                step_codes_args = pa.pa_decode_step_int8_args if self.int8 else pa.pa_decode_step_fp8_args
             else:
                 cpy = pa.pa_copy_blocks_args(self.k[r], self.v[r], check[n:3 * n].view(n, 2))
             for b in range(RING):
@@ -254,8 +250,10 @@ class Runner:
                 self.copy_args[r, b] = (list(cpy[:pairs_at]) + [ctypes.c_void_p(base + 4 * n)] +
                                         list(cpy[pairs_at + 1:]))
                 if self.fp8:
-                    self.append_args[r, b] = app[:6] + (ctypes.c_void_p(base),) + app[7:]
-                    self.step_args[r, b] = dec
+                    self.step_args[r, b], _ = step_codes_args(
+                        self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], self.ks[r], self.vs[r],
+                        check[:n], self.d_tables, self.d_lens, w.scale, self.max_ctx, workspace=self.ws,
+                        slot_pointer=base)
                 elif self.shared:
                     self.step_args[r, b], _ = pa.pa_decode_step_shared_args(
                         self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], check[:n], self.d_tables,
@@ -291,10 +289,9 @@ class Runner:
                 ca = self.copy_args[r, k]
                 ca[5] = npairs
                 assert (L.pa_copy_blocks_int8 if self.int8 else L.pa_copy_blocks_fp8)(*ca) == 0
-            assert (L.pa_append_step_int8 if self.int8 else L.pa_append_step_fp8)(*self.append_args[r, k]) == 0
             if timing is not None and timing[0] is not None:
                 timing[0].record()
-            assert (L.pa_decode_int8 if self.int8 else L.pa_decode_fp8)(*self.step_args[r, k]) == 0
+            assert (L.pa_decode_step_int8 if self.int8 else L.pa_decode_step_fp8)(*self.step_args[r, k]) == 0
             if timing is not None and timing[1] is not None:
                 timing[1].record()
         else:
@@ -537,12 +534,12 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # The decode is bracketed by events on the stream it is launched on.  An event
     # record costs the stream a few microseconds, part of it inside the bracket, so
-    # where a step launches nothing but the decode (bf16 without copy-on-write) one
-    # pair brackets EVENT_SPAN consecutive steps, placed between the ring's own
-    # event records; elsewhere (an append or copy kernel between decodes) one pair
-    # brackets the decode of every EVENT_EVERY-th step.
+    # where a step launches nothing but the decode step's two kernels (no
+    # copy-on-write) one pair brackets EVENT_SPAN consecutive steps, placed between
+    # the ring's own event records; elsewhere (the fork workload's copies, the long
+    # workload's appends) one pair brackets the decode of every EVENT_EVERY-th step.
     long_ctx = w.name == "long"
-    span = EVENT_SPAN if not (long_ctx or run.fp8 or run.fork) else 1
+    span = EVENT_SPAN if not (long_ctx or run.fork) else 1
     sampled = list(range(0, args.steps, 1 if long_ctx else EVENT_EVERY))  # a long step is ~12 ms: events every step
     timing = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     spans, open_span = [], None  # [start event, end event, steps, bytes]
@@ -635,7 +632,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic[0]),
                      "traffic_algorithmic": None if traffic is None else int(traffic[1]),
-                     "kernel": f"pa_decode_{args.kv} (decode kernel + merge kernel)" if fp8 else
+                     "kernel": f"pa_decode_step_{args.kv} (decode kernel + merge/append kernel)" if fp8 else
                                ("pa_decode_step_shared (shared-prefix decode kernel + merge/append kernel)"
                                 if args.shared else
                                 (f"pa_decode x {w.layers} layers (decode kernel + merge kernel each)" if long_ctx

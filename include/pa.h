@@ -336,6 +336,33 @@ int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const f
                        int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
                        void* stream);
 
+/* pa_decode_step over an FP8 cache: one whole decode step of the batch
+ * ("PagedAttention: Virtual Memory for the KV Cache", sections 13 and 16).
+ * Row n attends to its S cached tokens and to its new token (bf16 k_new /
+ * v_new [num_seqs][Hkv][d_head]) as the cache will hold it: the codes
+ * pa_append_kv_fp8 stores for it under the scales of the block its slot
+ * lies in, slot = slot_mapping[n] (device-readable, as for pa_decode_step).
+ * Then those codes are stored and the row moved forward as pa_append_step_fp8
+ * does.  Where every slot is its row's next position the codes, tables and
+ * lengths are bit for bit those of pa_append_step_fp8, and the output is the
+ * attention over the cache that append leaves (the decode kernel attends to
+ * the cached tokens, the merge kernel adds the new token as one more piece,
+ * so the output bits may differ from pa_append_step_fp8 + pa_decode_fp8
+ * within the decode's tolerance).  A row whose slot lies outside
+ * [0, num_blocks * block_size)
+ * has no block whose scales its codes could use: it attends to its S cached
+ * tokens only (S = 0 gives zeros), and its codes, table and length stay.
+ * A row whose slot is in the pool but not its next position attends to its
+ * new token and keeps its table and length (its codes are not stored).
+ * Scales of the blocks the slots lie in must be set before the call.  Other
+ * arguments, the workspace (dtype PA_FP8_E4M3), shapes and errors as for
+ * pa_decode_fp8 and pa_decode_step. */
+int pa_decode_step_fp8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       const float* k_scale, const float* v_scale, const int32_t* slot_mapping, int32_t* block_tables,
+                       int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                       int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* pa_copy_blocks for an FP8 cache: codes of block src over block dst, and its
  * scales with them, k_scale[dst][*] = k_scale[src][*] and likewise v_scale
  * ("PagedAttention: Virtual Memory for the KV Cache", sections 15-16).
@@ -386,6 +413,13 @@ int pa_append_step_int8(void* k_pool, void* v_pool, const float* k_scale, const 
                         const void* v_new, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
                         int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
                         void* stream);
+
+/* pa_decode_step_fp8 over an INT8 cache (workspace: dtype PA_INT8). */
+int pa_decode_step_int8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const float* k_scale, const float* v_scale, const int32_t* slot_mapping,
+                        int32_t* block_tables, int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head,
+                        int block_size, float scale, int max_blocks_per_seq, int max_context_len, int num_blocks,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* pa_copy_blocks for an INT8 cache: codes and scales of block src over block
  * dst, exactly as pa_copy_blocks_fp8 (the copy moves bytes and scales,

@@ -89,6 +89,10 @@ _SIGS = {
     "pa_swap_blocks": (c_int, [c_void_p] * 5 + [c_int] * 8 + [c_int64, c_int64, c_void_p]),
     "pa_swap_blocks_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
     "pa_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
+    "pa_decode_step_fp8": (c_int, [c_void_p] * 11 + [c_int] * 5 + [c_float] + [c_int] * 3 +
+                           [c_void_p, c_size_t, c_void_p]),
+    "pa_decode_step_int8": (c_int, [c_void_p] * 11 + [c_int] * 5 + [c_float] + [c_int] * 3 +
+                            [c_void_p, c_size_t, c_void_p]),
     "pa_decode_int8": (c_int, [c_void_p] * 8 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
     "pa_append_kv_int8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
     "pa_copy_blocks_int8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
@@ -579,6 +583,59 @@ def pa_decode_int8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, conte
     args, _ws = pa_decode_int8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
                                     max_context_len, workspace, stream)
     _check(lib.pa_decode_int8(*args), "pa_decode_int8")
+    return out
+
+
+def _decode_step_codes_args(dtype_code, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                            block_tables, context_lens, scale, max_context_len, workspace, stream, slot_pointer):
+    import torch
+    args, workspace = _decode_codes_args(dtype_code, out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
+                                         context_lens, scale, max_context_len, workspace, stream)
+    n, hq, d = q.shape
+    hkv = k_scale.shape[1]
+    if tuple(k_new.shape) != (n, hkv, d) or tuple(v_new.shape) != (n, hkv, d):
+        raise ValueError("k_new / v_new must be [N][Hkv][D]")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new / v_new must be bf16")
+    if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (n,):
+        raise ValueError("slot_mapping must be int32 [N]")
+    slots = c_void_p(slot_pointer) if slot_pointer is not None else _dev(slot_mapping, "slot_mapping")
+    # pa_decode_*(out, q, k, v, ks, vs, tables, lens, ...) -> pa_decode_step_*(out, q, k_new, v_new, k, v, ks, vs,
+    # slots, tables, lens, ...)
+    return (args[:2] + (_dev(k_new, "k_new"), _dev(v_new, "v_new")) + args[2:6] + (slots,) + args[6:]), workspace
+
+
+def pa_decode_step_fp8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                            context_lens, scale, max_context_len, workspace=None, stream=None, slot_pointer=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode_step_fp8(*args)`` calls."""
+    return _decode_step_codes_args(PA_FP8_E4M3, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                                   slot_mapping, block_tables, context_lens, scale, max_context_len, workspace,
+                                   stream, slot_pointer)
+
+
+def pa_decode_step_int8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                             context_lens, scale, max_context_len, workspace=None, stream=None, slot_pointer=None):
+    """Validate once and return (args, workspace) for repeated ``lib.pa_decode_step_int8(*args)`` calls."""
+    return _decode_step_codes_args(PA_INT8, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                                   block_tables, context_lens, scale, max_context_len, workspace, stream,
+                                   slot_pointer)
+
+
+def pa_decode_step_fp8(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                       context_lens, scale, max_context_len, workspace=None, stream=None):
+    """pa_decode_step_fp8 of include/pa.h: attend to each row's new token as its codes, then store them."""
+    args, _ws = pa_decode_step_fp8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                                        block_tables, context_lens, scale, max_context_len, workspace, stream)
+    _check(lib.pa_decode_step_fp8(*args), "pa_decode_step_fp8")
+    return out
+
+
+def pa_decode_step_int8(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                        context_lens, scale, max_context_len, workspace=None, stream=None):
+    """pa_decode_step_int8 of include/pa.h: as pa_decode_step_fp8 over an INT8 cache."""
+    args, _ws = pa_decode_step_int8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                                         block_tables, context_lens, scale, max_context_len, workspace, stream)
+    _check(lib.pa_decode_step_int8(*args), "pa_decode_step_int8")
     return out
 
 

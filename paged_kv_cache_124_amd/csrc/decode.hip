@@ -649,7 +649,8 @@ namespace {
 int decode_codes(int codes, void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
                  const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq,
                  int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq, int max_context_len,
-                 int num_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+                 int num_blocks, void* workspace, size_t workspace_bytes, void* stream,
+                 const pa::StepInputs* step = nullptr) {
   using namespace pa;
   if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0 || num_blocks < 0)
@@ -665,7 +666,19 @@ int decode_codes(int codes, void* out, const void* q, const void* k_pool, const 
   if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
   return launch_stream(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, out,
                        workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq, num_blocks,
-                       scale * kLog2e, nullptr, k_scale, v_scale, codes);
+                       scale * kLog2e, step, k_scale, v_scale, codes);
+}
+
+int decode_step_codes(int codes, void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                      void* v_pool, const float* k_scale, const float* v_scale, const int32_t* slot_mapping,
+                      int32_t* block_tables, int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head,
+                      int block_size, float scale, int max_blocks_per_seq, int max_context_len, int num_blocks,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  const pa::StepInputs step{k_new, v_new, slot_mapping};
+  return decode_codes(codes, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, num_seqs, Hq, Hkv,
+                      d_head, block_size, scale, max_blocks_per_seq, max_context_len, num_blocks, workspace,
+                      workspace_bytes, stream, &step);
 }
 
 }  // namespace
@@ -690,3 +703,24 @@ extern "C" int pa_decode_int8(void* out, const void* q, const void* k_pool, cons
                       workspace_bytes, stream);
 }
 
+extern "C" int pa_decode_step_fp8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                  void* v_pool, const float* k_scale, const float* v_scale,
+                                  const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                                  int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                                  int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_step_codes(pa::kKvE4m3, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                           block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size, scale,
+                           max_blocks_per_seq, max_context_len, num_blocks, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_step_int8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                   void* v_pool, const float* k_scale, const float* v_scale,
+                                   const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
+                                   int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                                   int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return decode_step_codes(pa::kKvInt8, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                           block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size, scale,
+                           max_blocks_per_seq, max_context_len, num_blocks, workspace, workspace_bytes, stream);
+}

@@ -13,6 +13,8 @@ struct StreamPlan {
   size_t prefix_offset = 0;    // workspace: [tile prefix sums | step slots | summary records]
   size_t slots_offset = 0;
   size_t records_offset = 0;
+  size_t lens_offset = 0;       // code-cache step: the rows as the decode saw them, [num_seqs]
+  size_t whole_offset = 0;      // code-cache step: records of whole segments, [num_seqs][Hkv][g]
   size_t seq_group_offset = 0;  // decode_shared: tile range and record row of each sequence
   size_t workspace_bytes = 0;
   size_t lds_bytes = 0;
@@ -36,7 +38,7 @@ bool stream_eligible_fp8(int num_seqs, int g, int d, int block_size);
 // fp8: 64-token tiles over an FP8 cache instead of 32-token bf16 tiles.
 StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, bool fp8 = false);
 // codes != kKvBf16: the pools hold one-byte codes with per-(block, KV head)
-// scales k_scale / v_scale (no fused step for them).
+// scales k_scale / v_scale.
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
                   int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
@@ -46,8 +48,8 @@ int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void*
 // calls it for codes == kKvInt8.
 int launch_stream_int8(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
                        const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d,
-                       int block_size, int max_blocks, int num_blocks, float scale_log2, const float* k_scale,
-                       const float* v_scale);
+                       int block_size, int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
+                       const float* k_scale, const float* v_scale);
 
 // Shared-prefix kernel (decode_shared.hip): groups of consecutive rows whose
 // first P tokens lie in the same full blocks, int32 [num_groups][3] =

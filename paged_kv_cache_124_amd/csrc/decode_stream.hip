@@ -99,7 +99,11 @@ StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int
   const size_t prefix_bytes = ((static_cast<size_t>(num_seqs) + 1) * sizeof(int32_t) + 255) / 256 * 256;
   p.slots_offset = p.prefix_offset + prefix_bytes;
   p.records_offset = p.slots_offset + prefix_bytes;
-  p.workspace_bytes = p.records_offset + static_cast<size_t>(waves) * 2 * g * (d + 4) * sizeof(float);
+  p.lens_offset = p.records_offset + static_cast<size_t>(waves) * 2 * g * (d + 4) * sizeof(float);
+  p.whole_offset = p.lens_offset + (fp8 ? prefix_bytes : 0);
+  // code caches: one more record per (row, KV head) for a decode step, whose
+  // merge kernel adds the new token to every segment, whole ones included
+  p.workspace_bytes = p.whole_offset + (fp8 ? static_cast<size_t>(num_seqs) * hkv * g * (d + 4) * sizeof(float) : 0);
   p.lds_bytes = stream_lds(num_seqs);
   return p;
 }
@@ -108,15 +112,15 @@ int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void*
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
                   int max_blocks, int num_blocks, float scale_log2, const StepInputs* step, const float* k_scale,
                   const float* v_scale, int codes) {
-  if (codes != kKvBf16 && (step || !k_scale || !v_scale)) return PA_ERR_UNSUPPORTED;
+  if (codes != kKvBf16 && (!k_scale || !v_scale)) return PA_ERR_UNSUPPORTED;
   if (codes == kKvInt8)
     return launch_stream_int8(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, d, block_size, max_blocks, num_blocks,
-                              scale_log2, k_scale, v_scale);
+                              scale_log2, step, k_scale, v_scale);
 #define PA_STREAM_CASE(DD, BB)                                                                               \
   if (d == DD && block_size == BB) {                                                                         \
     if (codes == kKvE4m3)                                                                                    \
       launch_stream_db<DD, BB, kKvE4m3>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,  \
-                                        scale_log2, nullptr, k_scale, v_scale);                              \
+                                        scale_log2, step, k_scale, v_scale);                                 \
     else                                                                                                     \
       launch_stream_db<DD, BB, kKvBf16>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,  \
                                         scale_log2, step, nullptr, nullptr);                                 \

@@ -33,6 +33,7 @@
 
 #include <type_traits>
 
+#include "codes.h"
 #include "common.h"
 #include "decode_stream.h"
 #include "decode_tile.h"
@@ -221,13 +222,16 @@ __device__ __forceinline__ void pv_tile8(Acc<D>& st, const f32x4 (&s)[2], const 
 }
 
 // End of a piece of segment t: write the normalised output (whole segment) or a summary record.
+// With whole_rec non-null (a decode step over a cache of codes, whose merge
+// kernel adds the new token) a whole segment leaves its summary in
+// whole_rec[n][j] instead of its output.
 template <int D>
 __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slot, int64_t wave_id, uint16_t* out,
-                                      float* rec, int hq, int g, int r, int gq) {
+                                      float* rec, float* whole_rec, int hq, int hkv, int g, int r, int gq) {
   float zt = st.z + __shfl_xor(st.z, 16);
   zt += __shfl_xor(zt, 32);
   if (r < g) {
-    if (whole) {
+    if (whole && whole_rec == nullptr) {
       const float inv = 1.f / zt;
       uint16_t* o = out + (static_cast<int64_t>(t.n) * hq + t.j * g + r) * D + 4 * gq;
 #pragma unroll
@@ -237,7 +241,8 @@ __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slo
         *reinterpret_cast<uint2*>(o + 16 * mm) = make_uint2(lo, hi);
       }
     } else {
-      float* rr = rec + (static_cast<int64_t>(wave_id * 2 + slot) * g + r) * (D + 4);
+      float* rr = whole ? whole_rec + ((static_cast<int64_t>(t.n) * hkv + t.j) * g + r) * (D + 4)
+                        : rec + (static_cast<int64_t>(wave_id * 2 + slot) * g + r) * (D + 4);
 #pragma unroll
       for (int mm = 0; mm < D / 16; ++mm) *reinterpret_cast<f32x4*>(rr + 4 + 16 * mm + 4 * gq) = st.o[mm];
       if (gq == 0) {
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     float* __restrict__ rec, int32_t* __restrict__ prefix_out, int n_seqs, int hq, int hkv, int g, int max_blocks,
     int num_blocks, float scale_log2, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale) {
+    const float* __restrict__ v_scale, float* __restrict__ whole_rec, int32_t* __restrict__ lens_out) {
   constexpr bool F8 = KV != kKvBf16;  // one-byte codes (E4M3 or INT8) with scales
   constexpr bool I8 = KV == kKvInt8;
   constexpr int TOK = kTok<F8>;
@@ -300,8 +305,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   }
   if (tid == 0) s_pre[0] = 0;
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     for (int i = tid; i <= n_seqs; i += 256) prefix_out[i] = s_pre[i];
+    if (lens_out != nullptr)  // the rows as this decode saw them, for a merge kernel that moves them on
+      for (int i = tid; i < n_seqs; i += 256) lens_out[i] = s_len[i];
+  }
   // no barrier below this point: waves run independently
 
   Split sp;
@@ -381,6 +389,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       Buf8<D> b;
       read_tile8<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
       __builtin_amdgcn_sched_barrier(0);
+      // a step over codes: the row's slot, read where the row's head-0 segment
+      // ends and handed to the merge kernel through slots_out (read early, stored
+      // after this tile's compute)
+      const bool row_end = whole_rec != nullptr && cur.j == 0 && cur.ti == nt_cur - 1;
+      int row_slot = -1;
+      if (row_end) row_slot = slots[cur.n];
       tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
       scn = load_scales<B>(tbn, k_scale, v_scale, nxt.j, hkv, num_blocks, gq);
       dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
@@ -393,6 +407,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
         const float sv[2] = {scc.v[u][0], scc.v[u][1]};
         pv_tile8<D, I8>(st, sco, b.v[u], b.ok[u], t0 + 32 * u, S, full, sk, sv, gq);
       }
+      if (row_end && lane == 0) slots_out[cur.n] = row_slot;
     } else {
       Buf<D> b;
       read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
@@ -422,7 +437,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     }
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
-      flush<D>(st, cur, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, hq, g, r, gq);
+      flush<D>(st, cur, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, whole_rec, hq, hkv, g, r,
+                gq);
       first_piece = false;
       piece_start = 0;
     }
@@ -458,6 +474,126 @@ __global__ __launch_bounds__(256) void merge_stream(const float* __restrict__ re
   append_row<D>(ap, rt, n, j, hkv);
 }
 
+// ---- a decode step over a cache of codes -----------------------------------------
+//
+// The decode kernel attends to each row's cached tokens only.  The merge
+// kernel then codes the row's new token under the scales of its slot's block
+// (the append's quantizer, codes.h), adds it to the row's merge as one more
+// piece (weight sum 1, its value row the codes' values times the scale), and
+// where the slot is the row's next position stores the codes and moves the
+// row forward.  A slot outside the pool has no block whose scales could code
+// the token: that row attends its cached tokens only and stays as it is.
+
+struct CodeStepArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const uint16_t* k_new;   // [rows][Hkv][D] bf16
+  const uint16_t* v_new;
+  const int32_t* slots;    // the caller's slot of each row's new token (read here only for rows without tiles)
+  const float* k_scale;    // [num_blocks][Hkv]
+  const float* v_scale;
+  int32_t* block_tables;
+  int32_t* context_lens;
+  int max_blocks, block_size, num_blocks;
+};
+
+template <int D>
+struct NewTokenPiece {
+  static constexpr bool kOn = true;
+  bool has;            // the slot lies in the pool: the token is attended
+  float m[4];          // its base-2 scores for heads wave, wave + 4, ...
+  float v[D / 64];     // its value elements lane + 64 e (code value times scale)
+  const float* whole;  // whole-segment records [rows][Hkv][g] x (D + 4)
+  // the score of head wave + 4 hi; selects, not an indexed read (which would
+  // move the object out of registers)
+  __device__ __forceinline__ float score(int hi) const {
+    return hi == 0 ? m[0] : (hi == 1 ? m[1] : (hi == 2 ? m[2] : m[3]));
+  }
+};
+
+template <int D, bool I8>
+__global__ __launch_bounds__(256) void merge_step8(const float* __restrict__ rec, const float* __restrict__ whole,
+                                                   const int32_t* __restrict__ prefix,
+                                                   const int32_t* __restrict__ lens,
+                                                   const int32_t* __restrict__ row_slots, const uint16_t* __restrict__ q,
+                                                   uint16_t* __restrict__ out, int n_seqs, int hq, int hkv, int g,
+                                                   int64_t total_waves, float scale_log2, CodeStepArgs a) {
+  constexpr int E = D / 64;
+  const int j = blockIdx.x;
+  const int n = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int B = a.block_size;
+  // Every load that does not depend on the slot is issued first, together:
+  // the coding below branches, and loads placed after it would each wait
+  // out a memory latency of their own.
+  const bool has_tiles = prefix[n + 1] > prefix[n];
+  const int packed = lens[n];
+  const int copied_slot = row_slots[n];
+  const int64_t src = (static_cast<int64_t>(n) * hkv + j) * D;
+  uint32_t kb[E], vb[E], qb[4][E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kb[e] = a.k_new[src + lane + 64 * e];
+    vb[e] = a.v_new[src + lane + 64 * e];
+  }
+  const uint16_t* qrow = q + (static_cast<int64_t>(n) * hq + j * g) * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = min(wave + 4 * i, g - 1);  // heads past g load a valid row and are never used
+#pragma unroll
+    for (int e = 0; e < E; ++e) qb[i][e] = qrow[h * D + lane + 64 * e];
+  }
+  // the decode kernel copied the slot of every row with a cached token; a row
+  // without one had no tile, so its slot comes from the caller's array
+  const int slot = has_tiles ? copied_slot : a.slots[n];
+  const bool in_pool = slot >= 0 && static_cast<int64_t>(slot) < static_cast<int64_t>(a.num_blocks) * B;
+  const int64_t head = static_cast<int64_t>(in_pool ? slot / B : 0) * hkv + j;
+  const float ks = a.k_scale[head], vs = a.v_scale[head];
+  // the lane's elements d = lane + 64 e of the token, coded as the append codes them
+  uint32_t kc[E], vc[E];
+  float kv[E];
+  NewTokenPiece<D> x;
+  x.has = in_pool;
+  x.whole = whole;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kc[e] = code8<I8>(bf16_bits_to_f32(kb[e]), ks);
+    vc[e] = code8<I8>(bf16_bits_to_f32(vb[e]), vs);
+    kv[e] = code8_value<I8>(kc[e]);
+    x.v[e] = code8_value<I8>(vc[e]) * vs;
+  }
+  // scores: q . (key codes' values), times scale * log2(e) * key scale, as the decode kernel forms them
+  const float sk = scale_log2 * ks;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dot += bf16_bits_to_f32(qb[i][e]) * kv[e];
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
+    x.m[i] = dot * sk;
+  }
+  merge_segment<D, NewTokenPiece<D>>(rec, prefix, out, n_seqs, hq, hkv, g, g, total_waves, j, n, x);
+  // store the codes and move the row on where the slot is the row's next position
+  const int S0 = pool_tokens(packed);
+  if (!(next_fits(packed) && in_pool && slot % B == S0 % B) || wave != 0) return;
+  const int64_t pb = slot / B;
+  const int off = slot % B;
+  const int64_t hd = pb * hkv + j;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = lane + 64 * e;
+    a.k_pool[((hd * (D / 16) + d / 16) * B + off) * 16 + d % 16] = static_cast<uint8_t>(kc[e]);
+    a.v_pool[(hd * D + d) * B + off] = static_cast<uint8_t>(vc[e]);
+  }
+  if (j == 0 && lane == 0) {  // the only thread that reads or writes the row
+    const int pos = a.context_lens[n];
+    a.block_tables[static_cast<int64_t>(n) * a.max_blocks + pos / B] = static_cast<int32_t>(pb);
+    a.context_lens[n] = pos + 1;
+  }
+}
+
 // Both kernels of one decode on stream s.
 template <int D, int B, int KV>
 void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
@@ -483,11 +619,39 @@ void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const v
     ap.max_blocks = max_blocks;
     ap.block_size = B;
   }
+  const int64_t total_waves = static_cast<int64_t>(p.workgroups) * kSW;
+  if constexpr (KV != kKvBf16) {
+    if (step) {  // the decode attends the cached tokens; the merge kernel adds, codes and stores the new token
+      float* whole = reinterpret_cast<float*>(base + p.whole_offset);
+      int32_t* lens_ws = reinterpret_cast<int32_t*>(base + p.lens_offset);
+      decode_stream<D, B, KV><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
+          static_cast<const uint16_t*>(q), k, v, bt, cl, static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g,
+          max_blocks, num_blocks, scale_log2, nullptr, nullptr, step->slots, slots_ws, k_scale, v_scale, whole,
+          lens_ws);
+      CodeStepArgs ca{};
+      ca.k_pool = static_cast<uint8_t*>(const_cast<void*>(k));
+      ca.v_pool = static_cast<uint8_t*>(const_cast<void*>(v));
+      ca.k_new = static_cast<const uint16_t*>(step->k_new);
+      ca.v_new = static_cast<const uint16_t*>(step->v_new);
+      ca.slots = step->slots;
+      ca.k_scale = k_scale;
+      ca.v_scale = v_scale;
+      ca.block_tables = const_cast<int32_t*>(bt);
+      ca.context_lens = const_cast<int32_t*>(cl);
+      ca.max_blocks = max_blocks;
+      ca.block_size = B;
+      ca.num_blocks = num_blocks;
+      merge_step8<D, KV == kKvInt8><<<dim3(hkv, n), dim3(256), 0, s>>>(
+          rec, whole, prefix, lens_ws, slots_ws, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), n, hq,
+          hkv, g, total_waves, scale_log2, ca);
+      return;
+    }
+  }
   decode_stream<D, B, KV><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
       static_cast<const uint16_t*>(q), k, v, bt, cl, static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g,
-      max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws, k_scale, v_scale);
+      max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws, k_scale, v_scale, nullptr, nullptr);
   merge_stream<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, prefix, static_cast<uint16_t*>(out), n, hq, hkv, g,
-                                                     static_cast<int64_t>(p.workgroups) * kSW, ap);
+                                                     total_waves, ap);
 }
 
 }  // namespace

@@ -426,9 +426,17 @@ __device__ __forceinline__ void append_row(const AppendArgs& ap, const RowToken<
 // round trip.  Piece 0's record is at `first`, piece k >= 1's at
 // later + (k - 1) * stride; bit k of `present` says piece k exists (a range
 // can be empty when there are fewer tiles than waves).
-template <int D, int KP>
+// Without an extra piece the plain merge.  An extra piece (X::kOn) is one more
+// summary with weight sum 1: x.score(hi) its base-2 score, x.v its value row
+// (lane's elements); x.has says whether it exists.
+struct NoExtraPiece {
+  static constexpr bool kOn = false;
+};
+
+template <int D, int KP, class X = NoExtraPiece>
 __device__ __forceinline__ void merge_head_few(const float* __restrict__ first, const float* __restrict__ later,
-                                               int stride, uint64_t present, int cnt, uint16_t* o, int lane) {
+                                               int stride, uint64_t present, int cnt, uint16_t* o, int lane,
+                                               const X& x = X{}, int hi = 0) {
   constexpr int E = D / 64;  // output elements per lane
   const bool mine = (present >> lane) & 1;
   const float* ma = mine ? (lane == 0 ? first : later + (lane - 1) * stride) : first;
@@ -448,6 +456,9 @@ __device__ __forceinline__ void merge_head_few(const float* __restrict__ first, 
   float mx = mine ? m_l : -INFINITY;
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+  if constexpr (X::kOn) {
+    if (x.has) mx = fmaxf(mx, x.score(hi));
+  }
   const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
   float zz = mine ? f * z_l : 0.f;
 #pragma unroll
@@ -461,7 +472,16 @@ __device__ __forceinline__ void merge_head_few(const float* __restrict__ first, 
 #pragma unroll
     for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
   }
-  const float inv = 1.f / zz;
+  float inv;
+  if constexpr (X::kOn) {
+    const float fx = x.has ? __builtin_amdgcn_exp2f(x.score(hi) - mx) : 0.f;
+    zz += fx;
+#pragma unroll
+    for (int e = 0; e < E; ++e) uu[e] += fx * x.v[e];
+    inv = zz > 0.f ? 1.f / zz : 0.f;  // no piece at all: zeros
+  } else {
+    inv = 1.f / zz;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) o[lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
 }
@@ -473,16 +493,23 @@ __device__ __forceinline__ void merge_head_few(const float* __restrict__ first, 
 // h', h' + 4, ...; lanes read records in parallel (wave v_lo + lane), so the
 // merge costs a few memory latencies rather than one per record.  Records
 // combine in wave order, which is tile order.
-template <int D>
+template <int D, class X = NoExtraPiece>
 __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, const int32_t* __restrict__ prefix,
                                               uint16_t* __restrict__ out, int n_units, int hq, int hkv, int g,
-                                              int rows, int64_t total_waves, int j, int n) {
+                                              int rows, int64_t total_waves, int j, int n, const X& x = X{}) {
   constexpr int E = D / 64;  // output elements per lane
   const int64_t p_n = prefix[n];
   const int nt = prefix[n + 1] - prefix[n];
   uint16_t* o = out + (static_cast<int64_t>(n) * hq + j * g) * D;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   if (nt == 0) {
-    for (int e = threadIdx.x; e < g * D; e += blockDim.x) o[e] = 0;
+    if constexpr (X::kOn) {  // the extra piece alone (or zeros)
+      for (int h = wave; h < g; h += 4)
+        merge_head_few<D, 8, X>(x.whole, x.whole, 0, 0, 0, o + h * D, lane, x, h >> 2);
+    } else {
+      for (int e = threadIdx.x; e < g * D; e += blockDim.x) o[e] = 0;
+    }
     return;
   }
   Split sp;
@@ -491,10 +518,16 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
   const int64_t b = a + nt;                                    // one past its last tile
   const int64_t v_lo = sp.wave_of(a);
   const int64_t v_hi = sp.wave_of(b - 1);
-  if (v_lo == v_hi) return;  // finished inside one wave
+  if (v_lo == v_hi) {  // finished inside one wave
+    if constexpr (X::kOn) {  // which left its summary in the whole-segment records
+      for (int h = wave; h < g; h += 4) {
+        const float* w = x.whole + ((static_cast<int64_t>(n) * hkv + j) * rows + h) * (D + 4);
+        merge_head_few<D, 8, X>(w, w, 0, 1, 1, o + h * D, lane, x, h >> 2);
+      }
+    }
+    return;
+  }
   const bool lo_second = a > sp.start(v_lo);  // the segment is not the first piece of wave v_lo
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   // the record of wave v for head h, or nullptr for a wave with an empty range
   auto record = [&](int64_t v, int h) -> const float* {
     if (v > v_hi || sp.start(v) == sp.start(v + 1)) return nullptr;
@@ -515,9 +548,9 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
       const float* first = rec + ((v_lo * 2 + (lo_second ? 1 : 0)) * rows + h) * (D + 4);
       const float* later = rec + ((v_lo + 1) * 2 * rows + h) * (D + 4);
       if (cnt <= 8)
-        merge_head_few<D, 8>(first, later, stride, present, cnt, o + h * D, lane);
+        merge_head_few<D, 8, X>(first, later, stride, present, cnt, o + h * D, lane, x, h >> 2);
       else
-        merge_head_few<D, 16>(first, later, stride, present, cnt, o + h * D, lane);
+        merge_head_few<D, 16, X>(first, later, stride, present, cnt, o + h * D, lane, x, h >> 2);
     }
     return;
   }
@@ -529,6 +562,9 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
     }
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+    if constexpr (X::kOn) {
+      if (x.has) mx = fmaxf(mx, x.score(h >> 2));
+    }
     float zz = 0.f;
     float uu[E];
 #pragma unroll
@@ -563,7 +599,16 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
     }
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
-    const float inv = 1.f / zz;
+    float inv;
+    if constexpr (X::kOn) {
+      const float fx = x.has ? __builtin_amdgcn_exp2f(x.score(h >> 2) - mx) : 0.f;
+      zz += fx;
+#pragma unroll
+      for (int e = 0; e < E; ++e) uu[e] += fx * x.v[e];
+      inv = zz > 0.f ? 1.f / zz : 0.f;
+    } else {
+      inv = 1.f / zz;
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
   }
