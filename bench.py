@@ -554,10 +554,11 @@ def main():
         else:
             pos = run.step_i % (RING // 2)  # the ring's event is recorded after the step at pos RING / 2 - 1
             start = end = None
-            if open_span is None and pos == 0 and i + span <= args.steps:
+            # a span opens wherever it still ends before the ring's next record
+            if open_span is None and pos + span <= RING // 2 and i + span <= args.steps:
                 open_span = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), 0, 0]
                 start = open_span[0]
-            if open_span is not None and pos == span - 1:
+            if open_span is not None and open_span[2] == span - 1:  # this step is the span's last
                 end = open_span[1]
             ev = (start, end) if (start is not None or end is not None) else None
         step_bytes = run.step(ev)
