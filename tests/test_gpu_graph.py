@@ -127,3 +127,63 @@ def test_decode_step_graph_runs_a_decode_loop():
     ref = OA.paged_decode(qB.cpu().double().numpy(), k_log, v_log, tB.cpu().numpy(), lB.cpu().numpy().tolist(),
                           c.scale)
     assert_close(outB, ref, "graph step loop, last step")
+
+
+@pytest.mark.parametrize("codes", ["e4m3", "int8"])
+def test_decode_step_codes_graph_runs_a_decode_loop(codes):
+    """pa_decode_step_fp8 / _int8 captured once and replayed for 8 steps over a cache of codes: every step's output,
+    and the final codes, tables and lengths, equal an eager run of the same steps bit for bit.  Blocks a step opens
+    get their scales before the step, as a caller sets them."""
+    import paged_kv_cache_124_amd as pa
+    print(f"[case] graph decode_step {codes} loop", flush=True)
+    steps = 8
+    w = synth.gqa8b()
+    lens = [43, 1, 15, 16, 300, 511, 2047, 1024] * 2
+    bs = w.block_size
+    c = make_case(w, lens, num_blocks=sum(-(-(s + steps) // bs) for s in lens) + 64,
+                  max_blocks=-(-(max(lens) + steps) // bs) + 1, seed=4343, fp8=codes == "e4m3", int8=codes == "int8")
+    n = len(lens)
+    max_ctx = max(lens) + steps
+    args_of = pa.pa_decode_step_int8_args if codes == "int8" else pa.pa_decode_step_fp8_args
+    call = pa.lib.pa_decode_step_int8 if codes == "int8" else pa.lib.pa_decode_step_fp8
+    eager = pa.pa_decode_step_int8 if codes == "int8" else pa.pa_decode_step_fp8
+    kA, vA, tA, lA = (t.clone() for t in (c.k, c.v, c.tables_dev, c.lens_dev))
+    kB, vB, tB, lB = (t.clone() for t in (c.k, c.v, c.tables_dev, c.lens_dev))
+    qB = torch.empty_like(c.q)
+    knB = torch.empty((n, c.hkv, c.d), dtype=c.q.dtype, device="cuda")
+    vnB = torch.empty_like(knB)
+    slotsB = torch.zeros(n, dtype=torch.int32, device="cuda")
+    outB = torch.empty_like(c.q)
+    _, wsB = args_of(outB, qB, knB, vnB, kB, vB, c.k_scale, c.v_scale, slotsB, tB, lB, c.scale, max_ctx)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        args, _ = args_of(outB, qB, knB, vnB, kB, vB, c.k_scale, c.v_scale, slotsB, tB, lB, c.scale, max_ctx,
+                          workspace=wsB, stream=torch.cuda.current_stream())
+        assert call(*args) == 0
+    torch.cuda.synchronize()
+    outA = torch.empty_like(c.q)
+    seqs = list(range(n))
+    for step in range(steps):
+        st, slots, pairs, _ = c.bm.append_slots(seqs)
+        assert st == 0 and len(pairs) == 0
+        for s in slots:  # a block the step opens carries the NaN scales of unused blocks: give it real ones
+            b = int(s) // bs
+            if torch.isnan(c.k_scale[b]).any():
+                c.k_scale[b] = 0.0021 + 0.0001 * (b % 7)
+                c.v_scale[b] = 0.0017 + 0.0001 * (b % 5)
+        slots_t = torch.as_tensor(np.asarray(slots, dtype=np.int32), device="cuda")
+        q = synth.randn(tuple(c.q.shape), c.q.dtype, w.value_scale, 7300 + step, "cuda")
+        kn = synth.randn((n, c.hkv, c.d), c.q.dtype, 0.09, 7400 + step, "cuda")
+        vn = synth.randn((n, c.hkv, c.d), c.q.dtype, 0.09, 7500 + step, "cuda")
+        eager(outA, q, kn, vn, kA, vA, c.k_scale, c.v_scale, slots_t, tA, lA, c.scale, max_ctx)
+        qB.copy_(q)
+        knB.copy_(kn)
+        vnB.copy_(vn)
+        slotsB.copy_(slots_t)
+        outB.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(outA), _bits(outB)), f"step {step}: replay differs from the eager step"
+    for a, b, name in ((kA, kB, "K codes"), (vA, vB, "V codes"), (tA, tB, "tables"), (lA, lB, "lengths")):
+        assert torch.equal(a, b), f"{name} differ after {steps} steps"
+    assert lB.cpu().numpy().tolist() == [s + steps for s in lens]
