@@ -232,7 +232,7 @@ __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slo
   zt += __shfl_xor(zt, 32);
   if (r < g) {
     if (whole && whole_rec == nullptr) {
-      const float inv = 1.f / zt;
+      const float inv = zt > 0.f ? 1.f / zt : 0.f;  // every token left out: zeros
       uint16_t* o = out + (static_cast<int64_t>(t.n) * hq + t.j * g + r) * D + 4 * gq;
 #pragma unroll
       for (int mm = 0; mm < D / 16; ++mm) {

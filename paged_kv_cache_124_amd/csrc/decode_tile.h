@@ -154,7 +154,9 @@ template <int D>
 __device__ __forceinline__ void reset(Acc<D>& st) {
 #pragma unroll
   for (int mm = 0; mm < D / 16; ++mm) st.o[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
+  // finite: a tile whose tokens are all left out (blocks outside the pool) then
+  // keeps every exponent finite (exp2(-inf - -inf) would be NaN)
+  st.m = -__FLT_MAX__;
   st.z = 0.f;
 }
 
@@ -480,7 +482,7 @@ __device__ __forceinline__ void merge_head_few(const float* __restrict__ first, 
     for (int e = 0; e < E; ++e) uu[e] += fx * x.v[e];
     inv = zz > 0.f ? 1.f / zz : 0.f;  // no piece at all: zeros
   } else {
-    inv = 1.f / zz;
+    inv = zz > 0.f ? 1.f / zz : 0.f;  // every token left out: zeros
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) o[lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
@@ -607,7 +609,7 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
       for (int e = 0; e < E; ++e) uu[e] += fx * x.v[e];
       inv = zz > 0.f ? 1.f / zz : 0.f;
     } else {
-      inv = 1.f / zz;
+      inv = zz > 0.f ? 1.f / zz : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);

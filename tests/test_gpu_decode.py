@@ -184,3 +184,24 @@ def test_many_sequences_take_partitioned_path():
     assert_close(out[sample], oracle_outputs(c, sample), "3100 sequences")
     zero = [i for i, s in enumerate(lens) if s == 0]
     assert zero and torch.count_nonzero(out[zero].float()) == 0
+
+
+def test_decode_leading_tile_outside_pool_is_left_out():
+    """Both blocks of a row's first 32-token tile outside [0, num_blocks): that tile, the first of its piece, holds no
+    token, and the row attends to its other tokens (no NaN from an empty tile before any token)."""
+    from pool_layout import k_to_logical, v_to_logical
+    print("[case] bf16 leading tile out of pool", flush=True)
+    c = make_case(synth.gqa8b(), [100, 70], hq=8, hkv=2, seed=1760)
+    tables = c.tables.copy()
+    tables[0, 0] = c.num_blocks + 3
+    tables[0, 1] = c.num_blocks + 9  # tokens 0..31 of row 0
+    out = run_decode(c, tables_dev=torch.from_numpy(tables).cuda())
+    k_log = k_to_logical(c.k.cpu()).double().numpy()
+    v_log = v_to_logical(c.v.cpu()).double().numpy()
+    bs = c.block_size
+    keep = range(2 * bs, 100)
+    K = np.stack([k_log[int(c.tables[0][t // bs]), :, t % bs] for t in keep])
+    V = np.stack([v_log[int(c.tables[0][t // bs]), :, t % bs] for t in keep])
+    q = c.q.float().cpu().numpy().astype(np.float64)
+    assert_close(out[0:1], OA.dense_attention(q[0], K, V, c.scale)[None], "bf16 leading tile out of pool")
+    assert_close(out[1:2], oracle_outputs(c, [1]), "bf16 row 1 untouched")

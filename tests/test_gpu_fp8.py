@@ -274,3 +274,24 @@ def test_append_step_fp8_tracks_block_manager(d, bs):
         assert np.array_equal(gk, ek) and np.array_equal(gv, ev), f"codes differ after step {step}"
         assert np.array_equal(ks.cpu().double().numpy(), eks) and np.array_equal(vs.cpu().double().numpy(), evs)
     assert model.stats()["cow_copies"] == prompts * (samples - 1)
+
+
+def test_decode_fp8_leading_tile_outside_pool_is_left_out():
+    """All four blocks of a row's first 64-token tile outside the pool: that tile holds no token, and the row attends
+    to its other tokens (no NaN from an empty tile before any token)."""
+    print("[case] fp8 leading tile out of pool", flush=True)
+    c = make_case(synth.gqa8b(), [150, 70], hq=8, hkv=2, seed=1710, fp8=True)
+    tables = c.tables.copy()
+    for b in range(4):
+        tables[0, b] = c.num_blocks + 2 + b  # tokens 0..63 of row 0
+    out = run_decode(c, tables_dev=torch.from_numpy(tables).cuda())
+    kc, vc, ks, vs = fp8_logical(c, [int(b) for b in c.tables[0][:10]])
+    keep = list(range(64, 150))
+    kb = np.stack([kc[t // 16, :, t % 16][:, None, :] for t in keep])
+    vb = np.stack([vc[t // 16, :, t % 16][:, None, :] for t in keep])
+    ksb = np.stack([ks[t // 16] for t in keep])
+    vsb = np.stack([vs[t // 16] for t in keep])
+    q = c.q.float().cpu().numpy().astype(np.float64)
+    ref0 = OF.paged_decode(q[0:1], kb, vb, ksb, vsb, np.arange(len(keep))[None, :], [len(keep)], c.scale)
+    assert_close(out[0:1], ref0, "fp8 leading tile out of pool")
+    assert_close(out[1:2], oracle_outputs(c, [1]), "fp8 row 1 untouched")
