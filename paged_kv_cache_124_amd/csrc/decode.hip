@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_mfma(
   f32x4 acc[VT];
 #pragma unroll
   for (int mm = 0; mm < VT; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
+  float m_run = -__FLT_MAX__;  // finite: a tile with no token keeps every exponent finite
   float z_run = 0.f;
 
   const int tiles = min(part, S - tok0 + kTile - 1) / kTile;  // tiles holding >= 1 valid token
@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void decode_mfma(
     bf16x8 kop[2][KCH];
     bf16x8 vop[VT];
     uint2 vlo[VT], vhi[VT];
+    bool blk_ok[2];  // the block of the lane's 4-token group of slab a lies in the pool
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       // key row r of slab a
@@ -195,7 +196,8 @@ __global__ __launch_bounds__(256) void decode_mfma(
       // value rows: tokens 4 gq .. 4 gq + 3 of slab a
       const int tv = t0 + 16 * a + 4 * gq;
       const int pbv = __shfl(tbl, (tv / B) - lb0);
-      const bool vval = tv < S && pbv >= 0 && pbv < num_blocks;
+      blk_ok[a] = pbv >= 0 && pbv < num_blocks;
+      const bool vval = tv < S && blk_ok[a];
       const uint16_t* vb = vh + static_cast<int64_t>(pbv) * blk_stride + (tv % B);
 #pragma unroll
       for (int mm = 0; mm < VT; ++mm) {
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void decode_mfma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * a + 4 * gq + i;
-        x[a][i] = tok < S ? s[a][i] * scale_log2 : -INFINITY;
+        x[a][i] = tok < S && blk_ok[a] ? s[a][i] * scale_log2 : -INFINITY;  // out-of-pool tokens left out
         tmax = fmaxf(tmax, x[a][i]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -298,12 +300,12 @@ __global__ __launch_bounds__(256) void decode_mfma(
     float zz = 0.f, uu = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(lds_m[w * 16 + h] - mx);  // exp2(-inf) = 0 for idle waves
+      const float f = __builtin_amdgcn_exp2f(lds_m[w * 16 + h] - mx);  // 0 for idle waves (maximum: the most negative float)
       zz += f * lds_z[w * 16 + h];
       uu += f * lds_u[(w * g + h) * D + dd];
     }
     if (n_parts == 1) {
-      out[(head0 + h) * D + dd] = f32_to_bf16_bits(uu / zz);
+      out[(head0 + h) * D + dd] = f32_to_bf16_bits(zz > 0.f ? uu / zz : 0.f);  // no token at all: zeros
     } else {
       const int64_t row = (head0 + h) * p_max + part_id;
       const int64_t n_rows = static_cast<int64_t>(gridDim.z) * hq * p_max;
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(64) void decode_generic(
     qv[e] = Elem<T>::load(q + orow + lane + 64 * e);
     u[e] = 0.f;
   }
-  float m_run = -INFINITY, z_run = 0.f;
+  float m_run = -__FLT_MAX__, z_run = 0.f;  // finite: a block outside the pool first keeps exponents finite
   const int64_t blk_stride = static_cast<int64_t>(hkv) * D * block_size;
   for (int t = tok0; t < tok1; ++t) {
     const int lb = t / block_size;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(64) void decode_generic(
     }
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
-    const float s2 = dot * scale_log2;
+    const float s2 = ok ? dot * scale_log2 : -INFINITY;  // a block outside the pool is left out
     const float m_new = fmaxf(m_run, s2);
     const float alpha = exp2f(m_run - m_new);
     const float p = exp2f(s2 - m_new);
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(64) void decode_generic(
     m_run = m_new;
   }
   if (n_parts == 1) {
-    for (int e = 0; e < E; ++e) Elem<T>::store(out + orow + lane + 64 * e, u[e] / z_run);
+    for (int e = 0; e < E; ++e) Elem<T>::store(out + orow + lane + 64 * e, z_run > 0.f ? u[e] / z_run : 0.f);
   } else {
     const int64_t row = (static_cast<int64_t>(seq) * hq + h) * p_max + part_id;
     const int64_t n_rows = static_cast<int64_t>(gridDim.z) * hq * p_max;
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(D) void merge_partitions(const float* __restrict__ 
     zz += f * ws[n_rows + row0 + p];
     uu += f * ws[2 * n_rows + (row0 + p) * D + dd];
   }
-  Elem<T>::store(out + (static_cast<int64_t>(seq) * hq + h) * D + dd, uu / zz);
+  Elem<T>::store(out + (static_cast<int64_t>(seq) * hq + h) * D + dd, zz > 0.f ? uu / zz : 0.f);
 }
 
 template <int D, int B>

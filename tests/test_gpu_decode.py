@@ -186,12 +186,14 @@ def test_many_sequences_take_partitioned_path():
     assert zero and torch.count_nonzero(out[zero].float()) == 0
 
 
-def test_decode_leading_tile_outside_pool_is_left_out():
-    """Both blocks of a row's first 32-token tile outside [0, num_blocks): that tile, the first of its piece, holds no
-    token, and the row attends to its other tokens (no NaN from an empty tile before any token)."""
+@pytest.mark.parametrize("dtype,hq,hkv", [(torch.bfloat16, 8, 2), (torch.float32, 8, 2), (torch.bfloat16, 32, 1)])
+def test_decode_leading_tile_outside_pool_is_left_out(dtype, hq, hkv):
+    """Both blocks of a row's first 32 tokens outside [0, num_blocks): their tokens are left out of the softmax, with
+    no NaN from a tile that holds no token before any other (persistent bf16 kernel; fp32 token-loop kernel; the
+    partitioned MFMA kernel at 32 query heads per KV head)."""
     from pool_layout import k_to_logical, v_to_logical
-    print("[case] bf16 leading tile out of pool", flush=True)
-    c = make_case(synth.gqa8b(), [100, 70], hq=8, hkv=2, seed=1760)
+    print(f"[case] leading tile out of pool {dtype} hq={hq} hkv={hkv}", flush=True)
+    c = make_case(synth.gqa8b(), [100, 70], hq=hq, hkv=hkv, dtype=dtype, seed=1760)
     tables = c.tables.copy()
     tables[0, 0] = c.num_blocks + 3
     tables[0, 1] = c.num_blocks + 9  # tokens 0..31 of row 0
@@ -203,5 +205,5 @@ def test_decode_leading_tile_outside_pool_is_left_out():
     K = np.stack([k_log[int(c.tables[0][t // bs]), :, t % bs] for t in keep])
     V = np.stack([v_log[int(c.tables[0][t // bs]), :, t % bs] for t in keep])
     q = c.q.float().cpu().numpy().astype(np.float64)
-    assert_close(out[0:1], OA.dense_attention(q[0], K, V, c.scale)[None], "bf16 leading tile out of pool")
-    assert_close(out[1:2], oracle_outputs(c, [1]), "bf16 row 1 untouched")
+    assert_close(out[0:1], OA.dense_attention(q[0], K, V, c.scale)[None], f"leading tile out of pool {dtype} g={hq // hkv}")
+    assert_close(out[1:2], oracle_outputs(c, [1]), f"row 1 untouched {dtype} g={hq // hkv}")
