@@ -405,22 +405,50 @@ class LongRunner:
             raise RuntimeError("device lengths diverged from the block manager's")
 
 
-def cpu_baseline(w, seconds, kv_kind="bf16"):
-    """The fp64 oracle on this host's cores over a bounded sample of the same workload (one BLAS thread).
+# Oracle inputs of the CPU baseline, set before the worker processes fork (they
+# read them copy-on-write) and never touched by the GPU path.
+_CPU_INPUTS = []
+_CPU_ARGS = {}
 
-    Inputs (one decode step of every sequence, values as stored in bf16, or
-    FP8 / INT8 codes and scales) are built first and kept in host memory; then whole
-    passes over all sequences are timed until `seconds` of compute have
-    accumulated.
-    """
-    import torch
-    import synth
-    from threadpoolctl import threadpool_limits
+
+def _oracle_over(idx):
+    """The fp64 oracle over the listed sequences of _CPU_INPUTS (one BLAS thread in this process)."""
     from oracle import attention as OA
     from oracle import fp8 as OF
     from oracle import int8 as OI
+    a = _CPU_ARGS
+    OC = OI if a["kv"] == "int8" else OF
+    for i in idx:
+        q, kp, vp, ks, vs, table, s = _CPU_INPUTS[i]
+        if a["codes"]:
+            OC.paged_decode(q, kp, vp, ks, vs, table, [s], a["scale"])
+        else:
+            OA.paged_decode(q, kp, vp, table, [s], a["scale"])
+    return len(idx)
+
+
+def _limit_blas():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def cpu_baseline(w, seconds, kv_kind="bf16"):
+    """The fp64 oracle on this host's cores over a bounded sample of the same workload.
+
+    Inputs (one decode step of every sequence, values as stored in bf16, or
+    FP8 / INT8 codes and scales) are built first and kept in host memory; then
+    whole passes over all sequences are timed until `seconds` / 2 of wall time
+    have accumulated, first on one core (one process, one BLAS thread), then on
+    every core this process may use (capped at 16, the CPU share of one GPU on
+    the measurement hosts): one worker process per core, one BLAS thread each,
+    the sequences of a pass dealt round-robin to the workers.  Runs before the
+    GPU is initialised, so the workers are plain forks of a CPU-only process.
+    """
+    import multiprocessing as mp
+    import torch
+    import synth
+    from threadpoolctl import threadpool_limits
     fp8 = kv_kind in ("fp8", "int8")  # one-byte codes with scales
-    OC = OI if kv_kind == "int8" else OF
     fill = synth.fill_int8_codes_ if kv_kind == "int8" else synth.fill_fp8_codes_
     scales = synth.int8_scales if kv_kind == "int8" else synth.fp8_scales
     lens = synth.seq_lengths(w)
@@ -428,7 +456,8 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
         lens = lens[:2]  # one layer of two 32,768-token sequences (the oracle holds them in host memory)
     rng = np.random.default_rng(0)
     bs, hkv, d = w.block_size, w.hkv, w.d
-    inputs = []
+    _CPU_INPUTS.clear()
+    _CPU_ARGS.update(kv=kv_kind, codes=fp8, scale=w.scale)
     for n, s in enumerate(lens):
         nb = -(-s // bs)
         if fp8:
@@ -450,27 +479,39 @@ def cpu_baseline(w, seconds, kv_kind="bf16"):
             ks2[table[0]] = ks
             vs2[table[0]] = vs
             ks, vs = ks2, vs2
-        inputs.append((q, kp2, vp2, ks, vs, table, s))
+        _CPU_INPUTS.append((q, kp2, vp2, ks, vs, table, s))
     step_bytes = sum(lens) * 2 * hkv * d * (1 if fp8 else 2) + (sum(-(-s // bs) for s in lens) * 2 * hkv * 4 if fp8 else 0)
-    passes, t_total = 0, 0.0
-    with threadpool_limits(limits=1):
-        torch.set_num_threads(1)
-        while t_total < seconds:
+    every = list(range(len(lens)))
+
+    def timed(run_pass):
+        passes, t_total = 0, 0.0
+        while t_total < seconds / 2:
             t0 = time.perf_counter()
-            for q, kp, vp, ks, vs, table, s in inputs:
-                if fp8:
-                    OC.paged_decode(q, kp, vp, ks, vs, table, [s], w.scale)
-                else:
-                    OA.paged_decode(q, kp, vp, table, [s], w.scale)
+            run_pass()
             t_total += time.perf_counter() - t0
             passes += 1
-    return {"value": round(passes * step_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} passes over one decode step of {'one layer of ' if w.name == 'long' else ''}"
-                      f"{'the first' if w.name == 'long' else 'all'} {len(lens)} sequences of the same workload "
-                      f"({kv_kind.upper() + ' cache, ' if fp8 else ''}all {w.hq} query heads; fp64 NumPy oracle, "
-                      f"one thread), "
-                      f"{t_total:.1f} s of compute",
-            "us_per_step": round(t_total / passes * 1e6, 1)}
+        return passes, t_total
+
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        p1, t1 = timed(lambda: _oracle_over(every))
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    chunks = [every[c::cores] for c in range(cores)]
+    with mp.get_context("fork").Pool(cores, initializer=_limit_blas) as pool:
+        pool.map(_oracle_over, [[i] for i in range(min(cores, len(every)))])  # workers up
+        pn, tn = timed(lambda: pool.map(_oracle_over, chunks))
+    _CPU_INPUTS.clear()
+    what = (f"one decode step of {'one layer of ' if w.name == 'long' else ''}"
+            f"{'the first' if w.name == 'long' else 'all'} {len(lens)} sequences of the same workload "
+            f"({kv_kind.upper() + ' cache, ' if fp8 else ''}all {w.hq} query heads; fp64 NumPy oracle)")
+    return {"value": round(pn * step_bytes / tn / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "blas_threads_per_process": 1,
+            "sample": f"{pn} passes over {what} on {cores} worker processes, {tn:.1f} s wall",
+            "us_per_step": round(tn / pn * 1e6, 1),
+            "one_core": {"value": round(p1 * step_bytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "sample": f"{p1} passes over the same step in this process, one BLAS thread, "
+                                   f"{t1:.1f} s of compute",
+                         "us_per_step": round(t1 / p1 * 1e6, 1)}}
 
 
 def synth_fork_prompts():
@@ -496,17 +537,29 @@ def main():
                           "launches": 5}))
         return
     if args.read_ceiling:
-        import paged_kv_cache_124_amd as pa
+        import ctypes
+        import paged_kv_cache_124_amd as pa  # noqa: F401  (torch's HIP runtime first, as for libpa.so)
+        probe = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_124_amd", "libpa_probe.so"))
+        probe.pa_read_probe.restype = ctypes.c_int
+        probe.pa_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
         buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")  # 4 GiB, 16x the Infinity Cache
         sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def read_probe(wgs):
+            st = probe.pa_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4, ctypes.c_void_p(sink.data_ptr()),
+                                     wgs, stream)
+            if st != 0:
+                raise RuntimeError(f"pa_read_probe: status {st}")
         rates = {}
         for wgs in (256, 512, 1024, 2048):  # 4, 8, 16, 32 waves per CU on 256 CUs
             for _ in range(3):
-                pa.pa_read_probe(buf, sink, wgs)
+                read_probe(wgs)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             for _ in range(20):
-                pa.pa_read_probe(buf, sink, wgs)
+                read_probe(wgs)
             b.record()
             torch.cuda.synchronize()
             rates[wgs] = round(buf.numel() * 4 * 20 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
@@ -514,6 +567,10 @@ def main():
                           "launches": 20, "peak_gb_s": HBM_PEAK_GBS}))
         return
     w = workload(args.workload)
+    cpu = None
+    if not args.no_cpu_baseline:  # before the GPU is initialised: its worker processes are plain forks
+        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_seconds, args.kv)
     total = args.steps + args.warmup + 1
     print(f"[bench] building workload {w.name}", file=sys.stderr, flush=True)
     if args.shared and (w.name != "fork" or args.kv != "bf16"):
@@ -651,9 +708,8 @@ def main():
         res["roofline"]["achieved"] = round(achieved * unique_per_step / bytes_per_launch, 1)
         res["roofline"]["frac"] = round(res["roofline"]["achieved"] / HBM_PEAK_GBS, 4)
         res["roofline"]["bytes"] = "unique KV a step needs: each shared full block once, every row's own blocks"
-    if not args.no_cpu_baseline:
-        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.kv)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

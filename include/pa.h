@@ -123,6 +123,35 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode_partitioned: pa_decode computed by the partitioned kernels -- the
+ * shape of "PagedAttention: Virtual Memory for the KV Cache", section 13: one
+ * workgroup per (partition of `partition_tokens` tokens, KV head, sequence)
+ * looping over the partition's blocks, a summary per partition in
+ * `workspace`, and a second kernel that merges the partitions of a sequence
+ * in order ("PagedAttention in vLLM: scattered memory, exact attention",
+ * section 11).  pa_decode itself takes this path for shapes the persistent
+ * kernel does not serve (fp32, Hq / Hkv > 16, more than 3072 sequences);
+ * this entry point takes it for every shape pa_decode supports.
+ *   partition_tokens  0 = the size pa_decode would pick
+ *                     (pa_decode_partition_tokens); else a multiple of 128
+ *                     spanning at most 64 blocks (<= 64 * block_size);
+ *                     anything else is PA_ERR_INVALID_ARG
+ *   workspace         at least pa_decode_partitioned_workspace_bytes(...)
+ *                     bytes (0, and NULL allowed, when every sequence fits
+ *                     one partition); no initialisation needed
+ * Every other argument, the outputs and the errors are those of pa_decode.
+ */
+int pa_decode_partitioned(void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
+                          int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
+                          int partition_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_decode_partitioned needs for these sizes (0 for an
+ * invalid combination or when no sequence spans two partitions). */
+size_t pa_decode_partitioned_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                                             int max_context_len, int dtype, int partition_tokens);
+
 /* pa_decode_step: one whole decode step of the batch.  Each row attends to
  * its S cached tokens and to its new token (key and value from k_new / v_new,
  * at position S); then the new token is stored and the row moved forward
@@ -467,19 +496,6 @@ int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, 
                         int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
                         int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, int64_t src_scale_layer_stride,
                         int64_t dst_scale_layer_stride, void* stream);
-
-/* ---- measurement ---------------------------------------------------------------
- *
- * pa_read_probe: the achievable HBM read rate, against which the decode
- * kernels' rates are read (the decode is a bandwidth-bound gather, "PagedAttention:
- * Virtual Memory for the KV Cache", section 13).  Reads every byte of `buf`
- * (device, `bytes` a multiple of 4096) once: wave w of the `workgroups`
- * workgroups of 256 threads reads the 4 KiB pieces w, w + W, ... (W waves),
- * four pieces of 16-byte loads in flight, and one word per workgroup goes to
- * `sink` (device, uint32 [workgroups]).  Asynchronous on `stream`; time it
- * with events.
- */
-int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 /* ---- host block manager ------------------------------------------------------
  *

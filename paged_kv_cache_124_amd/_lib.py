@@ -17,6 +17,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PA_LIBRARY", os.path.join(_HERE, "libpa.so"))
+# PA_HOST_ONLY=1: LIB_PATH is a host-only build of the block manager
+# (libpa_host.so, libpa_host_asan.so): torch is not loaded and only the pa_bm_*
+# entry points and the status strings are bound.
+HOST_ONLY = os.environ.get("PA_HOST_ONLY", "") == "1"
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = 1
@@ -33,7 +37,8 @@ PA_INT8 = 3
 
 # torch first: libpa.so then binds to the HIP runtime torch has loaded, so
 # torch's streams and device memory are valid in the library's calls.
-import torch  # noqa: E402,F401
+if not HOST_ONLY:
+    import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libpa.so not found at {LIB_PATH}; build it with "
@@ -71,6 +76,9 @@ _SIGS = {
                           c_int, c_float, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "pa_decode_step": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_workspace_bytes": (c_size_t, [c_int] * 7),
+    "pa_decode_partitioned": (c_int, [c_void_p] * 6 + [c_int] * 5 + [c_float] + [c_int] * 5
+                              + [c_void_p, c_size_t, c_void_p]),
+    "pa_decode_partitioned_workspace_bytes": (c_size_t, [c_int] * 8),
     "pa_decode_shared": (c_int, [c_void_p] * 7 + [c_int] * 6 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_step_shared": (c_int, [c_void_p] * 10 + [c_int] * 6 + [c_float] + [c_int] * 4
                               + [c_void_p, c_size_t, c_void_p]),
@@ -88,7 +96,6 @@ _SIGS = {
     "pa_append_step_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
     "pa_swap_blocks": (c_int, [c_void_p] * 5 + [c_int] * 8 + [c_int64, c_int64, c_void_p]),
     "pa_swap_blocks_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
-    "pa_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
     "pa_decode_step_fp8": (c_int, [c_void_p] * 11 + [c_int] * 5 + [c_float] + [c_int] * 3 +
                            [c_void_p, c_size_t, c_void_p]),
     "pa_decode_step_int8": (c_int, [c_void_p] * 11 + [c_int] * 5 + [c_float] + [c_int] * 3 +
@@ -125,6 +132,8 @@ _SIGS = {
     "pa_bm_stats": (c_int, [c_void_p, POINTER(BMStats)]),
 }
 for _name, (_res, _args) in _SIGS.items():
+    if HOST_ONLY and not (_name.startswith("pa_bm_") or _name in ("pa_status_string", "pa_version")):
+        continue
     _f = getattr(lib, _name)
     _f.restype = _res
     _f.argtypes = _args
@@ -227,6 +236,31 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
     args, _ws = pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
                                workspace, stream)
     _check(lib.pa_decode(*args), "pa_decode")
+    return out
+
+
+def pa_decode_partitioned_workspace_bytes(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype,
+                                          partition_tokens=0) -> int:
+    return int(lib.pa_decode_partitioned_workspace_bytes(num_seqs, Hq, Hkv, d_head, block_size, max_context_len,
+                                                         dtype, partition_tokens))
+
+
+def pa_decode_partitioned(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                          partition_tokens=0, workspace=None, stream=None):
+    """pa_decode_partitioned of include/pa.h: pa_decode on the partitioned kernels (``partition_tokens`` 0 = auto)."""
+    import torch
+    args, _ = pa_decode_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+                             torch.empty(0, dtype=torch.uint8, device=q.device), stream)
+    n, hq, d = q.shape
+    nb, hkv, _, bs = _pool_dims(k_pool, v_pool)
+    need = pa_decode_partitioned_workspace_bytes(n, hq, hkv, d, bs, max_context_len, _dtype_code(q),
+                                                 partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
+    ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_partitioned(*args[:16], int(partition_tokens), ws_ptr, ws_bytes, args[18]),
+           "pa_decode_partitioned")
     return out
 
 
@@ -739,22 +773,6 @@ def pa_copy_blocks_int8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=
     _check(lib.pa_copy_blocks_int8(*pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs,
                                                             stream)), "pa_copy_blocks_int8")
 
-
-def pa_read_probe(buf, sink, workgroups=2048, stream=None):
-    """pa_read_probe of include/pa.h: stream every byte of the device tensor ``buf`` once (the HBM read ceiling).
-
-    ``sink`` is an int32 device tensor (one word per workgroup) of at least ``workgroups`` entries."""
-    import torch
-    if not buf.is_cuda or not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < workgroups:
-        raise ValueError("buf must be a contiguous device tensor and sink an int32 tensor of >= workgroups entries")
-    nbytes = buf.numel() * buf.element_size()
-    _check(lib.pa_read_probe(c_void_p(buf.data_ptr()), nbytes, _dev(sink, "sink"), workgroups, _stream_ptr(stream)),
-           "pa_read_probe")
-
-
-# ---------------------------------------------------------------------------
-# host block manager
-# ---------------------------------------------------------------------------
 
 def _i32(a):
     return np.ascontiguousarray(a, dtype=np.int32)

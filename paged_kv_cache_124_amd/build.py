@@ -1,11 +1,16 @@
-"""Build libpa.so (HIP kernels for gfx950 + C ABI + host block manager) in-tree.
+"""Build the libraries in-tree.
 
-    python paged_kv_cache_124_amd/build.py
+    python paged_kv_cache_124_amd/build.py [-v]
 
 (run as a file: importing the package loads the library this builds)
 
-Produces ``paged_kv_cache_124_amd/libpa.so``.  hipcc cross-compiles gfx950
-code objects without a GPU, so this runs on any machine with ROCm.
+Produces, in ``paged_kv_cache_124_amd/``:
+  libpa.so            HIP kernels for gfx950 + C ABI (include/pa.h) + host block manager
+  libpa_probe.so      the HBM read-rate probe (include/pa_probe.h), loaded by bench.py only
+  libpa_host.so       the host block manager and status strings alone (g++, no HIP)
+  libpa_host_asan.so  the same built with AddressSanitizer and UBSan, for the CPU tests
+hipcc cross-compiles gfx950 code objects without a GPU, so this runs on any
+machine with ROCm.
 """
 
 from __future__ import annotations
@@ -19,9 +24,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
+HOST_LIB = os.path.join(PKG, "libpa_host.so")
+HOST_ASAN_LIB = os.path.join(PKG, "libpa_host_asan.so")
 
-HIP_SOURCES = ["decode.hip", "decode_stream.hip", "decode_stream_i8.hip", "decode_shared.hip", "kv_ops.hip", "probe.hip"]
+HIP_SOURCES = ["decode.hip", "decode_stream.hip", "decode_stream_i8.hip", "decode_shared.hip", "kv_ops.hip"]
+PROBE_SOURCES = ["probe.hip"]
 HOST_SOURCES = ["block_manager.cpp", "status.cpp"]
+HOST_FLAGS = ["-O2", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops on its own.
 # atomic optimizer off: it turns the decode kernel's lane-0 work claim into a
@@ -40,10 +51,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES + HOST_SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [*cmd, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,10 +62,26 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
     if res.returncode != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"{cmd[0]} failed with exit code {res.returncode}")
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build_host(verbose: bool = False, sanitize: bool = False) -> str:
+    """The block manager without HIP (g++), optionally with AddressSanitizer and UBSan."""
+    srcs = [os.path.join(CSRC, s) for s in HOST_SOURCES]
+    flags = HOST_FLAGS + (SANITIZE_FLAGS if sanitize else [])
+    return _run(["g++", *flags, "-I", INCLUDE, *srcs], HOST_ASAN_LIB if sanitize else HOST_LIB, verbose)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES + HOST_SOURCES]
+    _run([hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *srcs], LIB, verbose)
+    _run([hipcc(), *HIP_FLAGS, "-I", INCLUDE, *[os.path.join(CSRC, s) for s in PROBE_SOURCES]], PROBE_LIB, verbose)
+    build_host(verbose)
+    build_host(verbose, sanitize=True)
     return LIB
 
 

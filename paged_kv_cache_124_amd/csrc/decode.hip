@@ -31,8 +31,6 @@
 // Pool layout (per layer), x = 16 / sizeof(elem):
 //   K [num_blocks][Hkv][D/x][B][x],  V [num_blocks][Hkv][D][B].
 
-#include <cstdlib>
-
 #include "common.h"
 #include "decode_stream.h"
 
@@ -59,8 +57,9 @@ bool mfma_eligible(int g, int d, int block_size, int dtype) {
 // Partition size: the largest of 512, 256, 128 tokens that still yields at
 // least ~2048 workgroups (8 per CU over 256 CUs) for the longest sequence,
 // capped so that a partition spans at most 64 blocks (one table entry per
-// lane).  PA_PART_TOKENS (a multiple of 128) overrides it for tuning sweeps.
-Plan make_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, int dtype) {
+// lane).  A caller of pa_decode_partitioned may fix it instead (`part_tokens`,
+// a multiple of 128 up to that cap; 0 = this rule).
+Plan make_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, int dtype, int part_tokens = 0) {
   Plan p{};
   const int g = hkv > 0 ? hq / hkv : 0;
   p.mfma = mfma_eligible(g, d, block_size, dtype);
@@ -73,10 +72,7 @@ Plan make_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx
       part = cand;
       if (wgs >= 2048) break;
     }
-    if (const char* env = std::getenv("PA_PART_TOKENS")) {
-      const int v = std::atoi(env);
-      if (v >= 128 && v % 128 == 0 && v <= cap) part = v;
-    }
+    if (part_tokens > 0) part = part_tokens;
     p.part = part;
   } else {
     p.part = kGenericPart;
@@ -460,13 +456,16 @@ void launch_merge(const Plan& pl, hipStream_t s, const float* ws, const int32_t*
 
 namespace pa {
 namespace {
-// The persistent stream kernel serves bf16 with G <= 16; PA_DECODE_PATH=partition
-// selects the partitioned kernel instead (kept for A/B measurements).
+// The persistent stream kernel serves bf16 with G <= 16 and N <= 3072; the
+// partitioned kernels serve the rest (and pa_decode_partitioned).
 bool use_stream(int num_seqs, int hq, int hkv, int d, int block_size, int dtype) {
   if (hkv <= 0 || hq % hkv != 0) return false;
-  if (!stream_eligible(num_seqs, hq / hkv, d, block_size, dtype)) return false;
-  const char* env = std::getenv("PA_DECODE_PATH");
-  return !(env && env[0] == 'p');
+  return stream_eligible(num_seqs, hq / hkv, d, block_size, dtype);
+}
+// Partition sizes a caller may fix: multiples of 128 tokens spanning at most
+// 64 blocks (0 = automatic).
+bool valid_part_tokens(int part_tokens, int block_size) {
+  return part_tokens == 0 || (part_tokens >= 128 && part_tokens % 128 == 0 && part_tokens <= 64 * block_size);
 }
 // Groups are served by the shared-prefix kernel where the persistent kernel
 // runs and the sizes fit it; elsewhere they are ignored, which gives the same
@@ -501,6 +500,15 @@ extern "C" size_t pa_decode_shared_workspace_bytes(int num_seqs, int num_groups,
   return pa_decode_workspace_bytes(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
 }
 
+extern "C" size_t pa_decode_partitioned_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                                                        int max_context_len, int dtype, int partition_tokens) {
+  if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_context_len < 0) return 0;
+  if (Hq % Hkv != 0 || (dtype != PA_F32 && dtype != PA_BF16)) return 0;
+  if (!pa::valid_part_tokens(partition_tokens, block_size)) return 0;
+  const pa::Plan p = pa::make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype, partition_tokens);
+  return pa::plan_workspace_bytes(p, num_seqs, Hq, d_head);
+}
+
 extern "C" int pa_decode_partition_tokens(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                           int max_context_len, int dtype) {
   if (num_seqs <= 0 || Hq <= 0 || Hkv <= 0) return 0;
@@ -514,7 +522,7 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
                 const int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
                 int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream, const pa::StepInputs* step, const int32_t* groups = nullptr,
-                int num_groups = 0) {
+                int num_groups = 0, bool partitioned = false, int part_tokens = 0) {
   using namespace pa;
   if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0 || num_blocks < 0)
@@ -532,21 +540,22 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
 
   const float scale_log2_s = scale * kLog2e;
   if (num_groups < 0 || (num_groups > 0 && !groups)) return PA_ERR_INVALID_ARG;
-  if (use_shared(num_seqs, num_groups, Hq, Hkv, d_head, block_size, dtype)) {
+  if (partitioned && (step || num_groups > 0 || !valid_part_tokens(part_tokens, block_size))) return PA_ERR_INVALID_ARG;
+  if (!partitioned && use_shared(num_seqs, num_groups, Hq, Hkv, d_head, block_size, dtype)) {
     const StreamPlan sp = shared_plan(num_seqs, num_groups, Hq, Hkv, d_head, block_size, max_context_len);
     if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
     return launch_shared(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, groups,
                          num_groups, out, workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq,
                          num_blocks, scale_log2_s, step);
   }
-  if (use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) {
+  if (!partitioned && use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) {
     const StreamPlan sp = stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len);
     if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
     return launch_stream(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, out,
                          workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq, num_blocks,
                          scale_log2_s, step);
   }
-  const Plan pl = make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype);
+  const Plan pl = make_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype, part_tokens);
   const size_t need = plan_workspace_bytes(pl, num_seqs, Hq, d_head);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
   float* ws = static_cast<float*>(workspace);
@@ -601,6 +610,16 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_pool, const voi
   return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
                      scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes, stream,
                      nullptr);
+}
+
+extern "C" int pa_decode_partitioned(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq,
+                                     int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq,
+                                     int max_context_len, int num_blocks, int dtype, int partition_tokens,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
+                     scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes, stream,
+                     nullptr, nullptr, 0, true, partition_tokens);
 }
 
 extern "C" int pa_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,

@@ -334,7 +334,7 @@ __device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], const UTile& t, cons
     const int c = 16 * cb + r;
     if (c < cols) {
       if (whole) {
-        const float inv = 1.f / zt;
+        const float inv = zt > 0.f ? 1.f / zt : 0.f;  // every token left out (blocks outside the pool): zeros
         const int seq = grp ? first + col_m[cb] : t.n;
         const int h = grp ? col_h[cb] : c;
         uint16_t* o = out + (static_cast<int64_t>(seq) * hq + t.j * us.g + h) * D + 4 * gq;
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
           val[k][e] = pb[k] ? x : 0.f;
         }
       }
-      float mx = mine ? m_l : -INFINITY;
+      float mx = mine ? m_l : -__FLT_MAX__;  // finite: exp2(m - mx) is never exp2(-inf - -inf)
 #pragma unroll
       for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
       const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
 #pragma unroll
         for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
       }
-      const float inv = 1.f / zz;
+      const float inv = zz > 0.f ? 1.f / zz : 0.f;  // every token left out: zeros
 #pragma unroll
       for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
     }
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
       return p0 ? p0 + (row0 + h) * (D + 4) : nullptr;
     };
     for (int h = wave; h < g; h += 4) {
-      float mx = -INFINITY;
+      float mx = -__FLT_MAX__;  // finite, as above
       for (int base = 0; base < sg.cnt; base += 64) {
         const float* rr = base + lane < sg.cnt ? record(base + lane, h) : nullptr;
         if (rr) mx = fmaxf(mx, rr[0]);
@@ -742,7 +742,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
       }
 #pragma unroll
       for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
-      const float inv = 1.f / zz;
+      const float inv = zz > 0.f ? 1.f / zz : 0.f;  // every token left out: zeros
 #pragma unroll
       for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
     }

@@ -3,7 +3,6 @@
 // the resident-workgroup query and the dispatch over head size, block size and
 // cache format (bf16 and FP8 E4M3 here; INT8 in decode_stream_i8.hip).
 
-#include <cstdlib>
 #include <mutex>
 
 #include "decode_stream_kernel.h"
@@ -11,55 +10,25 @@
 namespace pa {
 namespace {
 
-template <int D, int B>
-const void* stream_kernel() {
-  return reinterpret_cast<const void*>(&decode_stream<D, B, kKvBf16>);
-}
-
-const void* stream_kernel_for(int d, int b) {
-  if (d == 128) return b == 8 ? stream_kernel<128, 8>() : (b == 16 ? stream_kernel<128, 16>() : stream_kernel<128, 32>());
-  return b == 8 ? stream_kernel<64, 8>() : (b == 16 ? stream_kernel<64, 16>() : stream_kernel<64, 32>());
-}
-
 size_t stream_lds(int n_seqs) { return (2 * static_cast<size_t>(n_seqs) + 1) * sizeof(int32_t); }
 
-// Resident workgroups per CU and CU count of the current device, cached.
-// Without a device (host-only use) the MI355X figures (256 CUs) and 2
-// workgroups per CU are assumed.
-struct DeviceShape {
-  int cus = 256;
-  int wg_per_cu[2][3] = {{2, 2, 2}, {2, 2, 2}};
-};
-
-const DeviceShape& device_shape() {
-  static DeviceShape shapes[16];
-  static bool ready[16] = {};
+// CU count of the current device, cached per device.  Without a device
+// (host-only use) the MI355X figure (256 CUs) is assumed.
+int device_cus() {
+  static int cus[16] = {};
   static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
     (void)hipGetLastError();
-    static DeviceShape fallback;
-    return fallback;
+    return 256;
   }
   std::lock_guard<std::mutex> lock(mu);
-  if (!ready[dev]) {
-    DeviceShape s;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) s.cus = cus;
-    const int ds[2] = {64, 128}, bs[3] = {8, 16, 32};
-    for (int a = 0; a < 2; ++a)
-      for (int c = 0; c < 3; ++c) {
-        int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, stream_kernel_for(ds[a], bs[c]), 256,
-                                                         stream_lds(kMaxSeqs)) == hipSuccess &&
-            nb > 0)
-          s.wg_per_cu[a][c] = nb;
-      }
+  if (cus[dev] == 0) {
+    int c = 0;
+    cus[dev] = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0 ? c : 256;
     (void)hipGetLastError();
-    shapes[dev] = s;
-    ready[dev] = true;
   }
-  return shapes[dev];
+  return cus[dev];
 }
 
 }  // namespace
@@ -74,18 +43,10 @@ bool stream_eligible_fp8(int num_seqs, int g, int d, int block_size) {
 }
 
 StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, bool fp8) {
-  const DeviceShape& ds = device_shape();
-  const int ai = d == 128 ? 1 : 0;
-  const int bi = block_size == 8 ? 0 : (block_size == 16 ? 1 : 2);
   StreamPlan p;
   // One workgroup (4 waves, one per SIMD) per CU: with two or more per CU the
   // oldest waves win the memory pipe and the split's completion times spread.
-  int per_cu = 1;
-  if (const char* env = std::getenv("PA_STREAM_WG_PER_CU")) {  // tuning sweeps
-    const int v = std::atoi(env);
-    if (v >= 1 && v <= ds.wg_per_cu[ai][bi]) per_cu = v;
-  }
-  int64_t wgs = static_cast<int64_t>(ds.cus) * per_cu;
+  int64_t wgs = device_cus();
   // no more waves than tiles / 2 (upper bound of the work from max_context_len)
   const int tok = fp8 ? kTok<true> : kTok<false>;
   const int64_t t_bound = static_cast<int64_t>(num_seqs) * hkv * ((max_ctx + tok - 1) / tok);

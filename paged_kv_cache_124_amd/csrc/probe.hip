@@ -5,7 +5,11 @@
 // 16-byte loads, no LDS, no compute beyond an XOR that keeps the loads alive --
 // is the ceiling a kernel that streams whole blocks can approach.
 
-#include "common.h"
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa_probe.h"
 
 namespace pa {
 namespace {
@@ -44,10 +48,10 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 
 extern "C" int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
   using namespace pa;
-  if (bytes % 4096 != 0 || workgroups < 1 || workgroups > 65535) return PA_ERR_INVALID_ARG;
-  if (bytes == 0) return PA_OK;
-  if (!buf || !sink) return PA_ERR_INVALID_ARG;
+  if (bytes % 4096 != 0 || workgroups < 1 || workgroups > 65535) return 1;
+  if (bytes == 0) return 0;
+  if (!buf || !sink) return 1;
   read_probe_kernel<<<dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint4*>(buf), static_cast<int64_t>(bytes / 4096), sink);
-  return launch_status();
+  return hipGetLastError() == hipSuccess ? 0 : 7;
 }

@@ -155,20 +155,31 @@ def test_short_lengths_with_large_launch_bound():
     assert_close(out, ref, "short lengths, launch bound 4096")
 
 
-def test_partitioned_path_gqa8b_and_edges(monkeypatch):
-    """The partitioned bf16 kernel + merge (the path for very large batches), forced on the 8B GQA layer and edge lengths."""
+def _run_partitioned(c, part=0):
     import paged_kv_cache_124_amd as pa
-    monkeypatch.setenv("PA_DECODE_PATH", "partition")
+    out = torch.empty_like(c.q)
+    pa.pa_decode_partitioned(out, c.q, c.k, c.v, c.tables_dev, c.lens_dev, c.scale, c.max_ctx, part)
+    return out
+
+
+def test_partitioned_path_gqa8b_and_edges():
+    """The partitioned bf16 kernel + merge (the path for very large batches), on the 8B GQA layer at every partition
+    size it takes and on edge lengths."""
+    import paged_kv_cache_124_amd as pa
     print("[case] partitioned gqa8b", flush=True)
     c = make_case(synth.gqa8b())
-    assert pa.pa_decode_partition_tokens(len(c.lens), c.hq, c.hkv, c.d, c.block_size, c.max_ctx, pa.PA_BF16) > 0
-    out = run_decode(c)
-    assert_close(out, oracle_outputs(c, range(len(c.lens))), "partitioned gqa8b")
+    ref = oracle_outputs(c, range(len(c.lens)))
+    for part in (0, 128, 256, 512, 1024):
+        assert_close(_run_partitioned(c, part), ref, f"partitioned gqa8b part={part}")
     for bs in (8, 16, 32):
         e = make_case(synth.gqa8b(), EDGE_LENS, block_size=bs, seed=800 + bs)
-        out = run_decode(e)
+        out = _run_partitioned(e)
         assert torch.count_nonzero(out[0].float()) == 0
         assert_close(out, oracle_outputs(e, range(len(EDGE_LENS))), f"partitioned edges bs={bs}")
+    # partition sizes outside the documented set are refused before any launch
+    for bad in (64, 100, 129, 64 * 16 + 128):
+        with pytest.raises(pa.PAError):
+            _run_partitioned(c, bad)
 
 
 def test_many_sequences_take_partitioned_path():

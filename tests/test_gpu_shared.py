@@ -271,3 +271,34 @@ def test_fork_workload_shared_sixteen_steps(fused):
             assert_close(out[sample], ref, f"fork shared step {step}")
     gk, gv = _bits(k, v)
     assert np.array_equal(gk, ek) and np.array_equal(gv, ev), "pool differs from the oracle's copy + append"
+
+
+def test_rows_with_every_block_outside_the_pool_give_zeros():
+    """A grouped row set and an ungrouped row whose table entries all lie outside [0, num_blocks): no token is
+    attended, so pa_decode_shared writes zeros for them (as pa_decode does), never NaN; the other rows keep the
+    oracle's attention."""
+    import paged_kv_cache_124_amd as pa
+    hq, hkv, d, bs = 32, 8, 128, 16
+    print("[case] shared rows outside the pool", flush=True)
+    case, seqs = _forest(1234, hq, hkv, d, bs)
+    groups = _groups(case, seqs)
+    assert len(groups) > 0
+    first, rows, _ = (int(x) for x in groups[0])
+    in_group = set()
+    for f, r_, _ in groups.tolist():
+        in_group |= set(range(f, f + r_))
+    lone = [i for i in range(len(seqs)) if i not in in_group]
+    assert lone, "the forest has an ungrouped row"
+    dead = list(range(first, first + rows)) + [lone[0]]
+    tables = case.tables.copy()
+    for i in dead:
+        nb_i = -(-int(case.lens[i]) // bs)
+        tables[i, :nb_i] = case.num_blocks + 3 + np.arange(nb_i)
+    out = torch.full_like(case.q, float("nan"))
+    pa.pa_decode_shared(out, case.q, case.k, case.v, torch.from_numpy(tables).cuda(), case.lens_dev,
+                        torch.from_numpy(groups).cuda(), case.scale, case.max_ctx)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    assert torch.count_nonzero(out[dead].float()) == 0
+    keep = [i for i in range(len(seqs)) if i not in dead]
+    assert_close(out[keep], oracle_outputs(case, keep), "rows inside the pool")
