@@ -186,6 +186,33 @@ int pa_decode_step(void* out, const void* q, const void* k_new, const void* v_ne
                    int max_context_len, int num_blocks, int dtype, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* pa_decode_step_noalloc: pa_decode_step for callers that cannot allocate
+ * device memory -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, outputs, row updates and
+ * errors as pa_decode_step, without `workspace` / `workspace_bytes`: the
+ * workspace is a fixed device array of PA_NOALLOC_SCRATCH_BYTES bytes inside
+ * the library, one per GPU, held from the first call on that GPU until the
+ * process ends.  The call allocates and frees nothing (no hipMalloc, no
+ * allocating library routine); it only enqueues the two kernels on `stream`.
+ *   - Limit: the workspace pa_decode_step would need for these sizes
+ *     (pa_decode_workspace_bytes) must fit PA_NOALLOC_SCRATCH_BYTES, else
+ *     PA_ERR_WORKSPACE before any launch.  It is 2 * 256 * ceil(4 (N + 1) / 256)
+ *     bytes plus 2 * W * (Hq / Hkv) * (d_head + 4) * 4, W = 4 waves per CU
+ *     (1024 on 256 CUs): up to Hq / Hkv = 7 at d_head 128 on MI355X (the 8B
+ *     GQA shape, Hq / Hkv = 4, needs 4.3 MB).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind; no word of it needs clearing (each call writes every word it
+ *     reads).  Calls that may overlap in time on one GPU (other streams, other
+ *     host threads) race on the array and must be serialised by the caller.
+ *   - PA_ERR_HIP when the runtime cannot give the array's device address.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int pa_decode_step_noalloc(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                           void* v_pool, const int32_t* slot_mapping, int32_t* block_tables,
+                           int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head, int block_size,
+                           float scale, int max_blocks_per_seq, int max_context_len, int num_blocks, int dtype,
+                           void* stream);
+
 /* pa_decode_shared: pa_decode, with the full blocks that a group of
  * consecutive rows shares read once for the whole group.  A full block
  * referenced by several sequences is immutable, so every sharer sees the same

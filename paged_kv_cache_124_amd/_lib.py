@@ -76,6 +76,7 @@ _SIGS = {
                           c_int, c_float, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "pa_decode_step": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_workspace_bytes": (c_size_t, [c_int] * 7),
+    "pa_decode_step_noalloc": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float] + [c_int] * 4 + [c_void_p]),
     "pa_decode_partitioned": (c_int, [c_void_p] * 6 + [c_int] * 5 + [c_float] + [c_int] * 5
                               + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_partitioned_workspace_bytes": (c_size_t, [c_int] * 8),
@@ -265,7 +266,7 @@ def pa_decode_partitioned(out, q, k_pool, v_pool, block_tables, context_lens, sc
 
 
 def pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens, scale,
-                        max_context_len, workspace=None, stream=None, slot_pointer=None):
+                        max_context_len, workspace=None, stream=None, slot_pointer=None, allocate=True):
     """Validate once and return (args, workspace) for repeated ``lib.pa_decode_step(*args)`` calls.
 
     ``slot_pointer`` (an int) replaces slot_mapping's data pointer, e.g. with the
@@ -289,7 +290,7 @@ def pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, bloc
         raise ValueError("block_tables must be [N][max_blocks]")
     dt = _dtype_code(q)
     need = pa_decode_workspace_bytes(n, hq, hkv, d, bs, max_context_len, dt)
-    if workspace is None and need > 0:
+    if workspace is None and need > 0 and allocate:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)  # every word is written before it is read
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -307,6 +308,22 @@ def pa_decode_step(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tab
     args, _ws = pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens,
                                     scale, max_context_len, workspace, stream)
     _check(lib.pa_decode_step(*args), "pa_decode_step")
+    return out
+
+
+PA_NOALLOC_SCRATCH_BYTES = 8 << 20  # the fixed device array of pa_decode_step_noalloc (include/pa.h)
+
+
+def pa_decode_step_noalloc(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens, scale,
+                           max_context_len, stream=None):
+    """pa_decode_step_noalloc of include/pa.h: pa_decode_step with the library's fixed device workspace.
+
+    Allocates nothing, here or in the library: the argument checks are those of
+    pa_decode_step_args without its workspace.
+    """
+    args, _ = pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens,
+                                  scale, max_context_len, stream=stream, allocate=False)
+    _check(lib.pa_decode_step_noalloc(*args[:19], args[21]), "pa_decode_step_noalloc")
     return out
 
 

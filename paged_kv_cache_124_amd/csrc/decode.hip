@@ -31,6 +31,8 @@
 // Pool layout (per layer), x = 16 / sizeof(elem):
 //   K [num_blocks][Hkv][D/x][B][x],  V [num_blocks][Hkv][D][B].
 
+#include <mutex>
+
 #include "common.h"
 #include "decode_stream.h"
 
@@ -636,6 +638,70 @@ extern "C" int pa_decode_step(void* out, const void* q, const void* k_new, const
   return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
                      scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, workspace, workspace_bytes,
                      stream, &step);
+}
+
+// ---- pa_decode_step_noalloc: the step with its workspace in a fixed device array ----
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops, harnesses that forbid allocation): the workspace of pa_decode_step
+// lives in `scratch`, one array per GPU that the library holds until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is a stand-in, not a device pointer): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+
+namespace {
+constexpr size_t kNoAllocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch is a whole number of 256-byte lines");
+}  // namespace
+
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// The device address of `scratch` on the current device, or nullptr when the
+// runtime cannot give it.  Taken on a device's first call and kept.
+void* scratch_on_current_device() {
+  constexpr int kMaxDevices = 64;
+  static void* ptrs[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptrs[dev] = ptr;
+  }
+  return ptrs[dev];
+}
+
+}  // namespace
+
+extern "C" int pa_decode_step_noalloc(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                      void* v_pool, const int32_t* slot_mapping, int32_t* block_tables,
+                                      int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head,
+                                      int block_size, float scale, int max_blocks_per_seq, int max_context_len,
+                                      int num_blocks, int dtype, void* stream) {
+  using namespace pa;
+  if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d_head <= 0 || block_size <= 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  if (!use_stream(num_seqs, Hq, Hkv, d_head, block_size, dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  const size_t need = stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len).workspace_bytes;
+  if (need > kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return PA_ERR_HIP;
+  const StepInputs step{k_new, v_new, slot_mapping};
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size,
+                     scale, max_blocks_per_seq, max_context_len, num_blocks, dtype, ws, kNoAllocScratchBytes, stream,
+                     &step);
 }
 
 extern "C" int pa_decode_shared(void* out, const void* q, const void* k_pool, const void* v_pool,
