@@ -94,9 +94,12 @@ def test_fork_cow_sixteen_steps(fused):
         mst, mtables, mlens = model.build_batch(seqs, mb)
         assert st == mst == 0 and tables.tolist() == mtables and lens.tolist() == mlens
         assert np.array_equal(d_tables.cpu().numpy(), tables) and np.array_equal(d_lens.cpu().numpy(), lens)
-        if step in (0, 8, steps - 1):
+        if step in (0, 8):
             ref = oracle_outputs(case, sample, q=q, lens=lens, tables=mtables)
             assert_close(out[sample], ref, f"fork step {step}")
+        elif step in (9, steps - 1):  # the step that opens block 129 (position 2,064) and the last: every row
+            ref = oracle_outputs(case, seqs, q=q, lens=lens, tables=mtables)
+            assert_close(out, ref, f"fork step {step}, every row")
     assert total_pairs == P * (S - 1), total_pairs
     gk, gv = _bits(k, v)
     assert np.array_equal(gk, ek) and np.array_equal(gv, ev), "pool differs from the oracle's copy + append"
@@ -105,7 +108,7 @@ def test_fork_cow_sixteen_steps(fused):
     assert bm.stats() == model.stats()
 
 
-def test_long_context_32_layers_sampled():
+def test_long_context_32_layers():
     w = synth.long()
     print("[case] long: 32 layers x 16 x 32768 tokens (64 GiB pool)", flush=True)
     c = make_case(w, layers=w.layers)
@@ -115,9 +118,12 @@ def test_long_context_32_layers_sampled():
         outs.append(run_decode(c, layer=layer))
     torch.cuda.synchronize()
     print("[case] long: 32 layers decoded", flush=True)
+    # every sequence of the first and the last layer, and sampled (layer, sequence) pairs of the others
+    for layer in (0, w.layers - 1):
+        ref = oracle_outputs(c, range(16), layer=layer)
+        assert_close(outs[layer], ref, f"long layer {layer}, every sequence")
     rng = np.random.default_rng(9)
-    pairs = [(0, 0), (w.layers - 1, 15)] + [(int(a), int(b)) for a, b in
-                                           zip(rng.integers(0, w.layers, 4), rng.integers(0, 16, 4))]
+    pairs = [(int(a), int(b)) for a, b in zip(rng.integers(1, w.layers - 1, 6), rng.integers(0, 16, 6))]
     for layer, seq in pairs:
         ref = oracle_outputs(c, [seq], layer=layer)
         assert_close(outs[layer][seq:seq + 1], ref, f"long layer {layer} seq {seq}")

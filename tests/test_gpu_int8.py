@@ -158,14 +158,13 @@ def test_decode_int8_gqa8b_all_sequences():
     assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "run-to-run"
 
 
-def test_decode_int8_sweep_sampled():
-    """256 sequences of 4096 - r tokens over an INT8 cache (B = 16); 16 sampled sequences against the oracle."""
-    print("[case] int8 sweep", flush=True)
-    c = make_case(synth.sweep(16), int8=True)
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_decode_int8_sweep_every_row(bs):
+    """256 sequences of 4096 - r tokens over an INT8 cache; every output against the oracle."""
+    print(f"[case] int8 sweep bs={bs}", flush=True)
+    c = make_case(synth.sweep(bs), int8=True)
     out = run_decode(c)
-    rng = np.random.default_rng(216)
-    sample = sorted(rng.choice(len(c.lens), size=16, replace=False).tolist())
-    assert_close(out[sample], oracle_outputs(c, sample), "int8 sweep")
+    assert_close(out, oracle_outputs(c, range(len(c.lens))), f"int8 sweep bs={bs}")
     del c
     torch.cuda.empty_cache()
 

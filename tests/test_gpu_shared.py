@@ -266,9 +266,12 @@ def test_fork_workload_shared_sixteen_steps(fused):
         assert np.array_equal(d_tables.cpu().numpy(), tables) and np.array_equal(d_lens.cpu().numpy(), lens)
         # the groups found before the steps still hold: the prefix blocks are never written
         assert bm.shared_groups(seqs, S)[1].tolist() == groups.tolist()
-        if step in (0, 9, steps - 1):
+        if step == 0:
             ref = oracle_outputs(case, sample, q=q, lens=lens, tables=mtables)
             assert_close(out[sample], ref, f"fork shared step {step}")
+        elif step in (9, steps - 1):  # the step that opens block 129 (position 2,064) and the last: every row
+            ref = oracle_outputs(case, seqs, q=q, lens=lens, tables=mtables)
+            assert_close(out, ref, f"fork shared step {step}, every row")
     gk, gv = _bits(k, v)
     assert np.array_equal(gk, ek) and np.array_equal(gv, ev), "pool differs from the oracle's copy + append"
 

@@ -159,7 +159,5 @@ def test_step_gqa8b_matches_oracle_and_is_repeatable():
     st, tab2, lens2 = c.bm.build_batch(list(range(n)), max_blocks)
     assert np.array_equal(t.cpu().numpy(), tab2) and np.array_equal(ln.cpu().numpy(), lens2)
     c.k, c.v = k, v
-    rng = np.random.default_rng(3)
-    sample = sorted(rng.choice(n, 16, replace=False).tolist())
-    ref = oracle_outputs(c, sample, lens=lens2, tables=tab2)
-    assert_close(outs[0][sample], ref, "decode_step gqa8b")
+    ref = oracle_outputs(c, range(n), lens=lens2, tables=tab2)
+    assert_close(outs[0], ref, "decode_step gqa8b, every row")
