@@ -23,21 +23,22 @@
  *     synchronisation.  No C++ exception crosses the ABI.
  *   - All sizes are in elements unless a name ends in _bytes.
  *
- * Physical pool layout (one layer; a multi-layer pool stacks layers with a
- * stride of layer_stride_elems elements).  E = element size, x = 16 / E
- * (x = 8 for bf16, 4 for fp32), B = block_size, D = d_head:
+ * Pool layout (one layer; a multi-layer pool stacks layers with a stride of
+ * layer_stride_elems elements).  B = block_size, D = d_head; K and V pools
+ * alike, every element type (fp32, bf16, or one-byte codes):
  *
- *   K pool: [num_blocks][Hkv][D / x][B][x]
+ *   [num_blocks][Hkv][B][D]
  *       key element d of the token in slot `off` of block `pb`, KV head j:
- *       k_pool[(((pb * Hkv + j) * (D / x) + d / x) * B + off) * x + d % x]
- *   V pool: [num_blocks][Hkv][D][B]
- *       value element d: v_pool[((pb * Hkv + j) * D + d) * B + off]
+ *       k_pool[((pb * Hkv + j) * B + off) * D + d]
+ *       value element d: v_pool[((pb * Hkv + j) * B + off) * D + d]
  *
- *   The pages call the in-block layout an implementation choice ("PagedAttention:
- *   Virtual Memory for the KV Cache", section 12).  This one is chosen for
- *   gfx950 matrix-core operands: one 16-byte load per lane of each key row
- *   chunk, and runs of consecutive tokens per value element.  Each
- *   (block, KV head) is one contiguous run of B * D * E bytes in each pool.
+ *   Each (block, KV head) is one contiguous run of B * D * E bytes (E the
+ *   element size) in each pool, its B token rows of D contiguous elements
+ *   ("PagedAttention: Virtual Memory for the KV Cache", section 12 leaves the
+ *   in-block layout to the implementation).  The decode kernels copy whole
+ *   rows into LDS with 16-byte loads and form their matrix-core operands there
+ *   (the value operand with gfx950's transposing LDS reads); the appends store
+ *   each new row with 16-byte stores.
  *
  * Address translation ("PagedAttention: Virtual Memory for the KV Cache",
  * section 7): token i of a sequence lives in logical block i / B at offset
@@ -353,8 +354,7 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int
  * caller, positive and finite.  Code c of block pb, KV head j stands for
  * value(c) * scale[pb][j].  Static per-head scaling is the case where all
  * blocks of a head carry the same scale.
- * Pool layout: as above with E = 1, x = 16:
- *   K codes [num_blocks][Hkv][D / 16][B][16], V codes [num_blocks][Hkv][D][B].
+ * Pool layout: as above with E = 1: K and V codes [num_blocks][Hkv][B][D].
  */
 
 /* pa_decode over an FP8 cache.  q and out are bf16 [num_seqs][Hq][d_head];

@@ -173,19 +173,17 @@ def _dev(t, name):
     return c_void_p(t.data_ptr())
 
 
-def pool_shapes(num_blocks: int, hkv: int, d_head: int, block_size: int, elem_bytes: int):
-    """Shapes of one layer's K and V pools in the library's layout (see include/pa.h)."""
-    x = 16 // elem_bytes
-    return (num_blocks, hkv, d_head // x, block_size, x), (num_blocks, hkv, d_head, block_size)
+def pool_shapes(num_blocks: int, hkv: int, d_head: int, block_size: int, elem_bytes: int = 2):
+    """Shapes of one layer's K and V pools: [num_blocks][Hkv][B][D] each (see include/pa.h)."""
+    shape = (num_blocks, hkv, block_size, d_head)
+    return shape, shape
 
 
 def _pool_dims(k_pool, v_pool):
-    if k_pool.dim() != 5 or v_pool.dim() != 4:
-        raise ValueError("k_pool must be [num_blocks][Hkv][D/x][B][x] and v_pool [num_blocks][Hkv][D][B]")
-    nb, hkv, dx, bs, x = k_pool.shape
-    if tuple(v_pool.shape) != (nb, hkv, dx * x, bs) or x * k_pool.element_size() != 16:
-        raise ValueError("k_pool / v_pool shapes do not match the pool layout")
-    return nb, hkv, dx * x, bs
+    if k_pool.dim() != 4 or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool must both be [num_blocks][Hkv][B][D]")
+    nb, hkv, bs, d = k_pool.shape
+    return nb, hkv, d, bs
 
 
 def pa_decode_workspace_bytes(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, dtype) -> int:
@@ -464,7 +462,7 @@ def pa_copy_blocks_args(k_pool, v_pool, src_dst_pairs, stream=None):
     returned tuple's 4th entry to use a prefix of the pairs).
     """
     import torch
-    layered = k_pool.dim() == 6
+    layered = k_pool.dim() == 5
     kl, vl = (k_pool[0], v_pool[0]) if layered else (k_pool, v_pool)
     nb, hkv, d, bs = _pool_dims(kl, vl)
     layers = k_pool.shape[0] if layered else 1
@@ -512,7 +510,7 @@ def _pool_ptr(t, name):
 
 def _layers(k_pool):
     """(layers, blocks per layer, elements per layer) of a one-layer [nb]... or layered [L][nb]... K pool."""
-    if k_pool.dim() == 6:
+    if k_pool.dim() == 5:
         return k_pool.shape[0], k_pool.shape[1], k_pool[0].numel()
     return 1, k_pool.shape[0], k_pool.numel()
 
@@ -527,7 +525,7 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None):
     ld, nbd, ed = _layers(dst_k)
     if ls != ld or src_k.dtype != dst_k.dtype:
         raise ValueError("pools disagree in layers or element type")
-    kl = src_k[0] if src_k.dim() == 6 else src_k
+    kl = src_k[0] if src_k.dim() == 5 else src_k
     vl = src_v[0] if src_v.dim() == 5 else src_v
     _, hkv, d, bs = _pool_dims(kl, vl)
     _check(lib.pa_swap_blocks(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), _pool_ptr(src_k, "src_k"),
@@ -561,7 +559,7 @@ def pa_swap_blocks_int8(dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_
 
 
 # ---------------------------------------------------------------------------
-# FP8 (E4M3) and INT8 caches: uint8 code pools in the layout above (x = 16)
+# FP8 (E4M3) and INT8 caches: uint8 code pools [num_blocks][Hkv][B][D]
 # and float32 scales [num_blocks][Hkv] (or [L][num_blocks][Hkv] for a layered
 # copy); the INT8 functions take the same arguments as the FP8 ones
 # ---------------------------------------------------------------------------
@@ -765,7 +763,7 @@ def pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, str
     Pools and scales are one layer or all layers (leading [L] on both).
     """
     import torch
-    layered = k_pool.dim() == 6
+    layered = k_pool.dim() == 5
     kl, vl = (k_pool[0], v_pool[0]) if layered else (k_pool, v_pool)
     nb, hkv, d, bs = _fp8_pools(kl, vl)
     layers = k_pool.shape[0] if layered else 1

@@ -77,8 +77,17 @@ def build_host(verbose: bool = False, sanitize: bool = False) -> str:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES + HOST_SOURCES]
-    _run([hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *srcs], LIB, verbose)
+    # one hipcc per source, in parallel, then one link
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"] + ["-c", *(extra_flags or []), "-I", INCLUDE, "-I", CSRC]
+    srcs = HIP_SOURCES + HOST_SOURCES
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in srcs]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda so: _run([hipcc(), *compile_flags, os.path.join(CSRC, so[0])], so[1], verbose),
+                    zip(srcs, objs)))
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs], LIB, verbose)
     _run([hipcc(), *HIP_FLAGS, "-I", INCLUDE, *[os.path.join(CSRC, s) for s in PROBE_SOURCES]], PROBE_LIB, verbose)
     build_host(verbose)
     build_host(verbose, sanitize=True)

@@ -28,13 +28,13 @@
 //   decode_generic fp32 or bf16, any G: one wave per (partition, query head,
 //                 sequence); per-token dot products with wave reductions.
 //
-// Pool layout (per layer), x = 16 / sizeof(elem):
-//   K [num_blocks][Hkv][D/x][B][x],  V [num_blocks][Hkv][D][B].
+// Pool layout (per layer): K and V [num_blocks][Hkv][B][D].
 
 #include <mutex>
 
 #include "common.h"
 #include "decode_stream.h"
+#include "decode_tile.h"
 
 namespace pa {
 namespace {
@@ -96,12 +96,15 @@ size_t plan_workspace_bytes(const Plan& p, int num_seqs, int hq, int d) {
 // made of two 16-token slabs a = 0, 1:
 //   q.K^T  S^T[token][head] = K[token][:] . Q[head][:]
 //          A operand (16 x 32): lane holds key row r of the slab, d-chunk
-//          c = 4 jj + gq (8 elements, one 16-byte load from the K layout);
+//          c = 4 jj + gq (8 elements, one 16-byte load from the key row);
 //          B operand (32 x 16): Q[head r][chunk c], zero for r >= G;
 //          result: lane holds S^T[tokens 4 gq .. 4 gq + 3][head r].
 //   P.V    O^T[d][head] += V^T[d][tokens] . P^T[tokens][head]
 //          A operand: V^T[d = 16 mm + r][8 tokens] = 4 tokens of slab 0 and 4
-//          of slab 1 at rows 4 gq .. 4 gq + 3 (two 8-byte loads);
+//          of slab 1 at rows 4 gq .. 4 gq + 3: the wave copies the tile's 32
+//          value rows into its LDS buffer (16 bytes per lane, chunks swizzled
+//          as the persistent kernel stages them) and reads each 4-token group
+//          back with one transposing 8-byte read;
 //          B operand: P^T for those 8 tokens and head r -- exactly the 8
 //          scores this lane already holds, so P needs no data movement;
 //          result: lane holds O^T[d = 16 mm + 4 gq + i][head r].
@@ -118,7 +121,10 @@ __global__ __launch_bounds__(256) void decode_mfma(
   constexpr int VT = D / 16;      // output tiles over d in P.V
   constexpr int64_t BLK = static_cast<int64_t>(D) * B;  // elements per (block, KV head)
 
-  extern __shared__ float lds[];  // [kWaves][g][D] values, then [kWaves][16] m, [kWaves][16] z
+  // [kWaves][16] m, [kWaves][16] z, then one region per wave of max(g D, 16 D) floats: the wave's staged value
+  // rows ([32][D] bf16) while it computes tiles, its summary values ([g][D] fp32) once it is done
+  extern __shared__ float lds[];
+  const int wreg = (g > 16 ? g : 16) * D;  // floats per wave region
 
   const int part_id = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -166,6 +172,10 @@ __global__ __launch_bounds__(256) void decode_mfma(
   float z_run = 0.f;
 
   const int tiles = min(part, S - tok0 + kTile - 1) / kTile;  // tiles holding >= 1 valid token
+  constexpr int RB = D * 2;                // bytes of one value row
+  constexpr int RPP = 1024 / RB;           // rows per 1 KiB of the staging buffer
+  unsigned char* vst = reinterpret_cast<unsigned char*>(lds + 2 * kWaves * 16 + wave * wreg);
+  const int vj = r >> 2, vq = r & 3;       // the value row / d quarter this lane points at in a transposing read
   const uint16_t* kh = k_pool + static_cast<int64_t>(kvh) * BLK;
   const uint16_t* vh = v_pool + static_cast<int64_t>(kvh) * BLK;
   const int64_t blk_stride = static_cast<int64_t>(hkv) * BLK;
@@ -178,32 +188,53 @@ __global__ __launch_bounds__(256) void decode_mfma(
     bf16x8 vop[VT];
     uint2 vlo[VT], vhi[VT];
     bool blk_ok[2];  // the block of the lane's 4-token group of slab a lies in the pool
+    // value rows t0 .. t0 + 31 into this wave's LDS buffer (zeros where the
+    // token is past the end or its block outside the pool)
+#pragma unroll
+    for (int p = 0; p < kTile * RB / 1024; ++p) {
+      const int row = p * RPP + lane * 16 / RB;
+      const int slot = (lane * 16 % RB) / 16;
+      const int tv = t0 + row;
+      const int pbv = __shfl(tbl, (tv / B) - lb0);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (tv < S && pbv >= 0 && pbv < num_blocks)
+        v = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(pbv) * blk_stride + (tv % B) * D +
+                                            ((slot ^ stage_swz<D, false>(row)) << 3));
+      *reinterpret_cast<uint4*>(vst + p * 1024 + lane * 16) = v;
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       // key row r of slab a
       const int tk = t0 + 16 * a + r;
       const int pbk = __shfl(tbl, (tk / B) - lb0);
       const bool kval = tk < S && pbk >= 0 && pbk < num_blocks;
-      const uint16_t* kb = kh + static_cast<int64_t>(pbk) * blk_stride + (tk % B) * X;
+      const uint16_t* kb = kh + static_cast<int64_t>(pbk) * blk_stride + (tk % B) * D;
 #pragma unroll
       for (int jj = 0; jj < KCH; ++jj) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (kval) v = *reinterpret_cast<const uint4*>(kb + (4 * jj + gq) * (B * X));
+        if (kval) v = *reinterpret_cast<const uint4*>(kb + (4 * jj + gq) * X);
         kop[a][jj] = __builtin_bit_cast(bf16x8, v);
       }
-      // value rows: tokens 4 gq .. 4 gq + 3 of slab a
       const int tv = t0 + 16 * a + 4 * gq;
-      const int pbv = __shfl(tbl, (tv / B) - lb0);
-      blk_ok[a] = pbv >= 0 && pbv < num_blocks;
-      const bool vval = tv < S && blk_ok[a];
-      const uint16_t* vb = vh + static_cast<int64_t>(pbv) * blk_stride + (tv % B);
+      blk_ok[a] = [&] {
+        const int pbv = __shfl(tbl, (tv / B) - lb0);
+        return pbv >= 0 && pbv < num_blocks;
+      }();
+    }
+    // the wave's own LDS writes above are done before its reads below (LDS
+    // instructions of one wave execute in order; the compiler keeps the order)
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int row = 16 * a + 4 * gq + vj;
+      const int sv = stage_swz<D, false>(row);
 #pragma unroll
       for (int mm = 0; mm < VT; ++mm) {
-        uint2 v = make_uint2(0, 0);
-        if (vval) v = *reinterpret_cast<const uint2*>(vb + (16 * mm + r) * B);
+        const uint2 v = lds_read_tr16(vst + row * RB + (((2 * mm + (vq >> 1)) ^ sv) << 4) + (vq & 1) * 8);
         if (a == 0) vlo[mm] = v; else vhi[mm] = v;
       }
     }
+    __asm__ volatile("" ::: "memory");
     // zero the value elements of tokens past the end (a stale or NaN slot
     // must not reach P.V: 0 * NaN is NaN)
     {
@@ -274,13 +305,15 @@ __global__ __launch_bounds__(256) void decode_mfma(
   // ---- merge the 4 waves through LDS -----------------------------------------
   z_run += __shfl_xor(z_run, 16);
   z_run += __shfl_xor(z_run, 32);
-  float* lds_u = lds;                         // [kWaves][g][D]
-  float* lds_m = lds + kWaves * g * D;        // [kWaves][16]
+  // the wave's region now holds its summary values (its own tiles are done: no other wave reads it before the barrier)
+  __asm__ volatile("" ::: "memory");
+  float* lds_m = lds;                         // [kWaves][16]
   float* lds_z = lds_m + kWaves * 16;         // [kWaves][16]
+  float* lds_u = lds_z + kWaves * 16;         // [kWaves][wreg]: [g][D] used
   if (r < g) {
 #pragma unroll
     for (int mm = 0; mm < VT; ++mm)
-      *reinterpret_cast<f32x4*>(lds_u + (wave * g + r) * D + 16 * mm + 4 * gq) = acc[mm];
+      *reinterpret_cast<f32x4*>(lds_u + wave * wreg + r * D + 16 * mm + 4 * gq) = acc[mm];
     if (gq == 0) {
       lds_m[wave * 16 + r] = m_run;
       lds_z[wave * 16 + r] = z_run;
@@ -300,7 +333,7 @@ __global__ __launch_bounds__(256) void decode_mfma(
     for (int w = 0; w < kWaves; ++w) {
       const float f = __builtin_amdgcn_exp2f(lds_m[w * 16 + h] - mx);  // 0 for idle waves (maximum: the most negative float)
       zz += f * lds_z[w * 16 + h];
-      uu += f * lds_u[(w * g + h) * D + dd];
+      uu += f * lds_u[w * wreg + h * D + dd];
     }
     if (n_parts == 1) {
       out[(head0 + h) * D + dd] = f32_to_bf16_bits(zz > 0.f ? uu / zz : 0.f);  // no token at all: zeros
@@ -325,7 +358,6 @@ __global__ __launch_bounds__(64) void decode_generic(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, T* __restrict__ out,
     float* __restrict__ ws, int hq, int hkv, int block_size, int max_blocks, int num_blocks, int part, int p_max,
     float scale_log2) {
-  constexpr int X = 16 / static_cast<int>(sizeof(T));
   constexpr int E = D / 64;  // elements per lane
   const int part_id = blockIdx.x;
   const int h = blockIdx.y;
@@ -362,8 +394,8 @@ __global__ __launch_bounds__(64) void decode_generic(
     float vv[E];
     for (int e = 0; e < E; ++e) {
       const int d = lane + 64 * e;
-      const float kx = ok ? Elem<T>::load(kb + ((d / X) * block_size + off) * X + d % X) : 0.f;
-      vv[e] = ok ? Elem<T>::load(vb + d * block_size + off) : 0.f;
+      const float kx = ok ? Elem<T>::load(kb + off * D + d) : 0.f;
+      vv[e] = ok ? Elem<T>::load(vb + off * D + d) : 0.f;
       dot += qv[e] * kx;
     }
 #pragma unroll
@@ -567,7 +599,7 @@ int decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool
 
   if (pl.mfma) {
     const dim3 grid(pl.p_max, Hkv, num_seqs);
-    const size_t lds = (static_cast<size_t>(kWaves) * g * d_head + 2 * kWaves * 16) * sizeof(float);
+    const size_t lds = (2 * kWaves * 16 + static_cast<size_t>(kWaves) * (g > 16 ? g : 16) * d_head) * sizeof(float);
     if (d_head == 128)
       launch_mfma_b<128>(block_size, pl, grid, lds, s, q, k_pool, v_pool, block_tables, context_lens, out, ws, Hq,
                          Hkv, g, max_blocks_per_seq, num_blocks, scale_log2);

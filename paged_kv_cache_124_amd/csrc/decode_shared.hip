@@ -542,6 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int first = us.is_group(cur.n) ? us.s_gfirst[cur.n - n_seqs] : cur.n;
     const QRows q_next = q_rows<D>(nxt, us, q, hq, col_m, col_h, r, gq);
     Buf<D> b;
+    wait_stage_copies();
     read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
     // keep the stage's LDS reads ahead of the copies below
     __builtin_amdgcn_sched_barrier(0);

@@ -26,7 +26,8 @@
 // Per tile the matrix-core roles of decode_tile.h, with the G query heads of
 // the KV head as the 16 columns (head r, padding for r >= G).
 //
-// Pool layout (per layer): K [num_blocks][Hkv][D/8][B][8], V [num_blocks][Hkv][D][B].
+// Pool layout (per layer): K and V [num_blocks][Hkv][B][D] (rows of D bf16
+// values or D one-byte codes).
 
 
 #pragma once
@@ -58,7 +59,7 @@ constexpr int kMaxSeqs = 3072;  // lengths and tile prefix sums live in LDS besi
 template <int D>
 struct Buf8 {
   uint4 k[2][2][D / 64];     // [sub-tile][slab] key row 16 slab + r: the 16-byte chunks of d quarter gq
-  uint32_t v[2][2][D / 16];  // [sub-tile][slab][mm] value row 16 mm + r, tokens 4 gq .. 4 gq + 3 of the slab
+  uint32_t v[2][2][D / 16];  // [sub-tile][slab][mm] tokens 4 gq .. 4 gq + 3 of the slab at d = 16 mm + r
   bool ok[2][2];             // the block of that value group is in the pool
 };
 
@@ -129,26 +130,38 @@ __device__ __forceinline__ Sc8 load_scales(const Tb<64 / B>& tb, const float* __
   return sc;
 }
 
+// Operands of a staged tile of codes (rows of D bytes, chunks swizzled as in
+// dma_tile).  Key: row 32 u + 16 a + r, the chunks of d quarter gq.  Value:
+// one transposing read per (sub-tile u, d block mm) gives the lane the codes
+// of tokens 4 gq .. + 3 of both slabs at d = 16 mm + r: in-lane i = 2 j + h of
+// the 16-lane group points at d = 16 mm + 8 h .. + 7 of token 4 gq + j (j < 4,
+// slab 0) or 16 + 4 gq + j - 4 (slab 1).
 template <int D, int B>
 __device__ __forceinline__ void read_tile8(Buf8<D>& b, const unsigned char* stage, const Tb<64 / B>& tb, int num_blocks,
                                            int r, int gq) {
-  constexpr int IMG = D * B;
+  constexpr int RB = D;
+  const int vj = r >> 1, vh = r & 1;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < 2; ++u) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int tk = 32 * u + 16 * a + r;  // key row
-      const unsigned char* kimg = stage + (tk / B) * IMG + (tk % B) * 16;
+      const int sk = stage_swz<D, true>(tk);
 #pragma unroll
       for (int w = 0; w < D / 64; ++w)
-        b.k[u][a][w] = *reinterpret_cast<const uint4*>(kimg + (gq * (D / 64) + w) * B * 16);
-      const int tv = 32 * u + 16 * a + 4 * gq;  // first token of the value group
-      const unsigned char* vimg = stage + kStageHalf<D> + (tv / B) * IMG + tv % B;
-#pragma unroll
-      for (int mm = 0; mm < D / 16; ++mm) b.v[u][a][mm] = *reinterpret_cast<const uint32_t*>(vimg + (16 * mm + r) * B);
+        b.k[u][a][w] = *reinterpret_cast<const uint4*>(stage + tk * RB + (((gq * (D / 64) + w) ^ sk) << 4));
       const int e = group_block<B>(tb, 32 * u + 16 * a, gq);
       b.ok[u][a] = e >= 0 && e < num_blocks;
     }
+    const int tv = 32 * u + (vj < 4 ? 4 * gq + vj : 16 + 4 * gq + vj - 4);  // the value row this lane points at
+    const int sv = stage_swz<D, true>(tv);
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm) {
+      const uint2 v = lds_read_tr8(stage + kStageHalf<D> + tv * RB + ((mm ^ sv) << 4) + vh * 8);
+      b.v[u][0][mm] = v.x;
+      b.v[u][1][mm] = v.y;
+    }
+  }
 }
 
 template <int D, bool I8>
@@ -387,6 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int t0 = cur.ti * TOK;
     if constexpr (F8) {
       Buf8<D> b;
+      wait_stage_copies();
       read_tile8<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
       __builtin_amdgcn_sched_barrier(0);
       // a step over codes: the row's slot, read where the row's head-0 segment
@@ -410,6 +424,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       if (row_end && lane == 0) slots_out[cur.n] = row_slot;
     } else {
       Buf<D> b;
+      wait_stage_copies();
       read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
       // keep the stage's LDS reads ahead of the copies below: an LDS read issued
       // after them would wait for all of them
@@ -583,9 +598,9 @@ __global__ __launch_bounds__(256) void merge_step8(const float* __restrict__ rec
   const int64_t hd = pb * hkv + j;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int d = lane + 64 * e;
-    a.k_pool[((hd * (D / 16) + d / 16) * B + off) * 16 + d % 16] = static_cast<uint8_t>(kc[e]);
-    a.v_pool[(hd * D + d) * B + off] = static_cast<uint8_t>(vc[e]);
+    const int64_t at = (hd * B + off) * D + lane + 64 * e;
+    a.k_pool[at] = static_cast<uint8_t>(kc[e]);
+    a.v_pool[at] = static_cast<uint8_t>(vc[e]);
   }
   if (j == 0 && lane == 0) {  // the only thread that reads or writes the row
     const int pos = a.context_lens[n];

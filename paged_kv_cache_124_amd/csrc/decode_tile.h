@@ -12,12 +12,16 @@
 //
 // Per tile (lane = 16 gq + r):
 //   q.K^T  A = 16 key rows x 32 d (lane: row r, chunk 4 jj + gq, one 16-byte
-//          load), B = Q^T (column r) -> S^T[4 gq + i][r]
-//   P.V    A = V^T rows d = 16 mm + r, 8 tokens (4 of each 16-token slab,
-//          two 8-byte loads), B = P^T: the lane's own 8 probabilities, split
-//          into bf16 high and residual parts -> O^T[16 mm + 4 gq + i][r].
+//          LDS read), B = Q^T (column r) -> S^T[4 gq + i][r]
+//   P.V    A = V^T rows d = 16 mm + r, 8 tokens (4 of each 16-token slab:
+//          one transposing 8-byte LDS read per slab), B = P^T: the lane's own
+//          8 probabilities, split into bf16 high and residual parts
+//          -> O^T[16 mm + 4 gq + i][r].
 //
-// Pool layout (per layer): K [num_blocks][Hkv][D/8][B][8], V [num_blocks][Hkv][D][B].
+// Pool layout (per layer): K and V [num_blocks][Hkv][B][D] -- a token's row of
+// one KV head is D contiguous elements.  A tile is staged in LDS with the same
+// rows; the 16-byte chunks of each row are permuted (stage_swz) so that the
+// MFMA operand reads hit distinct LDS banks.
 #pragma once
 
 #include <type_traits>
@@ -169,80 +173,130 @@ constexpr int kStageBytes = 2 * 32 * 128 * 2;
 __shared__ __attribute__((aligned(16))) unsigned char g_stage0[4][kStageBytes];
 __shared__ __attribute__((aligned(16))) unsigned char g_stage1[4][kStageBytes];
 
-// Bytes of one tile's keys (and, again, of its values) in LDS: the images of
-// the blocks that hold its tokens -- 32 / B bf16 images of B * D * 2 bytes, or
-// 64 / B FP8 images of B * D bytes.
+// Bytes of one tile's keys (and, again, of its values) in LDS: its rows of
+// D bf16 (32 tokens) or D one-byte codes (64 tokens).
 template <int D>
 constexpr int kStageHalf = 64 * D;
 
-// Copy one tile's key and value block images into an LDS stage with
-// global_load_lds (16 bytes per lane, 1 KiB per instruction, straight to LDS:
-// no registers held while in flight).  A missing block (past the end, or an
-// id outside the pool) is read from block 0 -- a valid address -- and its
-// tokens are masked out in pv_tile.
-// The tile's images lie back to back in the stage; 1 KiB piece p of them is
-// one instruction, lane l bringing bytes p * 1024 + 16 l .. + 15.  An image
-// smaller than 1 KiB (FP8, D = 64, B = 8: 512 bytes) shares a piece with the
-// next block's image, so the lanes of one instruction read two blocks.
+// LDS slot of 16-byte chunk c of staged tile row t: c ^ stage_swz<D, F8>(t).
+// Each bit of the swizzle is the parity of a few bits of t, chosen (every
+// operand read below checked lane by lane against 32- and 64-bank LDS) so that the 16 key rows of an MFMA operand, and the 4 or 8 value rows of a
+// transposing read, never share a bank.
+__device__ __forceinline__ int parity(int x) { return __builtin_popcount(x) & 1; }
+
+template <int D, bool F8>
+__device__ __forceinline__ int stage_swz(int t) {
+  if constexpr (!F8 && D == 128)  // 16 chunks per row
+    return parity(t & 0x4) | parity(t & 0x6) << 1 | parity(t & 0x1) << 2 | parity(t & 0xa) << 3;
+  else if constexpr (!F8)  // D = 64: 8 chunks per row
+    return parity(t & 0x4) | parity(t & 0xd) << 1 | parity(t & 0x2) << 2;
+  else if constexpr (D == 128)  // codes, 8 chunks per row
+    return parity(t & 0x19) | parity(t & 0x5) << 1 | parity(t & 0x2) << 2;
+  else  // codes, D = 64: 4 chunks per row
+    return parity(t & 0xe) | parity(t & 0x14) << 1;
+}
+
+// Copy one tile's key and value rows into an LDS stage with global_load_lds
+// (16 bytes per lane, 1 KiB per instruction, straight to LDS: no registers
+// held while in flight).  A missing block (past the end, or an id outside the
+// pool) is read from block 0 -- a valid address -- and its tokens are masked
+// out in pv_tile.
+// Instruction p fills stage bytes p * 1024 .. + 1023, i.e. tile rows
+// p * RPP .. + RPP - 1; lane l writes 16 bytes at p * 1024 + 16 l: slot s of
+// row t, so it fetches chunk s ^ stage_swz(t) of that token's row.  Per
+// instruction the lanes read RPP whole rows.  Where a piece spans two blocks
+// (FP8, D = 64, B = 8: 16 rows of 64 bytes) the lane picks its block by a select.
 template <int D, int B, bool F8>
 __device__ __forceinline__ void dma_tile(unsigned char* stage_ptr, int j, const Tb<kTok<F8> / B>& tb,
                                          const void* __restrict__ k_pool, const void* __restrict__ v_pool, int hkv,
                                          int num_blocks, int lane) {
-  constexpr int NB = kTok<F8> / B;
-  constexpr int IMG = D * B * (F8 ? 1 : 2);  // bytes of one (block, KV head) image
-  constexpr int PIECES = NB * IMG / 1024;
+  constexpr int RB = D * (F8 ? 1 : 2);  // bytes of one token row
+  constexpr int IMG = B * RB;           // bytes of one (block, KV head) image
+  constexpr int RPP = 1024 / RB;        // rows per 1 KiB piece
+  constexpr int PIECES = kTok<F8> * RB / 1024;
   lds_byte* stage = (lds_byte*)stage_ptr;  // LDS address for the copy engine
   const int64_t blk_stride = static_cast<int64_t>(hkv) * IMG;
   const char* kb = reinterpret_cast<const char*>(k_pool) + static_cast<int64_t>(j) * IMG;
   const char* vb = reinterpret_cast<const char*>(v_pool) + static_cast<int64_t>(j) * IMG;
+  const int lrow = lane * 16 / RB;       // the lane's row within a piece
+  const int slot = (lane * 16 % RB) / 16;
 #pragma unroll
   for (int p = 0; p < PIECES; ++p) {
-    int e, off;
-    if constexpr (IMG >= 1024) {
-      e = tb.blk[p * 1024 / IMG];
-      off = p * 1024 % IMG + lane * 16;
-    } else {
-      constexpr int PER = 1024 / IMG;  // images per piece
-      const int bi = p * PER + lane * 16 / IMG;
-      e = tb.blk[p * PER];  // tb.blk[bi] by selects: a lane-dependent index would put tb in scratch
-#pragma unroll
-      for (int i = 1; i < PER; ++i)
-        if (bi == p * PER + i) e = tb.blk[p * PER + i];
-      off = lane * 16 % IMG;
+    const int t = p * RPP + lrow;  // tile row
+    int e;
+    if constexpr (RPP <= B) {
+      e = tb.blk[p * RPP / B];
+    } else {  // two blocks per piece: tb.blk[t / B] by a select (an indexed read would put tb in scratch)
+      e = lrow >= B ? tb.blk[p * RPP / B + 1] : tb.blk[p * RPP / B];
     }
     const int64_t pb = (e >= 0 && e < num_blocks) ? e : 0;
-    __builtin_amdgcn_global_load_lds(kb + pb * blk_stride + off, stage + p * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb + pb * blk_stride + off, stage + kStageHalf<D> + p * 1024, 16, 0, 0);
+    const int64_t off = pb * blk_stride + (t % B) * RB + ((slot ^ stage_swz<D, F8>(t)) << 4);
+    __builtin_amdgcn_global_load_lds(kb + off, stage + p * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + off, stage + kStageHalf<D> + p * 1024, 16, 0, 0);
   }
 }
 
-// Read a staged tile's MFMA operands from LDS into registers (the same lane
-// roles as direct loads would give) and mark which value groups exist.
+// Wait until every vector memory operation of the wave has completed -- in
+// particular the LDS copies of the stage about to be read.  The stage reads
+// must not rely on the compiler's own wait: its alias analysis has let some
+// reads of a stage run ahead of that stage's copies.  When a step starts,
+// everything outstanding was issued before the current stage's copies (table
+// entries, scales, Q and new-token loads of the next tile), so this waits for
+// nothing that the copies did not already hold back.
+__device__ __forceinline__ void wait_stage_copies() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+
+// Transposing LDS reads of gfx950 (ds_read_b64_tr_b16 / _b8).  Within each
+// group of 16 lanes, lane i receives element j from the 8 bytes that lane
+// 4 j + i / 4 (16-bit elements) or lane 2 j + i / 8 (bytes) points at,
+// element i % 4 (i % 8) of them.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_byte*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+__device__ __forceinline__ uint2 lds_read_tr8(const unsigned char* p) {
+  const v2i32 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(lds_byte*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Read a staged tile's MFMA operands from LDS into registers and mark which
+// value groups exist.
+//   key operand (slab a, step jj): row 16 a + r, chunk 4 jj + gq.
+//   value operand (slab a, d block mm): tokens 16 a + 4 gq .. + 3 of d = 16 mm + r,
+//     one transposing read: in-lane i = 4 j + q of the 16-lane group points at
+//     d = 16 mm + 4 q .. + 3 of token 16 a + 4 gq + j.
 template <int D, int B>
 __device__ __forceinline__ void read_tile(Buf<D>& b, const unsigned char* stage, const Tb<32 / B>& tb, int num_blocks,
                                           int r, int gq) {
-  constexpr int IMG = D * B * 2;
+  constexpr int RB = D * 2;
+  const int vj = r >> 2, vq = r & 3;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int tk = 16 * a + r;  // key row of slab a
-    const unsigned char* kimg = stage + (tk / B) * IMG + (tk % B) * 16;
+    const int sk = stage_swz<D, false>(tk);
 #pragma unroll
     for (int jj = 0; jj < D / 32; ++jj)
-      b.k[a][jj] = *reinterpret_cast<const bf16x8*>(kimg + (4 * jj + gq) * B * 16);
-    const int tv = 16 * a + 4 * gq;  // first token of the value group
-    const unsigned char* vimg = stage + kStageHalf<D> + (tv / B) * IMG + (tv % B) * 2;
+      b.k[a][jj] = *reinterpret_cast<const bf16x8*>(stage + tk * RB + (((4 * jj + gq) ^ sk) << 4));
+    const int tv = 16 * a + 4 * gq + vj;  // the value row this lane points at
+    const int sv = stage_swz<D, false>(tv);
 #pragma unroll
     for (int mm = 0; mm < D / 16; ++mm) {
-      const uint2 v = *reinterpret_cast<const uint2*>(vimg + (16 * mm + r) * B * 2);
+      const int c = 2 * mm + (vq >> 1);
+      const uint2 v = lds_read_tr16(stage + kStageHalf<D> + tv * RB + ((c ^ sv) << 4) + (vq & 1) * 8);
       if (a == 0)
         b.v0[mm] = v;
       else
         b.v1[mm] = v;
     }
-    int pv = tb.blk[0];  // tb.blk[tv / B] by selects: a lane-dependent index would put tb in scratch
+    const int tg = 16 * a + 4 * gq;  // first token of the lane's value group
+    int pv = tb.blk[0];  // tb.blk[tg / B] by selects: a lane-dependent index would put tb in scratch
 #pragma unroll
     for (int i = 1; i < 32 / B; ++i)
-      if (tv / B == i) pv = tb.blk[i];
+      if (tg / B == i) pv = tb.blk[i];
     const bool ok = pv >= 0 && pv < num_blocks;
     if (a == 0)
       b.blk0 = ok;
@@ -385,14 +439,13 @@ struct AppendArgs {
   int max_blocks, block_size;
 };
 
-// The new token of (row n, KV head j) as thread t of the workgroup holds it:
-// key chunk t (t < D / 8) and value row d = t (t < D).  Loaded when the merge
-// kernel starts, stored when it ends.
+// The new token of (row n, KV head j) as thread t < D / 8 of the workgroup
+// holds it: 16-byte chunk t of its key row and of its value row.  Loaded when
+// the merge kernel starts, stored when it ends.
 template <int D>
 struct RowToken {
   int64_t slot;
-  uint4 k;
-  uint16_t v;
+  uint4 k, v;
 };
 
 template <int D>
@@ -402,7 +455,7 @@ __device__ __forceinline__ RowToken<D> load_row_token(const AppendArgs& ap, int 
   const int t = threadIdx.x;
   rt.slot = ap.slots[n];
   rt.k = t < D / 8 ? *reinterpret_cast<const uint4*>(ap.k_new + src + t * 8) : make_uint4(0, 0, 0, 0);
-  rt.v = t < D ? ap.v_new[src + t] : 0;
+  rt.v = t < D / 8 ? *reinterpret_cast<const uint4*>(ap.v_new + src + t * 8) : make_uint4(0, 0, 0, 0);
   return rt;
 }
 
@@ -412,10 +465,12 @@ __device__ __forceinline__ void append_row(const AppendArgs& ap, const RowToken<
   const int B = ap.block_size;
   const int64_t pb = rt.slot / B;
   const int off = static_cast<int>(rt.slot % B);
-  const int64_t head = pb * hkv + j;
+  const int64_t row = ((pb * hkv + j) * B + off) * D;
   const int t = threadIdx.x;
-  if (t < D / 8) *reinterpret_cast<uint4*>(ap.k_pool + ((head * (D / 8) + t) * B + off) * 8) = rt.k;
-  if (t < D) ap.v_pool[(head * D + t) * B + off] = rt.v;
+  if (t < D / 8) {
+    *reinterpret_cast<uint4*>(ap.k_pool + row + t * 8) = rt.k;
+    *reinterpret_cast<uint4*>(ap.v_pool + row + t * 8) = rt.v;
+  }
   if (j == 0 && t == 0) {  // the only thread that reads or writes the row
     const int pos = ap.context_lens[n];
     ap.block_tables[static_cast<int64_t>(n) * ap.max_blocks + pos / B] = static_cast<int32_t>(pb);

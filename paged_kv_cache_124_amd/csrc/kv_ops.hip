@@ -7,8 +7,8 @@
 // Copy: same page, sections 15-16 -- a shared tail block is cloned before a
 // sequence writes into it.  Both are pure data movement and bit-exact.
 //
-// Pool layout (per layer), x = 16 / sizeof(elem):
-//   K [num_blocks][Hkv][D/x][B][x],  V [num_blocks][Hkv][D][B].
+// Pool layout (per layer): K and V [num_blocks][Hkv][B][D] -- each token's
+// key (and value) row of one KV head is D contiguous elements.
 
 #include "codes.h"
 #include "common.h"
@@ -16,9 +16,8 @@
 namespace pa {
 namespace {
 
-// One thread per (token, KV head, 16-byte key chunk).  The key chunk is one
-// 16-byte store; the matching x value elements go to x different rows of the
-// value block (stride B elements).
+// One thread per (token, KV head, 16-byte chunk of the row): one 16-byte
+// store into the key row and one into the value row of the token's slot.
 template <typename T>
 __global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ k_pool, T* __restrict__ v_pool,
                                                         const T* __restrict__ k_new,
@@ -40,17 +39,9 @@ __global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ k_pool, 
   const int off = static_cast<int>(slot % block_size);
 
   const int64_t src = (t * hkv + j) * d + static_cast<int64_t>(c) * X;
-  const int64_t head = pb * hkv + j;  // (block, KV head) index
-  // key: one 16-byte chunk
-  const uint4 kc = *reinterpret_cast<const uint4*>(k_new + src);
-  *reinterpret_cast<uint4*>(k_pool + ((head * chunks + c) * block_size + off) * X) = kc;
-  // value: X elements, one per row d of the transposed block
-  const uint4 vc = *reinterpret_cast<const uint4*>(v_new + src);
-  T vals[X];
-  __builtin_memcpy(vals, &vc, 16);
-  T* vdst = v_pool + (head * d + static_cast<int64_t>(c) * X) * block_size + off;
-#pragma unroll
-  for (int e = 0; e < X; ++e) vdst[static_cast<int64_t>(e) * block_size] = vals[e];
+  const int64_t dst = ((pb * hkv + j) * block_size + off) * d + static_cast<int64_t>(c) * X;
+  *reinterpret_cast<uint4*>(k_pool + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+  *reinterpret_cast<uint4*>(v_pool + dst) = *reinterpret_cast<const uint4*>(v_new + src);
 }
 
 // One decode step's append for a batch whose block tables and lengths stay
@@ -91,21 +82,15 @@ __global__ __launch_bounds__(256) void append_step_kernel(T* __restrict__ k_pool
     }
   }
   const int64_t src = (n * hkv + j) * d + static_cast<int64_t>(c) * X;
-  const int64_t head = pb * hkv + j;
-  const uint4 kc = *reinterpret_cast<const uint4*>(k_new + src);
-  *reinterpret_cast<uint4*>(k_pool + ((head * chunks + c) * block_size + off) * X) = kc;
-  const uint4 vc = *reinterpret_cast<const uint4*>(v_new + src);
-  T vals[X];
-  __builtin_memcpy(vals, &vc, 16);
-  T* vdst = v_pool + (head * d + static_cast<int64_t>(c) * X) * block_size + off;
-#pragma unroll
-  for (int e = 0; e < X; ++e) vdst[static_cast<int64_t>(e) * block_size] = vals[e];
+  const int64_t dst = ((pb * hkv + j) * block_size + off) * d + static_cast<int64_t>(c) * X;
+  *reinterpret_cast<uint4*>(k_pool + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+  *reinterpret_cast<uint4*>(v_pool + dst) = *reinterpret_cast<const uint4*>(v_new + src);
 }
 
 // One thread per (token, KV head, 4 consecutive elements): a 4-byte store of
-// four key codes (inside one 16-code chunk) and four one-byte value stores
-// (stride B).  Four elements per thread keep enough waves in flight to hide
-// the fp64 division of each element.  With block_tables non-null (a decode
+// four key codes and one of four value codes into the slot's rows.  Four
+// elements per thread keep enough waves in flight to hide the fp64 division
+// of each element.  With block_tables non-null (a decode
 // step, token n = row n) the thread of (n, head 0, elements 0..3) also moves
 // the row forward, as append_step_kernel does.
 template <bool I8>
@@ -144,14 +129,15 @@ __global__ __launch_bounds__(256) void append_codes_kernel(uint8_t* __restrict__
   const uint2 vin = *reinterpret_cast<const uint2*>(v_new + src);
   const uint32_t kb[4] = {kin.x & 0xffffu, kin.x >> 16, kin.y & 0xffffu, kin.y >> 16};
   const uint32_t vb[4] = {vin.x & 0xffffu, vin.x >> 16, vin.y & 0xffffu, vin.y >> 16};
-  uint32_t kw = 0;
+  uint32_t kw = 0, vw = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) kw |= code8<I8>(bf16_bits_to_f32(kb[e]), ks) << (8 * e);
-  *reinterpret_cast<uint32_t*>(k_pool + ((head * (d / 16) + e0 / 16) * block_size + off) * 16 + e0 % 16) = kw;
-  uint8_t* vdst = v_pool + (head * d + e0) * block_size + off;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    vdst[static_cast<int64_t>(e) * block_size] = static_cast<uint8_t>(code8<I8>(bf16_bits_to_f32(vb[e]), vs));
+  for (int e = 0; e < 4; ++e) {
+    kw |= code8<I8>(bf16_bits_to_f32(kb[e]), ks) << (8 * e);
+    vw |= code8<I8>(bf16_bits_to_f32(vb[e]), vs) << (8 * e);
+  }
+  const int64_t dst = (head * block_size + off) * d + e0;
+  *reinterpret_cast<uint32_t*>(k_pool + dst) = kw;
+  *reinterpret_cast<uint32_t*>(v_pool + dst) = vw;
 }
 
 // grid = (ceil((2 * n16 + 2 * scales_per_block) / 256), num_pairs, num_layers);

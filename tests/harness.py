@@ -22,7 +22,6 @@ from oracle import attention as OA
 from oracle import fp8 as OF
 from oracle import int8 as OI
 from oracle.block_manager import BlockManagerModel
-from pool_layout import k_to_logical, poison_unused_
 
 # Acceptance bar for attention against the fp64 oracle (bf16 inputs, fp32 accumulation).
 MAX_ABS = 1e-2
@@ -43,7 +42,7 @@ class DecodeCase:
     bm: object                  # product block manager
     model: BlockManagerModel    # oracle block manager
     tables: np.ndarray          # int32 [N][max_blocks] from the product manager
-    k: torch.Tensor             # device, [L][nb][Hkv][D/x][B][x] or [nb]...
+    k: torch.Tensor             # device, [L][nb][Hkv][B][D] or [nb][Hkv][B][D]
     v: torch.Tensor
     q: torch.Tensor             # device [N][Hq][D]
     tables_dev: torch.Tensor
@@ -61,6 +60,28 @@ class DecodeCase:
     @property
     def max_ctx(self):
         return max(self.lens) if self.lens else 0
+
+
+def poison_unused_(k, v, tables, lens, block_size, value=float("nan")):
+    """Fill every block no sequence uses, and every slot past a sequence's end, with `value` (pools [nb][Hkv][B][D]).
+
+    The oracle never reads those slots, so the device output must not depend on them.
+    """
+    used = torch.zeros(k.shape[0], dtype=torch.bool)
+    for row, s in zip(tables, lens):
+        nb = -(-int(s) // block_size)
+        used[torch.as_tensor(row[:nb], dtype=torch.long)] = True
+    unused = (~used).nonzero().flatten().to(k.device)
+    if unused.numel():
+        k.index_fill_(0, unused, value)
+        v.index_fill_(0, unused, value)
+    for row, s in zip(tables, lens):
+        s = int(s)
+        off = s % block_size
+        if s > 0 and off:
+            pb = int(row[(s - 1) // block_size])
+            k[pb, :, off:, :] = value
+            v[pb, :, off:, :] = value
 
 
 def make_case(w: synth.Workload, lens: Optional[Sequence[int]] = None, *, hq=None, hkv=None, d=None,
@@ -154,9 +175,7 @@ def run_decode(case: DecodeCase, layer: Optional[int] = None, q=None, out=None, 
 def logical_blocks(pool: torch.Tensor, blocks: Sequence[int], is_key: bool) -> np.ndarray:
     """Read some physical blocks back and return them in the oracle's logical layout, fp32 (exact for bf16)."""
     idx = torch.as_tensor(list(blocks), dtype=torch.long, device=pool.device)
-    sel = pool.index_select(0, idx).cpu()
-    sel = k_to_logical(sel) if is_key else sel.permute(0, 1, 3, 2)
-    return sel.float().numpy()
+    return pool.index_select(0, idx).cpu().float().numpy()
 
 
 def oracle_outputs(case: DecodeCase, seqs: Sequence[int], layer: Optional[int] = None, q=None, lens=None,
@@ -190,8 +209,8 @@ def oracle_outputs(case: DecodeCase, seqs: Sequence[int], layer: Optional[int] =
 def fp8_logical(case: DecodeCase, blocks: Sequence[int]):
     """Codes (uint8, logical [n][Hkv][B][D]) and scales (float64 [n][Hkv]) of some physical blocks of an FP8 case."""
     idx = torch.as_tensor(list(blocks), dtype=torch.long, device=case.k.device)
-    kc = k_to_logical(case.k.index_select(0, idx).cpu()).numpy()
-    vc = case.v.index_select(0, idx).cpu().permute(0, 1, 3, 2).numpy()
+    kc = case.k.index_select(0, idx).cpu().numpy()
+    vc = case.v.index_select(0, idx).cpu().numpy()
     ks = case.k_scale.index_select(0, idx).cpu().double().numpy()
     vs = case.v_scale.index_select(0, idx).cpu().double().numpy()
     return kc, vc, ks, vs

@@ -20,14 +20,14 @@ import synth
 from harness import DecodeCase, assert_close, make_case, oracle_outputs, run_decode
 from oracle import attention as OA
 from oracle.block_manager import BlockManagerModel
-from pool_layout import k_to_logical, poison_unused_, v_to_logical
+from harness import poison_unused_
 
 pytestmark = pytest.mark.gpu
 
 
 def _bits(k, v):
-    kl = k_to_logical(k.cpu()).contiguous().view(torch.int16).numpy().copy()
-    vl = v_to_logical(v.cpu()).contiguous().view(torch.int16).numpy().copy()
+    kl = k.cpu().contiguous().view(torch.int16).numpy().copy()
+    vl = v.cpu().contiguous().view(torch.int16).numpy().copy()
     return kl, vl
 
 

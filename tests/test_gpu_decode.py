@@ -19,7 +19,6 @@ def test_tiny_decode_append_decode():
     slots, decoded through the oracle manager's tables.
     """
     import paged_kv_cache_124_amd as pa
-    from pool_layout import k_to_logical, v_to_logical
     w = synth.tiny()
     print("[case] tiny", flush=True)
     c = make_case(w)
@@ -27,8 +26,8 @@ def test_tiny_decode_append_decode():
     ref = oracle_outputs(c, range(4))
     assert_close(out, ref, "tiny step 1", max_abs=1e-4, rel_l2=1e-5)
 
-    k_or = k_to_logical(c.k.cpu()).double().numpy().copy()
-    v_or = v_to_logical(c.v.cpu()).double().numpy().copy()
+    k_or = c.k.cpu().double().numpy().copy()
+    v_or = c.v.cpu().double().numpy().copy()
     st, slots, pairs, _ = c.bm.append_slots(list(range(4)))
     mst, mslots, mpairs, _ = c.model.append_slots(list(range(4)))
     assert st == mst == 0 and list(slots) == mslots and len(pairs) == len(mpairs) == 0
@@ -37,8 +36,8 @@ def test_tiny_decode_append_decode():
     pa.pa_append_kv(c.k, c.v, kn, vn, torch.tensor(slots, dtype=torch.int32, device="cuda"))
     OA.append_kv(k_or, v_or, kn.cpu().double().numpy(), vn.cpu().double().numpy(), mslots)
     # device pool after the append equals the oracle's pool, NaN slots included
-    assert np.array_equal(k_to_logical(c.k.cpu()).double().numpy(), k_or, equal_nan=True)
-    assert np.array_equal(v_to_logical(c.v.cpu()).double().numpy(), v_or, equal_nan=True)
+    assert np.array_equal(c.k.cpu().double().numpy(), k_or, equal_nan=True)
+    assert np.array_equal(c.v.cpu().double().numpy(), v_or, equal_nan=True)
 
     lens2 = [s + 1 for s in c.lens]
     st, tables2, l2 = c.bm.build_batch(list(range(4)), c.max_blocks + 1)
@@ -200,15 +199,14 @@ def test_decode_leading_tile_outside_pool_is_left_out(dtype, hq, hkv):
     """Both blocks of a row's first 32 tokens outside [0, num_blocks): their tokens are left out of the softmax, with
     no NaN from a tile that holds no token before any other (persistent bf16 kernel; fp32 token-loop kernel; the
     partitioned MFMA kernel at 32 query heads per KV head)."""
-    from pool_layout import k_to_logical, v_to_logical
     print(f"[case] leading tile out of pool {dtype} hq={hq} hkv={hkv}", flush=True)
     c = make_case(synth.gqa8b(), [100, 70], hq=hq, hkv=hkv, dtype=dtype, seed=1760)
     tables = c.tables.copy()
     tables[0, 0] = c.num_blocks + 3
     tables[0, 1] = c.num_blocks + 9  # tokens 0..31 of row 0
     out = run_decode(c, tables_dev=torch.from_numpy(tables).cuda())
-    k_log = k_to_logical(c.k.cpu()).double().numpy()
-    v_log = v_to_logical(c.v.cpu()).double().numpy()
+    k_log = c.k.cpu().double().numpy()
+    v_log = c.v.cpu().double().numpy()
     bs = c.block_size
     keep = range(2 * bs, 100)
     K = np.stack([k_log[int(c.tables[0][t // bs]), :, t % bs] for t in keep])

@@ -15,7 +15,6 @@ import torch
 import synth
 from harness import assert_close, make_case, oracle_outputs
 from oracle import attention as OA
-from pool_layout import k_to_logical, v_to_logical
 
 pytestmark = pytest.mark.gpu
 
@@ -122,8 +121,8 @@ def test_decode_step_graph_runs_a_decode_loop():
         nb = -(-s_r // bs)
         assert tb[r, :nb].tolist() == tables[r, :nb].tolist()
     # the last step against the oracle over the final pool (it holds every appended token)
-    k_log = k_to_logical(kB.cpu()).double().numpy()
-    v_log = v_to_logical(vB.cpu()).double().numpy()
+    k_log = kB.cpu().double().numpy()
+    v_log = vB.cpu().double().numpy()
     ref = OA.paged_decode(qB.cpu().double().numpy(), k_log, v_log, tB.cpu().numpy(), lB.cpu().numpy().tolist(),
                           c.scale)
     assert_close(outB, ref, "graph step loop, last step")

@@ -6,7 +6,6 @@ import torch
 
 import synth
 from oracle import attention as OA
-from pool_layout import k_to_logical, v_to_logical
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +22,8 @@ def _pools(num_blocks, hkv, d, bs, dtype, seed, layers=1):
 
 def _logical_np(k, v):
     """Whole pool in the oracle's layout as raw bits (int16/int32 views) so comparisons are bit-exact."""
-    kl = k_to_logical(k.cpu()).contiguous()
-    vl = v_to_logical(v.cpu()).contiguous()
+    kl = k.cpu().contiguous()
+    vl = v.cpu().contiguous()
     view = torch.int16 if k.dtype == torch.bfloat16 else torch.int32
     return kl.view(view).numpy().copy(), vl.view(view).numpy().copy()
 

@@ -19,7 +19,7 @@ import synth
 from harness import DecodeCase, assert_close, oracle_outputs
 from oracle import attention as OA
 from oracle.block_manager import BlockManagerModel, shared_prefix_groups
-from pool_layout import k_to_logical, poison_unused_, v_to_logical
+from harness import poison_unused_
 
 pytestmark = pytest.mark.gpu
 
@@ -191,8 +191,8 @@ def test_member_with_no_tokens_of_its_own():
 
 
 def _bits(k, v):
-    kl = k_to_logical(k.cpu()).contiguous().view(torch.int16).numpy().copy()
-    vl = v_to_logical(v.cpu()).contiguous().view(torch.int16).numpy().copy()
+    kl = k.cpu().contiguous().view(torch.int16).numpy().copy()
+    vl = v.cpu().contiguous().view(torch.int16).numpy().copy()
     return kl, vl
 
 

@@ -15,7 +15,6 @@ import torch
 import synth
 from harness import assert_close, make_case, oracle_outputs
 from oracle import attention as OA
-from pool_layout import k_to_logical, v_to_logical
 
 pytestmark = pytest.mark.gpu
 
@@ -78,8 +77,8 @@ def test_step_equals_append_then_decode(d, bs):
     g = c.hq // c.hkv
     for h in range(c.hq):
         assert torch.equal(_bits(out2[3, h]), _bits(vn[3, h // g]))
-    k_log = k_to_logical(k2.cpu()).double().numpy()
-    v_log = v_to_logical(v2.cpu()).double().numpy()
+    k_log = k2.cpu().double().numpy()
+    v_log = v2.cpu().double().numpy()
     ref = OA.paged_decode(c.q.cpu().double().numpy(), k_log, v_log, t2.cpu().numpy(), l2.cpu().numpy().tolist(),
                           c.scale)
     assert_close(out2, ref, f"decode_step d={d} bs={bs}")
@@ -95,8 +94,8 @@ def test_step_rows_that_skip_or_misplace_their_slot():
     k2, v2, t2, l2 = _state(c)
     lens0 = c.lens_dev.cpu().numpy().tolist()
     tables0 = c.tables_dev.cpu().numpy()
-    k0 = k_to_logical(c.k.cpu()).double().numpy()
-    v0 = v_to_logical(c.v.cpu()).double().numpy()
+    k0 = c.k.cpu().double().numpy()
+    v0 = c.v.cpu().double().numpy()
     # what the rows that take the step store: pa_append_step without the odd rows
     ok = slots.clone()
     ok[6] = -1

@@ -15,7 +15,7 @@ import torch
 import synth
 from harness import DecodeCase, assert_close, make_case, oracle_outputs, run_decode
 from oracle.block_manager import BlockManagerModel
-from pool_layout import poison_unused_
+from harness import poison_unused_
 
 pytestmark = pytest.mark.gpu
 
