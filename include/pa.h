@@ -153,6 +153,38 @@ int pa_decode_partitioned(void* out, const void* q, const void* k_pool, const vo
 size_t pa_decode_partitioned_workspace_bytes(int num_seqs, int Hq, int Hkv, int d_head, int block_size,
                                              int max_context_len, int dtype, int partition_tokens);
 
+/* pa_check_batch: validate a batch's lengths and block tables on the device,
+ * against the sizes a decode call would be given.  The decode kernels trust
+ * them for speed: a block id outside [0, num_blocks) is never dereferenced
+ * but its tokens silently leave the softmax, and tokens past
+ * max_blocks_per_seq * B are dropped.  This call makes such inputs visible
+ * without a host copy of the tables ("PagedAttention: Virtual Memory for the
+ * KV Cache", section 7: token i lives in physical block block_table[i / B];
+ * section 8: the table holds int32 ids of pool blocks).  It enqueues one
+ * kernel on `stream` that reads only context_lens[0 .. num_seqs) and the
+ * table entries below each row's ceil(S / B), and writes
+ *
+ *   status[0]  rows with S < 0, S > max_context_len or
+ *              ceil(S / B) > max_blocks_per_seq
+ *   status[1]  table entries outside [0, num_blocks), among the first
+ *              ceil(S / B) entries of every other row
+ *   status[2]  the lowest row counted in status[0], -1 when none
+ *   status[3]  the lowest row holding an entry counted in status[1], -1 when none
+ *
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq], device
+ *   context_lens  int32 [num_seqs], device
+ *   status        int32 [4], device (or pinned host memory mapped for the
+ *                 device); every word is written, nothing needs clearing
+ * The batch is valid for pa_decode with these sizes iff status[0] and
+ * status[1] are 0 once the stream reaches this point.  Errors (host, before
+ * any launch): PA_ERR_INVALID_ARG for num_seqs < 0, max_blocks_per_seq < 1,
+ * max_context_len < 0, num_blocks < 0, block_size < 1 or a NULL pointer the
+ * call needs.  For pa_decode_step call it before the step (the step then
+ * moves each row forward by one token). */
+int pa_check_batch(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                   int max_blocks_per_seq, int max_context_len, int num_blocks, int block_size,
+                   int32_t* status, void* stream);
+
 /* pa_decode_step: one whole decode step of the batch.  Each row attends to
  * its S cached tokens and to its new token (key and value from k_new / v_new,
  * at position S); then the new token is stored and the row moved forward

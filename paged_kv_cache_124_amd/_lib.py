@@ -80,6 +80,7 @@ _SIGS = {
     "pa_decode_partitioned": (c_int, [c_void_p] * 6 + [c_int] * 5 + [c_float] + [c_int] * 5
                               + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_partitioned_workspace_bytes": (c_size_t, [c_int] * 8),
+    "pa_check_batch": (c_int, [c_void_p, c_void_p] + [c_int] * 5 + [c_void_p, c_void_p]),
     "pa_decode_shared": (c_int, [c_void_p] * 7 + [c_int] * 6 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_step_shared": (c_int, [c_void_p] * 10 + [c_int] * 6 + [c_float] + [c_int] * 4
                               + [c_void_p, c_size_t, c_void_p]),
@@ -261,6 +262,29 @@ def pa_decode_partitioned(out, q, k_pool, v_pool, block_tables, context_lens, sc
     _check(lib.pa_decode_partitioned(*args[:16], int(partition_tokens), ws_ptr, ws_bytes, args[18]),
            "pa_decode_partitioned")
     return out
+
+
+def pa_check_batch(block_tables, context_lens, max_context_len, num_blocks, block_size, status=None, stream=None):
+    """pa_check_batch of include/pa.h: validate lengths and table entries on the device.
+
+    Returns the int32 device tensor ``status`` of 4 words (allocated when None):
+    bad rows, bad entries, first bad row, first row with a bad entry (-1 when
+    none).  Read it after the stream has reached the call.
+    """
+    import torch
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    n = context_lens.shape[0]
+    if context_lens.dim() != 1 or block_tables.dim() != 2 or block_tables.shape[0] != n:
+        raise ValueError("block_tables must be [N][max_blocks] and context_lens [N]")
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=context_lens.device)
+    if status.dtype != torch.int32 or status.numel() < 4:
+        raise ValueError("status must hold 4 int32 words")
+    _check(lib.pa_check_batch(_dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), n,
+                              block_tables.shape[1], int(max_context_len), int(num_blocks), int(block_size),
+                              _dev(status, "status"), _stream_ptr(stream)), "pa_check_batch")
+    return status
 
 
 def pa_decode_step_args(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables, context_lens, scale,

@@ -28,7 +28,8 @@ PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 HOST_LIB = os.path.join(PKG, "libpa_host.so")
 HOST_ASAN_LIB = os.path.join(PKG, "libpa_host_asan.so")
 
-HIP_SOURCES = ["decode.hip", "decode_stream.hip", "decode_stream_i8.hip", "decode_shared.hip", "kv_ops.hip"]
+HIP_SOURCES = ["decode.hip", "decode_stream.hip", "decode_stream_i8.hip", "decode_shared.hip", "kv_ops.hip",
+               "check.hip"]
 PROBE_SOURCES = ["probe.hip"]
 HOST_SOURCES = ["block_manager.cpp", "status.cpp"]
 HOST_FLAGS = ["-O2", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter"]

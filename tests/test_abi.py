@@ -181,3 +181,17 @@ def test_fp8_host_validation():
     assert L.pa_copy_blocks_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 100, 2, full, 10, NUL) == 1
 
 
+
+def test_check_batch_host_validation():
+    """pa_check_batch(tables, lens, n, max_blocks, max_ctx, num_blocks, B, status, stream): bad sizes and NULL
+    pointers are refused before any launch."""
+    import paged_kv_cache_124_amd as pa
+    L = pa.lib
+    assert L.pa_check_batch(FAKE, FAKE, -1, 4, 64, 10, 16, FAKE, NUL) == 1
+    assert L.pa_check_batch(FAKE, FAKE, 4, 0, 64, 10, 16, FAKE, NUL) == 1
+    assert L.pa_check_batch(FAKE, FAKE, 4, 4, -1, 10, 16, FAKE, NUL) == 1
+    assert L.pa_check_batch(FAKE, FAKE, 4, 4, 64, -1, 16, FAKE, NUL) == 1
+    assert L.pa_check_batch(FAKE, FAKE, 4, 4, 64, 10, 0, FAKE, NUL) == 1
+    assert L.pa_check_batch(FAKE, FAKE, 4, 4, 64, 10, 16, NUL, NUL) == 1
+    assert L.pa_check_batch(NUL, FAKE, 4, 4, 64, 10, 16, FAKE, NUL) == 1
+    assert L.pa_check_batch(FAKE, NUL, 4, 4, 64, 10, 16, FAKE, NUL) == 1
