@@ -174,10 +174,10 @@ class Runner:
                       for r in range(replicas)]
             self.v = [fill(torch.empty(vshape, dtype=torch.uint8, device=device), w.seed * 10 + 2 + 7 * r)
                       for r in range(replicas)]
-            self.ks = [scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 8 + 7 * r, device)
-                       for r in range(replicas)]
-            self.vs = [scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 9 + 7 * r, device)
-                       for r in range(replicas)]
+            # one array [nb][Hkv][2] of (key scale, value scale) per replica
+            self.sc = [torch.stack([scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 8 + 7 * r, device),
+                                    scales(self.num_blocks, w.hkv, w.value_scale, w.seed * 10 + 9 + 7 * r, device)],
+                                   -1).contiguous() for r in range(replicas)]
         else:
             kshape, vshape = pa.pool_shapes(self.num_blocks, w.hkv, w.d, bs, torch.tensor([], dtype=dt).element_size())
             self.k = [synth.fill_randn_(torch.empty(kshape, dtype=dt, device=device), w.value_scale,
@@ -240,7 +240,7 @@ class Runner:
         self.step_args, self.copy_args, self.append_args = {}, {}, {}
         for r in range(replicas):
             if self.fp8:
-                cpy = pa.pa_copy_blocks_fp8_args(self.k[r], self.v[r], self.ks[r], self.vs[r], check[n:3 * n].view(n, 2))
+                cpy = pa.pa_copy_blocks_fp8_args(self.k[r], self.v[r], self.sc[r], check[n:3 * n].view(n, 2))
                 step_codes_args = pa.pa_decode_step_int8_args if self.int8 else pa.pa_decode_step_fp8_args
             else:
                 cpy = pa.pa_copy_blocks_args(self.k[r], self.v[r], check[n:3 * n].view(n, 2))
@@ -251,7 +251,7 @@ class Runner:
                                         list(cpy[pairs_at + 1:]))
                 if self.fp8:
                     self.step_args[r, b], _ = step_codes_args(
-                        self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], self.ks[r], self.vs[r],
+                        self.out, self.q, self.k_new, self.v_new, self.k[r], self.v[r], self.sc[r],
                         check[:n], self.d_tables, self.d_lens, w.scale, self.max_ctx, workspace=self.ws,
                         slot_pointer=base)
                 elif self.shared:

@@ -381,24 +381,31 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int
  *
  * Codes: FP8 E4M3 of the OCP 8-bit floating point format (exponent bias 7,
  * subnormals, no infinities, NaN = 0x7F / 0xFF, largest finite 448).
- * Scales: fp32, one per (physical block, KV head) for keys (k_scale) and one
- * for values (v_scale), each [num_blocks][Hkv] on the device, owned by the
- * caller, positive and finite.  Code c of block pb, KV head j stands for
- * value(c) * scale[pb][j].  Static per-head scaling is the case where all
- * blocks of a head carry the same scale.
+ * Scales: fp32, one per (physical block, KV head) for keys and one for
+ * values, interleaved in one device array `scales` [num_blocks][Hkv][2]
+ * owned by the caller, 8-byte aligned (PA_ERR_INVALID_ARG otherwise),
+ * positive and finite:
+ *
+ *     key scale of block pb, KV head j:   scales[(pb * Hkv + j) * 2 + 0]
+ *     value scale:                        scales[(pb * Hkv + j) * 2 + 1]
+ *
+ * so the decode fetches both of a (block, head) with one 8-byte load.  Key
+ * code c of block pb, KV head j stands for value(c) * key scale, value codes
+ * likewise.  Static per-head scaling is the case where all blocks of a head
+ * carry the same scales.
  * Pool layout: as above with E = 1: K and V codes [num_blocks][Hkv][B][D].
  */
 
 /* pa_decode over an FP8 cache.  q and out are bf16 [num_seqs][Hq][d_head];
  * the other arguments, the workspace (pa_decode_workspace_bytes with dtype
  * PA_FP8_E4M3), the split and the errors are as for pa_decode.  Scores are
- * scale * k_scale * dot(q, value(codes)) and P.V weighs value(codes) *
- * v_scale, accumulated in fp32.  Served for Hq / Hkv <= 16, num_seqs <= 3072,
+ * scale * key scale * dot(q, value(codes)) and P.V weighs value(codes) *
+ * value scale, accumulated in fp32.  Served for Hq / Hkv <= 16, num_seqs <= 3072,
  * d_head in {64, 128}, block_size in {8, 16, 32}; other shapes return
  * PA_ERR_UNSUPPORTED.  Scales of blocks the tables reach must be positive and
  * finite; a block id outside [0, num_blocks) is never dereferenced. */
-int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
-                  const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* scales,
+                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                   int Hq, int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq,
                   int max_context_len, int num_blocks, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -410,8 +417,7 @@ int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_po
  * even mantissa; magnitudes beyond 448 saturate to 448.  NaN input, or a scale
  * that is not positive and finite, stores 0x7F.  Slots as for pa_append_kv.
  * Deterministic: the codes depend only on x and the scale. */
-int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
-                     const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* scales, const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
                      int Hkv, int d_head, int block_size, int num_blocks, void* stream);
 
 /* pa_append_step into an FP8 cache: the codes as pa_append_kv_fp8 stores
@@ -419,7 +425,7 @@ int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const flo
  * pa_append_step does (block_tables[n][S / B] = slot / B, context_lens[n] =
  * S + 1 when the slot is the row's next position).  k_new, v_new bf16
  * [num_seqs][Hkv][d_head]; other arguments as for pa_append_step. */
-int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+int pa_append_step_fp8(void* k_pool, void* v_pool, const float* scales, const void* k_new,
                        const void* v_new, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
                        int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
                        void* stream);
@@ -446,18 +452,19 @@ int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const f
  * arguments, the workspace (dtype PA_FP8_E4M3), shapes and errors as for
  * pa_decode_fp8 and pa_decode_step. */
 int pa_decode_step_fp8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                       const float* k_scale, const float* v_scale, const int32_t* slot_mapping, int32_t* block_tables,
+                       const float* scales, const int32_t* slot_mapping, int32_t* block_tables,
                        int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
                        int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /* pa_copy_blocks for an FP8 cache: codes of block src over block dst, and its
- * scales with them, k_scale[dst][*] = k_scale[src][*] and likewise v_scale
+ * scales with them, scales[dst][*][*] = scales[src][*][*]
  * ("PagedAttention: Virtual Memory for the KV Cache", sections 15-16).
  * Bit-exact.  layer_stride_elems counts codes (bytes) between layers of each
- * pool, scale_layer_stride floats between layers of each scale array (both
- * ignored when num_layers == 1).  Pairs as for pa_copy_blocks. */
-int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, const int32_t* src_dst_pairs,
+ * pool, scale_layer_stride floats between layers of the scale array (at least
+ * num_blocks * Hkv * 2; both ignored when num_layers == 1).  Pairs as for
+ * pa_copy_blocks. */
+int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* scales, const int32_t* src_dst_pairs,
                        int num_pairs, int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
                        int64_t layer_stride_elems, int64_t scale_layer_stride, void* stream);
 
@@ -479,8 +486,8 @@ int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scal
 /* pa_decode over an INT8 cache: as pa_decode_fp8 with the values c * scale
  * (workspace: pa_decode_workspace_bytes with dtype PA_INT8; shapes, split and
  * errors as for pa_decode_fp8). */
-int pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
-                   const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+int pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* scales,
+                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                    int Hq, int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq,
                    int max_context_len, int num_blocks, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -490,29 +497,27 @@ int pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_p
  * x / scale of the destination (block, KV head), ties to even, clamped to
  * -127..127.  NaN input, or a scale that is not positive and finite, stores 0
  * (an 8-bit integer has no NaN).  Other arguments as for pa_append_kv_fp8. */
-int pa_append_kv_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
-                      const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
+int pa_append_kv_int8(void* k_pool, void* v_pool, const float* scales, const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
                       int Hkv, int d_head, int block_size, int num_blocks, void* stream);
 
 /* pa_append_step into an INT8 cache: the codes as pa_append_kv_int8 stores
  * them and each row moved forward as pa_append_step does; arguments as for
  * pa_append_step_fp8. */
-int pa_append_step_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+int pa_append_step_int8(void* k_pool, void* v_pool, const float* scales, const void* k_new,
                         const void* v_new, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
                         int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
                         void* stream);
 
 /* pa_decode_step_fp8 over an INT8 cache (workspace: dtype PA_INT8). */
 int pa_decode_step_int8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                        const float* k_scale, const float* v_scale, const int32_t* slot_mapping,
-                        int32_t* block_tables, int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head,
+                        const float* scales, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head,
                         int block_size, float scale, int max_blocks_per_seq, int max_context_len, int num_blocks,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* pa_copy_blocks for an INT8 cache: codes and scales of block src over block
  * dst, exactly as pa_copy_blocks_fp8 (the copy moves bytes and scales,
  * whatever the codes mean). */
-int pa_copy_blocks_int8(void* k_pool, void* v_pool, float* k_scale, float* v_scale, const int32_t* src_dst_pairs,
+int pa_copy_blocks_int8(void* k_pool, void* v_pool, float* scales, const int32_t* src_dst_pairs,
                         int num_pairs, int Hkv, int d_head, int block_size, int num_blocks, int num_layers,
                         int64_t layer_stride_elems, int64_t scale_layer_stride, void* stream);
 
@@ -536,22 +541,21 @@ int pa_copy_blocks_int8(void* k_pool, void* v_pool, float* k_scale, float* v_sca
  *                     num_layers == 1)
  *   dtype             PA_F32 or PA_BF16; pa_swap_blocks_fp8 moves FP8 codes
  *                     and their per-(block, KV head) key and value scales
- *                     (scale strides in floats), pa_swap_blocks_int8 INT8
- *                     codes and scales the same way.
+ *                     (interleaved [num_blocks][Hkv][2] arrays; scale strides
+ *                     in floats, at least blocks * Hkv * 2),
+ *                     pa_swap_blocks_int8 INT8 codes and scales the same way.
  * Argument errors as for pa_copy_blocks. */
 int pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_pool, const void* src_v_pool,
                    const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size, int dtype,
                    int src_num_blocks, int dst_num_blocks, int num_layers, int64_t src_layer_stride_elems,
                    int64_t dst_layer_stride_elems, void* stream);
-int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
-                       const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
-                       const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head,
+int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst_scales, const void* src_k_pool,
+                       const void* src_v_pool, const float* src_scales, const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head,
                        int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
                        int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, int64_t src_scale_layer_stride,
                        int64_t dst_scale_layer_stride, void* stream);
-int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
-                        const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
-                        const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head,
+int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_scales, const void* src_k_pool,
+                        const void* src_v_pool, const float* src_scales, const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head,
                         int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
                         int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems, int64_t src_scale_layer_stride,
                         int64_t dst_scale_layer_stride, void* stream);

@@ -92,21 +92,21 @@ _SIGS = {
                                c_int, c_int, c_int, c_int, c_int, c_void_p]),
     "pa_copy_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int64,
                                c_int, c_void_p]),
-    "pa_decode_fp8": (c_int, [c_void_p] * 8 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
-    "pa_append_kv_fp8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
-    "pa_copy_blocks_fp8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
-    "pa_append_step_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
+    "pa_decode_fp8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
+    "pa_append_kv_fp8": (c_int, [c_void_p] * 6 + [c_int] * 5 + [c_void_p]),
+    "pa_copy_blocks_fp8": (c_int, [c_void_p] * 4 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
+    "pa_append_step_fp8": (c_int, [c_void_p] * 8 + [c_int] * 6 + [c_void_p]),
     "pa_swap_blocks": (c_int, [c_void_p] * 5 + [c_int] * 8 + [c_int64, c_int64, c_void_p]),
-    "pa_swap_blocks_fp8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
-    "pa_decode_step_fp8": (c_int, [c_void_p] * 11 + [c_int] * 5 + [c_float] + [c_int] * 3 +
+    "pa_swap_blocks_fp8": (c_int, [c_void_p] * 7 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
+    "pa_decode_step_fp8": (c_int, [c_void_p] * 10 + [c_int] * 5 + [c_float] + [c_int] * 3 +
                            [c_void_p, c_size_t, c_void_p]),
-    "pa_decode_step_int8": (c_int, [c_void_p] * 11 + [c_int] * 5 + [c_float] + [c_int] * 3 +
+    "pa_decode_step_int8": (c_int, [c_void_p] * 10 + [c_int] * 5 + [c_float] + [c_int] * 3 +
                             [c_void_p, c_size_t, c_void_p]),
-    "pa_decode_int8": (c_int, [c_void_p] * 8 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
-    "pa_append_kv_int8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_void_p]),
-    "pa_copy_blocks_int8": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
-    "pa_append_step_int8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_void_p]),
-    "pa_swap_blocks_int8": (c_int, [c_void_p] * 9 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
+    "pa_decode_int8": (c_int, [c_void_p] * 7 + [c_int] * 5 + [c_float] + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
+    "pa_append_kv_int8": (c_int, [c_void_p] * 6 + [c_int] * 5 + [c_void_p]),
+    "pa_copy_blocks_int8": (c_int, [c_void_p] * 4 + [c_int] * 6 + [c_int64, c_int64, c_void_p]),
+    "pa_append_step_int8": (c_int, [c_void_p] * 8 + [c_int] * 6 + [c_void_p]),
+    "pa_swap_blocks_int8": (c_int, [c_void_p] * 7 + [c_int] * 6 + [c_int64] * 4 + [c_void_p]),
     "pa_bm_create": (c_void_p, [c_int, c_int, _P32]),
     "pa_bm_destroy": (None, [c_void_p]),
     "pa_bm_add_seq": (c_int, [c_void_p, c_int64, c_int]),
@@ -558,34 +558,37 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None):
                               _stream_ptr(stream)), "pa_swap_blocks")
 
 
-def _swap_codes(fn, name, dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream):
+def _swap_codes(fn, name, dst_k, dst_v, dst_scales, src_k, src_v, src_scales, pairs, stream):
     import torch
     if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be int32 [P][2]")
-    _, hkv, d, bs = _fp8_pools(src_k, src_v)
-    _check(fn(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), _pool_ptr(dst_ks, "dst_ks"),
-              _pool_ptr(dst_vs, "dst_vs"), _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"),
-              _pool_ptr(src_ks, "src_ks"), _pool_ptr(src_vs, "src_vs"),
+    nbs, hkv, d, bs = _fp8_pools(src_k, src_v)
+    nbd, _, _, _ = _fp8_pools(dst_k, dst_v)
+    _scales(src_scales, nbs, hkv)
+    _scales(dst_scales, nbd, hkv)
+    _check(fn(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), _pool_ptr(dst_scales, "dst_scales"),
+              _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"), _pool_ptr(src_scales, "src_scales"),
               _dev(pairs, "pairs") if pairs.shape[0] else c_void_p(0), pairs.shape[0], hkv, d, bs,
-              src_k.shape[0], dst_k.shape[0], 1, 0, 0, 0, 0, _stream_ptr(stream)), name)
+              nbs, nbd, 1, 0, 0, 0, 0, _stream_ptr(stream)), name)
 
 
-def pa_swap_blocks_fp8(dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream=None):
-    """pa_swap_blocks_fp8 of include/pa.h (one-layer FP8 pools with their [nb][Hkv] scales)."""
-    _swap_codes(lib.pa_swap_blocks_fp8, "pa_swap_blocks_fp8", dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks,
-                src_vs, pairs, stream)
+def pa_swap_blocks_fp8(dst_k, dst_v, dst_scales, src_k, src_v, src_scales, pairs, stream=None):
+    """pa_swap_blocks_fp8 of include/pa.h (one-layer FP8 pools with their [nb][Hkv][2] scales)."""
+    _swap_codes(lib.pa_swap_blocks_fp8, "pa_swap_blocks_fp8", dst_k, dst_v, dst_scales, src_k, src_v, src_scales,
+                pairs, stream)
 
 
-def pa_swap_blocks_int8(dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks, src_vs, pairs, stream=None):
-    """pa_swap_blocks_int8 of include/pa.h (one-layer INT8 pools with their [nb][Hkv] scales)."""
-    _swap_codes(lib.pa_swap_blocks_int8, "pa_swap_blocks_int8", dst_k, dst_v, dst_ks, dst_vs, src_k, src_v, src_ks,
-                src_vs, pairs, stream)
+def pa_swap_blocks_int8(dst_k, dst_v, dst_scales, src_k, src_v, src_scales, pairs, stream=None):
+    """pa_swap_blocks_int8 of include/pa.h (one-layer INT8 pools with their [nb][Hkv][2] scales)."""
+    _swap_codes(lib.pa_swap_blocks_int8, "pa_swap_blocks_int8", dst_k, dst_v, dst_scales, src_k, src_v, src_scales,
+                pairs, stream)
 
 
 # ---------------------------------------------------------------------------
 # FP8 (E4M3) and INT8 caches: uint8 code pools [num_blocks][Hkv][B][D]
-# and float32 scales [num_blocks][Hkv] (or [L][num_blocks][Hkv] for a layered
-# copy); the INT8 functions take the same arguments as the FP8 ones
+# and one float32 scale array [num_blocks][Hkv][2] (key, value; or
+# [L][num_blocks][Hkv][2] for a layered copy); the INT8 functions take the same
+# arguments as the FP8 ones
 # ---------------------------------------------------------------------------
 
 def _fp8_pools(k_pool, v_pool):
@@ -595,34 +598,33 @@ def _fp8_pools(k_pool, v_pool):
     return _pool_dims(k_pool, v_pool)
 
 
-def _scales(k_scale, v_scale, nb, hkv, lead=()):
+def _scales(scales, nb, hkv, lead=()):
     import torch
-    want = tuple(lead) + (nb, hkv)
-    for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
-        if t.dtype != torch.float32 or tuple(t.shape) != want:
-            raise ValueError(f"{name} must be float32 {list(want)}")
+    want = tuple(lead) + (nb, hkv, 2)
+    if scales.dtype != torch.float32 or tuple(scales.shape) != want or not scales.is_contiguous():
+        raise ValueError(f"scales must be contiguous float32 {list(want)} (key, value)")
 
 
-def pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+def pa_decode_fp8_args(out, q, k_pool, v_pool, scales, block_tables, context_lens, scale,
                        max_context_len, workspace=None, stream=None):
     """Validate once and return (args, workspace) for repeated ``lib.pa_decode_fp8(*args)`` calls."""
-    return _decode_codes_args(PA_FP8_E4M3, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+    return _decode_codes_args(PA_FP8_E4M3, out, q, k_pool, v_pool, scales, block_tables, context_lens,
                               scale, max_context_len, workspace, stream)
 
 
-def pa_decode_int8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+def pa_decode_int8_args(out, q, k_pool, v_pool, scales, block_tables, context_lens, scale,
                         max_context_len, workspace=None, stream=None):
     """Validate once and return (args, workspace) for repeated ``lib.pa_decode_int8(*args)`` calls."""
-    return _decode_codes_args(PA_INT8, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+    return _decode_codes_args(PA_INT8, out, q, k_pool, v_pool, scales, block_tables, context_lens,
                               scale, max_context_len, workspace, stream)
 
 
-def _decode_codes_args(dtype_code, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+def _decode_codes_args(dtype_code, out, q, k_pool, v_pool, scales, block_tables, context_lens, scale,
                        max_context_len, workspace, stream):
     import torch
     n, hq, d = q.shape
     nb, hkv, d2, bs = _fp8_pools(k_pool, v_pool)
-    _scales(k_scale, v_scale, nb, hkv)
+    _scales(scales, nb, hkv)
     if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or d2 != d:
         raise ValueError("q and out must be bf16 [N][Hq][D] matching the pools")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -635,37 +637,37 @@ def _decode_codes_args(dtype_code, out, q, k_pool, v_pool, k_scale, v_scale, blo
     ws_ptr = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-            _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(block_tables, "block_tables"),
+            _dev(scales, "scales"), _dev(block_tables, "block_tables"),
             _dev(context_lens, "context_lens"), n, hq, hkv, d, bs, float(scale), block_tables.shape[1],
             int(max_context_len), nb, ws_ptr, ws_bytes, _stream_ptr(stream))
     return args, workspace
 
 
-def pa_decode_fp8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale, max_context_len,
+def pa_decode_fp8(out, q, k_pool, v_pool, scales, block_tables, context_lens, scale, max_context_len,
                   workspace=None, stream=None):
     """pa_decode_fp8 of include/pa.h: bf16 q/out over uint8 E4M3 code pools with float32 scales."""
-    args, _ws = pa_decode_fp8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+    args, _ws = pa_decode_fp8_args(out, q, k_pool, v_pool, scales, block_tables, context_lens, scale,
                                    max_context_len, workspace, stream)
     _check(lib.pa_decode_fp8(*args), "pa_decode_fp8")
     return out
 
 
-def pa_decode_int8(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale, max_context_len,
+def pa_decode_int8(out, q, k_pool, v_pool, scales, block_tables, context_lens, scale, max_context_len,
                    workspace=None, stream=None):
     """pa_decode_int8 of include/pa.h: bf16 q/out over INT8 code pools (uint8 bytes) with float32 scales."""
-    args, _ws = pa_decode_int8_args(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale,
+    args, _ws = pa_decode_int8_args(out, q, k_pool, v_pool, scales, block_tables, context_lens, scale,
                                     max_context_len, workspace, stream)
     _check(lib.pa_decode_int8(*args), "pa_decode_int8")
     return out
 
 
-def _decode_step_codes_args(dtype_code, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+def _decode_step_codes_args(dtype_code, out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping,
                             block_tables, context_lens, scale, max_context_len, workspace, stream, slot_pointer):
     import torch
-    args, workspace = _decode_codes_args(dtype_code, out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
+    args, workspace = _decode_codes_args(dtype_code, out, q, k_pool, v_pool, scales, block_tables,
                                          context_lens, scale, max_context_len, workspace, stream)
     n, hq, d = q.shape
-    hkv = k_scale.shape[1]
+    hkv = scales.shape[1]
     if tuple(k_new.shape) != (n, hkv, d) or tuple(v_new.shape) != (n, hkv, d):
         raise ValueError("k_new / v_new must be [N][Hkv][D]")
     if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
@@ -673,50 +675,50 @@ def _decode_step_codes_args(dtype_code, out, q, k_new, v_new, k_pool, v_pool, k_
     if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (n,):
         raise ValueError("slot_mapping must be int32 [N]")
     slots = c_void_p(slot_pointer) if slot_pointer is not None else _dev(slot_mapping, "slot_mapping")
-    # pa_decode_*(out, q, k, v, ks, vs, tables, lens, ...) -> pa_decode_step_*(out, q, k_new, v_new, k, v, ks, vs,
+    # pa_decode_*(out, q, k, v, scales, tables, lens, ...) -> pa_decode_step_*(out, q, k_new, v_new, k, v, scales,
     # slots, tables, lens, ...)
-    return (args[:2] + (_dev(k_new, "k_new"), _dev(v_new, "v_new")) + args[2:6] + (slots,) + args[6:]), workspace
+    return (args[:2] + (_dev(k_new, "k_new"), _dev(v_new, "v_new")) + args[2:5] + (slots,) + args[5:]), workspace
 
 
-def pa_decode_step_fp8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+def pa_decode_step_fp8_args(out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping, block_tables,
                             context_lens, scale, max_context_len, workspace=None, stream=None, slot_pointer=None):
     """Validate once and return (args, workspace) for repeated ``lib.pa_decode_step_fp8(*args)`` calls."""
-    return _decode_step_codes_args(PA_FP8_E4M3, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+    return _decode_step_codes_args(PA_FP8_E4M3, out, q, k_new, v_new, k_pool, v_pool, scales,
                                    slot_mapping, block_tables, context_lens, scale, max_context_len, workspace,
                                    stream, slot_pointer)
 
 
-def pa_decode_step_int8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+def pa_decode_step_int8_args(out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping, block_tables,
                              context_lens, scale, max_context_len, workspace=None, stream=None, slot_pointer=None):
     """Validate once and return (args, workspace) for repeated ``lib.pa_decode_step_int8(*args)`` calls."""
-    return _decode_step_codes_args(PA_INT8, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+    return _decode_step_codes_args(PA_INT8, out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping,
                                    block_tables, context_lens, scale, max_context_len, workspace, stream,
                                    slot_pointer)
 
 
-def pa_decode_step_fp8(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+def pa_decode_step_fp8(out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping, block_tables,
                        context_lens, scale, max_context_len, workspace=None, stream=None):
     """pa_decode_step_fp8 of include/pa.h: attend to each row's new token as its codes, then store them."""
-    args, _ws = pa_decode_step_fp8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+    args, _ws = pa_decode_step_fp8_args(out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping,
                                         block_tables, context_lens, scale, max_context_len, workspace, stream)
     _check(lib.pa_decode_step_fp8(*args), "pa_decode_step_fp8")
     return out
 
 
-def pa_decode_step_int8(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+def pa_decode_step_int8(out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping, block_tables,
                         context_lens, scale, max_context_len, workspace=None, stream=None):
     """pa_decode_step_int8 of include/pa.h: as pa_decode_step_fp8 over an INT8 cache."""
-    args, _ws = pa_decode_step_int8_args(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+    args, _ws = pa_decode_step_int8_args(out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping,
                                          block_tables, context_lens, scale, max_context_len, workspace, stream)
     _check(lib.pa_decode_step_int8(*args), "pa_decode_step_int8")
     return out
 
 
-def pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, stream=None):
+def pa_append_kv_fp8_args(k_pool, v_pool, scales, k_new, v_new, slot_mapping, stream=None):
     """Validate once and return the argument tuple for ``lib.pa_append_kv_fp8(*args)``."""
     import torch
     nb, hkv, d, bs = _fp8_pools(k_pool, v_pool)
-    _scales(k_scale, v_scale, nb, hkv)
+    _scales(scales, nb, hkv)
     t = k_new.shape[0]
     if tuple(k_new.shape) != (t, hkv, d) or tuple(v_new.shape) != (t, hkv, d):
         raise ValueError("k_new / v_new must be [T][Hkv][D]")
@@ -724,29 +726,29 @@ def pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_m
         raise ValueError("k_new / v_new must be bf16")
     if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (t,):
         raise ValueError("slot_mapping must be int32 [T]")
-    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(scales, "scales"),
             _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"), t, hkv, d, bs, nb,
             _stream_ptr(stream))
 
 
-def pa_append_kv_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, stream=None):
+def pa_append_kv_fp8(k_pool, v_pool, scales, k_new, v_new, slot_mapping, stream=None):
     """pa_append_kv_fp8 of include/pa.h: quantize bf16 k_new/v_new [T][Hkv][D] into their slots."""
-    _check(lib.pa_append_kv_fp8(*pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+    _check(lib.pa_append_kv_fp8(*pa_append_kv_fp8_args(k_pool, v_pool, scales, k_new, v_new,
                                                        slot_mapping, stream)), "pa_append_kv_fp8")
 
 
-def pa_append_kv_int8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, stream=None):
+def pa_append_kv_int8(k_pool, v_pool, scales, k_new, v_new, slot_mapping, stream=None):
     """pa_append_kv_int8 of include/pa.h: quantize bf16 k_new/v_new [T][Hkv][D] into their slots as INT8 codes."""
-    _check(lib.pa_append_kv_int8(*pa_append_kv_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+    _check(lib.pa_append_kv_int8(*pa_append_kv_fp8_args(k_pool, v_pool, scales, k_new, v_new,
                                                         slot_mapping, stream)), "pa_append_kv_int8")
 
 
-def pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables,
+def pa_append_step_fp8_args(k_pool, v_pool, scales, k_new, v_new, slot_mapping, block_tables,
                             context_lens, stream=None):
     """Validate once and return the argument tuple for ``lib.pa_append_step_fp8(*args)``."""
     import torch
     nb, hkv, d, bs = _fp8_pools(k_pool, v_pool)
-    _scales(k_scale, v_scale, nb, hkv)
+    _scales(scales, nb, hkv)
     n = k_new.shape[0]
     if tuple(k_new.shape) != (n, hkv, d) or tuple(v_new.shape) != (n, hkv, d):
         raise ValueError("k_new / v_new must be [N][Hkv][D]")
@@ -759,29 +761,29 @@ def pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot
         raise ValueError("slot_mapping and context_lens must be [N]")
     if block_tables.dim() != 2 or block_tables.shape[0] != n:
         raise ValueError("block_tables must be [N][max_blocks]")
-    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(scales, "scales"),
             _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"),
             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), n, block_tables.shape[1], hkv, d,
             bs, nb, _stream_ptr(stream))
 
 
-def pa_append_step_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables, context_lens,
+def pa_append_step_fp8(k_pool, v_pool, scales, k_new, v_new, slot_mapping, block_tables, context_lens,
                        stream=None):
     """pa_append_step_fp8 of include/pa.h: quantizing append of row n's token and the row moved forward."""
-    _check(lib.pa_append_step_fp8(*pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+    _check(lib.pa_append_step_fp8(*pa_append_step_fp8_args(k_pool, v_pool, scales, k_new, v_new,
                                                            slot_mapping, block_tables, context_lens, stream)),
            "pa_append_step_fp8")
 
 
-def pa_append_step_int8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables, context_lens,
+def pa_append_step_int8(k_pool, v_pool, scales, k_new, v_new, slot_mapping, block_tables, context_lens,
                         stream=None):
     """pa_append_step_int8 of include/pa.h: INT8 quantizing append of row n's token and the row moved forward."""
-    _check(lib.pa_append_step_int8(*pa_append_step_fp8_args(k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+    _check(lib.pa_append_step_int8(*pa_append_step_fp8_args(k_pool, v_pool, scales, k_new, v_new,
                                                             slot_mapping, block_tables, context_lens, stream)),
            "pa_append_step_int8")
 
 
-def pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
+def pa_copy_blocks_fp8_args(k_pool, v_pool, scales, src_dst_pairs, stream=None):
     """Validate once and return the argument tuple for ``lib.pa_copy_blocks_fp8(*args)``.
 
     Pools and scales are one layer or all layers (leading [L] on both).
@@ -791,25 +793,25 @@ def pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, str
     kl, vl = (k_pool[0], v_pool[0]) if layered else (k_pool, v_pool)
     nb, hkv, d, bs = _fp8_pools(kl, vl)
     layers = k_pool.shape[0] if layered else 1
-    _scales(k_scale, v_scale, nb, hkv, (layers,) if layered else ())
+    _scales(scales, nb, hkv, (layers,) if layered else ())
     if src_dst_pairs.dtype != torch.int32 or src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
         raise ValueError("src_dst_pairs must be int32 [P][2]")
     stride = kl.numel() if layered else 0
-    sstride = nb * hkv if layered else 0
-    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+    sstride = nb * hkv * 2 if layered else 0
+    return (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(scales, "scales"),
             _dev(src_dst_pairs, "src_dst_pairs"), src_dst_pairs.shape[0], hkv, d, bs, nb, layers, stride, sstride,
             _stream_ptr(stream))
 
 
-def pa_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
+def pa_copy_blocks_fp8(k_pool, v_pool, scales, src_dst_pairs, stream=None):
     """pa_copy_blocks_fp8 of include/pa.h: codes and scales of each src block over its dst."""
-    _check(lib.pa_copy_blocks_fp8(*pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream)),
+    _check(lib.pa_copy_blocks_fp8(*pa_copy_blocks_fp8_args(k_pool, v_pool, scales, src_dst_pairs, stream)),
            "pa_copy_blocks_fp8")
 
 
-def pa_copy_blocks_int8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, stream=None):
+def pa_copy_blocks_int8(k_pool, v_pool, scales, src_dst_pairs, stream=None):
     """pa_copy_blocks_int8 of include/pa.h: INT8 codes and scales of each src block over its dst."""
-    _check(lib.pa_copy_blocks_int8(*pa_copy_blocks_fp8_args(k_pool, v_pool, k_scale, v_scale, src_dst_pairs,
+    _check(lib.pa_copy_blocks_int8(*pa_copy_blocks_fp8_args(k_pool, v_pool, scales, src_dst_pairs,
                                                             stream)), "pa_copy_blocks_int8")
 
 

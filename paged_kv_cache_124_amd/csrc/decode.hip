@@ -765,8 +765,8 @@ extern "C" int pa_decode_step_shared(void* out, const void* q, const void* k_new
 namespace {
 
 // pa_decode over a cache of one-byte codes (FP8 E4M3 or INT8) with scales.
-int decode_codes(int codes, void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
-                 const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq,
+int decode_codes(int codes, void* out, const void* q, const void* k_pool, const void* v_pool, const float* scales,
+                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int Hq,
                  int Hkv, int d_head, int block_size, float scale, int max_blocks_per_seq, int max_context_len,
                  int num_blocks, void* workspace, size_t workspace_bytes, void* stream,
                  const pa::StepInputs* step = nullptr) {
@@ -778,68 +778,68 @@ int decode_codes(int codes, void* out, const void* q, const void* k_pool, const 
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size < max_context_len) return PA_ERR_INVALID_ARG;
   if (!stream_eligible_fp8(num_seqs, Hq / Hkv, d_head, block_size) || Hq > 65535) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !context_lens)
-    return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_pool || !v_pool || !scales || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(scales) % 8 != 0) return PA_ERR_INVALID_ARG;  // read as (key, value) pairs
   if (num_blocks < 1 || max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;  // the kernel may read block 0 / entry 0
   const StreamPlan sp = stream_plan(num_seqs, Hq, Hkv, d_head, block_size, max_context_len, true);
   if (!workspace || workspace_bytes < sp.workspace_bytes) return PA_ERR_WORKSPACE;
   return launch_stream(sp, static_cast<hipStream_t>(stream), q, k_pool, v_pool, block_tables, context_lens, out,
                        workspace, num_seqs, Hq, Hkv, d_head, block_size, max_blocks_per_seq, num_blocks,
-                       scale * kLog2e, step, k_scale, v_scale, codes);
+                       scale * kLog2e, step, scales, codes);
 }
 
 int decode_step_codes(int codes, void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
-                      void* v_pool, const float* k_scale, const float* v_scale, const int32_t* slot_mapping,
+                      void* v_pool, const float* scales, const int32_t* slot_mapping,
                       int32_t* block_tables, int32_t* context_lens, int num_seqs, int Hq, int Hkv, int d_head,
                       int block_size, float scale, int max_blocks_per_seq, int max_context_len, int num_blocks,
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
   const pa::StepInputs step{k_new, v_new, slot_mapping};
-  return decode_codes(codes, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, num_seqs, Hq, Hkv,
+  return decode_codes(codes, out, q, k_pool, v_pool, scales, block_tables, context_lens, num_seqs, Hq, Hkv,
                       d_head, block_size, scale, max_blocks_per_seq, max_context_len, num_blocks, workspace,
                       workspace_bytes, stream, &step);
 }
 
 }  // namespace
 
-extern "C" int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
-                             const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+extern "C" int pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* scales,
+                             const int32_t* block_tables, const int32_t* context_lens,
                              int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
                              int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return decode_codes(pa::kKvE4m3, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, num_seqs,
+  return decode_codes(pa::kKvE4m3, out, q, k_pool, v_pool, scales, block_tables, context_lens, num_seqs,
                       Hq, Hkv, d_head, block_size, scale, max_blocks_per_seq, max_context_len, num_blocks, workspace,
                       workspace_bytes, stream);
 }
 
-extern "C" int pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
-                              const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+extern "C" int pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool, const float* scales,
+                              const int32_t* block_tables, const int32_t* context_lens,
                               int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
                               int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  return decode_codes(pa::kKvInt8, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, num_seqs,
+  return decode_codes(pa::kKvInt8, out, q, k_pool, v_pool, scales, block_tables, context_lens, num_seqs,
                       Hq, Hkv, d_head, block_size, scale, max_blocks_per_seq, max_context_len, num_blocks, workspace,
                       workspace_bytes, stream);
 }
 
 extern "C" int pa_decode_step_fp8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
-                                  void* v_pool, const float* k_scale, const float* v_scale,
+                                  void* v_pool, const float* scales,
                                   const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
                                   int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
                                   int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  return decode_step_codes(pa::kKvE4m3, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+  return decode_step_codes(pa::kKvE4m3, out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping,
                            block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size, scale,
                            max_blocks_per_seq, max_context_len, num_blocks, workspace, workspace_bytes, stream);
 }
 
 extern "C" int pa_decode_step_int8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
-                                   void* v_pool, const float* k_scale, const float* v_scale,
+                                   void* v_pool, const float* scales,
                                    const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
                                    int num_seqs, int Hq, int Hkv, int d_head, int block_size, float scale,
                                    int max_blocks_per_seq, int max_context_len, int num_blocks, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  return decode_step_codes(pa::kKvInt8, out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+  return decode_step_codes(pa::kKvInt8, out, q, k_new, v_new, k_pool, v_pool, scales, slot_mapping,
                            block_tables, context_lens, num_seqs, Hq, Hkv, d_head, block_size, scale,
                            max_blocks_per_seq, max_context_len, num_blocks, workspace, workspace_bytes, stream);
 }

@@ -38,18 +38,18 @@ bool stream_eligible_fp8(int num_seqs, int g, int d, int block_size);
 // fp8: 64-token tiles over an FP8 cache instead of 32-token bf16 tiles.
 StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int max_ctx, bool fp8 = false);
 // codes != kKvBf16: the pools hold one-byte codes with per-(block, KV head)
-// scales k_scale / v_scale.
+// key and value scales, interleaved [num_blocks][Hkv][2].
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
                   int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
-                  const float* k_scale = nullptr, const float* v_scale = nullptr, int codes = kKvBf16);
+                  const float* scales = nullptr, int codes = kKvBf16);
 
 // The INT8-cache instances of the kernel (decode_stream_i8.hip); launch_stream
 // calls it for codes == kKvInt8.
 int launch_stream_int8(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
                        const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d,
                        int block_size, int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
-                       const float* k_scale, const float* v_scale);
+                       const float* scales);
 
 // Shared-prefix kernel (decode_shared.hip): groups of consecutive rows whose
 // first P tokens lie in the same full blocks, int32 [num_groups][3] =

@@ -71,21 +71,21 @@ StreamPlan stream_plan(int num_seqs, int hq, int hkv, int d, int block_size, int
 
 int launch_stream(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v, const int32_t* bt,
                   const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d, int block_size,
-                  int max_blocks, int num_blocks, float scale_log2, const StepInputs* step, const float* k_scale,
-                  const float* v_scale, int codes) {
-  if (codes != kKvBf16 && (!k_scale || !v_scale)) return PA_ERR_UNSUPPORTED;
+                  int max_blocks, int num_blocks, float scale_log2, const StepInputs* step, const float* scales,
+                  int codes) {
+  if (codes != kKvBf16 && !scales) return PA_ERR_UNSUPPORTED;
   if (codes == kKvInt8)
     return launch_stream_int8(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, d, block_size, max_blocks, num_blocks,
-                              scale_log2, step, k_scale, v_scale);
-#define PA_STREAM_CASE(DD, BB)                                                                               \
-  if (d == DD && block_size == BB) {                                                                         \
-    if (codes == kKvE4m3)                                                                                    \
-      launch_stream_db<DD, BB, kKvE4m3>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,  \
-                                        scale_log2, step, k_scale, v_scale);                                 \
-    else                                                                                                     \
-      launch_stream_db<DD, BB, kKvBf16>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,  \
-                                        scale_log2, step, nullptr, nullptr);                                 \
-    return launch_status();                                                                                  \
+                              scale_log2, step, scales);
+#define PA_STREAM_CASE(DD, BB)                                                                                       \
+  if (d == DD && block_size == BB) {                                                                                 \
+    if (codes == kKvE4m3)                                                                                            \
+      launch_stream_db<DD, BB, kKvE4m3>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,          \
+                                        scale_log2, step, scales);                                                   \
+    else                                                                                                             \
+      launch_stream_db<DD, BB, kKvBf16>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks,          \
+                                        scale_log2, step, nullptr);                                                  \
+    return launch_status();                                                                                          \
   }
   PA_STREAM_CASE(128, 16)
   PA_STREAM_CASE(128, 8)

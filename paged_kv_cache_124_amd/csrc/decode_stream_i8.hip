@@ -11,12 +11,12 @@ namespace pa {
 int launch_stream_int8(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
                        const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv, int d,
                        int block_size, int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
-                       const float* k_scale, const float* v_scale) {
-#define PA_STREAM_CASE(DD, BB)                                                                                   \
-  if (d == DD && block_size == BB) {                                                                             \
+                       const float* scales) {
+#define PA_STREAM_CASE(DD, BB)                                                                                       \
+  if (d == DD && block_size == BB) {                                                                                 \
     launch_stream_db<DD, BB, kKvInt8>(p, s, q, k, v, bt, cl, out, ws, n, hq, hkv, max_blocks, num_blocks, scale_log2, \
-                                      step, k_scale, v_scale);                                                   \
-    return launch_status();                                                                                      \
+                                      step, scales);                                                                 \
+    return launch_status();                                                                                          \
   }
   PA_STREAM_CASE(128, 16)
   PA_STREAM_CASE(128, 8)

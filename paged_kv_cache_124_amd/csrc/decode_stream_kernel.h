@@ -63,7 +63,8 @@ struct Buf8 {
   bool ok[2][2];             // the block of that value group is in the pool
 };
 
-// Scales of the blocks of the lane's token groups (0 where the block is missing).
+// Scales of the blocks of the lane's token groups (0 where the block is missing),
+// from the interleaved array [num_blocks][Hkv][2] (key, value).
 struct Sc8 {
   float k[2][2], v[2][2];  // [sub-tile][slab]
 };
@@ -113,8 +114,8 @@ __device__ __forceinline__ int group_block(const Tb<64 / B>& tb, int first, int 
 }
 
 template <int B>
-__device__ __forceinline__ Sc8 load_scales(const Tb<64 / B>& tb, const float* __restrict__ k_scale,
-                                           const float* __restrict__ v_scale, int j, int hkv, int num_blocks, int gq) {
+__device__ __forceinline__ Sc8 load_scales(const Tb<64 / B>& tb, const float* __restrict__ scales, int j, int hkv,
+                                           int num_blocks, int gq) {
   Sc8 sc;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -123,9 +124,9 @@ __device__ __forceinline__ Sc8 load_scales(const Tb<64 / B>& tb, const float* __
       const int e = group_block<B>(tb, 32 * u + 16 * a, gq);
       const bool ok = e >= 0 && e < num_blocks;
       const int64_t idx = static_cast<int64_t>(ok ? e : 0) * hkv + j;
-      const float kv = k_scale[idx], vv = v_scale[idx];
-      sc.k[u][a] = ok ? kv : 0.f;
-      sc.v[u][a] = ok ? vv : 0.f;
+      const float2 kv = *reinterpret_cast<const float2*>(scales + 2 * idx);  // one 8-byte load per (block, head)
+      sc.k[u][a] = ok ? kv.x : 0.f;
+      sc.v[u][a] = ok ? kv.y : 0.f;
     }
   return sc;
 }
@@ -274,8 +275,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     float* __restrict__ rec, int32_t* __restrict__ prefix_out, int n_seqs, int hq, int hkv, int g, int max_blocks,
     int num_blocks, float scale_log2, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, float* __restrict__ whole_rec, int32_t* __restrict__ lens_out) {
+    const int32_t* __restrict__ slots, int32_t* __restrict__ slots_out, const float* __restrict__ scales,
+    float* __restrict__ whole_rec, int32_t* __restrict__ lens_out) {
   constexpr bool F8 = KV != kKvBf16;  // one-byte codes (E4M3 or INT8) with scales
   constexpr bool I8 = KV == kKvInt8;
   constexpr int TOK = kTok<F8>;
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   dma_tile<D, B, F8>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
   // FP8: the scales of a tile's blocks travel with it, one tile ahead like its Q
   Sc8 scA{}, scB{};
-  if constexpr (F8) scA = load_scales<B>(tbA, k_scale, v_scale, cur.j, hkv, num_blocks, gq);
+  if constexpr (F8) scA = load_scales<B>(tbA, scales, cur.j, hkv, num_blocks, gq);
 
   int64_t x = x0;
   // One step: tile `cur` (staged in stage SC, blocks tbc) is computed while
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       int row_slot = -1;
       if (row_end) row_slot = slots[cur.n];
       tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
-      scn = load_scales<B>(tbn, k_scale, v_scale, nxt.j, hkv, num_blocks, gq);
+      scn = load_scales<B>(tbn, scales, nxt.j, hkv, num_blocks, gq);
       dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
 #pragma unroll
@@ -505,8 +506,7 @@ struct CodeStepArgs {
   const uint16_t* k_new;   // [rows][Hkv][D] bf16
   const uint16_t* v_new;
   const int32_t* slots;    // the caller's slot of each row's new token (read here only for rows without tiles)
-  const float* k_scale;    // [num_blocks][Hkv]
-  const float* v_scale;
+  const float* scales;     // [num_blocks][Hkv][2]: key scale, value scale
   int32_t* block_tables;
   int32_t* context_lens;
   int max_blocks, block_size, num_blocks;
@@ -564,7 +564,8 @@ __global__ __launch_bounds__(256) void merge_step8(const float* __restrict__ rec
   const int slot = has_tiles ? copied_slot : a.slots[n];
   const bool in_pool = slot >= 0 && static_cast<int64_t>(slot) < static_cast<int64_t>(a.num_blocks) * B;
   const int64_t head = static_cast<int64_t>(in_pool ? slot / B : 0) * hkv + j;
-  const float ks = a.k_scale[head], vs = a.v_scale[head];
+  const float2 kvs = *reinterpret_cast<const float2*>(a.scales + 2 * head);
+  const float ks = kvs.x, vs = kvs.y;
   // the lane's elements d = lane + 64 e of the token, coded as the append codes them
   uint32_t kc[E], vc[E];
   float kv[E];
@@ -613,8 +614,8 @@ __global__ __launch_bounds__(256) void merge_step8(const float* __restrict__ rec
 template <int D, int B, int KV>
 void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const void* k, const void* v,
                       const int32_t* bt, const int32_t* cl, void* out, void* ws, int n, int hq, int hkv,
-                      int max_blocks, int num_blocks, float scale_log2, const StepInputs* step, const float* k_scale,
-                      const float* v_scale) {
+                      int max_blocks, int num_blocks, float scale_log2, const StepInputs* step,
+                      const float* scales) {
   char* base = static_cast<char*>(ws);
   int32_t* prefix = reinterpret_cast<int32_t*>(base + p.prefix_offset);
   int32_t* slots_ws = reinterpret_cast<int32_t*>(base + p.slots_offset);
@@ -641,7 +642,7 @@ void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const v
       int32_t* lens_ws = reinterpret_cast<int32_t*>(base + p.lens_offset);
       decode_stream<D, B, KV><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
           static_cast<const uint16_t*>(q), k, v, bt, cl, static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g,
-          max_blocks, num_blocks, scale_log2, nullptr, nullptr, step->slots, slots_ws, k_scale, v_scale, whole,
+          max_blocks, num_blocks, scale_log2, nullptr, nullptr, step->slots, slots_ws, scales, whole,
           lens_ws);
       CodeStepArgs ca{};
       ca.k_pool = static_cast<uint8_t*>(const_cast<void*>(k));
@@ -649,8 +650,7 @@ void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const v
       ca.k_new = static_cast<const uint16_t*>(step->k_new);
       ca.v_new = static_cast<const uint16_t*>(step->v_new);
       ca.slots = step->slots;
-      ca.k_scale = k_scale;
-      ca.v_scale = v_scale;
+      ca.scales = scales;
       ca.block_tables = const_cast<int32_t*>(bt);
       ca.context_lens = const_cast<int32_t*>(cl);
       ca.max_blocks = max_blocks;
@@ -664,7 +664,7 @@ void launch_stream_db(const StreamPlan& p, hipStream_t s, const void* q, const v
   }
   decode_stream<D, B, KV><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
       static_cast<const uint16_t*>(q), k, v, bt, cl, static_cast<uint16_t*>(out), rec, prefix, n, hq, hkv, g,
-      max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws, k_scale, v_scale, nullptr, nullptr);
+      max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws, scales, nullptr, nullptr);
   merge_stream<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, prefix, static_cast<uint16_t*>(out), n, hq, hkv, g,
                                                      total_waves, ap);
 }

@@ -95,8 +95,7 @@ __global__ __launch_bounds__(256) void append_step_kernel(T* __restrict__ k_pool
 // the row forward, as append_step_kernel does.
 template <bool I8>
 __global__ __launch_bounds__(256) void append_codes_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                                                         const float* __restrict__ k_scale,
-                                                         const float* __restrict__ v_scale,
+                                                         const float* __restrict__ scales,
                                                          const uint16_t* __restrict__ k_new,
                                                          const uint16_t* __restrict__ v_new,
                                                          const int32_t* __restrict__ slot_mapping, int num_tokens,
@@ -122,7 +121,8 @@ __global__ __launch_bounds__(256) void append_codes_kernel(uint8_t* __restrict__
     }
   }
   const int64_t head = pb * hkv + j;
-  const float ks = k_scale[head], vs = v_scale[head];
+  const float2 kvs = *reinterpret_cast<const float2*>(scales + 2 * head);  // [num_blocks][Hkv][2]
+  const float ks = kvs.x, vs = kvs.y;
   const int e0 = c4 * 4;  // first element
   const int64_t src = (t * hkv + j) * d + e0;
   const uint2 kin = *reinterpret_cast<const uint2*>(k_new + src);
@@ -140,24 +140,24 @@ __global__ __launch_bounds__(256) void append_codes_kernel(uint8_t* __restrict__
   *reinterpret_cast<uint32_t*>(v_pool + dst) = vw;
 }
 
-// grid = (ceil((2 * n16 + 2 * scales_per_block) / 256), num_pairs, num_layers);
-// each thread moves 16 bytes of a block image, or one of the block's (KV
-// head) scales when the pools hold FP8 codes (scales_per_block = Hkv, else 0).
+// grid = (ceil((2 * n16 + scales_per_block) / 256), num_pairs, num_layers);
+// each thread moves 16 bytes of a block image, or one of the block's scales
+// when the pools hold one-byte codes (scales [num_blocks][Hkv][2]:
+// scales_per_block = 2 Hkv, else 0).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                           const int32_t* __restrict__ pairs, int64_t block_bytes,
                                                           int num_blocks, int64_t layer_stride_bytes,
-                                                          float* __restrict__ k_scale, float* __restrict__ v_scale,
-                                                          int scales_per_block, int64_t scale_layer_stride) {
+                                                          float* __restrict__ scales, int scales_per_block,
+                                                          int64_t scale_layer_stride) {
   const int64_t n16 = block_bytes / 16;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= 2 * n16 + 2 * scales_per_block) return;
+  if (idx >= 2 * n16 + scales_per_block) return;
   const int32_t src = pairs[2 * blockIdx.y];
   const int32_t dst = pairs[2 * blockIdx.y + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
   if (idx >= 2 * n16) {
-    const int64_t i = idx - 2 * n16;
-    float* sc = (i < scales_per_block ? k_scale : v_scale) + static_cast<int64_t>(blockIdx.z) * scale_layer_stride;
-    const int64_t h = i < scales_per_block ? i : i - scales_per_block;
+    const int64_t h = idx - 2 * n16;
+    float* sc = scales + static_cast<int64_t>(blockIdx.z) * scale_layer_stride;
     sc[static_cast<int64_t>(dst) * scales_per_block + h] = sc[static_cast<int64_t>(src) * scales_per_block + h];
     return;
   }
@@ -173,26 +173,23 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
 // src of the source pool to block dst of the destination pool, in every
 // layer.  Either pool may be device memory or pinned host memory mapped for
 // the device (then each 16-byte access crosses PCIe).
-// grid = (ceil((2 * n16 + 2 * scales_per_block) / 256), num_pairs, num_layers).
+// grid = (ceil((2 * n16 + scales_per_block) / 256), num_pairs, num_layers).
 __global__ __launch_bounds__(256) void swap_blocks_kernel(
     uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, const uint8_t* __restrict__ src_k,
     const uint8_t* __restrict__ src_v, const int32_t* __restrict__ pairs, int64_t block_bytes, int src_blocks,
-    int dst_blocks, int64_t src_layer_bytes, int64_t dst_layer_bytes, float* __restrict__ dst_ks,
-    float* __restrict__ dst_vs, const float* __restrict__ src_ks, const float* __restrict__ src_vs,
-    int scales_per_block, int64_t src_scale_layer, int64_t dst_scale_layer) {
+    int dst_blocks, int64_t src_layer_bytes, int64_t dst_layer_bytes, float* __restrict__ dst_sc,
+    const float* __restrict__ src_sc, int scales_per_block, int64_t src_scale_layer, int64_t dst_scale_layer) {
   const int64_t n16 = block_bytes / 16;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= 2 * n16 + 2 * scales_per_block) return;
+  if (idx >= 2 * n16 + scales_per_block) return;
   const int32_t src = pairs[2 * blockIdx.y];
   const int32_t dst = pairs[2 * blockIdx.y + 1];
   if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const int64_t layer = blockIdx.z;
   if (idx >= 2 * n16) {
-    const int64_t i = idx - 2 * n16;
-    const bool key = i < scales_per_block;
-    const int64_t h = key ? i : i - scales_per_block;
-    const float* ss = (key ? src_ks : src_vs) + layer * src_scale_layer;
-    float* ds = (key ? dst_ks : dst_vs) + layer * dst_scale_layer;
+    const int64_t h = idx - 2 * n16;
+    const float* ss = src_sc + layer * src_scale_layer;
+    float* ds = dst_sc + layer * dst_scale_layer;
     ds[static_cast<int64_t>(dst) * scales_per_block + h] = ss[static_cast<int64_t>(src) * scales_per_block + h];
     return;
   }
@@ -290,8 +287,8 @@ extern "C" int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst
   copy_blocks_kernel<<<dim3(static_cast<uint32_t>(gx), num_pairs, num_layers), dim3(256), 0,
                        static_cast<hipStream_t>(stream)>>>(static_cast<uint8_t*>(k_pool),
                                                           static_cast<uint8_t*>(v_pool), src_dst_pairs,
-                                                          block_bytes, num_blocks, layer_stride_bytes, nullptr,
-                                                          nullptr, 0, 0);
+                                                          block_bytes, num_blocks, layer_stride_bytes, nullptr, 0,
+                                                          0);
   return launch_status();
 }
 
@@ -299,25 +296,26 @@ namespace pa {
 namespace {
 
 template <bool I8>
-int append_codes(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+int append_codes(void* k_pool, void* v_pool, const float* scales, const void* k_new,
                  const void* v_new, const int32_t* slot_mapping, int num_tokens, int Hkv, int d_head, int block_size,
                  int num_blocks, void* stream) {
   if (num_tokens < 0 || num_blocks < 0 || Hkv <= 0 || d_head <= 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
   if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
-  if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!k_pool || !v_pool || !scales || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(scales) % 8 != 0) return PA_ERR_INVALID_ARG;
   const int64_t threads = static_cast<int64_t>(num_tokens) * Hkv * (d_head / 4);
   const int64_t grid = (threads + 255) / 256;
   if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
   append_codes_kernel<I8><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scale, v_scale,
+      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), scales,
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, num_tokens, Hkv, d_head,
       block_size, static_cast<int64_t>(num_blocks) * block_size, nullptr, nullptr, 0);
   return launch_status();
 }
 
 template <bool I8>
-int append_step_codes(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale, const void* k_new,
+int append_step_codes(void* k_pool, void* v_pool, const float* scales, const void* k_new,
                       const void* v_new, const int32_t* slot_mapping, int32_t* block_tables, int32_t* context_lens,
                       int num_seqs, int max_blocks_per_seq, int Hkv, int d_head, int block_size, int num_blocks,
                       void* stream) {
@@ -325,14 +323,14 @@ int append_step_codes(void* k_pool, void* v_pool, const float* k_scale, const fl
   if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (max_blocks_per_seq < 1) return PA_ERR_INVALID_ARG;
-  if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !slot_mapping || !block_tables ||
-      !context_lens)
+  if (!k_pool || !v_pool || !scales || !k_new || !v_new || !slot_mapping || !block_tables || !context_lens)
     return PA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(scales) % 8 != 0) return PA_ERR_INVALID_ARG;
   const int64_t threads = static_cast<int64_t>(num_seqs) * Hkv * (d_head / 4);
   const int64_t grid = (threads + 255) / 256;
   if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
   append_codes_kernel<I8><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scale, v_scale,
+      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), scales,
       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, num_seqs, Hkv, d_head,
       block_size, static_cast<int64_t>(num_blocks) * block_size, block_tables, context_lens, max_blocks_per_seq);
   return launch_status();
@@ -341,39 +339,39 @@ int append_step_codes(void* k_pool, void* v_pool, const float* k_scale, const fl
 }  // namespace
 }  // namespace pa
 
-extern "C" int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+extern "C" int pa_append_kv_fp8(void* k_pool, void* v_pool, const float* scales,
                                 const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
                                 int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
-  return pa::append_codes<false>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, num_tokens, Hkv,
+  return pa::append_codes<false>(k_pool, v_pool, scales, k_new, v_new, slot_mapping, num_tokens, Hkv,
                                  d_head, block_size, num_blocks, stream);
 }
 
-extern "C" int pa_append_kv_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+extern "C" int pa_append_kv_int8(void* k_pool, void* v_pool, const float* scales,
                                  const void* k_new, const void* v_new, const int32_t* slot_mapping, int num_tokens,
                                  int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
-  return pa::append_codes<true>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, num_tokens, Hkv,
+  return pa::append_codes<true>(k_pool, v_pool, scales, k_new, v_new, slot_mapping, num_tokens, Hkv,
                                 d_head, block_size, num_blocks, stream);
 }
 
-extern "C" int pa_append_step_fp8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+extern "C" int pa_append_step_fp8(void* k_pool, void* v_pool, const float* scales,
                                   const void* k_new, const void* v_new, const int32_t* slot_mapping,
                                   int32_t* block_tables, int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
                                   int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
-  return pa::append_step_codes<false>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables,
+  return pa::append_step_codes<false>(k_pool, v_pool, scales, k_new, v_new, slot_mapping, block_tables,
                                       context_lens, num_seqs, max_blocks_per_seq, Hkv, d_head, block_size, num_blocks,
                                       stream);
 }
 
-extern "C" int pa_append_step_int8(void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+extern "C" int pa_append_step_int8(void* k_pool, void* v_pool, const float* scales,
                                    const void* k_new, const void* v_new, const int32_t* slot_mapping,
                                    int32_t* block_tables, int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
                                    int Hkv, int d_head, int block_size, int num_blocks, void* stream) {
-  return pa::append_step_codes<true>(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping, block_tables,
+  return pa::append_step_codes<true>(k_pool, v_pool, scales, k_new, v_new, slot_mapping, block_tables,
                                      context_lens, num_seqs, max_blocks_per_seq, Hkv, d_head, block_size, num_blocks,
                                      stream);
 }
 
-extern "C" int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+extern "C" int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* scales,
                                   const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size,
                                   int num_blocks, int num_layers, int64_t layer_stride_elems,
                                   int64_t scale_layer_stride, void* stream) {
@@ -382,25 +380,25 @@ extern "C" int pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, fl
     return PA_ERR_INVALID_ARG;
   if (!shape_ok(Hkv, d_head, block_size, PA_BF16)) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
-  if (!k_pool || !v_pool || !k_scale || !v_scale || !src_dst_pairs) return PA_ERR_INVALID_ARG;
+  if (!k_pool || !v_pool || !scales || !src_dst_pairs) return PA_ERR_INVALID_ARG;
   if (num_pairs > 65535 || num_layers > 65535) return PA_ERR_UNSUPPORTED;
   const int64_t block_bytes = static_cast<int64_t>(Hkv) * d_head * block_size;
   if (num_layers > 1 && (layer_stride_elems < static_cast<int64_t>(num_blocks) * block_bytes ||
-                         scale_layer_stride < static_cast<int64_t>(num_blocks) * Hkv))
+                         scale_layer_stride < static_cast<int64_t>(num_blocks) * Hkv * 2))
     return PA_ERR_INVALID_ARG;
-  const int64_t gx = (2 * (block_bytes / 16) + 2 * Hkv + 255) / 256;
+  const int64_t gx = (2 * (block_bytes / 16) + 2 * Hkv + 255) / 256;  // images, then 2 Hkv scales
   copy_blocks_kernel<<<dim3(static_cast<uint32_t>(gx), num_pairs, num_layers), dim3(256), 0,
                        static_cast<hipStream_t>(stream)>>>(
       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), src_dst_pairs, block_bytes, num_blocks,
-      num_layers > 1 ? layer_stride_elems : 0, k_scale, v_scale, Hkv, num_layers > 1 ? scale_layer_stride : 0);
+      num_layers > 1 ? layer_stride_elems : 0, scales, 2 * Hkv, num_layers > 1 ? scale_layer_stride : 0);
   return launch_status();
 }
 
 namespace {
 int swap_impl(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs, int num_pairs,
               int Hkv, int d_head, int block_size, int elem, int src_blocks, int dst_blocks, int num_layers,
-              int64_t src_layer_elems, int64_t dst_layer_elems, float* dst_ks, float* dst_vs, const float* src_ks,
-              const float* src_vs, int64_t src_scale_layer, int64_t dst_scale_layer, void* stream) {
+              int64_t src_layer_elems, int64_t dst_layer_elems, float* dst_sc, const float* src_sc,
+              int64_t src_scale_layer, int64_t dst_scale_layer, void* stream) {
   using namespace pa;
   if (num_pairs < 0 || src_blocks < 0 || dst_blocks < 0 || num_layers <= 0 || Hkv <= 0 || d_head <= 0 ||
       block_size <= 0)
@@ -415,18 +413,18 @@ int swap_impl(void* dst_k, void* dst_v, const void* src_k, const void* src_v, co
   if (num_layers > 1 && (src_layer_elems < static_cast<int64_t>(src_blocks) * block_elems ||
                          dst_layer_elems < static_cast<int64_t>(dst_blocks) * block_elems))
     return PA_ERR_INVALID_ARG;
-  const bool scales = src_ks != nullptr;
+  const bool scales = src_sc != nullptr;
+  const int spb = scales ? 2 * Hkv : 0;  // [num_blocks][Hkv][2]
   if (scales && num_layers > 1 &&
-      (src_scale_layer < static_cast<int64_t>(src_blocks) * Hkv || dst_scale_layer < static_cast<int64_t>(dst_blocks) * Hkv))
+      (src_scale_layer < static_cast<int64_t>(src_blocks) * spb || dst_scale_layer < static_cast<int64_t>(dst_blocks) * spb))
     return PA_ERR_INVALID_ARG;
-  const int spb = scales ? Hkv : 0;
-  const int64_t gx = (2 * (block_bytes / 16) + 2 * spb + 255) / 256;
+  const int64_t gx = (2 * (block_bytes / 16) + spb + 255) / 256;
   swap_blocks_kernel<<<dim3(static_cast<uint32_t>(gx), num_pairs, num_layers), dim3(256), 0,
                        static_cast<hipStream_t>(stream)>>>(
       static_cast<uint8_t*>(dst_k), static_cast<uint8_t*>(dst_v), static_cast<const uint8_t*>(src_k),
       static_cast<const uint8_t*>(src_v), pairs, block_bytes, src_blocks, dst_blocks,
-      num_layers > 1 ? src_layer_elems * elem : 0, num_layers > 1 ? dst_layer_elems * elem : 0, dst_ks, dst_vs, src_ks,
-      src_vs, spb, num_layers > 1 ? src_scale_layer : 0, num_layers > 1 ? dst_scale_layer : 0);
+      num_layers > 1 ? src_layer_elems * elem : 0, num_layers > 1 ? dst_layer_elems * elem : 0, dst_sc, src_sc, spb,
+      num_layers > 1 ? src_scale_layer : 0, num_layers > 1 ? dst_scale_layer : 0);
   return launch_status();
 }
 }  // namespace
@@ -439,40 +437,37 @@ extern "C" int pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* sr
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
   return swap_impl(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, src_dst_pairs, num_pairs, Hkv, d_head, block_size,
                    elem_bytes(dtype), src_num_blocks, dst_num_blocks, num_layers, src_layer_stride_elems,
-                   dst_layer_stride_elems, nullptr, nullptr, nullptr, nullptr, 0, 0, stream);
+                   dst_layer_stride_elems, nullptr, nullptr, 0, 0, stream);
 }
 
-extern "C" int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
-                                  const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
-                                  const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv,
+extern "C" int pa_swap_blocks_fp8(void* dst_k_pool, void* dst_v_pool, float* dst_scales, const void* src_k_pool,
+                                  const void* src_v_pool, const float* src_scales, const int32_t* src_dst_pairs, int num_pairs, int Hkv,
                                   int d_head, int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
                                   int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems,
                                   int64_t src_scale_layer_stride, int64_t dst_scale_layer_stride, void* stream) {
   using namespace pa;
-  if (num_pairs > 0 && (!dst_k_scale || !dst_v_scale || !src_k_scale || !src_v_scale)) return PA_ERR_INVALID_ARG;
+  if (num_pairs > 0 && (!dst_scales || !src_scales)) return PA_ERR_INVALID_ARG;
   return swap_impl(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, src_dst_pairs, num_pairs, Hkv, d_head, block_size,
                    1, src_num_blocks, dst_num_blocks, num_layers, src_layer_stride_elems, dst_layer_stride_elems,
-                   dst_k_scale, dst_v_scale, src_k_scale, src_v_scale, src_scale_layer_stride, dst_scale_layer_stride,
+                   dst_scales, src_scales, src_scale_layer_stride, dst_scale_layer_stride,
                    stream);
 }
 
 // An INT8 cache moves as an FP8 cache does: one-byte codes and their scales.
-extern "C" int pa_copy_blocks_int8(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+extern "C" int pa_copy_blocks_int8(void* k_pool, void* v_pool, float* scales,
                                    const int32_t* src_dst_pairs, int num_pairs, int Hkv, int d_head, int block_size,
                                    int num_blocks, int num_layers, int64_t layer_stride_elems,
                                    int64_t scale_layer_stride, void* stream) {
-  return pa_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src_dst_pairs, num_pairs, Hkv, d_head, block_size,
+  return pa_copy_blocks_fp8(k_pool, v_pool, scales, src_dst_pairs, num_pairs, Hkv, d_head, block_size,
                             num_blocks, num_layers, layer_stride_elems, scale_layer_stride, stream);
 }
 
-extern "C" int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_k_scale, float* dst_v_scale,
-                                   const void* src_k_pool, const void* src_v_pool, const float* src_k_scale,
-                                   const float* src_v_scale, const int32_t* src_dst_pairs, int num_pairs, int Hkv,
+extern "C" int pa_swap_blocks_int8(void* dst_k_pool, void* dst_v_pool, float* dst_scales, const void* src_k_pool,
+                                   const void* src_v_pool, const float* src_scales, const int32_t* src_dst_pairs, int num_pairs, int Hkv,
                                    int d_head, int block_size, int src_num_blocks, int dst_num_blocks, int num_layers,
                                    int64_t src_layer_stride_elems, int64_t dst_layer_stride_elems,
                                    int64_t src_scale_layer_stride, int64_t dst_scale_layer_stride, void* stream) {
-  return pa_swap_blocks_fp8(dst_k_pool, dst_v_pool, dst_k_scale, dst_v_scale, src_k_pool, src_v_pool, src_k_scale,
-                            src_v_scale, src_dst_pairs, num_pairs, Hkv, d_head, block_size, src_num_blocks,
+  return pa_swap_blocks_fp8(dst_k_pool, dst_v_pool, dst_scales, src_k_pool, src_v_pool, src_scales, src_dst_pairs, num_pairs, Hkv, d_head, block_size, src_num_blocks,
                             dst_num_blocks, num_layers, src_layer_stride_elems, dst_layer_stride_elems,
                             src_scale_layer_stride, dst_scale_layer_stride, stream);
 }

@@ -15,4 +15,4 @@ extern "C" const char* pa_status_string(int status) {
   }
 }
 
-extern "C" int pa_version(void) { return 1; }
+extern "C" int pa_version(void) { return 2; }

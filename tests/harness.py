@@ -48,14 +48,22 @@ class DecodeCase:
     tables_dev: torch.Tensor
     lens_dev: torch.Tensor
     scale: float
-    k_scale: Optional[torch.Tensor] = None   # FP8 or INT8 cache: float32 [nb][Hkv] device scales
-    v_scale: Optional[torch.Tensor] = None
+    scales: Optional[torch.Tensor] = None    # FP8 or INT8 cache: float32 [nb][Hkv][2] (key, value) device scales
     codes: str = ""                          # "e4m3" or "int8" for a cache of one-byte codes
 
     @property
     def fp8(self):
         """The cache holds one-byte codes with scales (E4M3 or INT8)."""
-        return self.k_scale is not None
+        return self.scales is not None
+
+    @property
+    def k_scale(self):
+        """Key scales [nb][Hkv]: a view into ``scales`` (writes go through)."""
+        return self.scales[..., 0]
+
+    @property
+    def v_scale(self):
+        return self.scales[..., 1]
 
     @property
     def max_ctx(self):
@@ -123,19 +131,18 @@ def make_case(w: synth.Workload, lens: Optional[Sequence[int]] = None, *, hq=Non
         kshape, vshape = pa.pool_shapes(num_blocks, hkv, d, bs, 1)
         k = fill(torch.empty(kshape, dtype=torch.uint8, device=device), seed * 10 + 1)
         v = fill(torch.empty(vshape, dtype=torch.uint8, device=device), seed * 10 + 2)
-        ks = scales(num_blocks, hkv, w.value_scale, seed * 10 + 4, device)
-        vs = scales(num_blocks, hkv, w.value_scale, seed * 10 + 5, device)
+        sc = torch.stack([scales(num_blocks, hkv, w.value_scale, seed * 10 + 4, device),
+                          scales(num_blocks, hkv, w.value_scale, seed * 10 + 5, device)], -1).contiguous()
         if poison:  # NaN (E4M3) or -128 (INT8) codes in unused blocks and tail slots, NaN scales on unused blocks
             poison_unused_(k, v, tables, lens, bs, value=0x80 if int8 else 0x7F)
             used = torch.zeros(num_blocks, dtype=torch.bool)
             for row, s in zip(tables, lens):
                 used[torch.as_tensor(row[: -(-int(s) // bs)], dtype=torch.long)] = True
-            ks[~used.to(device)] = float("nan")
-            vs[~used.to(device)] = float("nan")
+            sc[~used.to(device)] = float("nan")
         q = synth.randn((len(lens), hq, d), torch.bfloat16, w.value_scale, seed * 10 + 3, device)
         return DecodeCase(w, lens, hq, hkv, d, bs, torch.uint8, num_blocks, max_blocks, bm, model, tables, k, v, q,
                           torch.from_numpy(tables).to(device), torch.tensor(lens, dtype=torch.int32, device=device),
-                          1.0 / math.sqrt(d), ks, vs, "int8" if int8 else "e4m3")
+                          1.0 / math.sqrt(d), sc, "int8" if int8 else "e4m3")
     elem = torch.tensor([], dtype=dtype).element_size()
     kshape, vshape = pa.pool_shapes(num_blocks, hkv, d, bs, elem)
     if layers > 1:
@@ -166,7 +173,7 @@ def run_decode(case: DecodeCase, layer: Optional[int] = None, q=None, out=None, 
     max_ctx = case.max_ctx if max_ctx is None else max_ctx
     if case.fp8:
         dec = pa.pa_decode_int8 if case.codes == "int8" else pa.pa_decode_fp8
-        dec(out, q, k, v, case.k_scale, case.v_scale, tables_dev, lens_dev, case.scale, max_ctx)
+        dec(out, q, k, v, case.scales, tables_dev, lens_dev, case.scale, max_ctx)
     else:
         pa.pa_decode(out, q, k, v, tables_dev, lens_dev, case.scale, max_ctx)
     return out
@@ -248,3 +255,10 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, what: str, max_abs=MAX_ABS,
     print(f"[parity] {what}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
     assert ma <= max_abs and rl <= rel_l2, f"{what}: max_abs {ma:.3e} rel_l2 {rl:.3e}"
     return ma, rl
+
+
+def paired(k_scale: torch.Tensor, v_scale: torch.Tensor):
+    """One contiguous float32 scale array [..][Hkv][2] (key, value), the layout the library reads, and views of its
+    key and value halves (writes through the views land in the array)."""
+    sc = torch.stack([k_scale, v_scale], -1).contiguous()
+    return sc, sc[..., 0], sc[..., 1]

@@ -60,7 +60,7 @@ def test_binding_exposes_entry_points_with_the_c_names():
 
 def test_status_strings_and_version():
     import paged_kv_cache_124_amd as pa
-    assert pa.lib.pa_version() == 1
+    assert pa.lib.pa_version() == 2
     assert pa.lib.pa_status_string(0) == b"ok"
     assert pa.lib.pa_status_string(3) == b"no free blocks in the pool"
     assert pa.lib.pa_status_string(99) == b"unknown status"
@@ -155,31 +155,53 @@ def test_pool_shapes_follow_the_header_layout():
 def test_fp8_host_validation():
     import paged_kv_cache_124_amd as pa
     L = pa.lib
-    # pa_decode_fp8(out, q, k, v, k_scale, v_scale, tables, lens, n, Hq, Hkv, d, B, scale, maxb, maxctx, nb, ws, wsb, stream)
+    # pa_decode_fp8(out, q, k, v, scales, tables, lens, n, Hq, Hkv, d, B, scale, maxb, maxctx, nb, ws, wsb, stream)
     need = pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, pa.PA_FP8_E4M3)
     assert need > 0 and need == pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 8192, pa.PA_FP8_E4M3)
     assert pa.pa_decode_partition_tokens(64, 32, 8, 128, 16, 4096, pa.PA_FP8_E4M3) == 0
 
-    def dec(n=4, hq=32, hkv=8, d=128, bs=16, ks=FAKE, ws=FAKE, wsb=None):
+    def dec(n=4, hq=32, hkv=8, d=128, bs=16, sc=FAKE, ws=FAKE, wsb=None, fn=L.pa_decode_fp8):
         wsb = need if wsb is None else wsb
-        return L.pa_decode_fp8(FAKE, FAKE, FAKE, FAKE, ks, FAKE, FAKE, FAKE, n, hq, hkv, d, bs, 0.088, 256, 4096,
-                               1000, ws, wsb, NUL)
-    assert dec(n=0) == 0
-    assert dec(hq=30) == 1
-    assert dec(hq=64, hkv=2) == 2        # 32 query heads per KV head: not served
-    assert dec(d=96) == 2 and dec(bs=64) == 2
-    assert dec(ks=NUL) == 1
-    assert dec(ws=NUL) == 6 and dec(wsb=16) == 6
-    # pa_append_kv_fp8(k, v, k_scale, v_scale, k_new, v_new, slots, T, Hkv, d, B, nb, stream)
-    assert L.pa_append_kv_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, NUL) == 0
-    assert L.pa_append_kv_fp8(FAKE, FAKE, NUL, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 100, NUL) == 1
-    assert L.pa_append_kv_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 16, 100, NUL) == 2
-    # pa_copy_blocks_fp8(k, v, k_scale, v_scale, pairs, P, Hkv, d, B, nb, layers, stride, scale_stride, stream)
-    assert L.pa_copy_blocks_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, 1, 0, 0, NUL) == 0
-    assert L.pa_copy_blocks_fp8(FAKE, FAKE, NUL, FAKE, FAKE, 2, 8, 128, 16, 100, 1, 0, 0, NUL) == 1
-    full = 100 * 8 * 128 * 16
-    assert L.pa_copy_blocks_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 100, 2, full, 10, NUL) == 1
+        return fn(FAKE, FAKE, FAKE, FAKE, sc, FAKE, FAKE, n, hq, hkv, d, bs, 0.088, 256, 4096, 1000, ws, wsb, NUL)
+    for fn in (L.pa_decode_fp8, L.pa_decode_int8):
+        assert dec(n=0, fn=fn) == 0
+        assert dec(hq=30, fn=fn) == 1
+        assert dec(hq=64, hkv=2, fn=fn) == 2        # 32 query heads per KV head: not served
+        assert dec(d=96, fn=fn) == 2 and dec(bs=64, fn=fn) == 2
+        assert dec(sc=NUL, fn=fn) == 1
+        assert dec(sc=ctypes.c_void_p(0x1004), fn=fn) == 1   # (key, value) pairs are read 8 bytes at a time
+        assert dec(ws=NUL, fn=fn) == 6 and dec(wsb=16, fn=fn) == 6
+    # pa_append_kv_fp8(k, v, scales, k_new, v_new, slots, T, Hkv, d, B, nb, stream)
+    for fn in (L.pa_append_kv_fp8, L.pa_append_kv_int8):
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, NUL) == 0
+        assert fn(FAKE, FAKE, NUL, FAKE, FAKE, FAKE, 4, 8, 128, 16, 100, NUL) == 1
+        assert fn(FAKE, FAKE, ctypes.c_void_p(0x1004), FAKE, FAKE, FAKE, 4, 8, 128, 16, 100, NUL) == 1
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 16, 100, NUL) == 2
+    # pa_copy_blocks_fp8(k, v, scales, pairs, P, Hkv, d, B, nb, layers, stride, scale_stride, stream)
+    for fn in (L.pa_copy_blocks_fp8, L.pa_copy_blocks_int8):
+        assert fn(FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, 1, 0, 0, NUL) == 0
+        assert fn(FAKE, FAKE, NUL, FAKE, 2, 8, 128, 16, 100, 1, 0, 0, NUL) == 1
+        full = 100 * 8 * 128 * 16
+        assert fn(FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 100, 2, full, 100 * 8, NUL) == 1   # scale stride < nb*Hkv*2
+    # pa_swap_blocks_fp8(dk, dv, dsc, sk, sv, ssc, pairs, P, Hkv, d, B, src_nb, dst_nb, layers, 4 strides, stream)
+    for fn in (L.pa_swap_blocks_fp8, L.pa_swap_blocks_int8):
+        assert fn(FAKE, FAKE, NUL, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 10, 10, 1, 0, 0, 0, 0, NUL) == 1
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 10, 10, 1, 0, 0, 0, 0, NUL) == 0
 
+
+def test_fp8_binding_takes_one_interleaved_scale_array():
+    """The code-cache bindings take scales as one contiguous float32 [nb][Hkv][2] array (key, value)."""
+    import paged_kv_cache_124_amd as pa
+    kshape, vshape = pa.pool_shapes(4, 2, 64, 16, 1)
+    k = torch.zeros(kshape, dtype=torch.uint8)
+    v = torch.zeros(vshape, dtype=torch.uint8)
+    q = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    tables = torch.zeros(1, 4, dtype=torch.int32)
+    lens = torch.zeros(1, dtype=torch.int32)
+    for bad in (torch.zeros(4, 2), torch.zeros(4, 2, 2).transpose(1, 2).contiguous().transpose(1, 2),
+                torch.zeros(4, 2, 2, dtype=torch.float64)):
+        with pytest.raises(ValueError):
+            pa.pa_decode_fp8(torch.zeros_like(q), q, k, v, bad, tables, lens, 0.125, 64)
 
 
 def test_check_batch_host_validation():

@@ -97,7 +97,7 @@ def test_workspace_contents_do_not_matter(codes):
     out = torch.empty_like(c.q)
     if codes != "bf16":
         make = pa.pa_decode_int8_args if codes == "int8" else pa.pa_decode_fp8_args
-        args, ws = make(out, c.q, c.k, c.v, c.k_scale, c.v_scale, c.tables_dev, c.lens_dev, c.scale, c.max_ctx)
+        args, ws = make(out, c.q, c.k, c.v, c.scales, c.tables_dev, c.lens_dev, c.scale, c.max_ctx)
         call = pa.lib.pa_decode_int8 if codes == "int8" else pa.lib.pa_decode_fp8
     else:
         args, ws = pa.pa_decode_args(out, c.q, c.k, c.v, c.tables_dev, c.lens_dev, c.scale, c.max_ctx)

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import synth
-from harness import assert_close, fp8_logical, make_case, oracle_outputs, run_decode
+from harness import assert_close, fp8_logical, make_case, oracle_outputs, paired, run_decode
 from oracle import fp8 as OF
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +47,7 @@ def test_append_fp8_bit_exact(d, bs):
     v = synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8), 12).cuda()
     ks = synth.fp8_scales(nb, hkv, 0.09, 13, "cuda")
     vs = synth.fp8_scales(nb, hkv, 0.09, 14, "cuda")
+    sc, ks, vs = paired(ks, vs)
     # a few blocks with scales the rule maps to NaN codes, and power-of-two scales for exact midpoints
     ks[5, 1] = 0.0
     vs[6, 2] = -1.0
@@ -65,7 +66,7 @@ def test_append_fp8_bit_exact(d, bs):
     kn[11:14] *= 400.0                               # beyond 448 after scaling: saturation
     k_or, v_or = _logical_pools(k, v)
     ks_or, vs_or = ks.cpu().double().numpy(), vs.cpu().double().numpy()
-    pa.pa_append_kv_fp8(k, v, ks, vs, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda())
+    pa.pa_append_kv_fp8(k, v, sc, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()
     OF.append_kv(k_or, v_or, ks_or, vs_or, kn.float().numpy().astype(np.float64),
                  vn.float().numpy().astype(np.float64), slots)
@@ -89,10 +90,11 @@ def test_copy_blocks_fp8_bit_exact():
         v = synth.fill_fp8_codes_(torch.empty((layers,) + vshape, dtype=torch.uint8), 22).cuda()
         ks = synth.fp8_scales(layers * nb, hkv, 0.09, 23, "cuda").reshape(layers, nb, hkv)
         vs = synth.fp8_scales(layers * nb, hkv, 0.09, 24, "cuda").reshape(layers, nb, hkv)
+        sc, ks, vs = paired(ks, vs)
         if layers == 1:
-            k, v, ks, vs = k[0], v[0], ks[0], vs[0]
+            k, v, sc, ks, vs = k[0], v[0], sc[0], ks[0], vs[0]
         k0, v0, ks0, vs0 = (t.cpu().numpy().copy() for t in (k, v, ks, vs))
-        pa.pa_copy_blocks_fp8(k, v, ks, vs, torch.from_numpy(pairs).cuda())
+        pa.pa_copy_blocks_fp8(k, v, sc, torch.from_numpy(pairs).cuda())
         torch.cuda.synchronize()
         want = [k0.copy(), v0.copy(), ks0.copy(), vs0.copy()]
         for src, dst in pairs[:4]:
@@ -191,7 +193,7 @@ def test_fp8_step_append_then_decode():
     vs = np.where(np.isnan(vs), 0.002, vs)
     kn = synth.randn((n, w.hkv, w.d), torch.bfloat16, w.value_scale, 1801, "cuda")
     vn = synth.randn((n, w.hkv, w.d), torch.bfloat16, w.value_scale, 1802, "cuda")
-    pa.pa_append_kv_fp8(c.k, c.v, c.k_scale, c.v_scale, kn, vn, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    pa.pa_append_kv_fp8(c.k, c.v, c.scales, kn, vn, torch.tensor(slots, dtype=torch.int32, device="cuda"))
     remap = {b: i for i, b in enumerate(used)}
     local = [remap[s // c.block_size] * c.block_size + s % c.block_size for s in mslots]
     OF.append_kv(kc, vc, ks, vs, kn.float().cpu().numpy().astype(np.float64),
@@ -231,6 +233,7 @@ def test_append_step_fp8_tracks_block_manager(d, bs):
     v = synth.fill_fp8_codes_(torch.empty(vshape, dtype=torch.uint8), 62).cuda()
     ks = synth.fp8_scales(nb, hkv, 0.09, 63, "cuda")
     vs = synth.fp8_scales(nb, hkv, 0.09, 64, "cuda")
+    sc, ks, vs = paired(ks, vs)
     order = synth.pop_order(nb, 7)
     bm = pa.BlockManager(nb, bs, order)
     model = BlockManagerModel(nb, bs, [int(x) for x in order])
@@ -255,10 +258,10 @@ def test_append_step_fp8_tracks_block_manager(d, bs):
         row_slots = np.full(n, -1, dtype=np.int32)
         row_slots[active] = slots
         if len(pairs):
-            pa.pa_copy_blocks_fp8(k, v, ks, vs, torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda())
+            pa.pa_copy_blocks_fp8(k, v, sc, torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda())
         kn = synth.randn((n, hkv, d), torch.bfloat16, 0.09, 1000 + step, "cuda")
         vn = synth.randn((n, hkv, d), torch.bfloat16, 0.09, 2000 + step, "cuda")
-        pa.pa_append_step_fp8(k, v, ks, vs, kn, vn, torch.from_numpy(row_slots).cuda(), d_tables, d_lens)
+        pa.pa_append_step_fp8(k, v, sc, kn, vn, torch.from_numpy(row_slots).cuda(), d_tables, d_lens)
         torch.cuda.synchronize()
         st, tables, lens = bm.build_batch(seqs, mb)
         assert st == 0

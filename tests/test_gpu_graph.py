@@ -33,7 +33,7 @@ def test_decode_graph_replays_match_eager(fp8):
 
     def make_args(out, q, ws=None, stream=None):
         if fp8:
-            return pa.pa_decode_fp8_args(out, q, c.k, c.v, c.k_scale, c.v_scale, c.tables_dev, c.lens_dev, c.scale,
+            return pa.pa_decode_fp8_args(out, q, c.k, c.v, c.scales, c.tables_dev, c.lens_dev, c.scale,
                                          c.max_ctx, workspace=ws, stream=stream)
         return pa.pa_decode_args(out, q, c.k, c.v, c.tables_dev, c.lens_dev, c.scale, c.max_ctx, workspace=ws,
                                  stream=stream)
@@ -153,10 +153,10 @@ def test_decode_step_codes_graph_runs_a_decode_loop(codes):
     vnB = torch.empty_like(knB)
     slotsB = torch.zeros(n, dtype=torch.int32, device="cuda")
     outB = torch.empty_like(c.q)
-    _, wsB = args_of(outB, qB, knB, vnB, kB, vB, c.k_scale, c.v_scale, slotsB, tB, lB, c.scale, max_ctx)
+    _, wsB = args_of(outB, qB, knB, vnB, kB, vB, c.scales, slotsB, tB, lB, c.scale, max_ctx)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        args, _ = args_of(outB, qB, knB, vnB, kB, vB, c.k_scale, c.v_scale, slotsB, tB, lB, c.scale, max_ctx,
+        args, _ = args_of(outB, qB, knB, vnB, kB, vB, c.scales, slotsB, tB, lB, c.scale, max_ctx,
                           workspace=wsB, stream=torch.cuda.current_stream())
         assert call(*args) == 0
     torch.cuda.synchronize()
@@ -174,7 +174,7 @@ def test_decode_step_codes_graph_runs_a_decode_loop(codes):
         q = synth.randn(tuple(c.q.shape), c.q.dtype, w.value_scale, 7300 + step, "cuda")
         kn = synth.randn((n, c.hkv, c.d), c.q.dtype, 0.09, 7400 + step, "cuda")
         vn = synth.randn((n, c.hkv, c.d), c.q.dtype, 0.09, 7500 + step, "cuda")
-        eager(outA, q, kn, vn, kA, vA, c.k_scale, c.v_scale, slots_t, tA, lA, c.scale, max_ctx)
+        eager(outA, q, kn, vn, kA, vA, c.scales, slots_t, tA, lA, c.scale, max_ctx)
         qB.copy_(q)
         knB.copy_(kn)
         vnB.copy_(vn)

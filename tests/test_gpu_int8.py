@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import synth
-from harness import assert_close, fp8_logical, make_case, oracle_outputs, run_decode
+from harness import assert_close, fp8_logical, make_case, oracle_outputs, paired, run_decode
 from oracle import int8 as OI
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +49,7 @@ def test_append_int8_bit_exact(d, bs):
     v = synth.fill_int8_codes_(torch.empty(vshape, dtype=torch.uint8), 32).cuda()
     ks = synth.int8_scales(nb, hkv, 0.09, 33, "cuda")
     vs = synth.int8_scales(nb, hkv, 0.09, 34, "cuda")
+    sc, ks, vs = paired(ks, vs)
     ks[5, 1] = 0.0  # scales the rule maps to code 0
     vs[6, 2] = -1.0
     ks[7, 0] = float("inf")
@@ -65,7 +66,7 @@ def test_append_int8_bit_exact(d, bs):
     kn[11:14] *= 30.0  # beyond 127 steps after scaling: clamped
     k_or, v_or = _logical_pools(k, v)
     ks_or, vs_or = ks.cpu().double().numpy(), vs.cpu().double().numpy()
-    pa.pa_append_kv_int8(k, v, ks, vs, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda())
+    pa.pa_append_kv_int8(k, v, sc, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()
     OI.append_kv(k_or, v_or, ks_or, vs_or, kn.float().numpy().astype(np.float64),
                  vn.float().numpy().astype(np.float64), slots)
@@ -91,10 +92,11 @@ def test_copy_and_swap_int8_bit_exact():
         v = synth.fill_int8_codes_(torch.empty((layers,) + vshape, dtype=torch.uint8), 42).cuda()
         ks = synth.int8_scales(layers * nb, hkv, 0.09, 43, "cuda").reshape(layers, nb, hkv)
         vs = synth.int8_scales(layers * nb, hkv, 0.09, 44, "cuda").reshape(layers, nb, hkv)
+        sc, ks, vs = paired(ks, vs)
         if layers == 1:
-            k, v, ks, vs = k[0], v[0], ks[0], vs[0]
+            k, v, sc, ks, vs = k[0], v[0], sc[0], ks[0], vs[0]
         k0, v0, ks0, vs0 = (t.cpu().numpy().copy() for t in (k, v, ks, vs))
-        pa.pa_copy_blocks_int8(k, v, ks, vs, torch.from_numpy(pairs).cuda())
+        pa.pa_copy_blocks_int8(k, v, sc, torch.from_numpy(pairs).cuda())
         torch.cuda.synchronize()
         want = [k0.copy(), v0.copy(), ks0.copy(), vs0.copy()]
         for src, dst in pairs[:4]:
@@ -106,15 +108,14 @@ def test_copy_and_swap_int8_bit_exact():
         for got, exp, name in zip((k, v, ks, vs), want, ("k", "v", "k_scale", "v_scale")):
             assert np.array_equal(got.cpu().numpy().view(np.uint8), exp.view(np.uint8)), f"{name} layers={layers}"
     # swap, on layer 0 of the stack: blocks 4, 9, 21 out to host blocks 0, 1, 2 and back into 10, 11, 12
-    k, v, ks, vs = k[0], v[0], ks[0], vs[0]
+    k, v, sc, ks, vs = k[0], v[0], sc[0], ks[0], vs[0]
     hk = torch.empty((3,) + tuple(k.shape[1:]), dtype=torch.uint8, pin_memory=True)
     hv = torch.empty((3,) + tuple(v.shape[1:]), dtype=torch.uint8, pin_memory=True)
-    hks = torch.empty((3, hkv), dtype=torch.float32, pin_memory=True)
-    hvs = torch.empty((3, hkv), dtype=torch.float32, pin_memory=True)
+    hsc = torch.empty((3, hkv, 2), dtype=torch.float32, pin_memory=True)
     out_pairs = torch.tensor([[4, 0], [9, 1], [21, 2]], dtype=torch.int32, device="cuda")
     in_pairs = torch.tensor([[0, 10], [1, 11], [2, 12]], dtype=torch.int32, device="cuda")
-    pa.pa_swap_blocks_int8(hk, hv, hks, hvs, k, v, ks, vs, out_pairs)
-    pa.pa_swap_blocks_int8(k, v, ks, vs, hk, hv, hks, hvs, in_pairs)
+    pa.pa_swap_blocks_int8(hk, hv, hsc, k, v, sc, out_pairs)
+    pa.pa_swap_blocks_int8(k, v, sc, hk, hv, hsc, in_pairs)
     torch.cuda.synchronize()
     for a, b in ((4, 10), (9, 11), (21, 12)):
         assert torch.equal(k[a], k[b]) and torch.equal(v[a], v[b])
@@ -186,6 +187,7 @@ def test_int8_steps_track_block_manager_and_decode(d, bs):
     v = synth.fill_int8_codes_(torch.empty(vshape, dtype=torch.uint8), 72).cuda()
     ks = synth.int8_scales(nb, hkv, 0.09, 73, "cuda")
     vs = synth.int8_scales(nb, hkv, 0.09, 74, "cuda")
+    sc, ks, vs = paired(ks, vs)
     order = synth.pop_order(nb, 9)
     bm = pa.BlockManager(nb, bs, order)
     model = BlockManagerModel(nb, bs, [int(x) for x in order])
@@ -210,11 +212,11 @@ def test_int8_steps_track_block_manager_and_decode(d, bs):
         row_slots = np.full(n, -1, dtype=np.int32)
         row_slots[active] = slots
         if len(pairs):
-            pa.pa_copy_blocks_int8(k, v, ks, vs, torch.from_numpy(np.ascontiguousarray(pairs, np.int32)).cuda())
+            pa.pa_copy_blocks_int8(k, v, sc, torch.from_numpy(np.ascontiguousarray(pairs, np.int32)).cuda())
             OI.copy_blocks(ek, ev, eks, evs, mpairs)
         kn = synth.randn((n, hkv, d), torch.bfloat16, 0.09, 7300 + step, "cuda")
         vn = synth.randn((n, hkv, d), torch.bfloat16, 0.09, 7400 + step, "cuda")
-        pa.pa_append_step_int8(k, v, ks, vs, kn, vn, torch.from_numpy(row_slots).cuda(), d_tables, d_lens)
+        pa.pa_append_step_int8(k, v, sc, kn, vn, torch.from_numpy(row_slots).cuda(), d_tables, d_lens)
         OI.append_kv(ek, ev, eks, evs, kn.float().cpu().numpy().astype(np.float64),
                      vn.float().cpu().numpy().astype(np.float64), row_slots)
         torch.cuda.synchronize()
@@ -226,7 +228,7 @@ def test_int8_steps_track_block_manager_and_decode(d, bs):
                                                                                          evs.astype(np.float32))
     q = synth.randn((n, hq, d), torch.bfloat16, 0.09, 7500, "cuda")
     out = torch.empty_like(q)
-    pa.pa_decode_int8(out, q, k, v, ks, vs, d_tables, d_lens, 1.0 / np.sqrt(d), int(lens.max()))
+    pa.pa_decode_int8(out, q, k, v, sc, d_tables, d_lens, 1.0 / np.sqrt(d), int(lens.max()))
     ref = OI.paged_decode(q.float().cpu().numpy().astype(np.float64), ek, ev, eks, evs, tables, lens.tolist(),
                           1.0 / np.sqrt(d))
     assert_close(out, ref, f"int8 steps d={d} bs={bs}")

@@ -69,13 +69,13 @@ def test_step_equals_append_then_decode(codes, d, bs):
     k2, v2, t2, l2 = _state(c)
     lens0 = c.lens_dev.cpu().numpy()
     out1 = torch.empty_like(c.q)
-    append(k1, v1, c.k_scale, c.v_scale, kn, vn, slots, t1, l1)
-    decode(out1, c.q, k1, v1, c.k_scale, c.v_scale, t1, l1, c.scale, max_ctx)
+    append(k1, v1, c.scales, kn, vn, slots, t1, l1)
+    decode(out1, c.q, k1, v1, c.scales, t1, l1, c.scale, max_ctx)
     out2 = torch.full_like(c.q, float("nan"))
     need = pa.pa_decode_workspace_bytes(len(c.lens), c.hq, c.hkv, d, bs, max_ctx,
                                         pa.PA_INT8 if codes == "int8" else pa.PA_FP8_E4M3)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # every word is written before it is read
-    step(out2, c.q, kn, vn, k2, v2, c.k_scale, c.v_scale, slots, t2, l2, c.scale, max_ctx, workspace=ws)
+    step(out2, c.q, kn, vn, k2, v2, c.scales, slots, t2, l2, c.scale, max_ctx, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(k1, k2) and torch.equal(v1, v2), "codes differ"
     assert torch.equal(t1, t2) and torch.equal(l1, l2), "tables / lengths differ"
@@ -108,7 +108,7 @@ def test_rows_without_a_block_attend_their_cached_tokens(codes):
     need = pa.pa_decode_workspace_bytes(len(c.lens), c.hq, c.hkv, d, bs, max_ctx,
                                         pa.PA_INT8 if codes == "int8" else pa.PA_FP8_E4M3)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    step(out, c.q, kn, vn, c.k, c.v, c.k_scale, c.v_scale, slots, c.tables_dev, c.lens_dev, c.scale, max_ctx,
+    step(out, c.q, kn, vn, c.k, c.v, c.scales, slots, c.tables_dev, c.lens_dev, c.scale, max_ctx,
          workspace=ws)
     torch.cuda.synchronize()
     lens1 = c.lens_dev.cpu().numpy()

@@ -161,21 +161,20 @@ def test_swap_fp8_cache():
     assert st == 0 and [tuple(p) for p in pairs.tolist()] == c.model.swap_out(group)[1]
     hk = torch.empty((H,) + tuple(c.k.shape[1:]), dtype=torch.uint8, pin_memory=True)
     hv = torch.empty((H,) + tuple(c.v.shape[1:]), dtype=torch.uint8, pin_memory=True)
-    hks = torch.empty((H, c.hkv), dtype=torch.float32, pin_memory=True)
-    hvs = torch.empty((H, c.hkv), dtype=torch.float32, pin_memory=True)
-    pa.pa_swap_blocks_fp8(hk, hv, hks, hvs, c.k, c.v, c.k_scale, c.v_scale, torch.from_numpy(pairs).cuda())
+    hsc = torch.empty((H, c.hkv, 2), dtype=torch.float32, pin_memory=True)
+    pa.pa_swap_blocks_fp8(hk, hv, hsc, c.k, c.v, c.scales, torch.from_numpy(pairs).cuda())
     torch.cuda.synchronize()
     src = torch.as_tensor(pairs[:, 0], dtype=torch.long, device="cuda")
     dst = torch.as_tensor(pairs[:, 1], dtype=torch.long)
     assert torch.equal(c.k.index_select(0, src).cpu(), hk.index_select(0, dst))
-    assert torch.equal(c.k_scale.index_select(0, src).cpu().view(torch.int32), hks.index_select(0, dst).view(torch.int32))
+    assert torch.equal(c.scales.index_select(0, src).cpu().view(torch.int32), hsc.index_select(0, dst).view(torch.int32))
     c.k.index_fill_(0, src, 0x7F)
     c.v.index_fill_(0, src, 0x7F)
     c.k_scale.index_fill_(0, src, float("nan"))
     c.v_scale.index_fill_(0, src, float("nan"))
     st, pin = c.bm.swap_in(group)
     assert st == 0 and [tuple(p) for p in pin.tolist()] == c.model.swap_in(group)[1]
-    pa.pa_swap_blocks_fp8(c.k, c.v, c.k_scale, c.v_scale, hk, hv, hks, hvs, torch.from_numpy(pin).cuda())
+    pa.pa_swap_blocks_fp8(c.k, c.v, c.scales, hk, hv, hsc, torch.from_numpy(pin).cuda())
     seqs = list(range(len(c.lens)))
     st, tables, lens = c.bm.build_batch(seqs, c.max_blocks)
     out1 = run_decode(c, tables_dev=torch.from_numpy(tables).cuda())
