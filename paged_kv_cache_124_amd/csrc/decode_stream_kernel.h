@@ -44,18 +44,34 @@ namespace {
 
 constexpr int kMaxSeqs = 3072;  // lengths and tile prefix sums live in LDS beside the stages
 
-// ---- FP8 (E4M3) cache ----------------------------------------------------------
+// ---- caches of one-byte codes (FP8 E4M3 or INT8) --------------------------------
 //
-// Codes are OCP E4M3; a stored code c stands for value(c) * scale, one fp32
-// scale per (block, KV head) for keys and one for values.  gfx950 converts
-// two codes to two bf16 in one instruction, exactly (every E4M3 value is a
-// bf16 value), so both products stay bf16 x bf16 MFMAs on the codes' values
-// and the scales are applied outside them: the key scale multiplies a
-// token's score, the value scale its probability in P.V (the weight sum uses
-// the unscaled probability).  A 64-token tile is two 32-token sub-tiles,
-// each computed as a bf16 tile is.
+// A stored code c stands for value(c) * scale, one fp32 scale per (block, KV
+// head) for keys and one for values.  Both products run as fp16 MFMAs on the
+// codes' values; the scales are applied outside them: the key scale
+// multiplies a token's score, the value scale its probability in P.V (the
+// weight sum uses the unscaled probability).
+//   FP8: gfx950 converts two E4M3 codes to two fp16 values in one
+//   instruction, exactly (every E4M3 value is an fp16 value).
+//   INT8: the fp16 number with high byte 0x64 and low byte c ^ 0x80 is
+//   1024 + (c + 128), exactly.  One byte permute builds two of them from a
+//   word of four codes and one XOR per word flips the four sign bits: 0.75
+//   instructions per code.  The common offset kI8Offset = 1152 comes out
+//   afterwards: from a score as 1152 times the sum of the head's fp16 query,
+//   from P.V as 1152 times the sum of the tile's P column, on the tile's own
+//   accumulator (so the offset never grows with the context).
+//   Q: each head's row is scaled by the power of two that puts its largest
+//   magnitude in [2^14, 2^15) before the fp16 conversion (exact for every
+//   bf16 value down to 2^-28 of that magnitude); the score takes the power
+//   back.
+//   P: with fp16's 11 significant bits one MFMA per product suffices.  Its
+//   range is kept by weighing p * (value scale / vref), vref the largest
+//   value scale of the segment so far -- raised tile by tile like the running
+//   maximum, the accumulator rescaled with it -- and the segment's output is
+//   multiplied by vref when it is written.
+// A 64-token tile is two 32-token sub-tiles under one online-softmax update.
 
-// Register image of a staged FP8 tile for lane (r, gq).
+// Register image of a staged tile of codes for lane (r, gq).
 template <int D>
 struct Buf8 {
   uint4 k[2][2][D / 64];     // [sub-tile][slab] key row 16 slab + r: the 16-byte chunks of d quarter gq
@@ -69,36 +85,83 @@ struct Sc8 {
   float k[2][2], v[2][2];  // [sub-tile][slab]
 };
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Eight codes (two words, lowest byte first) as eight bf16 values.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
+// The fp16 image of INT8 code c is c + kI8Offset.
+constexpr float kI8Offset = 1152.f;
 
-// INT8 cache: eight signed codes as eight bf16 values, exactly (|c| <= 128
-// fits bf16's 8 significant bits): a sign-extending byte-select convert to
-// fp32 per code and a pack per pair.
-__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(lo >> (8 * i))));
-    r[4 + i] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(hi >> (8 * i))));
-  }
-  return r;
-}
-
+// Eight codes (two words, lowest byte first) as eight fp16 values: the E4M3
+// values, or the INT8 codes plus kI8Offset.
 template <bool I8>
-__device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t lo, uint32_t hi) {
-  if constexpr (I8)
-    return i8x8_to_bf16(lo, hi);
-  else
-    return fp8x8_to_bf16(lo, hi);
+__device__ __forceinline__ f16x8 codes8_to_f16(uint32_t lo, uint32_t hi) {
+  if constexpr (I8) {
+    const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+    // selector bytes 0-3 take bytes of the flipped code word, 4 the byte 0x64
+    return __builtin_bit_cast(f16x8, uint4{__builtin_amdgcn_perm(0x64646464u, a, 0x04010400u),
+                                           __builtin_amdgcn_perm(0x64646464u, a, 0x04030402u),
+                                           __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u),
+                                           __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)});
+  } else {
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+}
+
+// Query operand of a tile of codes: lane (r, gq) holds head r's elements
+// d = gq D / 4 + 8 jj .. + 7 (the key chunks the lane holds), scaled by 2^k.
+template <int D>
+struct QOp16 {
+  f16x8 q[D / 32];
+  float unscale;  // 2^-k
+  float offset;   // INT8: kI8Offset times the sum of head r's fp16 elements
+};
+
+template <int D, bool I8>
+__device__ __forceinline__ void load_q16(QOp16<D>& qo, TilePos t, const uint16_t* __restrict__ q, int hq, int g,
+                                         int r, int gq) {
+  // padding columns r >= G read head 0 of the group; their results are never used
+  const uint16_t* qh = q + (static_cast<int64_t>(t.n) * hq + t.j * g + (r < g ? r : 0)) * D;
+  uint4 raw[D / 32];
+  float amax = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj) {
+    raw[jj] = *reinterpret_cast<const uint4*>(qh + gq * (D / 4) + 8 * jj);
+    const uint32_t w[4] = {raw[jj].x, raw[jj].y, raw[jj].z, raw[jj].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xffff0000u))));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  int ex = 0;
+  if (amax > 0.f && amax <= __FLT_MAX__) frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+  const int k = min(max(15 - ex, -126), 126);
+  const float up = ldexpf(1.f, k);
+  qo.unscale = ldexpf(1.f, -k);
+  float sum = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj) {
+    const uint32_t w[4] = {raw[jj].x, raw[jj].y, raw[jj].z, raw[jj].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 lo = static_cast<_Float16>(__uint_as_float(w[e] << 16) * up);
+      const _Float16 hi = static_cast<_Float16>(__uint_as_float(w[e] & 0xffff0000u) * up);
+      qo.q[jj][2 * e] = lo;
+      qo.q[jj][2 * e + 1] = hi;
+      sum += static_cast<float>(lo) + static_cast<float>(hi);
+    }
+  }
+  if constexpr (I8) {
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    qo.offset = kI8Offset * sum;
+  } else {
+    qo.offset = 0.f;
+  }
 }
 
 // Block of the lane's 4-token group that starts at tile token first + 4 gq
@@ -165,88 +228,124 @@ __device__ __forceinline__ void read_tile8(Buf8<D>& b, const unsigned char* stag
   }
 }
 
+// One staged 64-token tile of codes into the lane's running state: scores of
+// both sub-tiles, one online-softmax update, P.V.  sc holds the tile's key and
+// value scales; `full` = all 64 tokens present.
 template <int D, bool I8>
-__device__ __forceinline__ void qk_tile8(f32x4 (&s)[2], const uint4 (&k)[2][D / 64], const QOp<D>& qo) {
+__device__ __forceinline__ void codes_tile(Acc<D>& st, const Buf8<D>& b, const Sc8& sc, const QOp16<D>& qc, int t0,
+                                           int S, bool full, float scale_log2, int gq) {
+  // scores: [sub-tile u][slab a][i] is token 32 u + 16 a + 4 gq + i for head r
+  f32x4 s[2][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int jj = 0; jj < D / 32; ++jj) {
-      const uint4 c = k[a][jj >> 1];
-      const bf16x8 kop = (jj & 1) ? codes8_to_bf16<I8>(c.z, c.w) : codes8_to_bf16<I8>(c.x, c.y);
-      s[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qo.q[jj], s[a], 0, 0, 0);
+    for (int a = 0; a < 2; ++a) {
+      s[u][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < D / 32; ++jj) {
+        const uint4 c = b.k[u][a][jj >> 1];
+        const f16x8 kop = (jj & 1) ? codes8_to_f16<I8>(c.z, c.w) : codes8_to_f16<I8>(c.x, c.y);
+        s[u][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qc.q[jj], s[u][a], 0, 0, 0);
+      }
     }
-  }
-}
-
-// pv_tile for one sub-tile of codes: sk[a] = scale_log2 * key scale and
-// sv[a] = value scale of the lane's token group in slab a.
-template <int D, bool I8>
-__device__ __forceinline__ void pv_tile8(Acc<D>& st, const f32x4 (&s)[2], const uint32_t (&v)[2][D / 16],
-                                         const bool (&ok)[2], int t0, int S, bool full, const float (&sk)[2],
-                                         const float (&sv)[2], int gq) {
-  int n0 = 4, n1 = 4;
-  if (!full) {
-    n0 = ok[0] ? min(max(S - (t0 + 4 * gq), 0), 4) : 0;
-    n1 = ok[1] ? min(max(S - (t0 + 16 + 4 * gq), 0), 4) : 0;
-  }
-  float x[2][4];
+  int n[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+      n[u][a] = full ? 4 : (b.ok[u][a] ? min(max(S - (t0 + 32 * u + 16 * a + 4 * gq), 0), 4) : 0);
+  float x[2][2][4];
   float tmax = -INFINITY;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[a][i] = i < (a ? n1 : n0) ? s[a][i] * sk[a] : -INFINITY;
-      tmax = fmaxf(tmax, x[a][i]);
+    for (int a = 0; a < 2; ++a) {
+      const float sk = scale_log2 * sc.k[u][a] * qc.unscale;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[u][a][i] = i < n[u][a] ? (s[u][a][i] - qc.offset) * sk : -INFINITY;
+        tmax = fmaxf(tmax, x[u][a][i]);
+      }
     }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   const float m_new = fmaxf(st.m, tmax);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
-  float psum = 0.f;
-  bf16x8 phi, plo;
+  // the value-scale reference: the largest scale of the segment so far (wave-uniform)
+  float tv = fmaxf(fmaxf(sc.v[0][0], sc.v[0][1]), fmaxf(sc.v[1][0], sc.v[1][1]));
+  tv = fmaxf(tv, __shfl_xor(tv, 16));
+  tv = fmaxf(tv, __shfl_xor(tv, 32));
+  float f = alpha;  // rescale of the accumulated P.V
+  if (tv > st.vref) {
+    f *= st.vref / tv;
+    st.vref = tv;
+  }
+  const float inv = st.vref > 0.f ? 1.f / st.vref : 0.f;
+  float psum = 0.f, pcol = 0.f;
+  f16x8 P[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(x[a][i] - m_new);
-      psum += p;
-      const float pv = p * sv[a];
-      const __bf16 h = static_cast<__bf16>(pv);
-      phi[4 * a + i] = h;
-      plo[4 * a + i] = static_cast<__bf16>(pv - static_cast<float>(h));
+    for (int a = 0; a < 2; ++a) {
+      const float w = sc.v[u][a] * inv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[u][a][i] - m_new);
+        psum += p;
+        const _Float16 h = static_cast<_Float16>(p * w);
+        P[u][4 * a + i] = h;
+        pcol += static_cast<float>(h);
+      }
     }
   st.z = st.z * alpha + psum;
-  if (__any(alpha != 1.f)) {
+  if constexpr (I8) {
+    // every code is finite, and a missing token has P = 0: no masking
+    pcol += __shfl_xor(pcol, 16);
+    pcol += __shfl_xor(pcol, 32);
+    const float off = kI8Offset * pcol;
 #pragma unroll
-    for (int mm = 0; mm < D / 16; ++mm) st.o[mm] *= alpha;
-  }
-  uint32_t m0 = 0xffffffffu, m1 = 0xffffffffu;
-  if (!full) {  // zero the codes of missing tokens (code 0 is 0 in both formats): stale or NaN codes must not reach P.V
-    m0 = n0 >= 4 ? 0xffffffffu : (1u << (8 * n0)) - 1u;
-    m1 = n1 >= 4 ? 0xffffffffu : (1u << (8 * n1)) - 1u;
-  }
+    for (int mm = 0; mm < D / 16; ++mm) {
+      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16<true>(b.v[0][0][mm], b.v[0][1][mm]), P[0],
+                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16<true>(b.v[1][0][mm], b.v[1][1][mm]), P[1], t, 0, 0, 0);
 #pragma unroll
-  for (int mm = 0; mm < D / 16; ++mm) {
-    const bf16x8 vop = codes8_to_bf16<I8>(v[0][mm] & m0, v[1][mm] & m1);
-    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi, st.o[mm], 0, 0, 0);
-    st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo, st.o[mm], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) st.o[mm][i] = st.o[mm][i] * f + (t[i] - off);
+    }
+  } else {
+    if (__any(f != 1.f)) {
+#pragma unroll
+      for (int mm = 0; mm < D / 16; ++mm) st.o[mm] *= f;
+    }
+    // zero the codes of missing tokens: stale or NaN codes must not reach P.V (code 0 is 0)
+    uint32_t msk[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) msk[u][a] = n[u][a] >= 4 ? 0xffffffffu : (1u << (8 * n[u][a])) - 1u;
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        st.o[mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            codes8_to_f16<false>(b.v[u][0][mm] & msk[u][0], b.v[u][1][mm] & msk[u][1]), P[u], st.o[mm], 0, 0, 0);
   }
 }
 
 // End of a piece of segment t: write the normalised output (whole segment) or a summary record.
+// The accumulated P.V is omul times the true one's (1, or a cache of codes' vref).
 // With whole_rec non-null (a decode step over a cache of codes, whose merge
 // kernel adds the new token) a whole segment leaves its summary in
 // whole_rec[n][j] instead of its output.
 template <int D>
 __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slot, int64_t wave_id, uint16_t* out,
-                                      float* rec, float* whole_rec, int hq, int hkv, int g, int r, int gq) {
+                                      float* rec, float* whole_rec, int hq, int hkv, int g, int r, int gq,
+                                      float omul) {
   float zt = st.z + __shfl_xor(st.z, 16);
   zt += __shfl_xor(zt, 32);
   if (r < g) {
     if (whole && whole_rec == nullptr) {
-      const float inv = zt > 0.f ? 1.f / zt : 0.f;  // every token left out: zeros
+      const float inv = zt > 0.f ? omul / zt : 0.f;  // every token left out: zeros
       uint16_t* o = out + (static_cast<int64_t>(t.n) * hq + t.j * g + r) * D + 4 * gq;
 #pragma unroll
       for (int mm = 0; mm < D / 16; ++mm) {
@@ -258,7 +357,7 @@ __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slo
       float* rr = whole ? whole_rec + ((static_cast<int64_t>(t.n) * hkv + t.j) * g + r) * (D + 4)
                         : rec + (static_cast<int64_t>(wave_id * 2 + slot) * g + r) * (D + 4);
 #pragma unroll
-      for (int mm = 0; mm < D / 16; ++mm) *reinterpret_cast<f32x4*>(rr + 4 + 16 * mm + 4 * gq) = st.o[mm];
+      for (int mm = 0; mm < D / 16; ++mm) *reinterpret_cast<f32x4*>(rr + 4 + 16 * mm + 4 * gq) = st.o[mm] * omul;
       if (gq == 0) {
         rr[0] = st.m;
         rr[1] = zt;
@@ -363,11 +462,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // unconditional (a missing successor repeats the current tile's addresses).
   // The queries are those of the segment: loaded when a segment starts, not
   // again for each of its tiles.
-  QOp<D> qc;
+  std::conditional_t<F8, QOp16<D>, QOp<D>> qc;
+  auto segment_queries = [&](TilePos t) {
+    if constexpr (F8)
+      load_q16<D, I8>(qc, t, q, hq, g, r, gq);
+    else
+      load_q<D, false>(qc, t, q, hq, g, r, gq);
+  };
   TilePos nxt = x1 - x0 > 1 ? advance(cur, s_pre, hkv) : cur;
   Tb<NB> tbA = load_tb<B, TOK>(cur, block_tables, max_blocks, s_len);
   Tb<NB> tbB = load_tb<B, TOK>(nxt, block_tables, max_blocks, s_len);
-  load_q<D, F8>(qc, cur, q, hq, g, r, gq);
+  segment_queries(cur);
   dma_tile<D, B, F8>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
   // FP8: the scales of a tile's blocks travel with it, one tile ahead like its Q
   Sc8 scA{}, scB{};
@@ -414,14 +519,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       scn = load_scales<B>(tbn, scales, nxt.j, hkv, num_blocks, gq);
       dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        f32x4 sco[2];
-        qk_tile8<D, I8>(sco, b.k[u], qc);
-        const float sk[2] = {scale_log2 * scc.k[u][0], scale_log2 * scc.k[u][1]};
-        const float sv[2] = {scc.v[u][0], scc.v[u][1]};
-        pv_tile8<D, I8>(st, sco, b.v[u], b.ok[u], t0 + 32 * u, S, full, sk, sv, gq);
-      }
+      codes_tile<D, I8>(st, b, scc, qc, t0, S, full, scale_log2, gq);
       if (row_end && lane == 0) slots_out[cur.n] = row_slot;
     } else {
       Buf<D> b;
@@ -454,12 +552,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
       flush<D>(st, cur, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, whole_rec, hq, hkv, g, r,
-                gq);
+                gq, F8 ? st.vref : 1.f);
       first_piece = false;
       piece_start = 0;
     }
     if (!has_next) return false;
-    if (seg_end) load_q<D, F8>(qc, nxt, q, hq, g, r, gq);  // the next segment's queries
+    if (seg_end) segment_queries(nxt);
     ++x;
     cur = nxt;
     nxt = nxt2;

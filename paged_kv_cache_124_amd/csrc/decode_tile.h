@@ -152,6 +152,7 @@ template <int D>
 struct Acc {
   f32x4 o[D / 16];
   float m, z;
+  float vref;  // a cache of codes: the value-scale reference the accumulated P.V is divided by
 };
 
 template <int D>
@@ -162,6 +163,7 @@ __device__ __forceinline__ void reset(Acc<D>& st) {
   // keeps every exponent finite (exp2(-inf - -inf) would be NaN)
   st.m = -__FLT_MAX__;
   st.z = 0.f;
+  st.vref = 0.f;
 }
 
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
