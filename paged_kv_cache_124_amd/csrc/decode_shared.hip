@@ -120,49 +120,75 @@ struct Units {
     }
     return t;
   }
-  // next tile in (unit, KV head, tile) order; only called when one exists
-  __device__ UTile advance(UTile t) const {
-    if (t.ti + 1 < tiles(t.n)) {
-      ++t.ti;
-      if (is_group(t.n)) {
-        if (t.m < 0) {
-          if (t.ti == prefix_tiles(t.n)) {
-            t.m = next_member(t.n, 0);
-            t.k = 0;
-          }
-        } else if (t.k + 1 < member_tiles(t.n, t.m)) {
-          ++t.k;
-        } else {
-          t.m = next_member(t.n, t.m + 1);
-          t.k = 0;
-        }
-      }
-      return t;
-    }
-    t.ti = 0;
-    t.m = -1;
-    t.k = 0;
-    if (t.j + 1 < hkv) {
-      ++t.j;
-      return t;
-    }
-    t.j = 0;
-    do {
-      ++t.n;
-    } while (tiles(t.n) == 0);
-    return t;
-  }
 };
+
+// What a step needs to know about one tile of the list.  Each lane works out
+// the tile of one position of a window of 64 consecutive tiles from the unit
+// tables in LDS (a binary search and a walk over the members); a step reads
+// its tiles' fields from their lanes (readlane, wave-uniform results).  So no
+// LDS lookup lies between one tile's copies and the next's: a new window is
+// built once per 62 tiles.
+struct TileInfo {
+  int n, j, ti, m;   // unit, KV head, tile of the segment, member (-1: not a member's own tile)
+  int seq;           // the row whose table, tokens and new token the tile uses
+  int packed;        // that row's packed tokens (a group prefix: P << 2), as Units::packed
+  int t0, base;      // first token of the tile after base (Units::t0, Units::base)
+  int nt;            // tiles of the unit's segment
+  int first, count;  // a group's first row and members; a sequence: itself and 1
+  int ends;          // the tile ends its row's attended tokens (where the new token is)
+};
+
+__device__ __forceinline__ TileInfo tile_info(const Units& us, int n_units, int64_t x) {
+  int lo = 0, hi = n_units - 1;
+  while (lo < hi) {  // last unit u with hkv * s_pre[u] <= x
+    const int mid = (lo + hi + 1) >> 1;
+    if (static_cast<int64_t>(us.hkv) * us.s_pre[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  const UTile t = us.locate(lo, x - static_cast<int64_t>(us.hkv) * us.s_pre[lo]);
+  const bool grp = us.is_group(t.n);
+  TileInfo d;
+  d.n = t.n;
+  d.j = t.j;
+  d.ti = t.ti;
+  d.m = t.m;
+  d.seq = us.seq_of(t);
+  d.packed = us.packed(t);
+  d.t0 = us.t0(t);
+  d.base = us.base(t);
+  d.nt = us.tiles(t.n);
+  d.first = grp ? us.s_gfirst[t.n - us.n_seqs] : t.n;
+  d.count = grp ? us.s_gcount[t.n - us.n_seqs] : 1;
+  d.ends = us.ends_seq(t) ? 1 : 0;
+  return d;
+}
+
+// The tile a lane of the window holds (idx wave-uniform).
+__device__ __forceinline__ TileInfo lane_tile(const TileInfo& d, int idx) {
+  TileInfo t;
+  t.n = __builtin_amdgcn_readlane(d.n, idx);
+  t.j = __builtin_amdgcn_readlane(d.j, idx);
+  t.ti = __builtin_amdgcn_readlane(d.ti, idx);
+  t.m = __builtin_amdgcn_readlane(d.m, idx);
+  t.seq = __builtin_amdgcn_readlane(d.seq, idx);
+  t.packed = __builtin_amdgcn_readlane(d.packed, idx);
+  t.t0 = __builtin_amdgcn_readlane(d.t0, idx);
+  t.base = __builtin_amdgcn_readlane(d.base, idx);
+  t.nt = __builtin_amdgcn_readlane(d.nt, idx);
+  t.first = __builtin_amdgcn_readlane(d.first, idx);
+  t.count = __builtin_amdgcn_readlane(d.count, idx);
+  t.ends = __builtin_amdgcn_readlane(d.ends, idx);
+  return t;
+}
 
 // Table entries of a tile: tokens base + t0 .. + 31 of its sequence's row (a
 // group's prefix: its first member's), -1 past the tokens in the pool.
 template <int B>
-__device__ __forceinline__ Tb<32 / B> load_tb_unit(const UTile& t, const Units& us,
-                                                   const int32_t* __restrict__ block_tables, int max_blocks) {
-  const int32_t* row = block_tables + static_cast<int64_t>(us.seq_of(t)) * max_blocks;
-  const int S = pool_tokens(us.packed(t));
-  const int t0 = us.t0(t);
-  const int b0 = (us.base(t) + t0) / B;
+__device__ __forceinline__ Tb<32 / B> load_tb_unit(const TileInfo& t, const int32_t* __restrict__ block_tables,
+                                                   int max_blocks) {
+  const int32_t* row = block_tables + static_cast<int64_t>(t.seq) * max_blocks;
+  const int S = pool_tokens(t.packed);
+  const int t0 = t.t0;
+  const int b0 = (t.base + t0) / B;
   Tb<32 / B> tb;
 #pragma unroll
   for (int i = 0; i < 32 / B; ++i) {
@@ -181,23 +207,22 @@ struct QRows {
 };
 
 template <int D>
-__device__ __forceinline__ QRows q_rows(const UTile& t, const Units& us, const uint16_t* __restrict__ q, int hq,
+__device__ __forceinline__ QRows q_rows(const TileInfo& t, int n_seqs, int g, const uint16_t* __restrict__ q, int hq,
                                         const int (&col_m)[2], const int (&col_h)[2], int r, int gq) {
   QRows qr;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     int seq, h;
-    if (!us.is_group(t.n)) {
+    if (t.n < n_seqs) {
       const int c = 16 * cb + r;
       seq = t.n;
-      h = c < us.g ? c : 0;
+      h = c < g ? c : 0;
     } else {
-      const int i = t.n - us.n_seqs;
-      const bool ok = col_m[cb] < us.s_gcount[i];
-      seq = us.s_gfirst[i] + (ok ? col_m[cb] : 0);
+      const bool ok = col_m[cb] < t.count;
+      seq = t.first + (ok ? col_m[cb] : 0);
       h = ok ? col_h[cb] : 0;
     }
-    qr.p[cb] = q + (static_cast<int64_t>(seq) * hq + t.j * us.g + h) * D + gq * 8;
+    qr.p[cb] = q + (static_cast<int64_t>(seq) * hq + t.j * g + h) * D + gq * 8;
   }
   return qr;
 }
@@ -320,12 +345,12 @@ __device__ __forceinline__ void tile_group(Acc<D> (&st)[NC], const Buf<D>& b, co
 // End of a piece of segment t: the normalised outputs (whole segment) or a
 // wave-slot record per column.
 // `cols` and `first` (the group's first row, or the sequence) are the
-// segment's, read from LDS before the next tile's copies were issued.
+// segment's.
 template <int D>
-__device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], const UTile& t, const Units& us, int cols, int first,
+__device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], const TileInfo& t, int n_seqs, int g, int cols, int first,
                                            bool whole, int slot, int64_t wave_id, uint16_t* out, float* rec, int hq,
                                            int r, int gq, const int (&col_m)[2], const int (&col_h)[2]) {
-  const bool grp = us.is_group(t.n);
+  const bool grp = t.n >= n_seqs;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     if (cb == 1 && cols <= 16) break;
@@ -337,7 +362,7 @@ __device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], const UTile& t, cons
         const float inv = zt > 0.f ? 1.f / zt : 0.f;  // every token left out (blocks outside the pool): zeros
         const int seq = grp ? first + col_m[cb] : t.n;
         const int h = grp ? col_h[cb] : c;
-        uint16_t* o = out + (static_cast<int64_t>(seq) * hq + t.j * us.g + h) * D + 4 * gq;
+        uint16_t* o = out + (static_cast<int64_t>(seq) * hq + t.j * g + h) * D + 4 * gq;
 #pragma unroll
         for (int mm = 0; mm < D / 16; ++mm) {
           const uint32_t lo =
@@ -484,12 +509,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   const int64_t x1 = sp.start(wave_id + 1);
   if (x0 >= x1) return;
 
-  int lo = 0, hi = n_units - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (static_cast<int64_t>(hkv) * s_pre[mid] <= x0) lo = mid; else hi = mid - 1;
-  }
-  UTile cur = us.locate(lo, x0 - static_cast<int64_t>(hkv) * s_pre[lo]);
+  // the window of tiles xb .. xb + 63 (past the range: its last tile again)
+  int64_t xb = x0;
+  TileInfo mine = tile_info(us, n_units, min(xb + lane, x1 - 1));
+  TileInfo cur = lane_tile(mine, 0);
   int piece_start = cur.ti;
   bool first_piece = true;
 
@@ -507,19 +530,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // operands, loaded when a segment starts (registers are short here: two
   // column blocks of accumulators, scores and operands).
   QOp<D> qc[2];
-  UTile nxt = x1 - x0 > 1 ? us.advance(cur) : cur;
-  Tb<32 / B> tbA = load_tb_unit<B>(cur, us, block_tables, max_blocks);
-  Tb<32 / B> tbB = load_tb_unit<B>(nxt, us, block_tables, max_blocks);
-  load_q_rows<D>(qc, q_rows<D>(cur, us, q, hq, col_m, col_h, r, gq));
+  TileInfo nxt = lane_tile(mine, 1);  // the range's last tile again when it has one tile
+  Tb<32 / B> tbA = load_tb_unit<B>(cur, block_tables, max_blocks);
+  Tb<32 / B> tbB = load_tb_unit<B>(nxt, block_tables, max_blocks);
+  load_q_rows<D>(qc, q_rows<D>(cur, n_seqs, g, q, hq, col_m, col_h, r, gq));
   dma_tile<D, B, false>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
 
   int64_t x = x0;
-  auto wants_new = [&](const UTile& t) -> bool {
-    return k_new != nullptr && has_new_token(us.packed(t)) && us.ends_seq(t);
+  auto wants_new = [&](const TileInfo& t) -> bool {
+    return k_new != nullptr && has_new_token(t.packed) && t.ends != 0;
   };
-  auto new_of = [&](NewTok<D>& nt, const UTile& t) {
+  auto new_of = [&](NewTok<D>& nt, const TileInfo& t) {
     TilePos p;
-    p.n = us.seq_of(t);
+    p.n = t.seq;
     p.j = t.j;
     p.ti = 0;
     load_new<D>(nt, p, k_new, v_new, slots, hkv, r, gq);
@@ -533,14 +556,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     // Every LDS read of the step comes before the next tile's copies below:
     // an LDS read issued after them would wait for all of them.
     const bool has_next = x + 1 < x1;
-    const int packed = us.packed(cur);
+    const int packed = cur.packed;
     const int S = attended_tokens(packed);
-    const int nt_cur = us.tiles(cur.n);
-    const UTile nxt2 = x + 2 < x1 ? us.advance(nxt) : nxt;
-    const int t0 = us.t0(cur);
-    const int cols = us.cols(cur.n);
-    const int first = us.is_group(cur.n) ? us.s_gfirst[cur.n - n_seqs] : cur.n;
-    const QRows q_next = q_rows<D>(nxt, us, q, hq, col_m, col_h, r, gq);
+    const int nt_cur = cur.nt;
+    // the tile after next: from the window, which moves on when it is used up
+    const int64_t x2 = min(x + 2, x1 - 1);
+    if (x2 - xb >= 64) {
+      xb = x2;
+      mine = tile_info(us, n_units, min(xb + lane, x1 - 1));
+    }
+    const TileInfo nxt2 = lane_tile(mine, static_cast<int>(x2 - xb));
+    const int t0 = cur.t0;
+    const bool grp = cur.n >= n_seqs;
+    const int cols = grp ? cur.count * g : g;
+    const int first = cur.first;
+    const QRows q_next = q_rows<D>(nxt, n_seqs, g, q, hq, col_m, col_h, r, gq);
     Buf<D> b;
     wait_stage_copies();
     read_tile<D, B>(b, &stc[wave][0], tbc, num_blocks, r, gq);
@@ -549,18 +579,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     if (wants_new(cur)) {
       patch_new<D>(b, ntok, pool_tokens(packed) - t0, r, gq);
       if (cur.j == 0 && lane == 0) {  // the row's slot goes on to the merge kernel, which stores the token
-        const int S0 = us.base(cur) + pool_tokens(packed);
+        const int S0 = cur.base + pool_tokens(packed);
         const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
                              static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
                              ntok.slot % B == S0 % B;
-        slots_out[us.seq_of(cur)] = at_next ? ntok.slot : -1;
+        slots_out[cur.seq] = at_next ? ntok.slot : -1;
       }
     }
-    tb2 = load_tb_unit<B>(nxt2, us, block_tables, max_blocks);
+    tb2 = load_tb_unit<B>(nxt2, block_tables, max_blocks);
     if (has_next && wants_new(nxt)) new_of(ntok, nxt);
     dma_tile<D, B, false>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
     const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
-    if (us.is_group(cur.n)) {
+    if (grp) {
       bool live[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) live[cb] = cur.m < 0 || col_m[cb] == cur.m;  // a member's tile: its columns
@@ -580,7 +610,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     }
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
-      flush_unit<D>(st, cur, us, cols, first, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec,
+      flush_unit<D>(st, cur, n_seqs, g, cols, first, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec,
                     hq, r, gq, col_m, col_h);
       first_piece = false;
       piece_start = 0;
