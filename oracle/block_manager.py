@@ -91,61 +91,95 @@ class BlockManagerModel:
         self.lens[seq] = num_tokens
         return OK
 
+    # -- the sharing rules of [P1] sections 14-17 --------------------------------
+    # Each operation checks its preconditions first and changes nothing when one
+    # fails; then it applies its whole effect.  Two primitives carry the
+    # reference counting of section 17: _pop (a free block becomes referenced
+    # once) and _unref (one reference goes away; at zero the block is released).
+
+    def _unref(self, b: int) -> None:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self._release(b)
+
     def fork(self, parent: int, child: int) -> int:
+        """The child becomes a second owner of every block of the parent ([P1] sections 14 and 16).
+
+        Pre: parent known and resident; child new.
+        Post: the child's table and length equal the parent's; each of those
+        blocks has one reference more; the free set is unchanged (no data moves).
+        """
         if parent not in self.tables:
             return ERR_NOT_FOUND
         if child in self.tables:
             return ERR_EXISTS
         if parent in self.swapped:
             return ERR_INVALID_ARG
-        for b in self.tables[parent]:
-            self.ref[b] += 1
-        self.tables[child] = list(self.tables[parent])
+        shared = self.tables[parent]
+        self.tables[child] = list(shared)
         self.lens[child] = self.lens[parent]
+        for b in shared:
+            self.ref[b] += 1
         return OK
 
+    def _placement(self, seq: int) -> str:
+        """Where position S = len(seq) goes ([P1] sections 15-16):
+
+        'open'   S is a multiple of B: the tail is full (or there is none), so
+                 a fresh block is added to the table;
+        'clone'  the tail is partly filled and shared (ref > 1): a shared block
+                 is immutable (section 15), so the sequence takes a private copy
+                 of it -- a fresh block, with (tail, fresh) reported for the
+                 device copy;
+        'write'  the tail is partly filled and only this sequence holds it: the
+                 token goes there.
+        """
+        if self.lens[seq] % self.block_size == 0:
+            return "open"
+        return "clone" if self.ref[self.tables[seq][-1]] > 1 else "write"
+
     def append_slot(self, seq: int) -> Tuple[int, int, int, int]:
-        """Reserve the slot of position len(seq).  Returns (status, slot, cow_src, cow_dst)."""
+        """Reserve the slot of position S = len(seq).  Returns (status, slot, copy src, copy dst).
+
+        Pre: seq known and resident; 'open' and 'clone' need a block to take
+        (else NO_FREE_BLOCKS, nothing changed).
+        Post: len(seq) = S + 1; the table covers ceil((S + 1) / B) blocks and
+        its last block is held by this sequence alone; the slot is
+        table[S // B] * B + S % B ([P1] section 7).  A clone moves this
+        sequence's reference from the shared tail to its copy; the other owners
+        keep the tail unchanged.
+        """
         if seq not in self.tables:
             return ERR_NOT_FOUND, -1, -1, -1
         if seq in self.swapped:
             return ERR_INVALID_ARG, -1, -1, -1
-        table = self.tables[seq]
-        length = self.lens[seq]
-        off = length % self.block_size
+        where = self._placement(seq)
+        if where != "write" and self._available() == 0:
+            return ERR_NO_FREE_BLOCKS, -1, -1, -1
+        table, S = self.tables[seq], self.lens[seq]
         src = dst = -1
-        if off != 0:
-            tail = table[-1]
-            if self.ref[tail] > 1:
-                if self._available() == 0:
-                    return ERR_NO_FREE_BLOCKS, -1, -1, -1
-                new = self._pop()
-                self.ref[tail] -= 1
-                table[-1] = new
-                src, dst = tail, new
-                self.cow_copies += 1
-                block = new
-            else:
-                block = tail
-        else:
-            if self._available() == 0:
-                return ERR_NO_FREE_BLOCKS, -1, -1, -1
-            block = self._pop()
-            table.append(block)
-        self.lens[seq] = length + 1
-        return OK, block * self.block_size + off, src, dst
+        if where == "open":
+            table.append(self._pop())
+        elif where == "clone":
+            src, dst = table[-1], self._pop()
+            table[-1] = dst
+            self._unref(src)  # still held by the other owners: never released here
+            self.cow_copies += 1
+        self.lens[seq] = S + 1
+        return OK, table[S // self.block_size] * self.block_size + S % self.block_size, src, dst
 
     def _undo_append(self, seq: int, src: int, dst: int) -> None:
+        """The inverse of one append_slot (a failed batch is rolled back newest first, which restores
+        the free list exactly: every block goes back on top of the stack it came from)."""
         table = self.tables[seq]
-        length = self.lens[seq] - 1
-        self.lens[seq] = length
-        if src >= 0:  # copy-on-write: give the new block back, re-share the old tail
+        self.lens[seq] -= 1
+        if src >= 0:  # drop the copy; the sequence shares the old tail again
+            table[-1] = src
+            self.ref[src] += 1
             self.ref[dst] = 0
             self.free.append(dst)
-            self.ref[src] += 1
-            table[-1] = src
             self.cow_copies -= 1
-        elif length % self.block_size == 0:  # a fresh block was taken
+        elif self.lens[seq] % self.block_size == 0:  # give back the block the append opened
             b = table.pop()
             self.ref[b] = 0
             self.free.append(b)
@@ -168,18 +202,37 @@ class BlockManagerModel:
         return OK, slots, pairs, -1
 
     def free_seq(self, seq: int) -> int:
+        """A finished sequence gives up its reference to each of its blocks ([P1] section 17).
+
+        Pre: seq known.  Post: seq is gone; each of its blocks has one
+        reference fewer, and those no one holds any more are free again, in
+        table order (reading: the last block released is the first reused).
+        """
         if seq not in self.tables:
             return ERR_NOT_FOUND
         if seq in self.swapped:
             self._free_host(seq)
             return OK
-        for b in self.tables[seq]:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
-        del self.tables[seq]
+        for b in self.tables.pop(seq):
+            self._unref(b)
         del self.lens[seq]
         return OK
+
+    def check_invariants(self) -> None:
+        """The bookkeeping facts of [P1] sections 8 and 17, asserted on the whole state:
+        every resident sequence of S tokens holds ceil(S / B) blocks; a block's count is the number of
+        table entries naming it; free blocks are referenced by no one and appear once."""
+        count = [0] * self.num_blocks
+        for seq, table in self.tables.items():
+            if seq in self.swapped:
+                continue
+            assert len(table) == -(-self.lens[seq] // self.block_size), seq
+            for b in table:
+                count[b] += 1
+        assert count == self.ref, "reference counts differ from the tables"
+        free = list(self.free) + list(getattr(self, "idle", []))
+        assert len(set(free)) == len(free), "a block is free twice"
+        assert all(self.ref[b] == 0 for b in free), "a referenced block is free"
 
     def _free_host(self, seq: int) -> None:
         for hb in self.tables[seq]:
@@ -561,9 +614,7 @@ class PrefixCachingModel(BlockManagerModel):
             self._free_host(seq)
         else:
             for b in reversed(self.tables[seq]):
-                self.ref[b] -= 1
-                if self.ref[b] == 0:
-                    self._release(b)
+                self._unref(b)
             del self.tables[seq]
             del self.lens[seq]
         del self.tokens[seq]

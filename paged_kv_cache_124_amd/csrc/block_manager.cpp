@@ -171,6 +171,19 @@ struct pa_bm {
     }
   }
 
+  // Where position S of sequence s goes ("PagedAttention: Virtual Memory for
+  // the KV Cache", sections 15-16): a fresh block when S is a multiple of B
+  // (kOpen); a private copy of a partly filled tail that other sequences share,
+  // since shared blocks are immutable (kClone); else the tail itself (kWrite).
+  enum Placement { kOpen, kClone, kWrite };
+  Placement placement(const Seq& s) const {
+    if (s.len % block_size == 0) return kOpen;
+    return ref[s.table.back()] > 1 ? kClone : kWrite;
+  }
+
+  // Reserve the slot of position S = len: checks first (nothing changes on an
+  // error), then the whole effect.  Afterwards the sequence holds its last
+  // block alone; a clone moves its reference from the shared tail to the copy.
   int append(int64_t id, int32_t* slot, int32_t* src, int32_t* dst) {
     *slot = -1;
     *src = -1;
@@ -179,28 +192,22 @@ struct pa_bm {
     if (it == seqs.end()) return PA_ERR_NOT_FOUND;
     Seq& s = it->second;
     if (s.swapped) return PA_ERR_INVALID_ARG;
-    const int32_t off = static_cast<int32_t>(s.len % block_size);
-    int32_t block;
-    if (off != 0) {
-      const int32_t tail = s.table.back();
-      if (ref[tail] > 1) {  // shared unaligned tail: clone before writing
-        if (available() == 0) return PA_ERR_NO_FREE_BLOCKS;
-        block = pop();
-        ref[tail] -= 1;
-        s.table.back() = block;
-        *src = tail;
-        *dst = block;
-        ++cow_copies;
-      } else {
-        block = tail;
-      }
-    } else {  // tail full (or no tail yet): take a fresh block
-      if (available() == 0) return PA_ERR_NO_FREE_BLOCKS;
-      block = pop();
-      s.table.push_back(block);
+    const Placement where = placement(s);
+    if (where != kWrite && available() == 0) return PA_ERR_NO_FREE_BLOCKS;
+    const int64_t S = s.len;
+    if (where == kOpen) {
+      s.table.push_back(pop());
+    } else if (where == kClone) {
+      const int32_t shared = s.table.back();
+      const int32_t copy = pop();
+      s.table.back() = copy;
+      ref[shared] -= 1;  // still held by the other owners
+      *src = shared;
+      *dst = copy;
+      ++cow_copies;
     }
-    s.len += 1;
-    *slot = block * block_size + off;
+    s.len = S + 1;
+    *slot = s.table[S / block_size] * block_size + static_cast<int32_t>(S % block_size);
     return PA_OK;
   }
 

@@ -188,3 +188,37 @@ def test_random_operations_keep_invariants_and_write_only_private_blocks():
             else:
                 m.free_seq(rng.choice(live))
             _check_invariants(m)
+
+
+def test_random_operations_keep_the_models_own_invariants_with_prefix_caching():
+    """The oracle's check_invariants (counts equal table entries, free and idle blocks unreferenced and listed once,
+    ceil(S / B) blocks per sequence) holds after every operation, with and without the prefix cache; a pin of the
+    plan-then-commit form of fork / append_slot / free_seq against the same random sequences as above."""
+    rng = random.Random(23)
+    for trial in range(20):
+        nb, B = rng.choice([(8, 4), (32, 8), (64, 16)])
+        caching = trial % 2 == 1
+        m = (BM.PrefixCachingModel if caching else BM.BlockManagerModel)(nb, B, rng.sample(range(nb), nb))
+        next_id = 0
+        prompts = [[rng.randrange(50) for _ in range(3 * B)] for _ in range(3)]
+        for _ in range(150):
+            live = [s for s in m.tables if s not in m.swapped]
+            op = rng.random()
+            if op < 0.25 or not live:
+                if caching:
+                    p = rng.choice(prompts)
+                    m.add_seq_tokens(next_id, p[:rng.randint(1, len(p))])
+                else:
+                    m.add_seq(next_id, rng.randint(1, 3 * B))
+                next_id += 1
+            elif op < 0.4:
+                m.fork(rng.choice(live), next_id)
+                next_id += 1
+            elif op < 0.85:
+                seq = rng.choice(live)
+                st, slot, src, dst = m.append_slot(seq)
+                if st == BM.OK:
+                    assert m.ref[slot // B] == 1 and slot // B == m.tables[seq][-1]
+            else:
+                m.free_seq(rng.choice(live))
+            m.check_invariants()
