@@ -654,7 +654,7 @@ template <int D>
 __device__ __forceinline__ const float* piece_record(const SegPieces& sg, int k, const Split& sp, const float* rec) {
   if (k < 0 || k >= sg.cnt) return nullptr;
   const int64_t v = sg.v_lo + k;
-  if (sp.start(v) == sp.start(v + 1)) return nullptr;
+  if (sp.T < sp.W && sp.start(v) == sp.start(v + 1)) return nullptr;  // with T >= W no range is empty
   const int slot = (v == sg.v_lo && sg.lo_second) ? 1 : 0;
   return rec + (v * 2 + slot) * kShCols * (D + 4);
 }
