@@ -185,6 +185,29 @@ int pa_check_batch(const int32_t* block_tables, const int32_t* context_lens, int
                    int max_blocks_per_seq, int max_context_len, int num_blocks, int block_size,
                    int32_t* status, void* stream);
 
+/* pa_check_pairs: validate a list of copy-on-write pairs on the device before
+ * pa_copy_blocks* ("PagedAttention: Virtual Memory for the KV Cache", sections
+ * 15-16: a copy clones a shared block into a fresh block).  The copy kernels
+ * assume what the block manager guarantees: no destination is named twice and
+ * no destination is also a source in the same call (else the result depends on
+ * the order the copies run in); a pair with an id outside [0, num_blocks) is
+ * skipped.  One kernel on `stream` reads the pairs and writes
+ *
+ *   status[0]  pairs with an id outside [0, num_blocks)
+ *   status[1]  pairs naming a destination that an earlier pair names
+ *              (pairs naming it minus one, summed over destinations)
+ *   status[2]  pairs whose destination is also some pair's source
+ *   status[3]  the lowest index of a pair counted in status[0] or status[2], or
+ *              naming a destination that another pair names; -1 when none
+ *
+ *   src_dst_pairs  int32 [num_pairs][2], device-readable
+ *   status         int32 [4], device; every word is written
+ * The pairs are valid for pa_copy_blocks* iff status[0..2] are 0.  Errors
+ * (host, before any launch): PA_ERR_INVALID_ARG for num_pairs < 0,
+ * num_blocks < 0 or a NULL pointer the call needs; PA_ERR_UNSUPPORTED for
+ * num_blocks > 524288 (the check keeps two bitmaps of the pool in LDS). */
+int pa_check_pairs(const int32_t* src_dst_pairs, int num_pairs, int num_blocks, int32_t* status, void* stream);
+
 /* pa_decode_step: one whole decode step of the batch.  Each row attends to
  * its S cached tokens and to its new token (key and value from k_new / v_new,
  * at position S); then the new token is stored and the row moved forward

@@ -81,6 +81,7 @@ _SIGS = {
                               + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_partitioned_workspace_bytes": (c_size_t, [c_int] * 8),
     "pa_check_batch": (c_int, [c_void_p, c_void_p] + [c_int] * 5 + [c_void_p, c_void_p]),
+    "pa_check_pairs": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p]),
     "pa_decode_shared": (c_int, [c_void_p] * 7 + [c_int] * 6 + [c_float] + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
     "pa_decode_step_shared": (c_int, [c_void_p] * 10 + [c_int] * 6 + [c_float] + [c_int] * 4
                               + [c_void_p, c_size_t, c_void_p]),
@@ -284,6 +285,26 @@ def pa_check_batch(block_tables, context_lens, max_context_len, num_blocks, bloc
     _check(lib.pa_check_batch(_dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), n,
                               block_tables.shape[1], int(max_context_len), int(num_blocks), int(block_size),
                               _dev(status, "status"), _stream_ptr(stream)), "pa_check_batch")
+    return status
+
+
+def pa_check_pairs(src_dst_pairs, num_blocks, status=None, stream=None):
+    """pa_check_pairs of include/pa.h: validate copy-on-write pairs on the device.
+
+    Returns the int32 device tensor ``status`` of 4 words (allocated when None):
+    out-of-pool pairs, repeated destinations, destinations that are sources,
+    lowest offending pair (-1 when none).
+    """
+    import torch
+    if src_dst_pairs.dtype != torch.int32 or src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int32 [P][2]")
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=src_dst_pairs.device)
+    if status.dtype != torch.int32 or status.numel() < 4:
+        raise ValueError("status must hold 4 int32 words")
+    p = src_dst_pairs.shape[0]
+    _check(lib.pa_check_pairs(_dev(src_dst_pairs, "src_dst_pairs") if p else c_void_p(0), p, int(num_blocks),
+                              _dev(status, "status"), _stream_ptr(stream)), "pa_check_pairs")
     return status
 
 

@@ -217,3 +217,15 @@ def test_check_batch_host_validation():
     assert L.pa_check_batch(FAKE, FAKE, 4, 4, 64, 10, 16, NUL, NUL) == 1
     assert L.pa_check_batch(NUL, FAKE, 4, 4, 64, 10, 16, FAKE, NUL) == 1
     assert L.pa_check_batch(FAKE, NUL, 4, 4, 64, 10, 16, FAKE, NUL) == 1
+
+
+def test_check_pairs_host_validation():
+    """pa_check_pairs(pairs, P, num_blocks, status, stream): bad sizes and NULL pointers refused before any launch;
+    pools beyond the two LDS bitmaps (524288 blocks) are unsupported."""
+    import paged_kv_cache_124_amd as pa
+    L = pa.lib
+    assert L.pa_check_pairs(FAKE, -1, 10, FAKE, NUL) == 1
+    assert L.pa_check_pairs(FAKE, 1, -1, FAKE, NUL) == 1
+    assert L.pa_check_pairs(NUL, 1, 10, FAKE, NUL) == 1
+    assert L.pa_check_pairs(FAKE, 1, 10, NUL, NUL) == 1
+    assert L.pa_check_pairs(FAKE, 1, (1 << 19) + 1, FAKE, NUL) == 2
