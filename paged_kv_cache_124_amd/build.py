@@ -27,6 +27,9 @@ LIB = os.path.join(PKG, "libpa.so")
 PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 HOST_LIB = os.path.join(PKG, "libpa_host.so")
 HOST_ASAN_LIB = os.path.join(PKG, "libpa_host_asan.so")
+# test build: the block manager with a 2-bit chain hash, so the prefix cache's exact chain comparison is
+# exercised on every lookup (tests/test_block_manager_collide.py)
+HOST_COLLIDE_LIB = os.path.join(PKG, "libpa_host_collide.so")
 
 HIP_SOURCES = ["decode.hip", "decode_stream.hip", "decode_stream_i8.hip", "decode_shared.hip", "kv_ops.hip",
                "check.hip"]
@@ -70,11 +73,12 @@ def _run(cmd, out, verbose):
     return out
 
 
-def build_host(verbose: bool = False, sanitize: bool = False) -> str:
-    """The block manager without HIP (g++), optionally with AddressSanitizer and UBSan."""
+def build_host(verbose: bool = False, sanitize: bool = False, collide: bool = False) -> str:
+    """The block manager without HIP (g++), optionally with AddressSanitizer and UBSan, or with a 2-bit chain hash."""
     srcs = [os.path.join(CSRC, s) for s in HOST_SOURCES]
-    flags = HOST_FLAGS + (SANITIZE_FLAGS if sanitize else [])
-    return _run(["g++", *flags, "-I", INCLUDE, *srcs], HOST_ASAN_LIB if sanitize else HOST_LIB, verbose)
+    flags = HOST_FLAGS + (SANITIZE_FLAGS if sanitize else []) + (["-DPA_CHAIN_HASH_BITS=2"] if collide else [])
+    out = HOST_COLLIDE_LIB if collide else (HOST_ASAN_LIB if sanitize else HOST_LIB)
+    return _run(["g++", *flags, "-I", INCLUDE, *srcs], out, verbose)
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
@@ -92,6 +96,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     _run([hipcc(), *HIP_FLAGS, "-I", INCLUDE, *[os.path.join(CSRC, s) for s in PROBE_SOURCES]], PROBE_LIB, verbose)
     build_host(verbose)
     build_host(verbose, sanitize=True)
+    build_host(verbose, collide=True)
     return LIB
 
 

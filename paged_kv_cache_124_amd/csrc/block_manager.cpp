@@ -28,19 +28,19 @@ namespace {
 struct Seq {
   std::vector<int32_t> table;
   int64_t len = 0;
-  // prefix cache: token ids of the partial tail block, chain hash of the
-  // tokens before it, and whether all token ids of the sequence are known
+  // prefix cache: token ids of the partial tail block, the interned chain of
+  // the full blocks before it (0: none), and whether all token ids of the
+  // sequence are known
   std::vector<int32_t> pending;
-  uint64_t chain = 0;
+  int64_t chain = 0;
   bool known = false;
   bool swapped = false;  // the table holds host block ids
 };
 
-// Chain hash of a full block: its B token ids after the chain hash of the
-// tokens before it (0 for the first block).  splitmix64's finaliser mixes
-// each word in; a match is also checked on the parent hash and the block's
-// token ids, so a false match needs a 64-bit collision of two different
-// prefixes ending in the same block of tokens.
+// Hash of a full block's B token ids after the chain id of the tokens before
+// it, for the chain index.  splitmix64's finaliser mixes each word in.  The
+// hash only picks candidates: a match compares the parent chain id and the
+// token ids exactly, so equal chain ids mean equal token chains.
 uint64_t mix64(uint64_t x) {
   x ^= x >> 30;
   x *= 0xbf58476d1ce4e5b9ull;
@@ -52,7 +52,10 @@ uint64_t mix64(uint64_t x) {
 uint64_t chain_hash(uint64_t parent, const int32_t* tokens, int n) {
   uint64_t h = mix64(parent + 0x9e3779b97f4a7c15ull);
   for (int i = 0; i < n; ++i) h = mix64(h ^ static_cast<uint32_t>(tokens[i]) ^ (static_cast<uint64_t>(i + 1) << 32));
-  return h | 1;  // never 0, the first block's parent
+#ifdef PA_CHAIN_HASH_BITS  // test builds only: a hash this narrow makes distinct chains collide all the time
+  h &= (uint64_t(1) << PA_CHAIN_HASH_BITS) - 1;
+#endif
+  return h;
 }
 
 struct Undo {  // what one append did, so a failed batch can be rolled back
@@ -72,12 +75,25 @@ struct pa_bm {
   int64_t cow_copies = 0;
 
   // ---- prefix cache (off unless enabled while no sequence exists) ----------
+  // A token chain (the token ids of the leading full blocks of some sequence)
+  // is interned: chain 0 is the empty chain, and chain c = (parent chain,
+  // B token ids) is unique, so two requests share a prefix exactly when they
+  // reach the same chain id.  A chain lives while something holds it: the
+  // cached block that stands for it, a longer chain, or a sequence whose
+  // tokens so far end with it.
+  struct Chain {
+    int64_t parent;
+    int32_t block;  // the cached block holding these tokens, or -1
+    int32_t refs;
+  };
   bool caching = false;
-  std::vector<uint8_t> cached;       // block holds a cached full block
-  std::vector<uint64_t> blk_hash;    // its chain hash
-  std::vector<uint64_t> blk_parent;  // chain hash of the tokens before it
-  std::vector<int32_t> blk_tokens;   // [num_blocks][B] its token ids
-  std::unordered_multimap<uint64_t, int32_t> index;  // chain hash -> cached block
+  std::vector<uint8_t> cached;         // block holds a cached full block
+  std::vector<int64_t> blk_chain;      // its chain
+  std::vector<Chain> chains;           // [0] the empty chain
+  std::vector<int32_t> chain_tokens;   // [chain][B]
+  std::vector<int64_t> chain_free;     // ids to reuse
+  std::unordered_multimap<uint64_t, int64_t> index;  // hash of (parent, tokens) -> chain
+  int64_t num_cached = 0;
   // idle list: cached blocks without references, least recently released at the head
   std::vector<int32_t> idle_prev, idle_next;
   int32_t idle_head = -1, idle_tail = -1;
@@ -104,37 +120,83 @@ struct pa_bm {
     --idle_count;
   }
 
-  // the cached block holding (parent, tokens), or -1
-  int32_t find(uint64_t parent, const int32_t* tokens) const {
-    const uint64_t h = chain_hash(parent, tokens, block_size);
-    auto range = index.equal_range(h);
+  // the chain (parent, tokens), or -1
+  int64_t chain_find(int64_t parent, const int32_t* tokens) const {
+    auto range = index.equal_range(chain_hash(static_cast<uint64_t>(parent), tokens, block_size));
     for (auto it = range.first; it != range.second; ++it) {
-      const int32_t b = it->second;
-      if (blk_parent[b] == parent &&
-          std::memcmp(&blk_tokens[static_cast<size_t>(b) * block_size], tokens, sizeof(int32_t) * block_size) == 0)
-        return b;
+      const int64_t c = it->second;
+      if (chains[c].parent == parent &&
+          std::memcmp(&chain_tokens[static_cast<size_t>(c) * block_size], tokens, sizeof(int32_t) * block_size) == 0)
+        return c;
     }
     return -1;
   }
-  // cache block b as (parent, tokens) unless that chain is cached already; returns the chain hash
-  uint64_t remember(int32_t b, uint64_t parent, const int32_t* tokens) {
-    const uint64_t h = chain_hash(parent, tokens, block_size);
-    if (find(parent, tokens) >= 0) return h;
-    cached[b] = 1;
-    blk_hash[b] = h;
-    blk_parent[b] = parent;
-    std::memcpy(&blk_tokens[static_cast<size_t>(b) * block_size], tokens, sizeof(int32_t) * block_size);
-    index.emplace(h, b);
-    return h;
+  void chain_ref(int64_t c) {
+    if (c > 0) ++chains[c].refs;
+  }
+  // one holder of chain c lets go; a chain no one holds is dropped, and lets go of its parent
+  void chain_unref(int64_t c) {
+    while (c > 0 && --chains[c].refs == 0) {
+      auto range = index.equal_range(chain_hash(static_cast<uint64_t>(chains[c].parent),
+                                                &chain_tokens[static_cast<size_t>(c) * block_size], block_size));
+      for (auto it = range.first; it != range.second; ++it)
+        if (it->second == c) {
+          index.erase(it);
+          break;
+        }
+      chain_free.push_back(c);
+      c = chains[c].parent;
+    }
+  }
+  // the chain (parent, tokens), made if it does not exist (it then holds its parent)
+  int64_t chain_intern(int64_t parent, const int32_t* tokens) {
+    const int64_t found = chain_find(parent, tokens);
+    if (found >= 0) return found;
+    int64_t c;
+    if (!chain_free.empty()) {
+      c = chain_free.back();
+      chain_free.pop_back();
+    } else {
+      c = static_cast<int64_t>(chains.size());
+      chains.push_back({});
+      chain_tokens.resize(chain_tokens.size() + block_size);
+    }
+    chains[c] = {parent, -1, 0};
+    std::memcpy(&chain_tokens[static_cast<size_t>(c) * block_size], tokens, sizeof(int32_t) * block_size);
+    index.emplace(chain_hash(static_cast<uint64_t>(parent), tokens, block_size), c);
+    chain_ref(parent);
+    return c;
+  }
+
+  // the cached block holding (parent, tokens), or -1
+  int32_t find(int64_t parent, const int32_t* tokens) const {
+    const int64_t c = chain_find(parent, tokens);
+    return c >= 0 ? chains[c].block : -1;
+  }
+  // cache block b as (parent, tokens) unless that chain is cached already; returns the chain
+  int64_t remember(int32_t b, int64_t parent, const int32_t* tokens) {
+    const int64_t c = chain_intern(parent, tokens);
+    if (chains[c].block < 0) {
+      chains[c].block = b;
+      chain_ref(c);
+      cached[b] = 1;
+      blk_chain[b] = c;
+      ++num_cached;
+    }
+    return c;
   }
   void forget(int32_t b) {
-    auto range = index.equal_range(blk_hash[b]);
-    for (auto it = range.first; it != range.second; ++it)
-      if (it->second == b) {
-        index.erase(it);
-        break;
-      }
+    const int64_t c = blk_chain[b];
+    chains[c].block = -1;
     cached[b] = 0;
+    --num_cached;
+    chain_unref(c);
+  }
+  // sequence s's chain moves to c
+  void set_chain(Seq& s, int64_t c) {
+    chain_ref(c);
+    chain_unref(s.chain);
+    s.chain = c;
   }
 
   int32_t pop() {
@@ -162,11 +224,12 @@ struct pa_bm {
     if (!token || !s.known) {
       s.known = false;
       s.pending.clear();
+      set_chain(s, 0);
       return;
     }
     s.pending.push_back(*token);
     if (s.len % block_size == 0) {  // the tail block is full: cache it
-      s.chain = remember(s.table.back(), s.chain, s.pending.data());
+      set_chain(s, remember(s.table.back(), s.chain, s.pending.data()));
       s.pending.clear();
     }
   }
@@ -277,9 +340,9 @@ int pa_bm_enable_prefix_cache(pa_bm* bm) {
   if (bm->caching) return PA_OK;
   const size_t nb = static_cast<size_t>(bm->num_blocks);
   bm->cached.assign(nb, 0);
-  bm->blk_hash.assign(nb, 0);
-  bm->blk_parent.assign(nb, 0);
-  bm->blk_tokens.assign(nb * static_cast<size_t>(bm->block_size), 0);
+  bm->blk_chain.assign(nb, 0);
+  bm->chains.assign(1, {0, -1, 0});  // the empty chain
+  bm->chain_tokens.assign(static_cast<size_t>(bm->block_size), 0);
   bm->idle_prev.assign(nb, -1);
   bm->idle_next.assign(nb, -1);
   bm->caching = true;
@@ -296,14 +359,14 @@ int pa_bm_add_seq_tokens(pa_bm* bm, int64_t seq, const int32_t* tokens, int num_
   const int64_t full = num_tokens / B;
   // the longest run of leading full blocks whose chains are cached (no change yet)
   std::vector<int32_t> hits;
-  uint64_t parent = 0;
+  int64_t parent = 0;
   int64_t idle_hits = 0;
   for (int64_t i = 0; i < full; ++i) {
     const int32_t b = bm->find(parent, tokens + i * B);
     if (b < 0) break;
     hits.push_back(b);
     if (bm->ref[b] == 0) ++idle_hits;
-    parent = bm->blk_hash[b];
+    parent = bm->blk_chain[b];
   }
   if (bm->available() - idle_hits < nblocks - static_cast<int64_t>(hits.size())) return PA_ERR_NO_FREE_BLOCKS;
   Seq s;
@@ -320,7 +383,8 @@ int pa_bm_add_seq_tokens(pa_bm* bm, int64_t seq, const int32_t* tokens, int num_
     if (i < full) parent = bm->remember(b, parent, tokens + i * B);  // a full block of the prompt
   }
   s.len = num_tokens;
-  s.chain = parent;
+  s.chain = 0;
+  bm->set_chain(s, parent);
   s.known = true;
   s.pending.assign(tokens + full * B, tokens + num_tokens);
   bm->seqs.emplace(seq, std::move(s));
@@ -336,6 +400,7 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (it->second.swapped) return PA_ERR_INVALID_ARG;
   Seq s = it->second;  // copy of the table; no data moves
   for (int32_t b : s.table) bm->ref[b] += 1;
+  if (bm->caching) bm->chain_ref(s.chain);  // the child's tokens end with the same chain
   bm->seqs.emplace(child, std::move(s));
   return PA_OK;
 }
@@ -449,6 +514,7 @@ int pa_bm_free_seq(pa_bm* bm, int64_t seq) {
     for (int32_t b : t)
       if (--bm->ref[b] == 0) bm->free_stack.push_back(b);
   }
+  if (bm->caching) bm->chain_unref(it->second.chain);
   bm->seqs.erase(it);
   return PA_OK;
 }
@@ -713,7 +779,7 @@ int pa_bm_swap_stats(pa_bm* bm, int64_t* num_swapped, int64_t* host_free, int64_
 int pa_bm_cache_stats(pa_bm* bm, pa_bm_cache_stats_t* out) {
   if (!bm || !out) return PA_ERR_INVALID_ARG;
   out->enabled = bm->caching ? 1 : 0;
-  out->num_cached = static_cast<int64_t>(bm->index.size());
+  out->num_cached = bm->num_cached;
   out->num_idle = bm->idle_count;
   out->hit_blocks = bm->hit_blocks;
   out->evictions = bm->evictions;

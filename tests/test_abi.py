@@ -40,7 +40,7 @@ def test_probe_library_exports_its_header_and_nothing_of_the_product():
     assert not set(names) & set(declared_functions())
 
 
-@pytest.mark.parametrize("name", ["libpa_host.so", "libpa_host_asan.so"])
+@pytest.mark.parametrize("name", ["libpa_host.so", "libpa_host_asan.so", "libpa_host_collide.so"])
 def test_host_only_libraries_export_the_block_manager(name):
     """The host-only builds (g++, no HIP) export every pa_bm_* entry point and the status strings."""
     import subprocess
