@@ -368,6 +368,64 @@ __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slo
 }
 
 
+// What a step needs to know about one tile of the list: its (row, KV head,
+// tile), the row's packed tokens and the segment's tile count.  Each lane
+// works out one tile of a window of 64 consecutive tiles of the wave's range
+// from the tables in LDS (a binary search over the prefix sums); a step reads
+// the tile after next from its lane (readlane, wave-uniform results), so no LDS
+// lookup lies between one tile's copies and the next's.  A new window is built
+// once per 62 tiles.
+struct STile {
+  int n, j, ti, packed, nt;
+};
+
+__device__ __forceinline__ STile stile_of(int64_t x, const int32_t* s_pre, const int32_t* s_len, int n_seqs,
+                                          int hkv) {
+  int lo = 0, hi = n_seqs - 1;  // last n with hkv * s_pre[n] <= x (a row with tiles)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (static_cast<int64_t>(hkv) * s_pre[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  STile t;
+  t.n = lo;
+  t.nt = tiles_of(s_pre, lo);
+  const int64_t rem = x - static_cast<int64_t>(hkv) * s_pre[lo];
+  t.j = static_cast<int>(rem / t.nt);
+  t.ti = static_cast<int>(rem - static_cast<int64_t>(t.j) * t.nt);
+  t.packed = s_len[lo];
+  return t;
+}
+
+__device__ __forceinline__ STile lane_stile(const STile& d, int idx) {
+  STile t;
+  t.n = __builtin_amdgcn_readlane(d.n, idx);
+  t.j = __builtin_amdgcn_readlane(d.j, idx);
+  t.ti = __builtin_amdgcn_readlane(d.ti, idx);
+  t.packed = __builtin_amdgcn_readlane(d.packed, idx);
+  t.nt = __builtin_amdgcn_readlane(d.nt, idx);
+  return t;
+}
+
+__device__ __forceinline__ TilePos pos_of(const STile& t) { return TilePos{t.n, t.j, t.ti}; }
+
+// Table entries of a tile's blocks.  Always loaded (index clamped into the
+// row) and replaced by -1 past the end of the row's tokens in the pool, so no
+// load sits behind a branch and the compiler keeps the pipeline's loads in flight.
+template <int B, int TOK>
+__device__ __forceinline__ Tb<TOK / B> load_tb_s(const STile& t, const int32_t* __restrict__ block_tables,
+                                                 int max_blocks) {
+  const int32_t* row = block_tables + static_cast<int64_t>(t.n) * max_blocks;
+  const int S = pool_tokens(t.packed);
+  const int t0 = t.ti * TOK;
+  Tb<TOK / B> tb;
+#pragma unroll
+  for (int i = 0; i < TOK / B; ++i) {
+    const int e = row[min(t0 / B + i, max_blocks - 1)];
+    tb.blk[i] = t0 + i * B < S ? e : -1;
+  }
+  return tb;
+}
+
 template <int D, int B, int KV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void decode_stream(
     const uint16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
@@ -437,20 +495,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   const int64_t x1 = sp.start(wave_id + 1);
   if (x0 >= x1) return;
 
-  // locate x0: last n with hkv * s_pre[n] <= x0
-  int lo = 0, hi = n_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (static_cast<int64_t>(hkv) * s_pre[mid] <= x0) lo = mid; else hi = mid - 1;
-  }
-  TilePos cur;
-  cur.n = lo;
-  {
-    const int64_t rem = x0 - static_cast<int64_t>(hkv) * s_pre[lo];
-    const int nt = tiles_of(s_pre, lo);
-    cur.j = static_cast<int>(rem / nt);
-    cur.ti = static_cast<int>(rem - static_cast<int64_t>(cur.j) * nt);
-  }
+  // the window of tiles xb .. xb + 63 (past the range: its last tile again)
+  int64_t xb = x0;
+  STile mine = stile_of(min(xb + lane, x1 - 1), s_pre, s_len, n_seqs, hkv);
+  STile cur = lane_stile(mine, 0);
   int piece_start = cur.ti;  // first tile of the current piece
   bool first_piece = true;
 
@@ -463,15 +511,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // The queries are those of the segment: loaded when a segment starts, not
   // again for each of its tiles.
   std::conditional_t<F8, QOp16<D>, QOp<D>> qc;
-  auto segment_queries = [&](TilePos t) {
+  auto segment_queries = [&](const STile& t) {
     if constexpr (F8)
-      load_q16<D, I8>(qc, t, q, hq, g, r, gq);
+      load_q16<D, I8>(qc, pos_of(t), q, hq, g, r, gq);
     else
-      load_q<D, false>(qc, t, q, hq, g, r, gq);
+      load_q<D, false>(qc, pos_of(t), q, hq, g, r, gq);
   };
-  TilePos nxt = x1 - x0 > 1 ? advance(cur, s_pre, hkv) : cur;
-  Tb<NB> tbA = load_tb<B, TOK>(cur, block_tables, max_blocks, s_len);
-  Tb<NB> tbB = load_tb<B, TOK>(nxt, block_tables, max_blocks, s_len);
+  STile nxt = lane_stile(mine, 1);  // the range's only tile again when it has one
+  Tb<NB> tbA = load_tb_s<B, TOK>(cur, block_tables, max_blocks);
+  Tb<NB> tbB = load_tb_s<B, TOK>(nxt, block_tables, max_blocks);
   segment_queries(cur);
   dma_tile<D, B, F8>(&g_stage0[wave][0], cur.j, tbA, k_pool, v_pool, hkv, num_blocks, lane);
   // FP8: the scales of a tile's blocks travel with it, one tile ahead like its Q
@@ -484,12 +532,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   // table entries of the tile after it load into tb2.  Returns false after
   // the last tile.
   // the step's new token, for tiles that end a segment holding one
-  auto wants_new = [&](TilePos t) -> bool {
-    return !F8 && k_new != nullptr && has_new_token(s_len[t.n]) && t.ti == tiles_of(s_pre, t.n) - 1;
+  auto wants_new = [&](const STile& t) -> bool {
+    return !F8 && k_new != nullptr && has_new_token(t.packed) && t.ti == t.nt - 1;
   };
   // one buffer: a step patches its tile before it loads the next tile's token
   NewTok<D> ntok;
-  if (wants_new(cur)) load_new<D>(ntok, cur, k_new, v_new, slots, hkv, r, gq);
+  if (wants_new(cur)) load_new<D>(ntok, pos_of(cur), k_new, v_new, slots, hkv, r, gq);
   auto step = [&](auto sc_tag, const Tb<NB>& tbc, const Sc8& scc, const Tb<NB>& tbn, Sc8& scn,
                   Tb<NB>& tb2) -> bool {
     constexpr int SC = decltype(sc_tag)::value;
@@ -499,10 +547,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     // current stage is read into registers first; the next tile's copies are
     // issued after it and stay in flight through this tile's compute.
     const bool has_next = x + 1 < x1;
-    const int packed = s_len[cur.n];
+    const int packed = cur.packed;
     const int S = attended_tokens(packed);
-    const int nt_cur = tiles_of(s_pre, cur.n);
-    const TilePos nxt2 = x + 2 < x1 ? advance(nxt, s_pre, hkv) : nxt;
+    const int nt_cur = cur.nt;
+    // the tile after next, from the window (rebuilt when used up)
+    const int64_t x2 = min(x + 2, x1 - 1);
+    if (x2 - xb >= 64) {
+      xb = x2;
+      mine = stile_of(min(xb + lane, x1 - 1), s_pre, s_len, n_seqs, hkv);
+    }
+    const STile nxt2 = lane_stile(mine, static_cast<int>(x2 - xb));
     const int t0 = cur.ti * TOK;
     if constexpr (F8) {
       Buf8<D> b;
@@ -515,7 +569,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       const bool row_end = whole_rec != nullptr && cur.j == 0 && cur.ti == nt_cur - 1;
       int row_slot = -1;
       if (row_end) row_slot = slots[cur.n];
-      tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
+      tb2 = load_tb_s<B, TOK>(nxt2, block_tables, max_blocks);
       scn = load_scales<B>(tbn, scales, nxt.j, hkv, num_blocks, gq);
       dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
@@ -541,8 +595,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
           slots_out[cur.n] = at_next ? ntok.slot : -1;
         }
       }
-      tb2 = load_tb<B, TOK>(nxt2, block_tables, max_blocks, s_len);
-      if (has_next && wants_new(nxt)) load_new<D>(ntok, nxt, k_new, v_new, slots, hkv, r, gq);
+      tb2 = load_tb_s<B, TOK>(nxt2, block_tables, max_blocks);
+      if (has_next && wants_new(nxt)) load_new<D>(ntok, pos_of(nxt), k_new, v_new, slots, hkv, r, gq);
       dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
       f32x4 sco[2];
@@ -551,7 +605,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     }
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
-      flush<D>(st, cur, piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, whole_rec, hq, hkv, g, r,
+      flush<D>(st, pos_of(cur), piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, whole_rec, hq, hkv, g, r,
                 gq, F8 ? st.vref : 1.f);
       first_piece = false;
       piece_start = 0;

@@ -64,23 +64,6 @@ constexpr int kTokShift = F8 ? 6 : 5;
 
 __device__ __forceinline__ int tiles_of(const int32_t* s_pre, int n) { return s_pre[n + 1] - s_pre[n]; }
 
-// Next tile in (n, j, ti) order; only called when one exists.
-__device__ __forceinline__ TilePos advance(TilePos t, const int32_t* s_pre, int hkv) {
-  if (t.ti + 1 < tiles_of(s_pre, t.n)) {
-    ++t.ti;
-    return t;
-  }
-  t.ti = 0;
-  if (t.j + 1 < hkv) {
-    ++t.j;
-    return t;
-  }
-  t.j = 0;
-  do {
-    ++t.n;
-  } while (tiles_of(s_pre, t.n) == 0);
-  return t;
-}
 
 // Per sequence the kernel keeps (tokens << 2) | (fits << 1) | new: `tokens`
 // counts the attended tokens, `new` marks that the last of them is the step's
@@ -114,23 +97,6 @@ __device__ __forceinline__ void load_new(NewTok<D>& nt, TilePos t, const uint16_
   if (t.j == 0) nt.slot = slots[t.n];
 }
 
-// Table entries of a tile's blocks.  Always loaded (index clamped into the
-// row) and replaced by -1 past the end of the sequence, so no load sits behind
-// a branch and the compiler can keep the pipeline's loads in flight.
-template <int B, int TOK>
-__device__ __forceinline__ Tb<TOK / B> load_tb(TilePos t, const int32_t* __restrict__ block_tables, int max_blocks,
-                                               const int32_t* s_len) {
-  const int32_t* row = block_tables + static_cast<int64_t>(t.n) * max_blocks;
-  const int S = pool_tokens(s_len[t.n]);
-  const int t0 = t.ti * TOK;
-  Tb<TOK / B> tb;
-#pragma unroll
-  for (int i = 0; i < TOK / B; ++i) {
-    const int e = row[min(t0 / B + i, max_blocks - 1)];
-    tb.blk[i] = t0 + i * B < S ? e : -1;
-  }
-  return tb;
-}
 
 // Q^T operand of MFMA jj: 8 elements of head r.  With a bf16 cache lane gq
 // takes d-chunk 4 jj + gq (as the key layout interleaves chunks); with an FP8
