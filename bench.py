@@ -28,6 +28,12 @@ With --kv int8 the cache holds INT8 codes with the same scales and layout and
 the INT8 entry points (pa_copy_blocks_int8, pa_decode_step_int8) take their
 places.
 
+The default run (gqa8b, bf16) also measures the other workloads -- FP8 and
+INT8 caches, the block-size sweep, the shared-prefix fork and the 32-layer
+long context -- each in a child run of this script before this process
+touches the GPU, and keeps their figures in its line under
+"other_workloads" (--no-others skips them).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa8b] [--kv bf16|fp8|int8]
 """
 
@@ -103,7 +109,55 @@ def parse():
                     help="run only a plain 1 GiB device-to-device copy (known bytes) to scale HBM counters")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="run only pa_read_probe over 4 GiB: the achievable HBM read rate of this GPU")
+    ap.add_argument("--no-others", action="store_true",
+                    help="default run: skip the other workloads' lines (FP8, INT8, block-size sweep, fork, long)")
     return ap.parse_args()
+
+
+# The other workloads, each measured by a child run of this script (its own
+# process, started before this one touches the GPU) and summarised inside the
+# default line under "other_workloads": name, arguments.
+OTHER_WORKLOADS = [
+    ("gqa8b-fp8", ["--kv", "fp8"]),
+    ("gqa8b-int8", ["--kv", "int8"]),
+    ("sweep_b8", ["--workload", "sweep_b8", "--steps", "50"]),
+    ("sweep_b16", ["--workload", "sweep_b16", "--steps", "50"]),
+    ("sweep_b32", ["--workload", "sweep_b32", "--steps", "50"]),
+    ("fork-shared", ["--workload", "fork", "--shared", "--steps", "40", "--warmup", "5"]),
+    ("long", ["--workload", "long", "--steps", "3", "--warmup", "1"]),
+]
+
+
+def summarize_line(line):
+    """The figures of one bench line that the default line keeps for another workload."""
+    d = json.loads(line)
+    rf = d.get("roofline", {})
+    return {"value": d["value"], "unit": d["unit"], "us_per_step": d["config"]["us_per_step"],
+            "steps": d["steps"], "warmup": d["warmup"], "dtype": d["dtype"],
+            "roofline_achieved": rf.get("achieved"), "roofline_frac": rf.get("frac"),
+            "kernel_avg_us": rf.get("avg_us"), "tail_waste_slots": d["config"].get("tail_waste_slots"),
+            "config": d["config"]["workload"]}
+
+
+def other_workloads(timeout_s=300):
+    """Run each of OTHER_WORKLOADS as a child `bench.py` and keep the figures of its line."""
+    import subprocess
+    rows = []
+    for name, extra in OTHER_WORKLOADS:
+        print(f"[bench] other workload {name}", file=sys.stderr, flush=True)
+        cmd = [sys.executable, os.path.abspath(__file__), "--no-cpu-baseline", "--no-others"] + extra
+        row = {"workload": name}
+        try:
+            cp = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout_s)
+            lines = [ln for ln in cp.stdout.splitlines() if ln.startswith("{")]
+            if cp.returncode != 0 or not lines:
+                row["error"] = f"exit {cp.returncode}: {cp.stderr.strip().splitlines()[-1:] or ''}"
+            else:
+                row.update(summarize_line(lines[-1]))
+        except subprocess.TimeoutExpired:
+            row["error"] = f"no line within {timeout_s} s"
+        rows.append(row)
+    return rows
 
 
 def workload(name):
@@ -571,6 +625,9 @@ def main():
     if not args.no_cpu_baseline:  # before the GPU is initialised: its worker processes are plain forks
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_seconds, args.kv)
+    others = None
+    if not args.no_others and args.workload == "gqa8b" and args.kv == "bf16" and not args.shared:
+        others = other_workloads()  # child processes, while this one has not touched the GPU
     total = args.steps + args.warmup + 1
     print(f"[bench] building workload {w.name}", file=sys.stderr, flush=True)
     if args.shared and (w.name != "fork" or args.kv != "bf16"):
@@ -710,6 +767,8 @@ def main():
         res["roofline"]["bytes"] = "unique KV a step needs: each shared full block once, every row's own blocks"
     if cpu is not None:
         res["cpu_baseline"] = cpu
+    if others is not None:
+        res["other_workloads"] = others
     print(json.dumps(res), flush=True)
 
 
