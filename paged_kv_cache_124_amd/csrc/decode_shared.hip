@@ -707,19 +707,16 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
           val[k][e] = pb[k] ? x : 0.f;
         }
       }
-      float mx = mine ? m_l : -__FLT_MAX__;  // finite: exp2(m - mx) is never exp2(-inf - -inf)
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+      // finite: exp2(m - mx) is never exp2(-inf - -inf)
+      const float mx = wave_max(mine ? m_l : -__FLT_MAX__);
       const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
-      float zz = mine ? f * z_l : 0.f;
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+      const float zz = wave_sum(mine ? f * z_l : 0.f);
       float uu[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) uu[e] = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float fk = __shfl(f, k);
+        const float fk = lane_f32(f, k);
 #pragma unroll
         for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
       }
@@ -738,8 +735,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
         const float* rr = base + lane < sg.cnt ? record(base + lane, h) : nullptr;
         if (rr) mx = fmaxf(mx, rr[0]);
       }
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+      mx = wave_max(mx);
       float zz = 0.f;
       float uu[E];
 #pragma unroll
@@ -756,7 +752,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
           for (int i = 0; i < 8; ++i) {
             const int k = k0 + i;
             const float* rk = k < c64 ? record(base + k, h) : nullptr;
-            fk[i] = __shfl(f, k & 63);
+            fk[i] = lane_f32(f, k & 63);
             if (!rk) fk[i] = 0.f;
             const float* ra = rk ? rk : rec;  // any valid address; the value is replaced by zero
 #pragma unroll
@@ -771,8 +767,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
             for (int e = 0; e < E; ++e) uu[e] += fk[i] * val[i][e];
         }
       }
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+      zz = wave_sum(zz);
       const float inv = zz > 0.f ? 1.f / zz : 0.f;  // every token left out: zeros
 #pragma unroll
       for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);

@@ -731,16 +731,18 @@ __global__ __launch_bounds__(256) void merge_step8(const float* __restrict__ rec
     kv[e] = code8_value<I8>(kc[e]);
     x.v[e] = code8_value<I8>(vc[e]) * vs;
   }
-  // scores: q . (key codes' values), times scale * log2(e) * key scale, as the decode kernel forms them
+  // scores: q . (key codes' values), times scale * log2(e) * key scale, as the decode kernel forms them;
+  // only for the heads this wave merges (wave, wave + 4, ... below g)
   const float sk = scale_log2 * ks;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float dot = 0.f;
+    x.m[i] = 0.f;
+    if (wave + 4 * i < g) {
+      float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) dot += bf16_bits_to_f32(qb[i][e]) * kv[e];
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
-    x.m[i] = dot * sk;
+      for (int e = 0; e < E; ++e) dot += bf16_bits_to_f32(qb[i][e]) * kv[e];
+      x.m[i] = wave_sum(dot) * sk;
+    }
   }
   merge_segment<D, NewTokenPiece<D>>(rec, prefix, out, n_seqs, hq, hkv, g, g, total_waves, j, n, x);
   // store the codes and move the row on where the slot is the row's next position

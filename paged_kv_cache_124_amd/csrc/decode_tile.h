@@ -446,6 +446,45 @@ __device__ __forceinline__ void append_row(const AppendArgs& ap, const RowToken<
   }
 }
 
+// ---- wave-wide reductions on the VALU ----------------------------------------
+// A sum or maximum over the 64 lanes of a wave with DPP row operations of
+// gfx9 (each a few cycles, where a shuffle through the LDS crossbar takes a
+// memory latency): quad swaps give every lane its quad's value, the half-row
+// and row mirrors its row's, row_bcast:15 adds row 0 into row 1 and row 2
+// into row 3, and row_bcast:31 the first two rows into rows 2 and 3, so lane
+// 63 ends with the whole wave's; readlane hands it to every lane.  All 64
+// lanes must be active.  The order of the operations is fixed, so the result
+// is deterministic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<0xB1, 0xf>(0.f, v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E, 0xf>(0.f, v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141, 0xf>(0.f, v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xf>(0.f, v);  // row_mirror
+  v += dpp_f32<0x142, 0xa>(0.f, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f32<0x143, 0xc>(0.f, v);  // row_bcast:31 into rows 2 and 3
+  return lane_f32(v, 63);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x4E, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x141, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x140, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x142, 0xa>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x143, 0xc>(-INFINITY, v));
+  return lane_f32(v, 63);
+}
+
 // One head's merge when the segment has at most KP pieces (2 <= cnt <= KP):
 // the maxima, sums and value rows of all pieces load together, in one memory
 // round trip.  Piece 0's record is at `first`, piece k >= 1's at
@@ -478,22 +517,18 @@ __device__ __forceinline__ void merge_head_few(const float* __restrict__ first, 
       val[k][e] = pk ? x : 0.f;
     }
   }
-  float mx = mine ? m_l : -INFINITY;
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+  float mx = wave_max(mine ? m_l : -INFINITY);
   if constexpr (X::kOn) {
     if (x.has) mx = fmaxf(mx, x.score(hi));
   }
   const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
-  float zz = mine ? f * z_l : 0.f;
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+  float zz = wave_sum(mine ? f * z_l : 0.f);
   float uu[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) uu[e] = 0.f;
 #pragma unroll
   for (int k = 0; k < KP; ++k) {
-    const float fk = __shfl(f, k);  // zero for missing pieces
+    const float fk = lane_f32(f, k);  // zero for missing pieces
 #pragma unroll
     for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
   }
@@ -585,8 +620,7 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
       const float* rr = record(base + lane, h);
       if (rr) mx = fmaxf(mx, rr[0]);
     }
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+    mx = wave_max(mx);
     if constexpr (X::kOn) {
       if (x.has) mx = fmaxf(mx, x.score(h >> 2));
     }
@@ -607,7 +641,7 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
         for (int i = 0; i < 8; ++i) {
           const int k = k0 + i;
           const float* rk = k < cnt ? record(base + k, h) : nullptr;
-          fk[i] = __shfl(f, k & 63);
+          fk[i] = lane_f32(f, k & 63);
           if (!rk) fk[i] = 0.f;
           const float* ra = rk ? rk : rec;  // any valid address; the value is replaced by zero
 #pragma unroll
@@ -622,8 +656,7 @@ __device__ __forceinline__ void merge_segment(const float* __restrict__ rec, con
           for (int e = 0; e < E; ++e) uu[e] += fk[i] * val[i][e];
       }
     }
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) zz += __shfl_xor(zz, sh);
+    zz = wave_sum(zz);
     float inv;
     if constexpr (X::kOn) {
       const float fx = x.has ? __builtin_amdgcn_exp2f(x.score(h >> 2) - mx) : 0.f;
