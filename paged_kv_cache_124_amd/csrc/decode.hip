@@ -274,8 +274,7 @@ __global__ __launch_bounds__(256) void decode_mfma(
         x[a][i] = tok < S && blk_ok[a] ? s[a][i] * scale_log2 : -INFINITY;  // out-of-pool tokens left out
         tmax = fmaxf(tmax, x[a][i]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_across_groups(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -303,8 +302,7 @@ __global__ __launch_bounds__(256) void decode_mfma(
   }
 
   // ---- merge the 4 waves through LDS -----------------------------------------
-  z_run += __shfl_xor(z_run, 16);
-  z_run += __shfl_xor(z_run, 32);
+  z_run = sum_across_groups(z_run);
   // the wave's region now holds its summary values (its own tiles are done: no other wave reads it before the barrier)
   __asm__ volatile("" ::: "memory");
   float* lds_m = lds;                         // [kWaves][16]

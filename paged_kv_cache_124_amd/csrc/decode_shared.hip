@@ -290,9 +290,7 @@ __device__ __forceinline__ void tile_group(Acc<D> (&st)[NC], const Buf<D>& b, co
       }
   }
 #pragma unroll
-  for (int cb = 0; cb < NC; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 16));
-#pragma unroll
-  for (int cb = 0; cb < NC; ++cb) tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 32));
+  for (int cb = 0; cb < NC; ++cb) tmax[cb] = max_across_groups(tmax[cb]);
   float alpha[NC];
   bf16x8 phi[NC], plo[NC];
   bool moved = false;
@@ -354,8 +352,7 @@ __device__ __forceinline__ void flush_unit(Acc<D> (&st)[2], const TileInfo& t, i
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     if (cb == 1 && cols <= 16) break;
-    float zt = st[cb].z + __shfl_xor(st[cb].z, 16);
-    zt += __shfl_xor(zt, 32);
+    const float zt = sum_across_groups(st[cb].z);
     const int c = 16 * cb + r;
     if (c < cols) {
       if (whole) {

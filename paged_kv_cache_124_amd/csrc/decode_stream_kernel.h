@@ -135,8 +135,7 @@ __device__ __forceinline__ void load_q16(QOp16<D>& qo, TilePos t, const uint16_t
     for (int e = 0; e < 4; ++e)
       amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xffff0000u))));
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  amax = max_across_groups(amax);
   int ex = 0;
   if (amax > 0.f && amax <= __FLT_MAX__) frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
   const int k = min(max(15 - ex, -126), 126);
@@ -156,8 +155,7 @@ __device__ __forceinline__ void load_q16(QOp16<D>& qo, TilePos t, const uint16_t
     }
   }
   if constexpr (I8) {
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
+    sum = sum_across_groups(sum);
     qo.offset = kI8Offset * sum;
   } else {
     qo.offset = 0.f;
@@ -267,15 +265,13 @@ __device__ __forceinline__ void codes_tile(Acc<D>& st, const Buf8<D>& b, const S
         tmax = fmaxf(tmax, x[u][a][i]);
       }
     }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_across_groups(tmax);
   const float m_new = fmaxf(st.m, tmax);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
   // the value-scale reference: the largest scale of the segment so far (wave-uniform)
   float tv = fmaxf(fmaxf(sc.v[0][0], sc.v[0][1]), fmaxf(sc.v[1][0], sc.v[1][1]));
-  tv = fmaxf(tv, __shfl_xor(tv, 16));
-  tv = fmaxf(tv, __shfl_xor(tv, 32));
+  tv = max_across_groups(tv);
   float f = alpha;  // rescale of the accumulated P.V
   if (tv > st.vref) {
     f *= st.vref / tv;
@@ -301,8 +297,7 @@ __device__ __forceinline__ void codes_tile(Acc<D>& st, const Buf8<D>& b, const S
   st.z = st.z * alpha + psum;
   if constexpr (I8) {
     // every code is finite, and a missing token has P = 0: no masking
-    pcol += __shfl_xor(pcol, 16);
-    pcol += __shfl_xor(pcol, 32);
+    pcol = sum_across_groups(pcol);
     const float off = kI8Offset * pcol;
 #pragma unroll
     for (int mm = 0; mm < D / 16; ++mm) {
@@ -341,8 +336,7 @@ template <int D>
 __device__ __forceinline__ void flush(Acc<D>& st, TilePos t, bool whole, int slot, int64_t wave_id, uint16_t* out,
                                       float* rec, float* whole_rec, int hq, int hkv, int g, int r, int gq,
                                       float omul) {
-  float zt = st.z + __shfl_xor(st.z, 16);
-  zt += __shfl_xor(zt, 32);
+  const float zt = sum_across_groups(st.z);
   if (r < g) {
     if (whole && whole_rec == nullptr) {
       const float inv = zt > 0.f ? omul / zt : 0.f;  // every token left out: zeros

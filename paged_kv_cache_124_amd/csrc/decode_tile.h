@@ -317,6 +317,45 @@ __device__ __forceinline__ void qk_tile(f32x4 (&s)[2], const Buf<D>& b, const QO
   }
 }
 
+// ---- across the 16-lane groups of a wave ----------------------------------------
+// op over lanes l, l ^ 16, l ^ 32, l ^ 48 -- the lanes that hold the same MFMA
+// column (or row) in the four 16-lane groups -- with gfx950's permlane swaps
+// (VALU operations; a shuffle goes through the LDS crossbar).  With both
+// operands holding the same value, v_permlane16_swap leaves in them the values
+// of the lanes with lane bit 4 clear and set, and v_permlane32_swap those with
+// bit 5 clear and set (checked lane by lane on the GPU).  The operand pairs
+// are those of two __shfl_xor steps (16, then 32), up to the order of a
+// commutative op: the same result bits.  Written as inline assembly: the
+// compiler's builtins for these instructions had op(first, second) folded to
+// the first value (the second treated as equal to it).  The s_nop pairs give
+// the VALU-write-to-permlane wait states the compiler inserts around them.
+__device__ __forceinline__ void permlane16_swap(unsigned& a, unsigned& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(unsigned& a, unsigned& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+template <class Op>
+__device__ __forceinline__ float across_groups(float x, Op op) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  permlane16_swap(a, b);
+  const float y = op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  unsigned c = __builtin_bit_cast(unsigned, y), e = c;
+  permlane32_swap(c, e);
+  return op(__builtin_bit_cast(float, c), __builtin_bit_cast(float, e));
+}
+
+struct MaxOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct SumOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
+__device__ __forceinline__ float max_across_groups(float x) { return across_groups(x, MaxOp{}); }
+__device__ __forceinline__ float sum_across_groups(float x) { return across_groups(x, SumOp{}); }
+
 // Online softmax (base 2) and weighted values on the matrix cores for one
 // tile.  `full` (wave-uniform): all 32 tokens exist and their blocks are in
 // the pool, so no masking is needed.
@@ -338,8 +377,7 @@ __device__ __forceinline__ void pv_tile(Acc<D>& st, const f32x4 (&s)[2], const B
       x[a][i] = i < (a ? n1 : n0) ? s[a][i] * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, x[a][i]);
     }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_across_groups(tmax);
   const float m_new = fmaxf(st.m, tmax);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
