@@ -54,8 +54,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: achieved HBM GB/s (KV read) + µs/step, 8B GQA shape"
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 10
-EVENT_SPAN = 10  # steps per event pair on workloads whose steps launch nothing but the decode
-RING = 32
+EVENT_SPAN = 100  # steps per event pair on workloads whose steps launch nothing but the decode
+RING = 512  # pinned staging buffers; the host records one event per half ring
 
 
 # HBM traffic of the decode kernels, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a
@@ -266,14 +266,15 @@ class Runner:
         self.ct = ctypes
         self.words = 3 * n
         self.ring = RING
-        self.host = [torch.empty(self.words, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+        # one pinned allocation, RING buffers of `words` int32 each (each 256-byte aligned)
+        stride = -(-self.words // 64) * 64
+        self.host_all = torch.empty(RING * stride, dtype=torch.int32, pin_memory=True)
+        self.host = [self.host_all[b * stride:b * stride + self.words] for b in range(RING)]
         hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded
-        self.mapped = []
-        for hb in self.host:
-            dp = ctypes.c_void_p()
-            ok = hip.hipHostGetDevicePointer(ctypes.byref(dp), ctypes.c_void_p(hb.data_ptr()), 0) == 0
-            self.mapped.append(dp.value if ok and dp.value else None)
-        self.zero_copy = all(m is not None for m in self.mapped)
+        dp = ctypes.c_void_p()
+        ok = hip.hipHostGetDevicePointer(ctypes.byref(dp), ctypes.c_void_p(self.host_all.data_ptr()), 0) == 0
+        self.zero_copy = bool(ok and dp.value)
+        self.mapped = [dp.value + 4 * b * stride if self.zero_copy else None for b in range(RING)]
         self.dev = None if self.zero_copy else [torch.empty(self.words, dtype=torch.int32, device=device)
                                                 for _ in range(RING)]
         self.half_ev = [torch.cuda.Event(), torch.cuda.Event()]
@@ -653,7 +654,7 @@ def main():
     # the ring's own event records; elsewhere (the fork workload's copies, the long
     # workload's appends) one pair brackets the decode of every EVENT_EVERY-th step.
     long_ctx = w.name == "long"
-    span = EVENT_SPAN if not (long_ctx or run.fork) else 1
+    span = min(EVENT_SPAN, args.steps) if not (long_ctx or run.fork) else 1
     sampled = list(range(0, args.steps, 1 if long_ctx else EVENT_EVERY))  # a long step is ~12 ms: events every step
     timing = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     spans, open_span = [], None  # [start event, end event, steps, bytes]
@@ -697,6 +698,9 @@ def main():
     else:  # per-launch averages of the spans, each counted once per step it covers
         dec_us = [1e3 * a.elapsed_time(b) / n for a, b, n, _ in spans for _ in range(n)]
         sampled_bytes = sum(b for _, _, _, b in spans)
+    if not dec_us:  # no span fitted between the ring's event records: the whole timed region instead
+        dec_us = [gpu_ms * 1e3 / args.steps] * args.steps
+        sampled_bytes = kv_bytes
     dec_avg_us = sum(dec_us) / len(dec_us)
     bytes_per_launch = kv_bytes / args.steps
     achieved = sampled_bytes / (sum(dec_us) * 1e-6) / 1e9
