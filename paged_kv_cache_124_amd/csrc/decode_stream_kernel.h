@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       if (row_end) row_slot = slots[cur.n];
       tb2 = load_tb_s<B, TOK>(nxt2, block_tables, max_blocks);
       scn = load_scales<B>(tbn, scales, nxt.j, hkv, num_blocks, gq);
-      dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
+      if (has_next) dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
       codes_tile<D, I8>(st, b, scc, qc, t0, S, full, scale_log2, gq);
       if (row_end && lane == 0) slots_out[cur.n] = row_slot;
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       }
       tb2 = load_tb_s<B, TOK>(nxt2, block_tables, max_blocks);
       if (has_next && wants_new(nxt)) load_new<D>(ntok, pos_of(nxt), k_new, v_new, slots, hkv, r, gq);
-      dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
+      if (has_next) dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
       f32x4 sco[2];
       qk_tile<D>(sco, b, qc);
