@@ -500,8 +500,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   reset(st);
   // Two LDS stages per wave: while tile x is computed (from registers read
   // out of one stage), tile x + 1's keys and values stream into the other
-  // stage and the table entries of tile x + 2 load as well.  These loads are
-  // unconditional (a missing successor repeats the current tile's addresses).
+  // stage and the table entries of tile x + 2 load as well.  The table-entry
+  // loads are unconditional (a missing successor repeats the current tile's
+  // addresses); a wave's last tile issues no copy.
   // The queries are those of the segment: loaded when a segment starts, not
   // again for each of its tiles.
   std::conditional_t<F8, QOp16<D>, QOp<D>> qc;
