@@ -585,7 +585,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     }
     tb2 = load_tb_unit<B>(nxt2, block_tables, max_blocks);
     if (has_next && wants_new(nxt)) new_of(ntok, nxt);
-    dma_tile<D, B, false>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
+    if (has_next) dma_tile<D, B, false>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
     const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
     if (grp) {
       bool live[2];
