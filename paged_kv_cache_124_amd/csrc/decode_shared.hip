@@ -661,8 +661,14 @@ __device__ __forceinline__ const float* piece_record(const SegPieces& sg, int k,
 // or its own) with the common-maximum rule, in wave order; a segment a decode
 // wave finished whole was written there.  The step's new token is stored and
 // the row moved forward as in merge_stream.
+// Two waves per workgroup, each merging heads wave, wave + 2, ...: the fork
+// workload's 2,048 (row, KV head) workgroups then hold 4,096 waves, which all
+// fit on the GPU at once (with four waves per workgroup, 8,192 waves at 7 per
+// SIMD needed a second round).
+constexpr int kMergeSharedWaves = 2;
+
 template <int D>
-__global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ rec, const int32_t* __restrict__ seq_info,
+__global__ __launch_bounds__(64 * kMergeSharedWaves) void merge_shared(const float* __restrict__ rec, const int32_t* __restrict__ seq_info,
                                                     uint16_t* __restrict__ out, int hq, int hkv, int g,
                                                     int64_t total_waves, AppendArgs ap) {
   constexpr int E = D / 64;
@@ -685,7 +691,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
     const float* pb[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) pb[k] = piece_record<D>(sg, k, sp, rec);
-    for (int h = wave; h < g; h += 4) {
+    for (int h = wave; h < g; h += kMergeSharedWaves) {
       const float* mine = nullptr;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -726,7 +732,7 @@ __global__ __launch_bounds__(256) void merge_shared(const float* __restrict__ re
       const float* p0 = piece_record<D>(sg, k, sp, rec);
       return p0 ? p0 + (row0 + h) * (D + 4) : nullptr;
     };
-    for (int h = wave; h < g; h += 4) {
+    for (int h = wave; h < g; h += kMergeSharedWaves) {
       float mx = -__FLT_MAX__;  // finite, as above
       for (int base = 0; base < sg.cnt; base += 64) {
         const float* rr = base + lane < sg.cnt ? record(base + lane, h) : nullptr;
@@ -823,7 +829,7 @@ static void launch_shared_db(const StreamPlan& p, hipStream_t s, const void* q, 
   decode_shared<D, B><<<dim3(p.workgroups), dim3(256), p.lds_bytes, s>>>(
       static_cast<const uint16_t*>(q), k, v, bt, cl, groups, n_groups, static_cast<uint16_t*>(out), rec, seq_info,
       n, hq, hkv, g, max_blocks, num_blocks, scale_log2, ap.k_new, ap.v_new, slots_in, slots_ws);
-  merge_shared<D><<<dim3(hkv, n), dim3(256), 0, s>>>(rec, seq_info, static_cast<uint16_t*>(out), hq, hkv, g,
+  merge_shared<D><<<dim3(hkv, n), dim3(64 * kMergeSharedWaves), 0, s>>>(rec, seq_info, static_cast<uint16_t*>(out), hq, hkv, g,
                                                      static_cast<int64_t>(p.workgroups) * kSW, ap);
 }
 
