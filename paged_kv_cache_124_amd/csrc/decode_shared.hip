@@ -691,14 +691,22 @@ __global__ __launch_bounds__(64 * kMergeSharedWaves) void merge_shared(const flo
     const float* pb[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) pb[k] = piece_record<D>(sg, k, sp, rec);
-    for (int h = wave; h < g; h += kMergeSharedWaves) {
+    // per head: the lane's piece (lane k holds piece k's maximum and sum) and
+    // the value rows of all pieces; two heads' loads are issued together
+    struct HeadLoad {
+      bool mine;
+      float m_l, z_l;
+      float val[8][E];
+    };
+    auto load_head = [&](int h, HeadLoad& hl) {
       const float* mine = nullptr;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (lane == k && pb[k]) mine = pb[k] + (row0 + h) * (D + 4);
       const float* ml = mine ? mine : rec;  // any valid address; unused
-      const float m_l = ml[0], z_l = ml[1];
-      float val[8][E];
+      hl.mine = mine != nullptr;
+      hl.m_l = ml[0];
+      hl.z_l = ml[1];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         // a missing piece loads from any valid address and contributes zero
@@ -707,13 +715,15 @@ __global__ __launch_bounds__(64 * kMergeSharedWaves) void merge_shared(const flo
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float x = rk[4 + lane + 64 * e];
-          val[k][e] = pb[k] ? x : 0.f;
+          hl.val[k][e] = pb[k] ? x : 0.f;
         }
       }
+    };
+    auto finish_head = [&](int h, const HeadLoad& hl) {
       // finite: exp2(m - mx) is never exp2(-inf - -inf)
-      const float mx = wave_max(mine ? m_l : -__FLT_MAX__);
-      const float f = mine ? __builtin_amdgcn_exp2f(m_l - mx) : 0.f;
-      const float zz = wave_sum(mine ? f * z_l : 0.f);
+      const float mx = wave_max(hl.mine ? hl.m_l : -__FLT_MAX__);
+      const float f = hl.mine ? __builtin_amdgcn_exp2f(hl.m_l - mx) : 0.f;
+      const float zz = wave_sum(hl.mine ? f * hl.z_l : 0.f);
       float uu[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) uu[e] = 0.f;
@@ -721,11 +731,19 @@ __global__ __launch_bounds__(64 * kMergeSharedWaves) void merge_shared(const flo
       for (int k = 0; k < 8; ++k) {
         const float fk = lane_f32(f, k);
 #pragma unroll
-        for (int e = 0; e < E; ++e) uu[e] += fk * val[k][e];
+        for (int e = 0; e < E; ++e) uu[e] += fk * hl.val[k][e];
       }
       const float inv = zz > 0.f ? 1.f / zz : 0.f;  // every token left out: zeros
 #pragma unroll
       for (int e = 0; e < E; ++e) o[h * D + lane + 64 * e] = f32_to_bf16_bits(uu[e] * inv);
+    };
+    for (int h = wave; h < g; h += 2 * kMergeSharedWaves) {
+      const int h2 = h + kMergeSharedWaves;
+      HeadLoad a, b;
+      load_head(h, a);
+      if (h2 < g) load_head(h2, b);
+      finish_head(h, a);
+      if (h2 < g) finish_head(h2, b);
     }
   } else if (!sg.whole) {
     auto record = [&](int k, int h) -> const float* {
