@@ -719,10 +719,17 @@ __global__ __launch_bounds__(256) void merge_step8(const float* __restrict__ rec
   NewTokenPiece<D> x;
   x.has = in_pool;
   x.whole = whole;
+  // all quotients first (their fp64 divisions overlap), then the codes
+  double kq[E], vq[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    kc[e] = code8<I8>(bf16_bits_to_f32(kb[e]), ks);
-    vc[e] = code8<I8>(bf16_bits_to_f32(vb[e]), vs);
+    kq[e] = code8_quotient<I8>(bf16_bits_to_f32(kb[e]), ks);
+    vq[e] = code8_quotient<I8>(bf16_bits_to_f32(vb[e]), vs);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kc[e] = code8_encode<I8>(kq[e], bf16_bits_to_f32(kb[e]), ks);
+    vc[e] = code8_encode<I8>(vq[e], bf16_bits_to_f32(vb[e]), vs);
     kv[e] = code8_value<I8>(kc[e]);
     x.v[e] = code8_value<I8>(vc[e]) * vs;
   }
