@@ -597,29 +597,31 @@ def main():
         probe = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_124_amd", "libpa_probe.so"))
         probe.pa_read_probe.restype = ctypes.c_int
         probe.pa_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                        ctypes.c_void_p]
+                                        ctypes.c_int, ctypes.c_void_p]
         buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")  # 4 GiB, 16x the Infinity Cache
         sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-        def read_probe(wgs):
+        def read_probe(wgs, nt):
             st = probe.pa_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4, ctypes.c_void_p(sink.data_ptr()),
-                                     wgs, stream)
+                                     wgs, nt, stream)
             if st != 0:
                 raise RuntimeError(f"pa_read_probe: status {st}")
-        rates = {}
-        for wgs in (256, 512, 1024, 2048):  # 4, 8, 16, 32 waves per CU on 256 CUs
-            for _ in range(3):
-                read_probe(wgs)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(20):
-                read_probe(wgs)
-            b.record()
-            torch.cuda.synchronize()
-            rates[wgs] = round(buf.numel() * 4 * 20 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
-        print(json.dumps({"read_ceiling_gb_s": max(rates.values()), "by_workgroups": rates, "bytes": buf.numel() * 4,
-                          "launches": 20, "peak_gb_s": HBM_PEAK_GBS}))
+        rates = {"nontemporal": {}, "default_policy": {}}
+        for nt, key in ((1, "nontemporal"), (0, "default_policy")):
+            for wgs in (256, 512, 1024, 2048):  # 4, 8, 16, 32 waves per CU on 256 CUs
+                for _ in range(3):
+                    read_probe(wgs, nt)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(20):
+                    read_probe(wgs, nt)
+                b.record()
+                torch.cuda.synchronize()
+                rates[key][wgs] = round(buf.numel() * 4 * 20 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+        print(json.dumps({"read_ceiling_gb_s": max(rates["nontemporal"].values()),
+                          "default_policy_gb_s": max(rates["default_policy"].values()), "by_workgroups": rates,
+                          "bytes": buf.numel() * 4, "launches": 20, "peak_gb_s": HBM_PEAK_GBS}))
         return
     w = workload(args.workload)
     cpu = None

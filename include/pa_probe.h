@@ -8,10 +8,12 @@
  * byte of `buf` (device, `bytes` a multiple of 4096) once: wave w of the
  * `workgroups` workgroups of 256 threads reads the 4 KiB pieces w, w + W, ...
  * (W waves), four pieces of 16-byte loads in flight, and one word per
- * workgroup goes to `sink` (device, uint32 [workgroups]).  Asynchronous on
- * `stream` (a hipStream_t as void*); time it with events.  Returns 0, or 1
- * (bytes not a multiple of 4096, workgroups outside 1..65535, NULL buffers)
- * before any launch, or 7 when the runtime refused the launch.
+ * workgroup goes to `sink` (device, uint32 [workgroups]).  `nontemporal` 1
+ * marks the loads non-temporal (the cache policy the decode kernels stream
+ * the KV pool with), 0 leaves the default policy.  Asynchronous on `stream`
+ * (a hipStream_t as void*); time it with events.  Returns 0, or 1 (bytes not
+ * a multiple of 4096, workgroups outside 1..65535, nontemporal not 0 or 1,
+ * NULL buffers) before any launch, or 7 when the runtime refused the launch.
  */
 #ifndef PA_PROBE_H
 #define PA_PROBE_H
@@ -23,7 +25,7 @@
 extern "C" {
 #endif
 
-int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
+int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, int nontemporal, void* stream);
 
 #ifdef __cplusplus
 }

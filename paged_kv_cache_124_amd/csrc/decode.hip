@@ -198,8 +198,8 @@ __global__ __launch_bounds__(256) void decode_mfma(
       const int pbv = __shfl(tbl, (tv / B) - lb0);
       uint4 v = make_uint4(0, 0, 0, 0);
       if (tv < S && pbv >= 0 && pbv < num_blocks)
-        v = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(pbv) * blk_stride + (tv % B) * D +
-                                            ((slot ^ stage_swz<D, false>(row)) << 3));
+        v = load_kv16(vh + static_cast<int64_t>(pbv) * blk_stride + (tv % B) * D +
+                      ((slot ^ stage_swz<D, false>(row)) << 3));
       *reinterpret_cast<uint4*>(vst + p * 1024 + lane * 16) = v;
     }
 #pragma unroll
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void decode_mfma(
 #pragma unroll
       for (int jj = 0; jj < KCH; ++jj) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (kval) v = *reinterpret_cast<const uint4*>(kb + (4 * jj + gq) * X);
+        if (kval) v = load_kv16(kb + (4 * jj + gq) * X);
         kop[a][jj] = __builtin_bit_cast(bf16x8, v);
       }
       const int tv = t0 + 16 * a + 4 * gq;

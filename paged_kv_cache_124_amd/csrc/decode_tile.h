@@ -166,7 +166,7 @@ __device__ __forceinline__ int stage_swz(int t) {
 
 // Copy one tile's key and value rows into an LDS stage with global_load_lds
 // (16 bytes per lane, 1 KiB per instruction, straight to LDS: no registers
-// held while in flight).  A missing block (past the end, or an id outside the
+// held while in flight), non-temporal (kKvLoadPolicy).  A missing block (past the end, or an id outside the
 // pool) is read from block 0 -- a valid address -- and its tokens are masked
 // out in pv_tile.
 // Instruction p fills stage bytes p * 1024 .. + 1023, i.e. tile rows
@@ -199,8 +199,8 @@ __device__ __forceinline__ void dma_tile(unsigned char* stage_ptr, int j, const 
     }
     const int64_t pb = (e >= 0 && e < num_blocks) ? e : 0;
     const int64_t off = pb * blk_stride + (t % B) * RB + ((slot ^ stage_swz<D, F8>(t)) << 4);
-    __builtin_amdgcn_global_load_lds(kb + off, stage + p * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb + off, stage + kStageHalf<D> + p * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kb + off, stage + p * 1024, 16, 0, kKvLoadPolicy);
+    __builtin_amdgcn_global_load_lds(vb + off, stage + kStageHalf<D> + p * 1024, 16, 0, kKvLoadPolicy);
   }
 }
 

@@ -3,7 +3,9 @@
 // gather: "PagedAttention: Virtual Memory for the KV Cache", section 13).
 // A plain streaming read -- every byte of a buffer once, in 4 KiB pieces of
 // 16-byte loads, no LDS, no compute beyond an XOR that keeps the loads alive --
-// is the ceiling a kernel that streams whole blocks can approach.
+// is the ceiling a kernel that streams whole blocks can approach.  The loads
+// take either the default cache policy or the non-temporal one (the "nt"
+// modifier: lines not kept for reuse), which the decode kernels use for the KV.
 
 #include <hip/hip_runtime.h>
 
@@ -14,9 +16,22 @@
 namespace pa {
 namespace {
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
 // Wave w reads the 4 KiB pieces w, w + W, w + 2W, ... of the buffer (W waves
 // in the launch), four pieces (16 loads of 16 bytes per lane) in flight; the
 // 64 lanes of one load cover 1 KiB contiguous, as the decode's block copies do.
+template <bool NT>
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ buf, int64_t pieces,
                                                          uint32_t* __restrict__ sink) {
   constexpr int UNR = 4;
@@ -31,7 +46,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
       const int64_t bb = b + u * W < pieces ? b + u * W : b;  // past the end: read piece b again (counted once below)
       const uint4* p = buf + bb * 256;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[u][k] = p[k * 64 + lane];
+      for (int k = 0; k < 4; ++k) v[u][k] = load16<NT>(p + k * 64 + lane);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
@@ -46,12 +61,15 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
 }  // namespace
 }  // namespace pa
 
-extern "C" int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
+extern "C" int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, int nontemporal,
+                             void* stream) {
   using namespace pa;
   if (bytes % 4096 != 0 || workgroups < 1 || workgroups > 65535) return 1;
   if (bytes == 0) return 0;
   if (!buf || !sink) return 1;
-  read_probe_kernel<<<dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+  if (nontemporal != 0 && nontemporal != 1) return 1;
+  const auto kernel = nontemporal ? read_probe_kernel<true> : read_probe_kernel<false>;
+  kernel<<<dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint4*>(buf), static_cast<int64_t>(bytes / 4096), sink);
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
