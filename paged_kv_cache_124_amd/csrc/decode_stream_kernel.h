@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   __shared__ int32_t s_wsum[kSW];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: stage addresses go to m0 from scalars
   const int lane = tid & 63;
   const int r = lane & 15;
   const int gq = lane >> 4;

@@ -198,9 +198,13 @@ __device__ __forceinline__ void dma_tile(unsigned char* stage_ptr, int j, const 
       e = lrow >= B ? tb.blk[p * RPP / B + 1] : tb.blk[p * RPP / B];
     }
     const int64_t pb = (e >= 0 && e < num_blocks) ? e : 0;
-    const int64_t off = pb * blk_stride + (t % B) * RB + ((slot ^ stage_swz<D, F8>(t)) << 4);
-    __builtin_amdgcn_global_load_lds(kb + off, stage + p * 1024, 16, 0, kKvLoadPolicy);
-    __builtin_amdgcn_global_load_lds(vb + off, stage + kStageHalf<D> + p * 1024, 16, 0, kKvLoadPolicy);
+    // block base (wave-uniform where the piece lies in one block) plus the
+    // lane's 32-bit offset inside the image: the copy takes the scalar-base
+    // form, with no per-lane 64-bit address arithmetic
+    const uint32_t loff = static_cast<uint32_t>((t % B) * RB + ((slot ^ stage_swz<D, F8>(t)) << 4));
+    __builtin_amdgcn_global_load_lds(kb + pb * blk_stride + loff, stage + p * 1024, 16, 0, kKvLoadPolicy);
+    __builtin_amdgcn_global_load_lds(vb + pb * blk_stride + loff, stage + kStageHalf<D> + p * 1024, 16, 0,
+                                     kKvLoadPolicy);
   }
 }
 
