@@ -39,13 +39,18 @@ HOST_FLAGS = ["-O2", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
 SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops on its own.
-# atomic optimizer off: it turns the decode kernel's lane-0 work claim into a
-# wave-aggregated atomic whose result is waited for at once, which would stall
-# the tile pipeline; the claim's result is only needed one worker later.
+# atomic optimizer off: it folds a wave's atomics on one address into a scan and
+# one atomic; the library's atomics are per-lane LDS updates (the batch checks'
+# bitmaps, the shared-prefix kernel's row claims) whose results are used at once.
+# MFMA in VGPR form: the matrix-core accumulators of the decode kernels are
+# loop-carried and rescaled by VALU code, and with the accumulator-register form
+# every tile copied them into AGPRs and back (64 moves per tile in the bf16
+# kernel; none in this form, and fewer registers).
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 
