@@ -532,6 +532,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
   };
   // one buffer: a step patches its tile before it loads the next tile's token
   NewTok<D> ntok;
+  // A store issued between two tiles makes the next stage wait for it as well
+  // (loads and stores count in one in-order counter).  So in the bf16 kernel
+  // the wave's first summary or output written before its last tile, and its
+  // first forwarded slot, are held here and stored after the last tile.  (The
+  // kernels over codes keep storing at once: holding the state there cost more
+  // in registers than the wait: FP8 +0.6 us, INT8 +2.5 us per step.)
+  Acc<D> pend;
+  reset(pend);
+  TilePos pend_pos{0, 0, 0};
+  bool pend_whole = false, has_pend = false;
+  int pend_slot = 0;
+  int pend_row = -1, pend_row_slot = -1;  // forwarded slot: row, value (lane 0)
+  auto forward_slot = [&](int n, int v) {
+    if (!F8 && pend_row < 0) {
+      pend_row = n;
+      pend_row_slot = v;
+    } else {
+      slots_out[n] = v;
+    }
+  };
   if (wants_new(cur)) load_new<D>(ntok, pos_of(cur), k_new, v_new, slots, hkv, r, gq);
   auto step = [&](auto sc_tag, const Tb<NB>& tbc, const Sc8& scc, const Tb<NB>& tbn, Sc8& scn,
                   Tb<NB>& tb2) -> bool {
@@ -569,7 +589,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       if (has_next) dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
       codes_tile<D, I8>(st, b, scc, qc, t0, S, full, scale_log2, gq);
-      if (row_end && lane == 0) slots_out[cur.n] = row_slot;
+      if (row_end && lane == 0) forward_slot(cur.n, row_slot);
     } else {
       Buf<D> b;
       wait_stage_copies();
@@ -587,7 +607,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
           const bool at_next = next_fits(packed) && ntok.slot >= 0 &&
                                static_cast<int64_t>(ntok.slot) < static_cast<int64_t>(num_blocks) * B &&
                                ntok.slot % B == S0 % B;
-          slots_out[cur.n] = at_next ? ntok.slot : -1;
+          forward_slot(cur.n, at_next ? ntok.slot : -1);
         }
       }
       tb2 = load_tb_s<B, TOK>(nxt2, block_tables, max_blocks);
@@ -600,12 +620,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
     }
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
-      flush<D>(st, pos_of(cur), piece_start == 0 && seg_end, first_piece ? 0 : 1, wave_id, out, rec, whole_rec, hq, hkv, g, r,
-                gq, F8 ? st.vref : 1.f);
+      const bool whole = piece_start == 0 && seg_end;
+      const int slot = first_piece ? 0 : 1;
+      if (!F8 && has_next && !has_pend) {
+        pend = st;
+        pend_pos = pos_of(cur);
+        pend_whole = whole;
+        pend_slot = slot;
+        has_pend = true;
+        reset(st);
+      } else {
+        flush<D>(st, pos_of(cur), whole, slot, wave_id, out, rec, whole_rec, hq, hkv, g, r, gq, F8 ? st.vref : 1.f);
+      }
       first_piece = false;
       piece_start = 0;
     }
-    if (!has_next) return false;
+    if (!has_next) {
+      if constexpr (!F8) {
+        if (has_pend) flush<D>(pend, pend_pos, pend_whole, pend_slot, wave_id, out, rec, whole_rec, hq, hkv, g, r, gq, 1.f);
+        if (lane == 0 && pend_row >= 0) slots_out[pend_row] = pend_row_slot;
+      }
+      return false;
+    }
     if (seg_end) segment_queries(nxt);
     ++x;
     cur = nxt;
