@@ -616,6 +616,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       const bool full = t0 + 32 <= S && __all(b.blk0 && b.blk1);
       f32x4 sco[2];
       qk_tile<D>(sco, b, qc);
+      // at a segment's last tile the next segment's queries load here, while
+      // the tile's softmax and P.V run: qc is free once the score products
+      // have read it (issued after the tile's math, they held up the next wait)
+      if (has_next && cur.ti == nt_cur - 1) segment_queries(nxt);
       pv_tile<D>(st, sco, b, t0, S, full, scale_log2, gq);
     }
     const bool seg_end = cur.ti == nt_cur - 1;
@@ -642,7 +646,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       }
       return false;
     }
-    if (seg_end) segment_queries(nxt);
+    if (F8 && seg_end) segment_queries(nxt);  // the bf16 tile loaded them after its score products
     ++x;
     cur = nxt;
     nxt = nxt2;
