@@ -130,6 +130,43 @@ def test_step_other_shapes_are_unsupported():
     assert e.value.status == 2  # PA_ERR_UNSUPPORTED
 
 
+def test_step_many_short_rows():
+    """1,500 rows of 1..100 tokens at the 8B GQA head shape: a decode wave's range then crosses about ten segment
+    ends (summaries, whole-segment outputs and forwarded slots stored before its last tile).  The fused step must
+    equal pa_append_step + pa_decode bit for bit, over a workspace of 0xFF bytes, and match the oracle on every row."""
+    import paged_kv_cache_124_amd as pa
+    print("[case] decode_step 1500 short rows", flush=True)
+    w = synth.gqa8b()
+    lens = [int(x) for x in np.random.default_rng(1201).integers(1, 101, size=1500)]
+    bs = w.block_size
+    c = make_case(w, lens, num_blocks=sum(-(-s // bs) for s in lens) + len(lens) + 16,
+                  max_blocks=-(-max(lens) // bs) + 2, seed=1202)
+    n = len(lens)
+    st, slots, pairs, _ = c.bm.append_slots(list(range(n)))
+    assert st == 0 and len(pairs) == 0
+    slots = torch.from_numpy(np.asarray(slots, np.int32)).cuda()
+    kn = synth.randn((n, w.hkv, w.d), torch.bfloat16, w.value_scale, 1203, "cuda")
+    vn = synth.randn((n, w.hkv, w.d), torch.bfloat16, w.value_scale, 1204, "cuda")
+    max_ctx = max(lens) + 1
+    k1, v1, t1, l1 = _state(c)
+    k2, v2, t2, l2 = _state(c)
+    out1 = torch.empty_like(c.q)
+    pa.pa_append_step(k1, v1, kn, vn, slots, t1, l1)
+    pa.pa_decode(out1, c.q, k1, v1, t1, l1, c.scale, max_ctx)
+    need = pa.pa_decode_workspace_bytes(n, c.hq, c.hkv, w.d, bs, max_ctx, pa.PA_BF16)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out2 = torch.empty_like(c.q)
+    pa.pa_decode_step(out2, c.q, kn, vn, k2, v2, slots, t2, l2, c.scale, max_ctx, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out1), _bits(out2)), "fused output differs from append + decode"
+    assert torch.equal(_bits(k1), _bits(k2)) and torch.equal(_bits(v1), _bits(v2)), "pools differ"
+    assert torch.equal(t1, t2) and torch.equal(l1, l2), "tables / lengths differ"
+    assert l2.cpu().numpy().tolist() == [s + 1 for s in lens]
+    ref = OA.paged_decode(c.q.cpu().double().numpy(), k2.cpu().double().numpy(), v2.cpu().double().numpy(),
+                          t2.cpu().numpy(), l2.cpu().numpy().tolist(), c.scale)
+    assert_close(out2, ref, "decode_step 1500 short rows")
+
+
 def test_step_gqa8b_matches_oracle_and_is_repeatable():
     """The 8B GQA layer: one fused step for all 64 sequences, twice from the same state."""
     import paged_kv_cache_124_amd as pa
