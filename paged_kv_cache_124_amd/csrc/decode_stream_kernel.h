@@ -228,10 +228,11 @@ __device__ __forceinline__ void read_tile8(Buf8<D>& b, const unsigned char* stag
 
 // One staged 64-token tile of codes into the lane's running state: scores of
 // both sub-tiles, one online-softmax update, P.V.  sc holds the tile's key and
-// value scales; `full` = all 64 tokens present.
-template <int D, bool I8>
+// value scales.  FULL: all 64 tokens present (the usual tile), so no score is
+// masked and no code zeroed; a separate instance takes the partial tiles.
+template <int D, bool I8, bool FULL>
 __device__ __forceinline__ void codes_tile(Acc<D>& st, const Buf8<D>& b, const Sc8& sc, const QOp16<D>& qc, int t0,
-                                           int S, bool full, float scale_log2, int gq) {
+                                           int S, float scale_log2, int gq) {
   // scores: [sub-tile u][slab a][i] is token 32 u + 16 a + 4 gq + i for head r
   f32x4 s[2][2];
 #pragma unroll
@@ -251,7 +252,7 @@ __device__ __forceinline__ void codes_tile(Acc<D>& st, const Buf8<D>& b, const S
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int a = 0; a < 2; ++a)
-      n[u][a] = full ? 4 : (b.ok[u][a] ? min(max(S - (t0 + 32 * u + 16 * a + 4 * gq), 0), 4) : 0);
+      n[u][a] = FULL ? 4 : (b.ok[u][a] ? min(max(S - (t0 + 32 * u + 16 * a + 4 * gq), 0), 4) : 0);
   float x[2][2][4];
   float tmax = -INFINITY;
 #pragma unroll
@@ -317,7 +318,7 @@ __device__ __forceinline__ void codes_tile(Acc<D>& st, const Buf8<D>& b, const S
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) msk[u][a] = n[u][a] >= 4 ? 0xffffffffu : (1u << (8 * n[u][a])) - 1u;
+      for (int a = 0; a < 2; ++a) msk[u][a] = FULL || n[u][a] >= 4 ? 0xffffffffu : (1u << (8 * n[u][a])) - 1u;
 #pragma unroll
     for (int mm = 0; mm < D / 16; ++mm)
 #pragma unroll
@@ -588,7 +589,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       scn = load_scales<B>(tbn, scales, nxt.j, hkv, num_blocks, gq);
       if (has_next) dma_tile<D, B, F8>(&stn[wave][0], nxt.j, tbn, k_pool, v_pool, hkv, num_blocks, lane);
       const bool full = t0 + TOK <= S && __all(b.ok[0][0] && b.ok[0][1] && b.ok[1][0] && b.ok[1][1]);
-      codes_tile<D, I8>(st, b, scc, qc, t0, S, full, scale_log2, gq);
+      if (full)
+        codes_tile<D, I8, true>(st, b, scc, qc, t0, S, scale_log2, gq);
+      else
+        codes_tile<D, I8, false>(st, b, scc, qc, t0, S, scale_log2, gq);
       if (row_end && lane == 0) forward_slot(cur.n, row_slot);
     } else {
       Buf<D> b;
@@ -620,7 +624,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void d
       // the tile's softmax and P.V run: qc is free once the score products
       // have read it (issued after the tile's math, they held up the next wait)
       if (has_next && cur.ti == nt_cur - 1) segment_queries(nxt);
-      pv_tile<D>(st, sco, b, t0, S, full, scale_log2, gq);
+      // constant flags, so that the full tile (the usual one) carries no masking
+      if (full)
+        pv_tile<D>(st, sco, b, t0, S, true, scale_log2, gq);
+      else
+        pv_tile<D>(st, sco, b, t0, S, false, scale_log2, gq);
     }
     const bool seg_end = cur.ti == nt_cur - 1;
     if (seg_end || !has_next) {
