@@ -299,14 +299,16 @@ __device__ __forceinline__ void codes_tile(Acc<D>& st, const Buf8<D>& b, const S
   if constexpr (I8) {
     // every code is finite, and a missing token has P = 0: no masking
     pcol = sum_across_groups(pcol);
-    const float off = kI8Offset * pcol;
+    // the tile's products start from minus the offset, so they come out without it
+    const float noff = -kI8Offset * pcol;
+    const f32x4 t0v{noff, noff, noff, noff};
 #pragma unroll
     for (int mm = 0; mm < D / 16; ++mm) {
-      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16<true>(b.v[0][0][mm], b.v[0][1][mm]), P[0],
-                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16<true>(b.v[0][0][mm], b.v[0][1][mm]), P[0], t0v,
+                                                       0, 0, 0);
       t = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16<true>(b.v[1][0][mm], b.v[1][1][mm]), P[1], t, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.o[mm][i] = st.o[mm][i] * f + (t[i] - off);
+      for (int i = 0; i < 4; ++i) st.o[mm][i] = st.o[mm][i] * f + t[i];
     }
   } else {
     if (__any(f != 1.f)) {
