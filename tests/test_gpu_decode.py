@@ -5,8 +5,10 @@ import pytest
 import torch
 
 import synth
-from harness import assert_close, make_case, oracle_outputs, run_decode
+from harness import assert_close, fp8_logical, make_case, oracle_outputs, run_decode
 from oracle import attention as OA
+from oracle import fp8 as OF
+from oracle import int8 as OI
 
 pytestmark = pytest.mark.gpu
 
@@ -214,3 +216,37 @@ def test_decode_leading_tile_outside_pool_is_left_out(dtype, hq, hkv):
     q = c.q.float().cpu().numpy().astype(np.float64)
     assert_close(out[0:1], OA.dense_attention(q[0], K, V, c.scale)[None], f"leading tile out of pool {dtype} g={hq // hkv}")
     assert_close(out[1:2], oracle_outputs(c, [1]), f"row 1 untouched {dtype} g={hq // hkv}")
+
+
+@pytest.mark.parametrize("codes", ["", "e4m3", "int8"])
+def test_decode_middle_block_outside_pool_between_full_tiles(codes):
+    """One block in the middle of a 1,000-token row lies outside [0, num_blocks): the tile that holds it runs the
+    masked tile math, the full tiles before and after it the unmasked instance, within one wave's range (forty
+    3,000-token rows give every wave several tiles).  The row attends to every other token; the other rows are
+    untouched."""
+    print(f"[case] middle block out of pool {codes or 'bf16'}", flush=True)
+    lens = [1000] + [3000] * 40
+    c = make_case(synth.gqa8b(), lens, hq=8, hkv=2, seed=1790, fp8=codes == "e4m3", int8=codes == "int8")
+    bs = c.block_size
+    tables = c.tables.copy()
+    tables[0, 20] = c.num_blocks + 5  # tokens 20 B .. 21 B - 1 of row 0
+    out = run_decode(c, tables_dev=torch.from_numpy(tables).cuda())
+    keep = [t for t in range(1000) if not 20 * bs <= t < 21 * bs]
+    q = c.q.float().cpu().numpy().astype(np.float64)
+    if codes:
+        kc, vc, ks, vs = fp8_logical(c, [int(b) for b in c.tables[0][: -(-1000 // bs)]])
+        # one "block" per kept token: codes [n][Hkv][1][D] with that token's block scale
+        kb = np.stack([kc[t // bs, :, t % bs][:, None, :] for t in keep])
+        vb = np.stack([vc[t // bs, :, t % bs][:, None, :] for t in keep])
+        ksb = np.stack([ks[t // bs] for t in keep])
+        vsb = np.stack([vs[t // bs] for t in keep])
+        oracle = OI if codes == "int8" else OF
+        ref = oracle.paged_decode(q[0:1], kb, vb, ksb, vsb, np.arange(len(keep))[None, :], [len(keep)], c.scale)
+    else:
+        k_log = c.k.cpu().double().numpy()
+        v_log = c.v.cpu().double().numpy()
+        K = np.stack([k_log[int(c.tables[0][t // bs]), :, t % bs] for t in keep])
+        V = np.stack([v_log[int(c.tables[0][t // bs]), :, t % bs] for t in keep])
+        ref = OA.dense_attention(q[0], K, V, c.scale)[None]
+    assert_close(out[0:1], ref, f"middle block out of pool {codes or 'bf16'}")
+    assert_close(out[[1, 40]], oracle_outputs(c, [1, 40]), f"other rows untouched {codes or 'bf16'}")
